@@ -1,0 +1,34 @@
+"""CPU oracle for the speculative-decoding verification step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product (the HIP library and its
+Python binding) imports, links or runs anything here.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+use this package.
+
+The oracle is a plain, slow, obviously-correct numpy implementation in fp64
+of what the verification step computes.  It shares no code with the GPU path.
+Each function cites the passage of the source pages it follows.  The pages are
+cited by title and section:
+
+  [P1] "投機的デコーディングとドラフトモデル" (tech-tldr.com)
+  [P2] "LLM推論の高速化｜KVキャッシュと投機的デコーディングを自作で実測" (r-jc.jp)
+  [P3] "Speculative Decoding（投機的デコーディング）とは？仕組みと速くなる条件、
+        LM Studio・llama.cpp・vLLMでの設定" (issoh.co.jp)
+
+Modules:
+  sampler    -- modified rejection sampling (accept test, first rejection,
+                residual / bonus inverse-CDF draw, emitted tokens)
+  attention  -- KV append and causal multi-query verify attention, plus the
+                uncached full-sequence recompute it must agree with
+  truncate   -- the KV length reset after verification
+  formulas   -- closed forms: acceptance rate, expected committed tokens,
+                speed-up estimate, KV-cache bytes
+  bf16       -- exact decoding of bfloat16 bit patterns to fp64
+
+Parity status: every function here is pinned by ``-m "not gpu"`` tests against
+printed values of the pages, closed forms, library routines or brute force.
+Nothing is "parity unpinned" except the mapping of decisions that fall inside
+the 1e-6 threshold band (those draws are counted, not compared).
+"""
+
+from . import attention, bf16, formulas, sampler, truncate  # noqa: F401

@@ -1,0 +1,96 @@
+"""The pins must catch plausible mistakes.
+
+Each test plants one mistake in the oracle on the CPU (monkeypatch, undone after
+the test) and checks that a pin of the other test files fails under it.  This
+is evidence that the pins constrain the oracle, not a test of the GPU path.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import formulas as F
+from oracle import sampler as S
+from tests import _law
+from tests import test_oracle_attention as TA
+from tests import test_oracle_sampler as TS
+
+
+def _small_law_pin():
+    """Brute-force pin on V=3, gamma=2 (fast version of the full pin)."""
+    TS.test_bruteforce_law_preserves_target_distribution(3, 2, 1, 0.0)
+
+
+def _assert_pin_fails(fn):
+    with pytest.raises(AssertionError):
+        fn()
+
+
+def test_pins_hold_unmutated():
+    _small_law_pin()
+    TA.test_matches_torch_sdpa(2, 4, 2, 5, 16, [0, 9])
+
+
+def test_swapped_ratio_is_caught(monkeypatch):
+    monkeypatch.setattr(S, "accept_threshold", lambda p, q: np.minimum(1.0, np.float64(q) / np.float64(p)))
+    _assert_pin_fails(_small_law_pin)
+
+
+def test_swapped_residual_is_caught(monkeypatch):
+    monkeypatch.setattr(S, "residual", lambda p, q: np.maximum(q - p, 0.0))
+    _assert_pin_fails(_small_law_pin)
+
+
+def test_unclipped_residual_is_caught(monkeypatch):
+    monkeypatch.setattr(S, "residual", lambda p, q: np.abs(p - q))
+    _assert_pin_fails(_small_law_pin)
+
+
+def test_non_strict_accept_is_caught(monkeypatch):
+    monkeypatch.setattr(S, "accepts", lambda u, thr: bool(np.float64(u) <= thr))
+    _assert_pin_fails(TS.test_accept_test_is_strict)
+
+
+def test_left_searchsorted_is_caught(monkeypatch):
+    def left(w, u):
+        c = np.cumsum(w)
+        return int(np.searchsorted(c / c[-1], u, side="left"))
+
+    monkeypatch.setattr(S, "inverse_cdf", left)
+    _assert_pin_fails(TS.test_zero_mass_tokens_never_drawn)
+
+
+def test_reversed_token_order_is_caught(monkeypatch):
+    def reversed_cdf(w, u):
+        c = np.cumsum(w[::-1])
+        return len(w) - 1 - int(np.searchsorted(c / c[-1], u, side="right"))
+
+    monkeypatch.setattr(S, "inverse_cdf", reversed_cdf)
+    _assert_pin_fails(TS.test_q_equal_p_accepts_all_and_bonus_is_numpy_choice)
+
+
+def test_temperature_as_multiplier_is_caught(monkeypatch):
+    orig = S.softmax_t
+    monkeypatch.setattr(S, "softmax_t", lambda z, T: orig(z, 1.0 / T))
+    # case (V=3, gamma=2, seed=1) runs at T = 0.7
+    _assert_pin_fails(lambda: TS.test_bruteforce_law_preserves_target_distribution(3, 2, 1, 0.0))
+
+
+def test_missing_causal_mask_is_caught(monkeypatch):
+    # every new row sees all n new keys
+    monkeypatch.setattr(A, "visible_keys", lambda L, i: L + 10**9)
+    _assert_pin_fails(lambda: TA.test_matches_torch_sdpa(2, 4, 2, 5, 16, [0, 9]))
+
+
+def test_off_by_one_mask_is_caught(monkeypatch):
+    monkeypatch.setattr(A, "visible_keys", lambda L, i: L + i)  # drops the row's own key
+    _assert_pin_fails(lambda: TA.test_matches_torch_sdpa(2, 4, 2, 5, 16, [3, 9]))
+
+
+def test_wrong_exponent_is_caught(monkeypatch):
+    from tests import test_oracle_formulas as TF
+
+    orig = F.expected_committed
+    monkeypatch.setattr(F, "expected_committed", lambda a, g: orig(a, g - 1) if g > 1 else orig(a, g) * 0.9)
+    row = {"T": 0.7, "k": 4, "alpha": 0.901, "E": 4.10, "factor": 2.19}
+    _assert_pin_fails(lambda: TF.test_expected_tokens_matches_printed_ksweep(row))

@@ -1,0 +1,193 @@
+"""Seeded generators for the synthetic workloads.
+
+Host generators (numpy, ``default_rng([config, stream, rep])``) serve configs
+1-4 and any reduced-size case; they are deterministic and device independent.
+Stream 0 draws logits and Q/K/V, stream 1 the draft-sampling noise, stream 2
+the verify uniforms, stream 3 the cache lengths.
+
+Device generators (torch, a seeded generator on the GPU) serve config 5, whose
+KV cache (about 34 GB) cannot be drawn on the host in reasonable time.  Its
+lengths still come from the host stream 3, so they match the host recipe.
+
+bfloat16 tensors are carried as uint16 bit patterns on the host and as
+``torch.bfloat16`` on the device.  fp32 -> bf16 is round-to-nearest-even on
+both (torch's conversion is RNE).
+"""
+
+import numpy as np
+
+from .configs import Config
+
+
+def rng(cfg: Config, stream: int, rep: int = 0):
+    return np.random.default_rng([cfg.cid, stream, rep])
+
+
+def bf16_bits(x):
+    """Round an fp32 array to bfloat16 (nearest, ties to even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _store(x32, dtype):
+    return bf16_bits(x32) if dtype == "bf16" else np.ascontiguousarray(x32, dtype=np.float32)
+
+
+def _as_f32(stored, dtype):
+    return bf16_bits_to_f32(stored) if dtype == "bf16" else stored
+
+
+def _gumbel_argmax(z_over_t, noise_uniform):
+    """Index of max(z/T + Gumbel), i.e. one draw from softmax(z/T) per row."""
+    with np.errstate(divide="ignore"):
+        g = -np.log(-np.log(noise_uniform))
+    return np.argmax(z_over_t + g, axis=-1).astype(np.int32)
+
+
+def sampler_inputs(cfg: Config, temperature=None, rep: int = 0, B=None):
+    """Host arrays for the rejection sampler.
+
+    Returns target_logits [B, gamma+1, V], draft_logits [B, gamma, V] (fp32, or
+    uint16 bf16 bits), draft_tokens int32 [B, gamma] drawn from
+    softmax(draft/T), uniforms fp64 [B, gamma+1] in [0, 1), and temperature.
+    """
+    T = cfg.temperatures[0] if temperature is None else float(temperature)
+    B = cfg.B if B is None else int(B)
+    g, V = cfg.gamma, cfg.V
+    r0 = rng(cfg, 0, rep)
+    if cfg.p is not None:
+        # Toy: every target row is ln p, the draft row is ln q.
+        zt = np.broadcast_to(np.log(np.array(cfg.p, np.float64)).astype(np.float32), (B, g + 1, V))
+        zd = np.broadcast_to(np.log(np.array(cfg.q, np.float64)).astype(np.float32), (B, g, V))
+        zt = np.ascontiguousarray(zt)
+        zd = np.ascontiguousarray(zd)
+    else:
+        zt = (cfg.t_std * r0.standard_normal((B, g + 1, V), dtype=np.float32)).astype(np.float32)
+        zd = (cfg.mix * zt[:, :g] + cfg.noise_std * r0.standard_normal((B, g, V), dtype=np.float32)).astype(
+            np.float32
+        )
+    zt_s = _store(zt, cfg.dtype)
+    zd_s = _store(zd, cfg.dtype)
+    # Drafts come from the distribution the verifier will see: the stored values.
+    zd_seen = _as_f32(zd_s, cfg.dtype).astype(np.float64) / T
+    noise = rng(cfg, 1, rep).random((B, g, V))
+    x = _gumbel_argmax(zd_seen, noise)
+    u = rng(cfg, 2, rep).random((B, g + 1))
+    return {
+        "target_logits": zt_s,
+        "draft_logits": zd_s,
+        "draft_tokens": np.ascontiguousarray(x, dtype=np.int32),
+        "uniforms": np.ascontiguousarray(u, dtype=np.float64),
+        "temperature": T,
+    }
+
+
+def lengths(cfg: Config, rep: int = 0, B=None):
+    B = cfg.B if B is None else int(B)
+    lo, hi = cfg.L
+    return rng(cfg, 3, rep).integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def attention_inputs(cfg: Config, rep: int = 0, B=None, max_T=None):
+    """Host arrays for verify attention (configs 3-5 shapes, or reduced B).
+
+    q [B, Hq, n_q, D], k_new / v_new [B, Hkv, n_q, D], k_cache / v_cache
+    [B, Hkv, max_T, D] -- every row filled with N(0,1), including rows past the
+    committed length, which the verifier must never read -- and lens int32 [B].
+    """
+    B = cfg.B if B is None else int(B)
+    max_T = cfg.max_T if max_T is None else int(max_T)
+    r0 = rng(cfg, 0, rep)
+    n, D = cfg.n_q, cfg.D
+
+    def draw(*shape):
+        return _store(r0.standard_normal(shape, dtype=np.float32), cfg.dtype)
+
+    out = {
+        "q": draw(B, cfg.Hq, n, D),
+        "k_new": draw(B, cfg.Hkv, n, D),
+        "v_new": draw(B, cfg.Hkv, n, D),
+        "k_cache": draw(B, cfg.Hkv, max_T, D),
+        "v_cache": draw(B, cfg.Hkv, max_T, D),
+        "lens": lengths(cfg, rep, B),
+    }
+    assert int(out["lens"].max()) + n <= max_T
+    return out
+
+
+# ----------------------------------------------------------------------------
+# device generators (torch); used for config 5 and for the benchmark
+# ----------------------------------------------------------------------------
+
+
+def _torch_gen(cfg: Config, stream: int, rep: int, device):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(1_000_003 * cfg.cid + 10_007 * stream + rep)
+    return g
+
+
+def attention_inputs_device(cfg: Config, device, rep: int = 0, B=None):
+    """Device tensors for verify attention; lens from the host stream 3."""
+    import torch
+
+    B = cfg.B if B is None else int(B)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    g = _torch_gen(cfg, 0, rep, device)
+    n, D = cfg.n_q, cfg.D
+
+    def draw(*shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dt)
+
+    k_cache = torch.empty((B, cfg.Hkv, cfg.max_T, D), device=device, dtype=dt)
+    v_cache = torch.empty_like(k_cache)
+    for b in range(B):  # slab by sequence to bound the fp32 temporary
+        k_cache[b] = draw(cfg.Hkv, cfg.max_T, D)
+        v_cache[b] = draw(cfg.Hkv, cfg.max_T, D)
+    lens = torch.from_numpy(lengths(cfg, rep, B)).to(device)
+    return {
+        "q": draw(B, cfg.Hq, n, D),
+        "k_new": draw(B, cfg.Hkv, n, D),
+        "v_new": draw(B, cfg.Hkv, n, D),
+        "k_cache": k_cache,
+        "v_cache": v_cache,
+        "lens": lens,
+    }
+
+
+def sampler_inputs_device(cfg: Config, device, temperature=None, rep: int = 0, B=None):
+    """Device tensors for the rejection sampler (same recipe as the host one)."""
+    import torch
+
+    T = cfg.temperatures[0] if temperature is None else float(temperature)
+    B = cfg.B if B is None else int(B)
+    gm, V = cfg.gamma, cfg.V
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    g0 = _torch_gen(cfg, 0, rep, device)
+    g1 = _torch_gen(cfg, 1, rep, device)
+    g2 = _torch_gen(cfg, 2, rep, device)
+    zt = torch.empty((B, gm + 1, V), device=device, dtype=dt)
+    zd = torch.empty((B, gm, V), device=device, dtype=dt)
+    x = torch.empty((B, gm), device=device, dtype=torch.int32)
+    for b in range(B):
+        t32 = cfg.t_std * torch.randn((gm + 1, V), generator=g0, device=device)
+        d32 = cfg.mix * t32[:gm] + cfg.noise_std * torch.randn((gm, V), generator=g0, device=device)
+        zt[b] = t32.to(dt)
+        zd[b] = d32.to(dt)
+        u = torch.rand((gm, V), generator=g1, device=device, dtype=torch.float64)
+        gum = -torch.log(-torch.log(u))
+        x[b] = torch.argmax(zd[b].double() / T + gum, dim=-1).to(torch.int32)
+    uni = torch.rand((B, gm + 1), generator=g2, device=device, dtype=torch.float64)
+    return {
+        "target_logits": zt,
+        "draft_logits": zd,
+        "draft_tokens": x,
+        "uniforms": uni,
+        "temperature": T,
+    }
