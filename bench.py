@@ -1,0 +1,257 @@
+"""Benchmark of the verification step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c4|c3]
+                    [--temperature T] [--no-cpu-baseline]
+
+A step is one pass of the whole hot path on one batch: verify attention with
+KV append, rejection sampling, length reset (three C-ABI calls on one
+stream).  Inputs are synthetic, seeded and already resident in HBM.  The
+default workload is the long-context large-batch configuration (B=256,
+gamma=8, GQA 64/8, head dim 128, bf16 cache with lengths uniform in
+[8192, 32768], vocabulary 128,256).  Lengths are restored before each step
+(a 1 KB device copy) so every step verifies the same batch.
+
+Prints one JSON line: verified draft positions per second for the whole step,
+per-call durations measured with HIP events on the launch stream, the
+achieved fraction of the HBM roofline for each part, and the CPU oracle timed
+on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense
+MFMA_F32_PEAK_TFLOPS = 157.3
+METRIC = "verified draft positions/sec + % of MI355X HBM peak (sampler, verify attn)"
+
+WORKLOADS = {"c3": 3, "c4": 4, "c5": 5}
+
+
+def algorithmic(cfg, lens, B):
+    """Bytes and flops the step must move / compute (every input read once)."""
+    e = cfg.elem_bytes
+    n, D = cfg.n_q, cfg.D
+    L = lens.astype(np.int64)
+    kv_read = int(np.sum(2 * cfg.Hkv * D * e * (L + n)))
+    append = int(B * 2 * cfg.Hkv * n * D * e)
+    q_o = int(B * 2 * cfg.Hq * n * D * e)
+    att_bytes = kv_read + append + q_o
+    att_flops = int(4 * cfg.Hq * D * np.sum(n * L + n * (n + 1) // 2))
+    g = cfg.gamma
+    smp_bytes = int(B * (2 * g + 1) * cfg.V * e + B * (g * 4 + (g + 1) * 8 + 4 + (g + 1) * 4 + 8 * g))
+    return att_bytes, att_flops, smp_bytes
+
+
+def make_inputs(cfg, device, temperature, rep):
+    import torch
+
+    import workloads as W
+
+    if cfg.cid == 5:
+        att = W.attention_inputs_device(cfg, device, rep=rep)
+        smp = W.sampler_inputs_device(cfg, device, temperature=temperature, rep=rep)
+    else:
+        from workloads.device import to_dev
+
+        a = W.attention_inputs(cfg, rep=rep)
+        s = W.sampler_inputs(cfg, temperature=temperature, rep=rep)
+        att = {k: to_dev(v, device=device) for k, v in a.items()}
+        smp = {k: (to_dev(v, device=device) if k != "temperature" else v) for k, v in s.items()}
+    att["lens_base"] = att["lens"].clone()
+    att["out"] = torch.empty_like(att["q"])
+    smp["n"] = torch.empty(cfg.B, dtype=torch.int32, device=device)
+    smp["tok"] = torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=device)
+    torch.cuda.synchronize()
+    return att, smp
+
+
+def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
+    """The oracle as it stands, on whole sequences of the workload, one BLAS thread."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as A
+    from oracle import sampler as S
+    from workloads.device import to_host
+
+    B = att["q"].shape[0]
+    order = np.random.default_rng(0).permutation(B)
+    done, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b in order:
+            sl = slice(int(b), int(b) + 1)
+            L = int(att["lens_base"][sl].item())
+            host = {k: to_host(att[k][sl]) for k in ("q", "k_new", "v_new")}
+            host["k_cache"] = to_host(att["k_cache"][sl, :, :L])
+            host["v_cache"] = to_host(att["v_cache"][sl, :, :L])
+            s0 = time.perf_counter()
+            A.verify_attention(host["q"], host["k_new"], host["v_new"], host["k_cache"], host["v_cache"],
+                               np.array([L]))
+            t_att = time.perf_counter() - s0
+            sh = {k: to_host(smp[k][sl]) for k in ("target_logits", "draft_logits", "draft_tokens", "uniforms")}
+            s1 = time.perf_counter()
+            S.verify_batch(sh["target_logits"], sh["draft_logits"], sh["draft_tokens"], sh["uniforms"], temperature)
+            t_smp = time.perf_counter() - s1
+            done += 1
+            if done == 1:
+                elapsed = t_att + t_smp
+            else:
+                elapsed += t_att + t_smp
+            if time.perf_counter() - t0 > budget_s:
+                break
+    pos = done * cfg.gamma
+    return {
+        "value": pos / elapsed,
+        "unit": "positions/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done} whole sequences of the workload (attention over their full cache + sampler over all "
+        f"{2 * cfg.gamma + 1} vocab rows), numpy fp64, one BLAS thread; host copies excluded from the time",
+        "seconds": elapsed,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    ap.add_argument("--temperature", type=float, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the verification step has no multi-GPU "
+              "path in this build; see DESIGN.md for how it would shard.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_decoding_verification_spec_amd as sv
+    import workloads as W
+
+    if not os.path.exists(sv.LIB_PATH):
+        import __graft_entry__
+
+        __graft_entry__.build()
+    sv.load()
+    dev = torch.device("cuda:0")
+    cfg = W.get(WORKLOADS[args.workload])
+    T = cfg.temperatures[-1] if args.temperature is None else args.temperature
+    print(f"[bench] workload config{cfg.cid} ({cfg.name}) T={T}: generating inputs", file=sys.stderr, flush=True)
+
+    # Enough input sets that the step's bytes exceed the 256 MB last-level cache.
+    att_bytes_est = cfg.B * 2 * cfg.Hkv * cfg.D * cfg.elem_bytes * (sum(cfg.L) / 2 + cfg.n_q)
+    smp_bytes_est = cfg.B * (2 * cfg.gamma + 1) * cfg.V * cfg.elem_bytes
+    nsets = max(1, min(4, math.ceil(768e6 / (att_bytes_est + smp_bytes_est))))
+    sets = [make_inputs(cfg, dev, T, rep) for rep in range(nsets)]
+    hint = cfg.L[1]
+    B = cfg.B
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+
+    def step(k, events=None):
+        att, smp = sets[k % nsets]
+        att["lens"].copy_(att["lens_base"])
+        if events:
+            events[0].record(stream)
+        sv.spec_verify_attention(att["q"], att["k_new"], att["v_new"], att["k_cache"], att["v_cache"], att["lens"],
+                                 hint, out=att["out"])
+        if events:
+            events[1].record(stream)
+        n, tok, _, _ = sv.spec_reject_sample(smp["target_logits"], smp["draft_logits"], smp["draft_tokens"],
+                                             smp["uniforms"], T, n_accepted=smp["n"], out_tokens=smp["tok"])
+        if events:
+            events[2].record(stream)
+        sv.spec_kv_truncate(att["lens"], n, cfg.n_q)
+        if events:
+            events[3].record(stream)
+        return n
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(k, ev[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    att_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    smp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    trn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+
+    lens = sets[0][0]["lens_base"].cpu().numpy()
+    att_b, att_f, smp_b = algorithmic(cfg, lens, B)
+    att_gbs = att_b / (att_ms * 1e-3) / 1e9
+    smp_gbs = smp_b / (smp_ms * 1e-3) / 1e9
+    positions = B * cfg.gamma
+    n_last = sets[(args.steps - 1) % nsets][1]["n"].cpu().numpy()
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+
+    res = {
+        "metric": METRIC,
+        "value": positions / (ms_step * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"config{cfg.cid} {cfg.name}: B={B} gamma={cfg.gamma} GQA {cfg.Hq}/{cfg.Hkv} D={cfg.D} "
+            f"{cfg.dtype} KV, lengths U[{cfg.L[0]},{cfg.L[1]}], vocab {cfg.V}, T={T}",
+            "batch": B,
+            "gamma": cfg.gamma,
+            "temperature": T,
+            "input_sets": nsets,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": att_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": att_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "kernel": "spec_verify_attention (split + combine kernels)",
+            "algorithmic_bytes": att_b,
+            "avg_ms": att_ms,
+        },
+        "parts": {
+            "attention": {"ms": att_ms, "bytes": att_b, "GB/s": att_gbs, "hbm_frac": att_gbs / HBM_PEAK_GBS,
+                          "positions/s": positions / (att_ms * 1e-3), "flops": att_f,
+                          "mfma_frac": att_f / (att_ms * 1e-3) / (mfma_peak * 1e12)},
+            "sampler": {"ms": smp_ms, "bytes": smp_b, "GB/s": smp_gbs, "hbm_frac": smp_gbs / HBM_PEAK_GBS,
+                        "positions/s": positions / (smp_ms * 1e-3)},
+            "truncate": {"ms": trn_ms},
+            "mean_accepted": float(n_last.mean()),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        att0, smp0 = sets[0]
+        res["cpu_baseline"] = cpu_baseline(cfg, att0, smp0, T)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

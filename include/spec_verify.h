@@ -1,0 +1,178 @@
+/* spec_verify.h -- C ABI of the speculative-decoding verification step on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Source pages (cited by title and section):
+ *   [P1] "投機的デコーディングとドラフトモデル" (tech-tldr.com)
+ *   [P2] "LLM推論の高速化｜KVキャッシュと投機的デコーディングを自作で実測" (r-jc.jp)
+ *   [P3] "Speculative Decoding（投機的デコーディング）とは？仕組みと速くなる条件、
+ *         LM Studio・llama.cpp・vLLMでの設定" (issoh.co.jp)
+ *
+ * One verification round of speculative decoding for a batch of B sequences:
+ *   1. spec_verify_attention: the target's single call over [last committed
+ *      token] + gamma drafts appends those n_q = gamma+1 tokens' K/V to each
+ *      sequence's cache and runs causal multi-query attention of the n_q rows
+ *      against it ([P2] numpyで小さなTransformerを自作する; 投機的デコーディングとは).
+ *   2. spec_reject_sample: modified rejection sampling over the vocabulary
+ *      ([P1] 受理判定の数理：修正版棄却サンプリング; [P2] 投機的デコーディングとは;
+ *      [P3] 受理・棄却の規則と出力分布が変わらない理由).
+ *   3. spec_kv_truncate: the length reset that drops the rejected drafts' K/V
+ *      ([P2] numpyで小さなTransformerを自作する, KVCache.truncate).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must point to device memory (e.g. the
+ *     data of PyTorch CUDA/HIP tensors); the caller owns all of them.
+ *   - Arrays are dense, row-major (C order), in the layouts stated below.
+ *   - All work is enqueued on `stream` (0 = the null stream); no call
+ *     synchronises, allocates device memory or keeps state across calls other
+ *     than what lives in the caller's workspace.
+ *   - Host-side argument checks run before any launch; a failed check returns
+ *     an error code and launches nothing.  Nothing throws across the ABI.
+ *   - Outputs must not alias inputs.  Calls that share a workspace must not
+ *     run concurrently.
+ *   - A workspace must be zero-filled before its first use; every call that
+ *     returns SPEC_OK and runs to completion leaves it zero-filled again (its
+ *     only persistent contents are completion counters).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_ERR_ARG = 1,         /* bad pointer, size, alignment or workspace size   */
+  SPEC_ERR_OVERFLOW = 2,    /* cache too small: max_len_hint + n_q > max_T      */
+  SPEC_ERR_UNSUPPORTED = 3, /* valid request outside what this build supports   */
+  SPEC_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch          */
+} spec_status_t;
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+
+/* Library version, e.g. "specverify 0.1.0 gfx950". Static string. */
+const char* spec_version(void);
+
+/* Human-readable name of a status code. Static string. */
+const char* spec_status_string(spec_status_t s);
+
+/* ------------------------------------------------------------------------- */
+/* Verify attention                                                           */
+/* ------------------------------------------------------------------------- */
+
+/* Workspace bytes spec_verify_attention needs for these sizes.  A workspace
+ * sized for max_len_hint h serves every call with the same other sizes and a
+ * hint <= h.  Returns 0 for invalid sizes. */
+size_t spec_verify_attention_workspace_size(int B, int Hq, int Hkv, int n_q, int D, int max_len_hint,
+                                            spec_dtype_t dtype);
+
+/* Causal multi-query verify attention with KV append.
+ *
+ * Defined by [P2] section numpyで小さなTransformerを自作する (the forward_cached
+ * listing): with p0 = the cache length before the call, the n new tokens' K/V
+ * go to cache rows [p0, p0+n); the i-th new query attends to rows [0, p0+i];
+ * scores are scaled by 1/sqrt(D) and soft-maxed.  Grouped-query sharing
+ * ([P2] section GQA・MQAでKVキャッシュを減らす): query head h reads KV head
+ * h / (Hq / Hkv) (contiguous groups).
+ *
+ *   q        device, [B][Hq][n_q][D]        dtype       queries of the n_q rows
+ *   k_new    device, [B][Hkv][n_q][D]       dtype       K of [last committed] + drafts
+ *   v_new    device, [B][Hkv][n_q][D]       dtype
+ *   k_cache  device, [B][Hkv][max_T][D]     dtype, in/out
+ *   v_cache  device, [B][Hkv][max_T][D]     dtype, in/out
+ *            rows [cache_len[b], cache_len[b] + n_q) are overwritten with
+ *            k_new / v_new; no other row is written; rows >= cache_len[b] are
+ *            never read (their contents may be anything, NaN included).
+ *   cache_len device, [B] int32, committed length L_b before the call (read only;
+ *            spec_kv_truncate commits the new length).
+ *   out      device, [B][Hq][n_q][D]        dtype       attention output
+ *   scale    score scale; the pages' value is 1/sqrt(D).
+ *   max_len_hint  host upper bound on max_b cache_len[b]; it sizes the launch.
+ *   workspace device, >= spec_verify_attention_workspace_size(...) bytes.
+ * Arithmetic: scores, softmax and accumulation in fp32; bf16 inputs are
+ * consumed exactly and the output is rounded to nearest-even.
+ * Supported: dtype SPEC_BF16 with D in {64, 128}; SPEC_F32 with D in {24, 32,
+ * 64, 128}; 1 <= n_q <= 16; Hq % Hkv == 0; Hq/Hkv * n_q <= 256.
+ * Errors: SPEC_ERR_ARG for null pointers, non-positive sizes, Hq % Hkv != 0,
+ * pointers not 16-byte aligned, or a small workspace; SPEC_ERR_OVERFLOW if
+ * max_len_hint + n_q > max_T; SPEC_ERR_UNSUPPORTED outside the supported set.
+ * A sequence whose device-side cache_len[b] is negative or exceeds
+ * max_len_hint is not processed: nothing is written to its cache rows and its
+ * output rows are set to NaN. */
+spec_status_t spec_verify_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                    void* v_cache, const int32_t* cache_len, void* out, int B, int Hq, int Hkv,
+                                    int n_q, int D, int max_T, int max_len_hint, float scale, spec_dtype_t dtype,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* Modified rejection sampler                                                 */
+/* ------------------------------------------------------------------------- */
+
+/* Workspace bytes spec_reject_sample needs.  Returns 0 for invalid sizes. */
+size_t spec_reject_sample_workspace_size(int B, int gamma, int V, spec_dtype_t dtype);
+
+/* Modified rejection sampling for one round.
+ *
+ * Defined by [P1] section 受理判定の数理：修正版棄却サンプリング, [P2] section
+ * 投機的デコーディングとは (the verify listing) and [P3] section
+ * 受理・棄却の規則と出力分布が変わらない理由 (the five steps):
+ *   p_i = softmax(target_logits[b][i] / T), i = 0..gamma
+ *   q_i = softmax(draft_logits[b][i] / T),  i = 0..gamma-1
+ *   position i is accepted iff uniforms[b][i] < min(1, p_i(x_i) / q_i(x_i));
+ *   n = the number of leading accepted positions (the scan stops at the first
+ *   rejection);
+ *   if n < gamma the final token is drawn from normalize(max(0, p_n - q_n))
+ *   (if that mass is exactly zero, from p_n); if n == gamma it is the bonus
+ *   token drawn from p_gamma; the draw is inverse-CDF with uniforms[b][gamma]:
+ *   the smallest j with C_j / C_{V-1} > u, C the prefix sum of the weights.
+ *
+ *   target_logits device, [B][gamma+1][V] dtype
+ *   draft_logits  device, [B][gamma][V]   dtype
+ *   draft_tokens  device, [B][gamma] int32, x_i, each in [0, V)
+ *   uniforms      device, [B][gamma+1] double in [0, 1): [i < gamma] the accept
+ *                 test at i, [gamma] the final draw (residual or bonus)
+ *   temperature   T > 0 applied to both target and draft logits
+ *   n_accepted    device out, [B] int32 in 0..gamma (-1: a draft token of this
+ *                 sequence was outside [0, V); its out_tokens are all -1)
+ *   out_tokens    device out, [B][gamma+1] int32: x_0..x_{n-1}, the final token,
+ *                 then -1
+ *   p_draft, q_draft  device out or NULL, [B][gamma] float: p_i(x_i), q_i(x_i)
+ *   workspace     device, >= spec_reject_sample_workspace_size(...) bytes
+ * Arithmetic: logits are read exactly; per-element exponentials and the
+ * residual weights in fp32; row sums and all prefix sums in fp64; the accept
+ * comparison in fp64.  Distributions are never assumed to sum to 1.
+ * Errors: SPEC_ERR_ARG for null required pointers, B < 1, gamma < 1,
+ * gamma > 31, V < 1, T <= 0 or not finite, or a small workspace;
+ * SPEC_ERR_UNSUPPORTED for T == 0 (greedy verification is not implemented). */
+spec_status_t spec_reject_sample(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                                 const double* uniforms, int B, int gamma, int V, float temperature,
+                                 spec_dtype_t dtype, int32_t* n_accepted, int32_t* out_tokens, float* p_draft,
+                                 float* q_draft, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------- */
+/* KV length reset                                                            */
+/* ------------------------------------------------------------------------- */
+
+/* cache_len[b] <- cache_len[b] + 1 + n_accepted[b].
+ *
+ * Defined by [P2] section 投機的デコーディングとは: after the round the target
+ * cache is cut back to base + 1 + n_accepted -- the last committed token and
+ * the accepted drafts keep their K/V, the rejected drafts' rows become dead
+ * (they are simply past the length).  The final (corrected or bonus) token has
+ * no K/V yet; it is the first input of the next round.
+ *   cache_len   device, [B] int32, in/out
+ *   n_accepted  device, [B] int32; values above n_q-1 are clamped to n_q-1;
+ *               negative values (a sampler error) leave cache_len[b] unchanged
+ * Errors: SPEC_ERR_ARG for null pointers, B < 1 or n_q < 1. */
+spec_status_t spec_kv_truncate(int32_t* cache_len, const int32_t* n_accepted, int B, int n_q, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

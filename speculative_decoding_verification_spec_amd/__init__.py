@@ -1,0 +1,27 @@
+"""Speculative-decoding verification step on AMD MI355X (gfx950).
+
+The step is three calls into the C-ABI library libspecverify.so, bound here
+with ctypes (see include/spec_verify.h for the contract of each):
+
+  spec_verify_attention  KV append + causal multi-query verify attention (GQA)
+  spec_reject_sample     modified rejection sampling over the vocabulary
+  spec_kv_truncate       length reset after the round
+
+PyTorch supplies device memory and streams; all arithmetic runs in the HIP
+kernels.  Importing this package does not load the library; the first call
+does, and raises if the library has not been built.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    SpecError,
+    Workspace,
+    load,
+    reject_sample_workspace_size,
+    spec_kv_truncate,
+    spec_reject_sample,
+    spec_verify_attention,
+    verify_attention_workspace_size,
+    version,
+)

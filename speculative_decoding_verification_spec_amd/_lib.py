@@ -1,0 +1,219 @@
+"""ctypes binding of libspecverify.so (the C ABI declared in include/spec_verify.h).
+
+Argument marshalling only: shapes and dtypes of PyTorch tensors are checked and
+turned into the plain pointers and sizes the C functions take; every step of
+the verification path runs in the library's HIP kernels.  PyTorch provides the
+device memory and the current stream.  There is no fallback: if the library is
+missing, or a call returns an error status, a Python exception is raised.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_OK, SPEC_ERR_ARG, SPEC_ERR_OVERFLOW, SPEC_ERR_UNSUPPORTED, SPEC_ERR_LAUNCH = range(5)
+SPEC_F32, SPEC_BF16 = 0, 1
+
+EXPORTED = (
+    "spec_version",
+    "spec_status_string",
+    "spec_verify_attention_workspace_size",
+    "spec_verify_attention",
+    "spec_reject_sample_workspace_size",
+    "spec_reject_sample",
+    "spec_kv_truncate",
+)
+
+
+class SpecError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} returned {msg} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load the library (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m speculative_decoding_verification_spec_amd.build` "
+            "(or __graft_entry__.build())"
+        )
+    L = ctypes.CDLL(path)
+    c_int, c_size, vp, c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+    L.spec_version.restype = ctypes.c_char_p
+    L.spec_version.argtypes = []
+    L.spec_status_string.restype = ctypes.c_char_p
+    L.spec_status_string.argtypes = [c_int]
+    L.spec_verify_attention_workspace_size.restype = c_size
+    L.spec_verify_attention_workspace_size.argtypes = [c_int] * 6 + [c_int]
+    L.spec_verify_attention.restype = c_int
+    L.spec_verify_attention.argtypes = [vp] * 7 + [c_int] * 7 + [c_float, c_int, vp, c_size, vp]
+    L.spec_reject_sample_workspace_size.restype = c_size
+    L.spec_reject_sample_workspace_size.argtypes = [c_int] * 4
+    L.spec_reject_sample.restype = c_int
+    L.spec_reject_sample.argtypes = [vp] * 4 + [c_int] * 3 + [c_float, c_int] + [vp] * 5 + [c_size, vp]
+    L.spec_kv_truncate.restype = c_int
+    L.spec_kv_truncate.argtypes = [vp, vp, c_int, c_int, vp]
+    _lib = L
+    return L
+
+
+def version():
+    return load().spec_version().decode()
+
+
+def _check(fn, status):
+    if status != SPEC_OK:
+        raise SpecError(fn, status, load().spec_status_string(status).decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+class Workspace:
+    """A zero-filled device buffer, grown on demand and reused across calls.
+
+    The kernels leave their completion counters at zero when a call finishes,
+    so a workspace stays valid for the next call on the same stream.
+    """
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes, device):
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = {}
+
+
+def _workspace(ws, key, nbytes, device):
+    if ws is None:
+        ws = _default_ws.setdefault((key, str(device)), Workspace())
+    return ws.get(nbytes, device)
+
+
+def verify_attention_workspace_size(B, Hq, Hkv, n_q, D, max_len_hint, dtype_code):
+    return load().spec_verify_attention_workspace_size(B, Hq, Hkv, n_q, D, max_len_hint, dtype_code)
+
+
+def spec_verify_attention(q, k_new, v_new, k_cache, v_cache, cache_len, max_len_hint, out=None, scale=None,
+                          workspace=None, stream=None):
+    """Verify attention with KV append; returns ``out`` [B, Hq, n_q, D]."""
+    L = load()
+    _need(q, "q")
+    B, Hq, n_q, D = q.shape
+    Hkv = k_new.shape[1]
+    max_T = k_cache.shape[2]
+    _need(k_new, "k_new", q.dtype, (B, Hkv, n_q, D))
+    _need(v_new, "v_new", q.dtype, (B, Hkv, n_q, D))
+    _need(k_cache, "k_cache", q.dtype, (B, Hkv, max_T, D))
+    _need(v_cache, "v_cache", q.dtype, (B, Hkv, max_T, D))
+    _need(cache_len, "cache_len", torch.int32, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, q.shape)
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = L.spec_verify_attention_workspace_size(B, Hq, Hkv, n_q, D, int(max_len_hint), dt)
+    if nbytes == 0:
+        raise SpecError("spec_verify_attention_workspace_size", SPEC_ERR_UNSUPPORTED, "no valid size")
+    ws = _workspace(workspace, "attn", nbytes, q.device)
+    st = L.spec_verify_attention(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(out),
+        B, Hq, Hkv, n_q, D, max_T, int(max_len_hint), scale, dt, _ptr(ws), ws.numel(), _stream(stream),
+    )
+    _check("spec_verify_attention", st)
+    return out
+
+
+def reject_sample_workspace_size(B, gamma, V, dtype_code):
+    return load().spec_reject_sample_workspace_size(B, gamma, V, dtype_code)
+
+
+def spec_reject_sample(target_logits, draft_logits, draft_tokens, uniforms, temperature, n_accepted=None,
+                       out_tokens=None, p_draft=None, q_draft=None, want_probs=False, workspace=None, stream=None):
+    """Modified rejection sampling; returns (n_accepted [B], out_tokens [B, gamma+1], p_draft, q_draft)."""
+    L = load()
+    _need(target_logits, "target_logits")
+    B, G1, V = target_logits.shape
+    G = G1 - 1
+    _need(draft_logits, "draft_logits", target_logits.dtype, (B, G, V))
+    _need(draft_tokens, "draft_tokens", torch.int32, (B, G))
+    _need(uniforms, "uniforms", torch.float64, (B, G + 1))
+    dev = target_logits.device
+    if n_accepted is None:
+        n_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    if want_probs and p_draft is None:
+        p_draft = torch.empty((B, G), dtype=torch.float32, device=dev)
+    if want_probs and q_draft is None:
+        q_draft = torch.empty((B, G), dtype=torch.float32, device=dev)
+    _need(n_accepted, "n_accepted", torch.int32, (B,))
+    _need(out_tokens, "out_tokens", torch.int32, (B, G + 1))
+    for t, name in ((p_draft, "p_draft"), (q_draft, "q_draft")):
+        if t is not None:
+            _need(t, name, torch.float32, (B, G))
+    dt = _dtype_code(target_logits)
+    nbytes = L.spec_reject_sample_workspace_size(B, G, V, dt)
+    if nbytes == 0:
+        raise SpecError("spec_reject_sample_workspace_size", SPEC_ERR_ARG, "no valid size")
+    ws = _workspace(workspace, "rs", nbytes, dev)
+    st = L.spec_reject_sample(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(uniforms), B, G, V, float(temperature),
+        dt, _ptr(n_accepted), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft), _ptr(ws), ws.numel(),
+        _stream(stream),
+    )
+    _check("spec_reject_sample", st)
+    return n_accepted, out_tokens, p_draft, q_draft
+
+
+def spec_kv_truncate(cache_len, n_accepted, n_q, stream=None):
+    """cache_len += 1 + n_accepted (in place)."""
+    L = load()
+    _need(cache_len, "cache_len", torch.int32)
+    B = cache_len.shape[0]
+    _need(n_accepted, "n_accepted", torch.int32, (B,))
+    _check("spec_kv_truncate", L.spec_kv_truncate(_ptr(cache_len), _ptr(n_accepted), B, int(n_q), _stream(stream)))
+    return cache_len

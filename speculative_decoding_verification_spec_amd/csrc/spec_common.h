@@ -1,0 +1,84 @@
+// Device helpers shared by the verification kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specv {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float neg_inf_f() { return -__builtin_huge_valf(); }
+__device__ __forceinline__ double neg_inf_d() { return -__builtin_huge_val(); }
+
+// 2^x on the hardware transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// bfloat16 bit pattern <-> fp32.  Widening is exact; narrowing rounds to
+// nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// ---- wave-wide reductions and scans (64 lanes, all active) ----------------
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order (Hillis-Steele).  The
+// association is fixed by the lane index, so equal inputs give equal outputs.
+__device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    double t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Release this wave's prior global writes, then count it in `*counter`.
+// Returns true in every lane of the one wave that arrives last (the count
+// reaches `total`); that wave also performs the acquire side.
+__device__ __forceinline__ bool wave_arrive_last(uint32_t* counter, uint32_t total, int lane) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0, kWave);
+  const bool last = (old == total - 1);
+  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return last;
+}
+
+}  // namespace specv

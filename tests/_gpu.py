@@ -1,0 +1,55 @@
+"""Helpers for GPU parity tests: host <-> device marshalling and the comparison rules.
+
+Rules (from the verification step's statement of parity):
+  * n_accepted and emitted tokens must be identical given the same uniforms,
+    except sequences with a decisive draw within 1e-6 of its threshold (the
+    accept test's min(1, p/q) or a CDF boundary of the drawn token, measured
+    on the oracle's values); those are counted and reported, not compared;
+  * p_i(x_i), q_i(x_i) within 1e-5 relative (fp32 outputs);
+  * attention within 1e-4 absolute (fp32) or 2e-2 absolute (bf16).
+"""
+
+import numpy as np
+import torch
+
+from oracle import bf16 as obf16
+
+BAND = 1e-6
+P_RTOL = 1e-5
+ATT_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+from workloads.device import to_dev, to_host  # noqa: E402,F401
+
+
+def as_f64(a):
+    return obf16.to_f64(a)
+
+
+def compare_sampler(orc, n_gpu, tok_gpu, p_gpu=None, q_gpu=None, seqs=None):
+    """Compare GPU sampler outputs with the oracle's (``oracle.sampler.verify_batch``).
+
+    Returns a dict of counts; asserts that no sequence outside the band differs
+    and that p/q agree within P_RTOL.
+    """
+    seqs = np.arange(len(n_gpu)) if seqs is None else np.asarray(seqs)
+    n_g = np.asarray(n_gpu)[seqs]
+    t_g = np.asarray(tok_gpu)[seqs]
+    band = orc["min_margin"] < BAND
+    same = (n_g == orc["n_accepted"]) & np.all(t_g == orc["out_tokens"], axis=1)
+    bad = ~same & ~band
+    stats = {
+        "sequences": int(len(seqs)),
+        "in_band": int(band.sum()),
+        "band_disagree": int((~same & band).sum()),
+        "mismatch_outside_band": int(bad.sum()),
+        "fallback": int(orc["fallback"].sum()),
+    }
+    assert not bad.any(), (stats, np.nonzero(bad)[0][:10], n_g[bad][:5], orc["n_accepted"][bad][:5])
+    for got, want, name in ((p_gpu, orc["p_x"], "p"), (q_gpu, orc["q_x"], "q")):
+        if got is None:
+            continue
+        g = np.asarray(got, np.float64)[seqs]
+        ok = np.isclose(g, want, rtol=P_RTOL, atol=1e-37) | (np.isnan(g) & np.isnan(want))
+        assert ok.all(), (name, np.nonzero(~ok)[:5], g[~ok][:5], want[~ok][:5])
+    return stats

@@ -1,0 +1,209 @@
+"""GPU parity of spec_reject_sample against the oracle, through the C ABI.
+
+Every case prints its name and shape before touching the GPU.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_verification_spec_amd as sv
+import workloads as W
+from oracle import formulas as F
+from oracle import sampler as S
+from tests import _gpu, _replay
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _run(inp, temperature=None, want_probs=True):
+    T = inp["temperature"] if temperature is None else temperature
+    dev = dict(
+        target_logits=_gpu.to_dev(inp["target_logits"]),
+        draft_logits=_gpu.to_dev(inp["draft_logits"]),
+        draft_tokens=_gpu.to_dev(inp["draft_tokens"]),
+        uniforms=_gpu.to_dev(inp["uniforms"]),
+    )
+    n, tok, p, q = sv.spec_reject_sample(**dev, temperature=T, want_probs=want_probs)
+    torch.cuda.synchronize()
+    return (
+        _gpu.to_host(n),
+        _gpu.to_host(tok),
+        None if p is None else _gpu.to_host(p),
+        None if q is None else _gpu.to_host(q),
+    )
+
+
+def _oracle(inp, temperature=None, seqs=None):
+    T = inp["temperature"] if temperature is None else temperature
+    return S.verify_batch(inp["target_logits"], inp["draft_logits"], inp["draft_tokens"], inp["uniforms"], T, seqs)
+
+
+def _case(name, **kw):
+    print(f"\n[case] {name} {kw}", flush=True)
+
+
+def test_page_toy_replay_on_gpu():
+    with open(os.path.join(GOLDEN, "p3_toy_v5.json")) as f:
+        g = json.load(f)
+    _case("p3-toy-replay", N=g["N"])
+    r = _replay.build(g["p"], g["q"], g["N"], seed=g["seed"])
+    N, V = g["N"], g["V"]
+    zt = np.broadcast_to(np.log(np.array(g["p"])).astype(np.float32), (N, 2, V)).copy()
+    zd = np.broadcast_to(np.log(np.array(g["q"])).astype(np.float32), (N, 1, V)).copy()
+    inp = {"target_logits": zt, "draft_logits": zd, "draft_tokens": r["x"][:, None].copy(),
+           "uniforms": r["u"], "temperature": 1.0}
+    n, tok, _, _ = _run(inp, want_probs=False)
+    freq = np.bincount(tok[:, 0], minlength=V) / N
+    assert list(np.round(freq, 3)) == g["printed_observed_freq_round3"]
+    assert round(float((n == 1).mean()), 3) == g["printed_accept_rate_round3"]
+    # trial by trial against the oracle's replay (fp32 logits here vs fp64 in
+    # the replay: compare only trials far from any threshold)
+    orc = _oracle(inp)
+    st = _gpu.compare_sampler(orc, n, tok)
+    print("stats", st)
+
+
+@pytest.mark.parametrize("cid", [1, 2])
+def test_small_configs_full(cid):
+    cfg = W.get(cid)
+    _case(f"config{cid}", B=cfg.B, gamma=cfg.gamma, V=cfg.V)
+    inp = W.sampler_inputs(cfg)
+    n, tok, p, q = _run(inp)
+    st = _gpu.compare_sampler(_oracle(inp), n, tok, p, q)
+    print("stats", st)
+
+
+def test_config2_thousand_batches_statistics():
+    cfg = W.get(2)
+    B = cfg.B * 1000
+    _case("config2x1000", B=B)
+    inp = W.sampler_inputs(cfg, B=B, rep=1)
+    n, tok, p, q = _run(inp)
+    orc = _oracle(inp)
+    st = _gpu.compare_sampler(orc, n, tok, p, q)
+    print("stats", st)
+    # Per tested position, the acceptance probability is sum_x min(p_i, q_i):
+    # compare the empirical rate with the mean of that closed form over the
+    # tested positions (4 sigma).
+    zt = inp["target_logits"].astype(np.float64)
+    zd = inp["draft_logits"].astype(np.float64)
+    tested, accepted, alpha = 0, 0, []
+    for b in range(B):
+        for i in range(min(int(n[b]) + 1, cfg.gamma)):
+            tested += 1
+            accepted += int(i < n[b])
+            alpha.append(F.acceptance_alpha(S.softmax_t(zt[b, i], 1.0), S.softmax_t(zd[b, i], 1.0)))
+    a = np.mean(alpha)
+    sigma = np.sqrt(np.mean(np.array(alpha) * (1 - np.array(alpha))) / tested)
+    print("accept", accepted / tested, "alpha", a, "sigma", sigma)
+    assert abs(accepted / tested - a) < 4 * sigma
+
+
+def test_config4_full():
+    cfg = W.get(4)
+    _case("config4", B=cfg.B, V=cfg.V)
+    inp = W.sampler_inputs(cfg)
+    n, tok, p, q = _run(inp)
+    st = _gpu.compare_sampler(_oracle(inp), n, tok, p, q)
+    print("stats", st)
+
+
+@pytest.mark.parametrize("T", [0.7, 1.0])
+def test_config5_full_size_sampled(T):
+    cfg = W.get(5)
+    _case("config5", B=cfg.B, V=cfg.V, T=T)
+    d = W.sampler_inputs_device(cfg, "cuda", temperature=T)
+    n, tok, p, q = sv.spec_reject_sample(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                         d["uniforms"], T, want_probs=True)
+    torch.cuda.synchronize()
+    seqs = np.random.default_rng(5).choice(cfg.B, size=24, replace=False)
+    host = {
+        "target_logits": _gpu.to_host(d["target_logits"][seqs]),
+        "draft_logits": _gpu.to_host(d["draft_logits"][seqs]),
+        "draft_tokens": _gpu.to_host(d["draft_tokens"][seqs]),
+        "uniforms": _gpu.to_host(d["uniforms"][seqs]),
+        "temperature": T,
+    }
+    orc = _oracle(host)
+    st = _gpu.compare_sampler(orc, _gpu.to_host(n)[seqs], _gpu.to_host(tok)[seqs],
+                              _gpu.to_host(p)[seqs], _gpu.to_host(q)[seqs])
+    print("stats", st)
+    # every sequence: the emitted prefix is the draft prefix, tokens are in range
+    n_all, tok_all, x_all = _gpu.to_host(n), _gpu.to_host(tok), _gpu.to_host(d["draft_tokens"])
+    for b in range(cfg.B):
+        k = int(n_all[b])
+        assert 0 <= k <= cfg.gamma
+        assert np.array_equal(tok_all[b, :k], x_all[b, :k])
+        assert 0 <= tok_all[b, k] < cfg.V and np.all(tok_all[b, k + 1:] == -1)
+
+
+@pytest.mark.parametrize(
+    "V,gamma,dtype,B",
+    [(1, 1, "f32", 5), (7, 3, "f32", 33), (1003, 5, "bf16", 17), (4099, 2, "f32", 9),
+     (40000, 31, "bf16", 3), (96, 4, "bf16", 70)],
+)
+def test_ragged_shapes(V, gamma, dtype, B):
+    _case("ragged", V=V, gamma=gamma, dtype=dtype, B=B)
+    cfg = W.Config(99, "ragged", B=B, gamma=gamma, V=V, dtype=dtype, t_std=2.5, mix=0.9, noise_std=1.0)
+    inp = W.sampler_inputs(cfg, temperature=0.8)
+    n, tok, p, q = _run(inp)
+    st = _gpu.compare_sampler(_oracle(inp), n, tok, p, q)
+    print("stats", st)
+
+
+def test_edge_conventions():
+    _case("edges")
+    V = 4
+    zt = np.zeros((6, 2, V), np.float32)  # p uniform: 1/4 each
+    zd = np.zeros((6, 1, V), np.float32)
+    zd[:, 0, 2:] = -np.inf  # q = [1/2, 1/2, 0, 0]
+    x = np.zeros((6, 1), np.int32)
+    u = np.zeros((6, 2))
+    # 0: u exactly at the threshold 1/2 -> reject; 1: just below -> accept
+    u[0, 0] = 0.5
+    u[1, 0] = np.nextafter(0.5, 0)
+    # 2: draft token with q = 0 < p -> accept for any u
+    x[2, 0] = 3
+    u[2, 0] = 0.999
+    # 3: p = q = 0 at the draft token -> reject, residual is zero -> draw from p
+    zt[3, 0, 3] = -np.inf
+    zd[3, 0, :] = 0.0
+    zd[3, 0, 3] = -np.inf
+    x[3, 0] = 3
+    u[3] = (0.0, 0.6)
+    # 4: zero-mass tokens at the front, u = 0 for the draw
+    zt[4, :, :2] = -np.inf
+    zd[4, 0, :] = [0, 0, 0, -np.inf]
+    x[4, 0] = 0
+    u[4] = (0.9, 0.0)
+    # 5: invalid draft token
+    x[5, 0] = V
+    inp = {"target_logits": zt, "draft_logits": zd, "draft_tokens": x, "uniforms": u, "temperature": 1.0}
+    n, tok, p, q = _run(inp)
+    assert n[0] == 0 and n[1] == 1 and n[2] == 1 and n[3] == 0
+    assert n[5] == -1 and np.all(tok[5] == -1)
+    assert tok[3, 0] == 1  # fallback to p = [1/3, 1/3, 1/3, 0]; u = 0.6 falls in token 1
+    assert tok[4, 0] == 2  # residual [0, 0, 1/6, 1/2]; u = 0 skips the zero-mass tokens
+    orc = _oracle({**inp, "draft_tokens": np.where(x >= V, 0, x)}, seqs=range(5))
+    assert np.array_equal(n[:5], orc["n_accepted"])
+    assert np.array_equal(tok[:5], orc["out_tokens"])
+
+
+def test_status_codes():
+    _case("status")
+    dev = "cuda"
+    zt = torch.zeros((2, 3, 8), device=dev)
+    zd = torch.zeros((2, 2, 8), device=dev)
+    x = torch.zeros((2, 2), dtype=torch.int32, device=dev)
+    u = torch.zeros((2, 3), dtype=torch.float64, device=dev)
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_reject_sample(zt, zd, x, u, 0.0)
+    assert e.value.status == 3  # greedy is not implemented
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_reject_sample(zt, zd, x, u, -1.0)
+    assert e.value.status == 1

@@ -1,0 +1,88 @@
+"""End-to-end verification rounds on the GPU through the C ABI.
+
+A round is spec_verify_attention -> spec_reject_sample -> spec_kv_truncate on
+one stream.  Two rounds are chained: after the first, every cache row at or
+past the new length is NaN-poisoned; the second round must still be finite and
+equal to the oracle (the rows of rejected drafts are dead, [P2] section
+投機的デコーディングとは).  A round that forgets the truncate must differ.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_verification_spec_amd as sv
+import workloads as W
+from oracle import attention as A
+from oracle import sampler as S
+from oracle import truncate as Tr
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def test_truncate_kernel():
+    print("\n[case] truncate", flush=True)
+    lens = np.array([0, 5, 384, 32768, 7, 9], np.int32)
+    n = np.array([0, 4, 2, 8, -1, 12], np.int32)  # -1: sampler error; 12 > n_q-1
+    dl = _gpu.to_dev(lens)
+    sv.spec_kv_truncate(dl, _gpu.to_dev(n), 9)
+    torch.cuda.synchronize()
+    assert list(_gpu.to_host(dl)) == [1, 10, 387, 32777, 7, 18]
+    ok = n[:4]
+    assert np.array_equal(_gpu.to_host(dl)[:4], Tr.truncate(lens[:4], ok))
+
+
+def _round(dev, samp, hint, n_q):
+    out = sv.spec_verify_attention(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+                                   dev["lens"], hint)
+    n, tok, _, _ = sv.spec_reject_sample(samp["target_logits"], samp["draft_logits"], samp["draft_tokens"],
+                                         samp["uniforms"], samp["temperature"])
+    sv.spec_kv_truncate(dev["lens"], n, n_q)
+    torch.cuda.synchronize()
+    return out, n, tok
+
+
+@pytest.mark.parametrize("cid", [3, 4])
+def test_two_rounds_with_poisoned_tail(cid):
+    cfg = W.get(cid)
+    B = min(cfg.B, 8)
+    print(f"\n[case] two-rounds config{cid} B={B}", flush=True)
+    att1 = W.attention_inputs(cfg, B=B, rep=0)
+    samp1 = W.sampler_inputs(cfg, B=B, rep=0)
+    dev = {k: _gpu.to_dev(v) for k, v in att1.items()}
+    sdev = {k: (_gpu.to_dev(v) if k != "temperature" else v) for k, v in samp1.items()}
+    hint = cfg.L[1] + cfg.n_q  # room for one more round
+    out1, n1, tok1 = _round(dev, sdev, hint, cfg.n_q)
+
+    # round 1 against the oracle
+    want1 = A.verify_attention(att1["q"], att1["k_new"], att1["v_new"], att1["k_cache"], att1["v_cache"], att1["lens"])
+    assert np.max(np.abs(_gpu.as_f64(_gpu.to_host(out1)) - want1)) < _gpu.ATT_TOL[cfg.dtype]
+    orc = S.verify_batch(samp1["target_logits"], samp1["draft_logits"], samp1["draft_tokens"], samp1["uniforms"],
+                         samp1["temperature"])
+    _gpu.compare_sampler(orc, _gpu.to_host(n1), _gpu.to_host(tok1))
+    new_len = _gpu.to_host(dev["lens"])
+    assert np.array_equal(new_len, Tr.truncate(att1["lens"], _gpu.to_host(n1)))
+
+    # poison every row at or past the new length, then run round 2
+    for b, L in enumerate(new_len):
+        dev["k_cache"][b, :, L:] = float("nan")
+        dev["v_cache"][b, :, L:] = float("nan")
+    att2 = W.attention_inputs(cfg, B=B, rep=1)
+    for k in ("q", "k_new", "v_new"):
+        dev[k] = _gpu.to_dev(att2[k])
+    kc_host, vc_host = A.kv_append(att1["k_cache"], att1["v_cache"], att1["k_new"], att1["v_new"], att1["lens"])
+    out2 = sv.spec_verify_attention(dev["q"], dev["k_new"], dev["v_new"], dev["k_cache"], dev["v_cache"],
+                                    dev["lens"], hint)
+    torch.cuda.synchronize()
+    got2 = _gpu.as_f64(_gpu.to_host(out2))
+    assert np.all(np.isfinite(got2))
+    want2 = A.verify_attention(att2["q"], att2["k_new"], att2["v_new"], kc_host, vc_host, new_len)
+    assert np.max(np.abs(got2 - want2)) < _gpu.ATT_TOL[cfg.dtype]
+    # forgetting the truncate (attending over the old length + n_q) gives a
+    # different answer wherever a draft was rejected
+    stale = att1["lens"] + cfg.n_q
+    wrong = A.verify_attention(att2["q"], att2["k_new"], att2["v_new"], kc_host, vc_host, stale)
+    rejected = _gpu.to_host(n1) < cfg.gamma
+    if rejected.any():
+        assert np.max(np.abs(wrong[rejected] - want2[rejected])) > 10 * _gpu.ATT_TOL[cfg.dtype]
