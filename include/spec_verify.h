@@ -29,9 +29,9 @@
  *     an error code and launches nothing.  Nothing throws across the ABI.
  *   - Outputs must not alias inputs.  Calls that share a workspace must not
  *     run concurrently.
- *   - A workspace must be zero-filled before its first use; every call that
- *     returns SPEC_OK and runs to completion leaves it zero-filled again (its
- *     only persistent contents are completion counters).
+ *   - Workspaces need no initialisation: every call writes each workspace
+ *     word before reading it, so one buffer may serve calls of any sizes (up
+ *     to its capacity) one after another on a stream.
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H

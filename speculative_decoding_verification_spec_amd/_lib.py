@@ -107,10 +107,11 @@ def _need(t, name, dtype=None, shape=None):
 
 
 class Workspace:
-    """A zero-filled device buffer, grown on demand and reused across calls.
+    """A device buffer grown on demand and reused across calls of any sizes.
 
-    The kernels leave their completion counters at zero when a call finishes,
-    so a workspace stays valid for the next call on the same stream.
+    The library writes every workspace word before reading it, so the buffer
+    needs no initialisation between calls.  Calls sharing a workspace must be
+    ordered (one stream).
     """
 
     def __init__(self, device=None):
@@ -120,7 +121,7 @@ class Workspace:
     def get(self, nbytes, device):
         nbytes = max(int(nbytes), 256)
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
-            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         return self.buf
 
 

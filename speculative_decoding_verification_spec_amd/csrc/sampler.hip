@@ -12,18 +12,20 @@
 // judging positions past the first rejection changes nothing but wasted work,
 // and the data-parallel pass reads every logit exactly once.
 //
-// Two kernels, one wave = one unit of work:
+// Three kernels, one wave = one unit of work:
 //   rs_stats    wave (b, row, segment): max and sum of exp((z - max)/T) over a
-//               segment of one target or draft row.  The last wave of sequence
-//               b (completion counter) merges the segments of all 2*gamma+1
-//               rows, evaluates p_i(x_i), q_i(x_i), the accept tests and n.
+//               segment of one target or draft row.
+//   rs_finalize wave b: merges the segments of all 2*gamma+1 rows, evaluates
+//               p_i(x_i), q_i(x_i), the accept tests and n.
 //   rs_resolve  wave (b, segment) of the decided row n: residual weights
 //               max(0, p_n - q_n) (or p_gamma for the bonus) summed per
 //               segment; the last wave of b locates the segment where the
 //               fp64 prefix sum first exceeds u * total, re-scans that segment
 //               and writes the emitted tokens.
 // Both merge steps are in fp64 and in a fixed order, so results do not depend
-// on which wave arrives last.
+// on which wave arrives last.  No workspace word is read before this call has
+// written it (the resolve counters are cleared by rs_finalize), so a workspace
+// needs no initialisation and may be shared by calls of different sizes.
 #include <math.h>
 #include <stdint.h>
 
@@ -107,17 +109,13 @@ __device__ __forceinline__ float tree_sum(const float* a) {
 }
 
 // ---------------------------------------------------------------------------
-// pass 1: row statistics, accept tests, first rejection
+// pass 1: row statistics; accept tests and the first rejection per sequence
 // ---------------------------------------------------------------------------
 
 template <typename T, int VEC, int NIT>
 __global__ __launch_bounds__(256) void rs_stats(const T* __restrict__ tgt, const T* __restrict__ drf,
-                                                const int32_t* __restrict__ xtok, const double* __restrict__ uni,
-                                                int B, int G, int V, int nseg, float c32, double c64,
-                                                RowPart* __restrict__ part, SeqState* __restrict__ st,
-                                                uint32_t* __restrict__ ctr, int32_t* __restrict__ n_out,
-                                                int32_t* __restrict__ tok_out, float* __restrict__ p_out,
-                                                float* __restrict__ q_out) {
+                                                int B, int G, int V, int nseg, float c32,
+                                                RowPart* __restrict__ part) {
   constexpr int SEG = kWave * VEC * NIT;
   const int lane = threadIdx.x & (kWave - 1);
   const int R = 2 * G + 1;
@@ -165,10 +163,24 @@ __global__ __launch_bounds__(256) void rs_stats(const T* __restrict__ tgt, const
     rp.S = S;
     part[gw] = rp;
   }
+}
 
-  if (!wave_arrive_last(&ctr[b], (uint32_t)(R * nseg), lane)) return;
-
-  // ---- last wave of sequence b: merge segments row by row (fp64) ----------
+// One wave per sequence: merge the segments of all 2*gamma+1 rows (fp64),
+// evaluate p_i(x_i), q_i(x_i) and the accept tests, find n, record the decided
+// row's statistics for the resolve pass and clear its completion counter.
+template <typename T>
+__global__ __launch_bounds__(256) void rs_finalize(const T* __restrict__ tgt, const T* __restrict__ drf,
+                                                   const int32_t* __restrict__ xtok, const double* __restrict__ uni,
+                                                   int B, int G, int V, int nseg, float c32, double c64,
+                                                   const RowPart* __restrict__ part, SeqState* __restrict__ st,
+                                                   uint32_t* __restrict__ ctr, int32_t* __restrict__ n_out,
+                                                   int32_t* __restrict__ tok_out, float* __restrict__ p_out,
+                                                   float* __restrict__ q_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int R = 2 * G + 1;
+  const long b = (long)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (b >= B) return;
+  // merge the segments row by row (fp64); lane r keeps row r's statistics
   const RowPart* pb = part + (size_t)b * R * nseg;
   float myM = neg_inf_f();
   double myS = 0.0;
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(256) void rs_stats(const T* __restrict__ tgt, const
     s_.Sd = Sd_n;
     st[b] = s_;
     n_out[b] = bad_mask ? -1 : n;
-    ctr[b] = 0u;  // leave the workspace clean for the next call
+    ctr[b] = 0u;  // the resolve pass counts its waves here
   }
   if (bad_mask && lane <= G) tok_out[(size_t)b * (G + 1) + lane] = -1;
 }
@@ -288,7 +300,7 @@ __global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, con
   const int seg = (int)(gw % nseg);
   const int b = (int)(gw / nseg);
   const SeqState s = st[b];
-  if (!s.valid) {
+  if (!s.valid || s.n < 0 || s.n > G) {
     if (lane == 0) part[gw] = make_double2(0.0, 0.0);
     if (wave_arrive_last(&ctr[b], (uint32_t)nseg, lane) && lane == 0) ctr[b] = 0u;
     return;
@@ -391,7 +403,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct RsPlan {
   int vec, nit, seg, nseg;
-  size_t off_part1, off_state, off_part2, off_ctr1, off_ctr2, total;
+  size_t off_part1, off_state, off_part2, off_ctr2, total;
 };
 
 static int pick_vec(int V, int esize, uintptr_t a, uintptr_t b) {
@@ -417,8 +429,6 @@ static RsPlan rs_plan(int B, int G, int V, int esize, int vec) {
   off = align256(off + sizeof(SeqState) * (size_t)B);
   p.off_part2 = off;
   off = align256(off + sizeof(double2) * (size_t)B * p.nseg);
-  p.off_ctr1 = off;
-  off = align256(off + sizeof(uint32_t) * (size_t)B);
   p.off_ctr2 = off;
   off = align256(off + sizeof(uint32_t) * (size_t)B);
   p.total = off;
@@ -436,12 +446,15 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
   RowPart* part1 = reinterpret_cast<RowPart*>(ws + pl.off_part1);
   SeqState* state = reinterpret_cast<SeqState*>(ws + pl.off_state);
   double2* part2 = reinterpret_cast<double2*>(ws + pl.off_part2);
-  uint32_t* ctr1 = reinterpret_cast<uint32_t*>(ws + pl.off_ctr1);
   uint32_t* ctr2 = reinterpret_cast<uint32_t*>(ws + pl.off_ctr2);
   hipLaunchKernelGGL((rs_stats<T, VEC, NIT>), dim3((unsigned)((waves1 + WPB - 1) / WPB)), dim3(256), 0, stream,
-                     (const T*)tgt, (const T*)drf, x, u, B, G, V, pl.nseg, c32, c64, part1, state, ctr1, n_out,
-                     tok_out, p_out, q_out);
+                     (const T*)tgt, (const T*)drf, B, G, V, pl.nseg, c32, part1);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rs_finalize<T>), dim3((unsigned)((B + WPB - 1) / WPB)), dim3(256), 0, stream, (const T*)tgt,
+                     (const T*)drf, x, u, B, G, V, pl.nseg, c32, c64, part1, state, ctr2, n_out, tok_out, p_out,
+                     q_out);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((rs_resolve<T, VEC, NIT>), dim3((unsigned)((waves2 + WPB - 1) / WPB)), dim3(256), 0, stream,
                      (const T*)tgt, (const T*)drf, x, u, B, G, V, pl.nseg, c32, state, part2, ctr2, tok_out);

@@ -115,8 +115,7 @@ def test_shapes_and_edges(dtype, B, Hq, Hkv, n_q, D, lens):
     max_T = max(lens) + n_q + 7
     cfg = W.Config(98, "shape", B=B, gamma=n_q - 1, V=1, dtype=dtype, Hq=Hq, Hkv=Hkv, D=D,
                    L=(0, max(lens)), max_T=max_T)
-    inp = W.attention_inputs(cfg, B=B, max_T=max_T)
-    inp["lens"] = np.array(lens, np.int32)
+    inp = W.attention_inputs(cfg, B=B, max_T=max_T, lens=lens)
     out, kc, vc = _run_host(inp, poison_tail=True)
     _check(inp, out, kc, vc, dtype)
 
@@ -125,8 +124,7 @@ def test_cache_full_to_capacity():
     cfg = W.get(4)
     B, max_T = 2, 1024
     _case("capacity", B=B, max_T=max_T)
-    inp = W.attention_inputs(cfg, B=B, max_T=max_T)
-    inp["lens"] = np.array([max_T - cfg.n_q, 3], np.int32)
+    inp = W.attention_inputs(cfg, B=B, max_T=max_T, lens=[max_T - cfg.n_q, 3])
     out, kc, vc = _run_host(inp, hint=max_T - cfg.n_q)
     _check(inp, out, kc, vc, "bf16")
 
@@ -135,12 +133,11 @@ def test_length_beyond_hint_is_flagged_not_written():
     cfg = W.get(4)
     B, max_T = 2, 512
     _case("bad-length", B=B)
-    inp = W.attention_inputs(cfg, B=B, max_T=max_T)
-    inp["lens"] = np.array([100, 400], np.int32)
+    inp = W.attention_inputs(cfg, B=B, max_T=max_T, lens=[100, 400])
     out, kc, vc = _run_host(inp, hint=200)  # sequence 1 exceeds the hint
     assert np.all(np.isnan(_gpu.as_f64(out[1])))
     assert np.array_equal(kc[1], inp["k_cache"][1]) and np.array_equal(vc[1], inp["v_cache"][1])
-    _check({k: (v[:1] if k != "lens" else v[:1]) for k, v in inp.items()}, out[:1], kc[:1], vc[:1], "bf16")
+    _check({k: v[:1] for k, v in inp.items()}, out[:1], kc[:1], vc[:1], "bf16")
 
 
 def test_status_codes():

@@ -93,7 +93,7 @@ def lengths(cfg: Config, rep: int = 0, B=None):
     return rng(cfg, 3, rep).integers(lo, hi + 1, size=B).astype(np.int32)
 
 
-def attention_inputs(cfg: Config, rep: int = 0, B=None, max_T=None):
+def attention_inputs(cfg: Config, rep: int = 0, B=None, max_T=None, lens=None):
     """Host arrays for verify attention (configs 3-5 shapes, or reduced B).
 
     q [B, Hq, n_q, D], k_new / v_new [B, Hkv, n_q, D], k_cache / v_cache
@@ -114,9 +114,9 @@ def attention_inputs(cfg: Config, rep: int = 0, B=None, max_T=None):
         "v_new": draw(B, cfg.Hkv, n, D),
         "k_cache": draw(B, cfg.Hkv, max_T, D),
         "v_cache": draw(B, cfg.Hkv, max_T, D),
-        "lens": lengths(cfg, rep, B),
+        "lens": lengths(cfg, rep, B) if lens is None else np.asarray(lens, np.int32),
     }
-    assert int(out["lens"].max()) + n <= max_T
+    assert int(out["lens"].max()) + n <= max_T and int(out["lens"].min()) >= 0
     return out
 
 
