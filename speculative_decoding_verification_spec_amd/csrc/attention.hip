@@ -7,36 +7,45 @@
 //   section GQA・MQAでKVキャッシュを減らす (query heads share KV heads; decode
 //   attention time is the time to read the cache).
 //
-// Work decomposition.  One wave (= one 64-thread workgroup) per work item
-// (b, g, rg, sp): sequence b, KV head g, row group rg, key split sp.  The
-// wave holds every query row of its group -- the G = Hq/Hkv heads that share
-// KV head g, times the n_q verify positions, padded to 16-row MFMA tiles --
-// so each K/V tile read from HBM serves all of them (the GQA reuse), and the
-// wave walks its split's keys in blocks of 32 with an online softmax.  The
-// partial (max, sum, unnormalised output) of each split goes to the workspace;
-// attn_combine merges the splits of (b, g, rg) and writes the output.
+// Work decomposition.  A work item is (b, g, rg, sp): sequence b, KV head g,
+// row group rg, key split sp.  The rows of (b, g) are the G = Hq/Hkv query
+// heads sharing KV head g times the n_q verify positions, padded to 16-row
+// MFMA tiles; all of them read the same K/V tiles (the GQA reuse).  Each split
+// walks C keys in blocks of 32 with an online softmax and leaves its
+// (max, sum, unnormalised output) in the workspace; attn_combine merges the
+// splits.  A (b, g) whose keys fit one split writes its output directly.
 //
-// MFMA layouts (gfx950, wave64).  For v_mfma_f32_16x16x32_bf16 lane l holds
-// A[l%16][8(l/16) .. 8(l/16)+7], B[8(l/16) .. +7][l%16] and returns
-// C[4(l/16) + j][l%16], j = 0..3; v_mfma_f32_16x16x4_f32 holds one element,
-// A[l%16][l/16], B[l/16][l%16], with the same C layout.
+// MFMA layouts (gfx950, wave64, checked on the hardware).  For
+// v_mfma_f32_16x16x32_bf16 lane l holds A[l%16][8(l/16) .. +7],
+// B[8(l/16) .. +7][l%16] and returns C[4(l/16) + j][l%16], j = 0..3;
+// v_mfma_f32_16x16x4_f32 holds A[l%16][l/16], B[l/16][l%16], same C layout.
 //   Scores are computed transposed, S^T = K Q^T (A = 16 keys x D, B = D x 16
-//   rows), so each lane ends with 4 keys x 1 row: the row statistics need
-//   only a reduction over the 4 lane groups, and the probabilities are
-//   already where the B operand of O^T = V^T P^T wants them (keys along the
-//   contraction).  The contraction over keys may take the keys in any order,
-//   so the 8 keys a lane holds from two 16-key tiles, {4(l/16) + j, 16 +
-//   4(l/16) + j}, form its 8 contiguous MFMA k-slots, and V^T is gathered in
-//   that same key order.
-//   V^T needs D along the rows and keys along the contraction, the transpose
-//   of how the cache stores V; a wave stages its 32 x D V block in LDS
-//   (coalesced 16-byte rows) and reads it back transposed.  For fp32 each
-//   MFMA takes one key per lane, so V is read straight from memory.
+//   rows), so each lane ends with 4 keys x 1 row: row statistics need only a
+//   reduction over the 4 lane groups, and the probabilities are already where
+//   the B operand of O^T = V^T P^T wants them (keys along the contraction).
+//   The contraction may take keys in any order, so the 8 keys a lane holds
+//   from two 16-key tiles, {4(l/16) + j, 16 + 4(l/16) + j}, are its 8 MFMA
+//   k-slots and V^T is gathered in the same order.
+//
+// bf16 kernel.  One workgroup per work item, one wave per 16-row tile.  K and
+// V blocks (32 keys x D) are copied from HBM straight into LDS with
+// global_load_lds (no registers, asynchronous), double buffered, and read by
+// every wave of the workgroup: K as 16-byte A fragments (ds_read_b128), V
+// transposed with ds_read_b64_tr_b16 (within each 16-lane group, lane i
+// receives element i mod 4 of the 8-byte pieces of lanes 4k + i/4, k = 0..3;
+// pointing lane 4k+q at V[key_k][d0 + 4q] hands lane i V[key_0..3][d0 + i]).
+// Each 16-byte column slot of a staged row is XOR-swizzled by the row so both
+// read patterns are free of LDS bank conflicts; the swizzle is applied on the
+// global side of the copy, which keeps every 16 lanes of a copy on one
+// contiguous row.
+//
+// fp32 kernel.  One wave per work item holding every row tile; one key per
+// lane per MFMA, so V is read straight from memory.
 //
 // Keys [0, L_b) come from the cache, keys [L_b, L_b + n_q) from k_new/v_new
 // directly (so the append in the same launch is never read back), and keys at
-// or past L_b + n_q are zero and masked.  The cache rows past L_b are never
-// read.  Row i of the verify block sees keys <= L_b + i.
+// or past L_b + n_q are masked (they read a finite dummy row).  Cache rows at
+// or past L_b are never read.  Row i of the verify block sees keys <= L_b + i.
 #include <math.h>
 #include <stdint.h>
 
@@ -48,36 +57,13 @@
 namespace specv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KB = 32;  // keys per block
 
 struct ML {  // per split and row: running max (log2 units) and sum
   float m, l;
-};
-
-template <typename T>
-struct Tr;
-
-template <>
-struct Tr<uint16_t> {  // bfloat16 storage
-  static constexpr int KSTEP = 32;  // contraction per MFMA
-  using frag = bf16x8;
-  __device__ static frag zero() { return frag{}; }
-  __device__ static frag load(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-  __device__ static f32x4 mma(frag a, frag b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-template <>
-struct Tr<float> {
-  static constexpr int KSTEP = 4;
-  using frag = float;
-  __device__ static frag zero() { return 0.f; }
-  __device__ static frag load(const float* p) { return *p; }
-  __device__ static f32x4 mma(frag a, frag b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
 };
 
 struct AttnArgs {
@@ -90,11 +76,30 @@ struct AttnArgs {
   void* out;
   float* part_o;
   ML* part_ml;
-  int B, Hq, Hkv, n_q, G, M, RG, NSP, C, max_T, hint;
+  int B, Hq, Hkv, n_q, G, M, RG, RT, NSP, C, max_T, hint;
   float qk_scale;  // scale * log2(e)
 };
 
-// Row pointer of key `key` of (b, g): cache row, new row, or null (masked).
+// Decode blockIdx into (b, g, rg, sp); sp varies fastest.
+struct Item {
+  int b, g, rg, sp;
+  long bg;
+};
+
+__device__ __forceinline__ Item decode_item(const AttnArgs& a) {
+  long item = blockIdx.x;
+  Item it;
+  it.sp = (int)(item % a.NSP);
+  item /= a.NSP;
+  it.rg = (int)(item % a.RG);
+  item /= a.RG;
+  it.g = (int)(item % a.Hkv);
+  it.b = (int)(item / a.Hkv);
+  it.bg = (long)it.b * a.Hkv + it.g;
+  return it;
+}
+
+// Row of key `key` of (b, g): the cache row, the new row, or null (masked).
 template <typename T>
 __device__ __forceinline__ const T* key_row(const T* cache, const T* fresh, int key, int L, int Ltot, int n_q,
                                             int max_T, int D, long bg) {
@@ -103,75 +108,257 @@ __device__ __forceinline__ const T* key_row(const T* cache, const T* fresh, int 
   return nullptr;
 }
 
-template <typename T, int D, int RT>
-__global__ __launch_bounds__(64) void attn_split(AttnArgs a) {
-  using TR = Tr<T>;
-  using frag = typename TR::frag;
-  constexpr bool BF = sizeof(T) == 2;
-  constexpr int KSTEP = TR::KSTEP;
-  constexpr int DS = D / KSTEP;          // MFMA steps over D for the scores
-  constexpr int DT = (D + 15) / 16;      // 16-wide output tiles over D
-  constexpr int VP = D + 8;              // LDS pitch of the staged V block (bf16)
-  __shared__ uint16_t vs[BF ? KB * VP : 1];
+// A1: copy the n_q new rows of (b, g) into the cache at rows [L, L + n_q).
+template <typename T, int D>
+__device__ __forceinline__ void append_rows(const AttnArgs& a, long bg, int L, int tid, int nthreads) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  const int chunks = a.n_q * D / EPC;
+  const uint4* skn = reinterpret_cast<const uint4*>(static_cast<const T*>(a.kn) + (size_t)bg * a.n_q * D);
+  const uint4* svn = reinterpret_cast<const uint4*>(static_cast<const T*>(a.vn) + (size_t)bg * a.n_q * D);
+  uint4* dkc = reinterpret_cast<uint4*>(static_cast<T*>(a.kc) + ((size_t)bg * a.max_T + L) * D);
+  uint4* dvc = reinterpret_cast<uint4*>(static_cast<T*>(a.vc) + ((size_t)bg * a.max_T + L) * D);
+  for (int c = tid; c < chunks; c += nthreads) {
+    dkc[c] = skn[c];
+    dvc[c] = svn[c];
+  }
+}
 
-  const int lane = threadIdx.x;
-  const int lr = lane & 15;  // row (or key) within a 16-tile
-  const int lg = lane >> 4;  // lane group 0..3
-  long item = blockIdx.x;
-  const int sp = (int)(item % a.NSP);
-  item /= a.NSP;
-  const int rg = (int)(item % a.RG);
-  item /= a.RG;
-  const int g = (int)(item % a.Hkv);
-  const int b = (int)(item / a.Hkv);
-  const long bg = (long)b * a.Hkv + g;
+// Online-softmax update of one row from 8 scaled scores (log2 domain);
+// returns the rescale factor of the previous state and writes the new
+// probabilities into s in place.
+__device__ __forceinline__ float softmax_update(float (&s)[8], float& mrow, float& lsum) {
+  float mx = s[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, s[j]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+  const float mnew = fmaxf(mrow, mx);
+  const bool none = (mnew == neg_inf_f());
+  const float alpha = none ? 1.f : exp2_fast(mrow - mnew);
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float p = none ? 0.f : exp2_fast(s[j] - mnew);
+    s[j] = p;
+    ps += p;
+  }
+  lsum = lsum * alpha + ps;
+  mrow = mnew;
+  return alpha;
+}
 
-  const int L = a.len[b];
+// ---------------------------------------------------------------------------
+// bf16 split kernel: NW waves, one 16-row tile each, K/V staged in LDS
+// ---------------------------------------------------------------------------
+
+template <int D>
+struct BfLayout {
+  static constexpr int CH = D / 8;               // 16-byte slots per row
+  static constexpr int RP = 256 / (2 * D);       // rows per 256-byte bank line (>= 1)
+  static constexpr int TILE = KB * D;            // elements per staged tile
+  static constexpr int NI = TILE * 2 / 1024;     // 1 KB global_load_lds copies per tile
+  // K rows are read 16 at a time at one slot: spread them over 16 slots.
+  __device__ static int kslot(int row, int c) { return c ^ ((row / RP) % CH); }
+  // V rows are read 8 at a time at a 32-byte slot pair: spread them over 8 pairs.
+  __device__ static int vslot(int row, int c) { return c ^ (2 * ((row / RP) % (CH / 2))); }
+};
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_split_bf16(AttnArgs a) {
+  using LY = BfLayout<D>;
+  constexpr int DS = D / 32;  // MFMA steps over D for the scores
+  constexpr int DT = D / 16;  // 16-wide output tiles over D
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][LY::TILE];  // [stage][K,V]
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid & (kWave - 1);
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const Item it = decode_item(a);
+  const int L = a.len[it.b];
   if (L < 0 || L > a.hint) return;  // flagged by attn_combine
   const int Ltot = L + a.n_q;
-  const int k0 = sp * a.C;
+  const int k0 = it.sp * a.C;
   if (k0 >= Ltot) return;
   const int k1 = min(k0 + a.C, Ltot);
+  const int nblk = (k1 - k0 + KB - 1) / KB;
+  const bool single = (Ltot <= a.C);  // this item is the whole of (b, g, rg)
 
-  const T* q = static_cast<const T*>(a.q);
-  const T* kn = static_cast<const T*>(a.kn);
-  const T* vn = static_cast<const T*>(a.vn);
-  const T* kc = static_cast<const T*>(a.kc);
-  const T* vc = static_cast<const T*>(a.vc);
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* kn = static_cast<const uint16_t*>(a.kn);
+  const uint16_t* vn = static_cast<const uint16_t*>(a.vn);
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
 
-  // A1: append the n_q new rows (done once per (b, g); no wave reads them
-  // from the cache in this launch).
-  if (sp == 0 && rg == 0) {
-    constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
-    const int chunks = a.n_q * D / EPC;
-    const uint4* skn = reinterpret_cast<const uint4*>(kn + (size_t)bg * a.n_q * D);
-    const uint4* svn = reinterpret_cast<const uint4*>(vn + (size_t)bg * a.n_q * D);
-    uint4* dkc = reinterpret_cast<uint4*>(static_cast<T*>(a.kc) + ((size_t)bg * a.max_T + L) * D);
-    uint4* dvc = reinterpret_cast<uint4*>(static_cast<T*>(a.vc) + ((size_t)bg * a.max_T + L) * D);
-    for (int c = lane; c < chunks; c += kWave) {
-      dkc[c] = skn[c];
-      dvc[c] = svn[c];
+  // Copies of one block: copy c of the 2*NI (first NI for K, then NI for V)
+  // is issued by wave c % NW; lane l fills LDS slot (64 c' + l) of its tile
+  // (c' = c mod NI), i.e. row (64 c' + l) / CH at swizzled slot (64 c' + l) % CH.
+  auto copy_tile = [&](const uint16_t* cache, const uint16_t* fresh, uint16_t* dst, int kb, int cc, bool is_v) {
+    const int p = cc * kWave + lane;
+    const int row = p / LY::CH, sl = p % LY::CH;
+    const int chunk = is_v ? LY::vslot(row, sl) : LY::kslot(row, sl);  // XOR is its own inverse
+    const uint16_t* src = key_row<uint16_t>(cache, fresh, kb + row, L, Ltot, a.n_q, a.max_T, D, it.bg);
+    if (!src) src = fresh + (size_t)it.bg * a.n_q * D;  // finite dummy row for masked keys
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + 8 * chunk),
+                                     (void __attribute__((address_space(3)))*)(dst + cc * 512), 16, 0, 0);
+  };
+  auto issue_block = [&](int kb, int stage) {
+    for (int c = wave; c < LY::NI; c += NW) copy_tile(kc, kn, lds[stage][0], kb, c, false);
+    for (int c = (wave + NW - LY::NI % NW) % NW; c < LY::NI; c += NW) copy_tile(vc, vn, lds[stage][1], kb, c, true);
+  };
+
+  issue_block(k0, 0);
+
+  if (it.sp == 0 && it.rg == 0) append_rows<uint16_t, D>(a, it.bg, L, tid, 64 * NW);
+
+  // Query fragment of this wave's tile (B operand of S^T = K Q^T).
+  const int m = it.rg * 16 * NW + 16 * wave + lr;
+  const bool valid = m < a.M;
+  const int h = it.g * a.G + (valid ? m / a.n_q : 0);
+  const int qi = valid ? m % a.n_q : a.n_q - 1;
+  const int lim = L + qi;  // last visible key of this row
+  bf16x8 qf[DS];
+  {
+    const uint16_t* qrow = q + (((size_t)it.b * a.Hq + h) * a.n_q + qi) * D;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      qf[s] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg) : bf16x8{};
+  }
+
+  float mrow = neg_inf_f(), lsum = 0.f;
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int j = 0; j < nblk; ++j) {
+    const int kb = k0 + j * KB;
+    const int stage = j & 1;
+    // This wave's copies of block j are complete; after the barrier every
+    // wave's are, and every wave has finished reading block j-1's stage.
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 1 < nblk) issue_block(kb + KB, stage ^ 1);
+
+    const uint16_t* ks = lds[stage][0];
+    const uint16_t* vs = lds[stage][1];
+    // Scores: lane holds keys kb + 16 kt + 4 lg + jj of row lr of the tile.
+    float sc[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int row = 16 * kt + lr;
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + row * D + 8 * LY::kslot(row, 4 * s + lg));
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], c, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) sc[4 * kt + jj] = c[jj] * a.qk_scale;
+    }
+    if (kb + KB > L) {  // the block reaches the new rows or the end: causal mask
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int key = kb + 16 * kt + 4 * lg + jj;
+          if (key >= Ltot || key > lim) sc[4 * kt + jj] = neg_inf_f();
+        }
+    }
+    const float alpha = softmax_update(sc, mrow, lsum);
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    }
+    bf16x8 pf;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) pf[jj] = (__bf16)sc[jj];
+
+    // V^T fragments: half h covers keys 16 h + 4 lg + (0..3); lane lr of the
+    // group points at V[16 h + 4 lg + lr/4][16 dt + 4 (lr%4)].
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      s16x4 v2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 16 * hh + 4 * lg + (lr >> 2);
+        const int q4 = lr & 3;
+        const int chunk = 2 * dt + (q4 >> 1);
+        const uint16_t* p = vs + row * D + 8 * LY::vslot(row, chunk) + 4 * (q4 & 1);
+        v2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+      }
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
     }
   }
 
-  // Query fragments (B operand of S^T = K Q^T) and each row's causal limit.
-  frag qf[RT][DS];
+  // Row sum over the 4 lane groups.
+  float lt = lsum;
+  lt += __shfl_xor(lt, 16, kWave);
+  lt += __shfl_xor(lt, 32, kWave);
+  const int row = 16 * wave + lr;  // row within the item
+  if (single) {
+    // The whole of (b, g, rg) is here: normalise and write the output.
+    if (valid) {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)it.b * a.Hq + h) * a.n_q + qi) * D;
+      const float inv = 1.f / lt;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + 4 * lg;
+        uint2 pk;
+        pk.x = uint32_t(f32_to_bf16(oacc[dt][0] * inv)) | (uint32_t(f32_to_bf16(oacc[dt][1] * inv)) << 16);
+        pk.y = uint32_t(f32_to_bf16(oacc[dt][2] * inv)) | (uint32_t(f32_to_bf16(oacc[dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(o + d) = pk;
+      }
+    }
+    return;
+  }
+  const size_t item_id = blockIdx.x;
+  float* po = a.part_o + item_id * (16 * NW) * D;
+  if (lg == 0) a.part_ml[item_id * (16 * NW) + row] = ML{mrow, lt};
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[dt];
+}
+
+// ---------------------------------------------------------------------------
+// fp32 split kernel: one wave per item holding RT row tiles
+// ---------------------------------------------------------------------------
+
+template <int D, int RT>
+__global__ __launch_bounds__(64) void attn_split_f32(AttnArgs a) {
+  constexpr int DS = D / 4;
+  constexpr int DT = (D + 15) / 16;
+  const int lane = threadIdx.x;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const Item it = decode_item(a);
+  const int L = a.len[it.b];
+  if (L < 0 || L > a.hint) return;
+  const int Ltot = L + a.n_q;
+  const int k0 = it.sp * a.C;
+  if (k0 >= Ltot) return;
+  const int k1 = min(k0 + a.C, Ltot);
+  const float* q = static_cast<const float*>(a.q);
+  const float* kn = static_cast<const float*>(a.kn);
+  const float* vn = static_cast<const float*>(a.vn);
+  const float* kc = static_cast<const float*>(a.kc);
+  const float* vc = static_cast<const float*>(a.vc);
+
+  if (it.sp == 0 && it.rg == 0) append_rows<float, D>(a, it.bg, L, lane, kWave);
+
+  float qf[RT][DS];
   int lim[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    const int m = rg * 16 * RT + 16 * r + lr;
+    const int m = it.rg * 16 * RT + 16 * r + lr;
     const bool valid = m < a.M;
-    const int h = g * a.G + (valid ? m / a.n_q : 0);
+    const int h = it.g * a.G + (valid ? m / a.n_q : 0);
     const int i = valid ? m % a.n_q : a.n_q - 1;
     lim[r] = L + i;
-    const T* qrow = q + (((size_t)b * a.Hq + h) * a.n_q + i) * D;
+    const float* qrow = q + (((size_t)it.b * a.Hq + h) * a.n_q + i) * D;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const int d = BF ? s * KSTEP + 8 * lg : s * KSTEP + lg;
-      qf[r][s] = valid ? TR::load(qrow + d) : TR::zero();
-    }
+    for (int s = 0; s < DS; ++s) qf[r][s] = valid ? qrow[4 * s + lg] : 0.f;
   }
-
   float mrow[RT], lsum[RT];
   f32x4 oacc[RT][DT];
 #pragma unroll
@@ -182,150 +369,62 @@ __global__ __launch_bounds__(64) void attn_split(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) oacc[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // K fragments of a block: kf[kt][s] = K[kb + 16 kt + lr][s*KSTEP + (8 lg | lg) ...]
-  auto load_k = [&](int kb, frag (&kf)[2][DS]) {
+  for (int kb = k0; kb < k1; kb += KB) {
+    float kf[2][DS];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const T* row = key_row<T>(kc, kn, kb + 16 * kt + lr, L, Ltot, a.n_q, a.max_T, D, bg);
+      const float* row = key_row<float>(kc, kn, kb + 16 * kt + lr, L, Ltot, a.n_q, a.max_T, D, it.bg);
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const int d = BF ? s * KSTEP + 8 * lg : s * KSTEP + lg;
-        kf[kt][s] = row ? TR::load(row + d) : TR::zero();
-      }
+      for (int s = 0; s < DS; ++s) kf[kt][s] = row ? row[4 * s + lg] : 0.f;
     }
-  };
-
-  frag kcur[2][DS], knext[2][DS];
-  load_k(k0, kcur);
-
-  for (int kb = k0; kb < k1; kb += KB) {
-    const bool has_next = kb + KB < k1;
-    if (has_next) load_k(kb + KB, knext);
-
-    // V of this block: bf16 rows into registers now, to LDS after the scores.
-    constexpr int VCH = BF ? (KB * D / 8) / kWave : 1;  // 16-byte chunks per lane
-    uint4 vreg[BF ? VCH : 1];
-    if constexpr (BF) {
+    float sc[RT][8];
 #pragma unroll
-      for (int c = 0; c < VCH; ++c) {
-        const int ch = lane + c * kWave;
-        const int krow = ch / (D / 8), kcol = ch % (D / 8);
-        const T* row = key_row<T>(vc, vn, kb + krow, L, Ltot, a.n_q, a.max_T, D, bg);
-        vreg[c] = row ? *reinterpret_cast<const uint4*>(row + 8 * kcol) : make_uint4(0, 0, 0, 0);
-      }
-    }
-
-    // Scores S^T for 2 key tiles x RT row tiles; lane holds keys
-    // kb + 16 kt + 4 lg + j of row 16 r + lr.
-    f32x4 sacc[2][RT];
+    for (int r = 0; r < RT; ++r)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
+      for (int kt = 0; kt < 2; ++kt) {
         f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < DS; ++s) c = TR::mma(kcur[kt][s], qf[r][s], c);
-        sacc[kt][r] = c * a.qk_scale;
+        for (int s = 0; s < DS; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[kt][s], qf[r][s], c, 0, 0, 0);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) sc[r][4 * kt + jj] = c[jj] * a.qk_scale;
       }
-    if (kb + KB > L) {  // block reaches the new rows or the end: causal mask
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < RT; ++r)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int key = kb + 16 * kt + 4 * lg + j;
-            if (key >= Ltot || key > lim[r]) sacc[kt][r][j] = neg_inf_f();
-          }
-    }
-
-    // Online softmax (log2 domain).
-    float pr[2][RT][4];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      float mx = neg_inf_f();
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, sacc[kt][r][j]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mnew = fmaxf(mrow[r], mx);
-      const bool none = (mnew == neg_inf_f());
-      const float alpha = none ? 1.f : exp2_fast(mrow[r] - mnew);
-      float ps = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = none ? 0.f : exp2_fast(sacc[kt][r][j] - mnew);
-          pr[kt][r][j] = p;
-          ps += p;
-        }
-      lsum[r] = lsum[r] * alpha + ps;
-      mrow[r] = mnew;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[r][dt] *= alpha;
-    }
-
-    if constexpr (BF) {
-      // Stage V (32 x D) in LDS, then gather V^T fragments in the key order
-      // the P fragments use.
-      __syncthreads();
-#pragma unroll
-      for (int c = 0; c < VCH; ++c) {
-        const int ch = lane + c * kWave;
-        const int krow = ch / (D / 8), kcol = ch % (D / 8);
-        *reinterpret_cast<uint4*>(&vs[krow * VP + 8 * kcol]) = vreg[c];
-      }
-      __syncthreads();
-      bf16x8 pf[RT];
+    if (kb + KB > L) {
 #pragma unroll
       for (int r = 0; r < RT; ++r)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pf[r][j] = (__bf16)pr[j >> 2][r][j & 3];
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        s16x8 vv;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int krow = (j < 4) ? (4 * lg + j) : (16 + 4 * lg + (j - 4));
-          vv[j] = (short)vs[krow * VP + 16 * dt + lr];
-        }
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-#pragma unroll
-        for (int r = 0; r < RT; ++r) oacc[r][dt] = TR::mma(vf, pf[r], oacc[r][dt]);
-      }
-    } else {
-      // fp32: one key per lane per MFMA; lane group lg supplies key
-      // kb + 16 kt + 4 lg + j at step (kt, j).
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const T* row = key_row<T>(vc, vn, kb + 16 * kt + 4 * lg + j, L, Ltot, a.n_q, a.max_T, D, bg);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) {
-            const int d = 16 * dt + lr;
-            const float vv = (row && d < D) ? reinterpret_cast<const float*>(row)[d] : 0.f;
-#pragma unroll
-            for (int r = 0; r < RT; ++r) oacc[r][dt] = TR::mma(vv, pr[kt][r][j], oacc[r][dt]);
+          for (int jj = 0; jj < 4; ++jj) {
+            const int key = kb + 16 * kt + 4 * lg + jj;
+            if (key >= Ltot || key > lim[r]) sc[r][4 * kt + jj] = neg_inf_f();
           }
+    }
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      const float alpha = softmax_update(sc[r], mrow[r], lsum[r]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[r][dt] *= alpha;
+    }
+    // One key per lane per MFMA: lane group lg supplies key kb + 16 kt + 4 lg + jj.
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float* row = key_row<float>(vc, vn, kb + 16 * kt + 4 * lg + jj, L, Ltot, a.n_q, a.max_T, D, it.bg);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 16 * dt + lr;
+          const float vv = (row && d < D) ? row[d] : 0.f;
+#pragma unroll
+          for (int r = 0; r < RT; ++r)
+            oacc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sc[r][4 * kt + jj], oacc[r][dt], 0, 0, 0);
         }
-    }
-
-    if (has_next) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int s = 0; s < DS; ++s) kcur[kt][s] = knext[kt][s];
-    }
+      }
   }
 
-  // Write this split's partial: O^T tile (d = 16 dt + 4 lg + j, row 16 r + lr).
-  const long item_id = blockIdx.x;
-  float* po = a.part_o + (size_t)item_id * (16 * RT) * D;
-  ML* pml = a.part_ml + (size_t)item_id * (16 * RT);
+  const size_t item_id = blockIdx.x;
+  float* po = a.part_o + item_id * (16 * RT) * D;
+  ML* pml = a.part_ml + item_id * (16 * RT);
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     float lt = lsum[r];
@@ -341,84 +440,66 @@ __global__ __launch_bounds__(64) void attn_split(AttnArgs a) {
   }
 }
 
-// Merge the splits of (b, g, rg) and write out[b][h][i][:].
+// ---------------------------------------------------------------------------
+// combine: merge the splits of (b, g, rg) and write out[b][h][i][:]
+// ---------------------------------------------------------------------------
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int RT) {
-  constexpr int MAXSP = 64;  // splits handled per pass of the weight table
-  __shared__ float coef[16 * 5][MAXSP];
-  const int rows = 16 * RT;
-  long item = blockIdx.x;
-  const int rg = (int)(item % a.RG);
-  item /= a.RG;
-  const int g = (int)(item % a.Hkv);
-  const int b = (int)(item / a.Hkv);
-  const int L = a.len[b];
-  T* out = static_cast<T*>(a.out);
-  const int tid = threadIdx.x;
-  const int row0 = rg * rows;
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int skip_single) {
+  const Item it = [&] {
+    long item = blockIdx.x;
+    Item x;
+    x.rg = (int)(item % a.RG);
+    item /= a.RG;
+    x.g = (int)(item % a.Hkv);
+    x.b = (int)(item / a.Hkv);
+    x.bg = (long)x.b * a.Hkv + x.g;
+    x.sp = 0;
+    return x;
+  }();
+  const int rows = 16 * a.RT;
+  const int row0 = it.rg * rows;
   const int nrows = min(rows, a.M - row0);
+  const int L = a.len[it.b];
+  T* out = static_cast<T*>(a.out);
   auto out_ptr = [&](int row) {
     const int m = row0 + row;
-    const int h = g * a.G + m / a.n_q, i = m % a.n_q;
-    return out + (((size_t)b * a.Hq + h) * a.n_q + i) * D;
+    return out + (((size_t)it.b * a.Hq + it.g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D;
   };
+  constexpr int D4 = D / 4;
   if (L < 0 || L > a.hint) {  // invalid length: NaN rows, nothing else touched
-    for (int e = tid; e < nrows * D; e += blockDim.x) {
-      T* o = out_ptr(e / D);
+    for (int e = threadIdx.x; e < nrows * D; e += blockDim.x) {
       if constexpr (sizeof(T) == 2)
-        o[e % D] = (T)0x7fc0;
+        out_ptr(e / D)[e % D] = (T)0x7fc0;
       else
-        o[e % D] = __builtin_nanf("");
+        out_ptr(e / D)[e % D] = __builtin_nanf("");
     }
     return;
   }
   const int nsp = (L + a.n_q + a.C - 1) / a.C;
-  const long base_item = ((long)b * a.Hkv + g) * a.RG + rg;  // item = base_item * NSP + sp
-  // Accumulate in register per (row, d) element, NSP in passes of MAXSP.
-  constexpr int EPT = (16 * 5 * D + 255) / 256;  // elements per thread (upper bound)
-  float acc[EPT];
-#pragma unroll
-  for (int k = 0; k < EPT; ++k) acc[k] = 0.f;
-  // Global max and denominator per row (over all splits).
-  __shared__ float rowmax[16 * 5], rowden[16 * 5];
-  if (tid < nrows) {
+  if (skip_single && nsp == 1) return;  // written by the split kernel
+  const size_t base = (((size_t)it.b * a.Hkv + it.g) * a.RG + it.rg) * a.NSP;  // item of split 0
+  for (int e = threadIdx.x; e < nrows * D4; e += blockDim.x) {
+    const int row = e / D4, d = 4 * (e % D4);
     float mx = neg_inf_f();
-    for (int sp = 0; sp < nsp; ++sp) mx = fmaxf(mx, a.part_ml[(base_item * a.NSP + sp) * rows + tid].m);
+    for (int sp = 0; sp < nsp; ++sp) mx = fmaxf(mx, a.part_ml[(base + sp) * rows + row].m);
     float den = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int sp = 0; sp < nsp; ++sp) {
-      const ML e = a.part_ml[(base_item * a.NSP + sp) * rows + tid];
-      den += e.l * exp2_fast(e.m - mx);
+      const ML ml = a.part_ml[(base + sp) * rows + row];
+      const float w = exp2_fast(ml.m - mx);
+      den += w * ml.l;
+      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + ((base + sp) * rows + row) * D + d);
     }
-    rowmax[tid] = mx;
-    rowden[tid] = den;
-  }
-  for (int sp0 = 0; sp0 < nsp; sp0 += MAXSP) {
-    const int cnt = min(MAXSP, nsp - sp0);
-    __syncthreads();
-    for (int e = tid; e < nrows * cnt; e += blockDim.x) {
-      const int row = e / cnt, k = e % cnt;
-      const ML ml = a.part_ml[(base_item * a.NSP + sp0 + k) * rows + row];
-      coef[row][k] = exp2_fast(ml.m - rowmax[row]) / rowden[row];
-    }
-    __syncthreads();
-    for (int k = 0; k < cnt; ++k) {
-      const float* po = a.part_o + (size_t)(base_item * a.NSP + sp0 + k) * rows * D;
-#pragma unroll
-      for (int t = 0; t < EPT; ++t) {
-        const int e = tid + t * 256;
-        if (e < nrows * D) acc[t] += coef[e / D][k] * po[e];
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < EPT; ++t) {
-    const int e = tid + t * 256;
-    if (e < nrows * D) {
-      T* o = out_ptr(e / D);
-      if constexpr (sizeof(T) == 2)
-        o[e % D] = f32_to_bf16(acc[t]);
-      else
-        o[e % D] = acc[t];
+    acc *= 1.f / den;
+    T* o = out_ptr(row) + d;
+    if constexpr (sizeof(T) == 2) {
+      uint2 pk;
+      pk.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+      pk.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+      *reinterpret_cast<uint2*>(o) = pk;
+    } else {
+      *reinterpret_cast<f32x4*>(o) = acc;
     }
   }
 }
@@ -429,13 +510,19 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a, int RT) {
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-struct AttnPlan {
-  int RT, RG, C, NSP;
-  size_t off_o, off_ml, total;
+struct SplitPolicy {
+  int cmin, cmax;  // split length: a power of two in [cmin, cmax]
+  long target;     // aim for about this many work items
 };
 
+static SplitPolicy policy(spec_dtype_t dt) {
+  // bf16: workgroups of one wave per row tile, a few resident per CU; fp32:
+  // single-wave items.
+  return dt == SPEC_BF16 ? SplitPolicy{256, 8192, 4096} : SplitPolicy{128, 4096, 8192};
+}
+
 static int max_rt(spec_dtype_t dt, int D) {
-  if (dt == SPEC_BF16) return 5;
+  if (dt == SPEC_BF16) return 8;  // waves per workgroup
   return D <= 32 ? 4 : (D <= 64 ? 2 : 1);
 }
 
@@ -445,17 +532,22 @@ static bool supported(spec_dtype_t dt, int D) {
   return false;
 }
 
+struct AttnPlan {
+  int RT, RG, C, NSP;
+  size_t off_o, off_ml, total;
+};
+
 static AttnPlan attn_plan(int B, int Hq, int Hkv, int n_q, int D, int hint, spec_dtype_t dt) {
   AttnPlan p{};
   const int M = (Hq / Hkv) * n_q;
   const int tiles = (M + 15) / 16;
   p.RG = (tiles + max_rt(dt, D) - 1) / max_rt(dt, D);
   p.RT = (tiles + p.RG - 1) / p.RG;
-  // Split length: aim at ~8192 waves; a power of two in [128, 4096] keys.
+  const SplitPolicy sp = policy(dt);
   const long keys = (long)B * Hkv * p.RG * (long)(hint + n_q);
-  long want = (keys + 8191) / 8192;
-  int C = 128;
-  while (C < want && C < 4096) C <<= 1;
+  const long want = (keys + sp.target - 1) / sp.target;
+  int C = sp.cmin;
+  while (C < want && C < sp.cmax) C <<= 1;
   p.C = C;
   p.NSP = (hint + n_q + C - 1) / C;
   const size_t items = (size_t)B * Hkv * p.RG * p.NSP;
@@ -468,24 +560,48 @@ static AttnPlan attn_plan(int B, int Hq, int Hkv, int n_q, int D, int hint, spec
   return p;
 }
 
-template <typename T, int D, int RT>
-static hipError_t attn_launch_rt(const AttnArgs& a, hipStream_t s) {
+template <int D, int NW>
+static hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
   const size_t items = (size_t)a.B * a.Hkv * a.RG * a.NSP;
-  hipLaunchKernelGGL((attn_split<T, D, RT>), dim3((unsigned)items), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((attn_split_bf16<D, NW>), dim3((unsigned)items), dim3(64 * NW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine<T, D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a, RT);
+  hipLaunchKernelGGL((attn_combine<uint16_t, D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a, 1);
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t attn_launch_d(const AttnArgs& a, int RT, hipStream_t s) {
-  switch (RT) {
-    case 1: return attn_launch_rt<T, D, 1>(a, s);
-    case 2: return attn_launch_rt<T, D, 2>(a, s);
-    case 3: if constexpr (sizeof(T) == 2 || D <= 32) return attn_launch_rt<T, D, 3>(a, s); else break;
-    case 4: if constexpr (sizeof(T) == 2 || D <= 32) return attn_launch_rt<T, D, 4>(a, s); else break;
-    case 5: if constexpr (sizeof(T) == 2) return attn_launch_rt<T, D, 5>(a, s); else break;
+template <int D>
+static hipError_t launch_bf16_d(const AttnArgs& a, hipStream_t s) {
+  switch (a.RT) {
+    case 1: return launch_bf16<D, 1>(a, s);
+    case 2: return launch_bf16<D, 2>(a, s);
+    case 3: return launch_bf16<D, 3>(a, s);
+    case 4: return launch_bf16<D, 4>(a, s);
+    case 5: return launch_bf16<D, 5>(a, s);
+    case 6: return launch_bf16<D, 6>(a, s);
+    case 7: return launch_bf16<D, 7>(a, s);
+    case 8: return launch_bf16<D, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, int RT>
+static hipError_t launch_f32(const AttnArgs& a, hipStream_t s) {
+  const size_t items = (size_t)a.B * a.Hkv * a.RG * a.NSP;
+  hipLaunchKernelGGL((attn_split_f32<D, RT>), dim3((unsigned)items), dim3(64), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_combine<float, D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a, 0);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_f32_d(const AttnArgs& a, hipStream_t s) {
+  switch (a.RT) {
+    case 1: return launch_f32<D, 1>(a, s);
+    case 2: return launch_f32<D, 2>(a, s);
+    case 3: if constexpr (D <= 32) return launch_f32<D, 3>(a, s); else break;
+    case 4: if constexpr (D <= 32) return launch_f32<D, 4>(a, s); else break;
     default: break;
   }
   return hipErrorInvalidValue;
@@ -500,14 +616,16 @@ extern "C" size_t spec_verify_attention_workspace_size(int B, int Hq, int Hkv, i
   if (B < 1 || Hq < 1 || Hkv < 1 || n_q < 1 || n_q > 16 || D < 1 || max_len_hint < 0) return 0;
   if (Hq % Hkv != 0 || (Hq / Hkv) * n_q > 256 || !supported(dtype, D)) return 0;
   // Bound on the split count over every hint h' <= max_len_hint: the split
-  // length C(h') is a power of two in [128, 4096] no smaller than
-  // K (h' + n_q) / 8192, so NSP(h') <= ceil(8192 / K) unless C is capped at
-  // 4096, and NSP(h') <= ceil((h' + n_q) / 128) always.  Both are monotone.
+  // length C(h') is a power of two in [cmin, cmax] no smaller than
+  // K (h' + n_q) / target, so NSP(h') <= ceil(target / K) unless C is capped
+  // at cmax, and NSP(h') <= ceil((h' + n_q) / cmin) always.  Both bounds grow
+  // with the hint.
   const AttnPlan p = attn_plan(B, Hq, Hkv, n_q, D, max_len_hint, dtype);
+  const SplitPolicy sp = policy(dtype);
   const long K = (long)B * Hkv * p.RG;
   const long span = (long)max_len_hint + n_q;
-  long nsp = std::max((8192 + K - 1) / K, (span + 4095) / 4096);
-  nsp = std::min(nsp, (span + 127) / 128);
+  long nsp = std::max((sp.target + K - 1) / K, (span + sp.cmax - 1) / sp.cmax);
+  nsp = std::min(nsp, (span + sp.cmin - 1) / sp.cmin);
   nsp = std::max(nsp, (long)p.NSP);
   const size_t items = (size_t)K * nsp;
   return align256(sizeof(float) * items * 16 * p.RT * D) + align256(sizeof(ML) * items * 16 * p.RT);
@@ -550,6 +668,7 @@ extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new,
   a.G = Hq / Hkv;
   a.M = a.G * n_q;
   a.RG = p.RG;
+  a.RT = p.RT;
   a.NSP = p.NSP;
   a.C = p.C;
   a.max_T = max_T;
@@ -558,13 +677,13 @@ extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new,
 
   hipError_t e = hipErrorInvalidValue;
   if (dtype == SPEC_BF16) {
-    if (D == 128) e = attn_launch_d<uint16_t, 128>(a, p.RT, stream);
-    else if (D == 64) e = attn_launch_d<uint16_t, 64>(a, p.RT, stream);
+    if (D == 128) e = launch_bf16_d<128>(a, stream);
+    else if (D == 64) e = launch_bf16_d<64>(a, stream);
   } else {
-    if (D == 24) e = attn_launch_d<float, 24>(a, p.RT, stream);
-    else if (D == 32) e = attn_launch_d<float, 32>(a, p.RT, stream);
-    else if (D == 64) e = attn_launch_d<float, 64>(a, p.RT, stream);
-    else if (D == 128) e = attn_launch_d<float, 128>(a, p.RT, stream);
+    if (D == 24) e = launch_f32_d<24>(a, stream);
+    else if (D == 32) e = launch_f32_d<32>(a, stream);
+    else if (D == 64) e = launch_f32_d<64>(a, stream);
+    else if (D == 128) e = launch_f32_d<128>(a, stream);
   }
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
 }

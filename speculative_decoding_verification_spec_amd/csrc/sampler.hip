@@ -12,20 +12,21 @@
 // judging positions past the first rejection changes nothing but wasted work,
 // and the data-parallel pass reads every logit exactly once.
 //
-// Three kernels, one wave = one unit of work:
+// Four kernels; the hand-offs between them are kernel boundaries (a
+// cross-workgroup hand-off inside a kernel would need device-scope release /
+// acquire, which on this chip writes back and invalidates the per-XCD L2):
 //   rs_stats    wave (b, row, segment): max and sum of exp((z - max)/T) over a
 //               segment of one target or draft row.
-//   rs_finalize wave b: merges the segments of all 2*gamma+1 rows, evaluates
-//               p_i(x_i), q_i(x_i), the accept tests and n.
+//   rs_finalize workgroup b: merges the segments of all 2*gamma+1 rows,
+//               evaluates p_i(x_i), q_i(x_i), the accept tests and n.
 //   rs_resolve  wave (b, segment) of the decided row n: residual weights
 //               max(0, p_n - q_n) (or p_gamma for the bonus) summed per
-//               segment; the last wave of b locates the segment where the
-//               fp64 prefix sum first exceeds u * total, re-scans that segment
-//               and writes the emitted tokens.
-// Both merge steps are in fp64 and in a fixed order, so results do not depend
-// on which wave arrives last.  No workspace word is read before this call has
-// written it (the resolve counters are cleared by rs_finalize), so a workspace
-// needs no initialisation and may be shared by calls of different sizes.
+//               segment.
+//   rs_draw     wave b: locates the segment where the fp64 prefix sum first
+//               exceeds u * total, re-scans it and writes the emitted tokens.
+// Every merge is in fp64 and in a fixed order.  No workspace word is read
+// before this call has written it, so a workspace needs no initialisation and
+// may be shared by calls of different sizes.
 #include <math.h>
 #include <stdint.h>
 
@@ -165,26 +166,26 @@ __global__ __launch_bounds__(256) void rs_stats(const T* __restrict__ tgt, const
   }
 }
 
-// One wave per sequence: merge the segments of all 2*gamma+1 rows (fp64),
-// evaluate p_i(x_i), q_i(x_i) and the accept tests, find n, record the decided
-// row's statistics for the resolve pass and clear its completion counter.
+// One workgroup per sequence: its waves merge the segments of the 2*gamma+1
+// rows (fp64, fixed order) into LDS; then one wave evaluates p_i(x_i),
+// q_i(x_i) and the accept tests, finds n and records the decided row's
+// statistics for the resolve pass.
 template <typename T>
 __global__ __launch_bounds__(256) void rs_finalize(const T* __restrict__ tgt, const T* __restrict__ drf,
                                                    const int32_t* __restrict__ xtok, const double* __restrict__ uni,
                                                    int B, int G, int V, int nseg, float c32, double c64,
                                                    const RowPart* __restrict__ part, SeqState* __restrict__ st,
-                                                   uint32_t* __restrict__ ctr, int32_t* __restrict__ n_out,
-                                                   int32_t* __restrict__ tok_out, float* __restrict__ p_out,
-                                                   float* __restrict__ q_out) {
+                                                   int32_t* __restrict__ n_out, int32_t* __restrict__ tok_out,
+                                                   float* __restrict__ p_out, float* __restrict__ q_out) {
+  __shared__ float rowM[64];
+  __shared__ double rowS[64];
   const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwave = blockDim.x / kWave;
   const int R = 2 * G + 1;
-  const long b = (long)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (b >= B) return;
-  // merge the segments row by row (fp64); lane r keeps row r's statistics
+  const int b = blockIdx.x;
   const RowPart* pb = part + (size_t)b * R * nseg;
-  float myM = neg_inf_f();
-  double myS = 0.0;
-  for (int rr = 0; rr < R; ++rr) {
+  for (int rr = wave; rr < R; rr += nwave) {
     float mm = neg_inf_f();
     for (int k = lane; k < nseg; k += kWave) mm = fmaxf(mm, pb[rr * nseg + k].M);
     mm = wave_max(mm);
@@ -196,17 +197,14 @@ __global__ __launch_bounds__(256) void rs_finalize(const T* __restrict__ tgt, co
       }
     }
     ss = wave_sum(ss);
-    if (lane == rr) {
-      myM = mm;
-      myS = ss;
+    if (lane == 0) {
+      rowM[rr] = mm;
+      rowS[rr] = ss;
     }
   }
-  // Lane i < G judges position i: target row i is held by lane i, draft row i
-  // by lane G + 1 + i.
-  const float Mt_i = __shfl(myM, lane < G ? lane : 0, kWave);
-  const double St_i = __shfl(myS, lane < G ? lane : 0, kWave);
-  const float Md_i = __shfl(myM, lane < G ? lane + G + 1 : 0, kWave);
-  const double Sd_i = __shfl(myS, lane < G ? lane + G + 1 : 0, kWave);
+  __syncthreads();
+  if (wave != 0) return;
+  // Lane i < G judges position i against target row i and draft row G+1+i.
   bool bad = false, reject = false;
   if (lane < G) {
     const int x = xtok[(size_t)b * G + lane];
@@ -216,8 +214,8 @@ __global__ __launch_bounds__(256) void rs_finalize(const T* __restrict__ tgt, co
     } else {
       const double zt = (double)to_f32<T>(tgt[((size_t)b * (G + 1) + lane) * V + x]);
       const double zd = (double)to_f32<T>(drf[((size_t)b * G + lane) * V + x]);
-      p = exp2((zt - (double)Mt_i) * c64) / St_i;
-      q = exp2((zd - (double)Md_i) * c64) / Sd_i;
+      p = exp2((zt - (double)rowM[lane]) * c64) / rowS[lane];
+      q = exp2((zd - (double)rowM[G + 1 + lane]) * c64) / rowS[G + 1 + lane];
       const double u = uni[(size_t)b * (G + 1) + lane];
       // u < min(1, p/q): q = 0 < p gives +inf (accept), p = q = 0 gives NaN
       // (reject), exactly as the IEEE comparison with a NaN-propagating min.
@@ -230,21 +228,16 @@ __global__ __launch_bounds__(256) void rs_finalize(const T* __restrict__ tgt, co
   const uint64_t rej_mask = __ballot(reject);
   const uint64_t bad_mask = __ballot(bad);
   const int n = rej_mask ? (__ffsll((long long)rej_mask) - 1) : G;
-  const float Mt_n = __shfl(myM, n, kWave);
-  const double St_n = __shfl(myS, n, kWave);
-  const float Md_n = __shfl(myM, n < G ? G + 1 + n : 0, kWave);
-  const double Sd_n = __shfl(myS, n < G ? G + 1 + n : 0, kWave);
   if (lane == 0) {
     SeqState s_;
     s_.n = n;
     s_.valid = bad_mask ? 0 : 1;
-    s_.Mt = Mt_n;
-    s_.St = St_n;
-    s_.Md = Md_n;
-    s_.Sd = Sd_n;
+    s_.Mt = rowM[n];
+    s_.St = rowS[n];
+    s_.Md = n < G ? rowM[G + 1 + n] : 0.f;
+    s_.Sd = n < G ? rowS[G + 1 + n] : 1.0;
     st[b] = s_;
     n_out[b] = bad_mask ? -1 : n;
-    ctr[b] = 0u;  // the resolve pass counts its waves here
   }
   if (bad_mask && lane <= G) tok_out[(size_t)b * (G + 1) + lane] = -1;
 }
@@ -287,11 +280,9 @@ __device__ __forceinline__ void lane_weights(const T* __restrict__ rt, const T* 
 }
 
 template <typename T, int VEC, int NIT>
-__global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, const T* __restrict__ drf,
-                                                  const int32_t* __restrict__ xtok, const double* __restrict__ uni,
-                                                  int B, int G, int V, int nseg, float c32,
-                                                  const SeqState* __restrict__ st, double2* __restrict__ part,
-                                                  uint32_t* __restrict__ ctr, int32_t* __restrict__ tok_out) {
+__global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, const T* __restrict__ drf, int B, int G,
+                                                  int V, int nseg, float c32, const SeqState* __restrict__ st,
+                                                  double2* __restrict__ part) {
   constexpr int E = VEC * NIT;  // contiguous elements per lane
   constexpr int SEG = kWave * E;
   const int lane = threadIdx.x & (kWave - 1);
@@ -300,22 +291,16 @@ __global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, con
   const int seg = (int)(gw % nseg);
   const int b = (int)(gw / nseg);
   const SeqState s = st[b];
-  if (!s.valid || s.n < 0 || s.n > G) {
-    if (lane == 0) part[gw] = make_double2(0.0, 0.0);
-    if (wave_arrive_last(&ctr[b], (uint32_t)nseg, lane) && lane == 0) ctr[b] = 0u;
-    return;
-  }
+  if (!s.valid || s.n < 0 || s.n > G) return;  // rs_draw skips this sequence
   const int n = s.n;
   const bool resid = n < G;
   const T* rt = tgt + ((size_t)b * (G + 1) + n) * V;
   const T* rd = resid ? drf + ((size_t)b * G + n) * V : rt;
   const float inv_st = (float)(1.0 / s.St), inv_sd = (float)(1.0 / s.Sd);
-
-  // Segment sums: lane-private sequential fp64 accumulation (the re-scan
-  // below repeats it element by element), then a fixed-order lane scan.
+  // Segment sums: lane-private sequential fp64 accumulation (rs_draw repeats
+  // it element by element), then a fixed-order lane scan.
   float w[E], pw[E];
-  const int idx0 = seg * SEG + lane * E;
-  lane_weights<T, VEC, NIT, true>(rt, rd, idx0, V, c32, s.Mt, inv_st, s.Md, inv_sd, resid, w, pw);
+  lane_weights<T, VEC, NIT, true>(rt, rd, seg * SEG + lane * E, V, c32, s.Mt, inv_st, s.Md, inv_sd, resid, w, pw);
   double lw = 0.0, lp = 0.0;
 #pragma unroll
   for (int k = 0; k < E; ++k) {
@@ -325,10 +310,29 @@ __global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, con
   const double segw = __shfl(wave_inclusive_scan(lw, lane), kWave - 1, kWave);
   const double segp = __shfl(wave_inclusive_scan(lp, lane), kWave - 1, kWave);
   if (lane == 0) part[gw] = make_double2(segw, segp);
+}
 
-  if (!wave_arrive_last(&ctr[b], (uint32_t)nseg, lane)) return;
+// One wave per sequence: fp64 total of the segment sums, the first segment
+// whose prefix exceeds u * total, then the first token inside it.
+template <typename T, int VEC, int NIT>
+__global__ __launch_bounds__(256) void rs_draw(const T* __restrict__ tgt, const T* __restrict__ drf,
+                                               const int32_t* __restrict__ xtok, const double* __restrict__ uni,
+                                               int B, int G, int V, int nseg, float c32,
+                                               const SeqState* __restrict__ st, const double2* __restrict__ part,
+                                               int32_t* __restrict__ tok_out) {
+  constexpr int E = VEC * NIT;
+  constexpr int SEG = kWave * E;
+  const int lane = threadIdx.x & (kWave - 1);
+  const long b = (long)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (b >= B) return;
+  const SeqState s = st[b];
+  if (!s.valid || s.n < 0 || s.n > G) return;  // tokens already set to -1
+  const int n = s.n;
+  const bool resid = n < G;
+  const T* rt = tgt + ((size_t)b * (G + 1) + n) * V;
+  const T* rd = resid ? drf + ((size_t)b * G + n) * V : rt;
+  const float inv_st = (float)(1.0 / s.St), inv_sd = (float)(1.0 / s.Sd);
 
-  // ---- last wave of sequence b: locate the draw --------------------------
   const double2* pb = part + (size_t)b * nseg;
   double W = 0.0;  // fixed-order fp64 total of the weights
   for (int c0 = 0; c0 < nseg; c0 += kWave) {
@@ -367,9 +371,10 @@ __global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, con
   const bool from_last = kseg < 0;  // the target reached the total by rounding
   if (from_last) kseg = last_pos < 0 ? 0 : last_pos;
 
-  // Re-scan the chosen segment with the same per-lane weights.
+  // Re-scan the chosen segment with the same per-lane weights (with the
+  // fallback, the weights are p itself: residual switched off).
+  float w[E], pw[E];
   const int j0 = kseg * SEG + lane * E;
-  // With the fallback, the weights are p itself (residual switched off).
   lane_weights<T, VEC, NIT, false>(rt, rd, j0, V, c32, s.Mt, inv_st, s.Md, inv_sd, resid && !use_p, w, pw);
   double l2 = 0.0;
 #pragma unroll
@@ -392,7 +397,6 @@ __global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, con
   if (lane < n) ob[lane] = xtok[(size_t)b * G + lane];
   if (lane == n) ob[lane] = t;
   if (lane > n && lane <= G) ob[lane] = -1;
-  if (lane == 0) ctr[b] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -403,7 +407,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct RsPlan {
   int vec, nit, seg, nseg;
-  size_t off_part1, off_state, off_part2, off_ctr2, total;
+  size_t off_part1, off_state, off_part2, total;
 };
 
 static int pick_vec(int V, int esize, uintptr_t a, uintptr_t b) {
@@ -429,8 +433,6 @@ static RsPlan rs_plan(int B, int G, int V, int esize, int vec) {
   off = align256(off + sizeof(SeqState) * (size_t)B);
   p.off_part2 = off;
   off = align256(off + sizeof(double2) * (size_t)B * p.nseg);
-  p.off_ctr2 = off;
-  off = align256(off + sizeof(uint32_t) * (size_t)B);
   p.total = off;
   return p;
 }
@@ -446,18 +448,20 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
   RowPart* part1 = reinterpret_cast<RowPart*>(ws + pl.off_part1);
   SeqState* state = reinterpret_cast<SeqState*>(ws + pl.off_state);
   double2* part2 = reinterpret_cast<double2*>(ws + pl.off_part2);
-  uint32_t* ctr2 = reinterpret_cast<uint32_t*>(ws + pl.off_ctr2);
   hipLaunchKernelGGL((rs_stats<T, VEC, NIT>), dim3((unsigned)((waves1 + WPB - 1) / WPB)), dim3(256), 0, stream,
                      (const T*)tgt, (const T*)drf, B, G, V, pl.nseg, c32, part1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rs_finalize<T>), dim3((unsigned)((B + WPB - 1) / WPB)), dim3(256), 0, stream, (const T*)tgt,
-                     (const T*)drf, x, u, B, G, V, pl.nseg, c32, c64, part1, state, ctr2, n_out, tok_out, p_out,
-                     q_out);
+  hipLaunchKernelGGL((rs_finalize<T>), dim3((unsigned)B), dim3(256), 0, stream, (const T*)tgt, (const T*)drf, x, u, B,
+                     G, V, pl.nseg, c32, c64, part1, state, n_out, tok_out, p_out, q_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((rs_resolve<T, VEC, NIT>), dim3((unsigned)((waves2 + WPB - 1) / WPB)), dim3(256), 0, stream,
-                     (const T*)tgt, (const T*)drf, x, u, B, G, V, pl.nseg, c32, state, part2, ctr2, tok_out);
+                     (const T*)tgt, (const T*)drf, B, G, V, pl.nseg, c32, state, part2);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rs_draw<T, VEC, NIT>), dim3((unsigned)((B + WPB - 1) / WPB)), dim3(256), 0, stream,
+                     (const T*)tgt, (const T*)drf, x, u, B, G, V, pl.nseg, c32, state, part2, tok_out);
   return hipGetLastError();
 }
 

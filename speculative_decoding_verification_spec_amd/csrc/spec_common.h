@@ -68,17 +68,4 @@ __device__ __forceinline__ double wave_inclusive_scan(double v, int lane) {
   return v;
 }
 
-// Release this wave's prior global writes, then count it in `*counter`.
-// Returns true in every lane of the one wave that arrives last (the count
-// reaches `total`); that wave also performs the acquire side.
-__device__ __forceinline__ bool wave_arrive_last(uint32_t* counter, uint32_t total, int lane) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  uint32_t old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  old = __shfl(old, 0, kWave);
-  const bool last = (old == total - 1);
-  if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  return last;
-}
-
 }  // namespace specv
