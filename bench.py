@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--temperature", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the verification step has no multi-GPU "
@@ -138,6 +140,18 @@ def main():
 
     import speculative_decoding_verification_spec_amd as sv
     import workloads as W
+
+    if args.copy_calibration:
+        # A plain device-to-device copy of known size: its FETCH_SIZE / WRITE_SIZE
+        # per launch is the scale for the byte counters of the path's kernels.
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 5}))
+        return
 
     if not os.path.exists(sv.LIB_PATH):
         import __graft_entry__

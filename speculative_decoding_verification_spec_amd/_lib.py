@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+# SPECV_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("SPECV_LIB") or os.path.join(_HERE, "libspecverify.so")
 
 SPEC_OK, SPEC_ERR_ARG, SPEC_ERR_OVERFLOW, SPEC_ERR_UNSUPPORTED, SPEC_ERR_LAUNCH = range(5)
 SPEC_F32, SPEC_BF16 = 0, 1

@@ -50,6 +50,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "spec_common.h"
 #include "spec_verify.h"
@@ -163,12 +164,75 @@ struct BfLayout {
   __device__ static int vslot(int row, int c) { return c ^ (2 * ((row / RP) % (CH / 2))); }
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_split_bf16(AttnArgs a) {
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier without a global memory fence.  __syncthreads() also
+// fences, which makes the compiler wait for every outstanding global_load_lds
+// copy, including those of later blocks still meant to be in flight.  Here
+// each wave has already waited for its own copies of the current block; it
+// drains its own LDS reads (so none of them can still be reading a stage
+// another wave is about to refill) and the asm statements keep the compiler
+// from moving LDS accesses across the barrier.
+__device__ __forceinline__ void block_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// Max / sum across the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48) with the gfx950 lane-swap instructions: swapping a register with
+// itself across 16-lane (32-lane) halves hands every lane its partner's value.
+__device__ __forceinline__ float group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+#ifndef SPECV_ATTN_WPE
+#define SPECV_ATTN_WPE 1
+#endif
+
+template <int D, int NW, int NST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_ATTN_WPE)))
+void attn_split_bf16(AttnArgs a) {
   using LY = BfLayout<D>;
   constexpr int DS = D / 32;  // MFMA steps over D for the scores
   constexpr int DT = D / 16;  // 16-wide output tiles over D
-  __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2][LY::TILE];  // [stage][K,V]
+  constexpr int NCP = 2 * LY::NI;                             // 1 KB copies per block (K then V)
+  constexpr int WI = NW >= 4 ? 4 : (NW >= 2 ? 2 : 1);         // waves that issue copies
+  constexpr int CPW = NCP / WI;                               // copies per issuing wave per block
+  static_assert(NCP % WI == 0, "copies must split evenly over the issuing waves");
+  static_assert(NST >= 2 && NST <= 3 && (NST - 2) * CPW <= 63, "stages");
+  // One LDS object per stage and tensor: reads of one stage then provably do
+  // not alias the asynchronous copies into another, so the compiler does not
+  // make them wait for those copies.
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[LY::TILE], v0s[LY::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k1s[LY::TILE], v1s[LY::TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k2s[NST > 2 ? LY::TILE : 8], v2s[NST > 2 ? LY::TILE : 8];
+  auto kbuf = [&](auto S) -> uint16_t* {
+    if constexpr (decltype(S)::value == 0) return k0s;
+    else if constexpr (decltype(S)::value == 1) return k1s;
+    else return k2s;
+  };
+  auto vbuf = [&](auto S) -> uint16_t* {
+    if constexpr (decltype(S)::value == 0) return v0s;
+    else if constexpr (decltype(S)::value == 1) return v1s;
+    else return v2s;
+  };
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -188,29 +252,43 @@ __global__ __launch_bounds__(64 * NW) void attn_split_bf16(AttnArgs a) {
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
   const uint16_t* kn = static_cast<const uint16_t*>(a.kn);
   const uint16_t* vn = static_cast<const uint16_t*>(a.vn);
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kc);
-  const uint16_t* vc = static_cast<const uint16_t*>(a.vc);
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (size_t)it.bg * a.max_T * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + (size_t)it.bg * a.max_T * D;
+  const uint16_t* knb = kn + (size_t)it.bg * a.n_q * D;
+  const uint16_t* vnb = vn + (size_t)it.bg * a.n_q * D;
 
-  // Copies of one block: copy c of the 2*NI (first NI for K, then NI for V)
-  // is issued by wave c % NW; lane l fills LDS slot (64 c' + l) of its tile
-  // (c' = c mod NI), i.e. row (64 c' + l) / CH at swizzled slot (64 c' + l) % CH.
+  // Copies of one block: copy c (first NI for K, then NI for V) is issued by
+  // wave c % WI; lane l fills LDS slot (64 c' + l) of its tile (c' = c mod
+  // NI), i.e. row (64 c' + l) / CH at swizzled slot (64 c' + l) % CH.  Every
+  // issuing wave issues CPW copies per block, so a fixed vmcnt tells it when
+  // an older block has landed.
   auto copy_tile = [&](const uint16_t* cache, const uint16_t* fresh, uint16_t* dst, int kb, int cc, bool is_v) {
     const int p = cc * kWave + lane;
     const int row = p / LY::CH, sl = p % LY::CH;
     const int chunk = is_v ? LY::vslot(row, sl) : LY::kslot(row, sl);  // XOR is its own inverse
-    const uint16_t* src = key_row<uint16_t>(cache, fresh, kb + row, L, Ltot, a.n_q, a.max_T, D, it.bg);
-    if (!src) src = fresh + (size_t)it.bg * a.n_q * D;  // finite dummy row for masked keys
+    const int key = kb + row;
+    const uint16_t* src;
+    if (kb + KB <= L) {
+      src = cache + (size_t)key * D;  // the whole block is committed cache
+    } else {
+      // new rows from k_new/v_new; keys past the end read a finite dummy row
+      src = key < L ? cache + (size_t)key * D : fresh + (size_t)(key < Ltot ? key - L : 0) * D;
+    }
     __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + 8 * chunk),
                                      (void __attribute__((address_space(3)))*)(dst + cc * 512), 16, 0, 0);
   };
-  auto issue_block = [&](int kb, int stage) {
-    for (int c = wave; c < LY::NI; c += NW) copy_tile(kc, kn, lds[stage][0], kb, c, false);
-    for (int c = (wave + NW - LY::NI % NW) % NW; c < LY::NI; c += NW) copy_tile(vc, vn, lds[stage][1], kb, c, true);
+  auto issue_block = [&](int kb, auto S) {
+    if (wave < WI) {
+#pragma unroll
+      for (int i = 0; i < CPW; ++i) {
+        const int c = wave + i * WI;
+        if (c < LY::NI)
+          copy_tile(kc, knb, kbuf(S), kb, c, false);
+        else
+          copy_tile(vc, vnb, vbuf(S), kb, c - LY::NI, true);
+      }
+    }
   };
-
-  issue_block(k0, 0);
-
-  if (it.sp == 0 && it.rg == 0) append_rows<uint16_t, D>(a, it.bg, L, tid, 64 * NW);
 
   // Query fragment of this wave's tile (B operand of S^T = K Q^T).
   const int m = it.rg * 16 * NW + 16 * wave + lr;
@@ -226,22 +304,31 @@ __global__ __launch_bounds__(64 * NW) void attn_split_bf16(AttnArgs a) {
       qf[s] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg) : bf16x8{};
   }
 
+  issue_block(k0, IC<0>{});
+  if constexpr (NST > 2) {
+    if (nblk > 1) issue_block(k0 + KB, IC<1>{});
+  }
+
   float mrow = neg_inf_f(), lsum = 0.f;
   f32x4 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int j = 0; j < nblk; ++j) {
+  // Block j lives in stage S = j mod NST.
+  auto step = [&](auto S, int j) {
     const int kb = k0 + j * KB;
-    const int stage = j & 1;
-    // This wave's copies of block j are complete; after the barrier every
-    // wave's are, and every wave has finished reading block j-1's stage.
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < nblk) issue_block(kb + KB, stage ^ 1);
+    // This wave's copies of block j have landed (only blocks issued after it
+    // may still be in flight); after the barrier every wave's have, and every
+    // wave has finished reading the stage the next copy refills.
+    if (NST > 2 && j + 1 < nblk)
+      wait_vmcnt<(NST > 2 ? CPW : 0)>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();
+    if (j + NST - 1 < nblk) issue_block(kb + (NST - 1) * KB, IC<(decltype(S)::value + NST - 1) % NST>{});
 
-    const uint16_t* ks = lds[stage][0];
-    const uint16_t* vs = lds[stage][1];
+    const uint16_t* ks = kbuf(S);
+    const uint16_t* vs = vbuf(S);
     // Scores: lane holds keys kb + 16 kt + 4 lg + jj of row lr of the tile.
     float sc[8];
 #pragma unroll
@@ -265,7 +352,21 @@ __global__ __launch_bounds__(64 * NW) void attn_split_bf16(AttnArgs a) {
           if (key >= Ltot || key > lim) sc[4 * kt + jj] = neg_inf_f();
         }
     }
-    const float alpha = softmax_update(sc, mrow, lsum);
+    // Online softmax in the log2 domain.
+    float mx = sc[0];
+#pragma unroll
+    for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
+    const float mnew = fmaxf(mrow, group_max(mx));
+    const bool none = (mnew == neg_inf_f());
+    const float alpha = none ? 1.f : exp2_fast(mrow - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      sc[jj] = none ? 0.f : exp2_fast(sc[jj] - mnew);
+      ps += sc[jj];
+    }
+    lsum = lsum * alpha + ps;
+    mrow = mnew;
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
@@ -274,8 +375,8 @@ __global__ __launch_bounds__(64 * NW) void attn_split_bf16(AttnArgs a) {
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) pf[jj] = (__bf16)sc[jj];
 
-    // V^T fragments: half h covers keys 16 h + 4 lg + (0..3); lane lr of the
-    // group points at V[16 h + 4 lg + lr/4][16 dt + 4 (lr%4)].
+    // V^T fragments: half hh covers keys 16 hh + 4 lg + (0..3); lane lr of
+    // the group points at V[16 hh + 4 lg + lr/4][16 dt + 4 (lr%4)].
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       s16x4 v2[2];
@@ -290,13 +391,21 @@ __global__ __launch_bounds__(64 * NW) void attn_split_bf16(AttnArgs a) {
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
     }
+  };
+
+  for (int j = 0; j < nblk; j += NST) {
+    step(IC<0>{}, j);
+    if (j + 1 < nblk) step(IC<1>{}, j + 1);
+    if constexpr (NST > 2) {
+      if (j + 2 < nblk) step(IC<2>{}, j + 2);
+    }
   }
 
-  // Row sum over the 4 lane groups.
-  float lt = lsum;
-  lt += __shfl_xor(lt, 16, kWave);
-  lt += __shfl_xor(lt, 32, kWave);
-  const int row = 16 * wave + lr;  // row within the item
+  // A1 (once per (b, g)); nothing in this launch reads these rows.
+  if (it.sp == 0 && it.rg == 0) append_rows<uint16_t, D>(a, it.bg, L, tid, 64 * NW);
+
+  const float lt = group_sum(lsum);  // row sum over the 4 lane groups
+  const int row = 16 * wave + lr;    // row within the item
   if (single) {
     // The whole of (b, g, rg) is here: normalise and write the output.
     if (valid) {
@@ -515,10 +624,17 @@ struct SplitPolicy {
   long target;     // aim for about this many work items
 };
 
+#ifndef SPECV_ATTN_ITEMS
+#define SPECV_ATTN_ITEMS 2048
+#endif
+#ifndef SPECV_ATTN_CMAX
+#define SPECV_ATTN_CMAX 8192
+#endif
+
 static SplitPolicy policy(spec_dtype_t dt) {
   // bf16: workgroups of one wave per row tile, a few resident per CU; fp32:
   // single-wave items.
-  return dt == SPEC_BF16 ? SplitPolicy{256, 8192, 4096} : SplitPolicy{128, 4096, 8192};
+  return dt == SPEC_BF16 ? SplitPolicy{256, SPECV_ATTN_CMAX, SPECV_ATTN_ITEMS} : SplitPolicy{128, 4096, 8192};
 }
 
 static int max_rt(spec_dtype_t dt, int D) {
@@ -560,10 +676,15 @@ static AttnPlan attn_plan(int B, int Hq, int Hkv, int n_q, int D, int hint, spec
   return p;
 }
 
+#ifndef SPECV_ATTN_STAGES
+#define SPECV_ATTN_STAGES 3
+#endif
+constexpr int kStages = SPECV_ATTN_STAGES;  // LDS stages; blocks in flight per workgroup: kStages - 1
+
 template <int D, int NW>
 static hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
   const size_t items = (size_t)a.B * a.Hkv * a.RG * a.NSP;
-  hipLaunchKernelGGL((attn_split_bf16<D, NW>), dim3((unsigned)items), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((attn_split_bf16<D, NW, kStages>), dim3((unsigned)items), dim3(64 * NW), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_combine<uint16_t, D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a, 1);

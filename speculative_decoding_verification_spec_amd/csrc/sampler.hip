@@ -30,6 +30,12 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
+#ifndef SPECV_RS_LANE_BYTES
+#define SPECV_RS_LANE_BYTES 64
+#endif
+
 #include "spec_common.h"
 #include "spec_verify.h"
 
@@ -283,8 +289,7 @@ template <typename T, int VEC, int NIT>
 __global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, const T* __restrict__ drf, int B, int G,
                                                   int V, int nseg, float c32, const SeqState* __restrict__ st,
                                                   double2* __restrict__ part) {
-  constexpr int E = VEC * NIT;  // contiguous elements per lane
-  constexpr int SEG = kWave * E;
+  constexpr int SEG = kWave * VEC * NIT;
   const int lane = threadIdx.x & (kWave - 1);
   const long gw = (long)blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (gw >= (long)B * nseg) return;
@@ -297,15 +302,31 @@ __global__ __launch_bounds__(256) void rs_resolve(const T* __restrict__ tgt, con
   const T* rt = tgt + ((size_t)b * (G + 1) + n) * V;
   const T* rd = resid ? drf + ((size_t)b * G + n) * V : rt;
   const float inv_st = (float)(1.0 / s.St), inv_sd = (float)(1.0 / s.Sd);
-  // Segment sums: lane-private sequential fp64 accumulation (rs_draw repeats
-  // it element by element), then a fixed-order lane scan.
-  float w[E], pw[E];
-  lane_weights<T, VEC, NIT, true>(rt, rd, seg * SEG + lane * E, V, c32, s.Mt, inv_st, s.Md, inv_sd, resid, w, pw);
+  // Segment sums with coalesced loads (iteration it covers 64*VEC consecutive
+  // elements).  rs_draw re-scans the chosen segment in index order; the two
+  // summation orders agree to rounding, which only matters for a draw that
+  // sits within rounding of a segment boundary (inside the 1e-6 band).
+  const float mt_c = s.Mt, md_c = s.Md;
   double lw = 0.0, lp = 0.0;
+  const int s0 = seg * SEG;
 #pragma unroll
-  for (int k = 0; k < E; ++k) {
-    lw += (double)w[k];
-    lp += (double)pw[k];
+  for (int it = 0; it < NIT; ++it) {
+    const int idx = s0 + (it * kWave + lane) * VEC;
+    if (idx < V) {
+      float zt[VEC], zd[VEC];
+      load_vec<T, VEC>(rt + idx, zt);
+      if (resid) load_vec<T, VEC>(rd + idx, zd);
+      float sw = 0.f, sp = 0.f;
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        const float p = exp2_fast((zt[k] - mt_c) * c32) * inv_st;
+        const float w = resid ? fmaxf(p - exp2_fast((zd[k] - md_c) * c32) * inv_sd, 0.f) : p;
+        sw += w;
+        sp += p;
+      }
+      lw += (double)sw;
+      lp += (double)sp;
+    }
   }
   const double segw = __shfl(wave_inclusive_scan(lw, lane), kWave - 1, kWave);
   const double segp = __shfl(wave_inclusive_scan(lp, lane), kWave - 1, kWave);
@@ -422,7 +443,8 @@ static RsPlan rs_plan(int B, int G, int V, int esize, int vec) {
   RsPlan p{};
   p.vec = vec;
   // about 64 bytes of each row per lane per segment
-  p.nit = (vec * esize >= 16) ? 4 : (vec * esize >= 8 ? 8 : 16);
+  // SPECV_RS_LANE_BYTES bytes of each row per lane per segment
+  p.nit = std::max(1, SPECV_RS_LANE_BYTES / (vec * esize));
   p.seg = kWave * vec * p.nit;
   p.nseg = (V + p.seg - 1) / p.seg;
   const int R = 2 * G + 1;
@@ -472,15 +494,16 @@ static hipError_t rs_dispatch(const RsPlan& pl, const void* tgt, const void* drf
 #define RS_CASE(VEC_, NIT_)                                                                                     \
   if (pl.vec == VEC_ && pl.nit == NIT_)                                                                         \
     return rs_launch<T, VEC_, NIT_>(pl, tgt, drf, x, u, B, G, V, c32, c64, ws, n_out, tok_out, p_out, q_out, s);
+  constexpr int LB = SPECV_RS_LANE_BYTES;
   if constexpr (sizeof(T) == 2) {
-    RS_CASE(8, 4)
-    RS_CASE(4, 8)
-    RS_CASE(2, 16)
-    RS_CASE(1, 16)
+    RS_CASE(8, LB / 16)
+    RS_CASE(4, LB / 8)
+    RS_CASE(2, LB / 4)
+    RS_CASE(1, LB / 2)
   } else {
-    RS_CASE(4, 4)
-    RS_CASE(2, 8)
-    RS_CASE(1, 16)
+    RS_CASE(4, LB / 16)
+    RS_CASE(2, LB / 8)
+    RS_CASE(1, LB / 4)
   }
 #undef RS_CASE
   return hipErrorInvalidValue;
