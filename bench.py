@@ -120,6 +120,28 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
     }
 
 
+def copy_ceiling(torch, nbytes=2 << 30, reps=5):
+    """Achieved HBM bytes/s of a plain 2 GiB device-to-device copy (read + write).
+
+    A practical ceiling beside the 8 TB/s specification peak: the fraction
+    of it that the path's kernels reach is reported too.
+    """
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB/s": gbs, "what": "torch device-to-device copy of 2 GiB, bytes read + written per second"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -260,6 +282,7 @@ def main():
             "mean_accepted": float(n_last.mean()),
         },
     }
+    res["copy_ceiling"] = copy_ceiling(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         att0, smp0 = sets[0]

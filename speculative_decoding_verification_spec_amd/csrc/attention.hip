@@ -81,15 +81,19 @@ struct AttnArgs {
   float qk_scale;  // scale * log2(e)
 };
 
-// Decode blockIdx into (b, g, rg, sp); sp varies fastest.
+// Decode blockIdx into (b, g, rg, sp); sp varies fastest, so consecutive
+// workgroups stream neighbouring parts of one (b, g) slab.  Partials are
+// stored at this index, id = ((b Hkv + g) RG + rg) NSP + sp.
 struct Item {
   int b, g, rg, sp;
   long bg;
+  size_t id;
 };
 
 __device__ __forceinline__ Item decode_item(const AttnArgs& a) {
   long item = blockIdx.x;
   Item it;
+  it.id = (size_t)item;
   it.sp = (int)(item % a.NSP);
   item /= a.NSP;
   it.rg = (int)(item % a.RG);
@@ -159,9 +163,15 @@ struct BfLayout {
   static constexpr int TILE = KB * D;            // elements per staged tile
   static constexpr int NI = TILE * 2 / 1024;     // 1 KB global_load_lds copies per tile
   // K rows are read 16 at a time at one slot: spread them over 16 slots.
-  __device__ static int kslot(int row, int c) { return c ^ ((row / RP) % CH); }
+  __host__ __device__ static constexpr int kslot(int row, int c) { return c ^ ((row / RP) % CH); }
   // V rows are read 8 at a time at a 32-byte slot pair: spread them over 8 pairs.
-  __device__ static int vslot(int row, int c) { return c ^ (2 * ((row / RP) % (CH / 2))); }
+  __host__ __device__ static constexpr int vslot(int row, int c) { return c ^ (2 * ((row / RP) % (CH / 2))); }
+  static constexpr bool same_swizzle_16_rows_apart() {
+    for (int r = 0; r < 16; ++r)
+      for (int c = 0; c < CH; ++c)
+        if (kslot(r + 16, c) != kslot(r, c) || vslot(r + 16, c) != vslot(r, c)) return false;
+    return true;
+  }
 };
 
 // Wait until at most N of this wave's vector-memory operations are in flight.
@@ -235,7 +245,7 @@ void attn_split_bf16(AttnArgs a) {
   };
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
   const int lane = tid & (kWave - 1);
   const int lr = lane & 15;
   const int lg = lane >> 4;
@@ -250,43 +260,46 @@ void attn_split_bf16(AttnArgs a) {
   const bool single = (Ltot <= a.C);  // this item is the whole of (b, g, rg)
 
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kn = static_cast<const uint16_t*>(a.kn);
-  const uint16_t* vn = static_cast<const uint16_t*>(a.vn);
   const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (size_t)it.bg * a.max_T * D;
   const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + (size_t)it.bg * a.max_T * D;
-  const uint16_t* knb = kn + (size_t)it.bg * a.n_q * D;
-  const uint16_t* vnb = vn + (size_t)it.bg * a.n_q * D;
+  const uint16_t* knb = static_cast<const uint16_t*>(a.kn) + (size_t)it.bg * a.n_q * D;
+  const uint16_t* vnb = static_cast<const uint16_t*>(a.vn) + (size_t)it.bg * a.n_q * D;
 
   // Copies of one block: copy c (first NI for K, then NI for V) is issued by
-  // wave c % WI; lane l fills LDS slot (64 c' + l) of its tile (c' = c mod
-  // NI), i.e. row (64 c' + l) / CH at swizzled slot (64 c' + l) % CH.  Every
-  // issuing wave issues CPW copies per block, so a fixed vmcnt tells it when
-  // an older block has landed.
-  auto copy_tile = [&](const uint16_t* cache, const uint16_t* fresh, uint16_t* dst, int kb, int cc, bool is_v) {
-    const int p = cc * kWave + lane;
-    const int row = p / LY::CH, sl = p % LY::CH;
-    const int chunk = is_v ? LY::vslot(row, sl) : LY::kslot(row, sl);  // XOR is its own inverse
-    const int key = kb + row;
-    const uint16_t* src;
-    if (kb + KB <= L) {
-      src = cache + (size_t)key * D;  // the whole block is committed cache
-    } else {
-      // new rows from k_new/v_new; keys past the end read a finite dummy row
-      src = key < L ? cache + (size_t)key * D : fresh + (size_t)(key < Ltot ? key - L : 0) * D;
-    }
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + 8 * chunk),
-                                     (void __attribute__((address_space(3)))*)(dst + cc * 512), 16, 0, 0);
-  };
-  auto issue_block = [&](int kb, auto S) {
-    if (wave < WI) {
+  // wave c % WI, as its i-th copy with c = wave + i WI (so copies i < NI/WI
+  // are K).  Lane l fills LDS slot (64 c' + l) of its tile (c' = c mod NI):
+  // row (64 c' + l) / CH at swizzled slot (64 c' + l) % CH, which holds the
+  // row's 16-byte chunk given by the same XOR.  Every issuing wave issues CPW
+  // copies per block, so a fixed vmcnt tells it when an older block landed.
+  int crow[CPW], cchunk[CPW];
 #pragma unroll
-      for (int i = 0; i < CPW; ++i) {
-        const int c = wave + i * WI;
-        if (c < LY::NI)
-          copy_tile(kc, knb, kbuf(S), kb, c, false);
-        else
-          copy_tile(vc, vnb, vbuf(S), kb, c - LY::NI, true);
+  for (int i = 0; i < CPW; ++i) {
+    const bool is_v = i >= LY::NI / WI;
+    const int cc = (wave + i * WI) - (is_v ? LY::NI : 0);
+    const int p = cc * kWave + lane;
+    crow[i] = p / LY::CH;
+    const int sl = p % LY::CH;
+    cchunk[i] = is_v ? LY::vslot(crow[i], sl) : LY::kslot(crow[i], sl);  // XOR is its own inverse
+  }
+  auto issue_block = [&](int kb, auto S) {
+    if (wave >= WI) return;
+    const bool full = kb + KB <= L;  // every key of the block is committed cache
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      const bool is_v = i >= LY::NI / WI;
+      const int cc = (wave + i * WI) - (is_v ? LY::NI : 0);
+      const uint16_t* cache = is_v ? vc : kc;
+      const uint16_t* fresh = is_v ? vnb : knb;
+      const int key = kb + crow[i];
+      const uint16_t* src;
+      if (full) {
+        src = cache + (size_t)kb * D + (crow[i] * D + 8 * cchunk[i]);
+      } else {  // new rows from k_new/v_new; keys past the end read a finite dummy row
+        src = (key < L ? cache + (size_t)key * D : fresh + (size_t)(key < Ltot ? key - L : 0) * D) + 8 * cchunk[i];
       }
+      uint16_t* dst = (is_v ? vbuf(S) : kbuf(S)) + cc * 512;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
     }
   };
 
@@ -309,7 +322,23 @@ void attn_split_bf16(AttnArgs a) {
     if (nblk > 1) issue_block(k0 + KB, IC<1>{});
   }
 
-  float mrow = neg_inf_f(), lsum = 0.f;
+  // Loop-invariant LDS element offsets of this lane's reads within a stage:
+  // K fragment (kt = 0) for each D step, and V^T pieces (hh = 0) for each D
+  // tile; kt = 1 / hh = 1 add 16 rows.
+  int kofs[DS], vofs[DT];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) kofs[s] = lr * D + 8 * LY::kslot(lr, 4 * s + lg);
+  {
+    const int vrow = 4 * lg + (lr >> 2), q4 = lr & 3;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vofs[dt] = vrow * D + 8 * LY::vslot(vrow, 2 * dt + (q4 >> 1)) + 4 * (q4 & 1);
+  }
+  // kt = 1 and hh = 1 reuse these offsets 16 rows further: rows 16 apart
+  // have the same swizzle.
+  static_assert(LY::same_swizzle_16_rows_apart(), "kt / hh offsets");
+
+  const float c = a.qk_scale;
+  float mrow = neg_inf_f(), lsum = 0.f;  // running max (scaled, log2 units) and partial sum
   f32x4 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -329,21 +358,38 @@ void attn_split_bf16(AttnArgs a) {
 
     const uint16_t* ks = kbuf(S);
     const uint16_t* vs = vbuf(S);
-    // Scores: lane holds keys kb + 16 kt + 4 lg + jj of row lr of the tile.
+    // Raw scores: lane holds keys kb + 16 kt + 4 lg + jj of row lr of the tile.
     float sc[8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int row = 16 * kt + lr;
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + row * D + 8 * LY::kslot(row, 4 * s + lg));
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], c, 0, 0, 0);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kofs[s] + 16 * kt * D);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sc[4 * kt + jj] = c[jj] * a.qk_scale;
+      for (int jj = 0; jj < 4; ++jj) sc[4 * kt + jj] = acc[jj];
     }
-    if (kb + KB > L) {  // the block reaches the new rows or the end: causal mask
+    // Online softmax in the log2 domain: p = 2^(s c - m) with m the running
+    // max of s c.
+    float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    float alpha;
+    if (kb + KB <= L) {
+      // Every key is visible to every row: scores are finite.
+      const float mnew = fmaxf(mrow, group_max(mx) * c);
+      alpha = exp2_fast(mrow - mnew);
+      float ps = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        sc[jj] = exp2_fast(fmaf(sc[jj], c, -mnew));
+        ps += sc[jj];
+      }
+      lsum = fmaf(lsum, alpha, ps);
+      mrow = mnew;
+    } else {
+      // The block reaches the new rows or the end: causal mask, and a row may
+      // have seen no visible key yet.
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -351,22 +397,21 @@ void attn_split_bf16(AttnArgs a) {
           const int key = kb + 16 * kt + 4 * lg + jj;
           if (key >= Ltot || key > lim) sc[4 * kt + jj] = neg_inf_f();
         }
-    }
-    // Online softmax in the log2 domain.
-    float mx = sc[0];
+      mx = sc[0];
 #pragma unroll
-    for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
-    const float mnew = fmaxf(mrow, group_max(mx));
-    const bool none = (mnew == neg_inf_f());
-    const float alpha = none ? 1.f : exp2_fast(mrow - mnew);
-    float ps = 0.f;
+      for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
+      const float mnew = fmaxf(mrow, group_max(mx) * c);
+      const bool none = (mnew == neg_inf_f());
+      alpha = none ? 1.f : exp2_fast(mrow - mnew);
+      float ps = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      sc[jj] = none ? 0.f : exp2_fast(sc[jj] - mnew);
-      ps += sc[jj];
+      for (int jj = 0; jj < 8; ++jj) {
+        sc[jj] = none ? 0.f : exp2_fast(fmaf(sc[jj], c, -mnew));
+        ps += sc[jj];
+      }
+      lsum = fmaf(lsum, alpha, ps);
+      mrow = mnew;
     }
-    lsum = lsum * alpha + ps;
-    mrow = mnew;
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
@@ -381,13 +426,9 @@ void attn_split_bf16(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) {
       s16x4 v2[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int row = 16 * hh + 4 * lg + (lr >> 2);
-        const int q4 = lr & 3;
-        const int chunk = 2 * dt + (q4 >> 1);
-        const uint16_t* p = vs + row * D + 8 * LY::vslot(row, chunk) + 4 * (q4 & 1);
-        v2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
-      }
+      for (int hh = 0; hh < 2; ++hh)
+        v2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vs + vofs[dt] + 16 * hh * D));
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
     }
@@ -422,7 +463,7 @@ void attn_split_bf16(AttnArgs a) {
     }
     return;
   }
-  const size_t item_id = blockIdx.x;
+  const size_t item_id = it.id;
   float* po = a.part_o + item_id * (16 * NW) * D;
   if (lg == 0) a.part_ml[item_id * (16 * NW) + row] = ML{mrow, lt};
 #pragma unroll
@@ -531,7 +572,7 @@ __global__ __launch_bounds__(64) void attn_split_f32(AttnArgs a) {
       }
   }
 
-  const size_t item_id = blockIdx.x;
+  const size_t item_id = it.id;
   float* po = a.part_o + item_id * (16 * RT) * D;
   ML* pml = a.part_ml + item_id * (16 * RT);
 #pragma unroll
