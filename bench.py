@@ -18,6 +18,7 @@ on a bounded sample of the same workload.
 """
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -35,6 +36,41 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 METRIC = "verified draft positions/sec + % of MI355X HBM peak (sampler, verify attn)"
 
 WORKLOADS = {"c3": 3, "c4": 4, "c5": 5}
+
+# Sources of the verify-attention kernels; the HBM byte counts stored under
+# profiles/ are used only while these files are unchanged.
+ATTN_SOURCES = (
+    "speculative_decoding_verification_spec_amd/csrc/attention.hip",
+    "speculative_decoding_verification_spec_amd/csrc/spec_common.h",
+)
+
+
+def attn_source_hash():
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cid):
+    """HBM bytes per spec_verify_attention call from the rocprofv3 byte counters.
+
+    profiles/verify_attention_config<cid>.hbm_traffic.md carries one JSON line
+    (FETCH_SIZE and WRITE_SIZE per call, each scaled by what the counter reads
+    for a plain device copy of known size).  None when the file is missing or
+    was taken from other kernel sources.
+    """
+    path = os.path.join(ROOT, "profiles", f"verify_attention_config{cid}.hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith('{"hbm_traffic"'):
+                d = json.loads(line)["hbm_traffic"]
+                if d.get("source_sha256") == attn_source_hash():
+                    return d
+    return None
 
 
 def algorithmic(cfg, lens, B):
@@ -232,12 +268,18 @@ def main():
     smp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     trn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
 
-    lens = sets[0][0]["lens_base"].cpu().numpy()
-    att_b, att_f, smp_b = algorithmic(cfg, lens, B)
+    # Algorithmic bytes per call, averaged over the rotated input sets (their
+    # lengths differ); set k is used by steps k, k + nsets, ...
+    per_set = [algorithmic(cfg, st[0]["lens_base"].cpu().numpy(), B) for st in sets]
+    counts = [len(range(k, args.steps, nsets)) for k in range(nsets)]
+    att_b = sum(c * a[0] for c, a in zip(counts, per_set)) / args.steps
+    att_f = sum(c * a[1] for c, a in zip(counts, per_set)) / args.steps
+    smp_b = per_set[0][2]
     att_gbs = att_b / (att_ms * 1e-3) / 1e9
     smp_gbs = smp_b / (smp_ms * 1e-3) / 1e9
     positions = B * cfg.gamma
     n_last = sets[(args.steps - 1) % nsets][1]["n"].cpu().numpy()
+    traffic = measured_traffic(cfg.cid)
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
 
     res = {
@@ -267,8 +309,8 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": att_gbs / HBM_PEAK_GBS,
-            "traffic": None,
-            "kernel": "spec_verify_attention (split + combine kernels)",
+            "traffic": None if traffic is None else traffic["bytes_per_call"],
+            "kernel": f"spec_verify_attention: attn_split_{'bf16' if cfg.dtype == 'bf16' else 'f32'} + attn_combine, one call",
             "algorithmic_bytes": att_b,
             "avg_ms": att_ms,
         },
