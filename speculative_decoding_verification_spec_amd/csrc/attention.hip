@@ -7,13 +7,17 @@
 //   section GQA・MQAでKVキャッシュを減らす (query heads share KV heads; decode
 //   attention time is the time to read the cache).
 //
-// Work decomposition.  A work item is (b, g, rg, sp): sequence b, KV head g,
-// row group rg, key split sp.  The rows of (b, g) are the G = Hq/Hkv query
-// heads sharing KV head g times the n_q verify positions, padded to 16-row
-// MFMA tiles; all of them read the same K/V tiles (the GQA reuse).  Each split
-// walks C keys in blocks of 32 with an online softmax and leaves its
-// (max, sum, unnormalised output) in the workspace; attn_combine merges the
-// splits.  A (b, g) whose keys fit one split writes its output directly.
+// Work decomposition.  A slab is (b, g, rg): sequence b, KV head g, row group
+// rg.  The rows of (b, g) are the G = Hq/Hkv query heads sharing KV head g
+// times the n_q verify positions, padded to 16-row MFMA tiles; all of them
+// read the same K/V tiles (the GQA reuse).  A piece of a slab walks a range
+// of its keys in blocks of 32 with an online softmax and leaves its (max,
+// sum, unnormalised output) in the workspace, or writes the output directly
+// when it is the whole slab; a combine kernel merges the pieces.
+//   bf16 (B <= 1024): the stream scheme.  One workgroup per resident slot;
+//   the slabs' key blocks are laid end to end and cut into equal shares, one
+//   per workgroup, so every workgroup has the same work whatever the lengths.
+//   fp32, and bf16 with B > 1024: fixed splits of C keys, one workgroup each.
 //
 // MFMA layouts (gfx950, wave64, checked on the hardware).  For
 // v_mfma_f32_16x16x32_bf16 lane l holds A[l%16][8(l/16) .. +7],
@@ -27,9 +31,10 @@
 //   from two 16-key tiles, {4(l/16) + j, 16 + 4(l/16) + j}, are its 8 MFMA
 //   k-slots and V^T is gathered in the same order.
 //
-// bf16 kernel.  One workgroup per work item, one wave per 16-row tile.  K and
+// bf16 kernels.  One wave per 16-row tile.  K and
 // V blocks (32 keys x D) are copied from HBM straight into LDS with
-// global_load_lds (no registers, asynchronous), double buffered, and read by
+// global_load_lds (no registers, asynchronous) through three LDS stages, two
+// blocks in flight, and read by
 // every wave of the workgroup: K as 16-byte A fragments (ds_read_b128), V
 // transposed with ds_read_b64_tr_b16 (within each 16-lane group, lane i
 // receives element i mod 4 of the 8-byte pieces of lanes 4k + i/4, k = 0..3;
@@ -50,6 +55,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "spec_common.h"
@@ -77,7 +83,9 @@ struct AttnArgs {
   void* out;
   float* part_o;
   ML* part_ml;
+  int* pre;  // stream scheme: [B + 1] blocks per slab before sequence b
   int B, Hq, Hkv, n_q, G, M, RG, RT, NSP, C, max_T, hint;
+  int P, MINB, JP;  // stream scheme: workgroups, minimum share, partial slots per slab
   float qk_scale;  // scale * log2(e)
 };
 
@@ -215,10 +223,37 @@ __device__ __forceinline__ float group_sum(float v) {
 #ifndef SPECV_ATTN_WPE
 #define SPECV_ATTN_WPE 1
 #endif
+#ifndef SPECV_STREAM_WPE
+#define SPECV_STREAM_WPE 4
+#endif
 
-template <int D, int NW, int NST>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_ATTN_WPE)))
-void attn_split_bf16(AttnArgs a) {
+// One LDS object per stage and tensor: reads of one stage then provably do
+// not alias the asynchronous copies into another, so the compiler does not
+// make them wait for those copies.
+#define SPECV_BF16_STAGE_LDS \
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[LY::TILE], v0s[LY::TILE]; \
+  __shared__ __attribute__((aligned(1024))) uint16_t k1s[LY::TILE], v1s[LY::TILE]; \
+  __shared__ __attribute__((aligned(1024))) uint16_t k2s[NST > 2 ? LY::TILE : 8], v2s[NST > 2 ? LY::TILE : 8]; \
+  auto kbuf = [&](auto S) -> uint16_t* { \
+    if constexpr (decltype(S)::value == 0) return k0s; \
+    else if constexpr (decltype(S)::value == 1) return k1s; \
+    else return k2s; \
+  }; \
+  auto vbuf = [&](auto S) -> uint16_t* { \
+    if constexpr (decltype(S)::value == 0) return v0s; \
+    else if constexpr (decltype(S)::value == 1) return v1s; \
+    else return v2s; \
+  };
+
+// One piece of one (b, g, rg): keys [k0, k1) of sequence b (length L, valid),
+// rows of row group rg of KV head g.  Writes the normalised output when the
+// piece is the whole of (b, g, rg) (whole), else its (max, sum, unnormalised
+// output) at partial slot `slot`.  append: also copy the n_q new rows of
+// (b, g) into the cache (A1).  kbuf / vbuf map a stage index to its LDS
+// objects.  Every wave of the workgroup calls it with the same arguments.
+template <int D, int NW, int NST, typename KBuf, typename VBuf>
+__device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vbuf, int b, int g, int rg, int L,
+                                           int k0, int k1, bool whole, size_t slot, bool append) {
   using LY = BfLayout<D>;
   constexpr int DS = D / 32;  // MFMA steps over D for the scores
   constexpr int DT = D / 16;  // 16-wide output tiles over D
@@ -227,43 +262,24 @@ void attn_split_bf16(AttnArgs a) {
   constexpr int CPW = NCP / WI;                               // copies per issuing wave per block
   static_assert(NCP % WI == 0, "copies must split evenly over the issuing waves");
   static_assert(NST >= 2 && NST <= 3 && (NST - 2) * CPW <= 63, "stages");
-  // One LDS object per stage and tensor: reads of one stage then provably do
-  // not alias the asynchronous copies into another, so the compiler does not
-  // make them wait for those copies.
-  __shared__ __attribute__((aligned(1024))) uint16_t k0s[LY::TILE], v0s[LY::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t k1s[LY::TILE], v1s[LY::TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t k2s[NST > 2 ? LY::TILE : 8], v2s[NST > 2 ? LY::TILE : 8];
-  auto kbuf = [&](auto S) -> uint16_t* {
-    if constexpr (decltype(S)::value == 0) return k0s;
-    else if constexpr (decltype(S)::value == 1) return k1s;
-    else return k2s;
-  };
-  auto vbuf = [&](auto S) -> uint16_t* {
-    if constexpr (decltype(S)::value == 0) return v0s;
-    else if constexpr (decltype(S)::value == 1) return v1s;
-    else return v2s;
-  };
-
-  const int tid = threadIdx.x;
+  // The thread index passes through an empty asm, so lane-derived values are
+  // recomputed per piece rather than hoisted out of a caller's piece loop
+  // and kept live across it.
+  int tid = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid));
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform per wave
   const int lane = tid & (kWave - 1);
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  const Item it = decode_item(a);
-  const int L = a.len[it.b];
-  if (L < 0 || L > a.hint) return;  // flagged by attn_combine
+  const long bg = (long)b * a.Hkv + g;
   const int Ltot = L + a.n_q;
-  const int k0 = it.sp * a.C;
-  if (k0 >= Ltot) return;
-  const int k1 = min(k0 + a.C, Ltot);
   const int nblk = (k1 - k0 + KB - 1) / KB;
-  const bool single = (Ltot <= a.C);  // this item is the whole of (b, g, rg)
 
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (size_t)it.bg * a.max_T * D;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + (size_t)it.bg * a.max_T * D;
-  const uint16_t* knb = static_cast<const uint16_t*>(a.kn) + (size_t)it.bg * a.n_q * D;
-  const uint16_t* vnb = static_cast<const uint16_t*>(a.vn) + (size_t)it.bg * a.n_q * D;
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (size_t)bg * a.max_T * D;
+  const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + (size_t)bg * a.max_T * D;
+  const uint16_t* knb = static_cast<const uint16_t*>(a.kn) + (size_t)bg * a.n_q * D;
+  const uint16_t* vnb = static_cast<const uint16_t*>(a.vn) + (size_t)bg * a.n_q * D;
 
   // Copies of one block: copy c (first NI for K, then NI for V) is issued by
   // wave c % WI, as its i-th copy with c = wave + i WI (so copies i < NI/WI
@@ -304,14 +320,14 @@ void attn_split_bf16(AttnArgs a) {
   };
 
   // Query fragment of this wave's tile (B operand of S^T = K Q^T).
-  const int m = it.rg * 16 * NW + 16 * wave + lr;
+  const int m = rg * 16 * NW + 16 * wave + lr;
   const bool valid = m < a.M;
-  const int h = it.g * a.G + (valid ? m / a.n_q : 0);
+  const int h = g * a.G + (valid ? m / a.n_q : 0);
   const int qi = valid ? m % a.n_q : a.n_q - 1;
   const int lim = L + qi;  // last visible key of this row
   bf16x8 qf[DS];
   {
-    const uint16_t* qrow = q + (((size_t)it.b * a.Hq + h) * a.n_q + qi) * D;
+    const uint16_t* qrow = q + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
 #pragma unroll
     for (int s = 0; s < DS; ++s)
       qf[s] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg) : bf16x8{};
@@ -443,14 +459,14 @@ void attn_split_bf16(AttnArgs a) {
   }
 
   // A1 (once per (b, g)); nothing in this launch reads these rows.
-  if (it.sp == 0 && it.rg == 0) append_rows<uint16_t, D>(a, it.bg, L, tid, 64 * NW);
+  if (append) append_rows<uint16_t, D>(a, bg, L, tid, 64 * NW);
 
   const float lt = group_sum(lsum);  // row sum over the 4 lane groups
   const int row = 16 * wave + lr;    // row within the item
-  if (single) {
+  if (whole) {
     // The whole of (b, g, rg) is here: normalise and write the output.
     if (valid) {
-      uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)it.b * a.Hq + h) * a.n_q + qi) * D;
+      uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
       const float inv = 1.f / lt;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
@@ -463,11 +479,214 @@ void attn_split_bf16(AttnArgs a) {
     }
     return;
   }
-  const size_t item_id = it.id;
-  float* po = a.part_o + item_id * (16 * NW) * D;
-  if (lg == 0) a.part_ml[item_id * (16 * NW) + row] = ML{mrow, lt};
+  float* po = a.part_o + slot * (16 * NW) * D;
+  if (lg == 0) a.part_ml[slot * (16 * NW) + row] = ML{mrow, lt};
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[dt];
+}
+
+template <int D, int NW, int NST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_ATTN_WPE)))
+void attn_split_bf16(AttnArgs a) {
+  using LY = BfLayout<D>;
+  SPECV_BF16_STAGE_LDS
+  const Item it = decode_item(a);
+  const int L = a.len[it.b];
+  if (L < 0 || L > a.hint) return;  // flagged by attn_combine
+  const int Ltot = L + a.n_q;
+  const int k0 = it.sp * a.C;
+  if (k0 >= Ltot) return;
+  bf16_piece<D, NW, NST>(a, kbuf, vbuf, it.b, it.g, it.rg, L, k0, min(k0 + a.C, Ltot), Ltot <= a.C, it.id,
+                         it.sp == 0 && it.rg == 0);
+}
+
+// Inclusive prefix sum of ints over the 64 lanes in lane order.
+__device__ __forceinline__ int wave_inclusive_scan_int(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// A wave-uniform 64-bit value moved to scalar registers.
+__device__ __forceinline__ long long uniform64(long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (long long)(((uint64_t)hi << 32) | lo);
+}
+
+// Blocks of KB keys in one (b, g, rg) slab of sequence b; 0 for a length the
+// call rejects (the combine writes NaN rows for it).
+__device__ __forceinline__ int slab_blocks(const AttnArgs& a, int b) {
+  const int L = a.len[b];
+  return (L < 0 || L > a.hint) ? 0 : (L + a.n_q + KB - 1) / KB;
+}
+
+// Blocks per workgroup: the total W spread over the P workgroups, but never
+// below MINB, so a slab is cut into at most JP pieces.
+__device__ __forceinline__ long long stream_share(const AttnArgs& a, long long W) {
+  return max((W + a.P - 1) / a.P, (long long)a.MINB);
+}
+
+// bf16 stream kernel: P persistent workgroups share the key blocks of every
+// slab evenly.  The slabs (b, g, rg) are laid end to end in that order (b
+// slowest), slab (b, .) holding slab_blocks(b) blocks, W blocks in all;
+// workgroup w takes blocks [w share, (w + 1) share) of that sequence, which
+// may end inside one slab and run on through the next ones.  Each piece it
+// covers is run like a split: a slab it covers whole gets its output
+// directly, otherwise the piece's state goes to partial slot j of the slab,
+// j = w - (first workgroup touching the slab), and attn_combine_stream merges
+// the pieces.  Equal shares keep every CU busy to the end whatever the
+// lengths, and one workgroup per slot means no workgroup waits to be
+// dispatched.  Workgroup 0 also stores the per-slab block prefix pre[b] for
+// the combine.
+template <int D, int NW, int NST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
+void attn_stream_bf16(AttnArgs a) {
+  using LY = BfLayout<D>;
+  SPECV_BF16_STAGE_LDS
+  __shared__ long long sh_x[3];
+  __shared__ int sh_b[2];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int HR = a.Hkv * a.RG;
+
+  // Locate this workgroup's first block (wave 0; two passes over the lengths).
+  if (tid < kWave) {
+    int run = 0;
+    for (int c0 = 0; c0 < a.B; c0 += kWave) {
+      const int bb = c0 + lane;
+      const int nb = bb < a.B ? slab_blocks(a, bb) : 0;
+      const int incl = run + wave_inclusive_scan_int(nb, lane);
+      if (blockIdx.x == 0 && bb < a.B) a.pre[bb + 1] = incl;
+      run = __shfl(incl, kWave - 1, kWave);
+    }
+    if (blockIdx.x == 0 && lane == 0) a.pre[0] = 0;
+    const long long W = (long long)HR * run;
+    const long long share = stream_share(a, W);
+    const long long x0 = (long long)blockIdx.x * share;
+    int b0 = a.B, pre0 = 0;
+    if (x0 < W) {
+      run = 0;
+      for (int c0 = 0; c0 < a.B; c0 += kWave) {
+        const int bb = c0 + lane;
+        const int nb = bb < a.B ? slab_blocks(a, bb) : 0;
+        const int incl = run + wave_inclusive_scan_int(nb, lane);
+        const uint64_t hit = __ballot(bb < a.B && (long long)HR * incl > x0);
+        if (hit) {
+          const int l = __ffsll((long long)hit) - 1;
+          b0 = c0 + l;
+          pre0 = __shfl(incl - nb, l, kWave);
+          break;
+        }
+        run = __shfl(incl, kWave - 1, kWave);
+      }
+    }
+    if (lane == 0) {
+      sh_x[0] = x0;
+      sh_x[1] = min(x0 + share, W);
+      sh_x[2] = share;
+      sh_b[0] = b0;
+      sh_b[1] = pre0;
+    }
+  }
+  __syncthreads();
+  // The piece walk is the same for every wave: keep its state in scalar
+  // registers.
+  const long long x1 = uniform64(sh_x[1]);
+  long long x = uniform64(sh_x[0]);
+  if (x >= x1) return;  // uniform: nothing left for this workgroup
+  const long long share = uniform64(sh_x[2]);
+  int b = __builtin_amdgcn_readfirstlane(sh_b[0]);
+  long long preb = __builtin_amdgcn_readfirstlane(sh_b[1]);  // blocks per slab before sequence b
+  auto ufl = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  int nbb = ufl(slab_blocks(a, b));
+  const long long q0 = x - (long long)HR * preb;
+  int sidx = ufl((int)(q0 / nbb));
+  int off = ufl((int)(q0 % nbb));
+  bool first = true;
+  while (x < x1 && b < a.B) {
+    if (nbb == 0) {  // a rejected length holds no blocks
+      ++b;
+      nbb = b < a.B ? ufl(slab_blocks(a, b)) : 0;
+      sidx = 0;
+      off = 0;
+      continue;
+    }
+    const int take = ufl((int)min((long long)(nbb - off), x1 - x));
+    const int end = off + take;
+    const int g = ufl(sidx / a.RG), rg = ufl(sidx % a.RG);
+    const long long S0 = (long long)HR * preb + (long long)sidx * nbb;  // first block of the slab
+    const int j = ufl((int)((long long)blockIdx.x - S0 / share));
+    const bool whole = (off == 0 && end == nbb);
+    if (whole || (j >= 0 && j < a.JP)) {
+      if (!first) block_barrier();  // every wave is done with the previous piece's stages
+      first = false;
+      const int L = ufl(a.len[b]);
+      const size_t slot = (((size_t)b * a.Hkv + g) * a.RG + rg) * a.JP + (size_t)j;
+      bf16_piece<D, NW, NST>(a, kbuf, vbuf, b, g, rg, L, off * KB, min(end * KB, L + a.n_q), whole, slot,
+                             off == 0 && rg == 0);
+    }
+    x = uniform64(x + take);
+    off = 0;
+    if (++sidx == HR) {
+      sidx = 0;
+      preb = uniform64(preb + nbb);
+      ++b;
+      nbb = b < a.B ? ufl(slab_blocks(a, b)) : 0;
+    }
+  }
+}
+
+// Merge the pieces of each (b, g, rg) slab the stream kernel cut; one
+// workgroup per slab.  Slabs covered whole were written by the stream kernel.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
+  const long slab = blockIdx.x;
+  const int rg = (int)(slab % a.RG);
+  const int g = (int)((slab / a.RG) % a.Hkv);
+  const int b = (int)(slab / ((long)a.RG * a.Hkv));
+  const int rows = 16 * a.RT;
+  const int row0 = rg * rows;
+  const int nrows = min(rows, a.M - row0);
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  auto out_ptr = [&](int row) {
+    const int m = row0 + row;
+    return out + (((size_t)b * a.Hq + g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D;
+  };
+  const int nbb = slab_blocks(a, b);
+  if (nbb == 0) {  // rejected length: NaN rows, nothing else touched
+    for (int e = threadIdx.x; e < nrows * D; e += blockDim.x) out_ptr(e / D)[e % D] = (uint16_t)0x7fc0;
+    return;
+  }
+  const int HR = a.Hkv * a.RG;
+  const long long share = stream_share(a, (long long)HR * a.pre[a.B]);
+  const long long S0 = (long long)HR * a.pre[b] + (long long)(g * a.RG + rg) * nbb;
+  const long long w0 = S0 / share, w1 = (S0 + nbb - 1) / share;
+  if (w0 == w1) return;
+  const int np = (int)min(w1 - w0 + 1, (long long)a.JP);
+  const size_t base = (size_t)slab * a.JP;
+  constexpr int D4 = D / 4;
+  for (int e = threadIdx.x; e < nrows * D4; e += blockDim.x) {
+    const int row = e / D4, d = 4 * (e % D4);
+    float mx = neg_inf_f();
+    for (int j = 0; j < np; ++j) mx = fmaxf(mx, a.part_ml[(base + j) * rows + row].m);
+    float den = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < np; ++j) {
+      const ML ml = a.part_ml[(base + j) * rows + row];
+      const float w = exp2_fast(ml.m - mx);
+      den += w * ml.l;
+      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + ((base + j) * rows + row) * D + d);
+    }
+    acc *= 1.f / den;
+    uint2 pk;
+    pk.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+    pk.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+    *reinterpret_cast<uint2*>(out_ptr(row) + d) = pk;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -722,8 +941,91 @@ static AttnPlan attn_plan(int B, int Hq, int Hkv, int n_q, int D, int hint, spec
 #endif
 constexpr int kStages = SPECV_ATTN_STAGES;  // LDS stages; blocks in flight per workgroup: kStages - 1
 
+// ---- stream scheme ---------------------------------------------------------
+
+// Upper bound on the workgroups of a stream launch: 256 CUs, at most 3
+// resident workgroups each (LDS).  The partial slots per slab follow from it,
+// so the workspace size does not depend on the device.
+constexpr int kStreamMaxWG = 768;
+
+// Sizes the stream scheme handles: every workgroup scans the B lengths, and
+// block counts stay in int.
+static bool stream_ok(spec_dtype_t dt, int B, int Hkv, int RG, int n_q, int hint) {
+  const long nbmax = ((long)hint + n_q + KB - 1) / KB;
+  return dt == SPEC_BF16 && B <= 1024 && (long)Hkv * RG * B * nbmax < (1L << 30);
+}
+
+struct StreamPlan {
+  int JP, MINB;
+  size_t off_o, off_ml, off_pre, total;
+};
+
+static StreamPlan stream_plan(int B, int Hkv, int RG, int RT, int n_q, int D, int hint) {
+  StreamPlan p{};
+  const long slabs = (long)B * Hkv * RG;
+  // With shares of at least MINB = ceil(nbmax / jcap) blocks a slab is cut
+  // into at most jcap + 1 pieces.  jcap is large enough that MINB stays below
+  // the even share W / P unless most lengths are far below the hint.
+  const long jcap = std::max(2L, 2 * ((kStreamMaxWG + slabs - 1) / slabs) + 2);
+  const long nbmax = ((long)hint + n_q + KB - 1) / KB;
+  p.JP = (int)(jcap + 1);
+  p.MINB = (int)std::max(1L, (nbmax + jcap - 1) / jcap);
+  const size_t slots = (size_t)slabs * p.JP;
+  size_t off = 0;
+  p.off_o = off;
+  off = align256(off + sizeof(float) * slots * 16 * RT * D);
+  p.off_ml = off;
+  off = align256(off + sizeof(ML) * slots * 16 * RT);
+  p.off_pre = off;
+  off = align256(off + sizeof(int) * ((size_t)B + 1));
+  p.total = off;
+  return p;
+}
+
+// Workgroups of a stream launch on the current device: CUs x resident
+// workgroups per CU.  Residency is the occupancy query's answer, further
+// limited because the waves of a workgroup are spread round-robin over the 4
+// SIMDs of a CU: a workgroup of NW waves puts ceil(NW / 4) on one SIMD, which
+// holds 512 / VGPRs waves.  Cached per device.
+template <typename K>
+static int stream_workgroups(K kernel, int NW) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>* slot = dev < 64 ? &cache[dev] : nullptr;
+  if (slot && slot->load(std::memory_order_relaxed) > 0) return slot->load(std::memory_order_relaxed);
+  int cus = 0, occ = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel), 64 * NW, 0) !=
+          hipSuccess ||
+      occ < 1)
+    occ = 1;
+  hipFuncAttributes fa{};
+  int per_simd = 4;
+  if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kernel)) == hipSuccess && fa.numRegs > 0)
+    per_simd = 512 / ((fa.numRegs + 7) / 8 * 8);
+  // Up to 4 waves a workgroup takes one slot on each of NW SIMDs; a larger
+  // one takes ceil(NW / 4) slots on every SIMD (measured: 5-, 6- and 8-wave
+  // workgroups fit 2 per CU whatever their registers and LDS).
+  const int by_slots = NW <= 4 ? 4 * per_simd / NW : per_simd / ((NW + 3) / 4);
+  const int k = std::max(1, std::min(occ, by_slots));
+  const int P = std::min(kStreamMaxWG, cus * k);
+  if (slot) slot->store(P, std::memory_order_relaxed);
+  return P;
+}
+
 template <int D, int NW>
-static hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_bf16(const AttnArgs& a0, hipStream_t s) {
+  if (a0.pre) {  // stream scheme
+    AttnArgs a = a0;
+    a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages>, NW);
+    hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  const AttnArgs& a = a0;
   const size_t items = (size_t)a.B * a.Hkv * a.RG * a.NSP;
   hipLaunchKernelGGL((attn_split_bf16<D, NW, kStages>), dim3((unsigned)items), dim3(64 * NW), 0, s, a);
   hipError_t e = hipGetLastError();
@@ -790,7 +1092,13 @@ extern "C" size_t spec_verify_attention_workspace_size(int B, int Hq, int Hkv, i
   nsp = std::min(nsp, (span + sp.cmin - 1) / sp.cmin);
   nsp = std::max(nsp, (long)p.NSP);
   const size_t items = (size_t)K * nsp;
-  return align256(sizeof(float) * items * 16 * p.RT * D) + align256(sizeof(ML) * items * 16 * p.RT);
+  const size_t split_bytes = align256(sizeof(float) * items * 16 * p.RT * D) + align256(sizeof(ML) * items * 16 * p.RT);
+  // bf16 uses the stream scheme while stream_ok holds, which for a larger
+  // hint can stop holding: cover both then.
+  if (dtype != SPEC_BF16 || B > 1024) return split_bytes;
+  const size_t stream_bytes = stream_plan(B, Hkv, p.RG, p.RT, n_q, D, max_len_hint).total;
+  if (stream_ok(dtype, B, Hkv, p.RG, n_q, max_len_hint)) return stream_bytes;
+  return std::max(split_bytes, stream_bytes);
 }
 
 extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
@@ -810,7 +1118,9 @@ extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new,
   if ((long)max_len_hint + n_q > (long)max_T) return SPEC_ERR_OVERFLOW;
   if (n_q > 16 || (Hq / Hkv) * n_q > 256 || !supported(dtype, D)) return SPEC_ERR_UNSUPPORTED;
   const AttnPlan p = attn_plan(B, Hq, Hkv, n_q, D, max_len_hint, dtype);
-  if (workspace_bytes < p.total) return SPEC_ERR_ARG;
+  const bool use_stream = stream_ok(dtype, B, Hkv, p.RG, n_q, max_len_hint);
+  const StreamPlan sp = use_stream ? stream_plan(B, Hkv, p.RG, p.RT, n_q, D, max_len_hint) : StreamPlan{};
+  if (workspace_bytes < (use_stream ? sp.total : p.total)) return SPEC_ERR_ARG;
   if ((size_t)B * Hkv * p.RG * p.NSP > 0x7fffffffu) return SPEC_ERR_UNSUPPORTED;
 
   AttnArgs a;
@@ -821,8 +1131,13 @@ extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new,
   a.vc = v_cache;
   a.len = cache_len;
   a.out = out;
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.off_o);
-  a.part_ml = reinterpret_cast<ML*>(static_cast<char*>(workspace) + p.off_ml);
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<float*>(ws + (use_stream ? sp.off_o : p.off_o));
+  a.part_ml = reinterpret_cast<ML*>(ws + (use_stream ? sp.off_ml : p.off_ml));
+  a.pre = use_stream ? reinterpret_cast<int*>(ws + sp.off_pre) : nullptr;
+  a.P = 0;
+  a.MINB = sp.MINB;
+  a.JP = sp.JP;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

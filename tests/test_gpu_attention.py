@@ -120,6 +120,26 @@ def test_shapes_and_edges(dtype, B, Hq, Hkv, n_q, D, lens):
     _check(inp, out, kc, vc, dtype)
 
 
+@pytest.mark.parametrize(
+    "B,Hq,Hkv,n_q,D,lo,hi",
+    [
+        (1, 8, 1, 5, 128, 5000, 5000),    # one slab cut into hundreds of pieces
+        (300, 4, 4, 3, 128, 0, 3),        # many slabs of one or two blocks
+        (1100, 2, 1, 2, 64, 0, 70),       # B > 1024: the fixed-split scheme
+    ],
+)
+def test_work_distribution_edges(B, Hq, Hkv, n_q, D, lo, hi):
+    """Batch shapes at the edges of how the bf16 kernel spreads key blocks over workgroups."""
+    _case("distribution", B=B, Hq=Hq, Hkv=Hkv, n_q=n_q, D=D, lens=(lo, hi))
+    lens = np.random.default_rng([B, lo, hi]).integers(lo, hi + 1, size=B).astype(np.int32)
+    max_T = hi + n_q + 3
+    cfg = W.Config(97, "distribution", B=B, gamma=n_q - 1, V=1, dtype="bf16", Hq=Hq, Hkv=Hkv, D=D,
+                   L=(lo, hi), max_T=max_T)
+    inp = W.attention_inputs(cfg, B=B, max_T=max_T, lens=lens)
+    out, kc, vc = _run_host(inp, poison_tail=True)
+    _check(inp, out, kc, vc, "bf16")
+
+
 def test_cache_full_to_capacity():
     cfg = W.get(4)
     B, max_T = 2, 1024
