@@ -18,6 +18,8 @@ cited by title and section:
 Modules:
   sampler    -- modified rejection sampling (accept test, first rejection,
                 residual / bonus inverse-CDF draw, emitted tokens)
+  greedy     -- temperature-0 verification (accept while the draft is the
+                target's argmax, then the target's argmax)
   attention  -- KV append and causal multi-query verify attention, plus the
                 uncached full-sequence recompute it must agree with
   truncate   -- the KV length reset after verification
@@ -31,4 +33,4 @@ Nothing is "parity unpinned" except the mapping of decisions that fall inside
 the 1e-6 threshold band (those draws are counted, not compared).
 """
 
-from . import attention, bf16, formulas, sampler, truncate  # noqa: F401
+from . import attention, bf16, formulas, greedy, sampler, truncate  # noqa: F401

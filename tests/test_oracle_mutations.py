@@ -94,3 +94,48 @@ def test_wrong_exponent_is_caught(monkeypatch):
     monkeypatch.setattr(F, "expected_committed", lambda a, g: orig(a, g - 1) if g > 1 else orig(a, g) * 0.9)
     row = {"T": 0.7, "k": 4, "alpha": 0.901, "E": 4.10, "factor": 2.19}
     _assert_pin_fails(lambda: TF.test_expected_tokens_matches_printed_ksweep(row))
+
+
+# ---- greedy verification ----------------------------------------------------
+
+from oracle import greedy as G  # noqa: E402
+from tests import test_oracle_greedy as TG  # noqa: E402
+
+
+def _greedy_pin():
+    TG.test_speculative_equals_greedy_decoding(50, 0.8, 1.0, False, 4)
+
+
+def _mutant(row_of_t=0, accept_on_mismatch=False):
+    def verify_sequence(z_target, x):
+        n = 0
+        for i in range(len(x)):
+            same = G.argmax(z_target[i]) == int(x[i])
+            if same == accept_on_mismatch:
+                break
+            n += 1
+        t = G.argmax(z_target[min(n + row_of_t, len(x))])
+        return n, [int(v) for v in x[:n]] + [t]
+
+    return verify_sequence
+
+
+def test_greedy_pins_hold_unmutated():
+    _greedy_pin()
+    TG.test_zero_temperature_limit_of_the_sampler()
+
+
+def test_greedy_correction_from_the_next_row_is_caught(monkeypatch):
+    monkeypatch.setattr(G, "verify_sequence", _mutant(row_of_t=1))
+    _assert_pin_fails(_greedy_pin)
+
+
+def test_greedy_inverted_accept_is_caught(monkeypatch):
+    monkeypatch.setattr(G, "verify_sequence", _mutant(accept_on_mismatch=True))
+    _assert_pin_fails(_greedy_pin)
+    _assert_pin_fails(TG.test_zero_temperature_limit_of_the_sampler)
+
+
+def test_greedy_last_index_ties_are_caught(monkeypatch):
+    monkeypatch.setattr(G, "argmax", lambda z: int(len(z) - 1 - np.argmax(np.asarray(G.to_f64(z))[::-1])))
+    _assert_pin_fails(TG.test_argmax_conventions)
