@@ -73,8 +73,11 @@ def measured_traffic(cid):
     return None
 
 
-def algorithmic(cfg, lens, B):
-    """Bytes and flops the step must move / compute (every input read once)."""
+def algorithmic(cfg, lens, B, greedy=False):
+    """Bytes and flops the step must move / compute (every input read once).
+
+    Greedy verification (T = 0) reads only the gamma+1 target rows and no uniforms.
+    """
     e = cfg.elem_bytes
     n, D = cfg.n_q, cfg.D
     L = lens.astype(np.int64)
@@ -84,7 +87,10 @@ def algorithmic(cfg, lens, B):
     att_bytes = kv_read + append + q_o
     att_flops = int(4 * cfg.Hq * D * np.sum(n * L + n * (n + 1) // 2))
     g = cfg.gamma
-    smp_bytes = int(B * (2 * g + 1) * cfg.V * e + B * (g * 4 + (g + 1) * 8 + 4 + (g + 1) * 4 + 8 * g))
+    if greedy:
+        smp_bytes = int(B * (g + 1) * cfg.V * e + B * (g * 4 + 4 + (g + 1) * 4 + 8 * g))
+    else:
+        smp_bytes = int(B * (2 * g + 1) * cfg.V * e + B * (g * 4 + (g + 1) * 8 + 4 + (g + 1) * 4 + 8 * g))
     return att_bytes, att_flops, smp_bytes
 
 
@@ -93,16 +99,20 @@ def make_inputs(cfg, device, temperature, rep):
 
     import workloads as W
 
+    t_gen = temperature if temperature > 0 else 1.0  # greedy: drafts are the draft model's argmax
     if cfg.cid == 5:
         att = W.attention_inputs_device(cfg, device, rep=rep)
-        smp = W.sampler_inputs_device(cfg, device, temperature=temperature, rep=rep)
+        smp = W.sampler_inputs_device(cfg, device, temperature=t_gen, rep=rep)
     else:
         from workloads.device import to_dev
 
         a = W.attention_inputs(cfg, rep=rep)
-        s = W.sampler_inputs(cfg, temperature=temperature, rep=rep)
+        s = W.sampler_inputs(cfg, temperature=t_gen, rep=rep)
         att = {k: to_dev(v, device=device) for k, v in a.items()}
         smp = {k: (to_dev(v, device=device) if k != "temperature" else v) for k, v in s.items()}
+    if temperature == 0:
+        smp["draft_tokens"] = torch.argmax(smp["draft_logits"].float(), dim=-1).to(torch.int32)
+        smp["temperature"] = 0.0
     att["lens_base"] = att["lens"].clone()
     att["out"] = torch.empty_like(att["q"])
     smp["n"] = torch.empty(cfg.B, dtype=torch.int32, device=device)
@@ -116,6 +126,7 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as A
+    from oracle import greedy as Gr
     from oracle import sampler as S
     from workloads.device import to_host
 
@@ -135,7 +146,11 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
             t_att = time.perf_counter() - s0
             sh = {k: to_host(smp[k][sl]) for k in ("target_logits", "draft_logits", "draft_tokens", "uniforms")}
             s1 = time.perf_counter()
-            S.verify_batch(sh["target_logits"], sh["draft_logits"], sh["draft_tokens"], sh["uniforms"], temperature)
+            if temperature == 0:
+                Gr.verify_batch(sh["target_logits"], sh["draft_tokens"])
+            else:
+                S.verify_batch(sh["target_logits"], sh["draft_logits"], sh["draft_tokens"], sh["uniforms"],
+                               temperature)
             t_smp = time.perf_counter() - s1
             done += 1
             if done == 1:
@@ -150,8 +165,10 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
         "unit": "positions/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"{done} whole sequences of the workload (attention over their full cache + sampler over all "
-        f"{2 * cfg.gamma + 1} vocab rows), numpy fp64, one BLAS thread; host copies excluded from the time",
+        "sample": f"{done} whole sequences of the workload (attention over their full cache + "
+        + (f"greedy verification over the {cfg.gamma + 1} target rows" if temperature == 0 else
+           f"sampler over all {2 * cfg.gamma + 1} vocab rows")
+        + "), numpy fp64, one BLAS thread; host copies excluded from the time",
         "seconds": elapsed,
     }
 
@@ -241,8 +258,10 @@ def main():
                                  hint, out=att["out"])
         if events:
             events[1].record(stream)
-        n, tok, _, _ = sv.spec_reject_sample(smp["target_logits"], smp["draft_logits"], smp["draft_tokens"],
-                                             smp["uniforms"], T, n_accepted=smp["n"], out_tokens=smp["tok"])
+        greedy = T == 0
+        n, tok, _, _ = sv.spec_reject_sample(smp["target_logits"], None if greedy else smp["draft_logits"],
+                                             smp["draft_tokens"], None if greedy else smp["uniforms"], T,
+                                             n_accepted=smp["n"], out_tokens=smp["tok"])
         if events:
             events[2].record(stream)
         sv.spec_kv_truncate(att["lens"], n, cfg.n_q)
@@ -270,7 +289,7 @@ def main():
 
     # Algorithmic bytes per call, averaged over the rotated input sets (their
     # lengths differ); set k is used by steps k, k + nsets, ...
-    per_set = [algorithmic(cfg, st[0]["lens_base"].cpu().numpy(), B) for st in sets]
+    per_set = [algorithmic(cfg, st[0]["lens_base"].cpu().numpy(), B, greedy=(T == 0)) for st in sets]
     counts = [len(range(k, args.steps, nsets)) for k in range(nsets)]
     att_b = sum(c * a[0] for c, a in zip(counts, per_set)) / args.steps
     att_f = sum(c * a[1] for c, a in zip(counts, per_set)) / args.steps

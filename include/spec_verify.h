@@ -131,12 +131,23 @@ size_t spec_reject_sample_workspace_size(int B, int gamma, int V, spec_dtype_t d
  *   token drawn from p_gamma; the draw is inverse-CDF with uniforms[b][gamma]:
  *   the smallest j with C_j / C_{V-1} > u, C the prefix sum of the weights.
  *
+ * T == 0 is greedy verification, [P2] section 投機的デコーディングとは (the
+ * listing omits its temperature-0 branch; the results after it state that the
+ * test becomes "the target's argmax equals the draft" and that the output
+ * equals greedy decoding of the target alone):
+ *   position i is accepted iff argmax target_logits[b][i] == x_i; n as above;
+ *   the final token is argmax target_logits[b][n].  argmax is the first index
+ *   of the largest value (values compared exactly; -0 == +0; NaN is largest).
+ *   draft_logits and uniforms are not read and may be NULL; p_draft[i] is 1.0
+ *   when x_i is the argmax, else 0.0; q_draft is written as NaN.
+ *
  *   target_logits device, [B][gamma+1][V] dtype
- *   draft_logits  device, [B][gamma][V]   dtype
+ *   draft_logits  device, [B][gamma][V]   dtype (NULL allowed when T == 0)
  *   draft_tokens  device, [B][gamma] int32, x_i, each in [0, V)
  *   uniforms      device, [B][gamma+1] double in [0, 1): [i < gamma] the accept
- *                 test at i, [gamma] the final draw (residual or bonus)
- *   temperature   T > 0 applied to both target and draft logits
+ *                 test at i, [gamma] the final draw (residual or bonus); NULL
+ *                 allowed when T == 0
+ *   temperature   T > 0 applied to both target and draft logits, or 0 (greedy)
  *   n_accepted    device out, [B] int32 in 0..gamma (-1: a draft token of this
  *                 sequence was outside [0, V); its out_tokens are all -1)
  *   out_tokens    device out, [B][gamma+1] int32: x_0..x_{n-1}, the final token,
@@ -147,8 +158,9 @@ size_t spec_reject_sample_workspace_size(int B, int gamma, int V, spec_dtype_t d
  * residual weights in fp32; row sums and all prefix sums in fp64; the accept
  * comparison in fp64.  Distributions are never assumed to sum to 1.
  * Errors: SPEC_ERR_ARG for null required pointers, B < 1, gamma < 1,
- * gamma > 31, V < 1, T <= 0 or not finite, or a small workspace;
- * SPEC_ERR_UNSUPPORTED for T == 0 (greedy verification is not implemented). */
+ * gamma > 31, V < 1, T < 0 or not finite, or a small workspace;
+ * SPEC_ERR_UNSUPPORTED when a row holds more than 1024 segments of the
+ * kernels' tiling (V above about 2 million). */
 spec_status_t spec_reject_sample(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                                  const double* uniforms, int B, int gamma, int V, float temperature,
                                  spec_dtype_t dtype, int32_t* n_accepted, int32_t* out_tokens, float* p_draft,

@@ -175,14 +175,21 @@ def reject_sample_workspace_size(B, gamma, V, dtype_code):
 
 def spec_reject_sample(target_logits, draft_logits, draft_tokens, uniforms, temperature, n_accepted=None,
                        out_tokens=None, p_draft=None, q_draft=None, want_probs=False, workspace=None, stream=None):
-    """Modified rejection sampling; returns (n_accepted [B], out_tokens [B, gamma+1], p_draft, q_draft)."""
+    """Modified rejection sampling; returns (n_accepted [B], out_tokens [B, gamma+1], p_draft, q_draft).
+
+    temperature 0 is greedy verification: draft_logits and uniforms are not
+    read and may be None.
+    """
     L = load()
     _need(target_logits, "target_logits")
     B, G1, V = target_logits.shape
     G = G1 - 1
-    _need(draft_logits, "draft_logits", target_logits.dtype, (B, G, V))
+    greedy = float(temperature) == 0.0
+    if not (greedy and draft_logits is None):
+        _need(draft_logits, "draft_logits", target_logits.dtype, (B, G, V))
     _need(draft_tokens, "draft_tokens", torch.int32, (B, G))
-    _need(uniforms, "uniforms", torch.float64, (B, G + 1))
+    if not (greedy and uniforms is None):
+        _need(uniforms, "uniforms", torch.float64, (B, G + 1))
     dev = target_logits.device
     if n_accepted is None:
         n_accepted = torch.empty(B, dtype=torch.int32, device=dev)

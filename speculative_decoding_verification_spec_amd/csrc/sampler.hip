@@ -448,6 +448,142 @@ __global__ __launch_bounds__(1024) void rs_tail(const T* __restrict__ tgt, const
   if (lane > n && lane <= G) ob[lane] = -1;
 }
 
+
+// ---------------------------------------------------------------------------
+// temperature 0: greedy verification
+// ---------------------------------------------------------------------------
+//
+// [P2] "LLM推論の高速化｜KVキャッシュと投機的デコーディングを自作で実測",
+// section 投機的デコーディングとは: the listing there leaves out its
+// temperature-0 branch; the results after it state that the accept test then
+// becomes "the target's argmax equals the draft", and that the output equals
+// greedy decoding with the target alone.  So: a_i = (argmax z_t[i] == x_i),
+// n = leading accepts, t = argmax z_t[n].  argmax is the first index of the
+// largest value, a NaN counting as largest.  Only the gamma+1 target rows are
+// read.
+//
+//   gs_stats  wave per two segments of a target row: the segment's argmax as
+//             one 64-bit key (ordered value key, then inverted index).
+//   gs_tail   workgroup per sequence: merges each row's keys, then one wave
+//             makes the decisions and writes the outputs.
+
+// Ordered key of a logit: a larger value gives a larger key; -0 and +0 are
+// equal; every NaN is above +inf.  Key 0 is below every value (padding).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  if (v != v) return 0xffffffffu;
+  const uint32_t u = (v == 0.f) ? 0u : __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// (key, index) -> one comparable word: larger key first, then smaller index.
+__device__ __forceinline__ uint64_t arg_word(uint32_t key, int idx) {
+  return ((uint64_t)key << 32) | (uint32_t)~(uint32_t)idx;
+}
+__device__ __forceinline__ int arg_index(uint64_t w) { return (int)~(uint32_t)w; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave), hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Grid: x = target row b * (gamma + 1) + r, y = group of waves along the row.
+template <typename T, int VEC, int NIT, int SPW>
+__global__ __launch_bounds__(1024) void gs_stats(const T* __restrict__ tgt, int V, int nseg, uint64_t* __restrict__ part) {
+  constexpr int SEG = kWave * VEC * NIT;
+  using Raw = typename RawVec<VEC * sizeof(T)>::type;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int seg0 = (blockIdx.y * (blockDim.x / kWave) + wave) * SPW;
+  if (seg0 >= nseg) return;  // uniform per wave
+  const T* row = tgt + (size_t)blockIdx.x * V;
+  uint64_t* out = part + (size_t)blockIdx.x * nseg;
+  Raw raw[SPW][NIT];
+  bool ok[SPW][NIT];
+#pragma unroll
+  for (int k = 0; k < SPW; ++k)
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = (seg0 + k) * SEG + (it * kWave + lane) * VEC;
+      ok[k][it] = idx < V;
+      if (ok[k][it]) raw[k][it] = *reinterpret_cast<const Raw*>(row + idx);
+    }
+#pragma unroll
+  for (int k = 0; k < SPW; ++k) {
+    const int seg = seg0 + k;
+    if (seg >= nseg) break;
+    // A lane sees its elements in increasing index order, so a strict '>'
+    // keeps the first of equal keys.  Every value's key exceeds 0.
+    uint32_t best = 0u;
+    int bidx = 0;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if (!ok[k][it]) continue;
+      float v[VEC];
+      raw_to_f32<T, VEC>(raw[k][it], v);
+      const int idx0 = seg * SEG + (it * kWave + lane) * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const uint32_t key = order_key(v[e]);
+        if (key > best) {
+          best = key;
+          bidx = idx0 + e;
+        }
+      }
+    }
+    const uint64_t w = wave_max_u64(best == 0u ? 0ull : arg_word(best, bidx));
+    if (lane == 0) out[seg] = w;
+  }
+}
+
+__global__ __launch_bounds__(1024) void gs_tail(const int32_t* __restrict__ xtok, int G, int V, int nseg,
+                                                const uint64_t* __restrict__ part, int32_t* __restrict__ n_out,
+                                                int32_t* __restrict__ tok_out, float* __restrict__ p_out,
+                                                float* __restrict__ q_out) {
+  __shared__ int arg[32];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int nwave = blockDim.x / kWave;
+  const int b = blockIdx.x;
+  const uint64_t* pb = part + (size_t)b * (G + 1) * nseg;
+  for (int r = wave; r <= G; r += nwave) {
+    uint64_t m = 0;
+    for (int k = lane; k < nseg; k += kWave) {
+      const uint64_t w = pb[(size_t)r * nseg + k];
+      m = w > m ? w : m;
+    }
+    m = wave_max_u64(m);
+    if (lane == 0) arg[r] = arg_index(m);
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  bool bad = false, reject = false;
+  if (lane < G) {
+    const int x = xtok[(size_t)b * G + lane];
+    bad = x < 0 || x >= V;
+    reject = bad || arg[lane] != x;
+    if (p_out) p_out[(size_t)b * G + lane] = bad ? __builtin_nanf("") : (arg[lane] == x ? 1.f : 0.f);
+    if (q_out) q_out[(size_t)b * G + lane] = __builtin_nanf("");  // the draft side is not read
+  }
+  const uint64_t bad_mask = __ballot(bad);
+  const uint64_t rej_mask = __ballot(reject);
+  const int n = rej_mask ? (__ffsll((long long)rej_mask) - 1) : G;
+  int32_t* ob = tok_out + (size_t)b * (G + 1);
+  if (bad_mask) {
+    if (lane == 0) n_out[b] = -1;
+    if (lane <= G) ob[lane] = -1;
+    return;
+  }
+  if (lane == 0) n_out[b] = n;
+  if (lane < n) ob[lane] = xtok[(size_t)b * G + lane];
+  if (lane == n) ob[lane] = arg[n];
+  if (lane > n && lane <= G) ob[lane] = -1;
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -523,6 +659,43 @@ static hipError_t rs_dispatch(const RsPlan& pl, const void* tgt, const void* drf
   return hipErrorInvalidValue;
 }
 
+template <typename T, int VEC, int NIT>
+static hipError_t gs_launch(const RsPlan& pl, const void* tgt, const int32_t* x, int B, int G, int V, char* ws,
+                            int32_t* n_out, int32_t* tok_out, float* p_out, float* q_out, hipStream_t stream) {
+  uint64_t* part = reinterpret_cast<uint64_t*>(ws + pl.off_part1);
+  constexpr int SPW = SPECV_RS_SEGS_PER_WAVE;
+  const int waves_row = (pl.nseg + SPW - 1) / SPW;
+  const int wpb = std::min(SPECV_RS_WAVES_PER_BLOCK, waves_row);
+  hipLaunchKernelGGL((gs_stats<T, VEC, NIT, SPW>), dim3((unsigned)((long)B * (G + 1)), (unsigned)((waves_row + wpb - 1) / wpb)),
+                     dim3(kWave * wpb), 0, stream, (const T*)tgt, V, pl.nseg, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nw = std::min(16, G + 1);
+  hipLaunchKernelGGL(gs_tail, dim3((unsigned)B), dim3(kWave * nw), 0, stream, x, G, V, pl.nseg, part, n_out, tok_out,
+                     p_out, q_out);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t gs_dispatch(const RsPlan& pl, const void* tgt, const int32_t* x, int B, int G, int V, char* ws,
+                              int32_t* n_out, int32_t* tok_out, float* p_out, float* q_out, hipStream_t s) {
+#define GS_CASE(VEC_, NIT_) \
+  if (pl.vec == VEC_ && pl.nit == NIT_) return gs_launch<T, VEC_, NIT_>(pl, tgt, x, B, G, V, ws, n_out, tok_out, p_out, q_out, s);
+  constexpr int LB = SPECV_RS_LANE_BYTES;
+  if constexpr (sizeof(T) == 2) {
+    GS_CASE(8, LB / 16)
+    GS_CASE(4, LB / 8)
+    GS_CASE(2, LB / 4)
+    GS_CASE(1, LB / 2)
+  } else {
+    GS_CASE(4, LB / 16)
+    GS_CASE(2, LB / 8)
+    GS_CASE(1, LB / 4)
+  }
+#undef GS_CASE
+  return hipErrorInvalidValue;
+}
+
 }  // namespace specv
 
 using namespace specv;
@@ -540,19 +713,28 @@ extern "C" spec_status_t spec_reject_sample(const void* target_logits, const voi
                                             int V, float temperature, spec_dtype_t dtype, int32_t* n_accepted,
                                             int32_t* out_tokens, float* p_draft, float* q_draft, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream) {
-  if (!target_logits || !draft_logits || !draft_tokens || !uniforms || !n_accepted || !out_tokens || !workspace)
-    return SPEC_ERR_ARG;
+  const bool greedy = temperature == 0.f;
+  if (!target_logits || !draft_tokens || !n_accepted || !out_tokens || !workspace) return SPEC_ERR_ARG;
+  if (!greedy && (!draft_logits || !uniforms)) return SPEC_ERR_ARG;  // greedy reads neither
   if (B < 1 || gamma < 1 || gamma > 31 || V < 1) return SPEC_ERR_ARG;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_ARG;
-  if (temperature == 0.f) return SPEC_ERR_UNSUPPORTED;
-  if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_ARG;
+  if (!greedy && (!(temperature > 0.f) || !isfinite(temperature))) return SPEC_ERR_ARG;
   if (workspace_bytes < spec_reject_sample_workspace_size(B, gamma, V, dtype)) return SPEC_ERR_ARG;
   if (rs_plan(B, gamma, V, dtype == SPEC_BF16 ? 2 : 4, 1).nseg > kMaxSeg) return SPEC_ERR_UNSUPPORTED;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
   const int esize = dtype == SPEC_BF16 ? 2 : 4;
   const int vec = pick_vec(V, esize, reinterpret_cast<uintptr_t>(target_logits),
-                           reinterpret_cast<uintptr_t>(draft_logits));
+                           reinterpret_cast<uintptr_t>(greedy ? target_logits : draft_logits));
   const RsPlan pl = rs_plan(B, gamma, V, esize, vec);
+  if (greedy) {
+    char* ws = static_cast<char*>(workspace);
+    const hipError_t e = dtype == SPEC_BF16
+                             ? gs_dispatch<uint16_t>(pl, target_logits, draft_tokens, B, gamma, V, ws, n_accepted,
+                                                     out_tokens, p_draft, q_draft, stream)
+                             : gs_dispatch<float>(pl, target_logits, draft_tokens, B, gamma, V, ws, n_accepted,
+                                                  out_tokens, p_draft, q_draft, stream);
+    return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+  }
   // 2^((z - M) * c) = exp((z - M) / T)
   const double c64 = 1.4426950408889634073599246810019 / (double)temperature;
   const float c32 = (float)c64;

@@ -71,9 +71,13 @@ def test_argument_checks_reject_before_launch():
     ws = ctypes.c_void_p(1 << 20)
     # null pointers
     assert L.spec_reject_sample(null, fake, fake, fake, 2, 2, 8, 1.0, 0, fake, fake, null, null, ws, 1 << 20, null) == 1
-    # greedy temperature is unsupported; negative is an argument error
-    assert L.spec_reject_sample(fake, fake, fake, fake, 2, 2, 8, 0.0, 0, fake, fake, null, null, ws, 1 << 20, null) == 3
+    # negative or NaN temperature is an argument error; T = 0 (greedy) needs no
+    # draft logits or uniforms but still checks the workspace
     assert L.spec_reject_sample(fake, fake, fake, fake, 2, 2, 8, -1.0, 0, fake, fake, null, null, ws, 1 << 20, null) == 1
+    nan = float("nan")
+    assert L.spec_reject_sample(fake, fake, fake, fake, 2, 2, 8, nan, 0, fake, fake, null, null, ws, 1 << 20, null) == 1
+    assert L.spec_reject_sample(fake, null, fake, null, 2, 2, 8, 0.0, 0, fake, fake, null, null, ws, 16, null) == 1
+    assert L.spec_reject_sample(fake, null, fake, fake, 2, 2, 8, 1.0, 0, fake, fake, null, null, ws, 1 << 20, null) == 1
     # workspace too small
     assert L.spec_reject_sample(fake, fake, fake, fake, 2, 2, 8, 1.0, 0, fake, fake, null, null, ws, 16, null) == 1
     # attention: cache overflow, bad head ratio, unsupported head dim

@@ -1,0 +1,125 @@
+"""GPU parity of greedy (temperature 0) verification through the C ABI.
+
+spec_reject_sample with T = 0 against ``oracle.greedy``: n_accepted, the
+emitted tokens and p_i(x_i) (1.0 or 0.0) must be identical -- the decisions
+are exact comparisons of the same decoded values, so there is no tolerance
+band -- and q_draft is NaN.  The draft logits and uniforms are passed as NULL
+(greedy verification reads neither).  Every case prints its name first.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_verification_spec_amd as sv
+import workloads as W
+from oracle import bf16 as obf16
+from oracle import greedy as G
+from tests import _gpu
+from workloads.gen import bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, **kw):
+    print(f"\n[case] {name} {kw}", flush=True)
+
+
+def _greedy_drafts(zd):
+    """A temperature-0 draft model proposes its own argmax (input generation)."""
+    return np.argmax(obf16.to_f64(zd), axis=-1).astype(np.int32)
+
+
+def _run(zt, x):
+    dev_zt, dev_x = _gpu.to_dev(zt), _gpu.to_dev(np.ascontiguousarray(x, np.int32))
+    n, tok, p, q = sv.spec_reject_sample(dev_zt, None, dev_x, None, 0.0, want_probs=True)
+    torch.cuda.synchronize()
+    return _gpu.to_host(n), _gpu.to_host(tok), _gpu.to_host(p), _gpu.to_host(q)
+
+
+def _check(zt, x, got, seqs=None):
+    n_g, t_g, p_g, q_g = got
+    if seqs is not None:
+        n_g, t_g, p_g, q_g = n_g[seqs], t_g[seqs], p_g[seqs], q_g[seqs]
+    n_o, t_o, p_o = G.verify_batch(zt, x)
+    assert np.array_equal(n_g, n_o), (np.nonzero(n_g != n_o)[0][:8], n_g[n_g != n_o][:8], n_o[n_g != n_o][:8])
+    assert np.array_equal(t_g, t_o)
+    assert np.array_equal(p_g.astype(np.float64), p_o)
+    assert np.all(np.isnan(q_g))
+    hist = np.bincount(n_o, minlength=x.shape[1] + 1)
+    print("n_accepted histogram", hist.tolist(), flush=True)
+    return hist
+
+
+@pytest.mark.parametrize("cid", [2, 4])
+def test_config_full(cid):
+    cfg = W.get(cid)
+    _case(f"greedy config{cid}", B=cfg.B, gamma=cfg.gamma, V=cfg.V, dtype=cfg.dtype)
+    inp = W.sampler_inputs(cfg)
+    zt = inp["target_logits"]
+    x = _greedy_drafts(inp["draft_logits"])
+    hist = _check(zt, x, _run(zt, x))
+    assert hist[0] > 0 and hist[1:].sum() > 0  # both rejections and acceptances occur
+    # the drafts as sampled at T = 1 (mostly rejected) and the target's own argmax (all accepted)
+    _check(zt, inp["draft_tokens"], _run(zt, inp["draft_tokens"]))
+    xa = np.argmax(obf16.to_f64(zt[:, : cfg.gamma]), axis=-1).astype(np.int32)
+    assert _check(zt, xa, _run(zt, xa))[cfg.gamma] == cfg.B
+
+
+def test_config5_full_size_sampled():
+    cfg = W.get(5)
+    _case("greedy config5", B=cfg.B, gamma=cfg.gamma, V=cfg.V)
+    d = W.sampler_inputs_device(cfg, "cuda", temperature=1.0)
+    x = torch.argmax(d["draft_logits"].float(), dim=-1).to(torch.int32)  # greedy drafts
+    n, tok, p, q = sv.spec_reject_sample(d["target_logits"], None, x, None, 0.0, want_probs=True)
+    torch.cuda.synchronize()
+    seqs = [0, 1, 100, 255]
+    zt = _gpu.to_host(d["target_logits"][seqs])
+    got = tuple(_gpu.to_host(a) for a in (n, tok, p, q))
+    _check(zt, _gpu.to_host(x[seqs]), got, seqs=seqs)
+    # every sequence: the emitted prefix and the final token are the target's argmax
+    am = torch.argmax(d["target_logits"].float(), dim=-1).cpu().numpy()  # first index of equal maxima
+    n_h, tok_h = got[0], got[1]
+    for b in range(cfg.B):
+        k = int(n_h[b])
+        assert np.array_equal(tok_h[b, : k + 1], am[b, : k + 1])
+
+
+def _row_cases(V, rng):
+    rows = []
+    base = rng.standard_normal(V).astype(np.float32)
+    r = base.copy(); r[[V // 7, V - 1]] = 9.0; rows.append(r)          # equal maxima far apart
+    r = base.copy(); r[-1] = 9.0; rows.append(r)                         # maximum at the last index
+    r = np.zeros(V, np.float32); r[0] = -0.0; rows.append(r)             # all zero, -0 first
+    r = np.full(V, -np.inf, np.float32); rows.append(r)                  # all -inf
+    r = base.copy(); r[V // 2] = np.nan; r[V // 3] = 50.0; rows.append(r)  # a NaN wins
+    r = base.copy(); r[1 % V] = np.inf; rows.append(r)
+    return rows
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,gamma", [(1, 1), (7, 3), (1003, 4), (4099, 2), (40000, 31), (151936, 4)])
+def test_edges(dtype, V, gamma):
+    _case("greedy edges", dtype=dtype, V=V, gamma=gamma)
+    rng = np.random.default_rng([V, gamma])
+    cases = _row_cases(V, rng)
+    B = 2 * len(cases) + 3
+    zt = rng.standard_normal((B, gamma + 1, V)).astype(np.float32)
+    for b in range(B):  # constructed rows at varying positions of the round
+        for i in range(gamma + 1):
+            if (b + i) % 2 == 0:
+                zt[b, i] = cases[(b + i) % len(cases)]
+    zs = bf16_bits(zt) if dtype == "bf16" else zt
+    am = np.argmax(obf16.to_f64(zs[:, :gamma]), axis=-1).astype(np.int32)
+    x = am.copy()
+    for b in range(B):
+        if b % 3 == 1:  # a mismatch at a position that varies with b
+            i = b % gamma
+            x[b, i] = (x[b, i] + 1) % V if V > 1 else 0
+    x[B - 1, gamma - 1] = V      # outside [0, V): the sequence is flagged
+    x[B - 2, 0] = -1
+    got = _run(zs, x)
+    ok = np.arange(B) < B - 2
+    _check(zs[ok], x[ok], tuple(a[ok] for a in got))
+    n_g, t_g = got[0], got[1]
+    assert np.all(n_g[B - 2 :] == -1) and np.all(t_g[B - 2 :] == -1)

@@ -202,8 +202,8 @@ def test_status_codes():
     x = torch.zeros((2, 2), dtype=torch.int32, device=dev)
     u = torch.zeros((2, 3), dtype=torch.float64, device=dev)
     with pytest.raises(sv.SpecError) as e:
-        sv.spec_reject_sample(zt, zd, x, u, 0.0)
-    assert e.value.status == 3  # greedy is not implemented
+        sv.spec_reject_sample(zt, zd, x, u, float("nan"))
+    assert e.value.status == 1
     with pytest.raises(sv.SpecError) as e:
         sv.spec_reject_sample(zt, zd, x, u, -1.0)
     assert e.value.status == 1
