@@ -22,6 +22,8 @@ Modules:
                 target's argmax, then the target's argmax)
   attention  -- KV append and causal multi-query verify attention, plus the
                 uncached full-sequence recompute it must agree with
+  paged      -- verify attention over a paged cache (block tables), and the
+                allocation-waste count of paging
   truncate   -- the KV length reset after verification
   formulas   -- closed forms: acceptance rate, expected committed tokens,
                 speed-up estimate, KV-cache bytes
@@ -33,4 +35,4 @@ Nothing is "parity unpinned" except the mapping of decisions that fall inside
 the 1e-6 threshold band (those draws are counted, not compared).
 """
 
-from . import attention, bf16, formulas, greedy, sampler, truncate  # noqa: F401
+from . import attention, bf16, formulas, greedy, paged, sampler, truncate  # noqa: F401

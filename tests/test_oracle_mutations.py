@@ -139,3 +139,25 @@ def test_greedy_inverted_accept_is_caught(monkeypatch):
 def test_greedy_last_index_ties_are_caught(monkeypatch):
     monkeypatch.setattr(G, "argmax", lambda z: int(len(z) - 1 - np.argmax(np.asarray(G.to_f64(z))[::-1])))
     _assert_pin_fails(TG.test_argmax_conventions)
+
+
+# ---- paged cache --------------------------------------------------------------
+
+from oracle import paged as Pg  # noqa: E402
+from tests import test_oracle_paged as TP  # noqa: E402
+
+
+def test_paged_pins_hold_unmutated():
+    TP.test_allocation_waste_matches_the_page(16, 0.007)
+    TP.test_paging_does_not_change_attention(True)
+
+
+def test_floor_block_count_is_caught(monkeypatch):
+    monkeypatch.setattr(Pg, "blocks_needed", lambda length, page: int(length) // int(page))
+    _assert_pin_fails(lambda: TP.test_allocation_waste_matches_the_page(16, 0.007))
+
+
+def test_ignoring_the_block_table_is_caught(monkeypatch):
+    real = Pg.gather
+    monkeypatch.setattr(Pg, "gather", lambda pages, row, length: real(pages, np.arange(len(row)), length))
+    _assert_pin_fails(lambda: TP.test_paging_does_not_change_attention(True))
