@@ -94,6 +94,37 @@ def algorithmic(cfg, lens, B, greedy=False):
     return att_bytes, att_flops, smp_bytes
 
 
+def paginate(att, cfg, hint, page, rep):
+    """Paged copies of the caches: [num_pages, Hkv, page, D] at seeded random slots, plus the block table."""
+    import torch
+
+    lens = att["lens"].cpu().numpy().astype(np.int64)
+    need = -(-(lens + cfg.n_q) // page)
+    max_blocks = -(-(hint + cfg.n_q) // page)
+    num_pages = int(need.sum())
+    g = torch.Generator(device="cpu").manual_seed(7919 * cfg.cid + rep)
+    perm = torch.randperm(num_pages, generator=g).to(torch.int32)
+    table = torch.full((cfg.B, max_blocks), -1, dtype=torch.int32)
+    off = 0
+    for b in range(cfg.B):
+        table[b, : need[b]] = perm[off : off + need[b]]
+        off += int(need[b])
+    table = table.to(att["k_cache"].device)
+    out = {}
+    for name in ("k_cache", "v_cache"):
+        c = att[name]
+        pages = torch.empty((num_pages, cfg.Hkv, page, cfg.D), dtype=c.dtype, device=c.device)
+        for b in range(cfg.B):
+            nb = int(need[b])
+            rows = min(nb * page, c.shape[2])
+            blk = torch.zeros((cfg.Hkv, nb * page, cfg.D), dtype=c.dtype, device=c.device)
+            blk[:, :rows] = c[b, :, :rows]
+            pages[table[b, :nb].long()] = blk.view(cfg.Hkv, nb, page, cfg.D).transpose(0, 1)
+        out[name.replace("cache", "pages")] = pages
+    out["table"] = table
+    return out
+
+
 def make_inputs(cfg, device, temperature, rep):
     import torch
 
@@ -127,6 +158,7 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
 
     from oracle import attention as A
     from oracle import greedy as Gr
+    from oracle import paged as Pg
     from oracle import sampler as S
     from workloads.device import to_host
 
@@ -138,11 +170,20 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
             sl = slice(int(b), int(b) + 1)
             L = int(att["lens_base"][sl].item())
             host = {k: to_host(att[k][sl]) for k in ("q", "k_new", "v_new")}
-            host["k_cache"] = to_host(att["k_cache"][sl, :, :L])
-            host["v_cache"] = to_host(att["v_cache"][sl, :, :L])
-            s0 = time.perf_counter()
-            A.verify_attention(host["q"], host["k_new"], host["v_new"], host["k_cache"], host["v_cache"],
-                               np.array([L]))
+            if "k_pages" in att:  # this sequence's pages, renumbered 0..nb-1
+                page = att["k_pages"].shape[2]
+                nb = -(-L // page)
+                rows = att["table"][b, :nb].long()
+                kp, vp = to_host(att["k_pages"][rows]), to_host(att["v_pages"][rows])
+                tab = np.arange(nb, dtype=np.int32)[None]
+                s0 = time.perf_counter()
+                Pg.verify_attention_paged(host["q"], host["k_new"], host["v_new"], kp, vp, tab, np.array([L]))
+            else:
+                host["k_cache"] = to_host(att["k_cache"][sl, :, :L])
+                host["v_cache"] = to_host(att["v_cache"][sl, :, :L])
+                s0 = time.perf_counter()
+                A.verify_attention(host["q"], host["k_new"], host["v_new"], host["k_cache"], host["v_cache"],
+                                   np.array([L]))
             t_att = time.perf_counter() - s0
             sh = {k: to_host(smp[k][sl]) for k in ("target_logits", "draft_logits", "draft_tokens", "uniforms")}
             s1 = time.perf_counter()
@@ -203,6 +244,8 @@ def main():
     ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
     ap.add_argument("--temperature", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--paged", type=int, default=0, choices=(0, 16, 32),
+                    help="run attention over a paged copy of the cache with this page size")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -244,6 +287,11 @@ def main():
     nsets = max(1, min(4, math.ceil(768e6 / (att_bytes_est + smp_bytes_est))))
     sets = [make_inputs(cfg, dev, T, rep) for rep in range(nsets)]
     hint = cfg.L[1]
+    if args.paged:
+        for rep, (att, _) in enumerate(sets):
+            att.update(paginate(att, cfg, hint, args.paged, rep))
+            del att["k_cache"], att["v_cache"]  # the paged copies are the cache now
+        torch.cuda.empty_cache()
     B = cfg.B
 
     stream = torch.cuda.current_stream()
@@ -254,8 +302,12 @@ def main():
         att["lens"].copy_(att["lens_base"])
         if events:
             events[0].record(stream)
-        sv.spec_verify_attention(att["q"], att["k_new"], att["v_new"], att["k_cache"], att["v_cache"], att["lens"],
-                                 hint, out=att["out"])
+        if args.paged:
+            sv.spec_verify_attention_paged(att["q"], att["k_new"], att["v_new"], att["k_pages"], att["v_pages"],
+                                           att["table"], att["lens"], hint, out=att["out"])
+        else:
+            sv.spec_verify_attention(att["q"], att["k_new"], att["v_new"], att["k_cache"], att["v_cache"],
+                                     att["lens"], hint, out=att["out"])
         if events:
             events[1].record(stream)
         greedy = T == 0
@@ -321,6 +373,7 @@ def main():
             "gamma": cfg.gamma,
             "temperature": T,
             "input_sets": nsets,
+            "kv_cache": f"paged, {args.paged}-position pages at random slots" if args.paged else "contiguous",
         },
         "roofline": {
             "bound": "hbm",

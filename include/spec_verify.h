@@ -109,6 +109,40 @@ spec_status_t spec_verify_attention(const void* q, const void* k_new, const void
                                     int n_q, int D, int max_T, int max_len_hint, float scale, spec_dtype_t dtype,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Verify attention with KV append over a paged cache.
+ *
+ * Defined by [P2] section PagedAttentionとKVキャッシュの量子化 (paging): a
+ * sequence's cache positions are held in fixed blocks of page_size positions,
+ * and a block table lists the page of each of its blocks; the attention is
+ * that of spec_verify_attention on the sequence's positions in table order.
+ *
+ *   k_pages, v_pages device, [num_pages][Hkv][page_size][D] dtype, in/out:
+ *            position j of sequence b, KV head g, is
+ *            pages[block_table[b][j / page_size]][g][j % page_size].  The new
+ *            rows go to positions [cache_len[b], cache_len[b] + n_q); no other
+ *            position is written, positions >= cache_len[b] are never read.
+ *            Pages may be shared by several sequences for reading; the pages
+ *            receiving new rows must not be.
+ *   block_table device, [B][max_blocks] int32: entries for the blocks that hold
+ *            positions [0, cache_len[b] + n_q) must lie in [0, num_pages).
+ *   page_size 16 or 32.
+ *   The other arguments are those of spec_verify_attention; the workspace size
+ *   is spec_verify_attention_workspace_size(...) for the same sizes.
+ * Supported: dtype SPEC_BF16, D in {64, 128}, B <= 1024, and the limits of
+ * spec_verify_attention.
+ * Errors: as spec_verify_attention, with max_T = max_blocks * page_size;
+ * SPEC_ERR_ARG for a null block_table, num_pages < 1 or max_blocks < 1;
+ * SPEC_ERR_UNSUPPORTED for another page size, dtype, or B > 1024.  A sequence
+ * with a table entry outside [0, num_pages) gets NaN output rows and nothing is
+ * written through that entry; a negative cache_len[b] or one above
+ * max_len_hint is handled as in spec_verify_attention. */
+spec_status_t spec_verify_attention_paged(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                                          void* v_pages, const int32_t* block_table, const int32_t* cache_len,
+                                          void* out, int B, int Hq, int Hkv, int n_q, int D, int page_size,
+                                          int num_pages, int max_blocks, int max_len_hint, float scale,
+                                          spec_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Modified rejection sampler                                                 */
 /* ------------------------------------------------------------------------- */

@@ -4,7 +4,9 @@ The step is three calls into the C-ABI library libspecverify.so, bound here
 with ctypes (see include/spec_verify.h for the contract of each):
 
   spec_verify_attention  KV append + causal multi-query verify attention (GQA)
+  spec_verify_attention_paged  the same over a paged cache (block tables)
   spec_reject_sample     modified rejection sampling over the vocabulary
+                         (greedy verification at temperature 0)
   spec_kv_truncate       length reset after the round
 
 PyTorch supplies device memory and streams; all arithmetic runs in the HIP
@@ -22,6 +24,7 @@ from ._lib import (  # noqa: F401
     spec_kv_truncate,
     spec_reject_sample,
     spec_verify_attention,
+    spec_verify_attention_paged,
     verify_attention_workspace_size,
     version,
 )

@@ -25,6 +25,7 @@ EXPORTED = (
     "spec_status_string",
     "spec_verify_attention_workspace_size",
     "spec_verify_attention",
+    "spec_verify_attention_paged",
     "spec_reject_sample_workspace_size",
     "spec_reject_sample",
     "spec_kv_truncate",
@@ -60,6 +61,8 @@ def load(path=LIB_PATH):
     L.spec_verify_attention_workspace_size.argtypes = [c_int] * 6 + [c_int]
     L.spec_verify_attention.restype = c_int
     L.spec_verify_attention.argtypes = [vp] * 7 + [c_int] * 7 + [c_float, c_int, vp, c_size, vp]
+    L.spec_verify_attention_paged.restype = c_int
+    L.spec_verify_attention_paged.argtypes = [vp] * 8 + [c_int] * 9 + [c_float, c_int, vp, c_size, vp]
     L.spec_reject_sample_workspace_size.restype = c_size
     L.spec_reject_sample_workspace_size.argtypes = [c_int] * 4
     L.spec_reject_sample.restype = c_int
@@ -166,6 +169,43 @@ def spec_verify_attention(q, k_new, v_new, k_cache, v_cache, cache_len, max_len_
         B, Hq, Hkv, n_q, D, max_T, int(max_len_hint), scale, dt, _ptr(ws), ws.numel(), _stream(stream),
     )
     _check("spec_verify_attention", st)
+    return out
+
+
+def spec_verify_attention_paged(q, k_new, v_new, k_pages, v_pages, block_table, cache_len, max_len_hint, out=None,
+                                scale=None, workspace=None, stream=None):
+    """Verify attention with KV append over a paged cache; returns ``out`` [B, Hq, n_q, D].
+
+    k_pages, v_pages: [num_pages, Hkv, page_size, D]; block_table: int32 [B, max_blocks].
+    """
+    L = load()
+    _need(q, "q")
+    B, Hq, n_q, D = q.shape
+    Hkv = k_new.shape[1]
+    num_pages, _, page, _ = k_pages.shape
+    _need(k_new, "k_new", q.dtype, (B, Hkv, n_q, D))
+    _need(v_new, "v_new", q.dtype, (B, Hkv, n_q, D))
+    _need(k_pages, "k_pages", q.dtype, (num_pages, Hkv, page, D))
+    _need(v_pages, "v_pages", q.dtype, (num_pages, Hkv, page, D))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise SpecError("spec_verify_attention_paged", SPEC_ERR_ARG, "block_table must be [B, max_blocks]")
+    _need(cache_len, "cache_len", torch.int32, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", q.dtype, q.shape)
+    dt = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = L.spec_verify_attention_workspace_size(B, Hq, Hkv, n_q, D, int(max_len_hint), dt)
+    if nbytes == 0:
+        raise SpecError("spec_verify_attention_workspace_size", SPEC_ERR_UNSUPPORTED, "no valid size")
+    ws = _workspace(workspace, "attn", nbytes, q.device)
+    st = L.spec_verify_attention_paged(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(cache_len),
+        _ptr(out), B, Hq, Hkv, n_q, D, page, num_pages, block_table.shape[1], int(max_len_hint), scale, dt,
+        _ptr(ws), ws.numel(), _stream(stream),
+    )
+    _check("spec_verify_attention_paged", st)
     return out
 
 

@@ -86,6 +86,10 @@ struct AttnArgs {
   int* pre;  // stream scheme: [B + 1] blocks per slab before sequence b
   int B, Hq, Hkv, n_q, G, M, RG, RT, NSP, C, max_T, hint;
   int P, MINB, JP;  // stream scheme: workgroups, minimum share, partial slots per slab
+  // Paged cache: kc / vc are [num_pages][Hkv][page][D]; table[b * max_blocks + i]
+  // is the page of logical block i of sequence b.
+  const int32_t* table;  // null: contiguous cache [B][Hkv][max_T][D]
+  int page, max_blocks, num_pages;
   float qk_scale;  // scale * log2(e)
 };
 
@@ -133,6 +137,24 @@ __device__ __forceinline__ void append_rows(const AttnArgs& a, long bg, int L, i
   for (int c = tid; c < chunks; c += nthreads) {
     dkc[c] = skn[c];
     dvc[c] = svn[c];
+  }
+}
+
+// A1 into a paged cache: row L + r of (b, g) goes to slot (L + r) % PG of the
+// page the table lists for block (L + r) / PG (entries checked by the caller).
+template <int D, int PG>
+__device__ __forceinline__ void append_rows_paged(const AttnArgs& a, int b, int g, int L, int tid, int nthreads) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const int chunks = a.n_q * CPR;
+  const long bg = (long)b * a.Hkv + g;
+  const uint4* skn = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.kn) + (size_t)bg * a.n_q * D);
+  const uint4* svn = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.vn) + (size_t)bg * a.n_q * D);
+  for (int c = tid; c < chunks; c += nthreads) {
+    const int pos = L + c / CPR;
+    const size_t page = (size_t)a.table[(size_t)b * a.max_blocks + pos / PG];
+    const size_t row = ((page * a.Hkv + g) * PG + pos % PG) * CPR + c % CPR;
+    reinterpret_cast<uint4*>(a.kc)[row] = skn[c];
+    reinterpret_cast<uint4*>(a.vc)[row] = svn[c];
   }
 }
 
@@ -251,7 +273,7 @@ __device__ __forceinline__ float group_sum(float v) {
 // output) at partial slot `slot`.  append: also copy the n_q new rows of
 // (b, g) into the cache (A1).  kbuf / vbuf map a stage index to its LDS
 // objects.  Every wave of the workgroup calls it with the same arguments.
-template <int D, int NW, int NST, typename KBuf, typename VBuf>
+template <int D, int NW, int NST, int PG, typename KBuf, typename VBuf>
 __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vbuf, int b, int g, int rg, int L,
                                            int k0, int k1, bool whole, size_t slot, bool append) {
   using LY = BfLayout<D>;
@@ -274,10 +296,47 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
   const long bg = (long)b * a.Hkv + g;
   const int Ltot = L + a.n_q;
   const int nblk = (k1 - k0 + KB - 1) / KB;
+  static_assert(PG == 0 || PG == 16 || PG == 32, "page size");
+  const int32_t* tab = PG ? a.table + (size_t)b * a.max_blocks : nullptr;
+  if constexpr (PG > 0) {
+    // Every table entry this piece will use (the committed keys it reads and,
+    // if it appends, the pages of the new rows) must name a page; otherwise
+    // the piece reads nothing and leaves NaN (every wave finds the same).
+    bool badp = false;
+    const int e1 = (min(k1, L) + PG - 1) / PG;
+    for (int e = k0 / PG + lane; e < e1; e += kWave) {
+      const int pg = tab[e];
+      badp |= pg < 0 || pg >= a.num_pages;
+    }
+    if (append) {
+      for (int e = L / PG + lane; e <= (Ltot - 1) / PG; e += kWave) {
+        const int pg = tab[e];
+        badp |= pg < 0 || pg >= a.num_pages;
+      }
+    }
+    if (__ballot(badp)) {
+      const float qnan = __builtin_nanf("");
+      const int m = rg * 16 * NW + 16 * wave + lr;
+      if (whole) {
+        if (m < a.M && lg == 0) {
+          uint16_t* o = static_cast<uint16_t*>(a.out) +
+                        (((size_t)b * a.Hq + g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D;
+          for (int d = 0; d < D; ++d) o[d] = 0x7fc0;
+        }
+      } else {
+        const int row = 16 * wave + lr;
+        if (lg == 0) a.part_ml[slot * (16 * NW) + row] = ML{qnan, qnan};
+        float* po = a.part_o + slot * (16 * NW) * D + (size_t)row * D;
+        for (int d = lg; d < D; d += 4) po[d] = qnan;
+      }
+      return;
+    }
+  }
 
   const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (size_t)bg * a.max_T * D;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + (size_t)bg * a.max_T * D;
+  // Contiguous cache: the (b, g) slab.  Paged: the page array (per-block bases below).
+  const uint16_t* kc = static_cast<const uint16_t*>(a.kc) + (PG ? 0 : (size_t)bg * a.max_T * D);
+  const uint16_t* vc = static_cast<const uint16_t*>(a.vc) + (PG ? 0 : (size_t)bg * a.max_T * D);
   const uint16_t* knb = static_cast<const uint16_t*>(a.kn) + (size_t)bg * a.n_q * D;
   const uint16_t* vnb = static_cast<const uint16_t*>(a.vn) + (size_t)bg * a.n_q * D;
 
@@ -297,9 +356,26 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
     const int sl = p % LY::CH;
     cchunk[i] = is_v ? LY::vslot(crow[i], sl) : LY::kslot(crow[i], sl);  // XOR is its own inverse
   }
+  // Start of committed key `key` (< L) of (b, g) in a cache.
+  auto cache_row = [&](const uint16_t* cache, int key) -> const uint16_t* {
+    if constexpr (PG == 0) {
+      return cache + (size_t)key * D;
+    } else {
+      return cache + (((size_t)tab[key / PG] * a.Hkv + g) * PG + key % PG) * D;
+    }
+  };
   auto issue_block = [&](int kb, auto S) {
     if (wave >= WI) return;
     const bool full = kb + KB <= L;  // every key of the block is committed cache
+    // Paged: the block's pages (kb is a multiple of 32, so a block is one
+    // 32-page or two 16-pages); row r of the block is at base + r D.
+    size_t pbase0 = 0, pbase1 = 0;
+    if constexpr (PG > 0) {
+      if (full) {
+        pbase0 = ((size_t)tab[kb / PG] * a.Hkv + g) * PG * D;
+        if constexpr (PG == 16) pbase1 = ((size_t)tab[kb / PG + 1] * a.Hkv + g) * PG * D - (size_t)16 * D;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
       const bool is_v = i >= LY::NI / WI;
@@ -309,9 +385,14 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
       const int key = kb + crow[i];
       const uint16_t* src;
       if (full) {
-        src = cache + (size_t)kb * D + (crow[i] * D + 8 * cchunk[i]);
+        if constexpr (PG == 0) {
+          src = cache + (size_t)kb * D + (crow[i] * D + 8 * cchunk[i]);
+        } else {
+          const size_t base = (PG == 16 && crow[i] >= 16) ? pbase1 : pbase0;
+          src = cache + base + (crow[i] * D + 8 * cchunk[i]);
+        }
       } else {  // new rows from k_new/v_new; keys past the end read a finite dummy row
-        src = (key < L ? cache + (size_t)key * D : fresh + (size_t)(key < Ltot ? key - L : 0) * D) + 8 * cchunk[i];
+        src = (key < L ? cache_row(cache, key) : fresh + (size_t)(key < Ltot ? key - L : 0) * D) + 8 * cchunk[i];
       }
       uint16_t* dst = (is_v ? vbuf(S) : kbuf(S)) + cc * 512;
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -459,7 +540,13 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
   }
 
   // A1 (once per (b, g)); nothing in this launch reads these rows.
-  if (append) append_rows<uint16_t, D>(a, bg, L, tid, 64 * NW);
+  if (append) {
+    if constexpr (PG == 0) {
+      append_rows<uint16_t, D>(a, bg, L, tid, 64 * NW);
+    } else {
+      append_rows_paged<D, PG>(a, b, g, L, tid, 64 * NW);
+    }
+  }
 
   const float lt = group_sum(lsum);  // row sum over the 4 lane groups
   const int row = 16 * wave + lr;    // row within the item
@@ -496,7 +583,7 @@ void attn_split_bf16(AttnArgs a) {
   const int Ltot = L + a.n_q;
   const int k0 = it.sp * a.C;
   if (k0 >= Ltot) return;
-  bf16_piece<D, NW, NST>(a, kbuf, vbuf, it.b, it.g, it.rg, L, k0, min(k0 + a.C, Ltot), Ltot <= a.C, it.id,
+  bf16_piece<D, NW, NST, 0>(a, kbuf, vbuf, it.b, it.g, it.rg, L, k0, min(k0 + a.C, Ltot), Ltot <= a.C, it.id,
                          it.sp == 0 && it.rg == 0);
 }
 
@@ -542,7 +629,7 @@ __device__ __forceinline__ long long stream_share(const AttnArgs& a, long long W
 // lengths, and one workgroup per slot means no workgroup waits to be
 // dispatched.  Workgroup 0 also stores the per-slab block prefix pre[b] for
 // the combine.
-template <int D, int NW, int NST>
+template <int D, int NW, int NST, int PG>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
 void attn_stream_bf16(AttnArgs a) {
   using LY = BfLayout<D>;
@@ -626,7 +713,7 @@ void attn_stream_bf16(AttnArgs a) {
       first = false;
       const int L = ufl(a.len[b]);
       const size_t slot = (((size_t)b * a.Hkv + g) * a.RG + rg) * a.JP + (size_t)j;
-      bf16_piece<D, NW, NST>(a, kbuf, vbuf, b, g, rg, L, off * KB, min(end * KB, L + a.n_q), whole, slot,
+      bf16_piece<D, NW, NST, PG>(a, kbuf, vbuf, b, g, rg, L, off * KB, min(end * KB, L + a.n_q), whole, slot,
                              off == 0 && rg == 0);
     }
     x = uniform64(x + take);
@@ -1014,16 +1101,22 @@ static int stream_workgroups(K kernel, int NW) {
   return P;
 }
 
+template <int D, int NW, int PG>
+static hipError_t launch_stream(const AttnArgs& a0, hipStream_t s) {
+  AttnArgs a = a0;
+  a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG>, NW);
+  hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int NW>
 static hipError_t launch_bf16(const AttnArgs& a0, hipStream_t s) {
   if (a0.pre) {  // stream scheme
-    AttnArgs a = a0;
-    a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages>, NW);
-    hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
-    return hipGetLastError();
+    if (a0.table) return a0.page == 16 ? launch_stream<D, NW, 16>(a0, s) : launch_stream<D, NW, 32>(a0, s);
+    return launch_stream<D, NW, 0>(a0, s);
   }
   const AttnArgs& a = a0;
   const size_t items = (size_t)a.B * a.Hkv * a.RG * a.NSP;
@@ -1101,11 +1194,13 @@ extern "C" size_t spec_verify_attention_workspace_size(int B, int Hq, int Hkv, i
   return std::max(split_bytes, stream_bytes);
 }
 
-extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
-                                               void* v_cache, const int32_t* cache_len, void* out, int B, int Hq,
-                                               int Hkv, int n_q, int D, int max_T, int max_len_hint, float scale,
-                                               spec_dtype_t dtype, void* workspace, size_t workspace_bytes,
-                                               hipStream_t stream) {
+// Shared by the contiguous and the paged entry points.  Paged: table != null,
+// k_cache / v_cache are the page arrays, max_T is unused.
+static spec_status_t verify_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                      void* v_cache, const int32_t* cache_len, void* out, int B, int Hq, int Hkv,
+                                      int n_q, int D, int max_T, int max_len_hint, float scale, spec_dtype_t dtype,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                      const int32_t* table, int page, int num_pages, int max_blocks) {
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_len || !out || !workspace) return SPEC_ERR_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || n_q < 1 || D < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
   if (Hq % Hkv != 0) return SPEC_ERR_ARG;
@@ -1119,6 +1214,7 @@ extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new,
   if (n_q > 16 || (Hq / Hkv) * n_q > 256 || !supported(dtype, D)) return SPEC_ERR_UNSUPPORTED;
   const AttnPlan p = attn_plan(B, Hq, Hkv, n_q, D, max_len_hint, dtype);
   const bool use_stream = stream_ok(dtype, B, Hkv, p.RG, n_q, max_len_hint);
+  if (table && !use_stream) return SPEC_ERR_UNSUPPORTED;  // paged: bf16, B <= 1024
   const StreamPlan sp = use_stream ? stream_plan(B, Hkv, p.RG, p.RT, n_q, D, max_len_hint) : StreamPlan{};
   if (workspace_bytes < (use_stream ? sp.total : p.total)) return SPEC_ERR_ARG;
   if ((size_t)B * Hkv * p.RG * p.NSP > 0x7fffffffu) return SPEC_ERR_UNSUPPORTED;
@@ -1138,6 +1234,10 @@ extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new,
   a.P = 0;
   a.MINB = sp.MINB;
   a.JP = sp.JP;
+  a.table = table;
+  a.page = page;
+  a.max_blocks = max_blocks;
+  a.num_pages = num_pages;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -1163,4 +1263,31 @@ extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new,
     else if (D == 128) e = launch_f32_d<128>(a, stream);
   }
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
+
+extern "C" spec_status_t spec_verify_attention(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                               void* v_cache, const int32_t* cache_len, void* out, int B, int Hq,
+                                               int Hkv, int n_q, int D, int max_T, int max_len_hint, float scale,
+                                               spec_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                                               hipStream_t stream) {
+  return verify_attention(q, k_new, v_new, k_cache, v_cache, cache_len, out, B, Hq, Hkv, n_q, D, max_T, max_len_hint,
+                          scale, dtype, workspace, workspace_bytes, stream, nullptr, 0, 0, 0);
+}
+
+extern "C" spec_status_t spec_verify_attention_paged(const void* q, const void* k_new, const void* v_new,
+                                                     void* k_pages, void* v_pages, const int32_t* block_table,
+                                                     const int32_t* cache_len, void* out, int B, int Hq, int Hkv,
+                                                     int n_q, int D, int page_size, int num_pages, int max_blocks,
+                                                     int max_len_hint, float scale, spec_dtype_t dtype,
+                                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!block_table) return SPEC_ERR_ARG;
+  if (page_size != 16 && page_size != 32) return SPEC_ERR_UNSUPPORTED;
+  if (num_pages < 1 || max_blocks < 1) return SPEC_ERR_ARG;
+  if (dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
+  // The logical capacity of a sequence is max_blocks pages.
+  const long cap = (long)max_blocks * page_size;
+  if (cap > 0x7fffffffL) return SPEC_ERR_ARG;
+  return verify_attention(q, k_new, v_new, k_pages, v_pages, cache_len, out, B, Hq, Hkv, n_q, D, (int)cap,
+                          max_len_hint, scale, dtype, workspace, workspace_bytes, stream, block_table, page_size,
+                          num_pages, max_blocks);
 }

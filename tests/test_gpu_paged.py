@@ -1,0 +1,153 @@
+"""GPU parity of spec_verify_attention_paged (paged KV cache, block tables).
+
+The caches of the contiguous workloads are cut into pages placed at seeded
+random physical slots; unused slots hold NaN.  The output must match the
+oracle (bf16 tolerance) and be bit-identical to the contiguous kernel on the
+same data; the new rows must land in the slots the table names and no other
+slot may change.  Every case prints its name first.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_verification_spec_amd as sv
+import workloads as W
+from oracle import paged as P
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = np.uint16(0x7FC0)
+
+
+def _case(name, **kw):
+    print(f"\n[case] {name} {kw}", flush=True)
+
+
+def _paginate(cache, lens, n_q, page, rng, hint, spare=3, share_prefix=False):
+    """Pages [num_pages, Hkv, page, D] and table [B, max_blocks] holding cache[b, :, :L_b].
+
+    The table has room for hint + n_q positions, as the call requires.
+    """
+    B, Hkv, _, D = cache.shape
+    need = [P.blocks_needed(int(L) + n_q, page) for L in lens]
+    max_blocks = max(max(need), P.blocks_needed(hint + n_q, page))
+    num_pages = sum(need) + spare
+    perm = rng.permutation(num_pages)
+    pages = np.full((num_pages, Hkv, page, D), NAN_BF16, dtype=cache.dtype)
+    table = np.full((B, max_blocks), -7, np.int32)  # entries past a sequence's blocks are never used
+    k = 0
+    for b in range(B):
+        for i in range(need[b]):
+            table[b, i] = perm[k]
+            k += 1
+    if share_prefix:  # sequence 1 reads sequence 0's first full blocks
+        full0 = min(int(lens[0]), int(lens[1])) // page
+        table[1, :full0] = table[0, :full0]
+    for b in range(B):
+        L = int(lens[b])
+        for pos0 in range(0, L, page):
+            m = min(page, L - pos0)
+            pages[table[b, pos0 // page], :, :m] = cache[b, :, pos0 : pos0 + m]
+    return pages, table
+
+
+def _run(inp, page, rng, hint=None, share_prefix=False, corrupt=None):
+    lens = inp["lens"]
+    n_q = inp["q"].shape[2]
+    if share_prefix:
+        full0 = min(int(lens[0]), int(lens[1])) // page * page
+        inp["k_cache"][1, :, :full0] = inp["k_cache"][0, :, :full0]
+        inp["v_cache"][1, :, :full0] = inp["v_cache"][0, :, :full0]
+    hint = int(lens.max()) if hint is None else hint
+    kp, table = _paginate(inp["k_cache"], lens, n_q, page, np.random.default_rng(rng), hint, share_prefix=share_prefix)
+    vp, _ = _paginate(inp["v_cache"], lens, n_q, page, np.random.default_rng(rng), hint, share_prefix=share_prefix)
+    if corrupt is not None:
+        b, i, val = corrupt
+        table[b, i] = val
+    d = {k: _gpu.to_dev(v) for k, v in inp.items()}
+    dkp, dvp, dtab = _gpu.to_dev(kp), _gpu.to_dev(vp), _gpu.to_dev(table)
+    out = sv.spec_verify_attention_paged(d["q"], d["k_new"], d["v_new"], dkp, dvp, dtab, d["lens"], hint)
+    ref = sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], hint)
+    torch.cuda.synchronize()
+    return (_gpu.to_host(out), _gpu.to_host(ref), kp, vp, table, _gpu.to_host(dkp), _gpu.to_host(dvp))
+
+
+def _check(inp, page, res, skip=()):
+    out, ref, kp, vp, table, kp2, vp2 = res
+    lens = inp["lens"]
+    n_q = inp["q"].shape[2]
+    seqs = [b for b in range(len(lens)) if b not in skip]
+    want = P.verify_attention_paged(inp["q"], inp["k_new"], inp["v_new"], kp, vp, table, lens, seqs=seqs)
+    got = _gpu.as_f64(out[seqs])
+    err = np.max(np.abs(got - want))
+    print("max abs err", err, flush=True)
+    assert np.all(np.isfinite(got)) and err < _gpu.ATT_TOL["bf16"]
+    assert np.array_equal(out[seqs], ref[seqs])  # same bits as the contiguous kernel
+    # the new rows, and nothing else, were written
+    kw, vw = P.kv_append_paged(kp, vp, inp["k_new"][seqs], inp["v_new"][seqs], table[seqs], lens[seqs])
+    assert np.array_equal(kp2, kw) and np.array_equal(vp2, vw)
+
+
+@pytest.mark.parametrize("page", [16, 32])
+def test_config4_paged(page):
+    cfg = W.get(4)
+    _case("paged config4", B=cfg.B, page=page)
+    inp = W.attention_inputs(cfg)
+    _check(inp, page, _run(inp, page, rng=page, hint=cfg.L[1]))
+
+
+@pytest.mark.parametrize(
+    "B,Hq,Hkv,n_q,D,lens,page",
+    [
+        (3, 8, 2, 5, 128, [0, 31, 33], 16),       # empty cache, block edges
+        (2, 16, 2, 9, 128, [257, 2000], 32),      # 72 rows per KV head (5 tiles)
+        (2, 4, 4, 1, 64, [1, 1000], 16),          # n_q = 1, D = 64
+        (1, 8, 1, 5, 128, [3000], 32),            # one sequence over many workgroups
+    ],
+)
+def test_shapes(B, Hq, Hkv, n_q, D, lens, page):
+    _case("paged shape", B=B, Hq=Hq, Hkv=Hkv, n_q=n_q, D=D, lens=lens, page=page)
+    max_T = max(lens) + n_q + 7
+    cfg = W.Config(96, "paged", B=B, gamma=n_q - 1, V=1, dtype="bf16", Hq=Hq, Hkv=Hkv, D=D, L=(0, max(lens)),
+                   max_T=max_T)
+    inp = W.attention_inputs(cfg, B=B, max_T=max_T, lens=lens)
+    _check(inp, page, _run(inp, page, rng=B))
+
+
+def test_shared_prefix_pages():
+    cfg = W.get(4)
+    _case("paged shared prefix")
+    inp = W.attention_inputs(cfg, B=4, lens=[1500, 1700, 1024, 2100])
+    _check(inp, 16, _run(inp, 16, rng=5, share_prefix=True))
+
+
+def test_bad_table_entry_flags_only_its_sequence():
+    cfg = W.get(4)
+    _case("paged bad entry")
+    inp = W.attention_inputs(cfg, B=3, lens=[700, 900, 1200])
+    res = _run(inp, 32, rng=7, corrupt=(1, 5, 10 ** 6))  # sequence 1, block 5: no such page
+    out = res[0]
+    assert np.all(np.isnan(_gpu.as_f64(out[1])))
+    out2, ref, kp, vp, table, kp2, vp2 = res
+    # the others are exact; sequence 1's new rows may or may not be written
+    want = P.verify_attention_paged(inp["q"], inp["k_new"], inp["v_new"], kp, vp, table, inp["lens"], seqs=[0, 2])
+    assert np.max(np.abs(_gpu.as_f64(out[[0, 2]]) - want)) < _gpu.ATT_TOL["bf16"]
+
+
+def test_status_codes():
+    _case("paged status")
+    dev = "cuda"
+    q = torch.zeros((1, 4, 5, 128), dtype=torch.bfloat16, device=dev)
+    kn = torch.zeros((1, 2, 5, 128), dtype=torch.bfloat16, device=dev)
+    pages = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16, device=dev)
+    table = torch.zeros((1, 4), dtype=torch.int32, device=dev)
+    lens = torch.zeros(1, dtype=torch.int32, device=dev)
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_verify_attention_paged(q, kn, kn, pages, pages.clone(), table, lens, 60)  # 60 + 5 > 4 * 16
+    assert e.value.status == 2
+    p8 = torch.zeros((4, 2, 8, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_verify_attention_paged(q, kn, kn, p8, p8.clone(), table, lens, 10)  # page size 8
+    assert e.value.status == 3
