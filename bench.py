@@ -94,8 +94,12 @@ def algorithmic(cfg, lens, B, greedy=False):
     return att_bytes, att_flops, smp_bytes
 
 
-def paginate(att, cfg, hint, page, rep):
-    """Paged copies of the caches: [num_pages, Hkv, page, D] at seeded random slots, plus the block table."""
+def paginate(att, cfg, hint, page, rep, order="random"):
+    """Paged copies of the caches: [num_pages, Hkv, page, D] plus the block table.
+
+    order "random": pages at seeded random slots; "sequential": each sequence's
+    pages in order, sequences one after another.
+    """
     import torch
 
     lens = att["lens"].cpu().numpy().astype(np.int64)
@@ -103,7 +107,7 @@ def paginate(att, cfg, hint, page, rep):
     max_blocks = -(-(hint + cfg.n_q) // page)
     num_pages = int(need.sum())
     g = torch.Generator(device="cpu").manual_seed(7919 * cfg.cid + rep)
-    perm = torch.randperm(num_pages, generator=g).to(torch.int32)
+    perm = (torch.randperm(num_pages, generator=g) if order == "random" else torch.arange(num_pages)).to(torch.int32)
     table = torch.full((cfg.B, max_blocks), -1, dtype=torch.int32)
     off = 0
     for b in range(cfg.B):
@@ -246,6 +250,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paged", type=int, default=0, choices=(0, 16, 32),
                     help="run attention over a paged copy of the cache with this page size")
+    ap.add_argument("--page-order", default="random", choices=("random", "sequential"),
+                    help="where the pages sit: seeded random slots, or in sequence order")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -289,7 +295,7 @@ def main():
     hint = cfg.L[1]
     if args.paged:
         for rep, (att, _) in enumerate(sets):
-            att.update(paginate(att, cfg, hint, args.paged, rep))
+            att.update(paginate(att, cfg, hint, args.paged, rep, args.page_order))
             del att["k_cache"], att["v_cache"]  # the paged copies are the cache now
         torch.cuda.empty_cache()
     B = cfg.B
@@ -373,7 +379,8 @@ def main():
             "gamma": cfg.gamma,
             "temperature": T,
             "input_sets": nsets,
-            "kv_cache": f"paged, {args.paged}-position pages at random slots" if args.paged else "contiguous",
+            "kv_cache": (f"paged, {args.paged}-position pages at {args.page_order} slots" if args.paged
+                         else "contiguous"),
         },
         "roofline": {
             "bound": "hbm",

@@ -275,7 +275,8 @@ __device__ __forceinline__ float group_sum(float v) {
 // objects.  Every wave of the workgroup calls it with the same arguments.
 template <int D, int NW, int NST, int PG, typename KBuf, typename VBuf>
 __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vbuf, int b, int g, int rg, int L,
-                                           int k0, int k1, bool whole, size_t slot, bool append) {
+                                           int k0, int k1, bool whole, size_t slot, bool append,
+                                           const int32_t* __restrict__ table = nullptr) {
   using LY = BfLayout<D>;
   constexpr int DS = D / 32;  // MFMA steps over D for the scores
   constexpr int DT = D / 16;  // 16-wide output tiles over D
@@ -297,16 +298,22 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
   const int Ltot = L + a.n_q;
   const int nblk = (k1 - k0 + KB - 1) / KB;
   static_assert(PG == 0 || PG == 16 || PG == 32, "page size");
-  const int32_t* tab = PG ? a.table + (size_t)b * a.max_blocks : nullptr;
+  // The table comes in as a read-only, non-aliased kernel argument, so the
+  // uniform per-block lookups below are scalar loads: a vector load would
+  // need a wait on the vector-memory counter, draining the copies in flight.
+  const int32_t* __restrict__ tab = PG ? table + (size_t)b * a.max_blocks : nullptr;
   if constexpr (PG > 0) {
     // Every table entry this piece will use (the committed keys it reads and,
     // if it appends, the pages of the new rows) must name a page; otherwise
     // the piece reads nothing and leaves NaN (every wave finds the same).
     bool badp = false;
     const int e1 = (min(k1, L) + PG - 1) / PG;
-    for (int e = k0 / PG + lane; e < e1; e += kWave) {
-      const int pg = tab[e];
-      badp |= pg < 0 || pg >= a.num_pages;
+    for (int e = k0 / PG + lane; e < e1; e += 8 * kWave) {
+      int pg[8];  // eight loads in flight per lane before any test
+#pragma unroll
+      for (int t = 0; t < 8; ++t) pg[t] = e + t * kWave < e1 ? tab[e + t * kWave] : 0;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) badp |= pg[t] < 0 || pg[t] >= a.num_pages;
     }
     if (append) {
       for (int e = L / PG + lane; e <= (Ltot - 1) / PG; e += kWave) {
@@ -356,24 +363,28 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
     const int sl = p % LY::CH;
     cchunk[i] = is_v ? LY::vslot(crow[i], sl) : LY::kslot(crow[i], sl);  // XOR is its own inverse
   }
-  // Start of committed key `key` (< L) of (b, g) in a cache.
-  auto cache_row = [&](const uint16_t* cache, int key) -> const uint16_t* {
-    if constexpr (PG == 0) {
-      return cache + (size_t)key * D;
-    } else {
-      return cache + (((size_t)tab[key / PG] * a.Hkv + g) * PG + key % PG) * D;
+  // Start of committed key `key` (< L) of (b, g) in a contiguous cache.
+  auto cache_row = [&](const uint16_t* cache, int key) -> const uint16_t* { return cache + (size_t)key * D; };
+  // Paged: the page(s) of a block holding committed keys (kb is a multiple of
+  // 32, so a block is one 32-page or two 16-pages), read one block ahead of
+  // its copies so the scalar load's latency is not on the copy issue path.
+  auto pages_of = [&](int kb, int& p0, int& p1) {
+    if constexpr (PG > 0) {
+      if (kb < L) p0 = tab[kb / PG];
+      if constexpr (PG == 16) {
+        if (kb + 16 < L) p1 = tab[kb / PG + 1];
+      }
     }
   };
-  auto issue_block = [&](int kb, auto S) {
+  auto issue_block = [&](int kb, auto S, int p0, int p1) {
     if (wave >= WI) return;
     const bool full = kb + KB <= L;  // every key of the block is committed cache
-    // Paged: the block's pages (kb is a multiple of 32, so a block is one
-    // 32-page or two 16-pages); row r of the block is at base + r D.
+    // Paged: committed row r of the block is at base + r D.
     size_t pbase0 = 0, pbase1 = 0;
     if constexpr (PG > 0) {
-      if (full) {
-        pbase0 = ((size_t)tab[kb / PG] * a.Hkv + g) * PG * D;
-        if constexpr (PG == 16) pbase1 = ((size_t)tab[kb / PG + 1] * a.Hkv + g) * PG * D - (size_t)16 * D;
+      if (kb < L) pbase0 = ((size_t)p0 * a.Hkv + g) * PG * D;
+      if constexpr (PG == 16) {
+        if (kb + 16 < L) pbase1 = ((size_t)p1 * a.Hkv + g) * PG * D - (size_t)16 * D;
       }
     }
 #pragma unroll
@@ -392,7 +403,13 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
           src = cache + base + (crow[i] * D + 8 * cchunk[i]);
         }
       } else {  // new rows from k_new/v_new; keys past the end read a finite dummy row
-        src = (key < L ? cache_row(cache, key) : fresh + (size_t)(key < Ltot ? key - L : 0) * D) + 8 * cchunk[i];
+        const uint16_t* crow_p;
+        if constexpr (PG == 0) {
+          crow_p = cache_row(cache, key);
+        } else {
+          crow_p = cache + ((PG == 16 && crow[i] >= 16) ? pbase1 : pbase0) + (size_t)crow[i] * D;
+        }
+        src = (key < L ? crow_p : fresh + (size_t)(key < Ltot ? key - L : 0) * D) + 8 * cchunk[i];
       }
       uint16_t* dst = (is_v ? vbuf(S) : kbuf(S)) + cc * 512;
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
@@ -414,10 +431,16 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
       qf[s] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg) : bf16x8{};
   }
 
-  issue_block(k0, IC<0>{});
+  int pf0 = 0, pf1 = 0;  // pages of the next block to issue
+  pages_of(k0, pf0, pf1);
+  issue_block(k0, IC<0>{}, pf0, pf1);
   if constexpr (NST > 2) {
-    if (nblk > 1) issue_block(k0 + KB, IC<1>{});
+    if (nblk > 1) {
+      pages_of(k0 + KB, pf0, pf1);
+      issue_block(k0 + KB, IC<1>{}, pf0, pf1);
+    }
   }
+  if (NST - 1 < nblk) pages_of(k0 + (NST - 1) * KB, pf0, pf1);
 
   // Loop-invariant LDS element offsets of this lane's reads within a stage:
   // K fragment (kt = 0) for each D step, and V^T pieces (hh = 0) for each D
@@ -451,7 +474,10 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
     else
       wait_vmcnt<0>();
     block_barrier();
-    if (j + NST - 1 < nblk) issue_block(kb + (NST - 1) * KB, IC<(decltype(S)::value + NST - 1) % NST>{});
+    if (j + NST - 1 < nblk) {
+      issue_block(kb + (NST - 1) * KB, IC<(decltype(S)::value + NST - 1) % NST>{}, pf0, pf1);
+      if (j + NST < nblk) pages_of(kb + NST * KB, pf0, pf1);
+    }
 
     const uint16_t* ks = kbuf(S);
     const uint16_t* vs = vbuf(S);
@@ -631,7 +657,7 @@ __device__ __forceinline__ long long stream_share(const AttnArgs& a, long long W
 // the combine.
 template <int D, int NW, int NST, int PG>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
-void attn_stream_bf16(AttnArgs a) {
+void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
   using LY = BfLayout<D>;
   SPECV_BF16_STAGE_LDS
   __shared__ long long sh_x[3];
@@ -714,7 +740,7 @@ void attn_stream_bf16(AttnArgs a) {
       const int L = ufl(a.len[b]);
       const size_t slot = (((size_t)b * a.Hkv + g) * a.RG + rg) * a.JP + (size_t)j;
       bf16_piece<D, NW, NST, PG>(a, kbuf, vbuf, b, g, rg, L, off * KB, min(end * KB, L + a.n_q), whole, slot,
-                             off == 0 && rg == 0);
+                                 off == 0 && rg == 0, table);
     }
     x = uniform64(x + take);
     off = 0;
@@ -1105,7 +1131,7 @@ template <int D, int NW, int PG>
 static hipError_t launch_stream(const AttnArgs& a0, hipStream_t s) {
   AttnArgs a = a0;
   a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG>, NW);
-  hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
+  hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a, a.table);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
