@@ -95,7 +95,7 @@ def algorithmic(cfg, lens, B, greedy=False):
 
 
 def paginate(att, cfg, hint, page, rep, order="random"):
-    """Paged copies of the caches: [num_pages, Hkv, page, D] plus the block table.
+    """Paged copies of the caches: [Hkv, num_pages, page, D] plus the block table.
 
     order "random": pages at seeded random slots; "sequential": each sequence's
     pages in order, sequences one after another.
@@ -117,13 +117,13 @@ def paginate(att, cfg, hint, page, rep, order="random"):
     out = {}
     for name in ("k_cache", "v_cache"):
         c = att[name]
-        pages = torch.empty((num_pages, cfg.Hkv, page, cfg.D), dtype=c.dtype, device=c.device)
+        pages = torch.empty((cfg.Hkv, num_pages, page, cfg.D), dtype=c.dtype, device=c.device)
         for b in range(cfg.B):
             nb = int(need[b])
             rows = min(nb * page, c.shape[2])
             blk = torch.zeros((cfg.Hkv, nb * page, cfg.D), dtype=c.dtype, device=c.device)
             blk[:, :rows] = c[b, :, :rows]
-            pages[table[b, :nb].long()] = blk.view(cfg.Hkv, nb, page, cfg.D).transpose(0, 1)
+            pages[:, table[b, :nb].long()] = blk.view(cfg.Hkv, nb, page, cfg.D)
         out[name.replace("cache", "pages")] = pages
     out["table"] = table
     return out
@@ -178,7 +178,7 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
                 page = att["k_pages"].shape[2]
                 nb = -(-L // page)
                 rows = att["table"][b, :nb].long()
-                kp, vp = to_host(att["k_pages"][rows]), to_host(att["v_pages"][rows])
+                kp, vp = to_host(att["k_pages"][:, rows]), to_host(att["v_pages"][:, rows])
                 tab = np.arange(nb, dtype=np.int32)[None]
                 s0 = time.perf_counter()
                 Pg.verify_attention_paged(host["q"], host["k_new"], host["v_new"], kp, vp, tab, np.array([L]))

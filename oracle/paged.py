@@ -12,16 +12,16 @@ verify step is then exactly ``oracle.attention`` (the ``forward_cached``
 listing of [P2] section numpyで小さなTransformerを自作する).
 
 Layouts:
-  k_pages, v_pages  [num_pages, Hkv, page, D]   page p holds positions
+  k_pages, v_pages  [Hkv, num_pages, page, D]   page p holds positions
                     [i*page, (i+1)*page) of the request whose table maps its
-                    logical block i to p
+                    logical block i to p (for every KV head)
   block_table       [B, max_blocks] int      physical page of logical block i
   lens              [B]                      committed length L_b before the call
 
-Reading (listed in the design doc): within a page, the KV heads are the outer
-index and positions the inner one, so one head's block of a page is
-contiguous; the pages fix only that a request's positions are grouped into
-fixed-size blocks.
+Reading (listed in the design doc): the KV head is the outermost index, then the
+page, then the position in the page: one head's part of a page is
+contiguous, and so is a run of consecutive pages; the pages fix only that a
+request's positions are grouped into fixed-size blocks.
 """
 
 import numpy as np
@@ -53,8 +53,8 @@ def gather(pages, table_row, length):
     """The first `length` positions of one request, [Hkv, length, D], from its pages."""
     page = pages.shape[2]
     nb = blocks_needed(length, page)
-    blocks = [pages[int(table_row[i])] for i in range(nb)]  # each [Hkv, page, D]
-    full = np.concatenate(blocks, axis=1) if blocks else pages[:0].reshape(pages.shape[1], 0, pages.shape[3])
+    blocks = [pages[:, int(table_row[i])] for i in range(nb)]  # each [Hkv, page, D]
+    full = np.concatenate(blocks, axis=1) if blocks else pages[:, :0].reshape(pages.shape[0], 0, pages.shape[3])
     return full[:, :length]
 
 
@@ -67,8 +67,8 @@ def kv_append_paged(k_pages, v_pages, k_new, v_new, block_table, lens):
         for r in range(n):
             pos = int(L) + r
             p = int(block_table[b][pos // page])
-            kp[p, :, pos % page] = k_new[b, :, r]
-            vp[p, :, pos % page] = v_new[b, :, r]
+            kp[:, p, pos % page] = k_new[b, :, r]
+            vp[:, p, pos % page] = v_new[b, :, r]
     return kp, vp
 
 

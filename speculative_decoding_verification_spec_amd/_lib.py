@@ -176,17 +176,17 @@ def spec_verify_attention_paged(q, k_new, v_new, k_pages, v_pages, block_table, 
                                 scale=None, workspace=None, stream=None):
     """Verify attention with KV append over a paged cache; returns ``out`` [B, Hq, n_q, D].
 
-    k_pages, v_pages: [num_pages, Hkv, page_size, D]; block_table: int32 [B, max_blocks].
+    k_pages, v_pages: [Hkv, num_pages, page_size, D]; block_table: int32 [B, max_blocks].
     """
     L = load()
     _need(q, "q")
     B, Hq, n_q, D = q.shape
     Hkv = k_new.shape[1]
-    num_pages, _, page, _ = k_pages.shape
+    _, num_pages, page, _ = k_pages.shape
     _need(k_new, "k_new", q.dtype, (B, Hkv, n_q, D))
     _need(v_new, "v_new", q.dtype, (B, Hkv, n_q, D))
-    _need(k_pages, "k_pages", q.dtype, (num_pages, Hkv, page, D))
-    _need(v_pages, "v_pages", q.dtype, (num_pages, Hkv, page, D))
+    _need(k_pages, "k_pages", q.dtype, (Hkv, num_pages, page, D))
+    _need(v_pages, "v_pages", q.dtype, (Hkv, num_pages, page, D))
     _need(block_table, "block_table", torch.int32)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise SpecError("spec_verify_attention_paged", SPEC_ERR_ARG, "block_table must be [B, max_blocks]")

@@ -86,7 +86,7 @@ struct AttnArgs {
   int* pre;  // stream scheme: [B + 1] blocks per slab before sequence b
   int B, Hq, Hkv, n_q, G, M, RG, RT, NSP, C, max_T, hint;
   int P, MINB, JP;  // stream scheme: workgroups, minimum share, partial slots per slab
-  // Paged cache: kc / vc are [num_pages][Hkv][page][D]; table[b * max_blocks + i]
+  // Paged cache: kc / vc are [Hkv][num_pages][page][D]; table[b * max_blocks + i]
   // is the page of logical block i of sequence b.
   const int32_t* table;  // null: contiguous cache [B][Hkv][max_T][D]
   int page, max_blocks, num_pages;
@@ -152,7 +152,7 @@ __device__ __forceinline__ void append_rows_paged(const AttnArgs& a, int b, int 
   for (int c = tid; c < chunks; c += nthreads) {
     const int pos = L + c / CPR;
     const size_t page = (size_t)a.table[(size_t)b * a.max_blocks + pos / PG];
-    const size_t row = ((page * a.Hkv + g) * PG + pos % PG) * CPR + c % CPR;
+    const size_t row = (((size_t)g * a.num_pages + page) * PG + pos % PG) * CPR + c % CPR;
     reinterpret_cast<uint4*>(a.kc)[row] = skn[c];
     reinterpret_cast<uint4*>(a.vc)[row] = svn[c];
   }
@@ -243,7 +243,7 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 #ifndef SPECV_ATTN_WPE
-#define SPECV_ATTN_WPE 1
+#define SPECV_ATTN_WPE 4
 #endif
 #ifndef SPECV_STREAM_WPE
 #define SPECV_STREAM_WPE 4
@@ -353,18 +353,22 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
   // row (64 c' + l) / CH at swizzled slot (64 c' + l) % CH, which holds the
   // row's 16-byte chunk given by the same XOR.  Every issuing wave issues CPW
   // copies per block, so a fixed vmcnt tells it when an older block landed.
-  int crow[CPW], cchunk[CPW];
+  // coff[i]: element offset, within a staged block, of the 16-byte chunk this
+  // lane copies in copy i (row crow = coff / D, chunk 8 cchunk = coff % D).
+  // A copy's rows are 512 / D consecutive rows of one 16-row half, so a
+  // copy never spans two 16-position pages.
+  uint32_t coff[CPW];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const bool is_v = i >= LY::NI / WI;
     const int cc = (wave + i * WI) - (is_v ? LY::NI : 0);
     const int p = cc * kWave + lane;
-    crow[i] = p / LY::CH;
+    const int crow = p / LY::CH;
     const int sl = p % LY::CH;
-    cchunk[i] = is_v ? LY::vslot(crow[i], sl) : LY::kslot(crow[i], sl);  // XOR is its own inverse
+    const int cchunk = is_v ? LY::vslot(crow, sl) : LY::kslot(crow, sl);  // XOR is its own inverse
+    coff[i] = (uint32_t)(crow * D + 8 * cchunk);
   }
-  // Start of committed key `key` (< L) of (b, g) in a contiguous cache.
-  auto cache_row = [&](const uint16_t* cache, int key) -> const uint16_t* { return cache + (size_t)key * D; };
+  static_assert(16 % (512 / D) == 0, "a copy stays inside one 16-row half");
   // Paged: the page(s) of a block holding committed keys (kb is a multiple of
   // 32, so a block is one 32-page or two 16-pages), read one block ahead of
   // its copies so the scalar load's latency is not on the copy issue path.
@@ -379,12 +383,14 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
   auto issue_block = [&](int kb, auto S, int p0, int p1) {
     if (wave >= WI) return;
     const bool full = kb + KB <= L;  // every key of the block is committed cache
-    // Paged: committed row r of the block is at base + r D.
-    size_t pbase0 = 0, pbase1 = 0;
+    // Element offset of the block's row 0 in the cache (contiguous), or of
+    // its page's row 0 (paged; pbase1 + 16 D is the 16-page holding rows
+    // 16..31).
+    size_t pbase0 = (size_t)kb * D, pbase1 = 0;
     if constexpr (PG > 0) {
-      if (kb < L) pbase0 = ((size_t)p0 * a.Hkv + g) * PG * D;
+      if (kb < L) pbase0 = ((size_t)g * a.num_pages + p0) * PG * D;
       if constexpr (PG == 16) {
-        if (kb + 16 < L) pbase1 = ((size_t)p1 * a.Hkv + g) * PG * D - (size_t)16 * D;
+        if (kb + 16 < L) pbase1 = ((size_t)g * a.num_pages + p1) * PG * D - (size_t)16 * D;
       }
     }
 #pragma unroll
@@ -393,27 +399,26 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
       const int cc = (wave + i * WI) - (is_v ? LY::NI : 0);
       const uint16_t* cache = is_v ? vc : kc;
       const uint16_t* fresh = is_v ? vnb : knb;
-      const int key = kb + crow[i];
-      const uint16_t* src;
-      if (full) {
-        if constexpr (PG == 0) {
-          src = cache + (size_t)kb * D + (crow[i] * D + 8 * cchunk[i]);
-        } else {
-          const size_t base = (PG == 16 && crow[i] >= 16) ? pbase1 : pbase0;
-          src = cache + base + (crow[i] * D + 8 * cchunk[i]);
-        }
-      } else {  // new rows from k_new/v_new; keys past the end read a finite dummy row
-        const uint16_t* crow_p;
-        if constexpr (PG == 0) {
-          crow_p = cache_row(cache, key);
-        } else {
-          crow_p = cache + ((PG == 16 && crow[i] >= 16) ? pbase1 : pbase0) + (size_t)crow[i] * D;
-        }
-        src = (key < L ? crow_p : fresh + (size_t)(key < Ltot ? key - L : 0) * D) + 8 * cchunk[i];
-      }
+      // The copy's base is uniform across the wave: its rows sit in one page.
+      const bool hi_half = PG == 16 && (cc * kWave) / LY::CH >= 16;
+      const uint16_t* cbase = cache + (hi_half ? pbase1 + (size_t)16 * D : pbase0);
+      const uint32_t loff = coff[i] - (hi_half ? 16 * D : 0);  // element offset from cbase
       uint16_t* dst = (is_v ? vbuf(S) : kbuf(S)) + cc * 512;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+      if (full) {
+        // Buffer load: the base in a scalar descriptor whose range is the
+        // block's (or page's) rows, the lane's byte offset in one VGPR.
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)cbase, (short)0, (PG == 16 ? 16 : KB) * D * 2, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3)))*)dst, 16,
+                                                 (int)(loff * 2), 0, 0, 0);
+      } else {  // new rows from k_new/v_new; keys past the end read a finite dummy row
+        const int crow = (int)(coff[i] / D);
+        const int key = kb + crow;
+        const uint16_t* src =
+            (key < L ? cbase + loff : fresh + (size_t)(key < Ltot ? key - L : 0) * D + coff[i] % D);
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                         (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+      }
     }
   };
 

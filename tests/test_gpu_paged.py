@@ -26,7 +26,7 @@ def _case(name, **kw):
 
 
 def _paginate(cache, lens, n_q, page, rng, hint, spare=3, share_prefix=False):
-    """Pages [num_pages, Hkv, page, D] and table [B, max_blocks] holding cache[b, :, :L_b].
+    """Pages [Hkv, num_pages, page, D] and table [B, max_blocks] holding cache[b, :, :L_b].
 
     The table has room for hint + n_q positions, as the call requires.
     """
@@ -35,7 +35,7 @@ def _paginate(cache, lens, n_q, page, rng, hint, spare=3, share_prefix=False):
     max_blocks = max(max(need), P.blocks_needed(hint + n_q, page))
     num_pages = sum(need) + spare
     perm = rng.permutation(num_pages)
-    pages = np.full((num_pages, Hkv, page, D), NAN_BF16, dtype=cache.dtype)
+    pages = np.full((Hkv, num_pages, page, D), NAN_BF16, dtype=cache.dtype)
     table = np.full((B, max_blocks), -7, np.int32)  # entries past a sequence's blocks are never used
     k = 0
     for b in range(B):
@@ -49,7 +49,7 @@ def _paginate(cache, lens, n_q, page, rng, hint, spare=3, share_prefix=False):
         L = int(lens[b])
         for pos0 in range(0, L, page):
             m = min(page, L - pos0)
-            pages[table[b, pos0 // page], :, :m] = cache[b, :, pos0 : pos0 + m]
+            pages[:, table[b, pos0 // page], :m] = cache[b, :, pos0 : pos0 + m]
     return pages, table
 
 
@@ -141,13 +141,13 @@ def test_status_codes():
     dev = "cuda"
     q = torch.zeros((1, 4, 5, 128), dtype=torch.bfloat16, device=dev)
     kn = torch.zeros((1, 2, 5, 128), dtype=torch.bfloat16, device=dev)
-    pages = torch.zeros((4, 2, 16, 128), dtype=torch.bfloat16, device=dev)
+    pages = torch.zeros((2, 4, 16, 128), dtype=torch.bfloat16, device=dev)
     table = torch.zeros((1, 4), dtype=torch.int32, device=dev)
     lens = torch.zeros(1, dtype=torch.int32, device=dev)
     with pytest.raises(sv.SpecError) as e:
         sv.spec_verify_attention_paged(q, kn, kn, pages, pages.clone(), table, lens, 60)  # 60 + 5 > 4 * 16
     assert e.value.status == 2
-    p8 = torch.zeros((4, 2, 8, 128), dtype=torch.bfloat16, device=dev)
+    p8 = torch.zeros((2, 4, 8, 128), dtype=torch.bfloat16, device=dev)
     with pytest.raises(sv.SpecError) as e:
         sv.spec_verify_attention_paged(q, kn, kn, p8, p8.clone(), table, lens, 10)  # page size 8
     assert e.value.status == 3

@@ -53,15 +53,16 @@ def _contiguous_case(B=3, Hq=4, Hkv=2, n=3, D=8, page=4, lens=(0, 5, 13), seed=0
 
 
 def _paginate(cache, page, perm):
-    """Pages and block table holding `cache` [B, Hkv, T, D]; block (b, i) goes to page perm[b * nb + i]."""
+    """Pages [Hkv, num_pages, page, D] and block table holding `cache` [B, Hkv, T, D];
+    block (b, i) goes to page perm[b * nb + i]."""
     B, Hkv, T, D = cache.shape
     nb = T // page
-    pages = np.full((B * nb, Hkv, page, D), np.nan)
+    pages = np.full((Hkv, B * nb, page, D), np.nan)
     table = np.zeros((B, nb), np.int32)
     for b in range(B):
         for i in range(nb):
             p = perm[b * nb + i]
-            pages[p] = cache[b, :, i * page : (i + 1) * page]
+            pages[:, p] = cache[b, :, i * page : (i + 1) * page]
             table[b, i] = p
     return pages, table
 
@@ -89,12 +90,12 @@ def test_shared_prefix_pages_and_unused_slots():
     kp, table = _paginate(kc[:, :, :T], page, np.arange(3 * nb))
     vp, _ = _paginate(vc[:, :, :T], page, np.arange(3 * nb))
     table[1, :2] = table[0, :2]  # point request 1 at request 0's pages
-    kp[nb : nb + 2] = np.nan     # its own copies are now unused: poisoned
-    vp[nb : nb + 2] = np.nan
+    kp[:, nb : nb + 2] = np.nan  # its own copies are now unused: poisoned
+    vp[:, nb : nb + 2] = np.nan
     for b in range(3):           # positions at or past L are unused too
         for pos in range(9, T):
-            kp[table[b, pos // page], :, pos % page] = np.nan
-            vp[table[b, pos // page], :, pos % page] = np.nan
+            kp[:, table[b, pos // page], pos % page] = np.nan
+            vp[:, table[b, pos // page], pos % page] = np.nan
     got = P.verify_attention_paged(q, kn, vn, kp, vp, table, lens)
     assert np.all(np.isfinite(got))
     assert np.allclose(got, A.verify_attention(q, kn, vn, kc, vc, lens), rtol=0, atol=0)
