@@ -389,7 +389,9 @@ def main():
             "unit": "GB/s",
             "frac": att_gbs / HBM_PEAK_GBS,
             "traffic": None if traffic is None else traffic["bytes_per_call"],
-            "kernel": f"spec_verify_attention: attn_split_{'bf16' if cfg.dtype == 'bf16' else 'f32'} + attn_combine, one call",
+            "kernel": ("spec_verify_attention: attn_stream_bf16 + attn_combine_stream, one call"
+                       if cfg.dtype == "bf16" and cfg.B <= 1024
+                       else f"spec_verify_attention: attn_split_{cfg.dtype} + attn_combine, one call"),
             "algorithmic_bytes": att_b,
             "avg_ms": att_ms,
         },
