@@ -24,6 +24,8 @@ Modules:
                 uncached full-sequence recompute it must agree with
   paged      -- verify attention over a paged cache (block tables), and the
                 allocation-waste count of paging
+  quant      -- verify attention over an int8 cache with per-row float16
+                scales (quantise, convert back, attend)
   truncate   -- the KV length reset after verification
   formulas   -- closed forms: acceptance rate, expected committed tokens,
                 speed-up estimate, KV-cache bytes
@@ -35,4 +37,4 @@ Nothing is "parity unpinned" except the mapping of decisions that fall inside
 the 1e-6 threshold band (those draws are counted, not compared).
 """
 
-from . import attention, bf16, formulas, greedy, paged, sampler, truncate  # noqa: F401
+from . import attention, bf16, formulas, greedy, paged, quant, sampler, truncate  # noqa: F401

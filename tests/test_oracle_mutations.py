@@ -161,3 +161,40 @@ def test_ignoring_the_block_table_is_caught(monkeypatch):
     real = Pg.gather
     monkeypatch.setattr(Pg, "gather", lambda pages, row, length: real(pages, np.arange(len(row)), length))
     _assert_pin_fails(lambda: TP.test_paging_does_not_change_attention(True))
+
+
+# ---- int8 cache -----------------------------------------------------------------
+
+from oracle import quant as Qn  # noqa: E402
+from tests import test_oracle_quant as TQ  # noqa: E402
+
+
+def test_quant_pins_hold_unmutated():
+    TQ.test_halves_round_to_even()
+    TQ.test_error_bound_and_granularity()
+
+
+def test_floor_rounding_is_caught(monkeypatch):
+    def floor_q(x):
+        x32 = np.asarray(x, np.float32)
+        s32 = np.max(np.abs(x32), axis=-1, keepdims=True) / np.float32(127)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.where(s32 > 0, np.floor(x32 / s32), 0)
+        return np.clip(q, -127, 127).astype(np.int8), s32[..., 0].astype(np.float16)
+
+    monkeypatch.setattr(Qn, "quantize_rows", floor_q)
+    _assert_pin_fails(TQ.test_halves_round_to_even)
+
+
+def test_scale_shared_over_heads_is_caught(monkeypatch):
+    def per_position(x):
+        x32 = np.asarray(x, np.float32)
+        a = np.max(np.abs(x32), axis=(-3, -1), keepdims=True) if x32.ndim >= 3 else np.max(np.abs(x32), axis=-1,
+                                                                                             keepdims=True)
+        s32 = np.broadcast_to(a / np.float32(127), x32.shape[:-1] + (1,))
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = np.where(s32 > 0, np.rint(x32 / s32), 0)
+        return np.clip(q, -127, 127).astype(np.int8), s32[..., 0].astype(np.float16)
+
+    monkeypatch.setattr(Qn, "quantize_rows", per_position)
+    _assert_pin_fails(TQ.test_error_bound_and_granularity)
