@@ -73,7 +73,7 @@ def measured_traffic(cid):
     return None
 
 
-def algorithmic(cfg, lens, B, greedy=False):
+def algorithmic(cfg, lens, B, greedy=False, kv="bf16"):
     """Bytes and flops the step must move / compute (every input read once).
 
     Greedy verification (T = 0) reads only the gamma+1 target rows and no uniforms.
@@ -81,8 +81,12 @@ def algorithmic(cfg, lens, B, greedy=False):
     e = cfg.elem_bytes
     n, D = cfg.n_q, cfg.D
     L = lens.astype(np.int64)
-    kv_read = int(np.sum(2 * cfg.Hkv * D * e * (L + n)))
-    append = int(B * 2 * cfg.Hkv * n * D * e)
+    if kv == "int8":  # cached rows: D int8 values + one fp16 scale; new rows read in bf16
+        kv_read = int(np.sum(2 * cfg.Hkv * (D + 2) * L) + B * 2 * cfg.Hkv * n * D * e)
+        append = int(B * 2 * cfg.Hkv * n * (D + 2))
+    else:
+        kv_read = int(np.sum(2 * cfg.Hkv * D * e * (L + n)))
+        append = int(B * 2 * cfg.Hkv * n * D * e)
     q_o = int(B * 2 * cfg.Hq * n * D * e)
     att_bytes = kv_read + append + q_o
     att_flops = int(4 * cfg.Hq * D * np.sum(n * L + n * (n + 1) // 2))
@@ -129,6 +133,29 @@ def paginate(att, cfg, hint, page, rep, order="random"):
     return out
 
 
+def quantized_cache(att, cfg, rep):
+    """int8 caches and fp16 scales drawn on the device with the host recipe of
+    ``workloads.gen.attention_inputs_int8`` (codes of N(0,1) rows, one code of
+    magnitude 127 per row, scales near 2.7 / 127); input generation only."""
+    import torch
+
+    g = torch.Generator(device=att["q"].device).manual_seed(104729 * cfg.cid + rep)
+    B, Hkv, T, D = att["k_cache"].shape
+    out = {}
+    for name in ("k", "v"):
+        codes = torch.empty((B, Hkv, T, D), dtype=torch.int8, device=att["q"].device)
+        for b in range(B):
+            c = torch.clamp(torch.round(torch.randn((Hkv, T, D), generator=g, device=codes.device) * (127 / 2.7)),
+                            -127, 127)
+            pos = torch.randint(0, D, (Hkv, T, 1), generator=g, device=codes.device)
+            sign = torch.where(torch.rand((Hkv, T, 1), generator=g, device=codes.device) < 0.5, -127.0, 127.0)
+            codes[b] = c.scatter(2, pos, sign).to(torch.int8)
+        out[f"{name}_q"] = codes
+        out[f"{name}_scale"] = (torch.exp(0.1 * torch.randn((B, Hkv, T), generator=g, device=codes.device))
+                                * (2.7 / 127)).to(torch.float16)
+    return out
+
+
 def make_inputs(cfg, device, temperature, rep):
     import torch
 
@@ -163,6 +190,7 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
     from oracle import attention as A
     from oracle import greedy as Gr
     from oracle import paged as Pg
+    from oracle import quant as Qn
     from oracle import sampler as S
     from workloads.device import to_host
 
@@ -174,7 +202,12 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
             sl = slice(int(b), int(b) + 1)
             L = int(att["lens_base"][sl].item())
             host = {k: to_host(att[k][sl]) for k in ("q", "k_new", "v_new")}
-            if "k_pages" in att:  # this sequence's pages, renumbered 0..nb-1
+            if "k_q" in att:
+                kq, ks = to_host(att["k_q"][sl, :, :L]), to_host(att["k_scale"][sl, :, :L])
+                vq, vs = to_host(att["v_q"][sl, :, :L]), to_host(att["v_scale"][sl, :, :L])
+                s0 = time.perf_counter()
+                Qn.verify_attention_int8(host["q"], host["k_new"], host["v_new"], kq, ks, vq, vs, np.array([L]))
+            elif "k_pages" in att:  # this sequence's pages, renumbered 0..nb-1
                 page = att["k_pages"].shape[2]
                 nb = -(-L // page)
                 rows = att["table"][b, :nb].long()
@@ -252,6 +285,8 @@ def main():
                     help="run attention over a paged copy of the cache with this page size")
     ap.add_argument("--page-order", default="random", choices=("random", "sequential"),
                     help="where the pages sit: seeded random slots, or in sequence order")
+    ap.add_argument("--kv", default="bf16", choices=("bf16", "int8"),
+                    help="cache storage: the workload's bf16, or int8 codes with an fp16 scale per row")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -293,6 +328,14 @@ def main():
     nsets = max(1, min(4, math.ceil(768e6 / (att_bytes_est + smp_bytes_est))))
     sets = [make_inputs(cfg, dev, T, rep) for rep in range(nsets)]
     hint = cfg.L[1]
+    if args.kv == "int8":
+        if args.paged or cfg.dtype != "bf16":
+            print("--kv int8 needs a contiguous cache and bf16 activations", file=sys.stderr)
+            sys.exit(2)
+        for rep, (att, _) in enumerate(sets):
+            att.update(quantized_cache(att, cfg, rep))
+            del att["k_cache"], att["v_cache"]
+        torch.cuda.empty_cache()
     if args.paged:
         for rep, (att, _) in enumerate(sets):
             att.update(paginate(att, cfg, hint, args.paged, rep, args.page_order))
@@ -308,7 +351,10 @@ def main():
         att["lens"].copy_(att["lens_base"])
         if events:
             events[0].record(stream)
-        if args.paged:
+        if args.kv == "int8":
+            sv.spec_verify_attention_int8(att["q"], att["k_new"], att["v_new"], att["k_q"], att["k_scale"],
+                                          att["v_q"], att["v_scale"], att["lens"], hint, out=att["out"])
+        elif args.paged:
             sv.spec_verify_attention_paged(att["q"], att["k_new"], att["v_new"], att["k_pages"], att["v_pages"],
                                            att["table"], att["lens"], hint, out=att["out"])
         else:
@@ -347,7 +393,7 @@ def main():
 
     # Algorithmic bytes per call, averaged over the rotated input sets (their
     # lengths differ); set k is used by steps k, k + nsets, ...
-    per_set = [algorithmic(cfg, st[0]["lens_base"].cpu().numpy(), B, greedy=(T == 0)) for st in sets]
+    per_set = [algorithmic(cfg, st[0]["lens_base"].cpu().numpy(), B, greedy=(T == 0), kv=args.kv) for st in sets]
     counts = [len(range(k, args.steps, nsets)) for k in range(nsets)]
     att_b = sum(c * a[0] for c, a in zip(counts, per_set)) / args.steps
     att_f = sum(c * a[1] for c, a in zip(counts, per_set)) / args.steps
@@ -356,7 +402,7 @@ def main():
     smp_gbs = smp_b / (smp_ms * 1e-3) / 1e9
     positions = B * cfg.gamma
     n_last = sets[(args.steps - 1) % nsets][1]["n"].cpu().numpy()
-    traffic = measured_traffic(cfg.cid)
+    traffic = measured_traffic(cfg.cid) if (not args.paged and args.kv == "bf16") else None
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
 
     res = {
@@ -380,7 +426,7 @@ def main():
             "temperature": T,
             "input_sets": nsets,
             "kv_cache": (f"paged, {args.paged}-position pages at {args.page_order} slots" if args.paged
-                         else "contiguous"),
+                         else "int8 codes + fp16 row scales, contiguous" if args.kv == "int8" else "contiguous"),
         },
         "roofline": {
             "bound": "hbm",
@@ -389,7 +435,9 @@ def main():
             "unit": "GB/s",
             "frac": att_gbs / HBM_PEAK_GBS,
             "traffic": None if traffic is None else traffic["bytes_per_call"],
-            "kernel": ("spec_verify_attention: attn_stream_bf16 + attn_combine_stream, one call"
+            "kernel": ("spec_verify_attention_int8: quant_new_rows + attn_stream_i8 + attn_combine_stream, one call"
+                       if args.kv == "int8" else
+                       "spec_verify_attention: attn_stream_bf16 + attn_combine_stream, one call"
                        if cfg.dtype == "bf16" and cfg.B <= 1024
                        else f"spec_verify_attention: attn_split_{cfg.dtype} + attn_combine, one call"),
             "algorithmic_bytes": att_b,

@@ -143,6 +143,41 @@ spec_status_t spec_verify_attention_paged(const void* q, const void* k_new, cons
                                           spec_dtype_t dtype, void* workspace, size_t workspace_bytes,
                                           hipStream_t stream);
 
+/* Workspace bytes spec_verify_attention_int8 needs (a workspace sized for a
+ * hint serves smaller hints).  Returns 0 for invalid or unsupported sizes. */
+size_t spec_verify_attention_int8_workspace_size(int B, int Hq, int Hkv, int n_q, int D, int max_len_hint);
+
+/* Verify attention with KV append over an int8 cache.
+ *
+ * Defined by [P2] section PagedAttentionとKVキャッシュの量子化 (quantisation):
+ * every cached row -- one KV head at one position -- holds int8 values q and a
+ * float16 scale s, and stands for q * s; the attention is that of
+ * spec_verify_attention on those values.  The n_q new rows are quantised on
+ * append: s = max|x| / 127, q = round-half-even(x / s) clipped to +-127, both
+ * in fp32 (a zero row gives s = 0, q = 0), the stored scale fp16(s) rounded to
+ * nearest-even; the call attends to the new rows' quantised values too.
+ *
+ *   q, k_new, v_new, out  as spec_verify_attention, dtype bf16.
+ *   k_cache, v_cache device, [B][Hkv][max_T][D] int8, in/out.
+ *   k_scale, v_scale device, [B][Hkv][max_T] float16 (bits), in/out.
+ *            Rows [cache_len[b], cache_len[b] + n_q) of both are overwritten
+ *            with the quantised new rows; no other row is written; rows >=
+ *            cache_len[b] are never used.
+ *   workspace device, >= spec_verify_attention_int8_workspace_size(...) bytes.
+ * Arithmetic: scores from the bf16 MFMA on the exact int8 values, times the
+ * key's scale in fp32; each probability is multiplied by its key's V scale
+ * before the bf16 PV product; the row sum uses the unscaled probabilities.
+ * Supported: D in {64, 128}, B <= 1024, and the limits of
+ * spec_verify_attention.
+ * Errors: as spec_verify_attention (dtype fixed to bf16 activations), and
+ * SPEC_ERR_ARG if max_T is not a multiple of 8 or a pointer is not 16-byte
+ * aligned; SPEC_ERR_UNSUPPORTED outside the supported set. */
+spec_status_t spec_verify_attention_int8(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                         void* k_scale, void* v_cache, void* v_scale, const int32_t* cache_len,
+                                         void* out, int B, int Hq, int Hkv, int n_q, int D, int max_T,
+                                         int max_len_hint, float scale, void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
 /* ------------------------------------------------------------------------- */
 /* Modified rejection sampler                                                 */
 /* ------------------------------------------------------------------------- */

@@ -5,6 +5,7 @@ with ctypes (see include/spec_verify.h for the contract of each):
 
   spec_verify_attention  KV append + causal multi-query verify attention (GQA)
   spec_verify_attention_paged  the same over a paged cache (block tables)
+  spec_verify_attention_int8   the same over an int8 cache with fp16 row scales
   spec_reject_sample     modified rejection sampling over the vocabulary
                          (greedy verification at temperature 0)
   spec_kv_truncate       length reset after the round
@@ -24,6 +25,7 @@ from ._lib import (  # noqa: F401
     spec_kv_truncate,
     spec_reject_sample,
     spec_verify_attention,
+    spec_verify_attention_int8,
     spec_verify_attention_paged,
     verify_attention_workspace_size,
     version,

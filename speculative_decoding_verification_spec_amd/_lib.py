@@ -26,6 +26,8 @@ EXPORTED = (
     "spec_verify_attention_workspace_size",
     "spec_verify_attention",
     "spec_verify_attention_paged",
+    "spec_verify_attention_int8_workspace_size",
+    "spec_verify_attention_int8",
     "spec_reject_sample_workspace_size",
     "spec_reject_sample",
     "spec_kv_truncate",
@@ -61,6 +63,10 @@ def load(path=LIB_PATH):
     L.spec_verify_attention_workspace_size.argtypes = [c_int] * 6 + [c_int]
     L.spec_verify_attention.restype = c_int
     L.spec_verify_attention.argtypes = [vp] * 7 + [c_int] * 7 + [c_float, c_int, vp, c_size, vp]
+    L.spec_verify_attention_int8_workspace_size.restype = c_size
+    L.spec_verify_attention_int8_workspace_size.argtypes = [c_int] * 6
+    L.spec_verify_attention_int8.restype = c_int
+    L.spec_verify_attention_int8.argtypes = [vp] * 9 + [c_int] * 7 + [c_float, vp, c_size, vp]
     L.spec_verify_attention_paged.restype = c_int
     L.spec_verify_attention_paged.argtypes = [vp] * 8 + [c_int] * 9 + [c_float, c_int, vp, c_size, vp]
     L.spec_reject_sample_workspace_size.restype = c_size
@@ -206,6 +212,42 @@ def spec_verify_attention_paged(q, k_new, v_new, k_pages, v_pages, block_table, 
         _ptr(ws), ws.numel(), _stream(stream),
     )
     _check("spec_verify_attention_paged", st)
+    return out
+
+
+def spec_verify_attention_int8(q, k_new, v_new, k_cache, k_scale, v_cache, v_scale, cache_len, max_len_hint,
+                               out=None, scale=None, workspace=None, stream=None):
+    """Verify attention with KV append over an int8 cache; returns ``out`` [B, Hq, n_q, D] (bf16).
+
+    k_cache, v_cache: int8 [B, Hkv, max_T, D]; k_scale, v_scale: float16 [B, Hkv, max_T]
+    (one scale per head and position); q, k_new, v_new: bfloat16.
+    """
+    L = load()
+    _need(q, "q", torch.bfloat16)
+    B, Hq, n_q, D = q.shape
+    Hkv = k_new.shape[1]
+    max_T = k_cache.shape[2]
+    _need(k_new, "k_new", torch.bfloat16, (B, Hkv, n_q, D))
+    _need(v_new, "v_new", torch.bfloat16, (B, Hkv, n_q, D))
+    _need(k_cache, "k_cache", torch.int8, (B, Hkv, max_T, D))
+    _need(v_cache, "v_cache", torch.int8, (B, Hkv, max_T, D))
+    _need(k_scale, "k_scale", torch.float16, (B, Hkv, max_T))
+    _need(v_scale, "v_scale", torch.float16, (B, Hkv, max_T))
+    _need(cache_len, "cache_len", torch.int32, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.bfloat16, q.shape)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    nbytes = L.spec_verify_attention_int8_workspace_size(B, Hq, Hkv, n_q, D, int(max_len_hint))
+    if nbytes == 0:
+        raise SpecError("spec_verify_attention_int8_workspace_size", SPEC_ERR_UNSUPPORTED, "no valid size")
+    ws = _workspace(workspace, "attn8", nbytes, q.device)
+    st = L.spec_verify_attention_int8(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale),
+        _ptr(cache_len), _ptr(out), B, Hq, Hkv, n_q, D, max_T, int(max_len_hint), scale, _ptr(ws), ws.numel(),
+        _stream(stream),
+    )
+    _check("spec_verify_attention_int8", st)
     return out
 
 

@@ -90,6 +90,15 @@ struct AttnArgs {
   // is the page of logical block i of sequence b.
   const int32_t* table;  // null: contiguous cache [B][Hkv][max_T][D]
   int page, max_blocks, num_pages;
+  // int8 cache: kc / vc are int8 [B][Hkv][max_T][D], ksc / vsc their fp16
+  // scales [B][Hkv][max_T]; nkq / nvq and nks / nvs hold the new rows
+  // quantised by quant_new_rows ([B][Hkv][n_q][D] int8, [B][Hkv][n_q] fp16).
+  const uint16_t* ksc;
+  const uint16_t* vsc;
+  int8_t* nkq;
+  int8_t* nvq;
+  uint16_t* nks;
+  uint16_t* nvs;
   float qk_scale;  // scale * log2(e)
 };
 
@@ -660,11 +669,13 @@ __device__ __forceinline__ long long stream_share(const AttnArgs& a, long long W
 // lengths, and one workgroup per slot means no workgroup waits to be
 // dispatched.  Workgroup 0 also stores the per-slab block prefix pre[b] for
 // the combine.
-template <int D, int NW, int NST, int PG>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
-void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
-  using LY = BfLayout<D>;
-  SPECV_BF16_STAGE_LDS
+// The stream scheme's walk, shared by the stream kernels: find this
+// workgroup's share of the slabs' key blocks and call
+// piece(b, g, rg, L, k0, k1, whole, slot, append) for every slab piece in it,
+// in order (every wave of the workgroup makes the same calls; a workgroup
+// barrier separates consecutive pieces).
+template <typename Piece>
+__device__ __forceinline__ void stream_walk(const AttnArgs& a, Piece&& piece) {
   __shared__ long long sh_x[3];
   __shared__ int sh_b[2];
   const int tid = threadIdx.x;
@@ -744,8 +755,7 @@ void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
       first = false;
       const int L = ufl(a.len[b]);
       const size_t slot = (((size_t)b * a.Hkv + g) * a.RG + rg) * a.JP + (size_t)j;
-      bf16_piece<D, NW, NST, PG>(a, kbuf, vbuf, b, g, rg, L, off * KB, min(end * KB, L + a.n_q), whole, slot,
-                                 off == 0 && rg == 0, table);
+      piece(b, g, rg, L, off * KB, min(end * KB, L + a.n_q), whole, slot, off == 0 && rg == 0);
     }
     x = uniform64(x + take);
     off = 0;
@@ -756,6 +766,389 @@ void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
       nbb = b < a.B ? ufl(slab_blocks(a, b)) : 0;
     }
   }
+}
+
+template <int D, int NW, int NST, int PG>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
+void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
+  using LY = BfLayout<D>;
+  SPECV_BF16_STAGE_LDS
+  stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append) {
+    bf16_piece<D, NW, NST, PG>(a, kbuf, vbuf, b, g, rg, L, k0, k1, whole, slot, append, table);
+  });
+}
+
+
+// ---------------------------------------------------------------------------
+// int8 cache ([P2] PagedAttentionとKVキャッシュの量子化: rows rounded to int8
+// with a per-(head, position) absmax scale kept in fp16)
+// ---------------------------------------------------------------------------
+
+// Quantise the n_q new K and V rows of each (b, g) into the workspace: s =
+// max|x| / 127, q = round-half-even(x / s) clipped to +-127 (fp32, correctly
+// rounded division), scale stored as fp16(s); a zero row gives s = 0, q = 0.
+// Grid B * Hkv; 16 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void quant_new_rows(AttnArgs a) {
+  constexpr int EPL = D / 16;  // elements per lane
+  const long bg = blockIdx.x;
+  const int grp = threadIdx.x >> 4, gl = threadIdx.x & 15;
+  for (int r = grp; r < 2 * a.n_q; r += 16) {
+    const bool is_v = r >= a.n_q;
+    const int rr = is_v ? r - a.n_q : r;
+    const uint16_t* src = static_cast<const uint16_t*>(is_v ? a.vn : a.kn) + ((size_t)bg * a.n_q + rr) * D + gl * EPL;
+    float x[EPL];
+    float m = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      x[e] = bf16_to_f32(src[e]);
+      m = fmaxf(m, fabsf(x[e]));
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 16));
+    const float sc = m / 127.f;
+    int8_t* dq = (is_v ? a.nvq : a.nkq) + ((size_t)bg * a.n_q + rr) * D + gl * EPL;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float qv = sc > 0.f ? fminf(fmaxf(__builtin_rintf(x[e] / sc), -127.f), 127.f) : 0.f;
+      dq[e] = (int8_t)(int)qv;
+    }
+    if (gl == 0) {
+      const _Float16 h = (_Float16)sc;
+      (is_v ? a.nvs : a.nks)[(size_t)bg * a.n_q + rr] = __builtin_bit_cast(uint16_t, h);
+    }
+  }
+}
+
+// Stages of the int8 kernel: raw int8 K and V tiles and the block's 32 K
+// then 32 V scales, one LDS object each (see the bf16 stages); the widened
+// bf16 tiles (swizzled like the bf16 kernel's stages) and the new rows'
+// scales.
+#define SPECV_I8_STAGE_LDS \
+  __shared__ __attribute__((aligned(1024))) int8_t qk0[KB * D], qv0[KB * D]; \
+  __shared__ __attribute__((aligned(1024))) int8_t qk1[KB * D], qv1[KB * D]; \
+  __shared__ __attribute__((aligned(1024))) int8_t qk2[NST > 2 ? KB * D : 16], qv2[NST > 2 ? KB * D : 16]; \
+  __shared__ __attribute__((aligned(16))) uint16_t sc0[64], sc1[64], sc2[64]; \
+  __shared__ __attribute__((aligned(1024))) uint16_t cvk[KB * D], cvv[KB * D]; \
+  __shared__ float nsk[16], nsv[16]; \
+  auto qkbuf = [&](auto S) -> int8_t* { \
+    if constexpr (decltype(S)::value == 0) return qk0; \
+    else if constexpr (decltype(S)::value == 1) return qk1; \
+    else return qk2; \
+  }; \
+  auto qvbuf = [&](auto S) -> int8_t* { \
+    if constexpr (decltype(S)::value == 0) return qv0; \
+    else if constexpr (decltype(S)::value == 1) return qv1; \
+    else return qv2; \
+  }; \
+  auto scbuf = [&](auto S) -> uint16_t* { \
+    if constexpr (decltype(S)::value == 0) return sc0; \
+    else if constexpr (decltype(S)::value == 1) return sc1; \
+    else return sc2; \
+  };
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// One piece of one (b, g, rg) over the int8 cache.  As bf16_piece, with:
+// copies move raw int8 rows (32 D bytes per tile) and the block's scales;
+// after the barrier every wave widens its share of the int8 tiles into the
+// bf16 tiles cvk / cvv (exactly: |q| <= 127), a second barrier, then the
+// bf16 MFMA path runs on them.  Scores are multiplied by their key's K scale
+// before the softmax, and each probability by its key's V scale before PV
+// (the row sum uses the unscaled probabilities).  Keys [L, L + n_q) are the
+// quantised new rows from the workspace.
+template <int D, int NW, int NST, typename QK, typename QV, typename SC>
+__device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, SC scbuf, uint16_t* cvk,
+                                         uint16_t* cvv, float* nsk, float* nsv, int b, int g, int rg, int L, int k0,
+                                         int k1, bool whole, size_t slot, bool append) {
+  using LY = BfLayout<D>;
+  constexpr int DS = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int NI8 = KB * D / 1024;                    // 1 KB copies per int8 tile
+  constexpr int WI = NW >= 4 ? 4 : (NW >= 2 ? 2 : 1);
+  constexpr int CPW8 = 2 * NI8 / WI;                    // data copies per issuing wave per block
+  constexpr int CPW = CPW8 + 1;                         // plus the scale copy
+  static_assert((2 * NI8) % WI == 0, "copies must split evenly over the issuing waves");
+  static_assert(NST >= 2 && NST <= 3 && (NST - 2) * CPW <= 63, "stages");
+  int tid = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid));
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const long bg = (long)b * a.Hkv + g;
+  const int Ltot = L + a.n_q;
+  const int nblk = (k1 - k0 + KB - 1) / KB;
+
+  const int8_t* kc = static_cast<const int8_t*>(a.kc) + (size_t)bg * a.max_T * D;
+  const int8_t* vc = static_cast<const int8_t*>(a.vc) + (size_t)bg * a.max_T * D;
+  const int8_t* knb = a.nkq + (size_t)bg * a.n_q * D;
+  const int8_t* vnb = a.nvq + (size_t)bg * a.n_q * D;
+  const uint16_t* ksr = a.ksc + (size_t)bg * a.max_T;
+  const uint16_t* vsr = a.vsc + (size_t)bg * a.max_T;
+
+  // The new rows' scales, for blocks reaching them (before any copy of this
+  // piece is in flight).
+  if (tid < a.n_q) {
+    nsk[tid] = f16_to_f32(a.nks[(size_t)bg * a.n_q + tid]);
+    nsv[tid] = f16_to_f32(a.nvs[(size_t)bg * a.n_q + tid]);
+  }
+
+  // Data copy i of an issuing wave: copy c = wave + i WI (K for c < NI8);
+  // lane l moves bytes [1024 c' + 16 l, +16) of the tile, row (1024 c' +
+  // 16 l) / D.  The scale copy: lanes 0..3 the K scales of keys 8 l .. 8 l +
+  // 7, lanes 4..7 the V scales; every issuing wave issues it (identical
+  // data), so each issues CPW copies per block.
+  auto issue_block = [&](int kb, auto S) {
+    if (wave >= WI) return;
+    const bool full = kb + KB <= L;
+#pragma unroll
+    for (int i = 0; i < CPW8; ++i) {
+      const int c = wave + i * WI;
+      const bool is_v = c >= NI8;
+      const int cc = is_v ? c - NI8 : c;
+      const uint32_t boff = (uint32_t)(cc * 1024 + 16 * lane);  // byte offset in the tile
+      int8_t* dst = (is_v ? qvbuf(S) : qkbuf(S)) + cc * 1024;
+      const int8_t* cache = is_v ? vc : kc;
+      if (full) {
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (size_t)kb * D), (short)0, KB * D, 0x00020000);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3)))*)dst, 16, (int)boff,
+                                                 0, 0, 0);
+      } else {
+        const int key = kb + (int)(boff / D);
+        const int8_t* fresh = is_v ? vnb : knb;
+        const int8_t* src = key < L ? cache + (size_t)kb * D + boff
+                                    : fresh + (size_t)(key < Ltot ? key - L : 0) * D + boff % D;
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                         (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+      }
+    }
+    if (lane < 8) {
+      // Rows past the cache's end are never used: clamp the key into it.
+      const int key = min(kb + 8 * (lane & 3), a.max_T - 8);
+      const uint16_t* src = (lane < 4 ? ksr : vsr) + key;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)scbuf(S), 16, 0, 0);
+    }
+  };
+
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const int m = rg * 16 * NW + 16 * wave + lr;
+  const bool valid = m < a.M;
+  const int h = g * a.G + (valid ? m / a.n_q : 0);
+  const int qi = valid ? m % a.n_q : a.n_q - 1;
+  const int lim = L + qi;
+  bf16x8 qf[DS];
+  {
+    const uint16_t* qrow = q + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+      qf[s] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg) : bf16x8{};
+  }
+
+  issue_block(k0, IC<0>{});
+  if constexpr (NST > 2) {
+    if (nblk > 1) issue_block(k0 + KB, IC<1>{});
+  }
+
+  int kofs[DS], vofs[DT];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) kofs[s] = lr * D + 8 * LY::kslot(lr, 4 * s + lg);
+  {
+    const int vrow = 4 * lg + (lr >> 2), q4 = lr & 3;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vofs[dt] = vrow * D + 8 * LY::vslot(vrow, 2 * dt + (q4 >> 1)) + 4 * (q4 & 1);
+  }
+  static_assert(LY::same_swizzle_16_rows_apart(), "kt / hh offsets");
+
+  const float c = a.qk_scale;
+  float mrow = neg_inf_f(), lsum = 0.f;
+  f32x4 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Scales of this lane's 8 keys kb + 16 kt + 4 lg + jj (K then V).
+  auto key_scales = [&](auto S, int kb, float (&sk)[8], float (&sv)[8]) {
+    const uint16_t* sc = scbuf(S);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint2 wk = *reinterpret_cast<const uint2*>(sc + 16 * kt + 4 * lg);
+      const uint2 wv = *reinterpret_cast<const uint2*>(sc + 32 + 16 * kt + 4 * lg);
+      const uint32_t hk[4] = {wk.x & 0xffffu, wk.x >> 16, wk.y & 0xffffu, wk.y >> 16};
+      const uint32_t hv[4] = {wv.x & 0xffffu, wv.x >> 16, wv.y & 0xffffu, wv.y >> 16};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        sk[4 * kt + jj] = f16_to_f32((uint16_t)hk[jj]);
+        sv[4 * kt + jj] = f16_to_f32((uint16_t)hv[jj]);
+      }
+    }
+    if (kb + KB > L) {  // keys at or past L: the new rows' scales, or 0 (masked)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int key = kb + 16 * kt + 4 * lg + jj;
+          if (key >= L) {
+            sk[4 * kt + jj] = key < Ltot ? nsk[key - L] : 0.f;
+            sv[4 * kt + jj] = key < Ltot ? nsv[key - L] : 0.f;
+          }
+        }
+    }
+  };
+
+  auto step = [&](auto S, int j) {
+    const int kb = k0 + j * KB;
+    if (NST > 2 && j + 1 < nblk)
+      wait_vmcnt<(NST > 2 ? CPW : 0)>();
+    else
+      wait_vmcnt<0>();
+    block_barrier();
+    if (j + NST - 1 < nblk) issue_block(kb + (NST - 1) * KB, IC<(decltype(S)::value + NST - 1) % NST>{});
+
+    // Widen the int8 tiles of block j into cvk / cvv (8 values per item).
+    // One loop per tile: each reads a single LDS object, so the compiler can
+    // tell the reads from the copies in flight into other stages and does not
+    // wait for them.
+    {
+      constexpr int PER = KB * D / 8;  // 8-value items per tile
+      auto widen = [&](const int8_t* tile, uint16_t* cv, bool is_v) {
+        for (int it = tid; it < PER; it += 64 * NW) {
+          const int row = it / (D / 8), sl = it % (D / 8);
+          const uint2 w = *reinterpret_cast<const uint2*>(tile + row * D + 8 * sl);
+          uint32_t o[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t word = k < 2 ? w.x : w.y;
+            const int sh = 16 * (k & 1);
+            const float lo = (float)(int)(int8_t)(uint8_t)(word >> sh);
+            const float hi = (float)(int)(int8_t)(uint8_t)(word >> (sh + 8));
+            o[k] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);  // exact in bf16
+          }
+          const int slot = is_v ? LY::vslot(row, sl) : LY::kslot(row, sl);
+          *reinterpret_cast<uint4*>(cv + row * D + 8 * slot) = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+      };
+      widen(qkbuf(S), cvk, false);
+      widen(qvbuf(S), cvv, true);
+    }
+    float skey[8], svkey[8];
+    key_scales(S, kb, skey, svkey);
+    block_barrier();
+
+    float sc[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cvk + kofs[s] + 16 * kt * D);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) sc[4 * kt + jj] = acc[jj] * skey[4 * kt + jj];
+    }
+    float alpha;
+    {
+      if (kb + KB > L) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int key = kb + 16 * kt + 4 * lg + jj;
+            if (key >= Ltot || key > lim) sc[4 * kt + jj] = neg_inf_f();
+          }
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
+      const float mnew = fmaxf(mrow, group_max(mx) * c);
+      const bool none = (mnew == neg_inf_f());
+      alpha = none ? 1.f : exp2_fast(mrow - mnew);
+      float ps = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        sc[jj] = none ? 0.f : exp2_fast(fmaf(sc[jj], c, -mnew));
+        ps += sc[jj];
+      }
+      lsum = fmaf(lsum, alpha, ps);
+      mrow = mnew;
+    }
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    }
+    bf16x8 pf;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) pf[jj] = (__bf16)(sc[jj] * svkey[jj]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      s16x4 v2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        v2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(cvv + vofs[dt] + 16 * hh * D));
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
+    }
+  };
+
+  for (int j = 0; j < nblk; j += NST) {
+    step(IC<0>{}, j);
+    if (j + 1 < nblk) step(IC<1>{}, j + 1);
+    if constexpr (NST > 2) {
+      if (j + 2 < nblk) step(IC<2>{}, j + 2);
+    }
+  }
+
+  // A1: the quantised new rows and their scales into the cache.
+  if (append) {
+    constexpr int CPR = D / 16;  // 16-byte chunks per int8 row
+    for (int cidx = tid; cidx < 2 * a.n_q * CPR; cidx += 64 * NW) {
+      const bool is_v = cidx >= a.n_q * CPR;
+      const int cc = is_v ? cidx - a.n_q * CPR : cidx;
+      const uint4* src = reinterpret_cast<const uint4*>(is_v ? vnb : knb) + cc;
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<int8_t*>(is_v ? a.vc : a.kc) + ((size_t)bg * a.max_T + L) * D) + cc;
+      *dst = *src;
+    }
+    if (tid < 2 * a.n_q) {
+      const bool is_v = tid >= a.n_q;
+      const int r = is_v ? tid - a.n_q : tid;
+      uint16_t* dst = const_cast<uint16_t*>(is_v ? a.vsc : a.ksc) + (size_t)bg * a.max_T + L + r;
+      *dst = (is_v ? a.nvs : a.nks)[(size_t)bg * a.n_q + r];
+    }
+  }
+
+  const float lt = group_sum(lsum);
+  const int row = 16 * wave + lr;
+  if (whole) {
+    if (valid) {
+      uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
+      const float inv = 1.f / lt;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 16 * dt + 4 * lg;
+        uint2 pk;
+        pk.x = uint32_t(f32_to_bf16(oacc[dt][0] * inv)) | (uint32_t(f32_to_bf16(oacc[dt][1] * inv)) << 16);
+        pk.y = uint32_t(f32_to_bf16(oacc[dt][2] * inv)) | (uint32_t(f32_to_bf16(oacc[dt][3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(o + d) = pk;
+      }
+    }
+    return;
+  }
+  float* po = a.part_o + slot * (16 * NW) * D;
+  if (lg == 0) a.part_ml[slot * (16 * NW) + row] = ML{mrow, lt};
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[dt];
+}
+
+template <int D, int NW, int NST>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
+void attn_stream_i8(AttnArgs a) {
+  SPECV_I8_STAGE_LDS
+  stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append) {
+    i8_piece<D, NW, NST>(a, qkbuf, qvbuf, scbuf, cvk, cvv, nsk, nsv, b, g, rg, L, k0, k1, whole, slot, append);
+  });
 }
 
 // Merge the pieces of each (b, g, rg) slab the stream kernel cut; one
@@ -1144,6 +1537,35 @@ static hipError_t launch_stream(const AttnArgs& a0, hipStream_t s) {
 }
 
 template <int D, int NW>
+static hipError_t launch_i8(const AttnArgs& a0, hipStream_t s) {
+  AttnArgs a = a0;
+  hipLaunchKernelGGL((quant_new_rows<D>), dim3((unsigned)((size_t)a.B * a.Hkv)), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  a.P = stream_workgroups(attn_stream_i8<D, NW, kStages>, NW);
+  hipLaunchKernelGGL((attn_stream_i8<D, NW, kStages>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_i8_d(const AttnArgs& a, hipStream_t s) {
+  switch (a.RT) {
+    case 1: return launch_i8<D, 1>(a, s);
+    case 2: return launch_i8<D, 2>(a, s);
+    case 3: return launch_i8<D, 3>(a, s);
+    case 4: return launch_i8<D, 4>(a, s);
+    case 5: return launch_i8<D, 5>(a, s);
+    case 6: return launch_i8<D, 6>(a, s);
+    case 7: return launch_i8<D, 7>(a, s);
+    case 8: return launch_i8<D, 8>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, int NW>
 static hipError_t launch_bf16(const AttnArgs& a0, hipStream_t s) {
   if (a0.pre) {  // stream scheme
     if (a0.table) return a0.page == 16 ? launch_stream<D, NW, 16>(a0, s) : launch_stream<D, NW, 32>(a0, s);
@@ -1321,4 +1743,99 @@ extern "C" spec_status_t spec_verify_attention_paged(const void* q, const void* 
   return verify_attention(q, k_new, v_new, k_pages, v_pages, cache_len, out, B, Hq, Hkv, n_q, D, (int)cap,
                           max_len_hint, scale, dtype, workspace, workspace_bytes, stream, block_table, page_size,
                           num_pages, max_blocks);
+}
+
+// ---- int8 cache entry points ------------------------------------------------
+
+// Stream-scheme workspace followed by the quantised new rows (int8 K, int8 V,
+// fp16 K scales, fp16 V scales).
+struct I8Plan {
+  StreamPlan sp;
+  size_t off_nkq, off_nvq, off_nks, off_nvs, total;
+};
+
+static I8Plan i8_plan(int B, int Hq, int Hkv, int n_q, int D, int hint) {
+  I8Plan p{};
+  const AttnPlan ap = attn_plan(B, Hq, Hkv, n_q, D, hint, SPEC_BF16);
+  p.sp = stream_plan(B, Hkv, ap.RG, ap.RT, n_q, D, hint);
+  const size_t rows = (size_t)B * Hkv * n_q;
+  size_t off = p.sp.total;
+  p.off_nkq = off;
+  off = align256(off + rows * D);
+  p.off_nvq = off;
+  off = align256(off + rows * D);
+  p.off_nks = off;
+  off = align256(off + rows * 2);
+  p.off_nvs = off;
+  off = align256(off + rows * 2);
+  p.total = off;
+  return p;
+}
+
+extern "C" size_t spec_verify_attention_int8_workspace_size(int B, int Hq, int Hkv, int n_q, int D, int max_len_hint) {
+  if (B < 1 || B > 1024 || Hq < 1 || Hkv < 1 || n_q < 1 || n_q > 16 || max_len_hint < 0) return 0;
+  if (Hq % Hkv != 0 || (Hq / Hkv) * n_q > 256 || (D != 64 && D != 128)) return 0;
+  const AttnPlan ap = attn_plan(B, Hq, Hkv, n_q, D, max_len_hint, SPEC_BF16);
+  if (!stream_ok(SPEC_BF16, B, Hkv, ap.RG, n_q, max_len_hint)) return 0;
+  return i8_plan(B, Hq, Hkv, n_q, D, max_len_hint).total;
+}
+
+extern "C" spec_status_t spec_verify_attention_int8(const void* q, const void* k_new, const void* v_new,
+                                                    void* k_cache, void* k_scale, void* v_cache, void* v_scale,
+                                                    const int32_t* cache_len, void* out, int B, int Hq, int Hkv,
+                                                    int n_q, int D, int max_T, int max_len_hint, float scale,
+                                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k_new || !v_new || !k_cache || !k_scale || !v_cache || !v_scale || !cache_len || !out || !workspace)
+    return SPEC_ERR_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || n_q < 1 || D < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
+  if (Hq % Hkv != 0) return SPEC_ERR_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return SPEC_ERR_ARG;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_new) |
+                       reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(k_scale) |
+                       reinterpret_cast<uintptr_t>(v_scale) | reinterpret_cast<uintptr_t>(out);
+  if (al % 16 != 0 || reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
+  if (max_T % 8 != 0) return SPEC_ERR_ARG;  // scale rows are copied 8 at a time
+  if ((long)max_len_hint + n_q > (long)max_T) return SPEC_ERR_OVERFLOW;
+  if (n_q > 16 || (Hq / Hkv) * n_q > 256 || (D != 64 && D != 128)) return SPEC_ERR_UNSUPPORTED;
+  const AttnPlan p = attn_plan(B, Hq, Hkv, n_q, D, max_len_hint, SPEC_BF16);
+  if (!stream_ok(SPEC_BF16, B, Hkv, p.RG, n_q, max_len_hint)) return SPEC_ERR_UNSUPPORTED;
+  const I8Plan ip = i8_plan(B, Hq, Hkv, n_q, D, max_len_hint);
+  if (workspace_bytes < ip.total) return SPEC_ERR_ARG;
+
+  AttnArgs a{};
+  a.q = q;
+  a.kn = k_new;
+  a.vn = v_new;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.len = cache_len;
+  a.out = out;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = reinterpret_cast<float*>(ws + ip.sp.off_o);
+  a.part_ml = reinterpret_cast<ML*>(ws + ip.sp.off_ml);
+  a.pre = reinterpret_cast<int*>(ws + ip.sp.off_pre);
+  a.MINB = ip.sp.MINB;
+  a.JP = ip.sp.JP;
+  a.ksc = static_cast<const uint16_t*>(k_scale);
+  a.vsc = static_cast<const uint16_t*>(v_scale);
+  a.nkq = reinterpret_cast<int8_t*>(ws + ip.off_nkq);
+  a.nvq = reinterpret_cast<int8_t*>(ws + ip.off_nvq);
+  a.nks = reinterpret_cast<uint16_t*>(ws + ip.off_nks);
+  a.nvs = reinterpret_cast<uint16_t*>(ws + ip.off_nvs);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.n_q = n_q;
+  a.G = Hq / Hkv;
+  a.M = a.G * n_q;
+  a.RG = p.RG;
+  a.RT = p.RT;
+  a.NSP = p.NSP;
+  a.C = p.C;
+  a.max_T = max_T;
+  a.hint = max_len_hint;
+  a.qk_scale = scale * 1.4426950408889634f;
+  const hipError_t e = D == 128 ? launch_i8_d<128>(a, stream) : launch_i8_d<64>(a, stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
 }

@@ -1,0 +1,107 @@
+"""GPU parity of spec_verify_attention_int8 (int8 KV cache with fp16 row scales).
+
+The cache is seeded int8 codes with fp16 scales; the new rows are bf16.  The
+output must match ``oracle.quant`` within the bf16 tolerance; the appended
+rows' int8 codes and fp16 scales must equal the oracle's quantisation bit
+for bit (the codes are decided in fp32 on both sides); no other row changes.
+Every case prints its name first.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import speculative_decoding_verification_spec_amd as sv
+import workloads as W
+from oracle import quant as Q
+from tests import _gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(name, **kw):
+    print(f"\n[case] {name} {kw}", flush=True)
+
+
+def _run(inp, hint=None):
+    d = {k: _gpu.to_dev(v) for k, v in inp.items()}
+    hint = int(inp["lens"].max()) if hint is None else hint
+    out = sv.spec_verify_attention_int8(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["k_scale"], d["v_cache"],
+                                        d["v_scale"], d["lens"], hint)
+    torch.cuda.synchronize()
+    return {"out": _gpu.to_host(out), **{k: _gpu.to_host(d[k]) for k in ("k_cache", "k_scale", "v_cache", "v_scale")}}
+
+
+def _check(inp, res, seqs=None, relative=False):
+    B = inp["q"].shape[0]
+    seqs = list(range(B)) if seqs is None else list(seqs)
+    want = Q.verify_attention_int8(inp["q"], inp["k_new"], inp["v_new"], inp["k_cache"], inp["k_scale"],
+                                   inp["v_cache"], inp["v_scale"], inp["lens"], seqs=seqs)
+    got = _gpu.as_f64(res["out"][seqs])
+    # bf16 outputs round relative to their size: outputs far above 1 (a loud
+    # new row) are held to the tolerance relative to their magnitude.
+    norm = np.maximum(1.0, np.abs(want)) if relative else 1.0
+    err = np.max(np.abs(got - want) / norm)
+    print("max abs err" + (" (relative above 1)" if relative else ""), err, flush=True)
+    assert np.all(np.isfinite(got)) and err < _gpu.ATT_TOL["bf16"]
+    kq, ks, vq, vs = Q.kv_append_int8(inp["k_cache"], inp["k_scale"], inp["v_cache"], inp["v_scale"],
+                                      inp["k_new"], inp["v_new"], inp["lens"])
+    for name, want_a in (("k_cache", kq), ("k_scale", ks), ("v_cache", vq), ("v_scale", vs)):
+        g, w = res[name][seqs], want_a[seqs]
+        assert np.array_equal(g.view(np.uint8) if g.dtype == np.int8 else g.view(np.uint16),
+                              w.view(np.uint8) if w.dtype == np.int8 else w.view(np.uint16)), name
+
+
+def test_config4_int8():
+    cfg = W.get(4)
+    _case("int8 config4", B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D)
+    inp = W.attention_inputs_int8(cfg)
+    _check(inp, _run(inp, hint=cfg.L[1]))
+
+
+@pytest.mark.parametrize(
+    "B,Hq,Hkv,n_q,D,lens",
+    [
+        (3, 8, 2, 5, 128, [0, 31, 33]),       # empty cache, block edges
+        (2, 16, 2, 9, 128, [257, 2000]),      # 72 rows per KV head (5 tiles)
+        (2, 4, 4, 1, 64, [1, 1000]),          # n_q = 1, D = 64
+        (1, 8, 1, 5, 128, [3000]),            # one sequence over many workgroups
+        (300, 4, 4, 3, 128, None),            # many one- or two-block slabs
+    ],
+)
+def test_shapes(B, Hq, Hkv, n_q, D, lens):
+    _case("int8 shape", B=B, Hq=Hq, Hkv=Hkv, n_q=n_q, D=D, lens=lens)
+    if lens is None:
+        lens = np.random.default_rng(B).integers(0, 4, B).astype(np.int32)
+    max_T = (max(lens) + n_q + 7 + 7) // 8 * 8
+    cfg = W.Config(95, "int8", B=B, gamma=n_q - 1, V=1, dtype="bf16", Hq=Hq, Hkv=Hkv, D=D, L=(0, int(max(lens))),
+                   max_T=max_T)
+    inp = W.attention_inputs_int8(cfg, B=B, max_T=max_T, lens=lens)
+    _check(inp, _run(inp))
+
+
+def test_zero_and_loud_new_rows():
+    cfg = W.get(4)
+    _case("int8 zero / loud new rows")
+    inp = W.attention_inputs_int8(cfg, B=2, lens=[100, 700])
+    inp["k_new"][0, 1, 2] = 0       # a zero row: scale 0, codes 0
+    inp["v_new"][1, 0, :] = W.bf16_bits(np.full(128, 1000.0, np.float32))  # one value per row
+    _check(inp, _run(inp, hint=cfg.L[1]), relative=True)
+
+
+def test_status_codes():
+    _case("int8 status")
+    dev = "cuda"
+    q = torch.zeros((1, 4, 5, 128), dtype=torch.bfloat16, device=dev)
+    kn = torch.zeros((1, 2, 5, 128), dtype=torch.bfloat16, device=dev)
+    kc = torch.zeros((1, 2, 68, 128), dtype=torch.int8, device=dev)     # max_T not a multiple of 8
+    ks = torch.zeros((1, 2, 68), dtype=torch.float16, device=dev)
+    lens = torch.zeros(1, dtype=torch.int32, device=dev)
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_verify_attention_int8(q, kn, kn, kc, ks, kc.clone(), ks.clone(), lens, 10)
+    assert e.value.status == 1
+    kc = torch.zeros((1, 2, 64, 128), dtype=torch.int8, device=dev)
+    ks = torch.zeros((1, 2, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_verify_attention_int8(q, kn, kn, kc, ks, kc.clone(), ks.clone(), lens, 60)  # 60 + 5 > 64
+    assert e.value.status == 2

@@ -2,7 +2,7 @@
 
 This module serves both the GPU path's tests/bench and the oracle.  It holds
 none of the verification method's arithmetic: it only draws logits, Q/K/V,
-lengths and uniforms, rounds fp32 to bfloat16 (round-to-nearest-even), and
+lengths, uniforms and int8 cache codes with their scales, rounds fp32 to bfloat16 (round-to-nearest-even), and
 samples draft tokens from the draft distribution with the Gumbel-max trick
 (argmax of z/T plus Gumbel noise), which is the draft model's job, not the
 verifier's, and uses none of the verifier's steps.
@@ -15,6 +15,7 @@ from .configs import CONFIGS, Config, get  # noqa: F401
 from .gen import (  # noqa: F401
     attention_inputs,
     attention_inputs_device,
+    attention_inputs_int8,
     bf16_bits,
     sampler_inputs,
     sampler_inputs_device,

@@ -191,3 +191,27 @@ def sampler_inputs_device(cfg: Config, device, temperature=None, rep: int = 0, B
         "uniforms": uni,
         "temperature": T,
     }
+
+
+def attention_inputs_int8(cfg: Config, rep: int = 0, B=None, max_T=None, lens=None):
+    """Host arrays for verify attention over an int8 cache.
+
+    q, k_new, v_new as ``attention_inputs`` (bf16 bits); k_cache / v_cache int8
+    [B, Hkv, max_T, D] and k_scale / v_scale float16 [B, Hkv, max_T], drawn so
+    that code * scale looks like the N(0, 1) rows of the other workloads: codes
+    are N(0, 1) * 127 / 2.7 rounded and clipped to [-127, 127], with one code
+    of magnitude 127 per row (the row's largest value), and scales 2.7 / 127
+    times a log-normal factor of spread 0.1.
+    """
+    base = attention_inputs(cfg, rep=rep, B=B, max_T=max_T, lens=lens)
+    B, Hkv, T, D = base["k_cache"].shape
+    r = rng(cfg, 4, rep)
+    out = {k: base[k] for k in ("q", "k_new", "v_new", "lens")}
+    for name in ("k", "v"):
+        codes = np.clip(np.rint(r.standard_normal((B, Hkv, T, D)) * (127 / 2.7)), -127, 127).astype(np.int8)
+        pos = r.integers(0, D, (B, Hkv, T))
+        sign = np.where(r.random((B, Hkv, T)) < 0.5, -127, 127).astype(np.int8)
+        np.put_along_axis(codes, pos[..., None], sign[..., None], axis=-1)
+        out[f"{name}_cache"] = codes
+        out[f"{name}_scale"] = (np.exp(0.1 * r.standard_normal((B, Hkv, T))) * (2.7 / 127)).astype(np.float16)
+    return out
