@@ -1182,15 +1182,33 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
   constexpr int D4 = D / 4;
   for (int e = threadIdx.x; e < nrows * D4; e += blockDim.x) {
     const int row = e / D4, d = 4 * (e % D4);
-    float mx = neg_inf_f();
-    for (int j = 0; j < np; ++j) mx = fmaxf(mx, a.part_ml[(base + j) * rows + row].m);
-    float den = 0.f;
+    // Online merge, four pieces at a time with all their loads in flight
+    // (the piece count is only known at run time).
+    float mx = neg_inf_f(), den = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < np; ++j) {
-      const ML ml = a.part_ml[(base + j) * rows + row];
-      const float w = exp2_fast(ml.m - mx);
-      den += w * ml.l;
-      acc += w * *reinterpret_cast<const f32x4*>(a.part_o + ((base + j) * rows + row) * D + d);
+    for (int j0 = 0; j0 < np; j0 += 4) {
+      ML ml[4];
+      f32x4 po[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool in = j0 + t < np;
+        const size_t pj = (base + j0 + t) * rows + row;
+        ml[t] = in ? a.part_ml[pj] : ML{neg_inf_f(), 0.f};
+        po[t] = in ? *reinterpret_cast<const f32x4*>(a.part_o + pj * D + d) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const float mc = fmaxf(fmaxf(ml[0].m, ml[1].m), fmaxf(ml[2].m, ml[3].m));
+      const float mn = fmaxf(mx, mc);
+      if (mn == neg_inf_f()) continue;  // no visible key in these pieces yet
+      const float r = exp2_fast(mx - mn);
+      den *= r;
+      acc *= r;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float w = exp2_fast(ml[t].m - mn);
+        den += w * ml[t].l;
+        acc += w * po[t];
+      }
+      mx = mn;
     }
     acc *= 1.f / den;
     uint2 pk;
@@ -1519,7 +1537,7 @@ static int stream_workgroups(K kernel, int NW) {
   // one takes ceil(NW / 4) slots on every SIMD (measured: 5-, 6- and 8-wave
   // workgroups fit 2 per CU whatever their registers and LDS).
   const int by_slots = NW <= 4 ? 4 * per_simd / NW : per_simd / ((NW + 3) / 4);
-  const int k = std::max(1, std::min(occ, by_slots));
+  int k = std::max(1, std::min(occ, by_slots));
   const int P = std::min(kStreamMaxWG, cus * k);
   if (slot) slot->store(P, std::memory_order_relaxed);
   return P;
