@@ -32,6 +32,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #ifndef SPECV_RS_LANE_BYTES
 #define SPECV_RS_LANE_BYTES 64
@@ -156,6 +157,32 @@ struct RawVec<4> { using type = uint32_t; };
 template <>
 struct RawVec<2> { using type = uint16_t; };
 
+// One raw vector through a buffer resource: a scalar base and a 32-bit byte
+// offset, so no 64-bit address is built in (and waits on) vector registers;
+// offsets past the resource's size read 0 and never fault.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <typename Raw>
+__device__ __forceinline__ Raw buf_raw(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ uint4 buf_raw<uint4>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <>
+__device__ __forceinline__ uint2 buf_raw<uint2>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
+template <>
+__device__ __forceinline__ uint32_t buf_raw<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ uint16_t buf_raw<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 template <typename T, int VEC>
 __device__ __forceinline__ void raw_to_f32(const typename RawVec<VEC * sizeof(T)>::type& r, float (&o)[VEC]) {
   constexpr int BYTES = VEC * (int)sizeof(T);
@@ -266,48 +293,99 @@ __device__ __forceinline__ void lane_weights(const T* __restrict__ rt, const T* 
   }
 }
 
+// The decision of sequence b, as rs_resid hands it to rs_draw.
+struct RsDecision {
+  int n;      // accepted positions; -1 when a draft token was out of range
+  int resid;  // 1: residual draw from max(0, p_n - q_n); 0: bonus draw from p_gamma
+  float Mt, inv_st, Md, inv_sd;
+  int pad[2];
+};
+
+// Merges the segments of every row of sequence b into rowM / rowS (fp64,
+// fixed order).  Waves over rows, two rows at a time; each part is loaded
+// once, 128 parts of a row per step (one step for up to 128 segments), and
+// the steps merge online.
+__device__ __forceinline__ void merge_rows(const RowPart* __restrict__ pb, int R, int nseg, float c32, int wave,
+                                           int nwave, int lane, float* rowM, double* rowS) {
+  for (int rr0 = wave; rr0 < R; rr0 += 2 * nwave) {
+    float m[2] = {neg_inf_f(), neg_inf_f()};
+    double sum[2] = {0.0, 0.0};
+    for (int c0 = 0; c0 < nseg; c0 += 2 * kWave) {
+      RowPart e[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rr = rr0 + j * nwave, k = c0 + h * kWave + lane;
+          if (rr < R && k < nseg) {
+            e[j][h] = pb[(size_t)rr * nseg + k];
+          } else {
+            e[j][h].M = neg_inf_f();
+            e[j][h].S = 0.0;
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float mc = wave_max(fmaxf(e[j][0].M, e[j][1].M));
+        if (mc == neg_inf_f()) continue;  // uniform: nothing in this step
+        double sc = 0.0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          if (e[j][h].M != neg_inf_f()) sc += e[j][h].S * (double)exp2_fast((e[j][h].M - mc) * c32);
+        sc = wave_sum(sc);
+        if (mc > m[j]) {
+          sum[j] = (m[j] == neg_inf_f() ? 0.0 : sum[j] * (double)exp2_fast((m[j] - mc) * c32)) + sc;
+          m[j] = mc;
+        } else {
+          sum[j] += sc * (double)exp2_fast((mc - m[j]) * c32);
+        }
+      }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rr = rr0 + j * nwave;
+        if (rr < R) {
+          rowM[rr] = m[j];
+          rowS[rr] = sum[j];
+        }
+      }
+    }
+  }
+}
+
+// Grid: x = sequence b, y = group of kResidWaves * spw segments of the
+// decided row; kResidWaves waves, spw segments each.  Every workgroup of b merges b's rows and takes the
+// decision (the same arithmetic in each, so all agree); workgroup y = 0 also
+// writes n_accepted, p_draft, q_draft and the decision record.  Then the
+// workgroup sums the residual weights max(0, p_n - q_n) (or p_gamma for the
+// bonus) and p_n (for the zero-residual fallback) over its segments, every
+// load of them issued before the arithmetic; lane sums in fp64.
+constexpr int kResidWaves = 8;
+
 template <typename T, int VEC, int NIT>
-__global__ __launch_bounds__(1024) void rs_tail(const T* __restrict__ tgt, const T* __restrict__ drf,
-                                                const int32_t* __restrict__ xtok, const double* __restrict__ uni,
-                                                int B, int G, int V, int nseg, float c32, double c64,
-                                                const RowPart* __restrict__ part, int32_t* __restrict__ n_out,
-                                                int32_t* __restrict__ tok_out, float* __restrict__ p_out,
-                                                float* __restrict__ q_out) {
+__global__ __launch_bounds__(kResidWaves * kWave) void rs_resid(
+    const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ xtok,
+    const double* __restrict__ uni, int G, int V, int nseg, int spw, float c32, double c64,
+    const RowPart* __restrict__ part, double2* __restrict__ segsum, RsDecision* __restrict__ dec, int32_t* __restrict__ n_out,
+    int32_t* __restrict__ tok_out, float* __restrict__ p_out, float* __restrict__ q_out) {
   constexpr int E = VEC * NIT;
   constexpr int SEG = kWave * E;
+  using Raw = typename RawVec<VEC * sizeof(T)>::type;
   __shared__ float rowM[64];
   __shared__ double rowS[64];
-  __shared__ double segw[kMaxSeg], segp[kMaxSeg];
   __shared__ int sh_n, sh_valid;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int nwave = blockDim.x / kWave;
   const int R = 2 * G + 1;
   const int b = blockIdx.x;
+  const bool lead = blockIdx.y == 0;
 
-  // (1) merge the segments of every row (fp64, fixed order); waves over rows
-  const RowPart* pb = part + (size_t)b * R * nseg;
-  for (int rr = wave; rr < R; rr += nwave) {
-    float mm = neg_inf_f();
-    for (int k = lane; k < nseg; k += kWave) mm = fmaxf(mm, pb[rr * nseg + k].M);
-    mm = wave_max(mm);
-    double ss = 0.0;
-    if (mm != neg_inf_f()) {
-      for (int k = lane; k < nseg; k += kWave) {
-        const RowPart e = pb[rr * nseg + k];
-        if (e.M != neg_inf_f()) ss += e.S * (double)exp2_fast((e.M - mm) * c32);
-      }
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) {
-      rowM[rr] = mm;
-      rowS[rr] = ss;
-    }
-  }
+  merge_rows(part + (size_t)b * R * nseg, R, nseg, c32, wave, kResidWaves, lane, rowM, rowS);
   __syncthreads();
 
-  // (2) wave 0: lane i < G judges position i against target row i and draft
-  // row G+1+i; n is the first rejection.
+  // wave 0: lane i < G judges position i against target row i and draft row
+  // G+1+i; n is the first rejection.
   if (wave == 0) {
     bool bad = false, reject = false;
     if (lane < G) {
@@ -326,8 +404,8 @@ __global__ __launch_bounds__(1024) void rs_tail(const T* __restrict__ tgt, const
         const double ratio = p / q;
         reject = !((u < 1.0) && (u < ratio));
       }
-      if (p_out) p_out[(size_t)b * G + lane] = (float)p;
-      if (q_out) q_out[(size_t)b * G + lane] = (float)q;
+      if (lead && p_out) p_out[(size_t)b * G + lane] = (float)p;
+      if (lead && q_out) q_out[(size_t)b * G + lane] = (float)q;
     }
     const uint64_t rej_mask = __ballot(reject);
     const uint64_t bad_mask = __ballot(bad);
@@ -335,113 +413,193 @@ __global__ __launch_bounds__(1024) void rs_tail(const T* __restrict__ tgt, const
     if (lane == 0) {
       sh_n = n;
       sh_valid = bad_mask ? 0 : 1;
-      n_out[b] = bad_mask ? -1 : n;
     }
-    if (bad_mask && lane <= G) tok_out[(size_t)b * (G + 1) + lane] = -1;
+    if (lead) {
+      if (lane == 0) n_out[b] = bad_mask ? -1 : n;
+      if (bad_mask && lane <= G) tok_out[(size_t)b * (G + 1) + lane] = -1;
+      if (lane == 0) {
+        RsDecision d{};
+        d.n = bad_mask ? -1 : n;
+        d.resid = n < G;
+        d.Mt = rowM[n];
+        d.inv_st = (float)(1.0 / rowS[n]);
+        d.Md = n < G ? rowM[G + 1 + n] : 0.f;
+        d.inv_sd = n < G ? (float)(1.0 / rowS[G + 1 + n]) : 1.f;
+        dec[b] = d;
+      }
+    }
   }
   __syncthreads();
   if (!sh_valid) return;  // uniform over the workgroup
-  const int n = sh_n;
+  // Uniform values in scalar registers: the row bases stay scalar.
+  const int n = __builtin_amdgcn_readfirstlane(sh_n);
   const bool resid = n < G;
   const T* rt = tgt + ((size_t)b * (G + 1) + n) * V;
-  const T* rd = resid ? drf + ((size_t)b * G + n) * V : rt;
+  const T* rd = drf + ((size_t)b * G + min(n, G - 1)) * V;  // never read unless resid
   const float Mt = rowM[n], Md = resid ? rowM[G + 1 + n] : 0.f;
   const float inv_st = (float)(1.0 / rowS[n]), inv_sd = resid ? (float)(1.0 / rowS[G + 1 + n]) : 1.f;
+  const __amdgpu_buffer_rsrc_t rsrc_t =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(rt), 0, (int)((long)V * sizeof(T)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsrc_d =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(rd), 0, (int)((long)V * sizeof(T)), 0x00020000);
 
-  // (3) per-segment sums of the residual weights max(0, p - q) (or p for the
-  // bonus) and of p (for the zero-residual fallback); waves over segments,
-  // coalesced loads, lane sums in fp64.
-  for (int seg = wave; seg < nseg; seg += nwave) {
-    double lw = 0.0, lp = 0.0;
-    const int s0 = seg * SEG;
+  // wave w takes segments [s0, s1) of this workgroup's spw * kResidWaves,
+  // two at a time
+  const int s0 = (blockIdx.y * kResidWaves + wave) * spw;
+  const int s1 = min(s0 + spw, nseg);
+  for (int seg0 = s0; seg0 < s1; seg0 += 2) {  // uniform per wave; no barrier follows
+    Raw at[2][NIT], ad[2][NIT];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int idx = s0 + (it * kWave + lane) * VEC;
-      if (idx < V) {
-        float zt[VEC], zd[VEC];
-        load_vec<T, VEC>(rt + idx, zt);
-        if (resid) load_vec<T, VEC>(rd + idx, zd);
-        float sw = 0.f, sp = 0.f;
+    for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-          const float p = exp2_fast((zt[k] - Mt) * c32) * inv_st;
-          sw += resid ? fmaxf(p - exp2_fast((zd[k] - Md) * c32) * inv_sd, 0.f) : p;
-          sp += p;
+      for (int it = 0; it < NIT; ++it) {
+        // elements past V read 0 from the buffer and are masked out below
+        const uint32_t off = (uint32_t)((seg0 + k) * SEG + (it * kWave + lane) * VEC) * (uint32_t)sizeof(T);
+        at[k][it] = buf_raw<Raw>(rsrc_t, off);
+        if (resid) ad[k][it] = buf_raw<Raw>(rsrc_d, off);
+      }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int seg = seg0 + k;
+      if (seg >= s1) break;
+      double lw = 0.0, lp = 0.0;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = seg * SEG + (it * kWave + lane) * VEC;
+        if (idx < V) {
+          float zt[VEC], zd[VEC];
+          raw_to_f32<T, VEC>(at[k][it], zt);
+          if (resid) raw_to_f32<T, VEC>(ad[k][it], zd);
+          float sw = 0.f, sp = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float p = exp2_fast((zt[e] - Mt) * c32) * inv_st;
+            sw += resid ? fmaxf(p - exp2_fast((zd[e] - Md) * c32) * inv_sd, 0.f) : p;
+            sp += p;
+          }
+          lw += (double)sw;
+          lp += (double)sp;
         }
-        lw += (double)sw;
-        lp += (double)sp;
+      }
+      lw = wave_sum(lw);
+      lp = wave_sum(lp);
+      if (lane == 0) segsum[(size_t)b * nseg + seg] = make_double2(lw, lp);
+    }
+  }
+}
+
+// Grid: x = sequence b; four waves.  Wave 0 takes the fp64 total of the
+// segment sums in a fixed order and the first segment whose prefix exceeds
+// u * total; then the four waves re-scan that segment in index order (lane l
+// of wave w holds the E/4 contiguous elements starting at (64 w + l) E/4;
+// the prefix is the segment's base, the totals of the waves before, then the
+// lane scan) and write the emitted tokens.  The segment sums and the re-scan
+// agree to rounding, which only matters for a draw within rounding of a
+// segment boundary -- inside the 1e-6 band.
+template <typename T, int VEC, int NIT>
+__global__ __launch_bounds__(4 * kWave) void rs_draw(const T* __restrict__ tgt, const T* __restrict__ drf,
+                                                    const int32_t* __restrict__ xtok,
+                                                    const double* __restrict__ uni, int G, int V, int nseg,
+                                                    float c32, const double2* __restrict__ segsum,
+                                                    const RsDecision* __restrict__ dec,
+                                                    int32_t* __restrict__ tok_out) {
+  constexpr int E = VEC * NIT;
+  constexpr int SEG = kWave * E;
+  constexpr int E4 = E / 4;
+  static_assert(NIT % 4 == 0, "the re-scan splits a segment over four waves");
+  __shared__ double sh_base, sh_target, sh_wtot[4];
+  __shared__ int sh_kseg, sh_from_last, sh_use_p, sh_hit[4], sh_lastj[4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int b = blockIdx.x;
+  const RsDecision d = dec[b];
+  if (d.n < 0) return;  // out-of-range draft token: outputs already written
+  const int n = __builtin_amdgcn_readfirstlane(d.n);
+  const bool resid = d.resid != 0;
+  const double2* sb = segsum + (size_t)b * nseg;
+
+  if (wave == 0) {
+    double W = 0.0;
+    for (int c0 = 0; c0 < nseg; c0 += kWave) {
+      const double v = (c0 + lane < nseg) ? sb[c0 + lane].x : 0.0;
+      W += __shfl(wave_inclusive_scan(v, lane), kWave - 1, kWave);
+    }
+    const bool use_p = resid && !(W > 0.0);  // zero residual mass: draw from p_n
+    if (use_p) {
+      W = 0.0;
+      for (int c0 = 0; c0 < nseg; c0 += kWave) {
+        const double v = (c0 + lane < nseg) ? sb[c0 + lane].y : 0.0;
+        W += __shfl(wave_inclusive_scan(v, lane), kWave - 1, kWave);
       }
     }
-    lw = wave_sum(lw);
-    lp = wave_sum(lp);
+    const double target = uni[(size_t)b * (G + 1) + G] * W;
+    int kseg = -1, last_pos = -1;
+    double base = 0.0, carry = 0.0;
+    for (int c0 = 0; c0 < nseg && kseg < 0; c0 += kWave) {
+      const bool in = c0 + lane < nseg;
+      const double v = in ? (use_p ? sb[c0 + lane].y : sb[c0 + lane].x) : 0.0;
+      const double incl = carry + wave_inclusive_scan(v, lane);
+      const double prev = __shfl_up(incl, 1, kWave);
+      const double excl = (lane == 0) ? carry : prev;
+      const uint64_t hit = __ballot(in && incl > target);
+      const uint64_t pos = __ballot(in && v > 0.0);
+      if (pos) last_pos = c0 + 63 - __builtin_clzll(pos);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        kseg = c0 + l;
+        base = __shfl(excl, l, kWave);
+      }
+      carry = __shfl(incl, kWave - 1, kWave);
+    }
+    const bool from_last = kseg < 0;  // the target reached the total by rounding
+    if (from_last) kseg = last_pos < 0 ? 0 : last_pos;
     if (lane == 0) {
-      segw[seg] = lw;
-      segp[seg] = lp;
+      sh_kseg = kseg;
+      sh_from_last = from_last;
+      sh_use_p = use_p;
+      sh_base = base;
+      sh_target = target;
     }
   }
   __syncthreads();
-  if (wave != 0) return;
 
-  // (4) wave 0: fp64 total in a fixed order, the first segment whose prefix
-  // exceeds u * total, then the first token inside it (re-scanned in index
-  // order; the two summation orders agree to rounding, which only matters for
-  // a draw within rounding of a segment boundary -- inside the 1e-6 band).
-  double W = 0.0;
-  for (int c0 = 0; c0 < nseg; c0 += kWave) {
-    const double v = (c0 + lane < nseg) ? segw[c0 + lane] : 0.0;
-    W += __shfl(wave_inclusive_scan(v, lane), kWave - 1, kWave);
-  }
-  const bool use_p = resid && !(W > 0.0);  // zero residual mass: draw from p_n
-  const double* sv = use_p ? segp : segw;
-  if (use_p) {
-    W = 0.0;
-    for (int c0 = 0; c0 < nseg; c0 += kWave) {
-      const double v = (c0 + lane < nseg) ? segp[c0 + lane] : 0.0;
-      W += __shfl(wave_inclusive_scan(v, lane), kWave - 1, kWave);
-    }
-  }
-  const double target = uni[(size_t)b * (G + 1) + G] * W;
-  int kseg = -1, last_pos = -1;
-  double base = 0.0, carry = 0.0;
-  for (int c0 = 0; c0 < nseg && kseg < 0; c0 += kWave) {
-    const bool in = c0 + lane < nseg;
-    const double v = in ? sv[c0 + lane] : 0.0;
-    const double incl = carry + wave_inclusive_scan(v, lane);
-    const double prev = __shfl_up(incl, 1, kWave);
-    const double excl = (lane == 0) ? carry : prev;
-    const uint64_t hit = __ballot(in && incl > target);
-    const uint64_t pos = __ballot(in && v > 0.0);
-    if (pos) last_pos = c0 + 63 - __builtin_clzll(pos);
-    if (hit) {
-      const int l = __ffsll((long long)hit) - 1;
-      kseg = c0 + l;
-      base = __shfl(excl, l, kWave);
-    }
-    carry = __shfl(incl, kWave - 1, kWave);
-  }
-  const bool from_last = kseg < 0;  // the target reached the total by rounding
-  if (from_last) kseg = last_pos < 0 ? 0 : last_pos;
-
-  float w[E];
-  const int j0 = kseg * SEG + lane * E;
-  lane_weights<T, VEC, NIT>(rt, rd, j0, V, c32, Mt, inv_st, Md, inv_sd, resid && !use_p, w);
+  const int kseg = __builtin_amdgcn_readfirstlane(sh_kseg);
+  const bool from_last = sh_from_last;
+  const double target = sh_target;
+  const T* rt = tgt + ((size_t)b * (G + 1) + n) * V;
+  const T* rd = drf + ((size_t)b * G + min(n, G - 1)) * V;  // never read unless resid
+  float w[E4];
+  const int j0 = kseg * SEG + (wave * kWave + lane) * E4;
+  lane_weights<T, VEC, NIT / 4>(rt, rd, j0, V, c32, d.Mt, d.inv_st, d.Md, d.inv_sd, resid && !sh_use_p, w);
   double l2 = 0.0;
 #pragma unroll
-  for (int k = 0; k < E; ++k) l2 += (double)w[k];
+  for (int k = 0; k < E4; ++k) l2 += (double)w[k];
   const double incl2 = wave_inclusive_scan(l2, lane);
+  if (lane == kWave - 1) sh_wtot[wave] = incl2;
+  __syncthreads();
+  double run = sh_base;
+  for (int q = 0; q < wave; ++q) run += sh_wtot[q];
   const double prev2 = __shfl_up(incl2, 1, kWave);
-  double run = base + (lane == 0 ? 0.0 : prev2);  // this lane's exclusive prefix
+  run += (lane == 0 ? 0.0 : prev2);  // this lane's exclusive prefix
   int hit_j = 0x7fffffff, last_j = -1;
 #pragma unroll
-  for (int k = 0; k < E; ++k) {
+  for (int k = 0; k < E4; ++k) {
     run += (double)w[k];
     if (w[k] > 0.f) {
       last_j = j0 + k;
       if (!from_last && hit_j == 0x7fffffff && run > target) hit_j = j0 + k;
     }
   }
-  int t = wave_min(hit_j);
-  if (t == 0x7fffffff) t = wave_max(last_j);
+  hit_j = wave_min(hit_j);
+  last_j = wave_max(last_j);
+  if (lane == 0) {
+    sh_hit[wave] = hit_j;
+    sh_lastj[wave] = last_j;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  int t = min(min(sh_hit[0], sh_hit[1]), min(sh_hit[2], sh_hit[3]));
+  if (t == 0x7fffffff) t = max(max(sh_lastj[0], sh_lastj[1]), max(sh_lastj[2], sh_lastj[3]));
   int32_t* ob = tok_out + (size_t)b * (G + 1);
   if (lane < n) ob[lane] = xtok[(size_t)b * G + lane];
   if (lane == n) ob[lane] = t;
@@ -590,9 +748,22 @@ __global__ __launch_bounds__(1024) void gs_tail(const int32_t* __restrict__ xtok
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>* slot = dev < 64 ? &cache[dev] : nullptr;
+  if (slot && slot->load(std::memory_order_relaxed) > 0) return slot->load(std::memory_order_relaxed);
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  if (slot) slot->store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 struct RsPlan {
   int vec, nit, seg, nseg;
-  size_t off_part1, total;
+  size_t off_part1, off_seg, off_dec, total;
 };
 
 static int pick_vec(int V, int esize, uintptr_t a, uintptr_t b) {
@@ -612,7 +783,9 @@ static RsPlan rs_plan(int B, int G, int V, int esize, int vec) {
   p.nseg = (V + p.seg - 1) / p.seg;
   const int R = 2 * G + 1;
   p.off_part1 = 0;
-  p.total = align256(sizeof(RowPart) * (size_t)B * R * p.nseg);
+  p.off_seg = align256(sizeof(RowPart) * (size_t)B * R * p.nseg);
+  p.off_dec = p.off_seg + align256(sizeof(double2) * (size_t)B * p.nseg);
+  p.total = p.off_dec + align256(sizeof(RsDecision) * (size_t)B);
   return p;
 }
 
@@ -629,11 +802,20 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
                      dim3(kWave * wpb), 0, stream, (const T*)tgt, (const T*)drf, G, V, pl.nseg, c32, part1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // One workgroup per sequence, one wave per segment of the decided row (up
-  // to 16 waves; at least one per row for the merge).
-  const int nw = std::min(16, std::max(std::max(1, (R + 1) / 2), pl.nseg));
-  hipLaunchKernelGGL((rs_tail<T, VEC, NIT>), dim3((unsigned)B), dim3(kWave * nw), 0, stream, (const T*)tgt,
-                     (const T*)drf, x, u, B, G, V, pl.nseg, c32, c64, part1, n_out, tok_out, p_out, q_out);
+  double2* segsum = reinterpret_cast<double2*>(ws + pl.off_seg);
+  RsDecision* dec = reinterpret_cast<RsDecision*>(ws + pl.off_dec);
+  // About two residual workgroups per CU, at least two segments per wave.
+  const int ngrp = std::max(1, std::min((2 * device_cus() + B - 1) / B, (pl.nseg + 2 * kResidWaves - 1) / (2 * kResidWaves)));
+  int spw = (pl.nseg + ngrp * kResidWaves - 1) / (ngrp * kResidWaves);
+  spw += spw & 1;
+  const int ny = (pl.nseg + spw * kResidWaves - 1) / (spw * kResidWaves);
+  hipLaunchKernelGGL((rs_resid<T, VEC, NIT>), dim3((unsigned)B, (unsigned)ny), dim3(kWave * kResidWaves), 0, stream,
+                     (const T*)tgt, (const T*)drf, x, u, G, V, pl.nseg, spw, c32, c64, part1, segsum, dec, n_out,
+                     tok_out, p_out, q_out);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((rs_draw<T, VEC, NIT>), dim3((unsigned)B), dim3(kWave * 4), 0, stream, (const T*)tgt,
+                     (const T*)drf, x, u, G, V, pl.nseg, c32, segsum, dec, tok_out);
   return hipGetLastError();
 }
 
