@@ -210,26 +210,38 @@ __device__ __forceinline__ void raw_to_f32(const typename RawVec<VEC * sizeof(T)
   }
 }
 
-// Grid: x = row (b * (2 gamma + 1) + r; target rows r <= gamma, then the
-// draft rows), y = group of waves along the row.  Each wave owns SPW
-// consecutive segments and issues every load of all of them before the
-// arithmetic (as many bytes in flight per wave as possible); a segment's
-// elements past V read as -inf.
+// Grid: x = chunk of rows (one workgroup per cpr-th of a row), rows in
+// position order gamma, gamma-1, ..., 0 and within a position by sequence,
+// the target row before the draft row; each wave owns SPW consecutive
+// segments and issues every load of all of them before the arithmetic (as
+// many bytes in flight per wave as possible); a segment's elements past V
+// read as -inf.  Position 0 comes last because the decided row is most often
+// an early position (each position is reached only if all before it were
+// accepted): read last, its rows are the likeliest still to be in the
+// memory-side cache when rs_resid reads the decided row again.
 template <typename T, int VEC, int NIT, int SPW>
-__global__ __launch_bounds__(1024) void rs_stats(const T* __restrict__ tgt, const T* __restrict__ drf, int G, int V,
-                                                 int nseg, float c32, RowPart* __restrict__ part) {
+__global__ __launch_bounds__(1024) void rs_stats(const T* __restrict__ tgt, const T* __restrict__ drf, int B, int G,
+                                                 int V, int nseg, int cpr, float c32, RowPart* __restrict__ part) {
   constexpr int SEG = kWave * VEC * NIT;
   using Raw = typename RawVec<VEC * sizeof(T)>::type;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int seg0 = (blockIdx.y * (blockDim.x / kWave) + wave) * SPW;
+  const int q = blockIdx.x / cpr, c = blockIdx.x - q * cpr;
+  const int seg0 = (c * (blockDim.x / kWave) + wave) * SPW;
   if (seg0 >= nseg) return;  // uniform per wave
+  int b, r;
+  if (q < B) {  // position gamma: the bonus row, target only
+    b = q;
+    r = G;
+  } else {
+    const int q2 = q - B, pos = G - 1 - q2 / (2 * B), rem = q2 % (2 * B);
+    b = rem >> 1;
+    r = (rem & 1) ? G + 1 + pos : pos;
+  }
   const int R = 2 * G + 1;
-  const int rowid = blockIdx.x;
-  const int b = rowid / R, r = rowid - b * R;
+  const int rowid = b * R + r;
   const T* row = (r <= G) ? tgt + ((size_t)b * (G + 1) + r) * V : drf + ((size_t)b * G + (r - G - 1)) * V;
   RowPart* out = part + (size_t)rowid * nseg;
-
   // Strided, fully coalesced loads: iteration it of a segment covers 64*VEC
   // consecutive elements.  Order does not matter for a max and a sum.
   Raw raw[SPW][NIT];
@@ -798,8 +810,9 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
   constexpr int SPW = SPECV_RS_SEGS_PER_WAVE;
   const int waves_row = (pl.nseg + SPW - 1) / SPW;
   const int wpb = std::min(SPECV_RS_WAVES_PER_BLOCK, waves_row);  // waves per block
-  hipLaunchKernelGGL((rs_stats<T, VEC, NIT, SPW>), dim3((unsigned)((long)B * R), (unsigned)((waves_row + wpb - 1) / wpb)),
-                     dim3(kWave * wpb), 0, stream, (const T*)tgt, (const T*)drf, G, V, pl.nseg, c32, part1);
+  const int cpr = (waves_row + wpb - 1) / wpb;  // workgroups per row
+  hipLaunchKernelGGL((rs_stats<T, VEC, NIT, SPW>), dim3((unsigned)((long)B * R * cpr)), dim3(kWave * wpb), 0, stream,
+                     (const T*)tgt, (const T*)drf, B, G, V, pl.nseg, cpr, c32, part1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   double2* segsum = reinterpret_cast<double2*>(ws + pl.off_seg);
@@ -902,7 +915,13 @@ extern "C" spec_status_t spec_reject_sample(const void* target_logits, const voi
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_ARG;
   if (!greedy && (!(temperature > 0.f) || !isfinite(temperature))) return SPEC_ERR_ARG;
   if (workspace_bytes < spec_reject_sample_workspace_size(B, gamma, V, dtype)) return SPEC_ERR_ARG;
-  if (rs_plan(B, gamma, V, dtype == SPEC_BF16 ? 2 : 4, 1).nseg > kMaxSeg) return SPEC_ERR_UNSUPPORTED;
+  {
+    const int nseg1 = rs_plan(B, gamma, V, dtype == SPEC_BF16 ? 2 : 4, 1).nseg;
+    if (nseg1 > kMaxSeg) return SPEC_ERR_UNSUPPORTED;
+    // the statistics grid (one workgroup per chunk of every row) must fit in int
+    const long long chunk = (long long)SPECV_RS_WAVES_PER_BLOCK * SPECV_RS_SEGS_PER_WAVE;
+    if ((long long)B * (2 * gamma + 1) * ((nseg1 + chunk - 1) / chunk) > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+  }
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
   const int esize = dtype == SPEC_BF16 ? 2 : 4;
   const int vec = pick_vec(V, esize, reinterpret_cast<uintptr_t>(target_logits),
