@@ -198,3 +198,54 @@ def test_scale_shared_over_heads_is_caught(monkeypatch):
 
     monkeypatch.setattr(Qn, "quantize_rows", per_position)
     _assert_pin_fails(TQ.test_error_bound_and_granularity)
+
+
+# ---- the model oracle ------------------------------------------------------
+
+from oracle import model as MO  # noqa: E402
+from tests import test_oracle_model as TM  # noqa: E402
+
+
+def test_model_pins_hold_unmutated():
+    TM.test_layer_norm_matches_torch()
+    TM.test_gelu_matches_torch_tanh_form()
+    TM.test_model_attention_matches_attention_oracle()
+    TM.test_value_path_and_head_layout_closed_form()
+
+
+def test_wrong_layer_norm_eps_is_caught(monkeypatch):
+    monkeypatch.setattr(MO, "LN_EPS", 1e-3)
+    _assert_pin_fails(TM.test_layer_norm_matches_torch)
+
+
+def test_erf_gelu_is_caught(monkeypatch):
+    from math import erf
+
+    monkeypatch.setattr(MO, "gelu", lambda x: 0.5 * x * (1 + np.vectorize(erf)(x / np.sqrt(2.0))))
+    _assert_pin_fails(TM.test_gelu_matches_torch_tanh_form)
+
+
+def test_unscaled_model_attention_is_caught(monkeypatch):
+    def unscaled(q, K, V, p0):
+        out = np.zeros_like(q)
+        for i in range(q.shape[1]):
+            m = p0 + i + 1
+            s = np.einsum("hd,hkd->hk", q[:, i], K[:, :m])
+            out[:, i] = np.einsum("hk,hkd->hd", MO.softmax(s), V[:, :m])
+        return out
+
+    monkeypatch.setattr(MO, "_attend", unscaled)
+    _assert_pin_fails(TM.test_model_attention_matches_attention_oracle)
+
+
+def test_model_attention_seeing_the_next_key_is_caught(monkeypatch):
+    def peeks(q, K, V, p0):
+        out = np.zeros_like(q)
+        for i in range(q.shape[1]):
+            m = min(p0 + i + 2, K.shape[1])
+            s = np.einsum("hd,hkd->hk", q[:, i], K[:, :m]) / np.sqrt(q.shape[2])
+            out[:, i] = np.einsum("hk,hkd->hd", MO.softmax(s), V[:, :m])
+        return out
+
+    monkeypatch.setattr(MO, "_attend", peeks)
+    _assert_pin_fails(TM.test_model_attention_matches_attention_oracle)

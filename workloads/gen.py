@@ -215,3 +215,39 @@ def attention_inputs_int8(cfg: Config, rep: int = 0, B=None, max_T=None, lens=No
         out[f"{name}_cache"] = codes
         out[f"{name}_scale"] = (np.exp(0.1 * r.standard_normal((B, Hkv, T))) * (2.7 / 127)).astype(np.float16)
     return out
+
+
+# ---------------------------------------------------------------------------
+# the verify forward of a decoder model (random weights)
+# ---------------------------------------------------------------------------
+
+
+def model_params(shapes, seed: int):
+    """Random fp32 weights for a packed parameter layout.
+
+    ``shapes`` is the ordered (name, shape) list of the layout.  Matrices are
+    N(0, 1/rows); LayerNorm gains (names ending in ``_g``) 1 + N(0, 0.1^2);
+    every other vector N(0, 0.1^2).  Stream 5 of ``default_rng([seed, 5])``.
+    """
+    r = np.random.default_rng([int(seed), 5])
+    parts = []
+    for name, shape in shapes:
+        if len(shape) == 2:
+            a = r.standard_normal(shape) / np.sqrt(shape[0])
+        elif name.endswith("_g"):
+            a = 1.0 + 0.1 * r.standard_normal(shape)
+        else:
+            a = 0.1 * r.standard_normal(shape)
+        parts.append(a.astype(np.float32).ravel())
+    return np.concatenate(parts)
+
+
+def forward_inputs(V: int, L: int, H: int, D: int, B: int, n: int, lens_range, max_T: int, seed: int):
+    """Tokens [B, n] uniform over the vocabulary, cache lengths [B] uniform in
+    ``lens_range`` (inclusive), and an fp32 cache [L, 2, B, H, max_T, D] of
+    N(0, 1) entries (stream 6 of ``default_rng([seed, 6])``)."""
+    r = np.random.default_rng([int(seed), 6])
+    tokens = r.integers(0, V, size=(B, n)).astype(np.int32)
+    lens = r.integers(lens_range[0], lens_range[1] + 1, size=B).astype(np.int32)
+    kv = r.standard_normal((L, 2, B, H, max_T, D)).astype(np.float32)
+    return {"tokens": tokens, "lens": lens, "kv": kv}
