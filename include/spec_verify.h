@@ -252,6 +252,73 @@ spec_status_t spec_reject_sample(const void* target_logits, const void* draft_lo
  * Errors: SPEC_ERR_ARG for null pointers, B < 1 or n_q < 1. */
 spec_status_t spec_kv_truncate(int32_t* cache_len, const int32_t* n_accepted, int B, int n_q, hipStream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* Verify forward of a GPT-2-type decoder                                     */
+/* ------------------------------------------------------------------------- */
+
+/* Shape of a decoder-only model as in [P2] section
+ * numpyで小さなTransformerを自作する: pre-LayerNorm blocks, learned token and
+ * position embeddings, GELU MLP of width 4C; head dimension D = C / H.  The
+ * section's parameter counts (513,600 for V=96 C=96 L=4 H=4 T=512; 61,968 for
+ * the draft V=96 C=48 L=1 H=2 T=512) fix the parameter set below. */
+typedef struct {
+  int V; /* vocabulary */
+  int C; /* width (C % H == 0) */
+  int L; /* layers */
+  int H; /* heads */
+  int T; /* positions: rows of the position embedding */
+} spec_model_t;
+
+/* Floats in the packed fp32 parameter array of `model` (0 for an invalid
+ * shape).  The array holds, in this order and each row-major:
+ *   wte [V][C], wpe [T][C],
+ *   per layer: ln1_g [C], ln1_b [C], wqkv [C][3C], wo [C][C], ln2_g [C],
+ *              ln2_b [C], w1 [C][4C], b1 [4C], w2 [4C][C], b2 [C],
+ *   lnf_g [C], lnf_b [C], wout [C][V].
+ * wqkv's columns are q, then k, then v; within each third, head h owns the
+ * columns [h D, (h+1) D). */
+size_t spec_model_param_count(const spec_model_t* model);
+
+size_t spec_verify_forward_workspace_size(const spec_model_t* model, int B, int n, int max_len_hint);
+
+/* Logits of the n new tokens of each of B sequences, appending their K/V to
+ * every layer's cache: the cached forward of [P2] section
+ * numpyで小さなTransformerを自作する (for the verify call, the n = gamma+1
+ * tokens [last committed token] + drafts, [P2] section 投機的デコーディングとは).
+ * For sequence b with p0 = cache_len[b]:
+ *   x_i = wte[tokens[b][i]] + wpe[p0 + i]
+ *   per layer: h = LN1(x); q, k, v = h wqkv (split in thirds, then by head);
+ *     the K/V rows go to positions [p0, p0+n) of the layer's cache; new row i
+ *     attends to positions [0, p0+i] with scores scaled by 1/sqrt(D);
+ *     x += (heads concatenated) wo; x += gelu(LN2(x) w1 + b1) w2 + b2
+ *   logits = LNf(x) wout
+ * LayerNorm: (x - mean) / sqrt(var + 1e-5) * g + b over C (population
+ * variance); gelu(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  All
+ * arithmetic is fp32 (the attention as spec_verify_attention with SPEC_F32).
+ *
+ *   model      host, the model's shape; the head dimension C/H must be one
+ *              spec_verify_attention supports for SPEC_F32 (24, 32, 64, 128)
+ *   params     device, spec_model_param_count(model) floats (layout above)
+ *   tokens     device, [B][n] int32; a token outside [0, V) gives NaN logits
+ *              for its sequence's affected rows
+ *   cache_len  device, [B] int32, p0 of each sequence; not modified (commit
+ *              the accepted length with spec_kv_truncate)
+ *   kv_cache   device, [L][2][B][H][max_T][D] float (layer, K then V,
+ *              sequence, head, position, dim); rows [p0, p0+n) of every
+ *              layer are written, rows below p0 are read, others untouched
+ *   logits     device out, [B][n][V] float
+ *   n          new tokens per sequence, 1..16
+ *   max_len_hint  host upper bound on max_b cache_len[b]
+ *   workspace  device, >= spec_verify_forward_workspace_size(...) bytes,
+ *              256-byte aligned
+ * Errors: SPEC_ERR_ARG for an invalid shape, null pointers, non-positive
+ * sizes, a small or unaligned workspace; SPEC_ERR_OVERFLOW when
+ * max_len_hint + n exceeds max_T or T; SPEC_ERR_UNSUPPORTED for a head
+ * dimension the attention does not support, n > 16, or widths above 128. */
+spec_status_t spec_verify_forward(const spec_model_t* model, const float* params, const int32_t* tokens,
+                                  const int32_t* cache_len, float* kv_cache, int max_T, float* logits, int B, int n,
+                                  int max_len_hint, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,8 @@ with ctypes (see include/spec_verify.h for the contract of each):
   spec_reject_sample     modified rejection sampling over the vocabulary
                          (greedy verification at temperature 0)
   spec_kv_truncate       length reset after the round
+  spec_verify_forward    the cached verify forward of a GPT-2-type decoder
+                         (embeddings, blocks with the verify attention, logits)
 
 PyTorch supplies device memory and streams; all arithmetic runs in the HIP
 kernels.  Importing this package does not load the library; the first call
@@ -19,14 +21,18 @@ from ._lib import (  # noqa: F401
     EXPORTED,
     LIB_PATH,
     SpecError,
+    SpecModel,
     Workspace,
     load,
+    model_param_count,
+    model_param_layout,
     reject_sample_workspace_size,
     spec_kv_truncate,
     spec_reject_sample,
     spec_verify_attention,
     spec_verify_attention_int8,
     spec_verify_attention_paged,
+    spec_verify_forward,
     verify_attention_workspace_size,
     version,
 )

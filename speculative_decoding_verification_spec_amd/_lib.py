@@ -31,7 +31,17 @@ EXPORTED = (
     "spec_reject_sample_workspace_size",
     "spec_reject_sample",
     "spec_kv_truncate",
+    "spec_model_param_count",
+    "spec_verify_forward_workspace_size",
+    "spec_verify_forward",
 )
+
+
+class SpecModel(ctypes.Structure):
+    """spec_model_t: the shape of a GPT-2-type decoder (MLP width 4C)."""
+
+    _fields_ = [("V", ctypes.c_int), ("C", ctypes.c_int), ("L", ctypes.c_int), ("H", ctypes.c_int),
+                ("T", ctypes.c_int)]
 
 
 class SpecError(RuntimeError):
@@ -75,6 +85,13 @@ def load(path=LIB_PATH):
     L.spec_reject_sample.argtypes = [vp] * 4 + [c_int] * 3 + [c_float, c_int] + [vp] * 5 + [c_size, vp]
     L.spec_kv_truncate.restype = c_int
     L.spec_kv_truncate.argtypes = [vp, vp, c_int, c_int, vp]
+    pm = ctypes.POINTER(SpecModel)
+    L.spec_model_param_count.restype = c_size
+    L.spec_model_param_count.argtypes = [pm]
+    L.spec_verify_forward_workspace_size.restype = c_size
+    L.spec_verify_forward_workspace_size.argtypes = [pm, c_int, c_int, c_int]
+    L.spec_verify_forward.restype = c_int
+    L.spec_verify_forward.argtypes = [pm, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, vp, c_size, vp]
     _lib = L
     return L
 
@@ -308,3 +325,64 @@ def spec_kv_truncate(cache_len, n_accepted, n_q, stream=None):
     _need(n_accepted, "n_accepted", torch.int32, (B,))
     _check("spec_kv_truncate", L.spec_kv_truncate(_ptr(cache_len), _ptr(n_accepted), B, int(n_q), _stream(stream)))
     return cache_len
+
+
+def _model(model):
+    if isinstance(model, SpecModel):
+        return model
+    if isinstance(model, dict):
+        return SpecModel(model["V"], model["C"], model["L"], model["H"], model["T"])
+    V, C, L, H, T = (getattr(model, k) for k in ("V", "C", "L", "H", "T"))
+    return SpecModel(V, C, L, H, T)
+
+
+def model_param_layout(model):
+    """(name, shape) of every parameter in the packed array, in order (the
+    layout documented with spec_model_param_count)."""
+    m = _model(model)
+    C, F, V, T = m.C, 4 * m.C, m.V, m.T
+    out = [("wte", (V, C)), ("wpe", (T, C))]
+    for l in range(m.L):
+        out += [(f"{l}.ln1_g", (C,)), (f"{l}.ln1_b", (C,)), (f"{l}.wqkv", (C, 3 * C)), (f"{l}.wo", (C, C)),
+                (f"{l}.ln2_g", (C,)), (f"{l}.ln2_b", (C,)), (f"{l}.w1", (C, F)), (f"{l}.b1", (F,)),
+                (f"{l}.w2", (F, C)), (f"{l}.b2", (C,))]
+    out += [("lnf_g", (C,)), ("lnf_b", (C,)), ("wout", (C, V))]
+    return out
+
+
+def model_param_count(model):
+    """Floats in the packed parameter array (the library's count)."""
+    m = _model(model)
+    return int(load().spec_model_param_count(ctypes.byref(m)))
+
+
+def spec_verify_forward(model, params, tokens, cache_len, kv_cache, max_len_hint, logits=None, workspace=None,
+                        stream=None):
+    """Cached verify forward; returns ``logits`` [B, n, V] (fp32).
+
+    params: [param_count] float32; tokens: [B, n] int32; cache_len: [B] int32
+    (not modified); kv_cache: [L, 2, B, H, max_T, D] float32 (rows
+    [cache_len[b], cache_len[b] + n) of every layer are written).
+    """
+    Lb = load()
+    m = _model(model)
+    _need(params, "params", torch.float32, (model_param_count(m),))
+    _need(tokens, "tokens", torch.int32)
+    B, n = tokens.shape
+    _need(cache_len, "cache_len", torch.int32, (B,))
+    _need(kv_cache, "kv_cache", torch.float32)
+    if kv_cache.dim() != 6 or tuple(kv_cache.shape[:4]) != (m.L, 2, B, m.H) or kv_cache.shape[5] != m.C // m.H:
+        raise ValueError(f"kv_cache has shape {tuple(kv_cache.shape)}, expected ({m.L}, 2, {B}, {m.H}, max_T, "
+                         f"{m.C // max(m.H, 1)})")
+    max_T = kv_cache.shape[4]
+    if logits is None:
+        logits = torch.empty((B, n, m.V), dtype=torch.float32, device=tokens.device)
+    _need(logits, "logits", torch.float32, (B, n, m.V))
+    nbytes = Lb.spec_verify_forward_workspace_size(ctypes.byref(m), B, n, int(max_len_hint))
+    if nbytes == 0:
+        raise SpecError("spec_verify_forward_workspace_size", SPEC_ERR_UNSUPPORTED, "no valid size")
+    ws = _workspace(workspace, "fwd", nbytes, tokens.device)
+    st = Lb.spec_verify_forward(ctypes.byref(m), _ptr(params), _ptr(tokens), _ptr(cache_len), _ptr(kv_cache), max_T,
+                                _ptr(logits), B, n, int(max_len_hint), _ptr(ws), ws.numel(), _stream(stream))
+    _check("spec_verify_forward", st)
+    return logits

@@ -1,0 +1,380 @@
+// The verify forward of a GPT-2-type decoder (gfx950, fp32).
+//
+// [P2] "LLM推論の高速化｜KVキャッシュと投機的デコーディングを自作で実測" section
+// numpyで小さなTransformerを自作する: the cached forward takes the n new tokens
+// of a sequence, adds token and position embeddings (positions p0 .. p0+n-1,
+// p0 = the cache length) and runs pre-LayerNorm blocks -- fused q/k/v
+// projection, the K/V append and causal attention over the cache, the output
+// projection and residual, a second LayerNorm and a GELU MLP with residual --
+// then a final LayerNorm and the vocabulary projection.  The same section's
+// parameter counts (513,600 for the 4-layer width-96 model, 61,968 for the
+// 1-layer width-48 draft) fix MLP width 4C, biases on the MLP only.  The
+// listing leaves LayerNorm and GELU undefined: GPT-2's readings are taken
+// (population variance, eps 1e-5; GELU in its tanh form).
+//
+// Per layer, for the M = B*n new rows:
+//   gemm<LN, QKV split>    h = LN1(x); q | k_new | v_new = h wqkv, written
+//                          head-major ([B][H][n][D]) for the attention
+//   spec_verify_attention  appends k_new, v_new at [p0, p0+n) of the layer's
+//                          cache and attends (the library's fp32 kernels)
+//   gemm<heads in, resid>  x += O wo, reading O [B][H][n][D] as [M][C]
+//   gemm<LN, bias, GELU>   u = gelu(LN2(x) w1 + b1)
+//   gemm<bias, resid>      x += u w2 + b2
+// then gemm<LN> logits = LNf(x) wout.  At the pages' sizes every matrix is a
+// few hundred by a few hundred: each product is one small launch, bound by
+// launch latency rather than by FLOPs or bytes, so the products are plain
+// LDS-staged fp32 FMA tiles (exact fp32 products, no conversion) rather than
+// matrix-core tiles.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "spec_common.h"
+#include "spec_verify.h"
+
+namespace specv {
+
+constexpr float kLnEps = 1e-5f;
+
+// Offsets (in floats) of the parameters in the packed array, in the order
+// wte, wpe, per layer (ln1_g, ln1_b, wqkv, wo, ln2_g, ln2_b, w1, b1, w2, b2),
+// lnf_g, lnf_b, wout.
+struct ModelLayout {
+  int V, C, L, H, T, F, D;
+  size_t wte, wpe, lnf_g, lnf_b, wout, total;
+  size_t layer0, layer_stride;  // first layer's ln1_g; floats per layer
+  // offsets inside a layer
+  size_t ln1_g, ln1_b, wqkv, wo, ln2_g, ln2_b, w1, b1, w2, b2;
+};
+
+static bool model_layout(const spec_model_t* m, ModelLayout* o) {
+  if (!m || m->V < 1 || m->C < 1 || m->L < 1 || m->H < 1 || m->T < 1 || m->C % m->H != 0) return false;
+  ModelLayout l{};
+  l.V = m->V;
+  l.C = m->C;
+  l.L = m->L;
+  l.H = m->H;
+  l.T = m->T;
+  l.F = 4 * m->C;
+  l.D = m->C / m->H;
+  const size_t C = l.C, F = l.F, V = l.V, T = l.T;
+  size_t off = 0;
+  l.wte = off;
+  off += V * C;
+  l.wpe = off;
+  off += T * C;
+  l.layer0 = off;
+  size_t in = 0;
+  l.ln1_g = in;
+  in += C;
+  l.ln1_b = in;
+  in += C;
+  l.wqkv = in;
+  in += 3 * C * C;
+  l.wo = in;
+  in += C * C;
+  l.ln2_g = in;
+  in += C;
+  l.ln2_b = in;
+  in += C;
+  l.w1 = in;
+  in += C * F;
+  l.b1 = in;
+  in += F;
+  l.w2 = in;
+  in += F * C;
+  l.b2 = in;
+  in += C;
+  l.layer_stride = in;
+  off += in * (size_t)l.L;
+  l.lnf_g = off;
+  off += C;
+  l.lnf_b = off;
+  off += C;
+  l.wout = off;
+  off += C * V;
+  l.total = off;
+  *o = l;
+  return true;
+}
+
+// x[b n + i][:] = wte[tok[b][i]][:] + wpe[lens[b] + i][:]; an out-of-range
+// token or position writes NaN rows (which then reach the logits).
+__global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wte, const float* __restrict__ wpe,
+                                                    const int32_t* __restrict__ tok,
+                                                    const int32_t* __restrict__ lens, float* __restrict__ x, int n,
+                                                    int C, int V, int T) {
+  const int row = blockIdx.x;
+  const int b = row / n, i = row - b * n;
+  const int t = tok[row];
+  const long pos = (long)lens[b] + i;
+  const bool ok = t >= 0 && t < V && pos >= 0 && pos < T;
+  for (int c = threadIdx.x; c < C; c += blockDim.x)
+    x[(size_t)row * C + c] = ok ? wte[(size_t)t * C + c] + wpe[(size_t)pos * C + c] : __builtin_nanf("");
+}
+
+enum { A_ROWS = 0, A_HEADS = 1 };    // A: token-major [M][K], or head-major [B][H][n][D] read as [M][C]
+enum { O_ROWS = 0, O_QKV = 1 };      // out: token-major [M][N], or q | k | v head-major
+constexpr int kBM = 32, kBN = 64;    // output tile; 256 threads, 8 rows x 1 column each
+
+struct GemmArgs {
+  const float* A;      // A_ROWS: [M][K]; A_HEADS: [B][H][n][D] with K = H*D
+  const float* W;      // [K][N]
+  const float* ln_g;   // LN gain / bias over K (LN only)
+  const float* ln_b;
+  const float* bias;   // [N] (BIAS only)
+  float* out;          // O_ROWS: [M][N] (RESID: also the addend, updated in place)
+  float* q;            // O_QKV: three [B][H][n][D] outputs, N = 3 H D
+  float* kn;
+  float* vn;
+  int M, N, K, n, H, D;
+};
+
+__device__ __forceinline__ float gelu_tanh(float v) {
+  const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);  // sqrt(2/pi) (v + 0.044715 v^3)
+  return 0.5f * v * (1.f + tanhf(u));
+}
+
+// out tile [m0, m0+32) x [n0, n0+64): the 32 A rows (LayerNorm-ed when LN)
+// are staged in LDS whole (K floats each); each wave owns 8 rows, each lane
+// one column, and streams W's row k for every k (64 consecutive floats per
+// wave: coalesced, and W stays in L2 across the row tiles).
+template <int AMODE, int OMODE, bool LN, bool BIAS, bool GELU, bool RESID>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  extern __shared__ float As[];  // [kBM][K]
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int K = g.K;
+
+  // stage the A rows
+  for (int e = threadIdx.x; e < kBM * K; e += blockDim.x) {
+    const int r = e / K, k = e - r * K;
+    const int m = m0 + r;
+    float a = 0.f;
+    if (m < g.M) {
+      if constexpr (AMODE == A_ROWS) {
+        a = g.A[(size_t)m * K + k];
+      } else {
+        const int b = m / g.n, i = m - b * g.n, h = k / g.D, d = k - h * g.D;
+        a = g.A[(((size_t)b * g.H + h) * g.n + i) * g.D + d];
+      }
+    }
+    As[r * K + k] = a;
+  }
+  __syncthreads();
+  if constexpr (LN) {
+    // each wave normalises its 8 rows: mean, then the variance about it
+    for (int r = wave * 8; r < wave * 8 + 8; ++r) {
+      float s = 0.f;
+      for (int k = lane; k < K; k += kWave) s += As[r * K + k];
+      const float mu = wave_sum(s) / (float)K;
+      float v = 0.f;
+      for (int k = lane; k < K; k += kWave) {
+        const float d = As[r * K + k] - mu;
+        v += d * d;
+      }
+      const float rstd = 1.f / sqrtf(wave_sum(v) / (float)K + kLnEps);
+      for (int k = lane; k < K; k += kWave) As[r * K + k] = (As[r * K + k] - mu) * rstd * g.ln_g[k] + g.ln_b[k];
+    }
+    __syncthreads();
+  }
+
+  const int col = n0 + lane;
+  const bool col_ok = col < g.N;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const float* Ar = As + wave * 8 * K;
+  for (int k = 0; k < K; ++k) {
+    const float w = col_ok ? g.W[(size_t)k * g.N + col] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = fmaf(Ar[j * K + k], w, acc[j]);
+  }
+  if (!col_ok) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = m0 + wave * 8 + j;
+    if (m >= g.M) break;
+    float v = acc[j];
+    if constexpr (BIAS) v += g.bias[col];
+    if constexpr (GELU) v = gelu_tanh(v);
+    if constexpr (OMODE == O_ROWS) {
+      float* o = g.out + (size_t)m * g.N + col;
+      *o = RESID ? *o + v : v;
+    } else {
+      const int C = g.H * g.D;
+      const int part = col / C, c = col - part * C, h = c / g.D, d = c - h * g.D;
+      const int b = m / g.n, i = m - b * g.n;
+      float* dst = part == 0 ? g.q : (part == 1 ? g.kn : g.vn);
+      dst[(((size_t)b * g.H + h) * g.n + i) * g.D + d] = v;
+    }
+  }
+}
+
+template <int AMODE, int OMODE, bool LN, bool BIAS, bool GELU, bool RESID>
+static hipError_t gemm(const GemmArgs& g, hipStream_t s) {
+  const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
+  hipLaunchKernelGGL((gemm_kernel<AMODE, OMODE, LN, BIAS, GELU, RESID>), grid, dim3(256),
+                     sizeof(float) * kBM * g.K, s, g);
+  return hipGetLastError();
+}
+
+struct FwdPlan {
+  size_t off_x, off_q, off_k, off_v, off_o, off_u, off_attn, attn_bytes, total;
+};
+
+static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static bool fwd_plan(const ModelLayout& l, int B, int n, int hint, FwdPlan* p) {
+  const size_t M = (size_t)B * n;
+  const size_t ab = spec_verify_attention_workspace_size(B, l.H, l.H, n, l.D, hint, SPEC_F32);
+  if (ab == 0) return false;
+  FwdPlan f{};
+  size_t off = 0;
+  f.off_x = off;
+  off = align256(off + sizeof(float) * M * l.C);
+  f.off_q = off;
+  off = align256(off + sizeof(float) * M * l.C);
+  f.off_k = off;
+  off = align256(off + sizeof(float) * M * l.C);
+  f.off_v = off;
+  off = align256(off + sizeof(float) * M * l.C);
+  f.off_o = off;
+  off = align256(off + sizeof(float) * M * l.C);
+  f.off_u = off;
+  off = align256(off + sizeof(float) * M * l.F);
+  f.off_attn = off;
+  f.attn_bytes = ab;
+  off = align256(off + ab);
+  f.total = off;
+  *p = f;
+  return true;
+}
+
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" size_t spec_model_param_count(const spec_model_t* model) {
+  ModelLayout l;
+  return model_layout(model, &l) ? l.total : 0;
+}
+
+extern "C" size_t spec_verify_forward_workspace_size(const spec_model_t* model, int B, int n, int max_len_hint) {
+  ModelLayout l;
+  FwdPlan p;
+  if (!model_layout(model, &l) || B < 1 || n < 1 || max_len_hint < 0) return 0;
+  if (!fwd_plan(l, B, n, max_len_hint, &p)) return 0;
+  return p.total;
+}
+
+extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const float* params, const int32_t* tokens,
+                                             const int32_t* cache_len, float* kv_cache, int max_T, float* logits,
+                                             int B, int n, int max_len_hint, void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+  ModelLayout l;
+  if (!model_layout(model, &l)) return SPEC_ERR_ARG;
+  if (!params || !tokens || !cache_len || !kv_cache || !logits || !workspace) return SPEC_ERR_ARG;
+  if (B < 1 || n < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
+  if ((long)max_len_hint + n > (long)max_T || (long)max_len_hint + n > (long)l.T) return SPEC_ERR_OVERFLOW;
+  // the staged A rows of one product tile must fit in LDS
+  if ((size_t)kBM * std::max(l.C, l.F) * sizeof(float) > 64 * 1024) return SPEC_ERR_UNSUPPORTED;
+  FwdPlan p;
+  if (!fwd_plan(l, B, n, max_len_hint, &p)) return SPEC_ERR_UNSUPPORTED;
+  if (workspace_bytes < p.total) return SPEC_ERR_ARG;
+  if ((long)B * n * std::max(std::max(l.C, l.F), l.V) >= 0x7fffffffL) return SPEC_ERR_UNSUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  float* x = reinterpret_cast<float*>(ws + p.off_x);
+  float* q = reinterpret_cast<float*>(ws + p.off_q);
+  float* kn = reinterpret_cast<float*>(ws + p.off_k);
+  float* vn = reinterpret_cast<float*>(ws + p.off_v);
+  float* o = reinterpret_cast<float*>(ws + p.off_o);
+  float* u = reinterpret_cast<float*>(ws + p.off_u);
+  void* aws = ws + p.off_attn;
+  const int M = B * n;
+  const size_t plane = (size_t)B * l.H * max_T * l.D;  // one layer's K (or V) cache
+
+  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)M), dim3(std::min(256, ((l.C + 63) / 64) * 64)), 0, stream,
+                     params + l.wte, params + l.wpe, tokens, cache_len, x, n, l.C, l.V, l.T);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
+
+  for (int layer = 0; layer < l.L; ++layer) {
+    const float* P = params + l.layer0 + (size_t)layer * l.layer_stride;
+    GemmArgs g{};
+    g.M = M;
+    g.n = n;
+    g.H = l.H;
+    g.D = l.D;
+
+    // q | k_new | v_new = LN1(x) wqkv
+    g.A = x;
+    g.K = l.C;
+    g.N = 3 * l.C;
+    g.W = P + l.wqkv;
+    g.ln_g = P + l.ln1_g;
+    g.ln_b = P + l.ln1_b;
+    g.q = q;
+    g.kn = kn;
+    g.vn = vn;
+    if (gemm<A_ROWS, O_QKV, true, false, false, false>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+
+    // append + causal attention over the layer's cache
+    float* kc = kv_cache + (size_t)(2 * layer) * plane;
+    float* vc = kv_cache + (size_t)(2 * layer + 1) * plane;
+    const spec_status_t st = spec_verify_attention(q, kn, vn, kc, vc, cache_len, o, B, l.H, l.H, n, l.D, max_T,
+                                                   max_len_hint, 1.f / sqrtf((float)l.D), SPEC_F32, aws,
+                                                   p.attn_bytes, stream);
+    if (st != SPEC_OK) return st;
+
+    // x += O wo
+    g = GemmArgs{};
+    g.M = M;
+    g.n = n;
+    g.H = l.H;
+    g.D = l.D;
+    g.A = o;
+    g.K = l.C;
+    g.N = l.C;
+    g.W = P + l.wo;
+    g.out = x;
+    if (gemm<A_HEADS, O_ROWS, false, false, false, true>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+
+    // u = gelu(LN2(x) w1 + b1)
+    g.A = x;
+    g.K = l.C;
+    g.N = l.F;
+    g.W = P + l.w1;
+    g.ln_g = P + l.ln2_g;
+    g.ln_b = P + l.ln2_b;
+    g.bias = P + l.b1;
+    g.out = u;
+    if (gemm<A_ROWS, O_ROWS, true, true, true, false>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+
+    // x += u w2 + b2
+    g.A = u;
+    g.K = l.F;
+    g.N = l.C;
+    g.W = P + l.w2;
+    g.bias = P + l.b2;
+    g.out = x;
+    if (gemm<A_ROWS, O_ROWS, false, true, false, true>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+  }
+
+  // logits = LNf(x) wout
+  GemmArgs g{};
+  g.M = M;
+  g.n = n;
+  g.H = l.H;
+  g.D = l.D;
+  g.A = x;
+  g.K = l.C;
+  g.N = l.V;
+  g.W = params + l.wout;
+  g.ln_g = params + l.lnf_g;
+  g.ln_b = params + l.lnf_b;
+  g.out = logits;
+  if (gemm<A_ROWS, O_ROWS, true, false, false, false>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+  return SPEC_OK;
+}

@@ -88,3 +88,40 @@ def test_argument_checks_reject_before_launch():
     # truncate
     assert L.spec_kv_truncate(null, fake, 4, 5, null) == 1
     assert L.spec_kv_truncate(fake, fake, 0, 5, null) == 1
+
+
+def test_model_layout_and_counts():
+    """The library's packed-parameter count matches its documented layout, the
+    model oracle's layout, and the pages' printed counts."""
+    _ensure_built()
+    from oracle import model as M
+
+    for cfg, want in ((M.TARGET, 513_600), (M.DRAFT, 61_968)):
+        assert sv.model_param_count(cfg) == want
+        assert sv.model_param_layout(cfg) == M.param_shapes(cfg)
+    L = _lib.load()
+    assert L.spec_model_param_count(None) == 0
+    bad = _lib.SpecModel(96, 50, 1, 4, 512)  # C % H != 0
+    assert L.spec_model_param_count(ctypes.byref(bad)) == 0
+    m = _lib.SpecModel(96, 96, 4, 4, 512)
+    assert L.spec_verify_forward_workspace_size(ctypes.byref(m), 64, 5, 384) > 0
+    assert L.spec_verify_forward_workspace_size(ctypes.byref(m), 64, 17, 384) == 0  # n > 16
+    assert L.spec_verify_forward_workspace_size(ctypes.byref(bad), 64, 5, 384) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="covered with device buffers by the GPU tests")
+def test_forward_argument_checks_reject_before_launch():
+    _ensure_built()
+    L = _lib.load()
+    fake = ctypes.c_void_p(4096)
+    null = ctypes.c_void_p(0)
+    ws = ctypes.c_void_p(1 << 20)
+    m = _lib.SpecModel(96, 96, 4, 4, 512)
+    need = L.spec_verify_forward_workspace_size(ctypes.byref(m), 2, 5, 100)
+    f = L.spec_verify_forward
+    assert f(None, fake, fake, fake, fake, 512, fake, 2, 5, 100, ws, need, null) == 1  # no model
+    assert f(ctypes.byref(m), null, fake, fake, fake, 512, fake, 2, 5, 100, ws, need, null) == 1  # null params
+    assert f(ctypes.byref(m), fake, fake, fake, fake, 512, fake, 2, 5, 100, ws, need - 1, null) == 1  # small ws
+    assert f(ctypes.byref(m), fake, fake, fake, fake, 104, fake, 2, 5, 100, ws, need, null) == 2  # 100 + 5 > 104
+    assert f(ctypes.byref(m), fake, fake, fake, fake, 1024, fake, 2, 5, 510, ws, 1 << 30, null) == 2  # > T
+    assert f(ctypes.byref(m), fake, fake, fake, fake, 512, fake, 2, 17, 100, ws, 1 << 30, null) == 3  # n > 16
