@@ -29,6 +29,8 @@ Modules:
   truncate   -- the KV length reset after verification
   model      -- the verify forward of the pages' GPT-2-type decoder (cached,
                 and the uncached full-sequence forward it must agree with)
+  round      -- one speculative round of a draft and a target model: draft
+                proposals, one verify call, the draw, both cache truncations
   formulas   -- closed forms: acceptance rate, expected committed tokens,
                 speed-up estimate, KV-cache bytes
   bf16       -- exact decoding of bfloat16 bit patterns to fp64
@@ -39,4 +41,4 @@ Nothing is "parity unpinned" except the mapping of decisions that fall inside
 the 1e-6 threshold band (those draws are counted, not compared).
 """
 
-from . import attention, bf16, formulas, greedy, model, paged, quant, sampler, truncate  # noqa: F401
+from . import attention, bf16, formulas, greedy, model, paged, quant, round, sampler, truncate  # noqa: F401

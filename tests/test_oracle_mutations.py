@@ -249,3 +249,38 @@ def test_model_attention_seeing_the_next_key_is_caught(monkeypatch):
 
     monkeypatch.setattr(MO, "_attend", peeks)
     _assert_pin_fails(TM.test_model_attention_matches_attention_oracle)
+
+
+# ---- the round oracle ------------------------------------------------------
+
+from oracle import round as RO  # noqa: E402
+from tests import test_oracle_round as TR  # noqa: E402
+
+
+def test_round_pins_hold_unmutated():
+    TR.test_draft_equal_to_target_accepts_everything()
+    TR.test_truncated_caches_hold_the_committed_prefix(1.0)
+
+
+def test_draft_cache_kept_at_full_length_is_caught(monkeypatch):
+    """Cutting the draft cache to len - 1 even when it lacks the last proposal."""
+    real = RO.propose
+
+    def lying(*a, **k):
+        xs, zs, dlen, m = real(*a, **k)
+        return xs, zs, dlen + 1, m
+
+    monkeypatch.setattr(RO, "propose", lying)
+    _assert_pin_fails(TR.test_draft_equal_to_target_accepts_everything)
+
+
+def test_target_cache_cut_one_short_is_caught(monkeypatch):
+    real = RO.speculative_round
+
+    def short(flat_t, cfg_t, flat_d, cfg_d, state, *a):
+        res = real(flat_t, cfg_t, flat_d, cfg_d, state, *a)
+        state["tlen"] -= 1
+        return res
+
+    monkeypatch.setattr(RO, "speculative_round", short)
+    _assert_pin_fails(lambda: TR.test_truncated_caches_hold_the_committed_prefix(1.0))
