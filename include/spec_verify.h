@@ -319,6 +319,62 @@ spec_status_t spec_verify_forward(const spec_model_t* model, const float* params
                                   const int32_t* cache_len, float* kv_cache, int max_T, float* logits, int B, int n,
                                   int max_len_hint, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* One speculative round: draft proposals, verify, draw, commit               */
+/* ------------------------------------------------------------------------- */
+
+size_t spec_speculative_round_workspace_size(const spec_model_t* target, const spec_model_t* draft, int B,
+                                             int gamma, int max_len_hint);
+
+/* One round of speculative decoding for B sequences, all on `stream`
+ * ([P2] section 投機的デコーディングとは: the round's listing and flowchart):
+ *   1. the draft proposes gamma tokens: its first call runs over the last two
+ *      committed tokens (positions L-2, L-1), then one call per proposal;
+ *      proposal j is the inverse-CDF draw of softmax(z_j / T) at
+ *      u_draft[b][j] (the smallest index whose prefix of the weights exceeds
+ *      u times their sum), or argmax z_j at T = 0;
+ *   2. the target runs once over [last committed token] + the proposals
+ *      (spec_verify_forward, n = gamma + 1);
+ *   3. spec_reject_sample decides n_accepted and the emitted tokens from the
+ *      target's and the draft's logits and u_verify (greedy at T = 0);
+ *   4. the n + 1 emitted tokens are appended to seq[b]; seq_len, target_len
+ *      and draft_len each grow by n + 1 (the pages' truncate of both caches).
+ * State on entry, for each sequence with L = seq_len[b] committed tokens:
+ * target_len[b] = L - 1 (the target cache holds seq[b][0 .. L-2]) and
+ * draft_len[b] = L - 2 (the draft cache holds at least seq[b][0 .. L-3]);
+ * every call leaves this so.  Start a sequence by prefilling both caches
+ * (spec_verify_forward over the prompt, 16 tokens per call).
+ *
+ *   target, draft   host, model shapes with the same V; params as for
+ *                   spec_verify_forward
+ *   seq             device, [B][max_len] int32 committed tokens, in/out
+ *   seq_len         device, [B] int32 L >= 2, in/out
+ *   target_kv, draft_kv  device, [L][2][B][H][max_T][D] caches of each model
+ *   target_len, draft_len  device, [B] int32, in/out (see above)
+ *   u_draft         device, [B][gamma] double in [0, 1) (NULL at T = 0)
+ *   u_verify        device, [B][gamma+1] double in [0, 1), as for
+ *                   spec_reject_sample (NULL at T = 0)
+ *   max_len_hint    host upper bound on max_b seq_len[b] (>= 2)
+ *   n_accepted      device out, [B]: as spec_reject_sample's; -1 also when a
+ *                   sequence's tokens would not fit in max_len (nothing is
+ *                   committed for it)
+ *   out_tokens      device out, [B][gamma+1]: the emitted tokens, then -1
+ *   workspace       device, >= spec_speculative_round_workspace_size(...)
+ *                   bytes, 256-byte aligned
+ * Errors: SPEC_ERR_ARG for null pointers, different vocabularies, a bad
+ * shape, T < 0, max_len_hint < 2 or a small workspace; SPEC_ERR_OVERFLOW when
+ * max_len_hint + gamma + 1 exceeds max_len, max_len_hint + gamma exceeds the
+ * target's max_T or T, or max_len_hint + gamma - 1 the draft's;
+ * SPEC_ERR_UNSUPPORTED for gamma > 15 or what spec_verify_forward or
+ * spec_reject_sample does not support. */
+spec_status_t spec_speculative_round(const spec_model_t* target, const float* target_params,
+                                     const spec_model_t* draft, const float* draft_params, int32_t* seq,
+                                     int32_t* seq_len, int max_len, float* target_kv, int32_t* target_len,
+                                     int target_max_T, float* draft_kv, int32_t* draft_len, int draft_max_T,
+                                     const double* u_draft, const double* u_verify, int B, int gamma,
+                                     float temperature, int max_len_hint, int32_t* n_accepted, int32_t* out_tokens,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,8 @@ with ctypes (see include/spec_verify.h for the contract of each):
   spec_kv_truncate       length reset after the round
   spec_verify_forward    the cached verify forward of a GPT-2-type decoder
                          (embeddings, blocks with the verify attention, logits)
+  spec_speculative_round one whole round on the device: draft proposals, the
+                         target's verify forward, the sampler, the commit
 
 PyTorch supplies device memory and streams; all arithmetic runs in the HIP
 kernels.  Importing this package does not load the library; the first call
@@ -29,6 +31,7 @@ from ._lib import (  # noqa: F401
     reject_sample_workspace_size,
     spec_kv_truncate,
     spec_reject_sample,
+    spec_speculative_round,
     spec_verify_attention,
     spec_verify_attention_int8,
     spec_verify_attention_paged,

@@ -34,6 +34,8 @@ EXPORTED = (
     "spec_model_param_count",
     "spec_verify_forward_workspace_size",
     "spec_verify_forward",
+    "spec_speculative_round_workspace_size",
+    "spec_speculative_round",
 )
 
 
@@ -92,6 +94,11 @@ def load(path=LIB_PATH):
     L.spec_verify_forward_workspace_size.argtypes = [pm, c_int, c_int, c_int]
     L.spec_verify_forward.restype = c_int
     L.spec_verify_forward.argtypes = [pm, vp, vp, vp, vp, c_int, vp, c_int, c_int, c_int, vp, c_size, vp]
+    L.spec_speculative_round_workspace_size.restype = c_size
+    L.spec_speculative_round_workspace_size.argtypes = [pm, pm, c_int, c_int, c_int]
+    L.spec_speculative_round.restype = c_int
+    L.spec_speculative_round.argtypes = ([pm, vp, pm, vp, vp, vp, c_int, vp, vp, c_int, vp, vp, c_int, vp, vp,
+                                          c_int, c_int, c_float, c_int, vp, vp, vp, c_size, vp])
     _lib = L
     return L
 
@@ -386,3 +393,52 @@ def spec_verify_forward(model, params, tokens, cache_len, kv_cache, max_len_hint
                                 _ptr(logits), B, n, int(max_len_hint), _ptr(ws), ws.numel(), _stream(stream))
     _check("spec_verify_forward", st)
     return logits
+
+
+def spec_speculative_round(target, target_params, draft, draft_params, seq, seq_len, target_kv, target_len, draft_kv,
+                           draft_len, u_draft, u_verify, temperature, max_len_hint, n_accepted=None, out_tokens=None,
+                           workspace=None, stream=None):
+    """One speculative round on the device; returns (n_accepted [B], out_tokens [B, gamma+1]).
+
+    seq [B, max_len] / seq_len [B] (committed tokens), target_len [B] = L - 1,
+    draft_len [B] = L - 2 and both caches are updated in place.  u_draft
+    [B, gamma] and u_verify [B, gamma+1] float64 (None at temperature 0; then
+    gamma comes from n_accepted/out_tokens or u shapes must be given).
+    """
+    Lb = load()
+    mt, md = _model(target), _model(draft)
+    _need(seq, "seq", torch.int32)
+    B, max_len = seq.shape
+    greedy = float(temperature) == 0.0
+    if u_verify is not None:
+        gamma = u_verify.shape[1] - 1
+    elif out_tokens is not None:
+        gamma = out_tokens.shape[1] - 1
+    else:
+        raise ValueError("give u_verify or out_tokens so that gamma is known")
+    _need(target_params, "target_params", torch.float32, (model_param_count(mt),))
+    _need(draft_params, "draft_params", torch.float32, (model_param_count(md),))
+    for t, name in ((seq_len, "seq_len"), (target_len, "target_len"), (draft_len, "draft_len")):
+        _need(t, name, torch.int32, (B,))
+    _need(target_kv, "target_kv", torch.float32)
+    _need(draft_kv, "draft_kv", torch.float32)
+    if not greedy:
+        _need(u_draft, "u_draft", torch.float64, (B, gamma))
+        _need(u_verify, "u_verify", torch.float64, (B, gamma + 1))
+    if n_accepted is None:
+        n_accepted = torch.empty(B, dtype=torch.int32, device=seq.device)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, gamma + 1), dtype=torch.int32, device=seq.device)
+    nbytes = Lb.spec_speculative_round_workspace_size(ctypes.byref(mt), ctypes.byref(md), B, gamma,
+                                                      int(max_len_hint))
+    if nbytes == 0:
+        raise SpecError("spec_speculative_round_workspace_size", SPEC_ERR_UNSUPPORTED, "no valid size")
+    ws = _workspace(workspace, "round", nbytes, seq.device)
+    st = Lb.spec_speculative_round(
+        ctypes.byref(mt), _ptr(target_params), ctypes.byref(md), _ptr(draft_params), _ptr(seq), _ptr(seq_len),
+        max_len, _ptr(target_kv), _ptr(target_len), target_kv.shape[4], _ptr(draft_kv), _ptr(draft_len),
+        draft_kv.shape[4], _ptr(None if greedy else u_draft), _ptr(None if greedy else u_verify), B, gamma,
+        float(temperature), int(max_len_hint), _ptr(n_accepted), _ptr(out_tokens), _ptr(ws), ws.numel(),
+        _stream(stream))
+    _check("spec_speculative_round", st)
+    return n_accepted, out_tokens

@@ -1,0 +1,275 @@
+// One speculative-decoding round of a draft and a target model, on the
+// device (gfx950).
+//
+// [P2] "LLM推論の高速化｜KVキャッシュと投機的デコーディングを自作で実測" section
+// 投機的デコーディングとは (the round's listing and flowchart): the draft
+// proposes gamma tokens, each drawn from its distribution q_j; the target is
+// called once over [last committed token] + proposals; the accept tests, the
+// residual or bonus draw and the emitted tokens are spec_reject_sample's; the
+// sequence grows by the accepted proposals and the drawn token, the target
+// cache is cut back to base + 1 + n and the draft cache likewise.
+//
+// Draft side.  A sequence of L committed tokens keeps the draft cache at
+// L - 2 tokens on entry: the draft's first call of a round runs over the last
+// two committed tokens at positions L-2, L-1 (re-running the second-to-last
+// one, whose K/V the cache may or may not hold: when every proposal of the
+// previous round was accepted, the draft never ran the last of them), then one
+// call per proposal.  Every sequence thus feeds the same number of tokens per
+// call, and after the round the draft cache is cut to L' - 2 with the same
+// length reset as the target's (+1 + n).  Each proposal is the inverse-CDF
+// draw of softmax(z / T) at its uniform (the convention of the final draw);
+// at T = 0 it is the argmax.
+//
+// Kernels here only move tokens and lengths and make the draft's draws; the
+// forwards are spec_verify_forward, the verification spec_reject_sample.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "spec_common.h"
+#include "spec_verify.h"
+
+namespace specv {
+
+// Inputs of draft call j for every sequence: j = 0: the tokens at positions
+// L-2 and L-1 from position draft_len = L-2; j > 0: proposal j-1 at position
+// L-1+j.
+__global__ __launch_bounds__(256) void round_draft_inputs(const int32_t* __restrict__ seq,
+                                                         const int32_t* __restrict__ seq_len, int max_len,
+                                                         const int32_t* __restrict__ draft_len,
+                                                         const int32_t* __restrict__ xs, int gamma, int j, int B,
+                                                         int32_t* __restrict__ tok, int32_t* __restrict__ pos) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int L = seq_len[b];
+  const bool ok = L >= 2 && L <= max_len;  // else token -1: NaN logits for this sequence only
+  if (j == 0) {
+    tok[2 * b] = ok ? seq[(size_t)b * max_len + L - 2] : -1;
+    tok[2 * b + 1] = ok ? seq[(size_t)b * max_len + L - 1] : -1;
+    pos[b] = draft_len[b];
+  } else {
+    tok[b] = xs[(size_t)b * gamma + j - 1];
+    pos[b] = draft_len[b] + j + 1;
+  }
+}
+
+// Ordered key of a logit for the argmax: a larger value gives a larger key,
+// -0 equals +0, a NaN is above every number.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  if (v != v) return 0xffffffffu;
+  const uint32_t u = (v == 0.f) ? 0u : __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave per sequence: copies the last logit row of draft call j into
+// draft_logits[b][j] and draws proposal j: at T > 0 the smallest index whose
+// fp64 prefix of w = 2^((z - max) c) exceeds u * sum(w) (the last positive
+// weight if rounding leaves none); at T = 0 the first index of the largest
+// logit.
+__global__ __launch_bounds__(64) void round_draft_draw(const float* __restrict__ step_logits, int rows, int V,
+                                                      const double* __restrict__ u_draft, int gamma, int j,
+                                                      float c32, int greedy, float* __restrict__ draft_logits,
+                                                      int32_t* __restrict__ xs) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* z = step_logits + ((size_t)b * rows + rows - 1) * V;
+  float* zd = draft_logits + ((size_t)b * gamma + j) * V;
+  float m = neg_inf_f();
+  uint64_t best = 0;
+  for (int k = lane; k < V; k += kWave) {
+    const float v = z[k];
+    zd[k] = v;
+    m = fmaxf(m, v);
+    const uint64_t w = ((uint64_t)logit_key(v) << 32) | (uint32_t)~(uint32_t)k;
+    best = w > best ? w : best;
+  }
+  if (greedy) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)best, o, kWave), hi = __shfl_xor((uint32_t)(best >> 32), o, kWave);
+      const uint64_t w = ((uint64_t)hi << 32) | lo;
+      best = w > best ? w : best;
+    }
+    if (lane == 0) xs[(size_t)b * gamma + j] = (int32_t)~(uint32_t)best;
+    return;
+  }
+  m = wave_max(m);
+  double s = 0.0;
+  for (int k = lane; k < V; k += kWave) s += (double)exp2_fast((z[k] - m) * c32);
+  const double target = u_draft[(size_t)b * gamma + j] * wave_sum(s);
+  double carry = 0.0;
+  int t = -1, last = -1;
+  for (int c0 = 0; c0 < V && t < 0; c0 += kWave) {
+    const int k = c0 + lane;
+    const float w = k < V ? exp2_fast((z[k] - m) * c32) : 0.f;
+    const double incl = carry + wave_inclusive_scan((double)w, lane);
+    const uint64_t hit = __ballot(k < V && incl > target);
+    const uint64_t pos = __ballot(k < V && w > 0.f);
+    if (pos) last = c0 + 63 - __builtin_clzll(pos);
+    if (hit) t = c0 + __ffsll((long long)hit) - 1;
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  if (t < 0) t = last < 0 ? 0 : last;
+  if (lane == 0) xs[(size_t)b * gamma + j] = t;
+}
+
+// Tokens of the target's verify call: [last committed token] + proposals.
+__global__ __launch_bounds__(256) void round_verify_inputs(const int32_t* __restrict__ seq,
+                                                          const int32_t* __restrict__ seq_len, int max_len,
+                                                          const int32_t* __restrict__ xs, int gamma, int B,
+                                                          int32_t* __restrict__ vtok) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= B * (gamma + 1)) return;
+  const int b = e / (gamma + 1), i = e - b * (gamma + 1);
+  const int L = seq_len[b];
+  if (i == 0)
+    vtok[e] = (L >= 1 && L <= max_len) ? seq[(size_t)b * max_len + L - 1] : -1;
+  else
+    vtok[e] = xs[(size_t)b * gamma + i - 1];
+}
+
+// Commit: append the n+1 emitted tokens, and advance the sequence, target
+// and draft lengths by n + 1.  A negative n (a sampler error) changes
+// nothing; so does a sequence whose tokens would not fit, and it is reported
+// as n_accepted = -1.
+__global__ __launch_bounds__(256) void round_commit(int32_t* __restrict__ seq, int32_t* __restrict__ seq_len,
+                                                   int max_len, int32_t* __restrict__ target_len,
+                                                   int32_t* __restrict__ draft_len,
+                                                   int32_t* __restrict__ n_accepted,
+                                                   const int32_t* __restrict__ out_tokens, int gamma, int B) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  const int n = n_accepted[b];
+  if (n < 0 || n > gamma) return;
+  const int L = seq_len[b];
+  if (L < 0 || (long)L + n + 1 > (long)max_len) {
+    n_accepted[b] = -1;
+    return;
+  }
+  for (int i = 0; i <= n; ++i) seq[(size_t)b * max_len + L + i] = out_tokens[(size_t)b * (gamma + 1) + i];
+  seq_len[b] = L + n + 1;
+  target_len[b] += n + 1;
+  draft_len[b] += n + 1;
+}
+
+struct RoundPlan {
+  size_t off_fwd, fwd_bytes, off_rs, rs_bytes, off_tok, off_pos, off_step, off_dl, off_xs, off_vtok, off_tl, total;
+};
+
+static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+static bool round_plan(const spec_model_t* t, const spec_model_t* d, int B, int gamma, int hint, RoundPlan* p) {
+  const int V = t->V;
+  size_t fwd = spec_verify_forward_workspace_size(t, B, gamma + 1, std::max(0, hint - 1));
+  const size_t f0 = spec_verify_forward_workspace_size(d, B, 2, std::max(0, hint - 2));
+  const size_t f1 = spec_verify_forward_workspace_size(d, B, 1, hint + gamma - 2);
+  if (fwd == 0 || f0 == 0 || f1 == 0) return false;
+  fwd = std::max(fwd, std::max(f0, f1));
+  const size_t rs = spec_reject_sample_workspace_size(B, gamma, V, SPEC_F32);
+  if (rs == 0) return false;
+  RoundPlan r{};
+  size_t off = 0;
+  r.off_fwd = off;
+  r.fwd_bytes = fwd;
+  off = align256(off + fwd);
+  r.off_rs = off;
+  r.rs_bytes = rs;
+  off = align256(off + rs);
+  r.off_tok = off;
+  off = align256(off + sizeof(int32_t) * 2 * (size_t)B);
+  r.off_pos = off;
+  off = align256(off + sizeof(int32_t) * (size_t)B);
+  r.off_step = off;
+  off = align256(off + sizeof(float) * 2 * (size_t)B * V);
+  r.off_dl = off;
+  off = align256(off + sizeof(float) * (size_t)B * gamma * V);
+  r.off_xs = off;
+  off = align256(off + sizeof(int32_t) * (size_t)B * gamma);
+  r.off_vtok = off;
+  off = align256(off + sizeof(int32_t) * (size_t)B * (gamma + 1));
+  r.off_tl = off;
+  off = align256(off + sizeof(float) * (size_t)B * (gamma + 1) * V);
+  r.total = off;
+  *p = r;
+  return true;
+}
+
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" size_t spec_speculative_round_workspace_size(const spec_model_t* target, const spec_model_t* draft, int B,
+                                                        int gamma, int max_len_hint) {
+  if (!target || !draft || B < 1 || gamma < 1 || gamma > 15 || max_len_hint < 2) return 0;
+  if (target->V != draft->V) return 0;
+  RoundPlan p;
+  return round_plan(target, draft, B, gamma, max_len_hint, &p) ? p.total : 0;
+}
+
+extern "C" spec_status_t spec_speculative_round(
+    const spec_model_t* target, const float* target_params, const spec_model_t* draft, const float* draft_params,
+    int32_t* seq, int32_t* seq_len, int max_len, float* target_kv, int32_t* target_len, int target_max_T,
+    float* draft_kv, int32_t* draft_len, int draft_max_T, const double* u_draft, const double* u_verify, int B,
+    int gamma, float temperature, int max_len_hint, int32_t* n_accepted, int32_t* out_tokens, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (!target || !draft || !target_params || !draft_params || !seq || !seq_len || !target_kv || !target_len ||
+      !draft_kv || !draft_len || !n_accepted || !out_tokens || !workspace)
+    return SPEC_ERR_ARG;
+  const bool greedy = temperature == 0.f;
+  if (!greedy && (!u_draft || !u_verify || !(temperature > 0.f) || !isfinite(temperature))) return SPEC_ERR_ARG;
+  if (B < 1 || gamma < 1 || max_len_hint < 2 || max_len < 1) return SPEC_ERR_ARG;
+  if (target->V != draft->V || spec_model_param_count(target) == 0 || spec_model_param_count(draft) == 0)
+    return SPEC_ERR_ARG;
+  if (gamma > 15) return SPEC_ERR_UNSUPPORTED;  // the verify call runs gamma + 1 <= 16 tokens
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
+  // room for the round: gamma + 1 more tokens, caches and positions
+  if ((long)max_len_hint + gamma + 1 > (long)max_len) return SPEC_ERR_OVERFLOW;
+  if ((long)max_len_hint + gamma > (long)target_max_T || (long)max_len_hint + gamma > (long)target->T)
+    return SPEC_ERR_OVERFLOW;
+  if ((long)max_len_hint + gamma - 1 > (long)draft_max_T || (long)max_len_hint + gamma - 1 > (long)draft->T)
+    return SPEC_ERR_OVERFLOW;
+  RoundPlan p;
+  if (!round_plan(target, draft, B, gamma, max_len_hint, &p)) return SPEC_ERR_UNSUPPORTED;
+  if (workspace_bytes < p.total) return SPEC_ERR_ARG;
+
+  char* ws = static_cast<char*>(workspace);
+  void* fws = ws + p.off_fwd;
+  void* rws = ws + p.off_rs;
+  int32_t* tok = reinterpret_cast<int32_t*>(ws + p.off_tok);
+  int32_t* pos = reinterpret_cast<int32_t*>(ws + p.off_pos);
+  float* step = reinterpret_cast<float*>(ws + p.off_step);
+  float* dlog = reinterpret_cast<float*>(ws + p.off_dl);
+  int32_t* xs = reinterpret_cast<int32_t*>(ws + p.off_xs);
+  int32_t* vtok = reinterpret_cast<int32_t*>(ws + p.off_vtok);
+  float* tlog = reinterpret_cast<float*>(ws + p.off_tl);
+  const int V = target->V;
+  const float c32 = greedy ? 0.f : (float)(1.4426950408889634 / (double)temperature);  // 2^(z c) = e^(z/T)
+  const unsigned gB = (unsigned)((B + 255) / 256);
+
+  for (int j = 0; j < gamma; ++j) {
+    const int n = j == 0 ? 2 : 1;
+    hipLaunchKernelGGL(round_draft_inputs, dim3(gB), dim3(256), 0, stream, seq, seq_len, max_len, draft_len, xs,
+                       gamma, j, B, tok, pos);
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
+    const int hint = j == 0 ? max_len_hint - 2 : max_len_hint + j - 1;
+    spec_status_t st = spec_verify_forward(draft, draft_params, tok, pos, draft_kv, draft_max_T, step, B, n, hint,
+                                           fws, p.fwd_bytes, stream);
+    if (st != SPEC_OK) return st;
+    hipLaunchKernelGGL(round_draft_draw, dim3((unsigned)B), dim3(kWave), 0, stream, step, n, V, u_draft, gamma, j,
+                       c32, greedy ? 1 : 0, dlog, xs);
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL(round_verify_inputs, dim3((unsigned)((B * (gamma + 1) + 255) / 256)), dim3(256), 0, stream, seq,
+                     seq_len, max_len, xs, gamma, B, vtok);
+  if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
+  spec_status_t st = spec_verify_forward(target, target_params, vtok, target_len, target_kv, target_max_T, tlog, B,
+                                         gamma + 1, max_len_hint - 1, fws, p.fwd_bytes, stream);
+  if (st != SPEC_OK) return st;
+  st = spec_reject_sample(tlog, greedy ? nullptr : dlog, xs, greedy ? nullptr : u_verify, B, gamma, V, temperature,
+                          SPEC_F32, n_accepted, out_tokens, nullptr, nullptr, rws, p.rs_bytes, stream);
+  if (st != SPEC_OK) return st;
+  hipLaunchKernelGGL(round_commit, dim3(gB), dim3(256), 0, stream, seq, seq_len, max_len, target_len, draft_len,
+                     n_accepted, out_tokens, gamma, B);
+  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
