@@ -278,7 +278,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c5", choices=sorted(WORKLOADS) + ["model"],
+                    help="a config of the verification step, or 'model': the pages' char models "
+                         "(verify forward and whole speculative rounds, random weights)")
     ap.add_argument("--temperature", type=float, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--paged", type=int, default=0, choices=(0, 16, 32),
@@ -318,6 +320,9 @@ def main():
         __graft_entry__.build()
     sv.load()
     dev = torch.device("cuda:0")
+    if args.workload == "model":
+        model_bench(args, torch, sv, dev)
+        return
     cfg = W.get(WORKLOADS[args.workload])
     T = cfg.temperatures[-1] if args.temperature is None else args.temperature
     print(f"[bench] workload config{cfg.cid} ({cfg.name}) T={T}: generating inputs", file=sys.stderr, flush=True)
@@ -460,6 +465,125 @@ def main():
         res["cpu_baseline"] = cpu_baseline(cfg, att0, smp0, T)
     print(json.dumps(res), flush=True)
 
+
+
+def model_bench(args, torch, sv, dev):
+    """The pages' char models with random weights ([P2] section
+    numpyで小さなTransformerを自作する: target V=96 C=96 L=4 H=4, draft C=48 L=1
+    H=2, 512 positions), B=64 sequences with 384 cached tokens, gamma=4, T=1:
+      * the target's verify forward over gamma+1 tokens (spec_verify_forward);
+      * whole speculative rounds (spec_speculative_round), generated tokens/s,
+        against target-only decoding (one forward of one token per sequence
+        per generated token; its draw is left out, which favours the
+        baseline);
+    all inputs resident on the device.  Random weights make the draft a poor
+    guesser, so the acceptance rate (and the round's gain) is low; the numbers
+    measure the machinery, not a trained draft."""
+    from workloads import gen
+
+    tcfg = dict(V=96, C=96, L=4, H=4, T=512)
+    dcfg = dict(V=96, C=48, L=1, H=2, T=512)
+    B, gamma, prefix, T, max_T = 64, 4, 384, 1.0, 512
+    pt = torch.from_numpy(gen.model_params(sv.model_param_layout(tcfg), 40)).to(dev)
+    pd = torch.from_numpy(gen.model_params(sv.model_param_layout(dcfg), 41)).to(dev)
+    ti = gen.forward_inputs(96, 4, 4, 24, B, gamma + 1, (prefix, prefix), max_T, 42)
+    di = gen.forward_inputs(96, 1, 2, 24, B, 1, (prefix, prefix), max_T, 43)
+    tkv0 = torch.from_numpy(ti["kv"]).to(dev)
+    dkv0 = torch.from_numpy(di["kv"]).to(dev)
+    tok = torch.from_numpy(ti["tokens"]).to(dev)
+    lens = torch.from_numpy(ti["lens"]).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps  # ms
+
+    print("[bench] model: verify forward", file=sys.stderr, flush=True)
+    tkv = tkv0.clone()
+    fwd_ms = timed(lambda: sv.spec_verify_forward(tcfg, pt, tok, lens, tkv, prefix), args.steps, args.warmup)
+    one = tok[:, :1].contiguous()
+    base_ms = timed(lambda: sv.spec_verify_forward(tcfg, pt, one, lens, tkv, prefix), args.steps, args.warmup)
+
+    print("[bench] model: speculative rounds", file=sys.stderr, flush=True)
+    rounds = min(args.steps, (max_T - prefix - gamma - 2) // (gamma + 1))
+    max_len = max_T
+    seq = torch.from_numpy(np.random.default_rng(44).integers(0, 96, size=(B, max_len)).astype(np.int32)).to(dev)
+    r = np.random.default_rng(45)
+    ud = [torch.from_numpy(r.random((B, gamma))).to(dev) for _ in range(rounds + 2)]
+    uv = [torch.from_numpy(r.random((B, gamma + 1))).to(dev) for _ in range(rounds + 2)]
+
+    def fresh():
+        st = {"seq_len": torch.full((B,), prefix, dtype=torch.int32, device=dev),
+              "tlen": torch.full((B,), prefix - 1, dtype=torch.int32, device=dev),
+              "dlen": torch.full((B,), prefix - 2, dtype=torch.int32, device=dev),
+              "tkv": tkv0.clone(), "dkv": dkv0.clone(), "k": 0}
+        return st
+
+    def one_round(st, k):
+        return sv.spec_speculative_round(tcfg, pt, dcfg, pd, seq, st["seq_len"], st["tkv"], st["tlen"], st["dkv"],
+                                         st["dlen"], ud[k], uv[k], T, prefix + k * (gamma + 1))
+
+    st = fresh()
+    one_round(st, 0)  # warm-up round (and library load)
+    torch.cuda.synchronize()
+    st = fresh()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ns = []
+    a.record(stream)
+    for k in range(rounds):
+        n, _ = one_round(st, k)
+        ns.append(n)
+    b.record(stream)
+    torch.cuda.synchronize()
+    round_ms = a.elapsed_time(b) / rounds
+    nacc = torch.stack(ns).cpu().numpy()
+    gen_tokens = int((nacc + 1).sum())
+    tested = np.where(nacc < gamma, nacc + 1, gamma)
+    alpha = float(nacc.sum() / tested.sum())
+    tok_s = gen_tokens / (rounds * round_ms * 1e-3)
+    base_tok_s = B / (base_ms * 1e-3)
+    # verify forward bytes: weights once, every layer's K/V read over prefix + n
+    # rows and the n new rows written, activations ignored
+    n = gamma + 1
+    w_bytes = 4 * sv.model_param_count(tcfg)
+    kv_bytes = 4 * 4 * B * 4 * 24 * 2 * ((prefix + n) + n)
+    fwd_bytes = w_bytes + kv_bytes
+    line = {
+        "metric": "generated tokens/sec (speculative rounds) and verified positions/sec (verify forward)",
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": rounds,
+        "warmup": 1,
+        "ms_per_step": round_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic: random weights, random tokens, N(0,1) cached K/V",
+        "config": {"workload": f"pages' char models (target V=96 C=96 L=4 H=4, draft C=48 L=1 H=2), B={B}, "
+                               f"cached prefix {prefix}, gamma={gamma}, T={T}"},
+        "roofline": {"bound": "hbm", "achieved": fwd_bytes / (fwd_ms * 1e-3) / 1e9, "peak": 8000.0, "unit": "GB/s",
+                     "frac": fwd_bytes / (fwd_ms * 1e-3) / 8e12, "traffic": None,
+                     "kernel": "spec_verify_forward (target, gamma+1 tokens): 26 launches, launch-latency bound",
+                     "algorithmic_bytes": fwd_bytes, "avg_ms": fwd_ms},
+        "parts": {
+            "verify_forward": {"ms": fwd_ms, "positions/s": B * gamma / (fwd_ms * 1e-3)},
+            "target_only_decode": {"ms_per_token_step": base_ms, "tokens/s": base_tok_s},
+            "round": {"ms": round_ms, "tokens/s": tok_s, "speedup_vs_target_only": tok_s / base_tok_s,
+                      "alpha": alpha, "tokens_per_target_call": float((nacc + 1).mean()),
+                      "accepted_per_proposed": float(nacc.sum() / (gamma * nacc.size))},
+        },
+    }
+    print(json.dumps(line))
 
 if __name__ == "__main__":
     main()

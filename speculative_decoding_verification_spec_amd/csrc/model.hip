@@ -117,6 +117,8 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wt
 enum { A_ROWS = 0, A_HEADS = 1 };    // A: token-major [M][K], or head-major [B][H][n][D] read as [M][C]
 enum { O_ROWS = 0, O_QKV = 1 };      // out: token-major [M][N], or q | k | v head-major
 constexpr int kBM = 32, kBN = 64;    // output tile; 256 threads, 8 rows x 1 column each
+constexpr int kKC = 32;              // rows of W per staged chunk
+constexpr int kStage = kKC * kBN / 256;  // elements of a chunk each thread loads
 
 struct GemmArgs {
   const float* A;      // A_ROWS: [M][K]; A_HEADS: [B][H][n][D] with K = H*D
@@ -138,11 +140,12 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 
 // out tile [m0, m0+32) x [n0, n0+64): the 32 A rows (LayerNorm-ed when LN)
 // are staged in LDS whole (K floats each); each wave owns 8 rows, each lane
-// one column, and streams W's row k for every k (64 consecutive floats per
-// wave: coalesced, and W stays in L2 across the row tiles).
+// one column; W comes through LDS in chunks of rows (W stays in L2 across
+// the row tiles).
 template <int AMODE, int OMODE, bool LN, bool BIAS, bool GELU, bool RESID>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   extern __shared__ float As[];  // [kBM][K]
+  __shared__ float Ws[2][kKC][kBN];
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
@@ -181,14 +184,46 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     __syncthreads();
   }
 
+  // W in chunks of kKC rows of the tile's 64 columns, double-buffered in LDS:
+  // each thread loads 8 elements of the next chunk into registers before the
+  // FMAs of the current one, so a chunk's load latency overlaps the work of
+  // the one before (the products are far too small to hide it otherwise).
   const int col = n0 + lane;
   const bool col_ok = col < g.N;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float* Ar = As + wave * 8 * K;
-  for (int k = 0; k < K; ++k) {
-    const float w = col_ok ? g.W[(size_t)k * g.N + col] : 0.f;
+  auto gload = [&](int k0, float (&r)[kStage]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = fmaf(Ar[j * K + k], w, acc[j]);
+    for (int i = 0; i < kStage; ++i) {
+      const int e = threadIdx.x + 256 * i, k = k0 + (e >> 6), c = n0 + (e & 63);
+      r[i] = (k < K && c < g.N) ? g.W[(size_t)k * g.N + c] : 0.f;
+    }
+  };
+  auto sstore = [&](int buf, const float (&r)[kStage]) {
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      Ws[buf][e >> 6][e & 63] = r[i];
+    }
+  };
+  {
+    float r[kStage];
+    gload(0, r);
+    sstore(0, r);
+    __syncthreads();
+    for (int k0 = 0, buf = 0; k0 < K; k0 += kKC, buf ^= 1) {
+      const bool more = k0 + kKC < K;
+      if (more) gload(k0 + kKC, r);
+      const int kn = min(kKC, K - k0);
+#pragma unroll 8
+      for (int kk = 0; kk < kn; ++kk) {
+        const float w = Ws[buf][kk][lane];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = fmaf(Ar[j * K + k0 + kk], w, acc[j]);
+      }
+      if (more) sstore(buf ^ 1, r);
+      __syncthreads();
+    }
   }
   if (!col_ok) return;
 #pragma unroll
@@ -278,8 +313,9 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
   if (B < 1 || n < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
   if ((long)max_len_hint + n > (long)max_T || (long)max_len_hint + n > (long)l.T) return SPEC_ERR_OVERFLOW;
-  // the staged A rows of one product tile must fit in LDS
-  if ((size_t)kBM * std::max(l.C, l.F) * sizeof(float) > 64 * 1024) return SPEC_ERR_UNSUPPORTED;
+  // the staged A rows and W chunks of one product tile must fit in 64 KB of LDS
+  if ((size_t)kBM * std::max(l.C, l.F) * sizeof(float) + sizeof(float) * 2 * kKC * kBN > 64 * 1024)
+    return SPEC_ERR_UNSUPPORTED;
   FwdPlan p;
   if (!fwd_plan(l, B, n, max_len_hint, &p)) return SPEC_ERR_UNSUPPORTED;
   if (workspace_bytes < p.total) return SPEC_ERR_ARG;
