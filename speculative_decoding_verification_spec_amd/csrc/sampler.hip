@@ -12,22 +12,24 @@
 // judging positions past the first rejection changes nothing but wasted work,
 // and the data-parallel pass reads every logit exactly once.
 //
-// Two kernels:
+// Three kernels:
 //   rs_stats   per segment of every target and draft row: max and sum of
 //              exp((z - max)/T) (every logit read once).
-//   rs_tail    workgroup b: merges each row's segments, evaluates p_i(x_i),
-//              q_i(x_i) and the accept tests, finds n; its waves then sum the
+//   rs_resid   per (sequence, group of segments of its decided row): merges
+//              each row's segments, evaluates p_i(x_i), q_i(x_i) and the
+//              accept tests, finds n (every workgroup of the sequence alike;
+//              the first also writes n, p, q and the decision), then sums the
 //              residual weights max(0, p_n - q_n) (or p_gamma for the bonus)
-//              per segment of the decided row into LDS, and one wave locates
-//              the segment where the fp64 prefix sum first exceeds u * total,
-//              re-scans it and writes the emitted tokens.
-// The hand-off between the kernels is the kernel boundary; inside rs_tail all
-// hand-offs are workgroup barriers.  (A hand-off between workgroups inside a
-// kernel would need device-scope release / acquire, which on this chip
-// writes back and invalidates the per-XCD L2.)  Every merge is in fp64 and in
-// a fixed order.  No workspace word is read before this call has written it,
-// so a workspace needs no initialisation and may be shared by calls of any
-// sizes.
+//              over its segments.
+//   rs_draw    per sequence: locates the segment where the fp64 prefix sum
+//              first exceeds u * total, re-scans it and writes the tokens.
+// The hand-offs are kernel boundaries; inside a kernel they are workgroup
+// barriers.  (A hand-off between workgroups inside one kernel costs more on
+// this chip than the pass itself: an agent-scope release or acquire writes
+// back or invalidates a whole per-XCD L2, and same-line atomics from every XCD
+// serialise.)  Every merge is in fp64 and in a fixed order.  No workspace
+// word is read before this call has written it, so a workspace needs no
+// initialisation and may be shared by calls of any sizes.
 #include <math.h>
 #include <stdint.h>
 
