@@ -12,24 +12,28 @@
 // judging positions past the first rejection changes nothing but wasted work,
 // and the data-parallel pass reads every logit exactly once.
 //
-// Three kernels:
+// Two kernels:
 //   rs_stats   per segment of every target and draft row: max and sum of
 //              exp((z - max)/T) (every logit read once).
 //   rs_resid   per (sequence, group of segments of its decided row): merges
 //              each row's segments, evaluates p_i(x_i), q_i(x_i) and the
 //              accept tests, finds n (every workgroup of the sequence alike;
-//              the first also writes n, p, q and the decision), then sums the
-//              residual weights max(0, p_n - q_n) (or p_gamma for the bonus)
-//              over its segments.
-//   rs_draw    per sequence: locates the segment where the fp64 prefix sum
-//              first exceeds u * total, re-scans it and writes the tokens.
-// The hand-offs are kernel boundaries; inside a kernel they are workgroup
-// barriers.  (A hand-off between workgroups inside one kernel costs more on
-// this chip than the pass itself: an agent-scope release or acquire writes
-// back or invalidates a whole per-XCD L2, and same-line atomics from every XCD
-// serialise.)  Every merge is in fp64 and in a fixed order.  No workspace
-// word is read before this call has written it, so a workspace needs no
-// initialisation and may be shared by calls of any sizes.
+//              the first also writes n, p and q), then sums the residual
+//              weights max(0, p_n - q_n) (or p_gamma for the bonus) over its
+//              segments; the last of the sequence's workgroups to finish
+//              locates the segment where the fp64 prefix sum first exceeds
+//              u * total, re-scans it and writes the tokens.
+// The hand-off between the kernels is the kernel boundary.  Inside rs_resid
+// the segment sums pass between a sequence's workgroups through device-scope
+// (write-through) stores, completed before a device-scope counter add, and
+// device-scope loads by the workgroup whose add completes the count: a few
+// workgroups per counter, so the adds do not queue, and nobody waits.  (A
+// fence-based hand-off would cost more than the pass itself on this chip: an
+// agent-scope release or acquire writes back or invalidates a whole per-XCD
+// L2.)  Every merge is in fp64 and in a fixed order.  The counters are zeroed
+// by rs_stats; no other workspace word is read before this call has written
+// it, so a workspace needs no initialisation and may be shared by calls of
+// any sizes.
 #include <math.h>
 #include <stdint.h>
 
@@ -223,11 +227,14 @@ __device__ __forceinline__ void raw_to_f32(const typename RawVec<VEC * sizeof(T)
 // memory-side cache when rs_resid reads the decided row again.
 template <typename T, int VEC, int NIT, int SPW>
 __global__ __launch_bounds__(1024) void rs_stats(const T* __restrict__ tgt, const T* __restrict__ drf, int B, int G,
-                                                 int V, int nseg, int cpr, float c32, RowPart* __restrict__ part) {
+                                                 int V, int nseg, int cpr, float c32, RowPart* __restrict__ part,
+                                                 uint32_t* __restrict__ cnt) {
   constexpr int SEG = kWave * VEC * NIT;
   using Raw = typename RawVec<VEC * sizeof(T)>::type;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (blockIdx.x == 0)  // rs_resid's arrival counters start at zero
+    for (int i = threadIdx.x; i < B; i += blockDim.x) cnt[i] = 0u;
   const int q = blockIdx.x / cpr, c = blockIdx.x - q * cpr;
   const int seg0 = (c * (blockDim.x / kWave) + wave) * SPW;
   if (seg0 >= nseg) return;  // uniform per wave
@@ -307,13 +314,137 @@ __device__ __forceinline__ void lane_weights(const T* __restrict__ rt, const T* 
   }
 }
 
-// The decision of sequence b, as rs_resid hands it to rs_draw.
-struct RsDecision {
-  int n;      // accepted positions; -1 when a draft token was out of range
-  int resid;  // 1: residual draw from max(0, p_n - q_n); 0: bonus draw from p_gamma
-  float Mt, inv_st, Md, inv_sd;
-  int pad[2];
-};
+// Wait until every vector memory access this wave has issued is complete
+// (for device-scope stores: visible to every XCD).
+__device__ __forceinline__ void wait_vm_all() { __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// One segment sum pair (residual, p) through device-scope stores and loads:
+// written by every workgroup of a sequence, read by the one that draws.
+__device__ __forceinline__ void store_segsum(double2* p, double w, double pp) {
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+  __hip_atomic_store(q, (unsigned long long)__double_as_longlong(w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (unsigned long long)__double_as_longlong(pp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_segsum(const double2* p, int half) {
+  const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p) + half;
+  return __longlong_as_double((long long)__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// The draw of sequence b, by every thread of a workgroup (waves beyond the
+// fourth only take the barriers).  Wave 0 takes the fp64 total of the segment
+// sums in a fixed order and the first segment whose prefix exceeds u * total;
+// then four waves re-scan that segment in index order (lane l of wave w holds
+// the E/4 contiguous elements starting at (64 w + l) E/4; the prefix is the
+// segment's base, the totals of the waves before, then the lane scan) and
+// write the emitted tokens.  The segment sums and the re-scan agree to
+// rounding, which only matters for a draw within rounding of a segment
+// boundary -- inside the 1e-6 band.
+template <typename T, int VEC, int NIT>
+__device__ __forceinline__ void draw_tokens(const T* __restrict__ rt, const T* __restrict__ rd,
+                                            const int32_t* __restrict__ xtok, const double* __restrict__ uni,
+                                            int b, int G, int V, int nseg, float c32, int n, bool resid, float Mt,
+                                            float inv_st, float Md, float inv_sd, const double2* __restrict__ sb,
+                                            int32_t* __restrict__ tok_out) {
+  constexpr int E = VEC * NIT;
+  constexpr int SEG = kWave * E;
+  constexpr int E4 = E / 4;
+  static_assert(NIT % 4 == 0, "the re-scan splits a segment over four waves");
+  __shared__ double sh_base, sh_target, sh_wtot[4];
+  __shared__ int sh_kseg, sh_from_last, sh_use_p, sh_hit[4], sh_lastj[4];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  if (wave == 0) {
+    double W = 0.0;
+    for (int c0 = 0; c0 < nseg; c0 += kWave) {
+      const double v = (c0 + lane < nseg) ? load_segsum(sb + c0 + lane, 0) : 0.0;
+      W += __shfl(wave_inclusive_scan(v, lane), kWave - 1, kWave);
+    }
+    const bool use_p = resid && !(W > 0.0);  // zero residual mass: draw from p_n
+    if (use_p) {
+      W = 0.0;
+      for (int c0 = 0; c0 < nseg; c0 += kWave) {
+        const double v = (c0 + lane < nseg) ? load_segsum(sb + c0 + lane, 1) : 0.0;
+        W += __shfl(wave_inclusive_scan(v, lane), kWave - 1, kWave);
+      }
+    }
+    const double target = uni[(size_t)b * (G + 1) + G] * W;
+    int kseg = -1, last_pos = -1;
+    double base = 0.0, carry = 0.0;
+    for (int c0 = 0; c0 < nseg && kseg < 0; c0 += kWave) {
+      const bool in = c0 + lane < nseg;
+      const double v = in ? load_segsum(sb + c0 + lane, use_p ? 1 : 0) : 0.0;
+      const double incl = carry + wave_inclusive_scan(v, lane);
+      const double prev = __shfl_up(incl, 1, kWave);
+      const double excl = (lane == 0) ? carry : prev;
+      const uint64_t hit = __ballot(in && incl > target);
+      const uint64_t pos = __ballot(in && v > 0.0);
+      if (pos) last_pos = c0 + 63 - __builtin_clzll(pos);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        kseg = c0 + l;
+        base = __shfl(excl, l, kWave);
+      }
+      carry = __shfl(incl, kWave - 1, kWave);
+    }
+    const bool from_last = kseg < 0;  // the target reached the total by rounding
+    if (from_last) kseg = last_pos < 0 ? 0 : last_pos;
+    if (lane == 0) {
+      sh_kseg = kseg;
+      sh_from_last = from_last;
+      sh_use_p = use_p;
+      sh_base = base;
+      sh_target = target;
+    }
+  }
+  __syncthreads();
+
+  const int kseg = __builtin_amdgcn_readfirstlane(sh_kseg);
+  const bool from_last = sh_from_last;
+  const double target = sh_target;
+  float w[E4];
+  double incl2 = 0.0;
+  const int j0 = kseg * SEG + (wave * kWave + lane) * E4;
+  if (wave < 4) {
+    lane_weights<T, VEC, NIT / 4>(rt, rd, j0, V, c32, Mt, inv_st, Md, inv_sd, resid && !sh_use_p, w);
+    double l2 = 0.0;
+#pragma unroll
+    for (int k = 0; k < E4; ++k) l2 += (double)w[k];
+    incl2 = wave_inclusive_scan(l2, lane);
+    if (lane == kWave - 1) sh_wtot[wave] = incl2;
+  }
+  __syncthreads();
+  if (wave < 4) {
+    double run = sh_base;
+    for (int q = 0; q < wave; ++q) run += sh_wtot[q];
+    const double prev2 = __shfl_up(incl2, 1, kWave);
+    run += (lane == 0 ? 0.0 : prev2);  // this lane's exclusive prefix
+    int hit_j = 0x7fffffff, last_j = -1;
+#pragma unroll
+    for (int k = 0; k < E4; ++k) {
+      run += (double)w[k];
+      if (w[k] > 0.f) {
+        last_j = j0 + k;
+        if (!from_last && hit_j == 0x7fffffff && run > target) hit_j = j0 + k;
+      }
+    }
+    hit_j = wave_min(hit_j);
+    last_j = wave_max(last_j);
+    if (lane == 0) {
+      sh_hit[wave] = hit_j;
+      sh_lastj[wave] = last_j;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  int t = min(min(sh_hit[0], sh_hit[1]), min(sh_hit[2], sh_hit[3]));
+  if (t == 0x7fffffff) t = max(max(sh_lastj[0], sh_lastj[1]), max(sh_lastj[2], sh_lastj[3]));
+  int32_t* ob = tok_out + (size_t)b * (G + 1);
+  if (lane < n) ob[lane] = xtok[(size_t)b * G + lane];
+  if (lane == n) ob[lane] = t;
+  if (lane > n && lane <= G) ob[lane] = -1;
+}
+
 
 // Merges the segments of every row of sequence b into rowM / rowS (fp64,
 // fixed order).  Waves over rows, two rows at a time; each part is loaded
@@ -371,24 +502,26 @@ __device__ __forceinline__ void merge_rows(const RowPart* __restrict__ pb, int R
 // Grid: x = sequence b, y = group of kResidWaves * spw segments of the
 // decided row; kResidWaves waves, spw segments each.  Every workgroup of b merges b's rows and takes the
 // decision (the same arithmetic in each, so all agree); workgroup y = 0 also
-// writes n_accepted, p_draft, q_draft and the decision record.  Then the
-// workgroup sums the residual weights max(0, p_n - q_n) (or p_gamma for the
-// bonus) and p_n (for the zero-residual fallback) over its segments, every
-// load of them issued before the arithmetic; lane sums in fp64.
+// writes n_accepted, p_draft and q_draft.  Then the workgroup sums the
+// residual weights max(0, p_n - q_n) (or p_gamma for the bonus) and p_n (for
+// the zero-residual fallback) over its segments, every load of them issued
+// before the arithmetic; lane sums in fp64.  The last of b's workgroups to
+// count itself in cnt[b] (zeroed by rs_stats) then draws (draw_tokens).
 constexpr int kResidWaves = 8;
 
 template <typename T, int VEC, int NIT>
 __global__ __launch_bounds__(kResidWaves * kWave) void rs_resid(
     const T* __restrict__ tgt, const T* __restrict__ drf, const int32_t* __restrict__ xtok,
     const double* __restrict__ uni, int G, int V, int nseg, int spw, float c32, double c64,
-    const RowPart* __restrict__ part, double2* __restrict__ segsum, RsDecision* __restrict__ dec, int32_t* __restrict__ n_out,
-    int32_t* __restrict__ tok_out, float* __restrict__ p_out, float* __restrict__ q_out) {
+    const RowPart* __restrict__ part, double2* __restrict__ segsum, uint32_t* __restrict__ cnt,
+    int32_t* __restrict__ n_out, int32_t* __restrict__ tok_out, float* __restrict__ p_out,
+    float* __restrict__ q_out) {
   constexpr int E = VEC * NIT;
   constexpr int SEG = kWave * E;
   using Raw = typename RawVec<VEC * sizeof(T)>::type;
   __shared__ float rowM[64];
   __shared__ double rowS[64];
-  __shared__ int sh_n, sh_valid;
+  __shared__ int sh_n, sh_valid, sh_last;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int R = 2 * G + 1;
@@ -431,16 +564,6 @@ __global__ __launch_bounds__(kResidWaves * kWave) void rs_resid(
     if (lead) {
       if (lane == 0) n_out[b] = bad_mask ? -1 : n;
       if (bad_mask && lane <= G) tok_out[(size_t)b * (G + 1) + lane] = -1;
-      if (lane == 0) {
-        RsDecision d{};
-        d.n = bad_mask ? -1 : n;
-        d.resid = n < G;
-        d.Mt = rowM[n];
-        d.inv_st = (float)(1.0 / rowS[n]);
-        d.Md = n < G ? rowM[G + 1 + n] : 0.f;
-        d.inv_sd = n < G ? (float)(1.0 / rowS[G + 1 + n]) : 1.f;
-        dec[b] = d;
-      }
     }
   }
   __syncthreads();
@@ -461,7 +584,7 @@ __global__ __launch_bounds__(kResidWaves * kWave) void rs_resid(
   // two at a time
   const int s0 = (blockIdx.y * kResidWaves + wave) * spw;
   const int s1 = min(s0 + spw, nseg);
-  for (int seg0 = s0; seg0 < s1; seg0 += 2) {  // uniform per wave; no barrier follows
+  for (int seg0 = s0; seg0 < s1; seg0 += 2) {  // uniform per wave
     Raw at[2][NIT], ad[2][NIT];
 #pragma unroll
     for (int k = 0; k < 2; ++k)
@@ -497,129 +620,20 @@ __global__ __launch_bounds__(kResidWaves * kWave) void rs_resid(
       }
       lw = wave_sum(lw);
       lp = wave_sum(lp);
-      if (lane == 0) segsum[(size_t)b * nseg + seg] = make_double2(lw, lp);
+      if (lane == 0) store_segsum(segsum + (size_t)b * nseg + seg, lw, lp);
     }
   }
+  // The last of b's workgroups to finish draws: its count follows every
+  // other workgroup's completed segment stores (device-scope, write-through).
+  wait_vm_all();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    sh_last = __hip_atomic_fetch_add(cnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.y - 1;
+  __syncthreads();
+  if (!sh_last) return;  // uniform over the workgroup
+  draw_tokens<T, VEC, NIT>(rt, rd, xtok, uni, b, G, V, nseg, c32, n, resid, Mt, inv_st, Md, inv_sd,
+                           segsum + (size_t)b * nseg, tok_out);
 }
-
-// Grid: x = sequence b; four waves.  Wave 0 takes the fp64 total of the
-// segment sums in a fixed order and the first segment whose prefix exceeds
-// u * total; then the four waves re-scan that segment in index order (lane l
-// of wave w holds the E/4 contiguous elements starting at (64 w + l) E/4;
-// the prefix is the segment's base, the totals of the waves before, then the
-// lane scan) and write the emitted tokens.  The segment sums and the re-scan
-// agree to rounding, which only matters for a draw within rounding of a
-// segment boundary -- inside the 1e-6 band.
-template <typename T, int VEC, int NIT>
-__global__ __launch_bounds__(4 * kWave) void rs_draw(const T* __restrict__ tgt, const T* __restrict__ drf,
-                                                    const int32_t* __restrict__ xtok,
-                                                    const double* __restrict__ uni, int G, int V, int nseg,
-                                                    float c32, const double2* __restrict__ segsum,
-                                                    const RsDecision* __restrict__ dec,
-                                                    int32_t* __restrict__ tok_out) {
-  constexpr int E = VEC * NIT;
-  constexpr int SEG = kWave * E;
-  constexpr int E4 = E / 4;
-  static_assert(NIT % 4 == 0, "the re-scan splits a segment over four waves");
-  __shared__ double sh_base, sh_target, sh_wtot[4];
-  __shared__ int sh_kseg, sh_from_last, sh_use_p, sh_hit[4], sh_lastj[4];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int b = blockIdx.x;
-  const RsDecision d = dec[b];
-  if (d.n < 0) return;  // out-of-range draft token: outputs already written
-  const int n = __builtin_amdgcn_readfirstlane(d.n);
-  const bool resid = d.resid != 0;
-  const double2* sb = segsum + (size_t)b * nseg;
-
-  if (wave == 0) {
-    double W = 0.0;
-    for (int c0 = 0; c0 < nseg; c0 += kWave) {
-      const double v = (c0 + lane < nseg) ? sb[c0 + lane].x : 0.0;
-      W += __shfl(wave_inclusive_scan(v, lane), kWave - 1, kWave);
-    }
-    const bool use_p = resid && !(W > 0.0);  // zero residual mass: draw from p_n
-    if (use_p) {
-      W = 0.0;
-      for (int c0 = 0; c0 < nseg; c0 += kWave) {
-        const double v = (c0 + lane < nseg) ? sb[c0 + lane].y : 0.0;
-        W += __shfl(wave_inclusive_scan(v, lane), kWave - 1, kWave);
-      }
-    }
-    const double target = uni[(size_t)b * (G + 1) + G] * W;
-    int kseg = -1, last_pos = -1;
-    double base = 0.0, carry = 0.0;
-    for (int c0 = 0; c0 < nseg && kseg < 0; c0 += kWave) {
-      const bool in = c0 + lane < nseg;
-      const double v = in ? (use_p ? sb[c0 + lane].y : sb[c0 + lane].x) : 0.0;
-      const double incl = carry + wave_inclusive_scan(v, lane);
-      const double prev = __shfl_up(incl, 1, kWave);
-      const double excl = (lane == 0) ? carry : prev;
-      const uint64_t hit = __ballot(in && incl > target);
-      const uint64_t pos = __ballot(in && v > 0.0);
-      if (pos) last_pos = c0 + 63 - __builtin_clzll(pos);
-      if (hit) {
-        const int l = __ffsll((long long)hit) - 1;
-        kseg = c0 + l;
-        base = __shfl(excl, l, kWave);
-      }
-      carry = __shfl(incl, kWave - 1, kWave);
-    }
-    const bool from_last = kseg < 0;  // the target reached the total by rounding
-    if (from_last) kseg = last_pos < 0 ? 0 : last_pos;
-    if (lane == 0) {
-      sh_kseg = kseg;
-      sh_from_last = from_last;
-      sh_use_p = use_p;
-      sh_base = base;
-      sh_target = target;
-    }
-  }
-  __syncthreads();
-
-  const int kseg = __builtin_amdgcn_readfirstlane(sh_kseg);
-  const bool from_last = sh_from_last;
-  const double target = sh_target;
-  const T* rt = tgt + ((size_t)b * (G + 1) + n) * V;
-  const T* rd = drf + ((size_t)b * G + min(n, G - 1)) * V;  // never read unless resid
-  float w[E4];
-  const int j0 = kseg * SEG + (wave * kWave + lane) * E4;
-  lane_weights<T, VEC, NIT / 4>(rt, rd, j0, V, c32, d.Mt, d.inv_st, d.Md, d.inv_sd, resid && !sh_use_p, w);
-  double l2 = 0.0;
-#pragma unroll
-  for (int k = 0; k < E4; ++k) l2 += (double)w[k];
-  const double incl2 = wave_inclusive_scan(l2, lane);
-  if (lane == kWave - 1) sh_wtot[wave] = incl2;
-  __syncthreads();
-  double run = sh_base;
-  for (int q = 0; q < wave; ++q) run += sh_wtot[q];
-  const double prev2 = __shfl_up(incl2, 1, kWave);
-  run += (lane == 0 ? 0.0 : prev2);  // this lane's exclusive prefix
-  int hit_j = 0x7fffffff, last_j = -1;
-#pragma unroll
-  for (int k = 0; k < E4; ++k) {
-    run += (double)w[k];
-    if (w[k] > 0.f) {
-      last_j = j0 + k;
-      if (!from_last && hit_j == 0x7fffffff && run > target) hit_j = j0 + k;
-    }
-  }
-  hit_j = wave_min(hit_j);
-  last_j = wave_max(last_j);
-  if (lane == 0) {
-    sh_hit[wave] = hit_j;
-    sh_lastj[wave] = last_j;
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  int t = min(min(sh_hit[0], sh_hit[1]), min(sh_hit[2], sh_hit[3]));
-  if (t == 0x7fffffff) t = max(max(sh_lastj[0], sh_lastj[1]), max(sh_lastj[2], sh_lastj[3]));
-  int32_t* ob = tok_out + (size_t)b * (G + 1);
-  if (lane < n) ob[lane] = xtok[(size_t)b * G + lane];
-  if (lane == n) ob[lane] = t;
-  if (lane > n && lane <= G) ob[lane] = -1;
-}
-
 
 // ---------------------------------------------------------------------------
 // temperature 0: greedy verification
@@ -777,7 +791,7 @@ static int device_cus() {
 
 struct RsPlan {
   int vec, nit, seg, nseg;
-  size_t off_part1, off_seg, off_dec, total;
+  size_t off_part1, off_seg, off_cnt, total;
 };
 
 static int pick_vec(int V, int esize, uintptr_t a, uintptr_t b) {
@@ -798,8 +812,8 @@ static RsPlan rs_plan(int B, int G, int V, int esize, int vec) {
   const int R = 2 * G + 1;
   p.off_part1 = 0;
   p.off_seg = align256(sizeof(RowPart) * (size_t)B * R * p.nseg);
-  p.off_dec = p.off_seg + align256(sizeof(double2) * (size_t)B * p.nseg);
-  p.total = p.off_dec + align256(sizeof(RsDecision) * (size_t)B);
+  p.off_cnt = p.off_seg + align256(sizeof(double2) * (size_t)B * p.nseg);
+  p.total = p.off_cnt + align256(sizeof(uint32_t) * (size_t)B);
   return p;
 }
 
@@ -813,24 +827,20 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
   const int waves_row = (pl.nseg + SPW - 1) / SPW;
   const int wpb = std::min(SPECV_RS_WAVES_PER_BLOCK, waves_row);  // waves per block
   const int cpr = (waves_row + wpb - 1) / wpb;  // workgroups per row
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
   hipLaunchKernelGGL((rs_stats<T, VEC, NIT, SPW>), dim3((unsigned)((long)B * R * cpr)), dim3(kWave * wpb), 0, stream,
-                     (const T*)tgt, (const T*)drf, B, G, V, pl.nseg, cpr, c32, part1);
+                     (const T*)tgt, (const T*)drf, B, G, V, pl.nseg, cpr, c32, part1, cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   double2* segsum = reinterpret_cast<double2*>(ws + pl.off_seg);
-  RsDecision* dec = reinterpret_cast<RsDecision*>(ws + pl.off_dec);
   // About two residual workgroups per CU, at least two segments per wave.
   const int ngrp = std::max(1, std::min((2 * device_cus() + B - 1) / B, (pl.nseg + 2 * kResidWaves - 1) / (2 * kResidWaves)));
   int spw = (pl.nseg + ngrp * kResidWaves - 1) / (ngrp * kResidWaves);
   spw += spw & 1;
   const int ny = (pl.nseg + spw * kResidWaves - 1) / (spw * kResidWaves);
   hipLaunchKernelGGL((rs_resid<T, VEC, NIT>), dim3((unsigned)B, (unsigned)ny), dim3(kWave * kResidWaves), 0, stream,
-                     (const T*)tgt, (const T*)drf, x, u, G, V, pl.nseg, spw, c32, c64, part1, segsum, dec, n_out,
+                     (const T*)tgt, (const T*)drf, x, u, G, V, pl.nseg, spw, c32, c64, part1, segsum, cnt, n_out,
                      tok_out, p_out, q_out);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rs_draw<T, VEC, NIT>), dim3((unsigned)B), dim3(kWave * 4), 0, stream, (const T*)tgt,
-                     (const T*)drf, x, u, G, V, pl.nseg, c32, segsum, dec, tok_out);
   return hipGetLastError();
 }
 
