@@ -1534,9 +1534,11 @@ static int stream_workgroups(K kernel, int NW) {
   if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kernel)) == hipSuccess && fa.numRegs > 0)
     per_simd = 512 / ((fa.numRegs + 7) / 8 * 8);
   // Up to 4 waves a workgroup takes one slot on each of NW SIMDs; a larger
-  // one takes ceil(NW / 4) slots on every SIMD (measured: 5-, 6- and 8-wave
-  // workgroups fit 2 per CU whatever their registers and LDS).
-  const int by_slots = NW <= 4 ? 4 * per_simd / NW : per_simd / ((NW + 3) / 4);
+  // one takes ceil(NW / 4) slots on every SIMD, and never more than 2 fit
+  // (measured: 5-, 6- and 8-wave workgroups fit 2 per CU whatever their
+  // registers and LDS; a build that used fewer registers and launched 3 per
+  // CU left a third of them waiting for a slot).
+  const int by_slots = NW <= 4 ? 4 * per_simd / NW : std::min(2, per_simd / ((NW + 3) / 4));
   int k = std::max(1, std::min(occ, by_slots));
   const int P = std::min(kStreamMaxWG, cus * k);
   if (slot) slot->store(P, std::memory_order_relaxed);
