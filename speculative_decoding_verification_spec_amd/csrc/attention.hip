@@ -946,6 +946,15 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
     for (int s = 0; s < DS; ++s)
       qf[s] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg) : bf16x8{};
   }
+  // The tiles are widened as k' = q + 128 (0..255, exact in bf16), so a score
+  // is s_k (k' . q_row - 128 sum_d q_row[d]): 128 times this row's sum of the
+  // same bf16 query values, subtracted after the product.
+  float qsum = 0.f;
+#pragma unroll
+  for (int s = 0; s < DS; ++s)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qsum += (float)qf[s][i];
+  const float q128 = 128.f * group_sum(qsum);
 
   issue_block(k0, IC<0>{});
   if constexpr (NST > 2) {
@@ -964,6 +973,7 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
 
   const float c = a.qk_scale;
   float mrow = neg_inf_f(), lsum = 0.f;
+  float wsum = 0.f;  // this lane's share of sum_key P' (the bf16 values fed to PV), for the V offset
   f32x4 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1006,31 +1016,58 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
     block_barrier();
     if (j + NST - 1 < nblk) issue_block(kb + (NST - 1) * KB, IC<(decltype(S)::value + NST - 1) % NST>{});
 
-    // Widen the int8 tiles of block j into cvk / cvv (8 values per item).
-    // One loop per tile: each reads a single LDS object, so the compiler can
-    // tell the reads from the copies in flight into other stages and does not
-    // wait for them.
+    // Widen the int8 tiles of block j into cvk / cvv (8 values per item) as
+    // k' = q + 128: flipping each byte's top bit makes it the unsigned q + 128,
+    // which converts to fp32 in one instruction per byte, and an integer of
+    // 0..255 is exact in bf16 (the top half of its fp32 bits).  The offsets
+    // come back out per row: -128 sum_d q in the scores, -128 sum_key P' in
+    // the output.  Each thread issues the reads of all its items of both
+    // tiles before converting any (one LDS round trip, not one per item);
+    // each read names a single LDS object, so the compiler can tell the
+    // reads from the copies in flight into other stages and does not wait
+    // for them.
     {
-      constexpr int PER = KB * D / 8;  // 8-value items per tile
-      auto widen = [&](const int8_t* tile, uint16_t* cv, bool is_v) {
-        for (int it = tid; it < PER; it += 64 * NW) {
-          const int row = it / (D / 8), sl = it % (D / 8);
-          const uint2 w = *reinterpret_cast<const uint2*>(tile + row * D + 8 * sl);
-          uint32_t o[4];
+      constexpr int PER = KB * D / 8;            // 8-value items per tile
+      constexpr int NT = 64 * NW;                // threads
+      constexpr int IPT = (PER + NT - 1) / NT;   // items per thread per tile
+      constexpr int SPR = D / 8;                 // items per row
+      static_assert((SPR & (SPR - 1)) == 0, "row of a power-of-two number of items");
+      // Item i covers bytes [8 i, 8 i + 8) of a tile: row i / SPR, slot i % SPR.
+      // Every read of both tiles is issued before the first conversion.
+      auto widen8 = [&](uint2 w) {
+        uint32_t o[4];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint32_t word = k < 2 ? w.x : w.y;
-            const int sh = 16 * (k & 1);
-            const float lo = (float)(int)(int8_t)(uint8_t)(word >> sh);
-            const float hi = (float)(int)(int8_t)(uint8_t)(word >> (sh + 8));
-            o[k] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);  // exact in bf16
-          }
-          const int slot = is_v ? LY::vslot(row, sl) : LY::kslot(row, sl);
-          *reinterpret_cast<uint4*>(cv + row * D + 8 * slot) = make_uint4(o[0], o[1], o[2], o[3]);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t word = (k < 2 ? w.x : w.y) ^ 0x80808080u;
+          const int sh = 16 * (k & 1);
+          const float lo = (float)((word >> sh) & 0xffu);
+          const float hi = (float)((word >> (sh + 8)) & 0xffu);
+          o[k] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
         }
+        return make_uint4(o[0], o[1], o[2], o[3]);
       };
-      widen(qkbuf(S), cvk, false);
-      widen(qvbuf(S), cvv, true);
+      const int8_t* tk = qkbuf(S);
+      const int8_t* tv = qvbuf(S);
+      uint2 wk[IPT], wv[IPT];
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        const unsigned it = (unsigned)tid + (unsigned)(k * NT);
+        if (it < (unsigned)PER) wk[k] = *reinterpret_cast<const uint2*>(tk + 8 * it);
+      }
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        const unsigned it = (unsigned)tid + (unsigned)(k * NT);
+        if (it < (unsigned)PER) wv[k] = *reinterpret_cast<const uint2*>(tv + 8 * it);
+      }
+#pragma unroll
+      for (int k = 0; k < IPT; ++k) {
+        const unsigned it = (unsigned)tid + (unsigned)(k * NT);
+        if (it < (unsigned)PER) {
+          const int row = (int)(it / SPR), sl = (int)(it % SPR);
+          *reinterpret_cast<uint4*>(cvk + row * D + 8 * LY::kslot(row, sl)) = widen8(wk[k]);
+          *reinterpret_cast<uint4*>(cvv + row * D + 8 * LY::vslot(row, sl)) = widen8(wv[k]);
+        }
+      }
     }
     float skey[8], svkey[8];
     key_scales(S, kb, skey, svkey);
@@ -1046,7 +1083,7 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sc[4 * kt + jj] = acc[jj] * skey[4 * kt + jj];
+      for (int jj = 0; jj < 4; ++jj) sc[4 * kt + jj] = (acc[jj] - q128) * skey[4 * kt + jj];
     }
     float alpha;
     {
@@ -1081,6 +1118,12 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
     bf16x8 pf;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) pf[jj] = (__bf16)(sc[jj] * svkey[jj]);
+    {
+      float pw = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) pw += (float)pf[jj];
+      wsum = fmaf(wsum, alpha, pw);
+    }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       s16x4 v2[2];
@@ -1120,6 +1163,14 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
   }
 
   const float lt = group_sum(lsum);
+  {
+    // the V offset: O = sum P' v' - 128 sum P'
+    const float v128 = 128.f * group_sum(wsum);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) oacc[dt][jj] -= v128;
+  }
   const int row = 16 * wave + lr;
   if (whole) {
     if (valid) {
