@@ -254,6 +254,9 @@ __device__ __forceinline__ float group_sum(float v) {
 #ifndef SPECV_ATTN_WPE
 #define SPECV_ATTN_WPE 4
 #endif
+#ifndef SPECV_I8_STAGES
+#define SPECV_I8_STAGES 2  // raw int8 stages: with two bf16 buffers, 2 keep the kernel in 128 VGPRs
+#endif
 #ifndef SPECV_STREAM_WPE
 #define SPECV_STREAM_WPE 4
 #endif
@@ -829,7 +832,8 @@ __global__ __launch_bounds__(256) void quant_new_rows(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) int8_t qk1[KB * D], qv1[KB * D]; \
   __shared__ __attribute__((aligned(1024))) int8_t qk2[NST > 2 ? KB * D : 16], qv2[NST > 2 ? KB * D : 16]; \
   __shared__ __attribute__((aligned(16))) uint16_t sc0[64], sc1[64], sc2[64]; \
-  __shared__ __attribute__((aligned(1024))) uint16_t cvk[KB * D], cvv[KB * D]; \
+  __shared__ __attribute__((aligned(1024))) uint16_t cvk[2 * KB * D], cvv[2 * KB * D]; \
+  __shared__ __attribute__((aligned(16))) uint16_t scv[128]; \
   __shared__ float nsk[16], nsv[16]; \
   auto qkbuf = [&](auto S) -> int8_t* { \
     if constexpr (decltype(S)::value == 0) return qk0; \
@@ -859,7 +863,7 @@ __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builti
 // quantised new rows from the workspace.
 template <int D, int NW, int NST, typename QK, typename QV, typename SC>
 __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, SC scbuf, uint16_t* cvk,
-                                         uint16_t* cvv, float* nsk, float* nsv, int b, int g, int rg, int L, int k0,
+                                         uint16_t* cvv, uint16_t* scv, float* nsk, float* nsv, int b, int g, int rg, int L, int k0,
                                          int k1, bool whole, size_t slot, bool append) {
   using LY = BfLayout<D>;
   constexpr int DS = D / 32;
@@ -957,9 +961,7 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
   const float q128 = 128.f * group_sum(qsum);
 
   issue_block(k0, IC<0>{});
-  if constexpr (NST > 2) {
-    if (nblk > 1) issue_block(k0 + KB, IC<1>{});
-  }
+  if (nblk > 1) issue_block(k0 + KB, IC<1>{});
 
   int kofs[DS], vofs[DT];
 #pragma unroll
@@ -979,8 +981,7 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Scales of this lane's 8 keys kb + 16 kt + 4 lg + jj (K then V).
-  auto key_scales = [&](auto S, int kb, float (&sk)[8], float (&sv)[8]) {
-    const uint16_t* sc = scbuf(S);
+  auto key_scales = [&](const uint16_t* sc, int kb, float (&sk)[8], float (&sv)[8]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const uint2 wk = *reinterpret_cast<const uint2*>(sc + 16 * kt + 4 * lg);
@@ -1007,71 +1008,79 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
     }
   };
 
+  // Widen the int8 tiles of the block in raw stage S into bf16 buffer cb of
+  // cvk / cvv (8 values per item) as k' = q + 128: flipping each byte's top
+  // bit makes it the unsigned q + 128, which converts to fp32 in one
+  // instruction per byte, and an integer of 0..255 is exact in bf16 (the top
+  // half of its fp32 bits).  The offsets come back out per row: -128 sum_d q
+  // in the scores, -128 sum_key P' in the output.  Each thread issues the
+  // reads of all its items of both tiles before converting any (one LDS round
+  // trip, not one per item); each read names a single LDS object, so the
+  // compiler can tell the reads from the copies in flight into other stages
+  // and does not wait for them.
+  auto widen_block = [&](auto S, int cb) {
+    constexpr int PER = KB * D / 8;            // 8-value items per tile
+    constexpr int NT = 64 * NW;                // threads
+    constexpr int IPT = (PER + NT - 1) / NT;   // items per thread per tile
+    constexpr int SPR = D / 8;                 // items per row
+    static_assert((SPR & (SPR - 1)) == 0, "row of a power-of-two number of items");
+    auto widen8 = [&](uint2 w) {
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t word = (k < 2 ? w.x : w.y) ^ 0x80808080u;
+        const int sh = 16 * (k & 1);
+        const float lo = (float)((word >> sh) & 0xffu);
+        const float hi = (float)((word >> (sh + 8)) & 0xffu);
+        o[k] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+      }
+      return make_uint4(o[0], o[1], o[2], o[3]);
+    };
+    if (tid < 64) scv[(cb ? 64 : 0) + tid] = scbuf(S)[tid];  // the block's K, V scales
+    const int8_t* tk = qkbuf(S);
+    const int8_t* tv = qvbuf(S);
+    uint2 wk[IPT], wv[IPT];
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const unsigned it = (unsigned)tid + (unsigned)(k * NT);
+      if (it < (unsigned)PER) wk[k] = *reinterpret_cast<const uint2*>(tk + 8 * it);
+    }
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const unsigned it = (unsigned)tid + (unsigned)(k * NT);
+      if (it < (unsigned)PER) wv[k] = *reinterpret_cast<const uint2*>(tv + 8 * it);
+    }
+#pragma unroll
+    for (int k = 0; k < IPT; ++k) {
+      const unsigned it = (unsigned)tid + (unsigned)(k * NT);
+      if (it < (unsigned)PER) {
+        const int row = (int)(it / SPR), sl = (int)(it % SPR);
+        *reinterpret_cast<uint4*>(cvk + cb + row * D + 8 * LY::kslot(row, sl)) = widen8(wk[k]);
+        *reinterpret_cast<uint4*>(cvv + cb + row * D + 8 * LY::vslot(row, sl)) = widen8(wv[k]);
+      }
+    }
+  };
+
+  // Software pipeline, one barrier per block.  Step j: wait for block j+1's
+  // copies; barrier (block j+1's raw tiles have landed, block j's widened
+  // tiles are complete, and every read of block j-1's widened buffer is
+  // done); copy block j+NST into raw stage j (free: block j was widened, and
+  // its scales copied, in step j-1); widen block j+1 into the other bf16
+  // buffer (and its scales into the other half of scv); then the product of
+  // block j.
   auto step = [&](auto S, int j) {
     const int kb = k0 + j * KB;
-    if (NST > 2 && j + 1 < nblk)
-      wait_vmcnt<(NST > 2 ? CPW : 0)>();
+    const bool next = j + 1 < nblk;
+    if (NST > 2 && next && j + 2 < nblk)
+      wait_vmcnt<(NST > 2 ? CPW : 0)>();  // block j+2's copies may stay in flight
     else
       wait_vmcnt<0>();
     block_barrier();
-    if (j + NST - 1 < nblk) issue_block(kb + (NST - 1) * KB, IC<(decltype(S)::value + NST - 1) % NST>{});
-
-    // Widen the int8 tiles of block j into cvk / cvv (8 values per item) as
-    // k' = q + 128: flipping each byte's top bit makes it the unsigned q + 128,
-    // which converts to fp32 in one instruction per byte, and an integer of
-    // 0..255 is exact in bf16 (the top half of its fp32 bits).  The offsets
-    // come back out per row: -128 sum_d q in the scores, -128 sum_key P' in
-    // the output.  Each thread issues the reads of all its items of both
-    // tiles before converting any (one LDS round trip, not one per item);
-    // each read names a single LDS object, so the compiler can tell the
-    // reads from the copies in flight into other stages and does not wait
-    // for them.
-    {
-      constexpr int PER = KB * D / 8;            // 8-value items per tile
-      constexpr int NT = 64 * NW;                // threads
-      constexpr int IPT = (PER + NT - 1) / NT;   // items per thread per tile
-      constexpr int SPR = D / 8;                 // items per row
-      static_assert((SPR & (SPR - 1)) == 0, "row of a power-of-two number of items");
-      // Item i covers bytes [8 i, 8 i + 8) of a tile: row i / SPR, slot i % SPR.
-      // Every read of both tiles is issued before the first conversion.
-      auto widen8 = [&](uint2 w) {
-        uint32_t o[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t word = (k < 2 ? w.x : w.y) ^ 0x80808080u;
-          const int sh = 16 * (k & 1);
-          const float lo = (float)((word >> sh) & 0xffu);
-          const float hi = (float)((word >> (sh + 8)) & 0xffu);
-          o[k] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-        }
-        return make_uint4(o[0], o[1], o[2], o[3]);
-      };
-      const int8_t* tk = qkbuf(S);
-      const int8_t* tv = qvbuf(S);
-      uint2 wk[IPT], wv[IPT];
-#pragma unroll
-      for (int k = 0; k < IPT; ++k) {
-        const unsigned it = (unsigned)tid + (unsigned)(k * NT);
-        if (it < (unsigned)PER) wk[k] = *reinterpret_cast<const uint2*>(tk + 8 * it);
-      }
-#pragma unroll
-      for (int k = 0; k < IPT; ++k) {
-        const unsigned it = (unsigned)tid + (unsigned)(k * NT);
-        if (it < (unsigned)PER) wv[k] = *reinterpret_cast<const uint2*>(tv + 8 * it);
-      }
-#pragma unroll
-      for (int k = 0; k < IPT; ++k) {
-        const unsigned it = (unsigned)tid + (unsigned)(k * NT);
-        if (it < (unsigned)PER) {
-          const int row = (int)(it / SPR), sl = (int)(it % SPR);
-          *reinterpret_cast<uint4*>(cvk + row * D + 8 * LY::kslot(row, sl)) = widen8(wk[k]);
-          *reinterpret_cast<uint4*>(cvv + row * D + 8 * LY::vslot(row, sl)) = widen8(wv[k]);
-        }
-      }
-    }
+    if (j + NST < nblk) issue_block(kb + NST * KB, S);
+    const int cb = (j & 1) * KB * D;
+    if (next) widen_block(IC<(decltype(S)::value + 1) % NST>{}, KB * D - cb);
     float skey[8], svkey[8];
-    key_scales(S, kb, skey, svkey);
-    block_barrier();
+    key_scales(scv + (j & 1) * 64, kb, skey, svkey);
 
     float sc[8];
 #pragma unroll
@@ -1079,7 +1088,7 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cvk + kofs[s] + 16 * kt * D);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cvk + cb + kofs[s] + 16 * kt * D);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
       }
 #pragma unroll
@@ -1130,11 +1139,25 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
         v2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(cvv + vofs[dt] + 16 * hh * D));
+            (__attribute__((address_space(3))) s16x4*)(cvv + cb + vofs[dt] + 16 * hh * D));
       const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
     }
   };
+
+  // Prologue: blocks 0 .. NST-1 in flight (0 and 1 above), block 0 widened
+  // into buffer 0.
+  if constexpr (NST > 2) {
+    if (nblk > 2) issue_block(k0 + 2 * KB, IC<2>{});
+  }
+  if (NST > 2 && nblk > 2)
+    wait_vmcnt<(NST > 2 ? 2 * CPW : 0)>();  // blocks 1, 2 may stay in flight
+  else if (nblk > 1)
+    wait_vmcnt<CPW>();  // block 1 may stay in flight
+  else
+    wait_vmcnt<0>();
+  block_barrier();
+  widen_block(IC<0>{}, 0);
 
   for (int j = 0; j < nblk; j += NST) {
     step(IC<0>{}, j);
@@ -1198,7 +1221,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_S
 void attn_stream_i8(AttnArgs a) {
   SPECV_I8_STAGE_LDS
   stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append) {
-    i8_piece<D, NW, NST>(a, qkbuf, qvbuf, scbuf, cvk, cvv, nsk, nsv, b, g, rg, L, k0, k1, whole, slot, append);
+    i8_piece<D, NW, NST>(a, qkbuf, qvbuf, scbuf, cvk, cvv, scv, nsk, nsv, b, g, rg, L, k0, k1, whole, slot, append);
   });
 }
 
@@ -1613,8 +1636,8 @@ static hipError_t launch_i8(const AttnArgs& a0, hipStream_t s) {
   hipLaunchKernelGGL((quant_new_rows<D>), dim3((unsigned)((size_t)a.B * a.Hkv)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.P = stream_workgroups(attn_stream_i8<D, NW, kStages>, NW);
-  hipLaunchKernelGGL((attn_stream_i8<D, NW, kStages>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
+  a.P = stream_workgroups(attn_stream_i8<D, NW, SPECV_I8_STAGES>, NW);
+  hipLaunchKernelGGL((attn_stream_i8<D, NW, SPECV_I8_STAGES>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
