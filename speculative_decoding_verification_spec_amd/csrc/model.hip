@@ -20,11 +20,10 @@
 //   gemm<heads in, resid>  x += O wo, reading O [B][H][n][D] as [M][C]
 //   gemm<LN, bias, GELU>   u = gelu(LN2(x) w1 + b1)
 //   gemm<bias, resid>      x += u w2 + b2
-// then gemm<LN> logits = LNf(x) wout.  At the pages' sizes every matrix is a
-// few hundred by a few hundred: each product is one small launch, bound by
-// launch latency rather than by FLOPs or bytes, so the products are plain
-// LDS-staged fp32 FMA tiles (exact fp32 products, no conversion) rather than
-// matrix-core tiles.
+// then gemm<LN> logits = LNf(x) wout.  The products are fp32 matrix-core
+// tiles (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums), with the
+// LayerNorm fused in front and bias, GELU, residual add or the head-major
+// q/k/v scatter fused behind.
 #include <math.h>
 #include <stdint.h>
 
@@ -116,9 +115,9 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wt
 
 enum { A_ROWS = 0, A_HEADS = 1 };    // A: token-major [M][K], or head-major [B][H][n][D] read as [M][C]
 enum { O_ROWS = 0, O_QKV = 1 };      // out: token-major [M][N], or q | k | v head-major
-constexpr int kBM = 32, kBN = 64;    // output tile; 256 threads, 8 rows x 1 column each
-constexpr int kKC = 32;              // rows of W per staged chunk
-constexpr int kStage = kKC * kBN / 256;  // elements of a chunk each thread loads
+constexpr int kBM = 32, kBN = 32;    // output tile: 4 waves, 16 x 16 each
+constexpr int kPad = 4;              // floats of padding per staged A row (LDS banks)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
   const float* A;      // A_ROWS: [M][K]; A_HEADS: [B][H][n][D] with K = H*D
@@ -138,18 +137,23 @@ __device__ __forceinline__ float gelu_tanh(float v) {
   return 0.5f * v * (1.f + tanhf(u));
 }
 
-// out tile [m0, m0+32) x [n0, n0+64): the 32 A rows (LayerNorm-ed when LN)
-// are staged in LDS whole (K floats each); each wave owns 8 rows, each lane
-// one column; W comes through LDS in chunks of rows (W stays in L2 across
-// the row tiles).
+// Output tile [m0, m0+32) x [n0, n0+32) on v_mfma_f32_16x16x4_f32 (exact
+// fp32 products, fp32 accumulation).  The 32 A rows are staged in LDS whole
+// (K floats each, rows padded by kPad floats), LayerNorm-ed in place when
+// asked.  Wave w owns the 16 x 16 sub-tile (rows 16 (w / 2), columns
+// 16 (w % 2)).  The instruction takes A[l % 16][l / 16] and B[l / 16][l % 16]
+// from lane l and leaves C[4 (l / 16) + i][l % 16] in its i-th result; here
+// lane group l / 16 walks its own contiguous quarter of K, so its A values
+// are 16-byte LDS reads and its W values coalesce across the 16 columns.
+// W is read from L2 (it is small and shared by every row tile), the next
+// step's four values issued before the current step's products.
 template <int AMODE, int OMODE, bool LN, bool BIAS, bool GELU, bool RESID>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  extern __shared__ float As[];  // [kBM][K]
-  __shared__ float Ws[2][kKC][kBN];
+  extern __shared__ float As[];  // [kBM][K + kPad]
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
-  const int K = g.K;
+  const int K = g.K, KP = K + kPad;
 
   // stage the A rows
   for (int e = threadIdx.x; e < kBM * K; e += blockDim.x) {
@@ -164,73 +168,56 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         a = g.A[(((size_t)b * g.H + h) * g.n + i) * g.D + d];
       }
     }
-    As[r * K + k] = a;
+    As[r * KP + k] = a;
   }
   __syncthreads();
   if constexpr (LN) {
-    // each wave normalises its 8 rows: mean, then the variance about it
+    // each wave normalises 8 rows: mean, then the variance about it
     for (int r = wave * 8; r < wave * 8 + 8; ++r) {
       float s = 0.f;
-      for (int k = lane; k < K; k += kWave) s += As[r * K + k];
+      for (int k = lane; k < K; k += kWave) s += As[r * KP + k];
       const float mu = wave_sum(s) / (float)K;
       float v = 0.f;
       for (int k = lane; k < K; k += kWave) {
-        const float d = As[r * K + k] - mu;
+        const float d = As[r * KP + k] - mu;
         v += d * d;
       }
       const float rstd = 1.f / sqrtf(wave_sum(v) / (float)K + kLnEps);
-      for (int k = lane; k < K; k += kWave) As[r * K + k] = (As[r * K + k] - mu) * rstd * g.ln_g[k] + g.ln_b[k];
+      for (int k = lane; k < K; k += kWave) As[r * KP + k] = (As[r * KP + k] - mu) * rstd * g.ln_g[k] + g.ln_b[k];
     }
     __syncthreads();
   }
 
-  // W in chunks of kKC rows of the tile's 64 columns, double-buffered in LDS:
-  // each thread loads 8 elements of the next chunk into registers before the
-  // FMAs of the current one, so a chunk's load latency overlaps the work of
-  // the one before (the products are far too small to hide it otherwise).
-  const int col = n0 + lane;
+  const int lr = lane & 15, lgp = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int K4 = K / 4;  // this lane group's stretch of K (a multiple of 4)
+  const float* Ar = As + (16 * wr + lr) * KP + lgp * K4;
+  const int col = n0 + 16 * wc + lr;
   const bool col_ok = col < g.N;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const float* Ar = As + wave * 8 * K;
-  auto gload = [&](int k0, float (&r)[kStage]) {
+  const float* Wc = g.W + (size_t)lgp * K4 * g.N + (col_ok ? col : 0);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float w[4], wn[4];
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int e = threadIdx.x + 256 * i, k = k0 + (e >> 6), c = n0 + (e & 63);
-      r[i] = (k < K && c < g.N) ? g.W[(size_t)k * g.N + c] : 0.f;
-    }
-  };
-  auto sstore = [&](int buf, const float (&r)[kStage]) {
+  for (int t = 0; t < 4; ++t) w[t] = col_ok ? Wc[(size_t)t * g.N] : 0.f;
+  for (int s = 0; s < K4; s += 4) {
+    if (s + 4 < K4) {
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      Ws[buf][e >> 6][e & 63] = r[i];
+      for (int t = 0; t < 4; ++t) wn[t] = col_ok ? Wc[(size_t)(s + 4 + t) * g.N] : 0.f;
     }
-  };
-  {
-    float r[kStage];
-    gload(0, r);
-    sstore(0, r);
-    __syncthreads();
-    for (int k0 = 0, buf = 0; k0 < K; k0 += kKC, buf ^= 1) {
-      const bool more = k0 + kKC < K;
-      if (more) gload(k0 + kKC, r);
-      const int kn = min(kKC, K - k0);
-#pragma unroll 8
-      for (int kk = 0; kk < kn; ++kk) {
-        const float w = Ws[buf][kk][lane];
+    const float4 a4 = *reinterpret_cast<const float4*>(Ar + s);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, w[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, w[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, w[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, w[3], acc, 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = fmaf(Ar[j * K + k0 + kk], w, acc[j]);
-      }
-      if (more) sstore(buf ^ 1, r);
-      __syncthreads();
-    }
+    for (int t = 0; t < 4; ++t) w[t] = wn[t];
   }
   if (!col_ok) return;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = m0 + wave * 8 + j;
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + 16 * wr + 4 * lgp + i;
     if (m >= g.M) break;
-    float v = acc[j];
+    float v = acc[i];
     if constexpr (BIAS) v += g.bias[col];
     if constexpr (GELU) v = gelu_tanh(v);
     if constexpr (OMODE == O_ROWS) {
@@ -239,9 +226,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     } else {
       const int C = g.H * g.D;
       const int part = col / C, c = col - part * C, h = c / g.D, d = c - h * g.D;
-      const int b = m / g.n, i = m - b * g.n;
+      const int b = m / g.n, i2 = m - b * g.n;
       float* dst = part == 0 ? g.q : (part == 1 ? g.kn : g.vn);
-      dst[(((size_t)b * g.H + h) * g.n + i) * g.D + d] = v;
+      dst[(((size_t)b * g.H + h) * g.n + i2) * g.D + d] = v;
     }
   }
 }
@@ -250,7 +237,7 @@ template <int AMODE, int OMODE, bool LN, bool BIAS, bool GELU, bool RESID>
 static hipError_t gemm(const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
   hipLaunchKernelGGL((gemm_kernel<AMODE, OMODE, LN, BIAS, GELU, RESID>), grid, dim3(256),
-                     sizeof(float) * kBM * g.K, s, g);
+                     sizeof(float) * kBM * (g.K + kPad), s, g);
   return hipGetLastError();
 }
 
@@ -313,8 +300,9 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
   if (B < 1 || n < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
   if ((long)max_len_hint + n > (long)max_T || (long)max_len_hint + n > (long)l.T) return SPEC_ERR_OVERFLOW;
-  // the staged A rows and W chunks of one product tile must fit in 64 KB of LDS
-  if ((size_t)kBM * std::max(l.C, l.F) * sizeof(float) + sizeof(float) * 2 * kKC * kBN > 64 * 1024)
+  // the staged A rows of one product tile must fit in 64 KB of LDS, and each
+  // lane group's quarter of K must be a multiple of 4 (C a multiple of 16)
+  if ((size_t)kBM * (std::max(l.C, l.F) + kPad) * sizeof(float) > 64 * 1024 || l.C % 16 != 0)
     return SPEC_ERR_UNSUPPORTED;
   FwdPlan p;
   if (!fwd_plan(l, B, n, max_len_hint, &p)) return SPEC_ERR_UNSUPPORTED;
