@@ -1341,14 +1341,36 @@ __global__ __launch_bounds__(64) void attn_split_f32(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) oacc[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int kb = k0; kb < k1; kb += KB) {
-    float kf[2][DS];
+  // The K and V values of the block this lane feeds to the products: K as
+  // [kt][s] (key kb + 16 kt + lr, dims 4 s + lg), V as [4 kt + jj][dt] (key
+  // kb + 16 kt + 4 lg + jj, dim 16 dt + lr).  The next block's are loaded
+  // before the current block's products, so one block's loads are in flight
+  // during the other's arithmetic.
+  auto load_kv = [&](int kb, float (&kf)[2][DS], float (&vf)[8][DT]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const float* row = key_row<float>(kc, kn, kb + 16 * kt + lr, L, Ltot, a.n_q, a.max_T, D, it.bg);
 #pragma unroll
       for (int s = 0; s < DS; ++s) kf[kt][s] = row ? row[4 * s + lg] : 0.f;
     }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float* row = key_row<float>(vc, vn, kb + 16 * kt + 4 * lg + jj, L, Ltot, a.n_q, a.max_T, D, it.bg);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 16 * dt + lr;
+          vf[4 * kt + jj][dt] = (row && d < D) ? row[d] : 0.f;
+        }
+      }
+  };
+  float kf[2][DS], vf[8][DT];
+  if (k0 < k1) load_kv(k0, kf, vf);
+  for (int kb = k0; kb < k1; kb += KB) {
+    float kf2[2][DS], vf2[8][DT];
+    const bool more = kb + KB < k1;
+    if (more) load_kv(kb + KB, kf2, vf2);
     float sc[RT][8];
 #pragma unroll
     for (int r = 0; r < RT; ++r)
@@ -1381,17 +1403,23 @@ __global__ __launch_bounds__(64) void attn_split_f32(AttnArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float* row = key_row<float>(vc, vn, kb + 16 * kt + 4 * lg + jj, L, Ltot, a.n_q, a.max_T, D, it.bg);
+      for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int d = 16 * dt + lr;
-          const float vv = (row && d < D) ? row[d] : 0.f;
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
           for (int r = 0; r < RT; ++r)
-            oacc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, sc[r][4 * kt + jj], oacc[r][dt], 0, 0, 0);
-        }
-      }
+            oacc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[4 * kt + jj][dt], sc[r][4 * kt + jj], oacc[r][dt],
+                                                               0, 0, 0);
+    if (more) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s2 = 0; s2 < DS; ++s2) kf[kt][s2] = kf2[kt][s2];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vf[e][dt] = vf2[e][dt];
+    }
   }
 
   const size_t item_id = it.id;
@@ -1493,11 +1521,18 @@ struct SplitPolicy {
 #ifndef SPECV_ATTN_CMAX
 #define SPECV_ATTN_CMAX 8192
 #endif
+#ifndef SPECV_F32_ITEMS
+#define SPECV_F32_ITEMS 8192
+#endif
+#ifndef SPECV_F32_CMIN
+#define SPECV_F32_CMIN 128
+#endif
 
 static SplitPolicy policy(spec_dtype_t dt) {
   // bf16: workgroups of one wave per row tile, a few resident per CU; fp32:
   // single-wave items.
-  return dt == SPEC_BF16 ? SplitPolicy{256, SPECV_ATTN_CMAX, SPECV_ATTN_ITEMS} : SplitPolicy{128, 4096, 8192};
+  return dt == SPEC_BF16 ? SplitPolicy{256, SPECV_ATTN_CMAX, SPECV_ATTN_ITEMS}
+                         : SplitPolicy{SPECV_F32_CMIN, 4096, SPECV_F32_ITEMS};
 }
 
 static int max_rt(spec_dtype_t dt, int D) {
