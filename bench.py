@@ -545,6 +545,29 @@ def model_bench(args, torch, sv, dev):
     torch.cuda.synchronize()
     round_ms = a.elapsed_time(b) / rounds
     nacc = torch.stack(ns).cpu().numpy()
+
+    # The same rounds replayed from one captured graph (the hint fixed at the
+    # largest length any of them can reach); the state advances as before.
+    print("[bench] model: rounds from a captured graph", file=sys.stderr, flush=True)
+    st = fresh()
+    hint_max = prefix + rounds * (gamma + 1)
+    gud, guv = ud[0].clone(), uv[0].clone()
+    sv.spec_speculative_round(tcfg, pt, dcfg, pd, seq, st["seq_len"], st["tkv"], st["tlen"], st["dkv"], st["dlen"],
+                              gud, guv, T, hint_max)  # sizes the workspace for the largest hint
+    torch.cuda.synchronize()
+    st = fresh()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sv.spec_speculative_round(tcfg, pt, dcfg, pd, seq, st["seq_len"], st["tkv"], st["tlen"], st["dkv"],
+                                  st["dlen"], gud, guv, T, hint_max)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for k in range(rounds):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = a.elapsed_time(b) / rounds
     gen_tokens = int((nacc + 1).sum())
     tested = np.where(nacc < gamma, nacc + 1, gamma)
     alpha = float(nacc.sum() / tested.sum())
@@ -578,6 +601,7 @@ def model_bench(args, torch, sv, dev):
         "parts": {
             "verify_forward": {"ms": fwd_ms, "positions/s": B * gamma / (fwd_ms * 1e-3)},
             "target_only_decode": {"ms_per_token_step": base_ms, "tokens/s": base_tok_s},
+            "round_graph": {"ms": graph_ms, "what": "the same rounds replayed from one captured HIP graph"},
             "round": {"ms": round_ms, "tokens/s": tok_s, "speedup_vs_target_only": tok_s / base_tok_s,
                       "alpha": alpha, "tokens_per_target_call": float((nacc + 1).mean()),
                       "accepted_per_proposed": float(nacc.sum() / (gamma * nacc.size))},
