@@ -579,6 +579,10 @@ def model_bench(args, torch, sv, dev):
     w_bytes = 4 * sv.model_param_count(tcfg)
     kv_bytes = 4 * 4 * B * 4 * 24 * 2 * ((prefix + n) + n)
     fwd_bytes = w_bytes + kv_bytes
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] model: timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = model_cpu_baseline(tcfg, dcfg, pt, pd, ti, di, gamma, T, prefix)
     line = {
         "metric": "generated tokens/sec (speculative rounds) and verified positions/sec (verify forward)",
         "value": tok_s,
@@ -607,7 +611,51 @@ def model_bench(args, torch, sv, dev):
                       "accepted_per_proposed": float(nacc.sum() / (gamma * nacc.size))},
         },
     }
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line))
+
+
+def model_cpu_baseline(tcfg, dcfg, pt, pd, ti, di, gamma, T, prefix, budget_s=10.0):
+    """The model and round oracles as they stand (fp64 numpy, one BLAS thread)
+    on whole sequences of the model workload: the target's verify forward of
+    gamma+1 tokens over each sequence's 384 cached rows, then whole rounds."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import model as M
+    from oracle import round as R
+
+    ct, cd = M.ModelConfig(**tcfg), M.ModelConfig(**dcfg)
+    flat_t, flat_d = pt.cpu().numpy(), pd.cpu().numpy()
+    B = ti["tokens"].shape[0]
+    with threadpool_limits(limits=1):
+        done, t0 = 0, time.perf_counter()
+        while done < B and time.perf_counter() - t0 < budget_s / 2:
+            b = done
+            M.forward_cached(flat_t, ct, ti["tokens"][b : b + 1], ti["kv"][:, :, b : b + 1], ti["lens"][b : b + 1])
+            done += 1
+        fwd_s = time.perf_counter() - t0
+        r = np.random.default_rng(46)
+        toks, rounds, t1 = 0, 0, time.perf_counter()
+        while time.perf_counter() - t1 < budget_s / 2:
+            st = {"seq": [list(r.integers(0, ct.V, size=prefix))],
+                  "tkv": ti["kv"][:, :, :1].astype(np.float64), "tlen": np.array([prefix - 1]),
+                  "dkv": di["kv"][:, :, :1].astype(np.float64), "dlen": np.array([prefix - 2])}
+            res = R.speculative_round(flat_t, ct, flat_d, cd, st, gamma, T, r.random((1, gamma)),
+                                      r.random((1, gamma + 1)))
+            toks += int(res["n_accepted"][0]) + 1
+            rounds += 1
+        round_s = time.perf_counter() - t1
+    return {
+        "value": toks / round_s,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{rounds} whole rounds of one sequence (4 draft forwards, the target's verify forward, the "
+                  f"sampler) and {done} target verify forwards over 384 cached rows, numpy fp64, one BLAS thread",
+        "verify_forward_positions/s": done * gamma / fwd_s,
+        "seconds": fwd_s + round_s,
+    }
 
 if __name__ == "__main__":
     main()
