@@ -145,8 +145,8 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 // from lane l and leaves C[4 (l / 16) + i][l % 16] in its i-th result; here
 // lane group l / 16 walks its own contiguous quarter of K, so its A values
 // are 16-byte LDS reads and its W values coalesce across the 16 columns.
-// W is read from L2 (it is small and shared by every row tile), the next
-// step's four values issued before the current step's products.
+// W is read from L2 (it is small and shared by every row tile), each step's
+// four values issued four steps ahead.
 template <int AMODE, int OMODE, bool LN, bool BIAS, bool GELU, bool RESID>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   extern __shared__ float As[];  // [kBM][K + kPad]
@@ -194,23 +194,42 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const float* Ar = As + (16 * wr + lr) * KP + lgp * K4;
   const int col = n0 + 16 * wc + lr;
   const bool col_ok = col < g.N;
-  const float* Wc = g.W + (size_t)lgp * K4 * g.N + (col_ok ? col : 0);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float w[4], wn[4];
+  // Iteration it takes K rows 4 it .. 4 it + 3 of this lane group's stretch;
+  // its four W values sit in ring slot it % kRing, loaded kRing iterations
+  // ahead (an L2 round trip is about one microsecond, several iterations).
+  constexpr int kRing = 4;
+  const int NIT = K4 / 4;
+  // Buffer loads from a scalar base with 32-bit lane offsets, issued without
+  // branches (a column past N or a step past the last reads a valid element
+  // whose product is discarded or zeroed), so the compiler can count them and
+  // wait for the oldest only.
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.W), 0, (int)((long)K * g.N * sizeof(float)), 0x00020000);
+  const uint32_t cbase = (uint32_t)(lgp * K4) * (uint32_t)g.N + (uint32_t)(col_ok ? col : 0);
+  float w[kRing][4];
+  auto load_it = [&](int it, float (&r)[4]) {
+    const int it_c = min(it, NIT - 1);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) w[t] = col_ok ? Wc[(size_t)t * g.N] : 0.f;
-  for (int s = 0; s < K4; s += 4) {
-    if (s + 4 < K4) {
+    for (int t = 0; t < 4; ++t)
+      r[t] = __builtin_bit_cast(
+          float, __builtin_amdgcn_raw_buffer_load_b32(wrs, (cbase + (uint32_t)(4 * it_c + t) * (uint32_t)g.N) * 4u, 0, 0));
+  };
 #pragma unroll
-      for (int t = 0; t < 4; ++t) wn[t] = col_ok ? Wc[(size_t)(s + 4 + t) * g.N] : 0.f;
+  for (int q = 0; q < kRing; ++q) load_it(q, w[q]);
+  for (int it0 = 0; it0 < NIT; it0 += kRing) {
+#pragma unroll
+    for (int q = 0; q < kRing; ++q) {
+      const int it = it0 + q;
+      if (it < NIT) {  // uniform
+        const float4 a4 = *reinterpret_cast<const float4*>(Ar + 4 * it);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, w[q][0], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, w[q][1], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, w[q][2], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, w[q][3], acc, 0, 0, 0);
+      }
+      load_it(it + kRing, w[q]);
     }
-    const float4 a4 = *reinterpret_cast<const float4*>(Ar + s);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, w[0], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, w[1], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, w[2], acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, w[3], acc, 0, 0, 0);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) w[t] = wn[t];
   }
   if (!col_ok) return;
 #pragma unroll
