@@ -49,6 +49,9 @@
 #ifndef SPECV_RS_WAVES_PER_BLOCK
 #define SPECV_RS_WAVES_PER_BLOCK 4
 #endif
+#ifndef SPECV_RS_RESID_PER_CU
+#define SPECV_RS_RESID_PER_CU 2  // residual workgroups per CU to aim for
+#endif
 
 #include "spec_common.h"
 #include "spec_verify.h"
@@ -834,7 +837,8 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
   if (e != hipSuccess) return e;
   double2* segsum = reinterpret_cast<double2*>(ws + pl.off_seg);
   // About two residual workgroups per CU, at least two segments per wave.
-  const int ngrp = std::max(1, std::min((2 * device_cus() + B - 1) / B, (pl.nseg + 2 * kResidWaves - 1) / (2 * kResidWaves)));
+  const int ngrp = std::max(1, std::min((SPECV_RS_RESID_PER_CU * device_cus() + B - 1) / B,
+                                        (pl.nseg + 2 * kResidWaves - 1) / (2 * kResidWaves)));
   int spw = (pl.nseg + ngrp * kResidWaves - 1) / (ngrp * kResidWaves);
   spw += spw & 1;
   const int ny = (pl.nseg + spw * kResidWaves - 1) / (spw * kResidWaves);
