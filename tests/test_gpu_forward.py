@@ -47,6 +47,8 @@ def _run(cfg, params, tokens, lens, kv, hint):
         ("draft", 8, 1, 0, 40, 64),        # one new token per sequence (a draft step)
         ("draft", 7, 9, 3, 50, 64),        # gamma + 1 = 9
         ("target", 64, 5, 384, 384, 512),  # the pages' verify shape: prefix 384, gamma = 4
+        ("target", 1, 16, 0, 30, 48),      # one sequence, the largest n
+        ("draft", 3, 16, 496, 496, 512),   # positions ending exactly at T = 512
     ],
 )
 def test_forward_matches_oracle(which, B, n, lo, hi, max_T):

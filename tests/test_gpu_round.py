@@ -31,7 +31,8 @@ def _case(name, **kw):
     print(f"\n[case] {name} {kw}", flush=True)
 
 
-@pytest.mark.parametrize("T,gamma,rounds", [(1.0, 4, 4), (0.0, 4, 4), (0.7, 6, 3)])
+@pytest.mark.parametrize("T,gamma,rounds", [(1.0, 4, 4), (0.0, 4, 4), (0.7, 6, 3), (1.0, 1, 5), (1.0, 15, 2),
+                                             (0.0, 8, 3)])
 def test_rounds_match_oracle(T, gamma, rounds):
     _case("rounds", T=T, gamma=gamma, rounds=rounds)
     dev = torch.device("cuda:0")
