@@ -314,7 +314,7 @@ size_t spec_verify_forward_workspace_size(const spec_model_t* model, int B, int 
  * Errors: SPEC_ERR_ARG for an invalid shape, null pointers, non-positive
  * sizes, a small or unaligned workspace; SPEC_ERR_OVERFLOW when
  * max_len_hint + n exceeds max_T or T; SPEC_ERR_UNSUPPORTED for a head
- * dimension the attention does not support, n > 16, or a width C above 112
+ * dimension the attention does not support, n > 16, or a width C above 144
  * or not a multiple of 16. */
 spec_status_t spec_verify_forward(const spec_model_t* model, const float* params, const int32_t* tokens,
                                   const int32_t* cache_len, float* kv_cache, int max_T, float* logits, int B, int n,

@@ -17,13 +17,13 @@
 //                          head-major ([B][H][n][D]) for the attention
 //   spec_verify_attention  appends k_new, v_new at [p0, p0+n) of the layer's
 //                          cache and attends (the library's fp32 kernels)
-//   gemm<heads in, resid>  x += O wo, reading O [B][H][n][D] as [M][C]
-//   gemm<LN, bias, GELU>   u = gelu(LN2(x) w1 + b1)
-//   gemm<bias, resid>      x += u w2 + b2
+//   block_mlp              x += O wo (reading O [B][H][n][D] as [M][C]);
+//                          x += gelu(LN2(x) w1 + b1) w2 + b2, 16 rows per
+//                          workgroup with the intermediates in LDS
 // then gemm<LN> logits = LNf(x) wout.  The products are fp32 matrix-core
-// tiles (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums), with the
-// LayerNorm fused in front and bias, GELU, residual add or the head-major
-// q/k/v scatter fused behind.
+// tiles (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums); the
+// LayerNorms, biases, GELU, residual adds and the head-major q/k/v scatter
+// are fused around them.
 #include <math.h>
 #include <stdint.h>
 
@@ -113,19 +113,17 @@ __global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wt
     x[(size_t)row * C + c] = ok ? wte[(size_t)t * C + c] + wpe[(size_t)pos * C + c] : __builtin_nanf("");
 }
 
-enum { A_ROWS = 0, A_HEADS = 1 };    // A: token-major [M][K], or head-major [B][H][n][D] read as [M][C]
 enum { O_ROWS = 0, O_QKV = 1 };      // out: token-major [M][N], or q | k | v head-major
 constexpr int kBM = 32, kBN = 32;    // output tile: 4 waves, 16 x 16 each
 constexpr int kPad = 4;              // floats of padding per staged A row (LDS banks)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct GemmArgs {
-  const float* A;      // A_ROWS: [M][K]; A_HEADS: [B][H][n][D] with K = H*D
+  const float* A;      // [M][K]
   const float* W;      // [K][N]
-  const float* ln_g;   // LN gain / bias over K (LN only)
+  const float* ln_g;   // LN gain / bias over K
   const float* ln_b;
-  const float* bias;   // [N] (BIAS only)
-  float* out;          // O_ROWS: [M][N] (RESID: also the addend, updated in place)
+  float* out;          // O_ROWS: [M][N]
   float* q;            // O_QKV: three [B][H][n][D] outputs, N = 3 H D
   float* kn;
   float* vn;
@@ -137,83 +135,35 @@ __device__ __forceinline__ float gelu_tanh(float v) {
   return 0.5f * v * (1.f + tanhf(u));
 }
 
-// Output tile [m0, m0+32) x [n0, n0+32) on v_mfma_f32_16x16x4_f32 (exact
-// fp32 products, fp32 accumulation).  The 32 A rows are staged in LDS whole
-// (K floats each, rows padded by kPad floats), LayerNorm-ed in place when
-// asked.  Wave w owns the 16 x 16 sub-tile (rows 16 (w / 2), columns
-// 16 (w % 2)).  The instruction takes A[l % 16][l / 16] and B[l / 16][l % 16]
-// from lane l and leaves C[4 (l / 16) + i][l % 16] in its i-th result; here
-// lane group l / 16 walks its own contiguous quarter of K, so its A values
-// are 16-byte LDS reads and its W values coalesce across the 16 columns.
-// W is read from L2 (it is small and shared by every row tile), each step's
-// four values issued four steps ahead.
-template <int AMODE, int OMODE, bool LN, bool BIAS, bool GELU, bool RESID>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-  extern __shared__ float As[];  // [kBM][K + kPad]
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
-  const int K = g.K, KP = K + kPad;
+// One 16 x 16 tile on v_mfma_f32_16x16x4_f32: the 16 rows of A (in LDS, row
+// stride KP floats) times columns col of W ([K][N], row-major, through the
+// buffer resource wrs).  The instruction takes A[l % 16][l / 16] and
+// B[l / 16][l % 16] from lane l and leaves C[4 (l / 16) + i][l % 16] in its
+// i-th result; here lane group l / 16 walks its own contiguous quarter of K
+// (K a multiple of 16), so its A values are 16-byte LDS reads and its W
+// values coalesce across the 16 columns.  W comes through buffer loads from a
+// scalar base, issued without branches four steps ahead (a column past N or a
+// step past the last reads a valid element whose product is discarded), so
+// the compiler waits for the oldest only.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const float* W, int K, int N) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(W), 0, (int)((long)K * N * sizeof(float)), 0x00020000);
+}
 
-  // stage the A rows
-  for (int e = threadIdx.x; e < kBM * K; e += blockDim.x) {
-    const int r = e / K, k = e - r * K;
-    const int m = m0 + r;
-    float a = 0.f;
-    if (m < g.M) {
-      if constexpr (AMODE == A_ROWS) {
-        a = g.A[(size_t)m * K + k];
-      } else {
-        const int b = m / g.n, i = m - b * g.n, h = k / g.D, d = k - h * g.D;
-        a = g.A[(((size_t)b * g.H + h) * g.n + i) * g.D + d];
-      }
-    }
-    As[r * KP + k] = a;
-  }
-  __syncthreads();
-  if constexpr (LN) {
-    // each wave normalises 8 rows: mean, then the variance about it
-    for (int r = wave * 8; r < wave * 8 + 8; ++r) {
-      float s = 0.f;
-      for (int k = lane; k < K; k += kWave) s += As[r * KP + k];
-      const float mu = wave_sum(s) / (float)K;
-      float v = 0.f;
-      for (int k = lane; k < K; k += kWave) {
-        const float d = As[r * KP + k] - mu;
-        v += d * d;
-      }
-      const float rstd = 1.f / sqrtf(wave_sum(v) / (float)K + kLnEps);
-      for (int k = lane; k < K; k += kWave) As[r * KP + k] = (As[r * KP + k] - mu) * rstd * g.ln_g[k] + g.ln_b[k];
-    }
-    __syncthreads();
-  }
-
-  const int lr = lane & 15, lgp = lane >> 4;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int K4 = K / 4;  // this lane group's stretch of K (a multiple of 4)
-  const float* Ar = As + (16 * wr + lr) * KP + lgp * K4;
-  const int col = n0 + 16 * wc + lr;
-  const bool col_ok = col < g.N;
+__device__ __forceinline__ f32x4 mfma_tile16(const float* A, int KP, int K, __amdgpu_buffer_rsrc_t wrs, int N, int col,
+                                             bool col_ok, int lr, int lgp) {
+  const int K4 = K / 4;
+  const float* Ar = A + lr * KP + lgp * K4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  // Iteration it takes K rows 4 it .. 4 it + 3 of this lane group's stretch;
-  // its four W values sit in ring slot it % kRing, loaded kRing iterations
-  // ahead (an L2 round trip is about one microsecond, several iterations).
   constexpr int kRing = 4;
   const int NIT = K4 / 4;
-  // Buffer loads from a scalar base with 32-bit lane offsets, issued without
-  // branches (a column past N or a step past the last reads a valid element
-  // whose product is discarded or zeroed), so the compiler can count them and
-  // wait for the oldest only.
-  const __amdgpu_buffer_rsrc_t wrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g.W), 0, (int)((long)K * g.N * sizeof(float)), 0x00020000);
-  const uint32_t cbase = (uint32_t)(lgp * K4) * (uint32_t)g.N + (uint32_t)(col_ok ? col : 0);
+  const uint32_t cbase = (uint32_t)(lgp * K4) * (uint32_t)N + (uint32_t)(col_ok ? col : 0);
   float w[kRing][4];
   auto load_it = [&](int it, float (&r)[4]) {
     const int it_c = min(it, NIT - 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       r[t] = __builtin_bit_cast(
-          float, __builtin_amdgcn_raw_buffer_load_b32(wrs, (cbase + (uint32_t)(4 * it_c + t) * (uint32_t)g.N) * 4u, 0, 0));
+          float, __builtin_amdgcn_raw_buffer_load_b32(wrs, (cbase + (uint32_t)(4 * it_c + t) * (uint32_t)N) * 4u, 0, 0));
   };
 #pragma unroll
   for (int q = 0; q < kRing; ++q) load_it(q, w[q]);
@@ -231,17 +181,57 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       load_it(it + kRing, w[q]);
     }
   }
+  return acc;
+}
+
+// Output tile [m0, m0+32) x [n0, n0+32) (exact fp32 products, fp32
+// accumulation).  The 32 A rows are staged in LDS whole (K floats each, rows
+// padded by kPad floats), and LayerNorm-ed in place.  Wave w owns the
+// 16 x 16 sub-tile (rows 16 (w / 2), columns 16 (w % 2)), computed by
+// mfma_tile16; W is read from L2 (it is small and shared by every row tile).
+template <int OMODE>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  extern __shared__ float As[];  // [kBM][K + kPad]
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int K = g.K, KP = K + kPad;
+
+  // stage the A rows
+  for (int e = threadIdx.x; e < kBM * K; e += blockDim.x) {
+    const int r = e / K, k = e - r * K;
+    const int m = m0 + r;
+    As[r * KP + k] = m < g.M ? g.A[(size_t)m * K + k] : 0.f;
+  }
+  __syncthreads();
+  // each wave normalises 8 rows: mean, then the variance about it
+  for (int r = wave * 8; r < wave * 8 + 8; ++r) {
+    float s = 0.f;
+    for (int k = lane; k < K; k += kWave) s += As[r * KP + k];
+    const float mu = wave_sum(s) / (float)K;
+    float v = 0.f;
+    for (int k = lane; k < K; k += kWave) {
+      const float d = As[r * KP + k] - mu;
+      v += d * d;
+    }
+    const float rstd = 1.f / sqrtf(wave_sum(v) / (float)K + kLnEps);
+    for (int k = lane; k < K; k += kWave) As[r * KP + k] = (As[r * KP + k] - mu) * rstd * g.ln_g[k] + g.ln_b[k];
+  }
+  __syncthreads();
+
+  const int lr = lane & 15, lgp = lane >> 4;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int col = n0 + 16 * wc + lr;
+  const bool col_ok = col < g.N;
+  const f32x4 acc = mfma_tile16(As + 16 * wr * KP, KP, K, w_rsrc(g.W, K, g.N), g.N, col, col_ok, lr, lgp);
   if (!col_ok) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 16 * wr + 4 * lgp + i;
     if (m >= g.M) break;
-    float v = acc[i];
-    if constexpr (BIAS) v += g.bias[col];
-    if constexpr (GELU) v = gelu_tanh(v);
+    const float v = acc[i];
     if constexpr (OMODE == O_ROWS) {
-      float* o = g.out + (size_t)m * g.N + col;
-      *o = RESID ? *o + v : v;
+      g.out[(size_t)m * g.N + col] = v;
     } else {
       const int C = g.H * g.D;
       const int part = col / C, c = col - part * C, h = c / g.D, d = c - h * g.D;
@@ -252,12 +242,101 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
-template <int AMODE, int OMODE, bool LN, bool BIAS, bool GELU, bool RESID>
+template <int OMODE>
 static hipError_t gemm(const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
-  hipLaunchKernelGGL((gemm_kernel<AMODE, OMODE, LN, BIAS, GELU, RESID>), grid, dim3(256),
+  hipLaunchKernelGGL((gemm_kernel<OMODE>), grid, dim3(256),
                      sizeof(float) * kBM * (g.K + kPad), s, g);
   return hipGetLastError();
+}
+
+// The half of a layer after its attention, for 16 rows per workgroup of 8
+// waves, with every intermediate in LDS:
+//   y = O wo (O read head-major as [M][C]); X = x + y
+//   u = gelu(LN2(X) w1 + b1)
+//   x = X + u w2 + b2
+// Waves take 16-column tiles of each product in turn (mfma_tile16).
+struct MlpArgs {
+  const float* O;  // [B][H][n][D]
+  float* x;        // [M][C], updated in place
+  const float *wo, *ln_g, *ln_b, *w1, *b1, *w2, *b2;
+  int M, n, H, D, C, F;
+};
+
+__global__ __launch_bounds__(512) void block_mlp_kernel(MlpArgs g) {
+  extern __shared__ float sm[];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int lr = lane & 15, lgp = lane >> 4;
+  const int C = g.C, F = g.F, CP = C + kPad, FP = F + kPad;
+  float* Os = sm;            // [16][CP]
+  float* Xs = Os + 16 * CP;  // [16][CP]
+  float* Hs = Xs + 16 * CP;  // [16][CP]
+  float* Us = Hs + 16 * CP;  // [16][FP]
+  const int m0 = blockIdx.x * 16;
+
+  for (int e = threadIdx.x; e < 16 * C; e += blockDim.x) {
+    const int r = e / C, k = e - r * C, m = m0 + r;
+    float a = 0.f;
+    if (m < g.M) {
+      const int b = m / g.n, i = m - b * g.n, h = k / g.D, d = k - h * g.D;
+      a = g.O[(((size_t)b * g.H + h) * g.n + i) * g.D + d];
+    }
+    Os[r * CP + k] = a;
+  }
+  __syncthreads();
+  {  // X = x + O wo
+    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.wo, C, C);
+    for (int ct = wave; ct < C / 16; ct += 8) {
+      const int col = 16 * ct + lr;
+      const f32x4 acc = mfma_tile16(Os, CP, C, wr, C, col, true, lr, lgp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lgp + i, m = m0 + r;
+        Xs[r * CP + col] = (m < g.M ? g.x[(size_t)m * C + col] : 0.f) + acc[i];
+      }
+    }
+  }
+  __syncthreads();
+  // LN2: two rows per wave, mean, then the variance about it
+  for (int r = 2 * wave; r < 2 * wave + 2; ++r) {
+    float s = 0.f;
+    for (int k = lane; k < C; k += kWave) s += Xs[r * CP + k];
+    const float mu = wave_sum(s) / (float)C;
+    float v = 0.f;
+    for (int k = lane; k < C; k += kWave) {
+      const float d = Xs[r * CP + k] - mu;
+      v += d * d;
+    }
+    const float rstd = 1.f / sqrtf(wave_sum(v) / (float)C + kLnEps);
+    for (int k = lane; k < C; k += kWave) Hs[r * CP + k] = (Xs[r * CP + k] - mu) * rstd * g.ln_g[k] + g.ln_b[k];
+  }
+  __syncthreads();
+  {  // u = gelu(H w1 + b1)
+    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w1, C, F);
+    for (int ct = wave; ct < F / 16; ct += 8) {
+      const int col = 16 * ct + lr;
+      const f32x4 acc = mfma_tile16(Hs, CP, C, wr, F, col, true, lr, lgp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Us[(4 * lgp + i) * FP + col] = gelu_tanh(acc[i] + g.b1[col]);
+    }
+  }
+  __syncthreads();
+  {  // x = X + u w2 + b2
+    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w2, F, C);
+    for (int ct = wave; ct < C / 16; ct += 8) {
+      const int col = 16 * ct + lr;
+      const f32x4 acc = mfma_tile16(Us, FP, F, wr, C, col, true, lr, lgp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lgp + i, m = m0 + r;
+        if (m < g.M) g.x[(size_t)m * C + col] = Xs[r * CP + col] + acc[i] + g.b2[col];
+      }
+    }
+  }
+}
+
+static size_t mlp_lds_bytes(const ModelLayout& l) {
+  return sizeof(float) * 16 * (3 * (size_t)(l.C + kPad) + l.F + kPad);
 }
 
 struct FwdPlan {
@@ -319,9 +398,10 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
   if (B < 1 || n < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
   if ((long)max_len_hint + n > (long)max_T || (long)max_len_hint + n > (long)l.T) return SPEC_ERR_OVERFLOW;
-  // the staged A rows of one product tile must fit in 64 KB of LDS, and each
-  // lane group's quarter of K must be a multiple of 4 (C a multiple of 16)
-  if ((size_t)kBM * (std::max(l.C, l.F) + kPad) * sizeof(float) > 64 * 1024 || l.C % 16 != 0)
+  // the staged rows of a product tile and of block_mlp must fit in 64 KB of
+  // LDS, and each lane group's quarter of K must be a multiple of 4 (C a
+  // multiple of 16); together these allow C up to 144
+  if ((size_t)kBM * (l.C + kPad) * sizeof(float) > 64 * 1024 || mlp_lds_bytes(l) > 64 * 1024 || l.C % 16 != 0)
     return SPEC_ERR_UNSUPPORTED;
   FwdPlan p;
   if (!fwd_plan(l, B, n, max_len_hint, &p)) return SPEC_ERR_UNSUPPORTED;
@@ -361,7 +441,7 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
     g.q = q;
     g.kn = kn;
     g.vn = vn;
-    if (gemm<A_ROWS, O_QKV, true, false, false, false>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+    if (gemm<O_QKV>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
 
     // append + causal attention over the layer's cache
     float* kc = kv_cache + (size_t)(2 * layer) * plane;
@@ -371,38 +451,25 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
                                                    p.attn_bytes, stream);
     if (st != SPEC_OK) return st;
 
-    // x += O wo
-    g = GemmArgs{};
-    g.M = M;
-    g.n = n;
-    g.H = l.H;
-    g.D = l.D;
-    g.A = o;
-    g.K = l.C;
-    g.N = l.C;
-    g.W = P + l.wo;
-    g.out = x;
-    if (gemm<A_HEADS, O_ROWS, false, false, false, true>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
-
-    // u = gelu(LN2(x) w1 + b1)
-    g.A = x;
-    g.K = l.C;
-    g.N = l.F;
-    g.W = P + l.w1;
-    g.ln_g = P + l.ln2_g;
-    g.ln_b = P + l.ln2_b;
-    g.bias = P + l.b1;
-    g.out = u;
-    if (gemm<A_ROWS, O_ROWS, true, true, true, false>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
-
-    // x += u w2 + b2
-    g.A = u;
-    g.K = l.F;
-    g.N = l.C;
-    g.W = P + l.w2;
-    g.bias = P + l.b2;
-    g.out = x;
-    if (gemm<A_ROWS, O_ROWS, false, true, false, true>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+    // x += O wo; x += gelu(LN2(x) w1 + b1) w2 + b2, 16 rows per workgroup
+    MlpArgs ma{};
+    ma.O = o;
+    ma.x = x;
+    ma.wo = P + l.wo;
+    ma.ln_g = P + l.ln2_g;
+    ma.ln_b = P + l.ln2_b;
+    ma.w1 = P + l.w1;
+    ma.b1 = P + l.b1;
+    ma.w2 = P + l.w2;
+    ma.b2 = P + l.b2;
+    ma.M = M;
+    ma.n = n;
+    ma.H = l.H;
+    ma.D = l.D;
+    ma.C = l.C;
+    ma.F = l.F;
+    hipLaunchKernelGGL(block_mlp_kernel, dim3((unsigned)((M + 15) / 16)), dim3(512), mlp_lds_bytes(l), stream, ma);
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   }
 
   // logits = LNf(x) wout
@@ -418,6 +485,6 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
   g.ln_g = params + l.lnf_g;
   g.ln_b = params + l.lnf_b;
   g.out = logits;
-  if (gemm<A_ROWS, O_ROWS, true, false, false, false>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+  if (gemm<O_ROWS>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
   return SPEC_OK;
 }

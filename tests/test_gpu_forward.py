@@ -21,6 +21,7 @@ from workloads import gen
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-4
+WIDE = M.ModelConfig(96, 144, 2, 6, 128)
 
 
 def _case(name, **kw):
@@ -49,10 +50,11 @@ def _run(cfg, params, tokens, lens, kv, hint):
         ("target", 64, 5, 384, 384, 512),  # the pages' verify shape: prefix 384, gamma = 4
         ("target", 1, 16, 0, 30, 48),      # one sequence, the largest n
         ("draft", 3, 16, 496, 496, 512),   # positions ending exactly at T = 512
+        ("wide", 5, 5, 0, 40, 64),         # the widest model the fused MLP's LDS takes: C = 144, D = 24
     ],
 )
 def test_forward_matches_oracle(which, B, n, lo, hi, max_T):
-    cfg = M.TARGET if which == "target" else M.DRAFT
+    cfg = {"target": M.TARGET, "draft": M.DRAFT, "wide": WIDE}[which]
     _case("forward", which=which, B=B, n=n, lens=(lo, hi), max_T=max_T)
     params = gen.model_params(M.param_shapes(cfg), 20)
     inp = gen.forward_inputs(cfg.V, cfg.L, cfg.H, cfg.D, B, n, (lo, hi), max_T, 21)
@@ -109,4 +111,9 @@ def test_argument_errors():
         sv.spec_verify_forward(M.ModelConfig(96, 40, 1, 2, 512), torch.zeros(
             sv.model_param_count(M.ModelConfig(96, 40, 1, 2, 512)), dtype=torch.float32, device=dev),
             tokens, lens, torch.zeros((1, 2, 2, 2, 8, 20), dtype=torch.float32, device=dev), 2)  # D = 20
+    assert e.value.status == 3
+    wide = M.ModelConfig(96, 160, 1, 5, 512)  # D = 32 is supported, C = 160 is above 144
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_verify_forward(wide, torch.zeros(sv.model_param_count(wide), dtype=torch.float32, device=dev),
+                               tokens, lens, torch.zeros((1, 2, 2, 5, 8, 32), dtype=torch.float32, device=dev), 2)
     assert e.value.status == 3
