@@ -33,8 +33,8 @@
 //
 // bf16 kernels.  One wave per 16-row tile.  K and
 // V blocks (32 keys x D) are copied from HBM straight into LDS with
-// global_load_lds (no registers, asynchronous) through three LDS stages, two
-// blocks in flight, and read by
+// global_load_lds (no registers, asynchronous, non-temporal) through two LDS
+// stages, the next block in flight while one is computed, and read by
 // every wave of the workgroup: K as 16-byte A fragments (ds_read_b128), V
 // transposed with ds_read_b64_tr_b16 (within each 16-lane group, lane i
 // receives element i mod 4 of the 8-byte pieces of lanes 4k + i/4, k = 0..3;
@@ -257,6 +257,14 @@ __device__ __forceinline__ float group_sum(float v) {
 #ifndef SPECV_I8_STAGES
 #define SPECV_I8_STAGES 2  // raw int8 stages: with two bf16 buffers, 2 keep the kernel in 128 VGPRs
 #endif
+// Cache policy of the cache-block loads, which stream every key once per
+// call: non-temporal (nt = 2).
+#ifndef SPECV_KV_CPOL
+#define SPECV_KV_CPOL 2
+#endif
+#ifndef SPECV_I8_CPOL
+#define SPECV_I8_CPOL 2
+#endif
 #ifndef SPECV_STREAM_WPE
 #define SPECV_STREAM_WPE 4
 #endif
@@ -422,7 +430,7 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc((void*)cbase, (short)0, (PG == 16 ? 16 : KB) * D * 2, 0x00020000);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3)))*)dst, 16,
-                                                 (int)(loff * 2), 0, 0, 0);
+                                                 (int)(loff * 2), 0, 0, SPECV_KV_CPOL);
       } else {  // new rows from k_new/v_new; keys past the end read a finite dummy row
         const int crow = (int)(coff[i] / D);
         const int key = kb + crow;
@@ -918,7 +926,7 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (size_t)kb * D), (short)0, KB * D, 0x00020000);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3)))*)dst, 16, (int)boff,
-                                                 0, 0, 0);
+                                                 0, 0, SPECV_I8_CPOL);
       } else {
         const int key = kb + (int)(boff / D);
         const int8_t* fresh = is_v ? vnb : knb;
@@ -1574,8 +1582,10 @@ static AttnPlan attn_plan(int B, int Hq, int Hkv, int n_q, int D, int hint, spec
   return p;
 }
 
+// Two stages measured faster than three with non-temporal loads (4.6%,
+// 32K-key caches), and halve the LDS.
 #ifndef SPECV_ATTN_STAGES
-#define SPECV_ATTN_STAGES 3
+#define SPECV_ATTN_STAGES 2
 #endif
 constexpr int kStages = SPECV_ATTN_STAGES;  // LDS stages; blocks in flight per workgroup: kStages - 1
 
@@ -1584,7 +1594,10 @@ constexpr int kStages = SPECV_ATTN_STAGES;  // LDS stages; blocks in flight per 
 // Upper bound on the workgroups of a stream launch: 256 CUs, at most 3
 // resident workgroups each (LDS).  The partial slots per slab follow from it,
 // so the workspace size does not depend on the device.
-constexpr int kStreamMaxWG = 768;
+#ifndef SPECV_STREAM_MAX_WG
+#define SPECV_STREAM_MAX_WG 768
+#endif
+constexpr int kStreamMaxWG = SPECV_STREAM_MAX_WG;
 
 // Sizes the stream scheme handles: every workgroup scans the B lengths, and
 // block counts stay in int.

@@ -169,27 +169,30 @@ struct RawVec<2> { using type = uint16_t; };
 // One raw vector through a buffer resource: a scalar base and a 32-bit byte
 // offset, so no 64-bit address is built in (and waits on) vector registers;
 // offsets past the resource's size read 0 and never fault.
+#ifndef SPECV_RESID_CPOL
+#define SPECV_RESID_CPOL 0  // cache policy bits of the buffer loads
+#endif
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 template <typename Raw>
 __device__ __forceinline__ Raw buf_raw(__amdgpu_buffer_rsrc_t r, uint32_t off);
 template <>
 __device__ __forceinline__ uint4 buf_raw<uint4>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SPECV_RESID_CPOL);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 template <>
 __device__ __forceinline__ uint2 buf_raw<uint2>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, SPECV_RESID_CPOL);
   return make_uint2(v.x, v.y);
 }
 template <>
 __device__ __forceinline__ uint32_t buf_raw<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, SPECV_RESID_CPOL);
 }
 template <>
 __device__ __forceinline__ uint16_t buf_raw<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, SPECV_RESID_CPOL);
 }
 
 template <typename T, int VEC>
@@ -228,6 +231,25 @@ __device__ __forceinline__ void raw_to_f32(const typename RawVec<VEC * sizeof(T)
 // an early position (each position is reached only if all before it were
 // accepted): read last, its rows are the likeliest still to be in the
 // memory-side cache when rs_resid reads the decided row again.
+// The statistics pass reads every logit once: non-temporal loads.
+#ifndef SPECV_RS_NT
+#define SPECV_RS_NT 1
+#endif
+// A logit vector of the single streaming pass.
+template <typename R>
+__device__ __forceinline__ R stream_load(const R* p) {
+#if SPECV_RS_NT
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  if constexpr (sizeof(R) == 16) return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p)));
+  else if constexpr (sizeof(R) == 8) return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p)));
+  else if constexpr (sizeof(R) == 4) return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const unsigned int*>(p)));
+  else return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p)));
+#else
+  return *p;
+#endif
+}
+
 template <typename T, int VEC, int NIT, int SPW>
 __global__ __launch_bounds__(1024) void rs_stats(const T* __restrict__ tgt, const T* __restrict__ drf, int B, int G,
                                                  int V, int nseg, int cpr, float c32, RowPart* __restrict__ part,
@@ -264,7 +286,7 @@ __global__ __launch_bounds__(1024) void rs_stats(const T* __restrict__ tgt, cons
     for (int it = 0; it < NIT; ++it) {
       const int idx = (seg0 + k) * SEG + (it * kWave + lane) * VEC;
       ok[k][it] = idx < V;
-      if (ok[k][it]) raw[k][it] = *reinterpret_cast<const Raw*>(row + idx);
+      if (ok[k][it]) raw[k][it] = stream_load(reinterpret_cast<const Raw*>(row + idx));
     }
 #pragma unroll
   for (int k = 0; k < SPW; ++k) {
@@ -699,7 +721,7 @@ __global__ __launch_bounds__(1024) void gs_stats(const T* __restrict__ tgt, int 
     for (int it = 0; it < NIT; ++it) {
       const int idx = (seg0 + k) * SEG + (it * kWave + lane) * VEC;
       ok[k][it] = idx < V;
-      if (ok[k][it]) raw[k][it] = *reinterpret_cast<const Raw*>(row + idx);
+      if (ok[k][it]) raw[k][it] = stream_load(reinterpret_cast<const Raw*>(row + idx));
     }
 #pragma unroll
   for (int k = 0; k < SPW; ++k) {
