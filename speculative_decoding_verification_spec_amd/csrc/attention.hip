@@ -1301,30 +1301,57 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 split kernel: one wave per item holding RT row tiles
+// fp32 kernel: one wave per split of C keys holding RT row tiles.
+//   NWK = 0: one wave per workgroup and item; its state goes to the partial
+//            slots and attn_combine merges the splits.
+//   NWK > 0: one workgroup per (b, g, rg) whose wave w takes split w (at most
+//            NWK splits); the waves' states are merged through LDS and the
+//            workgroup writes the output itself.
 // ---------------------------------------------------------------------------
 
-template <int D, int RT>
-__global__ __launch_bounds__(64) void attn_split_f32(AttnArgs a) {
+// LDS of the in-workgroup merge: every wave's O rows and (max, sum).
+template <int D, int RT, int NWK>
+constexpr size_t f32_merge_lds() {
+  return (size_t)NWK * 16 * RT * (D * sizeof(float) + sizeof(ML));
+}
+
+template <int D, int RT, int NWK>
+__global__ __launch_bounds__(64 * (NWK > 0 ? NWK : 1)) void attn_split_f32(AttnArgs a) {
+  constexpr bool kWG = NWK > 0;
   constexpr int DS = D / 4;
   constexpr int DT = (D + 15) / 16;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   const int lr = lane & 15;
   const int lg = lane >> 4;
-  const Item it = decode_item(a);
+  Item it;
+  if constexpr (kWG) {
+    long item = blockIdx.x;
+    it.rg = (int)(item % a.RG);
+    item /= a.RG;
+    it.g = (int)(item % a.Hkv);
+    it.b = (int)(item / a.Hkv);
+    it.bg = (long)it.b * a.Hkv + it.g;
+    it.sp = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    it.id = 0;
+  } else {
+    it = decode_item(a);
+  }
   const int L = a.len[it.b];
-  if (L < 0 || L > a.hint) return;
+  const bool bad = L < 0 || L > a.hint;
+  if (!kWG && bad) return;
   const int Ltot = L + a.n_q;
   const int k0 = it.sp * a.C;
-  if (k0 >= Ltot) return;
-  const int k1 = min(k0 + a.C, Ltot);
+  if (!kWG && k0 >= Ltot) return;
+  // an idle wave of a workgroup (bad length, or no keys in its split) runs
+  // no blocks and merges as an empty state
+  const int k1 = (bad || k0 >= Ltot) ? k0 : min(k0 + a.C, Ltot);
   const float* q = static_cast<const float*>(a.q);
   const float* kn = static_cast<const float*>(a.kn);
   const float* vn = static_cast<const float*>(a.vn);
   const float* kc = static_cast<const float*>(a.kc);
   const float* vc = static_cast<const float*>(a.vc);
 
-  if (it.sp == 0 && it.rg == 0) append_rows<float, D>(a, it.bg, L, lane, kWave);
+  if (!bad && it.sp == 0 && it.rg == 0) append_rows<float, D>(a, it.bg, L, lane, kWave);
 
   float qf[RT][DS];
   int lim[RT];
@@ -1430,9 +1457,17 @@ __global__ __launch_bounds__(64) void attn_split_f32(AttnArgs a) {
     }
   }
 
-  const size_t item_id = it.id;
-  float* po = a.part_o + item_id * (16 * RT) * D;
-  ML* pml = a.part_ml + item_id * (16 * RT);
+  constexpr int ROWS = 16 * RT;
+  float* po;
+  ML* pml;
+  if constexpr (kWG) {
+    __shared__ __attribute__((aligned(16))) char merge_lds[f32_merge_lds<D, RT, NWK>()];
+    po = reinterpret_cast<float*>(merge_lds) + (size_t)it.sp * ROWS * D;
+    pml = reinterpret_cast<ML*>(merge_lds + (size_t)NWK * ROWS * D * sizeof(float)) + it.sp * ROWS;
+  } else {
+    po = a.part_o + it.id * ROWS * D;
+    pml = a.part_ml + it.id * ROWS;
+  }
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     float lt = lsum[r];
@@ -1444,6 +1479,41 @@ __global__ __launch_bounds__(64) void attn_split_f32(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) {
       const int d = 16 * dt + 4 * lg;
       if (d < D) *reinterpret_cast<f32x4*>(po + (size_t)row * D + d) = oacc[r][dt];
+    }
+  }
+  if constexpr (kWG) {
+    __syncthreads();
+    // merge the NWK states of each row (weights 2^(m_w - max)) and write out
+    const float* so = po - (size_t)it.sp * ROWS * D;
+    const ML* sml = pml - it.sp * ROWS;
+    const int row0 = it.rg * ROWS;
+    const int nrows = min(ROWS, a.M - row0);
+    float* out = static_cast<float*>(a.out);
+    auto out_ptr = [&](int row) {
+      const int m = row0 + row;
+      return out + (((size_t)it.b * a.Hq + it.g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D;
+    };
+    if (bad) {  // NaN rows, nothing else touched
+      for (int e = threadIdx.x; e < nrows * D; e += blockDim.x) out_ptr(e / D)[e % D] = __builtin_nanf("");
+      return;
+    }
+    constexpr int D4 = D / 4;
+    for (int e = threadIdx.x; e < nrows * D4; e += blockDim.x) {
+      const int row = e / D4, d = 4 * (e % D4);
+      float mx = neg_inf_f();
+#pragma unroll
+      for (int w = 0; w < NWK; ++w) mx = fmaxf(mx, sml[w * ROWS + row].m);
+      float den = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NWK; ++w) {
+        const ML ml = sml[w * ROWS + row];
+        const float wt = exp2_fast(ml.m - mx);
+        den += wt * ml.l;
+        acc += wt * *reinterpret_cast<const f32x4*>(so + ((size_t)w * ROWS + row) * D + d);
+      }
+      acc *= 1.f / den;
+      *reinterpret_cast<f32x4*>(out_ptr(row) + d) = acc;
     }
   }
 }
@@ -1737,10 +1807,27 @@ static hipError_t launch_bf16_d(const AttnArgs& a, hipStream_t s) {
   }
 }
 
+template <int D, int RT, int NWK>
+static hipError_t launch_f32_wg(const AttnArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((attn_split_f32<D, RT, NWK>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(64 * NWK), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+// Up to 8 splits per (b, g, rg) run as the waves of one workgroup, merged in
+// LDS (no partials in HBM, no second launch); more go through attn_combine.
 template <int D, int RT>
 static hipError_t launch_f32(const AttnArgs& a, hipStream_t s) {
+  constexpr size_t kMaxLds = 48 * 1024;
+  if (a.NSP <= 1) return launch_f32_wg<D, RT, 1>(a, s);
+  if (a.NSP <= 2) return launch_f32_wg<D, RT, 2>(a, s);
+  if (a.NSP <= 4) {
+    if constexpr (f32_merge_lds<D, RT, 4>() <= kMaxLds) return launch_f32_wg<D, RT, 4>(a, s);
+  } else if (a.NSP <= 8) {
+    if constexpr (f32_merge_lds<D, RT, 8>() <= kMaxLds) return launch_f32_wg<D, RT, 8>(a, s);
+  }
   const size_t items = (size_t)a.B * a.Hkv * a.RG * a.NSP;
-  hipLaunchKernelGGL((attn_split_f32<D, RT>), dim3((unsigned)items), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((attn_split_f32<D, RT, 0>), dim3((unsigned)items), dim3(64), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_combine<float, D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a, 0);

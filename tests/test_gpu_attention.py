@@ -108,6 +108,10 @@ def test_config5_full_size_sampled():
         ("f32", 3, 4, 4, 5, 24, [0, 384, 500]),
         ("f32", 2, 6, 3, 3, 32, [45, 9]),
         ("f32", 2, 8, 2, 2, 128, [130, 64]),
+        ("f32", 2, 16, 2, 5, 24, [200, 77]),     # 3 row tiles, two splits merged in one workgroup
+        ("f32", 2, 4, 4, 5, 24, [700, 1000]),    # 8 splits in one workgroup, idle waves for the shorter cache
+        ("f32", 1, 32, 8, 4, 64, [300]),         # GQA, 3 splits in a 4-wave workgroup
+        ("f32", 2, 4, 2, 5, 24, [3000, 1200]),   # 24 splits: partial slots and attn_combine
     ],
 )
 def test_shapes_and_edges(dtype, B, Hq, Hkv, n_q, D, lens):
@@ -149,15 +153,16 @@ def test_cache_full_to_capacity():
     _check(inp, out, kc, vc, "bf16")
 
 
-def test_length_beyond_hint_is_flagged_not_written():
-    cfg = W.get(4)
+@pytest.mark.parametrize("cid", [4, 3])
+def test_length_beyond_hint_is_flagged_not_written(cid):
+    cfg = W.get(cid)
     B, max_T = 2, 512
-    _case("bad-length", B=B)
+    _case("bad-length", B=B, config=cid)
     inp = W.attention_inputs(cfg, B=B, max_T=max_T, lens=[100, 400])
     out, kc, vc = _run_host(inp, hint=200)  # sequence 1 exceeds the hint
     assert np.all(np.isnan(_gpu.as_f64(out[1])))
     assert np.array_equal(kc[1], inp["k_cache"][1]) and np.array_equal(vc[1], inp["v_cache"][1])
-    _check({k: v[:1] for k, v in inp.items()}, out[:1], kc[:1], vc[:1], "bf16")
+    _check({k: v[:1] for k, v in inp.items()}, out[:1], kc[:1], vc[:1], cfg.dtype)
 
 
 def test_status_codes():
