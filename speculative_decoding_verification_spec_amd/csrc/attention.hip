@@ -1309,6 +1309,14 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
 //            workgroup writes the output itself.
 // ---------------------------------------------------------------------------
 
+// Blocks of K/V held per wave (one computed, the rest in flight): three at
+// the small head dimensions, where a block takes 28 registers, else two.
+#ifndef SPECV_F32_RING
+#define SPECV_F32_RING 3
+#endif
+template <int D>
+constexpr int kF32Ring = D <= 32 ? SPECV_F32_RING : 2;
+
 // LDS of the in-workgroup merge: every wave's O rows and (max, sum).
 template <int D, int RT, int NWK>
 constexpr size_t f32_merge_lds() {
@@ -1400,12 +1408,8 @@ __global__ __launch_bounds__(64 * (NWK > 0 ? NWK : 1)) void attn_split_f32(AttnA
         }
       }
   };
-  float kf[2][DS], vf[8][DT];
-  if (k0 < k1) load_kv(k0, kf, vf);
-  for (int kb = k0; kb < k1; kb += KB) {
-    float kf2[2][DS], vf2[8][DT];
-    const bool more = kb + KB < k1;
-    if (more) load_kv(kb + KB, kf2, vf2);
+  // Block j's products, from ring slot kf/vf.
+  auto block = [&](int kb, const float (&kf)[2][DS], const float (&vf)[8][DT]) {
     float sc[RT][8];
 #pragma unroll
     for (int r = 0; r < RT; ++r)
@@ -1445,15 +1449,25 @@ __global__ __launch_bounds__(64 * (NWK > 0 ? NWK : 1)) void attn_split_f32(AttnA
           for (int r = 0; r < RT; ++r)
             oacc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf[4 * kt + jj][dt], sc[r][4 * kt + jj], oacc[r][dt],
                                                                0, 0, 0);
-    if (more) {
+  };
+  // A ring of NR blocks: block j + NR - 1 is loaded into the slot block j - 1
+  // used before block j is computed, so NR - 1 blocks are in flight during
+  // the products (the ring index is a compile-time constant).
+  constexpr int NR = kF32Ring<D>;
+  float kf[NR][2][DS], vf[NR][8][DT];
+  const int nblk = (k1 - k0 + KB - 1) / KB;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+  for (int q = 0; q < NR - 1; ++q)
+    if (q < nblk) load_kv(k0 + q * KB, kf[q], vf[q]);
+  for (int j0 = 0; j0 < nblk; j0 += NR) {
 #pragma unroll
-        for (int s2 = 0; s2 < DS; ++s2) kf[kt][s2] = kf2[kt][s2];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) vf[e][dt] = vf2[e][dt];
+    for (int q = 0; q < NR; ++q) {
+      const int j = j0 + q;
+      if (j < nblk) {  // uniform
+        const int nxt = (q + NR - 1) % NR;  // constant once the q loop is unrolled
+        if (j + NR - 1 < nblk) load_kv(k0 + (j + NR - 1) * KB, kf[nxt], vf[nxt]);
+        block(k0 + j * KB, kf[q], vf[q]);
+      }
     }
   }
 
