@@ -1681,6 +1681,13 @@ constexpr int kStages = SPECV_ATTN_STAGES;  // LDS stages; blocks in flight per 
 #ifndef SPECV_STREAM_MAX_WG
 #define SPECV_STREAM_MAX_WG 768
 #endif
+// Workgroups per CU of the bf16 stream kernel.  Its 2-wave build fits 3 per
+// CU but ran faster at 2 (fewer, longer shares: 78 -> 75 us at B = 32 with
+// 1-4K-key caches; 1 and 1.5 per CU were slower everywhere).  The int8
+// kernel keeps 3 (87 us against 109 us at 2).
+#ifndef SPECV_BF16_PER_CU
+#define SPECV_BF16_PER_CU 2
+#endif
 constexpr int kStreamMaxWG = SPECV_STREAM_MAX_WG;
 
 // Sizes the stream scheme handles: every workgroup scans the B lengths, and
@@ -1723,7 +1730,7 @@ static StreamPlan stream_plan(int B, int Hkv, int RG, int RT, int n_q, int D, in
 // SIMDs of a CU: a workgroup of NW waves puts ceil(NW / 4) on one SIMD, which
 // holds 512 / VGPRs waves.  Cached per device.
 template <typename K>
-static int stream_workgroups(K kernel, int NW) {
+static int stream_workgroups(K kernel, int NW, int max_per_cu) {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -1745,7 +1752,7 @@ static int stream_workgroups(K kernel, int NW) {
   // registers and LDS; a build that used fewer registers and launched 3 per
   // CU left a third of them waiting for a slot).
   const int by_slots = NW <= 4 ? 4 * per_simd / NW : std::min(2, per_simd / ((NW + 3) / 4));
-  int k = std::max(1, std::min(occ, by_slots));
+  int k = std::max(1, std::min(std::min(occ, by_slots), max_per_cu));
   const int P = std::min(kStreamMaxWG, cus * k);
   if (slot) slot->store(P, std::memory_order_relaxed);
   return P;
@@ -1754,7 +1761,7 @@ static int stream_workgroups(K kernel, int NW) {
 template <int D, int NW, int PG>
 static hipError_t launch_stream(const AttnArgs& a0, hipStream_t s) {
   AttnArgs a = a0;
-  a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG>, NW);
+  a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG>, NW, SPECV_BF16_PER_CU);
   hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a, a.table);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1768,7 +1775,7 @@ static hipError_t launch_i8(const AttnArgs& a0, hipStream_t s) {
   hipLaunchKernelGGL((quant_new_rows<D>), dim3((unsigned)((size_t)a.B * a.Hkv)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.P = stream_workgroups(attn_stream_i8<D, NW, SPECV_I8_STAGES>, NW);
+  a.P = stream_workgroups(attn_stream_i8<D, NW, SPECV_I8_STAGES>, NW, 3);
   hipLaunchKernelGGL((attn_stream_i8<D, NW, SPECV_I8_STAGES>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
