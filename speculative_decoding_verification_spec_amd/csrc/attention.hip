@@ -84,6 +84,7 @@ struct AttnArgs {
   float* part_o;
   ML* part_ml;
   int* pre;  // stream scheme: [B + 1] blocks per slab before sequence b
+  uint32_t* scnt;  // stream scheme merged in the kernel: pieces finished per slab
   int B, Hq, Hkv, n_q, G, M, RG, RT, NSP, C, max_T, hint;
   int P, MINB, JP;  // stream scheme: workgroups, minimum share, partial slots per slab
   // Paged cache: kc / vc are [Hkv][num_pages][page][D]; table[b * max_blocks + i]
@@ -287,13 +288,26 @@ __device__ __forceinline__ float group_sum(float v) {
     else return v2s; \
   };
 
+// Device-scope (write-through) stores and loads of piece partials that
+// another workgroup merges within the same launch.
+__device__ __forceinline__ void co_store2(float* p, float x, float y) {
+  const unsigned long long v = (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 co_load2(const float* p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
 // One piece of one (b, g, rg): keys [k0, k1) of sequence b (length L, valid),
 // rows of row group rg of KV head g.  Writes the normalised output when the
 // piece is the whole of (b, g, rg) (whole), else its (max, sum, unnormalised
 // output) at partial slot `slot`.  append: also copy the n_q new rows of
 // (b, g) into the cache (A1).  kbuf / vbuf map a stage index to its LDS
 // objects.  Every wave of the workgroup calls it with the same arguments.
-template <int D, int NW, int NST, int PG, typename KBuf, typename VBuf>
+// CO: partials through device-scope stores (merged within the launch).
+template <int D, int NW, int NST, int PG, bool CO = false, typename KBuf, typename VBuf>
 __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vbuf, int b, int g, int rg, int L,
                                            int k0, int k1, bool whole, size_t slot, bool append,
                                            const int32_t* __restrict__ table = nullptr) {
@@ -352,9 +366,14 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
         }
       } else {
         const int row = 16 * wave + lr;
-        if (lg == 0) a.part_ml[slot * (16 * NW) + row] = ML{qnan, qnan};
         float* po = a.part_o + slot * (16 * NW) * D + (size_t)row * D;
-        for (int d = lg; d < D; d += 4) po[d] = qnan;
+        if constexpr (CO) {
+          if (lg == 0) co_store2(reinterpret_cast<float*>(a.part_ml + slot * (16 * NW) + row), qnan, qnan);
+          for (int d = 2 * lg; d < D; d += 8) co_store2(po + d, qnan, qnan);
+        } else {
+          if (lg == 0) a.part_ml[slot * (16 * NW) + row] = ML{qnan, qnan};
+          for (int d = lg; d < D; d += 4) po[d] = qnan;
+        }
       }
       return;
     }
@@ -618,9 +637,19 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
     return;
   }
   float* po = a.part_o + slot * (16 * NW) * D;
-  if (lg == 0) a.part_ml[slot * (16 * NW) + row] = ML{mrow, lt};
+  if constexpr (CO) {
+    if (lg == 0) co_store2(reinterpret_cast<float*>(a.part_ml + slot * (16 * NW) + row), mrow, lt);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[dt];
+    for (int dt = 0; dt < DT; ++dt) {
+      float* pd = po + (size_t)row * D + 16 * dt + 4 * lg;
+      co_store2(pd, oacc[dt][0], oacc[dt][1]);
+      co_store2(pd + 2, oacc[dt][2], oacc[dt][3]);
+    }
+  } else {
+    if (lg == 0) a.part_ml[slot * (16 * NW) + row] = ML{mrow, lt};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[dt];
+  }
 }
 
 template <int D, int NW, int NST>
@@ -682,7 +711,8 @@ __device__ __forceinline__ long long stream_share(const AttnArgs& a, long long W
 // the combine.
 // The stream scheme's walk, shared by the stream kernels: find this
 // workgroup's share of the slabs' key blocks and call
-// piece(b, g, rg, L, k0, k1, whole, slot, append) for every slab piece in it,
+// piece(b, g, rg, L, k0, k1, whole, slot, append, np) for every slab piece in it
+// (np: the number of pieces the slab is cut into),
 // in order (every wave of the workgroup makes the same calls; a workgroup
 // barrier separates consecutive pieces).
 template <typename Piece>
@@ -766,7 +796,8 @@ __device__ __forceinline__ void stream_walk(const AttnArgs& a, Piece&& piece) {
       first = false;
       const int L = ufl(a.len[b]);
       const size_t slot = (((size_t)b * a.Hkv + g) * a.RG + rg) * a.JP + (size_t)j;
-      piece(b, g, rg, L, off * KB, min(end * KB, L + a.n_q), whole, slot, off == 0 && rg == 0);
+      const int np = ufl((int)min((S0 + nbb - 1) / share - S0 / share + 1, (long long)a.JP));  // pieces of the slab
+      piece(b, g, rg, L, off * KB, min(end * KB, L + a.n_q), whole, slot, off == 0 && rg == 0, np);
     }
     x = uniform64(x + take);
     off = 0;
@@ -779,14 +810,100 @@ __device__ __forceinline__ void stream_walk(const AttnArgs& a, Piece&& piece) {
   }
 }
 
-template <int D, int NW, int NST, int PG>
+// The piece-merge hand-off inside the stream launch: after a workgroup's
+// partial for one piece of a slab (device-scope stores, waited for), it
+// counts itself in scnt[slab] (zeroed by attn_stream_prep); the workgroup
+// whose add completes the count merges the slab's np partials (device-scope
+// loads) and writes the output, as attn_combine_stream would.  Every wave
+// calls it.
+template <int D, int NW>
+__device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, int rg, size_t slot, int np) {
+  __shared__ int sh_last;
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  const size_t slab = slot / (size_t)a.JP;
+  if (threadIdx.x == 0)
+    sh_last = __hip_atomic_fetch_add(a.scnt + slab, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(np - 1);
+  __syncthreads();
+  if (!sh_last) return;  // uniform over the workgroup
+  constexpr int ROWS = 16 * NW, D4 = D / 4;
+  const int row0 = rg * ROWS;
+  const int nrows = min(ROWS, a.M - row0);
+  const size_t base = slab * (size_t)a.JP;
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  for (int e = threadIdx.x; e < nrows * D4; e += 64 * NW) {
+    const int row = e / D4, d = 4 * (e % D4);
+    float mx = neg_inf_f(), den = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < np; j0 += 4) {
+      float2 ml[4];
+      f32x4 po[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool in = j0 + t < np;
+        const size_t pj = (base + j0 + t) * ROWS + row;
+        ml[t] = in ? co_load2(reinterpret_cast<const float*>(a.part_ml + pj)) : make_float2(neg_inf_f(), 0.f);
+        const float2 lo = in ? co_load2(a.part_o + pj * D + d) : make_float2(0.f, 0.f);
+        const float2 hi = in ? co_load2(a.part_o + pj * D + d + 2) : make_float2(0.f, 0.f);
+        po[t] = f32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      const float mc = fmaxf(fmaxf(ml[0].x, ml[1].x), fmaxf(ml[2].x, ml[3].x));
+      const float mn = fmaxf(mx, mc);
+      if (mn == neg_inf_f()) continue;  // no visible key in these pieces yet
+      const float r = exp2_fast(mx - mn);
+      den *= r;
+      acc *= r;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float w = exp2_fast(ml[t].x - mn);
+        den += w * ml[t].y;
+        acc += w * po[t];
+      }
+      mx = mn;
+    }
+    acc *= 1.f / den;
+    const int m = row0 + row;
+    uint2 pk;
+    pk.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
+    pk.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+    *reinterpret_cast<uint2*>(out + (((size_t)b * a.Hq + g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D + d) = pk;
+  }
+}
+
+// MERGE: the pieces of a slab are merged by the last of its workgroups
+// (stream_merge) instead of by attn_combine_stream.
+template <int D, int NW, int NST, int PG, bool MERGE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
 void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
   using LY = BfLayout<D>;
   SPECV_BF16_STAGE_LDS
-  stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append) {
-    bf16_piece<D, NW, NST, PG>(a, kbuf, vbuf, b, g, rg, L, k0, k1, whole, slot, append, table);
+  stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append, int np) {
+    bf16_piece<D, NW, NST, PG, MERGE>(a, kbuf, vbuf, b, g, rg, L, k0, k1, whole, slot, append, table);
+    if constexpr (MERGE) {
+      if (!whole) stream_merge<D, NW>(a, b, g, rg, slot, np);
+    }
   });
+}
+
+// Before a merging stream launch: zero the per-slab counters, and write NaN
+// rows for the slabs of a rejected length (the stream walk skips them).
+template <int D>
+__global__ __launch_bounds__(256) void attn_stream_prep(AttnArgs a) {
+  const long slabs = (long)a.B * a.Hkv * a.RG;
+  for (long sl = (long)blockIdx.x * blockDim.x + threadIdx.x; sl < slabs; sl += (long)gridDim.x * blockDim.x) {
+    a.scnt[sl] = 0u;
+    const int rg = (int)(sl % a.RG);
+    const int g = (int)((sl / a.RG) % a.Hkv);
+    const int b = (int)(sl / ((long)a.RG * a.Hkv));
+    if (slab_blocks(a, b) != 0) continue;
+    const int rows = 16 * a.RT, row0 = rg * rows, nrows = min(rows, a.M - row0);
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    for (int row = 0; row < nrows; ++row) {
+      const int m = row0 + row;
+      uint16_t* o = out + (((size_t)b * a.Hq + g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D;
+      for (int d = 0; d < D; ++d) o[d] = (uint16_t)0x7fc0;
+    }
+  }
 }
 
 
@@ -1228,7 +1345,7 @@ template <int D, int NW, int NST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
 void attn_stream_i8(AttnArgs a) {
   SPECV_I8_STAGE_LDS
-  stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append) {
+  stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append, int) {
     i8_piece<D, NW, NST>(a, qkbuf, qvbuf, scbuf, cvk, cvv, scv, nsk, nsv, b, g, rg, L, k0, k1, whole, slot, append);
   });
 }
@@ -1685,6 +1802,12 @@ constexpr int kStages = SPECV_ATTN_STAGES;  // LDS stages; blocks in flight per 
 // CU but ran faster at 2 (fewer, longer shares: 78 -> 75 us at B = 32 with
 // 1-4K-key caches; 1 and 1.5 per CU were slower everywhere).  The int8
 // kernel keeps 3 (87 us against 109 us at 2).
+#ifndef SPECV_STREAM_MERGE
+#define SPECV_STREAM_MERGE 1  // allow merging a slab's pieces inside the bf16 stream launch
+#endif
+#ifndef SPECV_MERGE_MIN_SHARE
+#define SPECV_MERGE_MIN_SHARE 256  // blocks per workgroup from which the merge is used
+#endif
 #ifndef SPECV_BF16_PER_CU
 #define SPECV_BF16_PER_CU 2
 #endif
@@ -1699,7 +1822,7 @@ static bool stream_ok(spec_dtype_t dt, int B, int Hkv, int RG, int n_q, int hint
 
 struct StreamPlan {
   int JP, MINB;
-  size_t off_o, off_ml, off_pre, total;
+  size_t off_o, off_ml, off_pre, off_cnt, total;
 };
 
 static StreamPlan stream_plan(int B, int Hkv, int RG, int RT, int n_q, int D, int hint) {
@@ -1720,6 +1843,8 @@ static StreamPlan stream_plan(int B, int Hkv, int RG, int RT, int n_q, int D, in
   off = align256(off + sizeof(ML) * slots * 16 * RT);
   p.off_pre = off;
   off = align256(off + sizeof(int) * ((size_t)B + 1));
+  p.off_cnt = off;
+  off = align256(off + sizeof(uint32_t) * (size_t)slabs);
   p.total = off;
   return p;
 }
@@ -1758,15 +1883,40 @@ static int stream_workgroups(K kernel, int NW, int max_per_cu) {
   return P;
 }
 
-template <int D, int NW, int PG>
-static hipError_t launch_stream(const AttnArgs& a0, hipStream_t s) {
+template <int D, int NW, int PG, bool kMerge>
+static hipError_t launch_stream_as(const AttnArgs& a0, hipStream_t s) {
   AttnArgs a = a0;
-  a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG>, NW, SPECV_BF16_PER_CU);
-  hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a, a.table);
+  const size_t slabs = (size_t)a.B * a.Hkv * a.RG;
+  if constexpr (kMerge) {
+    hipLaunchKernelGGL((attn_stream_prep<D>), dim3((unsigned)std::min<size_t>((slabs + 255) / 256, 1024)), dim3(256), 0,
+                       s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG, kMerge>, NW, SPECV_BF16_PER_CU);
+  hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG, kMerge>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a,
+                     a.table);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
+  if (e != hipSuccess || kMerge) return e;
+  hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)slabs), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+// The in-launch merge costs every workgroup a few microseconds per piece
+// (the write-through partials, the count, the last one's merge) and the
+// counters a launch of their own; the combine launch costs a fixed time that
+// grows with the slab count.  Merge when a workgroup's share can reach
+// SPECV_MERGE_MIN_SHARE blocks (measured: 32K-key caches, B = 256: 3.36 ->
+// 3.32 ms; 1-4K-key caches, B = 32: 74 -> 87 us, so those combine).
+template <int D, int NW, int PG>
+static hipError_t launch_stream(const AttnArgs& a, hipStream_t s) {
+  if constexpr (SPECV_STREAM_MERGE != 0) {
+    const long nbmax = ((long)a.hint + a.n_q + KB - 1) / KB;
+    const long wmax = (long)a.B * a.Hkv * a.RG * nbmax;
+    const int P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG, true>, NW, SPECV_BF16_PER_CU);
+    if (wmax >= (long)SPECV_MERGE_MIN_SHARE * P) return launch_stream_as<D, NW, PG, true>(a, s);
+  }
+  return launch_stream_as<D, NW, PG, false>(a, s);
 }
 
 template <int D, int NW>
@@ -1934,6 +2084,7 @@ static spec_status_t verify_attention(const void* q, const void* k_new, const vo
   a.part_o = reinterpret_cast<float*>(ws + (use_stream ? sp.off_o : p.off_o));
   a.part_ml = reinterpret_cast<ML*>(ws + (use_stream ? sp.off_ml : p.off_ml));
   a.pre = use_stream ? reinterpret_cast<int*>(ws + sp.off_pre) : nullptr;
+  a.scnt = use_stream ? reinterpret_cast<uint32_t*>(ws + sp.off_cnt) : nullptr;
   a.P = 0;
   a.MINB = sp.MINB;
   a.JP = sp.JP;

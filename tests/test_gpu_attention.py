@@ -98,6 +98,32 @@ def test_config5_full_size_sampled():
     _check(before, got, kc, vc, "bf16", seqs=range(len(seqs)))
 
 
+def test_long_caches_merged_in_launch():
+    """Shares long enough that the bf16 stream launch merges each slab's pieces
+    itself (its last workgroup), with empty, ragged, full-hint and rejected
+    lengths in one batch."""
+    cfg = W.Config(95, "merge", B=20, gamma=8, V=1, dtype="bf16", Hq=64, Hkv=8, D=128, L=(8192, 32768),
+                   max_T=32800)
+    hint = 32768
+    _case("merge-in-launch", B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, hint=hint)
+    d = W.attention_inputs_device(cfg, "cuda")
+    for b, L in ((1, 0), (2, 31), (3, hint + 1), (4, hint)):
+        d["lens"][b] = L
+    seqs = [0, 1, 2, 4, 19]
+    before = {k: _gpu.to_host(d[k][seqs]) for k in ("q", "k_new", "v_new", "k_cache", "v_cache", "lens")}
+    k3 = _gpu.to_host(d["k_cache"][3])
+    out = sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], hint)
+    torch.cuda.synchronize()
+    assert np.all(np.isnan(_gpu.as_f64(_gpu.to_host(out[3]))))  # length above the hint: flagged
+    assert np.array_equal(_gpu.to_host(d["k_cache"][3]), k3)
+    got = _gpu.to_host(out[seqs])
+    kc = _gpu.to_host(d["k_cache"][seqs])
+    vc = _gpu.to_host(d["v_cache"][seqs])
+    del d
+    torch.cuda.empty_cache()
+    _check(before, got, kc, vc, "bf16", seqs=range(len(seqs)))
+
+
 @pytest.mark.parametrize(
     "dtype,B,Hq,Hkv,n_q,D,lens",
     [
