@@ -442,9 +442,10 @@ def main():
             "traffic": None if traffic is None else traffic["bytes_per_call"],
             "kernel": ("spec_verify_attention_int8: quant_new_rows + attn_stream_i8 + attn_combine_stream, one call"
                        if args.kv == "int8" else
-                       "spec_verify_attention: attn_stream_bf16 + attn_combine_stream, one call"
+                       "spec_verify_attention: attn_stream_bf16 with attn_combine_stream or, for long shares, "
+                       "attn_stream_prep, one call"
                        if cfg.dtype == "bf16" and cfg.B <= 1024
-                       else f"spec_verify_attention: attn_split_{cfg.dtype} + attn_combine, one call"),
+                       else f"spec_verify_attention: attn_split_{cfg.dtype} (+ attn_combine past 8 splits), one call"),
             "algorithmic_bytes": att_b,
             "avg_ms": att_ms,
         },
