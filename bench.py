@@ -38,7 +38,7 @@ METRIC = "verified draft positions/sec + % of MI355X HBM peak (sampler, verify a
 WORKLOADS = {"c3": 3, "c4": 4, "c5": 5}
 
 # Sources of the verify-attention kernels; the HBM byte counts stored under
-# profiles/ are used only while these files are unchanged.
+# profiles/ are used only while their code is unchanged.
 ATTN_SOURCES = (
     "speculative_decoding_verification_spec_amd/csrc/attention.hip",
     "speculative_decoding_verification_spec_amd/csrc/spec_common.h",
@@ -46,10 +46,15 @@ ATTN_SOURCES = (
 
 
 def attn_source_hash():
+    """Hash of the sources' code: every line with its // comment and trailing
+    blanks removed, blank lines dropped (an edit to comments alone keeps it)."""
     h = hashlib.sha256()
     for rel in ATTN_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -13,11 +13,15 @@
 // read the same K/V tiles (the GQA reuse).  A piece of a slab walks a range
 // of its keys in blocks of 32 with an online softmax and leaves its (max,
 // sum, unnormalised output) in the workspace, or writes the output directly
-// when it is the whole slab; a combine kernel merges the pieces.
+// when it is the whole slab; the pieces are merged afterwards.
 //   bf16 (B <= 1024): the stream scheme.  One workgroup per resident slot;
 //   the slabs' key blocks are laid end to end and cut into equal shares, one
 //   per workgroup, so every workgroup has the same work whatever the lengths.
-//   fp32, and bf16 with B > 1024: fixed splits of C keys, one workgroup each.
+//   Long shares merge each slab's pieces inside the launch (the last of its
+//   workgroups to finish); short ones in a combine launch.
+//   fp32: fixed splits of C keys, one wave each; up to 8 splits of a slab
+//   are the waves of one workgroup and merge in LDS, more go through a
+//   combine launch.  bf16 with B > 1024: fixed splits and a combine launch.
 //
 // MFMA layouts (gfx950, wave64, checked on the hardware).  For
 // v_mfma_f32_16x16x32_bf16 lane l holds A[l%16][8(l/16) .. +7],
@@ -44,8 +48,8 @@
 // global side of the copy, which keeps every 16 lanes of a copy on one
 // contiguous row.
 //
-// fp32 kernel.  One wave per work item holding every row tile; one key per
-// lane per MFMA, so V is read straight from memory.
+// fp32 kernel.  One wave per split holding every row tile; one key per lane
+// per MFMA, so V is read straight from memory.
 //
 // Keys [0, L_b) come from the cache, keys [L_b, L_b + n_q) from k_new/v_new
 // directly (so the append in the same launch is never read back), and keys at
