@@ -606,7 +606,7 @@ def model_bench(args, torch, sv, dev):
                                f"cached prefix {prefix}, gamma={gamma}, T={T}"},
         "roofline": {"bound": "hbm", "achieved": fwd_bytes / (fwd_ms * 1e-3) / 1e9, "peak": 8000.0, "unit": "GB/s",
                      "frac": fwd_bytes / (fwd_ms * 1e-3) / 8e12, "traffic": None,
-                     "kernel": "spec_verify_forward (target, gamma+1 tokens): 14 launches, launch-latency bound",
+                     "kernel": "spec_verify_forward (target, gamma+1 tokens): 9 launches, launch-latency bound",
                      "algorithmic_bytes": fwd_bytes, "avg_ms": fwd_ms},
         "parts": {
             "verify_forward": {"ms": fwd_ms, "positions/s": B * gamma / (fwd_ms * 1e-3)},

@@ -12,18 +12,22 @@
 // listing leaves LayerNorm and GELU undefined: GPT-2's readings are taken
 // (population variance, eps 1e-5; GELU in its tanh form).
 //
-// Per layer, for the M = B*n new rows:
-//   gemm<LN, QKV split>    h = LN1(x); q | k_new | v_new = h wqkv, written
-//                          head-major ([B][H][n][D]) for the attention
+// Launches, for the M = B*n new rows, 16 rows per workgroup with every
+// intermediate of a row block in LDS:
+//   embed_qkv              x = wte[token] + wpe[position]; then layer 0's
+//                          q | k_new | v_new = LN1(x) wqkv, written head-major
+//                          ([B][H][n][D]) for the attention
+// and per layer:
 //   spec_verify_attention  appends k_new, v_new at [p0, p0+n) of the layer's
 //                          cache and attends (the library's fp32 kernels)
 //   block_mlp              x += O wo (reading O [B][H][n][D] as [M][C]);
-//                          x += gelu(LN2(x) w1 + b1) w2 + b2, 16 rows per
-//                          workgroup with the intermediates in LDS
-// then gemm<LN> logits = LNf(x) wout.  The products are fp32 matrix-core
-// tiles (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32 sums); the
-// LayerNorms, biases, GELU, residual adds and the head-major q/k/v scatter
-// are fused around them.
+//                          x += gelu(LN2(x) w1 + b1) w2 + b2; then the next
+//                          layer's q | k_new | v_new, or after the last layer
+//                          logits = LNf(x) wout (a launch of its own, gemm,
+//                          above kFusedVocabMax tokens)
+// The products are fp32 matrix-core tiles (v_mfma_f32_16x16x4_f32: exact
+// fp32 products, fp32 sums); the LayerNorms, biases, GELU, residual adds and
+// the head-major q/k/v scatter are fused around them.
 #include <math.h>
 #include <stdint.h>
 
@@ -100,21 +104,8 @@ static bool model_layout(const spec_model_t* m, ModelLayout* o) {
 
 // x[b n + i][:] = wte[tok[b][i]][:] + wpe[lens[b] + i][:]; an out-of-range
 // token or position writes NaN rows (which then reach the logits).
-__global__ __launch_bounds__(256) void embed_kernel(const float* __restrict__ wte, const float* __restrict__ wpe,
-                                                    const int32_t* __restrict__ tok,
-                                                    const int32_t* __restrict__ lens, float* __restrict__ x, int n,
-                                                    int C, int V, int T) {
-  const int row = blockIdx.x;
-  const int b = row / n, i = row - b * n;
-  const int t = tok[row];
-  const long pos = (long)lens[b] + i;
-  const bool ok = t >= 0 && t < V && pos >= 0 && pos < T;
-  for (int c = threadIdx.x; c < C; c += blockDim.x)
-    x[(size_t)row * C + c] = ok ? wte[(size_t)t * C + c] + wpe[(size_t)pos * C + c] : __builtin_nanf("");
-}
-
-enum { O_ROWS = 0, O_QKV = 1 };      // out: token-major [M][N], or q | k | v head-major
 constexpr int kBM = 32, kBN = 32;    // output tile: 4 waves, 16 x 16 each
+constexpr int kFusedVocabMax = 1024;  // vocabularies projected inside the last layer's launch
 constexpr int kPad = 4;              // floats of padding per staged A row (LDS banks)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -123,11 +114,8 @@ struct GemmArgs {
   const float* W;      // [K][N]
   const float* ln_g;   // LN gain / bias over K
   const float* ln_b;
-  float* out;          // O_ROWS: [M][N]
-  float* q;            // O_QKV: three [B][H][n][D] outputs, N = 3 H D
-  float* kn;
-  float* vn;
-  int M, N, K, n, H, D;
+  float* out;          // [M][N]
+  int M, N, K;
 };
 
 __device__ __forceinline__ float gelu_tanh(float v) {
@@ -189,7 +177,6 @@ __device__ __forceinline__ f32x4 mfma_tile16(const float* A, int KP, int K, __am
 // padded by kPad floats), and LayerNorm-ed in place.  Wave w owns the
 // 16 x 16 sub-tile (rows 16 (w / 2), columns 16 (w % 2)), computed by
 // mfma_tile16; W is read from L2 (it is small and shared by every row tile).
-template <int OMODE>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   extern __shared__ float As[];  // [kBM][K + kPad]
   const int lane = threadIdx.x & (kWave - 1);
@@ -229,25 +216,114 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + 16 * wr + 4 * lgp + i;
     if (m >= g.M) break;
-    const float v = acc[i];
-    if constexpr (OMODE == O_ROWS) {
-      g.out[(size_t)m * g.N + col] = v;
-    } else {
-      const int C = g.H * g.D;
-      const int part = col / C, c = col - part * C, h = c / g.D, d = c - h * g.D;
-      const int b = m / g.n, i2 = m - b * g.n;
-      float* dst = part == 0 ? g.q : (part == 1 ? g.kn : g.vn);
-      dst[(((size_t)b * g.H + h) * g.n + i2) * g.D + d] = v;
+    g.out[(size_t)m * g.N + col] = acc[i];
+  }
+}
+
+static hipError_t gemm(const GemmArgs& g, hipStream_t s) {
+  const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
+  hipLaunchKernelGGL(gemm_kernel, grid, dim3(256),
+                     sizeof(float) * kBM * (g.K + kPad), s, g);
+  return hipGetLastError();
+}
+
+// The product that follows a block of 16 rows held in LDS, by 8 waves:
+// LayerNorm of the rows (ln_g, ln_b) into Hs, then
+//   NEXT_QKV:    q | k_new | v_new = Hs wqkv (the next layer's), written
+//                head-major ([B][H][n][D]) for its attention;
+//   NEXT_LOGITS: logits = Hs wout ([M][V]);
+//   NEXT_NONE:   nothing (the vocabulary projection runs as its own launch).
+enum { NEXT_NONE = 0, NEXT_QKV = 1, NEXT_LOGITS = 2 };
+struct NextArgs {
+  int mode;
+  const float *ln_g, *ln_b, *W;  // W: [C][N]
+  float *q, *kn, *vn;            // NEXT_QKV
+  float* logits;                 // NEXT_LOGITS
+  int N;                         // 3C or V
+};
+
+// LayerNorm of 16 rows (Rs -> Hs, row stride CP), two rows per wave: the
+// mean, then the variance about it.
+__device__ __forceinline__ void rows_ln16(const float* Rs, float* Hs, int CP, int C, const float* __restrict__ ln_g,
+                                          const float* __restrict__ ln_b, int wave, int lane) {
+  for (int r = 2 * wave; r < 2 * wave + 2; ++r) {
+    float s = 0.f;
+    for (int k = lane; k < C; k += kWave) s += Rs[r * CP + k];
+    const float mu = wave_sum(s) / (float)C;
+    float v = 0.f;
+    for (int k = lane; k < C; k += kWave) {
+      const float d = Rs[r * CP + k] - mu;
+      v += d * d;
+    }
+    const float rstd = 1.f / sqrtf(wave_sum(v) / (float)C + kLnEps);
+    for (int k = lane; k < C; k += kWave) Hs[r * CP + k] = (Rs[r * CP + k] - mu) * rstd * ln_g[k] + ln_b[k];
+  }
+}
+
+// Rows [m0, m0 + 16) of Rs through the LayerNorm and product of nx.  Every
+// thread of the 8-wave workgroup calls it; it starts with a barrier.
+__device__ __forceinline__ void next_product(const NextArgs& nx, const float* Rs, float* Hs, int CP, int C, int m0,
+                                             int M, int n, int H, int D, int wave, int lane) {
+  if (nx.mode == NEXT_NONE) return;  // uniform
+  __syncthreads();
+  rows_ln16(Rs, Hs, CP, C, nx.ln_g, nx.ln_b, wave, lane);
+  __syncthreads();
+  const int lr = lane & 15, lgp = lane >> 4;
+  const __amdgpu_buffer_rsrc_t wr = w_rsrc(nx.W, C, nx.N);
+  for (int ct = wave; ct < (nx.N + 15) / 16; ct += 8) {
+    const int col = 16 * ct + lr;
+    const bool ok = col < nx.N;
+    const f32x4 acc = mfma_tile16(Hs, CP, C, wr, nx.N, col, ok, lr, lgp);
+    if (!ok) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + 4 * lgp + i;
+      if (m >= M) break;
+      if (nx.mode == NEXT_LOGITS) {
+        nx.logits[(size_t)m * nx.N + col] = acc[i];
+      } else {
+        const int part = col / C, c = col - part * C, h = c / D, d = c - h * D;
+        const int b = m / n, i2 = m - b * n;
+        float* dst = part == 0 ? nx.q : (part == 1 ? nx.kn : nx.vn);
+        dst[(((size_t)b * H + h) * n + i2) * D + d] = acc[i];
+      }
     }
   }
 }
 
-template <int OMODE>
-static hipError_t gemm(const GemmArgs& g, hipStream_t s) {
-  const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
-  hipLaunchKernelGGL((gemm_kernel<OMODE>), grid, dim3(256),
-                     sizeof(float) * kBM * (g.K + kPad), s, g);
-  return hipGetLastError();
+// Token and position embeddings of 16 rows per workgroup of 8 waves (NaN
+// rows for a token or position out of range), then the first layer's
+// LayerNorm and q/k/v product (next_product).
+struct EmbArgs {
+  const float *wte, *wpe;
+  const int32_t* tok;   // [M]
+  const int32_t* lens;  // [B]
+  float* x;             // [M][C]
+  NextArgs nx;
+  int M, n, H, D, C, V, T;
+};
+
+__global__ __launch_bounds__(512) void embed_qkv_kernel(EmbArgs g) {
+  extern __shared__ float sm[];
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int C = g.C, CP = C + kPad;
+  float* Rs = sm;            // [16][CP]
+  float* Hs = Rs + 16 * CP;  // [16][CP]
+  const int m0 = blockIdx.x * 16;
+  for (int e = threadIdx.x; e < 16 * C; e += blockDim.x) {
+    const int r = e / C, k = e - r * C, m = m0 + r;
+    float v = 0.f;
+    if (m < g.M) {
+      const int b = m / g.n, i = m - b * g.n;
+      const int t = g.tok[m];
+      const long pos = (long)g.lens[b] + i;
+      const bool ok = t >= 0 && t < g.V && pos >= 0 && pos < g.T;
+      v = ok ? g.wte[(size_t)t * C + k] + g.wpe[(size_t)pos * C + k] : __builtin_nanf("");
+      g.x[(size_t)m * C + k] = v;
+    }
+    Rs[r * CP + k] = v;
+  }
+  next_product(g.nx, Rs, Hs, CP, C, m0, g.M, g.n, g.H, g.D, wave, lane);
 }
 
 // The half of a layer after its attention, for 16 rows per workgroup of 8
@@ -255,11 +331,14 @@ static hipError_t gemm(const GemmArgs& g, hipStream_t s) {
 //   y = O wo (O read head-major as [M][C]); X = x + y
 //   u = gelu(LN2(X) w1 + b1)
 //   x = X + u w2 + b2
-// Waves take 16-column tiles of each product in turn (mfma_tile16).
+// then the next layer's LayerNorm and q/k/v product, or the final LayerNorm
+// and the vocabulary projection (next_product).  Waves take 16-column tiles
+// of each product in turn (mfma_tile16).
 struct MlpArgs {
   const float* O;  // [B][H][n][D]
   float* x;        // [M][C], updated in place
   const float *wo, *ln_g, *ln_b, *w1, *b1, *w2, *b2;
+  NextArgs nx;
   int M, n, H, D, C, F;
 };
 
@@ -297,19 +376,7 @@ __global__ __launch_bounds__(512) void block_mlp_kernel(MlpArgs g) {
     }
   }
   __syncthreads();
-  // LN2: two rows per wave, mean, then the variance about it
-  for (int r = 2 * wave; r < 2 * wave + 2; ++r) {
-    float s = 0.f;
-    for (int k = lane; k < C; k += kWave) s += Xs[r * CP + k];
-    const float mu = wave_sum(s) / (float)C;
-    float v = 0.f;
-    for (int k = lane; k < C; k += kWave) {
-      const float d = Xs[r * CP + k] - mu;
-      v += d * d;
-    }
-    const float rstd = 1.f / sqrtf(wave_sum(v) / (float)C + kLnEps);
-    for (int k = lane; k < C; k += kWave) Hs[r * CP + k] = (Xs[r * CP + k] - mu) * rstd * g.ln_g[k] + g.ln_b[k];
-  }
+  rows_ln16(Xs, Hs, CP, C, g.ln_g, g.ln_b, wave, lane);  // LN2
   __syncthreads();
   {  // u = gelu(H w1 + b1)
     const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w1, C, F);
@@ -321,7 +388,7 @@ __global__ __launch_bounds__(512) void block_mlp_kernel(MlpArgs g) {
     }
   }
   __syncthreads();
-  {  // x = X + u w2 + b2
+  {  // x = X + u w2 + b2, also kept in Os (free since the first product)
     const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w2, F, C);
     for (int ct = wave; ct < C / 16; ct += 8) {
       const int col = 16 * ct + lr;
@@ -329,10 +396,13 @@ __global__ __launch_bounds__(512) void block_mlp_kernel(MlpArgs g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * lgp + i, m = m0 + r;
-        if (m < g.M) g.x[(size_t)m * C + col] = Xs[r * CP + col] + acc[i] + g.b2[col];
+        const float xv = Xs[r * CP + col] + acc[i] + g.b2[col];
+        Os[r * CP + col] = xv;
+        if (m < g.M) g.x[(size_t)m * C + col] = xv;
       }
     }
   }
+  next_product(g.nx, Os, Hs, CP, C, m0, g.M, g.n, g.H, g.D, wave, lane);
 }
 
 static size_t mlp_lds_bytes(const ModelLayout& l) {
@@ -340,7 +410,7 @@ static size_t mlp_lds_bytes(const ModelLayout& l) {
 }
 
 struct FwdPlan {
-  size_t off_x, off_q, off_k, off_v, off_o, off_u, off_attn, attn_bytes, total;
+  size_t off_x, off_q, off_k, off_v, off_o, off_attn, attn_bytes, total;
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -361,8 +431,6 @@ static bool fwd_plan(const ModelLayout& l, int B, int n, int hint, FwdPlan* p) {
   off = align256(off + sizeof(float) * M * l.C);
   f.off_o = off;
   off = align256(off + sizeof(float) * M * l.C);
-  f.off_u = off;
-  off = align256(off + sizeof(float) * M * l.F);
   f.off_attn = off;
   f.attn_bytes = ab;
   off = align256(off + ab);
@@ -414,35 +482,48 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
   float* kn = reinterpret_cast<float*>(ws + p.off_k);
   float* vn = reinterpret_cast<float*>(ws + p.off_v);
   float* o = reinterpret_cast<float*>(ws + p.off_o);
-  float* u = reinterpret_cast<float*>(ws + p.off_u);
   void* aws = ws + p.off_attn;
   const int M = B * n;
   const size_t plane = (size_t)B * l.H * max_T * l.D;  // one layer's K (or V) cache
 
-  hipLaunchKernelGGL(embed_kernel, dim3((unsigned)M), dim3(std::min(256, ((l.C + 63) / 64) * 64)), 0, stream,
-                     params + l.wte, params + l.wpe, tokens, cache_len, x, n, l.C, l.V, l.T);
+  // The vocabulary projection joins the last layer's launch up to this width;
+  // a wider one is a launch of 32 x 32 tiles of its own.
+  const bool fuse_logits = l.V <= kFusedVocabMax;
+  auto qkv_of = [&](int layer) {
+    const float* P = params + l.layer0 + (size_t)layer * l.layer_stride;
+    NextArgs nx{};
+    nx.mode = NEXT_QKV;
+    nx.ln_g = P + l.ln1_g;
+    nx.ln_b = P + l.ln1_b;
+    nx.W = P + l.wqkv;
+    nx.q = q;
+    nx.kn = kn;
+    nx.vn = vn;
+    nx.N = 3 * l.C;
+    return nx;
+  };
+  const unsigned row_blocks = (unsigned)((M + 15) / 16);
+
+  // x = wte[token] + wpe[position]; q | k_new | v_new = LN1(x) wqkv (layer 0)
+  EmbArgs ea{};
+  ea.wte = params + l.wte;
+  ea.wpe = params + l.wpe;
+  ea.tok = tokens;
+  ea.lens = cache_len;
+  ea.x = x;
+  ea.nx = qkv_of(0);
+  ea.M = M;
+  ea.n = n;
+  ea.H = l.H;
+  ea.D = l.D;
+  ea.C = l.C;
+  ea.V = l.V;
+  ea.T = l.T;
+  hipLaunchKernelGGL(embed_qkv_kernel, dim3(row_blocks), dim3(512), sizeof(float) * 2 * 16 * (l.C + kPad), stream, ea);
   if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
 
   for (int layer = 0; layer < l.L; ++layer) {
     const float* P = params + l.layer0 + (size_t)layer * l.layer_stride;
-    GemmArgs g{};
-    g.M = M;
-    g.n = n;
-    g.H = l.H;
-    g.D = l.D;
-
-    // q | k_new | v_new = LN1(x) wqkv
-    g.A = x;
-    g.K = l.C;
-    g.N = 3 * l.C;
-    g.W = P + l.wqkv;
-    g.ln_g = P + l.ln1_g;
-    g.ln_b = P + l.ln1_b;
-    g.q = q;
-    g.kn = kn;
-    g.vn = vn;
-    if (gemm<O_QKV>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
-
     // append + causal attention over the layer's cache
     float* kc = kv_cache + (size_t)(2 * layer) * plane;
     float* vc = kv_cache + (size_t)(2 * layer + 1) * plane;
@@ -451,7 +532,8 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
                                                    p.attn_bytes, stream);
     if (st != SPEC_OK) return st;
 
-    // x += O wo; x += gelu(LN2(x) w1 + b1) w2 + b2, 16 rows per workgroup
+    // x += O wo; x += gelu(LN2(x) w1 + b1) w2 + b2; then the next layer's
+    // q | k_new | v_new, or the logits, 16 rows per workgroup
     MlpArgs ma{};
     ma.O = o;
     ma.x = x;
@@ -462,29 +544,39 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
     ma.b1 = P + l.b1;
     ma.w2 = P + l.w2;
     ma.b2 = P + l.b2;
+    if (layer + 1 < l.L) {
+      ma.nx = qkv_of(layer + 1);
+    } else if (fuse_logits) {
+      ma.nx.mode = NEXT_LOGITS;
+      ma.nx.ln_g = params + l.lnf_g;
+      ma.nx.ln_b = params + l.lnf_b;
+      ma.nx.W = params + l.wout;
+      ma.nx.logits = logits;
+      ma.nx.N = l.V;
+    } else {
+      ma.nx.mode = NEXT_NONE;
+    }
     ma.M = M;
     ma.n = n;
     ma.H = l.H;
     ma.D = l.D;
     ma.C = l.C;
     ma.F = l.F;
-    hipLaunchKernelGGL(block_mlp_kernel, dim3((unsigned)((M + 15) / 16)), dim3(512), mlp_lds_bytes(l), stream, ma);
+    hipLaunchKernelGGL(block_mlp_kernel, dim3(row_blocks), dim3(512), mlp_lds_bytes(l), stream, ma);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   }
 
-  // logits = LNf(x) wout
-  GemmArgs g{};
-  g.M = M;
-  g.n = n;
-  g.H = l.H;
-  g.D = l.D;
-  g.A = x;
-  g.K = l.C;
-  g.N = l.V;
-  g.W = params + l.wout;
-  g.ln_g = params + l.lnf_g;
-  g.ln_b = params + l.lnf_b;
-  g.out = logits;
-  if (gemm<O_ROWS>(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+  if (!fuse_logits) {  // logits = LNf(x) wout
+    GemmArgs g{};
+    g.M = M;
+    g.A = x;
+    g.K = l.C;
+    g.N = l.V;
+    g.W = params + l.wout;
+    g.ln_g = params + l.lnf_g;
+    g.ln_b = params + l.lnf_b;
+    g.out = logits;
+    if (gemm(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+  }
   return SPEC_OK;
 }

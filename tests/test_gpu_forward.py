@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = 1e-4
 WIDE = M.ModelConfig(96, 144, 2, 6, 128)
+BIGV = M.ModelConfig(1500, 48, 2, 2, 64)
 
 
 def _case(name, **kw):
@@ -51,10 +52,11 @@ def _run(cfg, params, tokens, lens, kv, hint):
         ("target", 1, 16, 0, 30, 48),      # one sequence, the largest n
         ("draft", 3, 16, 496, 496, 512),   # positions ending exactly at T = 512
         ("wide", 5, 5, 0, 40, 64),         # the widest model the fused MLP's LDS takes: C = 144, D = 24
+        ("bigvocab", 3, 4, 0, 30, 48),     # a vocabulary above 1024: its own projection launch
     ],
 )
 def test_forward_matches_oracle(which, B, n, lo, hi, max_T):
-    cfg = {"target": M.TARGET, "draft": M.DRAFT, "wide": WIDE}[which]
+    cfg = {"target": M.TARGET, "draft": M.DRAFT, "wide": WIDE, "bigvocab": BIGV}[which]
     _case("forward", which=which, B=B, n=n, lens=(lo, hi), max_T=max_T)
     params = gen.model_params(M.param_shapes(cfg), 20)
     inp = gen.forward_inputs(cfg.V, cfg.L, cfg.H, cfg.D, B, n, (lo, hi), max_T, 21)
