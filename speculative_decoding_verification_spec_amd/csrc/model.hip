@@ -133,6 +133,10 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 // scalar base, issued without branches four steps ahead (a column past N or a
 // step past the last reads a valid element whose product is discarded), so
 // the compiler waits for the oldest only.
+#ifndef SPECV_W_RING
+#define SPECV_W_RING 4  // steps of W loads in flight per lane group
+#endif
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const float* W, int K, int N) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(W), 0, (int)((long)K * N * sizeof(float)), 0x00020000);
 }
@@ -142,7 +146,7 @@ __device__ __forceinline__ f32x4 mfma_tile16(const float* A, int KP, int K, __am
   const int K4 = K / 4;
   const float* Ar = A + lr * KP + lgp * K4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int kRing = 4;
+  constexpr int kRing = SPECV_W_RING;
   const int NIT = K4 / 4;
   const uint32_t cbase = (uint32_t)(lgp * K4) * (uint32_t)N + (uint32_t)(col_ok ? col : 0);
   float w[kRing][4];
