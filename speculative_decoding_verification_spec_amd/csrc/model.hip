@@ -33,6 +33,7 @@
 
 #include <algorithm>
 
+#include "model_internal.h"
 #include "spec_common.h"
 #include "spec_verify.h"
 
@@ -306,15 +307,39 @@ __device__ __forceinline__ void next_product(const NextArgs& nx, const float* Rs
 
 // Token and position embeddings of 16 rows per workgroup of kRowWaves waves (NaN
 // rows for a token or position out of range), then the first layer's
-// LayerNorm and q/k/v product (next_product).
+// LayerNorm and q/k/v product (next_product).  The tokens and positions come
+// from src (TokenSource).
 struct EmbArgs {
   const float *wte, *wpe;
-  const int32_t* tok;   // [M]
-  const int32_t* lens;  // [B]
-  float* x;             // [M][C]
+  TokenSource src;
+  float* x;  // [M][C]
   NextArgs nx;
   int M, n, H, D, C, V, T;
 };
+
+// Token and position of row (b, i) of a call of n rows per sequence; a
+// draft step's i = 0 row also stores the step's cache length of b.
+__device__ __forceinline__ void row_input(const TokenSource& s, int b, int i, int n, int& tok, long& pos) {
+  if (s.mode == SRC_ARRAYS) {
+    tok = s.tokens[(size_t)b * n + i];
+    pos = (long)s.cache_len[b] + i;
+    return;
+  }
+  const int L = s.seq_len[b];
+  const int32_t* sb = s.seq + (size_t)b * s.max_len;
+  if (s.mode == SRC_DRAFT_STEP) {
+    const int base = s.j == 0 ? s.base_len[b] : s.base_len[b] + s.j + 1;
+    if (s.j == 0)
+      tok = (L >= 2 && L <= s.max_len) ? sb[L - 2 + i] : -1;
+    else
+      tok = s.xs[(size_t)b * s.gamma + s.j - 1];
+    if (i == 0) s.pos_out[b] = base;
+    pos = (long)base + i;
+  } else {  // SRC_VERIFY
+    tok = i == 0 ? ((L >= 1 && L <= s.max_len) ? sb[L - 1] : -1) : s.xs[(size_t)b * s.gamma + i - 1];
+    pos = (long)s.cache_len[b] + i;
+  }
+}
 
 __global__ __launch_bounds__(64 * kRowWaves) void embed_qkv_kernel(EmbArgs g) {
   extern __shared__ float sm[];
@@ -322,14 +347,20 @@ __global__ __launch_bounds__(64 * kRowWaves) void embed_qkv_kernel(EmbArgs g) {
   const int C = g.C, CP = C + kPad;
   float* Rs = sm;            // [16][CP]
   float* Hs = Rs + 16 * CP;  // [16][CP]
+  __shared__ int s_tok[16];
+  __shared__ long s_pos[16];
   const int m0 = blockIdx.x * 16;
+  if (threadIdx.x < 16 && m0 + (int)threadIdx.x < g.M) {
+    const int m = m0 + threadIdx.x, b = m / g.n;
+    row_input(g.src, b, m - b * g.n, g.n, s_tok[threadIdx.x], s_pos[threadIdx.x]);
+  }
+  __syncthreads();
   for (int e = threadIdx.x; e < 16 * C; e += blockDim.x) {
     const int r = e / C, k = e - r * C, m = m0 + r;
     float v = 0.f;
     if (m < g.M) {
-      const int b = m / g.n, i = m - b * g.n;
-      const int t = g.tok[m];
-      const long pos = (long)g.lens[b] + i;
+      const int t = s_tok[r];
+      const long pos = s_pos[r];
       const bool ok = t >= 0 && t < g.V && pos >= 0 && pos < g.T;
       v = ok ? g.wte[(size_t)t * C + k] + g.wpe[(size_t)pos * C + k] : __builtin_nanf("");
       g.x[(size_t)m * C + k] = v;
@@ -469,13 +500,17 @@ extern "C" size_t spec_verify_forward_workspace_size(const spec_model_t* model, 
   return p.total;
 }
 
-extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const float* params, const int32_t* tokens,
-                                             const int32_t* cache_len, float* kv_cache, int max_T, float* logits,
-                                             int B, int n, int max_len_hint, void* workspace, size_t workspace_bytes,
-                                             hipStream_t stream) {
+namespace specv {
+
+spec_status_t verify_forward(const spec_model_t* model, const float* params, const TokenSource& src,
+                             float* kv_cache, int max_T, float* logits, int B, int n, int max_len_hint,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
   ModelLayout l;
   if (!model_layout(model, &l)) return SPEC_ERR_ARG;
-  if (!params || !tokens || !cache_len || !kv_cache || !logits || !workspace) return SPEC_ERR_ARG;
+  if (!params || !kv_cache || !logits || !workspace) return SPEC_ERR_ARG;
+  // the attention's cache lengths: the caller's, or the ones a draft step writes
+  const int32_t* cache_len = src.mode == SRC_DRAFT_STEP ? src.pos_out : src.cache_len;
+  if (!cache_len || (src.mode == SRC_ARRAYS && !src.tokens)) return SPEC_ERR_ARG;
   if (B < 1 || n < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
   if ((long)max_len_hint + n > (long)max_T || (long)max_len_hint + n > (long)l.T) return SPEC_ERR_OVERFLOW;
@@ -521,8 +556,7 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
   EmbArgs ea{};
   ea.wte = params + l.wte;
   ea.wpe = params + l.wpe;
-  ea.tok = tokens;
-  ea.lens = cache_len;
+  ea.src = src;
   ea.x = x;
   ea.nx = qkv_of(0);
   ea.M = M;
@@ -593,4 +627,19 @@ extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const fl
     if (gemm(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
   }
   return SPEC_OK;
+}
+
+}  // namespace specv
+
+extern "C" spec_status_t spec_verify_forward(const spec_model_t* model, const float* params, const int32_t* tokens,
+                                             const int32_t* cache_len, float* kv_cache, int max_T, float* logits,
+                                             int B, int n, int max_len_hint, void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+  if (!tokens || !cache_len) return SPEC_ERR_ARG;
+  TokenSource src{};
+  src.mode = SRC_ARRAYS;
+  src.tokens = tokens;
+  src.cache_len = cache_len;
+  return verify_forward(model, params, src, kv_cache, max_T, logits, B, n, max_len_hint, workspace, workspace_bytes,
+                        stream);
 }

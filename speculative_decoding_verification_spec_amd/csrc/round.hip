@@ -20,39 +20,20 @@
 // draw of softmax(z / T) at its uniform (the convention of the final draw);
 // at T = 0 it is the argmax.
 //
-// Kernels here only move tokens and lengths and make the draft's draws; the
-// forwards are spec_verify_forward, the verification spec_reject_sample.
+// Kernels here only make the draft's draws and commit tokens and lengths; the
+// forwards are the verify forward's (taking their tokens and positions from
+// the sequence buffer and the proposals: TokenSource), the verification
+// spec_reject_sample.
 #include <math.h>
 #include <stdint.h>
 
 #include <algorithm>
 
+#include "model_internal.h"
 #include "spec_common.h"
 #include "spec_verify.h"
 
 namespace specv {
-
-// Inputs of draft call j for every sequence: j = 0: the tokens at positions
-// L-2 and L-1 from position draft_len = L-2; j > 0: proposal j-1 at position
-// L-1+j.
-__global__ __launch_bounds__(256) void round_draft_inputs(const int32_t* __restrict__ seq,
-                                                         const int32_t* __restrict__ seq_len, int max_len,
-                                                         const int32_t* __restrict__ draft_len,
-                                                         const int32_t* __restrict__ xs, int gamma, int j, int B,
-                                                         int32_t* __restrict__ tok, int32_t* __restrict__ pos) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= B) return;
-  const int L = seq_len[b];
-  const bool ok = L >= 2 && L <= max_len;  // else token -1: NaN logits for this sequence only
-  if (j == 0) {
-    tok[2 * b] = ok ? seq[(size_t)b * max_len + L - 2] : -1;
-    tok[2 * b + 1] = ok ? seq[(size_t)b * max_len + L - 1] : -1;
-    pos[b] = draft_len[b];
-  } else {
-    tok[b] = xs[(size_t)b * gamma + j - 1];
-    pos[b] = draft_len[b] + j + 1;
-  }
-}
 
 // Ordered key of a logit for the argmax: a larger value gives a larger key,
 // -0 equals +0, a NaN is above every number.
@@ -114,21 +95,6 @@ __global__ __launch_bounds__(64) void round_draft_draw(const float* __restrict__
   if (lane == 0) xs[(size_t)b * gamma + j] = t;
 }
 
-// Tokens of the target's verify call: [last committed token] + proposals.
-__global__ __launch_bounds__(256) void round_verify_inputs(const int32_t* __restrict__ seq,
-                                                          const int32_t* __restrict__ seq_len, int max_len,
-                                                          const int32_t* __restrict__ xs, int gamma, int B,
-                                                          int32_t* __restrict__ vtok) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= B * (gamma + 1)) return;
-  const int b = e / (gamma + 1), i = e - b * (gamma + 1);
-  const int L = seq_len[b];
-  if (i == 0)
-    vtok[e] = (L >= 1 && L <= max_len) ? seq[(size_t)b * max_len + L - 1] : -1;
-  else
-    vtok[e] = xs[(size_t)b * gamma + i - 1];
-}
-
 // Commit: append the n+1 emitted tokens, and advance the sequence, target
 // and draft lengths by n + 1.  A negative n (a sampler error) changes
 // nothing; so does a sequence whose tokens would not fit, and it is reported
@@ -154,7 +120,7 @@ __global__ __launch_bounds__(256) void round_commit(int32_t* __restrict__ seq, i
 }
 
 struct RoundPlan {
-  size_t off_fwd, fwd_bytes, off_rs, rs_bytes, off_tok, off_pos, off_step, off_dl, off_xs, off_vtok, off_tl, total;
+  size_t off_fwd, fwd_bytes, off_rs, rs_bytes, off_pos, off_step, off_dl, off_xs, off_tl, total;
 };
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -176,8 +142,6 @@ static bool round_plan(const spec_model_t* t, const spec_model_t* d, int B, int 
   r.off_rs = off;
   r.rs_bytes = rs;
   off = align256(off + rs);
-  r.off_tok = off;
-  off = align256(off + sizeof(int32_t) * 2 * (size_t)B);
   r.off_pos = off;
   off = align256(off + sizeof(int32_t) * (size_t)B);
   r.off_step = off;
@@ -186,8 +150,6 @@ static bool round_plan(const spec_model_t* t, const spec_model_t* d, int B, int 
   off = align256(off + sizeof(float) * (size_t)B * gamma * V);
   r.off_xs = off;
   off = align256(off + sizeof(int32_t) * (size_t)B * gamma);
-  r.off_vtok = off;
-  off = align256(off + sizeof(int32_t) * (size_t)B * (gamma + 1));
   r.off_tl = off;
   off = align256(off + sizeof(float) * (size_t)B * (gamma + 1) * V);
   r.total = off;
@@ -236,35 +198,41 @@ extern "C" spec_status_t spec_speculative_round(
   char* ws = static_cast<char*>(workspace);
   void* fws = ws + p.off_fwd;
   void* rws = ws + p.off_rs;
-  int32_t* tok = reinterpret_cast<int32_t*>(ws + p.off_tok);
   int32_t* pos = reinterpret_cast<int32_t*>(ws + p.off_pos);
   float* step = reinterpret_cast<float*>(ws + p.off_step);
   float* dlog = reinterpret_cast<float*>(ws + p.off_dl);
   int32_t* xs = reinterpret_cast<int32_t*>(ws + p.off_xs);
-  int32_t* vtok = reinterpret_cast<int32_t*>(ws + p.off_vtok);
   float* tlog = reinterpret_cast<float*>(ws + p.off_tl);
   const int V = target->V;
   const float c32 = greedy ? 0.f : (float)(1.4426950408889634 / (double)temperature);  // 2^(z c) = e^(z/T)
   const unsigned gB = (unsigned)((B + 255) / 256);
 
+  // The forwards read their tokens and positions from the sequence buffer
+  // and the proposals themselves (TokenSource), in their first launch.
+  TokenSource src{};
+  src.seq = seq;
+  src.seq_len = seq_len;
+  src.max_len = max_len;
+  src.xs = xs;
+  src.gamma = gamma;
   for (int j = 0; j < gamma; ++j) {
     const int n = j == 0 ? 2 : 1;
-    hipLaunchKernelGGL(round_draft_inputs, dim3(gB), dim3(256), 0, stream, seq, seq_len, max_len, draft_len, xs,
-                       gamma, j, B, tok, pos);
-    if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
+    src.mode = SRC_DRAFT_STEP;
+    src.base_len = draft_len;
+    src.pos_out = pos;
+    src.j = j;
     const int hint = j == 0 ? max_len_hint - 2 : max_len_hint + j - 1;
-    spec_status_t st = spec_verify_forward(draft, draft_params, tok, pos, draft_kv, draft_max_T, step, B, n, hint,
-                                           fws, p.fwd_bytes, stream);
+    spec_status_t st =
+        verify_forward(draft, draft_params, src, draft_kv, draft_max_T, step, B, n, hint, fws, p.fwd_bytes, stream);
     if (st != SPEC_OK) return st;
     hipLaunchKernelGGL(round_draft_draw, dim3((unsigned)B), dim3(kWave), 0, stream, step, n, V, u_draft, gamma, j,
                        c32, greedy ? 1 : 0, dlog, xs);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   }
-  hipLaunchKernelGGL(round_verify_inputs, dim3((unsigned)((B * (gamma + 1) + 255) / 256)), dim3(256), 0, stream, seq,
-                     seq_len, max_len, xs, gamma, B, vtok);
-  if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
-  spec_status_t st = spec_verify_forward(target, target_params, vtok, target_len, target_kv, target_max_T, tlog, B,
-                                         gamma + 1, max_len_hint - 1, fws, p.fwd_bytes, stream);
+  src.mode = SRC_VERIFY;
+  src.cache_len = target_len;
+  spec_status_t st = verify_forward(target, target_params, src, target_kv, target_max_T, tlog, B, gamma + 1,
+                                    max_len_hint - 1, fws, p.fwd_bytes, stream);
   if (st != SPEC_OK) return st;
   st = spec_reject_sample(tlog, greedy ? nullptr : dlog, xs, greedy ? nullptr : u_verify, B, gamma, V, temperature,
                           SPEC_F32, n_accepted, out_tokens, nullptr, nullptr, rws, p.rs_bytes, stream);
