@@ -232,6 +232,65 @@ static hipError_t gemm(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Ordered key of a logit for the argmax: a larger value gives a larger key,
+// -0 equals +0, a NaN is above every number.
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  if (v != v) return 0xffffffffu;
+  const uint32_t u = (v == 0.f) ? 0u : __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One wave, for sequence b whose last logit row is z: copies the row into
+// draft_logits[b][j] and draws proposal j: at T > 0 the smallest index whose
+// fp64 prefix of w = 2^((z - max) c) exceeds u * sum(w) (the last positive
+// weight if rounding leaves none); at T = 0 the first index of the largest
+// logit.
+__device__ __forceinline__ void draw_row(const DrawSpec& dr, const float* z, int V, int b, int lane) {
+  const int gamma = dr.gamma, j = dr.j;
+  const float c32 = dr.c32;
+  const int greedy = dr.greedy;
+  int32_t* xs = dr.xs;
+  const double* u_draft = dr.u;
+  float* zd = dr.draft_logits + ((size_t)b * gamma + j) * V;
+  float m = neg_inf_f();
+  uint64_t best = 0;
+  for (int k = lane; k < V; k += kWave) {
+    const float v = z[k];
+    zd[k] = v;
+    m = fmaxf(m, v);
+    const uint64_t w = ((uint64_t)logit_key(v) << 32) | (uint32_t)~(uint32_t)k;
+    best = w > best ? w : best;
+  }
+  if (greedy) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)best, o, kWave), hi = __shfl_xor((uint32_t)(best >> 32), o, kWave);
+      const uint64_t w = ((uint64_t)hi << 32) | lo;
+      best = w > best ? w : best;
+    }
+    if (lane == 0) xs[(size_t)b * gamma + j] = (int32_t)~(uint32_t)best;
+    return;
+  }
+  m = wave_max(m);
+  double s = 0.0;
+  for (int k = lane; k < V; k += kWave) s += (double)exp2_fast((z[k] - m) * c32);
+  const double target = u_draft[(size_t)b * gamma + j] * wave_sum(s);
+  double carry = 0.0;
+  int t = -1, last = -1;
+  for (int c0 = 0; c0 < V && t < 0; c0 += kWave) {
+    const int k = c0 + lane;
+    const float w = k < V ? exp2_fast((z[k] - m) * c32) : 0.f;
+    const double incl = carry + wave_inclusive_scan((double)w, lane);
+    const uint64_t hit = __ballot(k < V && incl > target);
+    const uint64_t pos = __ballot(k < V && w > 0.f);
+    if (pos) last = c0 + 63 - __builtin_clzll(pos);
+    if (hit) t = c0 + __ffsll((long long)hit) - 1;
+    carry = __shfl(incl, kWave - 1, kWave);
+  }
+  if (t < 0) t = last < 0 ? 0 : last;
+  if (lane == 0) xs[(size_t)b * gamma + j] = t;
+}
+
 // Waves of a 16-row block workgroup; each product's 16-column tiles are dealt
 // round-robin over them (16: 0.16 -> 0.14 ms per forward of the 4-layer
 // width-96 model against 8, and 4 were slower still).
@@ -254,6 +313,8 @@ struct NextArgs {
   float *q, *kn, *vn;            // NEXT_QKV
   float* logits;                 // NEXT_LOGITS
   int N;                         // 3C or V
+  int draw;                      // NEXT_LOGITS: then draw from each sequence's last row (dr)
+  DrawSpec dr;
 };
 
 // LayerNorm of 16 rows (Rs -> Hs, row stride CP), a row per wave at a time:
@@ -303,6 +364,20 @@ __device__ __forceinline__ void next_product(const NextArgs& nx, const float* Rs
       }
     }
   }
+  if (nx.mode == NEXT_LOGITS && nx.draw) {  // uniform
+    __syncthreads();  // the block's logit rows are written (same CU)
+    for (int r = wave; r < 16; r += kRowWaves) {
+      const int m = m0 + r;
+      if (m < M && m % n == n - 1) draw_row(nx.dr, nx.logits + (size_t)m * nx.N, nx.N, m / n, lane);
+    }
+  }
+}
+
+// The draws when the vocabulary projection is a launch of its own: one wave
+// per sequence, from its last row of n.
+__global__ __launch_bounds__(64) void draw_rows_kernel(DrawSpec dr, const float* __restrict__ logits, int n, int V) {
+  const int b = blockIdx.x;
+  draw_row(dr, logits + ((size_t)b * n + n - 1) * V, V, b, threadIdx.x);
 }
 
 // Token and position embeddings of 16 rows per workgroup of kRowWaves waves (NaN
@@ -504,7 +579,7 @@ namespace specv {
 
 spec_status_t verify_forward(const spec_model_t* model, const float* params, const TokenSource& src,
                              float* kv_cache, int max_T, float* logits, int B, int n, int max_len_hint,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                             void* workspace, size_t workspace_bytes, hipStream_t stream, const DrawSpec* draw) {
   ModelLayout l;
   if (!model_layout(model, &l)) return SPEC_ERR_ARG;
   if (!params || !kv_cache || !logits || !workspace) return SPEC_ERR_ARG;
@@ -601,6 +676,10 @@ spec_status_t verify_forward(const spec_model_t* model, const float* params, con
       ma.nx.W = params + l.wout;
       ma.nx.logits = logits;
       ma.nx.N = l.V;
+      if (draw) {
+        ma.nx.draw = 1;
+        ma.nx.dr = *draw;
+      }
     } else {
       ma.nx.mode = NEXT_NONE;
     }
@@ -625,6 +704,10 @@ spec_status_t verify_forward(const spec_model_t* model, const float* params, con
     g.ln_b = params + l.lnf_b;
     g.out = logits;
     if (gemm(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
+    if (draw) {
+      hipLaunchKernelGGL(draw_rows_kernel, dim3((unsigned)B), dim3(kWave), 0, stream, *draw, logits, n, l.V);
+      if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
+    }
   }
   return SPEC_OK;
 }

@@ -33,8 +33,21 @@ struct TokenSource {
   int max_len, gamma, j;
 };
 
+// A draw from the last logit row of each sequence, made by the forward as
+// soon as that row exists: the row is copied to draft_logits[b][j] and
+// proposal xs[b][j] is drawn at u[b][j] from softmax(z / T) (c32 = log2(e)/T),
+// or is the row's argmax when greedy.
+struct DrawSpec {
+  const double* u;     // [B][gamma]
+  float* draft_logits;  // [B][gamma][V]
+  int32_t* xs;          // [B][gamma]
+  int gamma, j, greedy;
+  float c32;
+};
+
 spec_status_t verify_forward(const spec_model_t* model, const float* params, const TokenSource& src,
                              float* kv_cache, int max_T, float* logits, int B, int n, int max_len_hint,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             const DrawSpec* draw = nullptr);
 
 }  // namespace specv

@@ -20,10 +20,10 @@
 // draw of softmax(z / T) at its uniform (the convention of the final draw);
 // at T = 0 it is the argmax.
 //
-// Kernels here only make the draft's draws and commit tokens and lengths; the
-// forwards are the verify forward's (taking their tokens and positions from
-// the sequence buffer and the proposals: TokenSource), the verification
-// spec_reject_sample.
+// The only kernel here commits tokens and lengths.  The forwards are the
+// verify forward's, taking their tokens and positions from the sequence
+// buffer and the proposals (TokenSource) and making the draft's draws
+// (DrawSpec); the verification is spec_reject_sample.
 #include <math.h>
 #include <stdint.h>
 
@@ -34,66 +34,6 @@
 #include "spec_verify.h"
 
 namespace specv {
-
-// Ordered key of a logit for the argmax: a larger value gives a larger key,
-// -0 equals +0, a NaN is above every number.
-__device__ __forceinline__ uint32_t logit_key(float v) {
-  if (v != v) return 0xffffffffu;
-  const uint32_t u = (v == 0.f) ? 0u : __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// One wave per sequence: copies the last logit row of draft call j into
-// draft_logits[b][j] and draws proposal j: at T > 0 the smallest index whose
-// fp64 prefix of w = 2^((z - max) c) exceeds u * sum(w) (the last positive
-// weight if rounding leaves none); at T = 0 the first index of the largest
-// logit.
-__global__ __launch_bounds__(64) void round_draft_draw(const float* __restrict__ step_logits, int rows, int V,
-                                                      const double* __restrict__ u_draft, int gamma, int j,
-                                                      float c32, int greedy, float* __restrict__ draft_logits,
-                                                      int32_t* __restrict__ xs) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* z = step_logits + ((size_t)b * rows + rows - 1) * V;
-  float* zd = draft_logits + ((size_t)b * gamma + j) * V;
-  float m = neg_inf_f();
-  uint64_t best = 0;
-  for (int k = lane; k < V; k += kWave) {
-    const float v = z[k];
-    zd[k] = v;
-    m = fmaxf(m, v);
-    const uint64_t w = ((uint64_t)logit_key(v) << 32) | (uint32_t)~(uint32_t)k;
-    best = w > best ? w : best;
-  }
-  if (greedy) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint32_t lo = __shfl_xor((uint32_t)best, o, kWave), hi = __shfl_xor((uint32_t)(best >> 32), o, kWave);
-      const uint64_t w = ((uint64_t)hi << 32) | lo;
-      best = w > best ? w : best;
-    }
-    if (lane == 0) xs[(size_t)b * gamma + j] = (int32_t)~(uint32_t)best;
-    return;
-  }
-  m = wave_max(m);
-  double s = 0.0;
-  for (int k = lane; k < V; k += kWave) s += (double)exp2_fast((z[k] - m) * c32);
-  const double target = u_draft[(size_t)b * gamma + j] * wave_sum(s);
-  double carry = 0.0;
-  int t = -1, last = -1;
-  for (int c0 = 0; c0 < V && t < 0; c0 += kWave) {
-    const int k = c0 + lane;
-    const float w = k < V ? exp2_fast((z[k] - m) * c32) : 0.f;
-    const double incl = carry + wave_inclusive_scan((double)w, lane);
-    const uint64_t hit = __ballot(k < V && incl > target);
-    const uint64_t pos = __ballot(k < V && w > 0.f);
-    if (pos) last = c0 + 63 - __builtin_clzll(pos);
-    if (hit) t = c0 + __ffsll((long long)hit) - 1;
-    carry = __shfl(incl, kWave - 1, kWave);
-  }
-  if (t < 0) t = last < 0 ? 0 : last;
-  if (lane == 0) xs[(size_t)b * gamma + j] = t;
-}
 
 // Commit: append the n+1 emitted tokens, and advance the sequence, target
 // and draft lengths by n + 1.  A negative n (a sampler error) changes
@@ -222,12 +162,17 @@ extern "C" spec_status_t spec_speculative_round(
     src.pos_out = pos;
     src.j = j;
     const int hint = j == 0 ? max_len_hint - 2 : max_len_hint + j - 1;
-    spec_status_t st =
-        verify_forward(draft, draft_params, src, draft_kv, draft_max_T, step, B, n, hint, fws, p.fwd_bytes, stream);
+    DrawSpec dr{};
+    dr.u = u_draft;
+    dr.draft_logits = dlog;
+    dr.xs = xs;
+    dr.gamma = gamma;
+    dr.j = j;
+    dr.greedy = greedy ? 1 : 0;
+    dr.c32 = c32;
+    spec_status_t st = verify_forward(draft, draft_params, src, draft_kv, draft_max_T, step, B, n, hint, fws,
+                                      p.fwd_bytes, stream, &dr);
     if (st != SPEC_OK) return st;
-    hipLaunchKernelGGL(round_draft_draw, dim3((unsigned)B), dim3(kWave), 0, stream, step, n, V, u_draft, gamma, j,
-                       c32, greedy ? 1 : 0, dlog, xs);
-    if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   }
   src.mode = SRC_VERIFY;
   src.cache_len = target_len;

@@ -31,12 +31,18 @@ def _case(name, **kw):
     print(f"\n[case] {name} {kw}", flush=True)
 
 
-@pytest.mark.parametrize("T,gamma,rounds", [(1.0, 4, 4), (0.0, 4, 4), (0.7, 6, 3), (1.0, 1, 5), (1.0, 15, 2),
-                                             (0.0, 8, 3)])
-def test_rounds_match_oracle(T, gamma, rounds):
-    _case("rounds", T=T, gamma=gamma, rounds=rounds)
+# Models with a 1,500-token vocabulary: their projection and the draft's draws
+# are launches of their own.
+BIGV_MODELS = (M.ModelConfig(1500, 48, 2, 2, 64), M.ModelConfig(1500, 48, 1, 2, 64))
+
+
+@pytest.mark.parametrize("T,gamma,rounds,models", [(1.0, 4, 4, "char"), (0.0, 4, 4, "char"), (0.7, 6, 3, "char"),
+                                                    (1.0, 1, 5, "char"), (1.0, 15, 2, "char"), (0.0, 8, 3, "char"),
+                                                    (1.0, 4, 2, "bigvocab"), (0.0, 3, 2, "bigvocab")])
+def test_rounds_match_oracle(T, gamma, rounds, models):
+    _case("rounds", T=T, gamma=gamma, rounds=rounds, models=models)
     dev = torch.device("cuda:0")
-    ct, cd = M.TARGET, M.DRAFT
+    ct, cd = (M.TARGET, M.DRAFT) if models == "char" else BIGV_MODELS
     pt = gen.model_params(M.param_shapes(ct), 30)
     pd = gen.model_params(M.param_shapes(cd), 31)
     B, max_len, max_T = 8, 64, 64
