@@ -151,3 +151,49 @@ def test_status_codes():
     with pytest.raises(sv.SpecError) as e:
         sv.spec_verify_attention_paged(q, kn, kn, p8, p8.clone(), table, lens, 10)  # page size 8
     assert e.value.status == 3
+
+
+def test_long_caches_merged_in_launch_equal_contiguous():
+    """Shares long enough that the stream launch merges each slab's pieces
+    itself: the paged kernel must give the contiguous kernel's bits (which
+    tests/test_gpu_attention.py checks against the oracle at the same shape),
+    with empty, ragged, full-hint and rejected lengths, pages at random slots."""
+    cfg = W.Config(95, "merge", B=20, gamma=8, V=1, dtype="bf16", Hq=64, Hkv=8, D=128, L=(8192, 32768),
+                   max_T=32800)
+    hint, page, n_q = 32768, 32, cfg.n_q
+    _case("paged merge-in-launch", B=cfg.B, page=page, hint=hint)
+    d = W.attention_inputs_device(cfg, "cuda")
+    for b, L in ((1, 0), (2, 31), (3, hint + 1), (4, hint)):
+        d["lens"][b] = L
+    lens = _gpu.to_host(d["lens"]).astype(np.int64)
+    rng = np.random.default_rng(96)
+    need = [(min(int(L), hint) + n_q + page - 1) // page for L in lens]
+    max_blocks = (hint + n_q + page - 1) // page
+    num_pages = sum(need) + 3
+    perm = torch.from_numpy(rng.permutation(num_pages)).to("cuda")
+    table = torch.full((cfg.B, max_blocks), -7, dtype=torch.int32, device="cuda")
+    pages = [torch.full((cfg.Hkv, num_pages, page, cfg.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+             for _ in range(2)]
+    k = 0
+    for b in range(cfg.B):
+        idx = perm[k : k + need[b]]
+        k += need[b]
+        table[b, : need[b]] = idx.to(torch.int32)
+        L = min(int(lens[b]), hint)
+        nf = L // page
+        for src, dst in ((d["k_cache"], pages[0]), (d["v_cache"], pages[1])):
+            if nf:
+                dst[:, idx[:nf]] = src[b, :, : nf * page].reshape(cfg.Hkv, nf, page, cfg.D)
+            if L % page:
+                dst[:, idx[nf], : L % page] = src[b, :, nf * page : L]
+    out_p = sv.spec_verify_attention_paged(d["q"], d["k_new"], d["v_new"], pages[0], pages[1], table, d["lens"], hint)
+    out_c = sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], hint)
+    torch.cuda.synchronize()
+    assert torch.equal(out_p.view(torch.int16), out_c.view(torch.int16))
+    assert torch.isnan(out_p[3].float()).all()
+    for b in (0, 4, 19):  # the appended rows landed in the tabled slots
+        L = int(lens[b])
+        for t in range(n_q):
+            slot = int(table[b, (L + t) // page])
+            assert torch.equal(pages[0][:, slot, (L + t) % page], d["k_cache"][b, :, L + t])
+            assert torch.equal(pages[1][:, slot, (L + t) % page], d["v_cache"][b, :, L + t])
