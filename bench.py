@@ -299,7 +299,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the verification step has no multi-GPU "
-              "path in this build; see DESIGN.md for how it would shard.", file=sys.stderr)
+              "path; sharded, each GPU would own B/N sequences and run the same calls with no exchange.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -49,7 +49,7 @@ typedef enum {
   SPEC_OK = 0,
   SPEC_ERR_ARG = 1,         /* bad pointer, size, alignment or workspace size   */
   SPEC_ERR_OVERFLOW = 2,    /* cache too small: max_len_hint + n_q > max_T      */
-  SPEC_ERR_UNSUPPORTED = 3, /* valid request outside what this build supports   */
+  SPEC_ERR_UNSUPPORTED = 3, /* valid request outside what the library supports */
   SPEC_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch          */
 } spec_status_t;
 

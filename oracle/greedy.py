@@ -17,7 +17,7 @@ What is computed, per sequence, following
                                                 rejection, or the bonus token)
   emitted tokens = x_0 .. x_{n-1}, t;   n_accepted = n
 
-Readings of points the pages leave open (listed in the design doc):
+Readings of points the pages leave open:
   * argmax is numpy's: the first index of the largest value; a NaN counts as
     the largest (the first NaN wins), as np.argmax does.
   * softmax(z / T) is monotone in z for T > 0, so the argmax of the logits is

@@ -18,7 +18,7 @@ Layouts:
   block_table       [B, max_blocks] int      physical page of logical block i
   lens              [B]                      committed length L_b before the call
 
-Reading (listed in the design doc): the KV head is the outermost index, then the
+Reading where the pages are silent: the KV head is the outermost index, then the
 page, then the position in the page: one head's part of a page is
 contiguous, and so is a run of consecutive pages; the pages fix only that a
 request's positions are grouped into fixed-size blocks.

@@ -10,7 +10,7 @@ bytes as the int8 values plus the float16 scales.  The attention is then that
 of ``oracle.attention`` (the ``forward_cached`` listing of [P2] section
 numpyで小さなTransformerを自作する) on the converted-back cache.
 
-Readings (listed in DESIGN.md):
+Readings where the pages leave the point open:
   * s = max|x| / 127, q = round-half-even(x / s) clipped to [-127, 127], both
     in float32 (the precision the codes are decided in on both sides, so the
     codes are exact integers to compare); a row of zeros has s = 0, q = 0.

@@ -20,7 +20,7 @@ What is computed, per sequence, following
   t = smallest j with C_j / C_{V-1} > u[gamma],  C = inclusive prefix sum of w
   emitted tokens = x_0 .. x_{n-1}, t;   n_accepted = n
 
-Readings of points the pages leave open (each listed in the design doc):
+Readings of points the pages leave open:
   * u[i] in [0, 1), one per judged position, drives the test at i; u[gamma]
     drives the final draw in either branch.
   * The test is the IEEE comparison u < min(1, p/q) with NaN propagating through

@@ -55,7 +55,7 @@ def test_two_rounds_with_poisoned_tail(cid):
     hint = cfg.L[1] + cfg.n_q  # room for one more round
     out1, n1, tok1 = _round(dev, sdev, hint, cfg.n_q)
 
-    # round 1 against the oracle
+    # the first verification step against the oracle
     want1 = A.verify_attention(att1["q"], att1["k_new"], att1["v_new"], att1["k_cache"], att1["v_cache"], att1["lens"])
     assert np.max(np.abs(_gpu.as_f64(_gpu.to_host(out1)) - want1)) < _gpu.ATT_TOL[cfg.dtype]
     orc = S.verify_batch(samp1["target_logits"], samp1["draft_logits"], samp1["draft_tokens"], samp1["uniforms"],
@@ -64,7 +64,7 @@ def test_two_rounds_with_poisoned_tail(cid):
     new_len = _gpu.to_host(dev["lens"])
     assert np.array_equal(new_len, Tr.truncate(att1["lens"], _gpu.to_host(n1)))
 
-    # poison every row at or past the new length, then run round 2
+    # poison every row at or past the new length, then run the second step
     for b, L in enumerate(new_len):
         dev["k_cache"][b, :, L:] = float("nan")
         dev["v_cache"][b, :, L:] = float("nan")
