@@ -128,3 +128,35 @@ def test_speculative_round_graph_replays_match_eager():
         one()  # eager work between replays
         torch.cuda.synchronize()
     print(f"n_accepted {n.cpu().tolist()}", flush=True)
+
+
+def test_merging_attention_graph_replays_match_eager():
+    """Long shares: the launch that zeroes the per-slab counters and the
+    stream launch that merges each slab's pieces, replayed from one graph."""
+    cfg = W.Config(95, "merge", B=20, gamma=8, V=1, dtype="bf16", Hq=64, Hkv=8, D=128, L=(8192, 32768),
+                   max_T=32800)
+    hint = 32768
+    _case("merge-graph", B=cfg.B, hint=hint)
+    d = W.attention_inputs_device(cfg, "cuda")
+    d["lens"][3] = hint + 1  # a rejected length: NaN rows from the counter launch
+    out = torch.empty_like(d["q"])
+    wa = sv.Workspace()
+
+    def call():
+        sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], hint,
+                                 out=out, workspace=wa)
+
+    call()
+    torch.cuda.synchronize()
+    want = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"replay {rep} differs from the eager call"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
