@@ -292,8 +292,8 @@ def main():
                     help="run attention over a paged copy of the cache with this page size")
     ap.add_argument("--page-order", default="random", choices=("random", "sequential"),
                     help="where the pages sit: seeded random slots, or in sequence order")
-    ap.add_argument("--kv", default="bf16", choices=("bf16", "int8"),
-                    help="cache storage: the workload's bf16, or int8 codes with an fp16 scale per row")
+    ap.add_argument("--kv", default="bf16", choices=("bf16", "f16", "int8"),
+                    help="cache storage: the workload's bf16, the same values in fp16, or int8 codes with an fp16 scale per row")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -346,6 +346,14 @@ def main():
         for rep, (att, _) in enumerate(sets):
             att.update(quantized_cache(att, cfg, rep))
             del att["k_cache"], att["v_cache"]
+        torch.cuda.empty_cache()
+    if args.kv == "f16":  # the same values (bf16 ones are exact in fp16), in IEEE half
+        if args.paged or cfg.dtype != "bf16":
+            print("--kv f16 needs a contiguous cache and a bf16 workload", file=sys.stderr)
+            sys.exit(2)
+        for att, _ in sets:
+            for k in ("q", "k_new", "v_new", "k_cache", "v_cache", "out"):
+                att[k] = att[k].to(torch.float16)
         torch.cuda.empty_cache()
     if args.paged:
         for rep, (att, _) in enumerate(sets):

@@ -53,7 +53,7 @@ typedef enum {
   SPEC_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch          */
 } spec_status_t;
 
-typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype_t;
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1, SPEC_F16 = 2 } spec_dtype_t;
 
 /* Library version, e.g. "specverify 0.1.0 gfx950". Static string. */
 const char* spec_version(void);
@@ -94,10 +94,13 @@ size_t spec_verify_attention_workspace_size(int B, int Hq, int Hkv, int n_q, int
  *   scale    score scale; the pages' value is 1/sqrt(D).
  *   max_len_hint  host upper bound on max_b cache_len[b]; it sizes the launch.
  *   workspace device, >= spec_verify_attention_workspace_size(...) bytes.
- * Arithmetic: scores, softmax and accumulation in fp32; bf16 inputs are
- * consumed exactly and the output is rounded to nearest-even.
- * Supported: dtype SPEC_BF16 with D in {64, 128}; SPEC_F32 with D in {24, 32,
- * 64, 128}; 1 <= n_q <= 16; Hq % Hkv == 0; Hq/Hkv * n_q <= 256.
+ * Arithmetic: scores, softmax and accumulation in fp32; bf16 and fp16 inputs
+ * are consumed exactly, the probabilities are rounded to the input type for
+ * the PV product, and the output is rounded to nearest-even.
+ * Supported: dtype SPEC_BF16 with D in {64, 128}; SPEC_F16 (the fp16 cache of
+ * [P2] section PagedAttentionとKVキャッシュの量子化) with D in {64, 128} and
+ * B <= 1024; SPEC_F32 with D in {24, 32, 64, 128}; 1 <= n_q <= 16;
+ * Hq % Hkv == 0; Hq/Hkv * n_q <= 256.
  * Errors: SPEC_ERR_ARG for null pointers, non-positive sizes, Hq % Hkv != 0,
  * pointers not 16-byte aligned, or a small workspace; SPEC_ERR_OVERFLOW if
  * max_len_hint + n_q > max_T; SPEC_ERR_UNSUPPORTED outside the supported set.

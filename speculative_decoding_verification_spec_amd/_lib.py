@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SPECV_LIB") or os.path.join(_HERE, "libspecverify.so")
 
 SPEC_OK, SPEC_ERR_ARG, SPEC_ERR_OVERFLOW, SPEC_ERR_UNSUPPORTED, SPEC_ERR_LAUNCH = range(5)
-SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_F32, SPEC_BF16, SPEC_F16 = 0, 1, 2
 
 EXPORTED = (
     "spec_version",
@@ -126,7 +126,9 @@ def _dtype_code(t):
         return SPEC_BF16
     if t.dtype == torch.float32:
         return SPEC_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    if t.dtype == torch.float16:
+        return SPEC_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float16 or float32)")
 
 
 def _need(t, name, dtype=None, shape=None):

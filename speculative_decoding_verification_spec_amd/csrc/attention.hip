@@ -68,10 +68,33 @@
 namespace specv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int KB = 32;  // keys per block
+
+// The 16-bit element of the bf16 kernels' layout: bf16, or IEEE half (F16).
+// Both are 2 bytes, staged and transposed alike; only the MFMA, the
+// conversions and the NaN pattern differ.
+template <bool F16>
+struct Half16;
+template <>
+struct Half16<false> {
+  typedef bf16x8 v8;
+  typedef __bf16 elem;
+  static constexpr uint16_t kNaN = 0x7fc0;
+  __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0); }
+  __device__ static uint16_t bits(float f) { return f32_to_bf16(f); }
+};
+template <>
+struct Half16<true> {
+  typedef f16x8 v8;
+  typedef _Float16 elem;
+  static constexpr uint16_t kNaN = 0x7e00;
+  __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+  __device__ static uint16_t bits(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }  // round to nearest even
+};
 
 struct ML {  // per split and row: running max (log2 units) and sum
   float m, l;
@@ -311,11 +334,12 @@ __device__ __forceinline__ float2 co_load2(const float* p) {
 // (b, g) into the cache (A1).  kbuf / vbuf map a stage index to its LDS
 // objects.  Every wave of the workgroup calls it with the same arguments.
 // CO: partials through device-scope stores (merged within the launch).
-template <int D, int NW, int NST, int PG, bool CO = false, typename KBuf, typename VBuf>
+template <int D, int NW, int NST, int PG, bool CO = false, bool F16 = false, typename KBuf, typename VBuf>
 __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vbuf, int b, int g, int rg, int L,
                                            int k0, int k1, bool whole, size_t slot, bool append,
                                            const int32_t* __restrict__ table = nullptr) {
   using LY = BfLayout<D>;
+  using H = Half16<F16>;
   constexpr int DS = D / 32;  // MFMA steps over D for the scores
   constexpr int DT = D / 16;  // 16-wide output tiles over D
   constexpr int NCP = 2 * LY::NI;                             // 1 KB copies per block (K then V)
@@ -366,7 +390,7 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
         if (m < a.M && lg == 0) {
           uint16_t* o = static_cast<uint16_t*>(a.out) +
                         (((size_t)b * a.Hq + g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D;
-          for (int d = 0; d < D; ++d) o[d] = 0x7fc0;
+          for (int d = 0; d < D; ++d) o[d] = H::kNaN;
         }
       } else {
         const int row = 16 * wave + lr;
@@ -471,12 +495,12 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
   const int h = g * a.G + (valid ? m / a.n_q : 0);
   const int qi = valid ? m % a.n_q : a.n_q - 1;
   const int lim = L + qi;  // last visible key of this row
-  bf16x8 qf[DS];
+  typename H::v8 qf[DS];
   {
     const uint16_t* qrow = q + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
 #pragma unroll
     for (int s = 0; s < DS; ++s)
-      qf[s] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg) : bf16x8{};
+      qf[s] = valid ? *reinterpret_cast<const typename H::v8*>(qrow + 32 * s + 8 * lg) : typename H::v8{};
   }
 
   int pf0 = 0, pf1 = 0;  // pages of the next block to issue
@@ -536,8 +560,8 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + kofs[s] + 16 * kt * D);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+        const typename H::v8 kf = *reinterpret_cast<const typename H::v8*>(ks + kofs[s] + 16 * kt * D);
+        acc = H::mfma(kf, qf[s], acc);
       }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) sc[4 * kt + jj] = acc[jj];
@@ -587,9 +611,9 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
     }
-    bf16x8 pf;
+    typename H::v8 pf;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) pf[jj] = (__bf16)sc[jj];
+    for (int jj = 0; jj < 8; ++jj) pf[jj] = (typename H::elem)sc[jj];
 
     // V^T fragments: half hh covers keys 16 hh + 4 lg + (0..3); lane lr of
     // the group points at V[16 hh + 4 lg + lr/4][16 dt + 4 (lr%4)].
@@ -600,8 +624,9 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
       for (int hh = 0; hh < 2; ++hh)
         v2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) s16x4*)(vs + vofs[dt] + 16 * hh * D));
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
+      const typename H::v8 vf =
+          __builtin_bit_cast(typename H::v8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      oacc[dt] = H::mfma(vf, pf, oacc[dt]);
     }
   };
 
@@ -633,8 +658,8 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 16 * dt + 4 * lg;
         uint2 pk;
-        pk.x = uint32_t(f32_to_bf16(oacc[dt][0] * inv)) | (uint32_t(f32_to_bf16(oacc[dt][1] * inv)) << 16);
-        pk.y = uint32_t(f32_to_bf16(oacc[dt][2] * inv)) | (uint32_t(f32_to_bf16(oacc[dt][3] * inv)) << 16);
+        pk.x = uint32_t(H::bits(oacc[dt][0] * inv)) | (uint32_t(H::bits(oacc[dt][1] * inv)) << 16);
+        pk.y = uint32_t(H::bits(oacc[dt][2] * inv)) | (uint32_t(H::bits(oacc[dt][3] * inv)) << 16);
         *reinterpret_cast<uint2*>(o + d) = pk;
       }
     }
@@ -820,8 +845,9 @@ __device__ __forceinline__ void stream_walk(const AttnArgs& a, Piece&& piece) {
 // whose add completes the count merges the slab's np partials (device-scope
 // loads) and writes the output, as attn_combine_stream would.  Every wave
 // calls it.
-template <int D, int NW>
+template <int D, int NW, bool F16>
 __device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, int rg, size_t slot, int np) {
+  using H = Half16<F16>;
   __shared__ int sh_last;
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -868,30 +894,30 @@ __device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, in
     acc *= 1.f / den;
     const int m = row0 + row;
     uint2 pk;
-    pk.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
-    pk.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+    pk.x = uint32_t(H::bits(acc[0])) | (uint32_t(H::bits(acc[1])) << 16);
+    pk.y = uint32_t(H::bits(acc[2])) | (uint32_t(H::bits(acc[3])) << 16);
     *reinterpret_cast<uint2*>(out + (((size_t)b * a.Hq + g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D + d) = pk;
   }
 }
 
 // MERGE: the pieces of a slab are merged by the last of its workgroups
 // (stream_merge) instead of by attn_combine_stream.
-template <int D, int NW, int NST, int PG, bool MERGE>
+template <int D, int NW, int NST, int PG, bool MERGE, bool F16 = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
 void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
   using LY = BfLayout<D>;
   SPECV_BF16_STAGE_LDS
   stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append, int np) {
-    bf16_piece<D, NW, NST, PG, MERGE>(a, kbuf, vbuf, b, g, rg, L, k0, k1, whole, slot, append, table);
+    bf16_piece<D, NW, NST, PG, MERGE, F16>(a, kbuf, vbuf, b, g, rg, L, k0, k1, whole, slot, append, table);
     if constexpr (MERGE) {
-      if (!whole) stream_merge<D, NW>(a, b, g, rg, slot, np);
+      if (!whole) stream_merge<D, NW, F16>(a, b, g, rg, slot, np);
     }
   });
 }
 
 // Before a merging stream launch: zero the per-slab counters, and write NaN
 // rows for the slabs of a rejected length (the stream walk skips them).
-template <int D>
+template <int D, bool F16 = false>
 __global__ __launch_bounds__(256) void attn_stream_prep(AttnArgs a) {
   const long slabs = (long)a.B * a.Hkv * a.RG;
   for (long sl = (long)blockIdx.x * blockDim.x + threadIdx.x; sl < slabs; sl += (long)gridDim.x * blockDim.x) {
@@ -905,7 +931,7 @@ __global__ __launch_bounds__(256) void attn_stream_prep(AttnArgs a) {
     for (int row = 0; row < nrows; ++row) {
       const int m = row0 + row;
       uint16_t* o = out + (((size_t)b * a.Hq + g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D;
-      for (int d = 0; d < D; ++d) o[d] = (uint16_t)0x7fc0;
+      for (int d = 0; d < D; ++d) o[d] = Half16<F16>::kNaN;
     }
   }
 }
@@ -1356,8 +1382,9 @@ void attn_stream_i8(AttnArgs a) {
 
 // Merge the pieces of each (b, g, rg) slab the stream kernel cut; one
 // workgroup per slab.  Slabs covered whole were written by the stream kernel.
-template <int D>
+template <int D, bool F16 = false>
 __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
+  using H = Half16<F16>;
   const long slab = blockIdx.x;
   const int rg = (int)(slab % a.RG);
   const int g = (int)((slab / a.RG) % a.Hkv);
@@ -1372,7 +1399,7 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
   };
   const int nbb = slab_blocks(a, b);
   if (nbb == 0) {  // rejected length: NaN rows, nothing else touched
-    for (int e = threadIdx.x; e < nrows * D; e += blockDim.x) out_ptr(e / D)[e % D] = (uint16_t)0x7fc0;
+    for (int e = threadIdx.x; e < nrows * D; e += blockDim.x) out_ptr(e / D)[e % D] = H::kNaN;
     return;
   }
   const int HR = a.Hkv * a.RG;
@@ -1415,8 +1442,8 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
     }
     acc *= 1.f / den;
     uint2 pk;
-    pk.x = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
-    pk.y = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+    pk.x = uint32_t(H::bits(acc[0])) | (uint32_t(H::bits(acc[1])) << 16);
+    pk.y = uint32_t(H::bits(acc[2])) | (uint32_t(H::bits(acc[3])) << 16);
     *reinterpret_cast<uint2*>(out_ptr(row) + d) = pk;
   }
 }
@@ -1744,17 +1771,17 @@ struct SplitPolicy {
 static SplitPolicy policy(spec_dtype_t dt) {
   // bf16: workgroups of one wave per row tile, a few resident per CU; fp32:
   // single-wave items.
-  return dt == SPEC_BF16 ? SplitPolicy{256, SPECV_ATTN_CMAX, SPECV_ATTN_ITEMS}
+  return dt != SPEC_F32 ? SplitPolicy{256, SPECV_ATTN_CMAX, SPECV_ATTN_ITEMS}
                          : SplitPolicy{SPECV_F32_CMIN, 4096, SPECV_F32_ITEMS};
 }
 
 static int max_rt(spec_dtype_t dt, int D) {
-  if (dt == SPEC_BF16) return 8;  // waves per workgroup
+  if (dt != SPEC_F32) return 8;  // waves per workgroup
   return D <= 32 ? 4 : (D <= 64 ? 2 : 1);
 }
 
 static bool supported(spec_dtype_t dt, int D) {
-  if (dt == SPEC_BF16) return D == 64 || D == 128;
+  if (dt == SPEC_BF16 || dt == SPEC_F16) return D == 64 || D == 128;
   if (dt == SPEC_F32) return D == 24 || D == 32 || D == 64 || D == 128;
   return false;
 }
@@ -1821,7 +1848,7 @@ constexpr int kStreamMaxWG = SPECV_STREAM_MAX_WG;
 // block counts stay in int.
 static bool stream_ok(spec_dtype_t dt, int B, int Hkv, int RG, int n_q, int hint) {
   const long nbmax = ((long)hint + n_q + KB - 1) / KB;
-  return dt == SPEC_BF16 && B <= 1024 && (long)Hkv * RG * B * nbmax < (1L << 30);
+  return (dt == SPEC_BF16 || dt == SPEC_F16) && B <= 1024 && (long)Hkv * RG * B * nbmax < (1L << 30);
 }
 
 struct StreamPlan {
@@ -1887,22 +1914,22 @@ static int stream_workgroups(K kernel, int NW, int max_per_cu) {
   return P;
 }
 
-template <int D, int NW, int PG, bool kMerge>
+template <int D, int NW, int PG, bool kMerge, bool F16>
 static hipError_t launch_stream_as(const AttnArgs& a0, hipStream_t s) {
   AttnArgs a = a0;
   const size_t slabs = (size_t)a.B * a.Hkv * a.RG;
   if constexpr (kMerge) {
-    hipLaunchKernelGGL((attn_stream_prep<D>), dim3((unsigned)std::min<size_t>((slabs + 255) / 256, 1024)), dim3(256), 0,
-                       s, a);
+    hipLaunchKernelGGL((attn_stream_prep<D, F16>), dim3((unsigned)std::min<size_t>((slabs + 255) / 256, 1024)),
+                       dim3(256), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG, kMerge>, NW, SPECV_BF16_PER_CU);
-  hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG, kMerge>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a,
-                     a.table);
+  a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG, kMerge, F16>, NW, SPECV_BF16_PER_CU);
+  hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG, kMerge, F16>), dim3((unsigned)a.P), dim3(64 * NW), 0, s,
+                     a, a.table);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || kMerge) return e;
-  hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)slabs), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_combine_stream<D, F16>), dim3((unsigned)slabs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1912,15 +1939,15 @@ static hipError_t launch_stream_as(const AttnArgs& a0, hipStream_t s) {
 // grows with the slab count.  Merge when a workgroup's share can reach
 // SPECV_MERGE_MIN_SHARE blocks (measured: 32K-key caches, B = 256: 3.36 ->
 // 3.32 ms; 1-4K-key caches, B = 32: 74 -> 87 us, so those combine).
-template <int D, int NW, int PG>
+template <int D, int NW, int PG, bool F16 = false>
 static hipError_t launch_stream(const AttnArgs& a, hipStream_t s) {
   if constexpr (SPECV_STREAM_MERGE != 0) {
     const long nbmax = ((long)a.hint + a.n_q + KB - 1) / KB;
     const long wmax = (long)a.B * a.Hkv * a.RG * nbmax;
-    const int P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG, true>, NW, SPECV_BF16_PER_CU);
-    if (wmax >= (long)SPECV_MERGE_MIN_SHARE * P) return launch_stream_as<D, NW, PG, true>(a, s);
+    const int P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG, true, F16>, NW, SPECV_BF16_PER_CU);
+    if (wmax >= (long)SPECV_MERGE_MIN_SHARE * P) return launch_stream_as<D, NW, PG, true, F16>(a, s);
   }
-  return launch_stream_as<D, NW, PG, false>(a, s);
+  return launch_stream_as<D, NW, PG, false, F16>(a, s);
 }
 
 template <int D, int NW>
@@ -1952,8 +1979,13 @@ static hipError_t launch_i8_d(const AttnArgs& a, hipStream_t s) {
   }
 }
 
-template <int D, int NW>
+// F16: IEEE-half elements, contiguous cache, stream scheme only.
+template <int D, int NW, bool F16 = false>
 static hipError_t launch_bf16(const AttnArgs& a0, hipStream_t s) {
+  if constexpr (F16) {
+    if (!a0.pre || a0.table) return hipErrorInvalidValue;  // rejected on the host before
+    return launch_stream<D, NW, 0, true>(a0, s);
+  }
   if (a0.pre) {  // stream scheme
     if (a0.table) return a0.page == 16 ? launch_stream<D, NW, 16>(a0, s) : launch_stream<D, NW, 32>(a0, s);
     return launch_stream<D, NW, 0>(a0, s);
@@ -1967,17 +1999,17 @@ static hipError_t launch_bf16(const AttnArgs& a0, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool F16 = false>
 static hipError_t launch_bf16_d(const AttnArgs& a, hipStream_t s) {
   switch (a.RT) {
-    case 1: return launch_bf16<D, 1>(a, s);
-    case 2: return launch_bf16<D, 2>(a, s);
-    case 3: return launch_bf16<D, 3>(a, s);
-    case 4: return launch_bf16<D, 4>(a, s);
-    case 5: return launch_bf16<D, 5>(a, s);
-    case 6: return launch_bf16<D, 6>(a, s);
-    case 7: return launch_bf16<D, 7>(a, s);
-    case 8: return launch_bf16<D, 8>(a, s);
+    case 1: return launch_bf16<D, 1, F16>(a, s);
+    case 2: return launch_bf16<D, 2, F16>(a, s);
+    case 3: return launch_bf16<D, 3, F16>(a, s);
+    case 4: return launch_bf16<D, 4, F16>(a, s);
+    case 5: return launch_bf16<D, 5, F16>(a, s);
+    case 6: return launch_bf16<D, 6, F16>(a, s);
+    case 7: return launch_bf16<D, 7, F16>(a, s);
+    case 8: return launch_bf16<D, 8, F16>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -2045,7 +2077,7 @@ extern "C" size_t spec_verify_attention_workspace_size(int B, int Hq, int Hkv, i
   const size_t split_bytes = align256(sizeof(float) * items * 16 * p.RT * D) + align256(sizeof(ML) * items * 16 * p.RT);
   // bf16 uses the stream scheme while stream_ok holds, which for a larger
   // hint can stop holding: cover both then.
-  if (dtype != SPEC_BF16 || B > 1024) return split_bytes;
+  if (dtype == SPEC_F32 || B > 1024) return split_bytes;
   const size_t stream_bytes = stream_plan(B, Hkv, p.RG, p.RT, n_q, D, max_len_hint).total;
   if (stream_ok(dtype, B, Hkv, p.RG, n_q, max_len_hint)) return stream_bytes;
   return std::max(split_bytes, stream_bytes);
@@ -2061,7 +2093,8 @@ static spec_status_t verify_attention(const void* q, const void* k_new, const vo
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !cache_len || !out || !workspace) return SPEC_ERR_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || n_q < 1 || D < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
   if (Hq % Hkv != 0) return SPEC_ERR_ARG;
-  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_ARG;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16 && dtype != SPEC_F16) return SPEC_ERR_ARG;
+  if (dtype == SPEC_F16 && table) return SPEC_ERR_UNSUPPORTED;  // paged: bf16 only
   if (!(scale > 0.f) || !isfinite(scale)) return SPEC_ERR_ARG;
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_new) |
                        reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_cache) |
@@ -2072,6 +2105,7 @@ static spec_status_t verify_attention(const void* q, const void* k_new, const vo
   const AttnPlan p = attn_plan(B, Hq, Hkv, n_q, D, max_len_hint, dtype);
   const bool use_stream = stream_ok(dtype, B, Hkv, p.RG, n_q, max_len_hint);
   if (table && !use_stream) return SPEC_ERR_UNSUPPORTED;  // paged: bf16, B <= 1024
+  if (dtype == SPEC_F16 && !use_stream) return SPEC_ERR_UNSUPPORTED;  // fp16: B <= 1024
   const StreamPlan sp = use_stream ? stream_plan(B, Hkv, p.RG, p.RT, n_q, D, max_len_hint) : StreamPlan{};
   if (workspace_bytes < (use_stream ? sp.total : p.total)) return SPEC_ERR_ARG;
   if ((size_t)B * Hkv * p.RG * p.NSP > 0x7fffffffu) return SPEC_ERR_UNSUPPORTED;
@@ -2114,6 +2148,9 @@ static spec_status_t verify_attention(const void* q, const void* k_new, const vo
   if (dtype == SPEC_BF16) {
     if (D == 128) e = launch_bf16_d<128>(a, stream);
     else if (D == 64) e = launch_bf16_d<64>(a, stream);
+  } else if (dtype == SPEC_F16) {
+    if (D == 128) e = launch_bf16_d<128, true>(a, stream);
+    else if (D == 64) e = launch_bf16_d<64, true>(a, stream);
   } else {
     if (D == 24) e = launch_f32_d<24>(a, stream);
     else if (D == 32) e = launch_f32_d<32>(a, stream);

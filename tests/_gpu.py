@@ -16,7 +16,10 @@ from oracle import bf16 as obf16
 
 BAND = 1e-6
 P_RTOL = 1e-5
-ATT_TOL = {"f32": 1e-4, "bf16": 2e-2}
+# fp16: the probabilities are rounded to fp16 for the PV product (2^-11
+# relative, against |v| <= 5 for N(0,1) rows: <= 2.5e-3) and the output to
+# fp16 (2^-11 relative on |o| <= 2: <= 1e-3), so 5e-3 absolute.
+ATT_TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 5e-3}
 
 
 from workloads.device import to_dev, to_host  # noqa: E402,F401

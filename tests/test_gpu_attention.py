@@ -98,14 +98,15 @@ def test_config5_full_size_sampled():
     _check(before, got, kc, vc, "bf16", seqs=range(len(seqs)))
 
 
-def test_long_caches_merged_in_launch():
-    """Shares long enough that the bf16 stream launch merges each slab's pieces
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_long_caches_merged_in_launch(dtype):
+    """Shares long enough that the stream launch merges each slab's pieces
     itself (its last workgroup), with empty, ragged, full-hint and rejected
     lengths in one batch."""
-    cfg = W.Config(95, "merge", B=20, gamma=8, V=1, dtype="bf16", Hq=64, Hkv=8, D=128, L=(8192, 32768),
+    cfg = W.Config(95, "merge", B=20, gamma=8, V=1, dtype=dtype, Hq=64, Hkv=8, D=128, L=(8192, 32768),
                    max_T=32800)
     hint = 32768
-    _case("merge-in-launch", B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, hint=hint)
+    _case("merge-in-launch", dtype=dtype, B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, hint=hint)
     d = W.attention_inputs_device(cfg, "cuda")
     for b, L in ((1, 0), (2, 31), (3, hint + 1), (4, hint)):
         d["lens"][b] = L
@@ -121,7 +122,19 @@ def test_long_caches_merged_in_launch():
     vc = _gpu.to_host(d["v_cache"][seqs])
     del d
     torch.cuda.empty_cache()
-    _check(before, got, kc, vc, "bf16", seqs=range(len(seqs)))
+    _check(before, got, kc, vc, dtype, seqs=range(len(seqs)))
+
+
+def test_f16_outside_its_support_is_refused():
+    _case("f16 status")
+    dev = "cuda"
+    q = torch.zeros((1100, 2, 2, 64), dtype=torch.float16, device=dev)
+    kn = torch.zeros((1100, 1, 2, 64), dtype=torch.float16, device=dev)
+    kc = torch.zeros((1100, 1, 8, 64), dtype=torch.float16, device=dev)
+    lens = torch.zeros(1100, dtype=torch.int32, device=dev)
+    with pytest.raises(sv.SpecError) as e:  # B > 1024: the fp16 cache has no fixed-split kernel
+        sv.spec_verify_attention(q, kn, kn, kc, kc.clone(), lens, 4)
+    assert e.value.status == 3
 
 
 @pytest.mark.parametrize(
@@ -138,6 +151,9 @@ def test_long_caches_merged_in_launch():
         ("f32", 2, 4, 4, 5, 24, [700, 1000]),    # 8 splits in one workgroup, idle waves for the shorter cache
         ("f32", 1, 32, 8, 4, 64, [300]),         # GQA, 3 splits in a 4-wave workgroup
         ("f32", 2, 4, 2, 5, 24, [3000, 1200]),   # 24 splits: partial slots and attn_combine
+        ("f16", 3, 8, 2, 5, 128, [0, 31, 33]),   # the fp16 cache: empty, block edges
+        ("f16", 2, 4, 4, 1, 64, [1, 1000]),      # fp16, n_q = 1, MHA, D = 64
+        ("f16", 4, 32, 8, 5, 128, [1024, 4096, 2000, 3001]),  # fp16 at config 4's head layout and lengths
     ],
 )
 def test_shapes_and_edges(dtype, B, Hq, Hkv, n_q, D, lens):

@@ -27,7 +27,7 @@ class Config:
     B: int
     gamma: int
     V: int
-    dtype: str  # "f32" or "bf16": logits and K/V/Q element type
+    dtype: str  # "f32", "bf16" or "f16" (attention only): logits and K/V/Q element type
     temperatures: Tuple[float, ...] = (1.0,)
     # sampler logits: z_t = t_std * N(0,1); z_d = mix * z_t + noise_std * N(0,1)
     t_std: float = 1.0

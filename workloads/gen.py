@@ -35,11 +35,17 @@ def bf16_bits_to_f32(bits):
 
 
 def _store(x32, dtype):
-    return bf16_bits(x32) if dtype == "bf16" else np.ascontiguousarray(x32, dtype=np.float32)
+    if dtype == "bf16":
+        return bf16_bits(x32)
+    if dtype == "f16":  # IEEE half, rounded to nearest even
+        return np.ascontiguousarray(x32, dtype=np.float16)
+    return np.ascontiguousarray(x32, dtype=np.float32)
 
 
 def _as_f32(stored, dtype):
-    return bf16_bits_to_f32(stored) if dtype == "bf16" else stored
+    if dtype == "bf16":
+        return bf16_bits_to_f32(stored)
+    return np.asarray(stored, dtype=np.float32)
 
 
 def _gumbel_argmax(z_over_t, noise_uniform):
@@ -138,7 +144,7 @@ def attention_inputs_device(cfg: Config, device, rep: int = 0, B=None):
     import torch
 
     B = cfg.B if B is None else int(B)
-    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg.dtype, torch.float32)
     g = _torch_gen(cfg, 0, rep, device)
     n, D = cfg.n_q, cfg.D
 
@@ -168,7 +174,7 @@ def sampler_inputs_device(cfg: Config, device, temperature=None, rep: int = 0, B
     T = cfg.temperatures[0] if temperature is None else float(temperature)
     B = cfg.B if B is None else int(B)
     gm, V = cfg.gamma, cfg.V
-    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg.dtype, torch.float32)
     g0 = _torch_gen(cfg, 0, rep, device)
     g1 = _torch_gen(cfg, 1, rep, device)
     g2 = _torch_gen(cfg, 2, rep, device)
