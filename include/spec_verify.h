@@ -119,9 +119,9 @@ spec_status_t spec_verify_attention(const void* q, const void* k_new, const void
  * and a block table lists the page of each of its blocks; the attention is
  * that of spec_verify_attention on the sequence's positions in table order.
  *
- *   k_pages, v_pages device, [num_pages][Hkv][page_size][D] dtype, in/out:
+ *   k_pages, v_pages device, [Hkv][num_pages][page_size][D] dtype, in/out:
  *            position j of sequence b, KV head g, is
- *            pages[block_table[b][j / page_size]][g][j % page_size].  The new
+ *            pages[g][block_table[b][j / page_size]][j % page_size].  The new
  *            rows go to positions [cache_len[b], cache_len[b] + n_q); no other
  *            position is written, positions >= cache_len[b] are never read.
  *            Pages may be shared by several sequences for reading; the pages
@@ -131,8 +131,8 @@ spec_status_t spec_verify_attention(const void* q, const void* k_new, const void
  *   page_size 16 or 32.
  *   The other arguments are those of spec_verify_attention; the workspace size
  *   is spec_verify_attention_workspace_size(...) for the same sizes.
- * Supported: dtype SPEC_BF16, D in {64, 128}, B <= 1024, and the limits of
- * spec_verify_attention.
+ * Supported: dtype SPEC_BF16 or SPEC_F16, D in {64, 128}, B <= 1024, and the
+ * limits of spec_verify_attention.
  * Errors: as spec_verify_attention, with max_T = max_blocks * page_size;
  * SPEC_ERR_ARG for a null block_table, num_pages < 1 or max_blocks < 1;
  * SPEC_ERR_UNSUPPORTED for another page size, dtype, or B > 1024.  A sequence

@@ -1979,11 +1979,12 @@ static hipError_t launch_i8_d(const AttnArgs& a, hipStream_t s) {
   }
 }
 
-// F16: IEEE-half elements, contiguous cache, stream scheme only.
+// F16: IEEE-half elements, stream scheme only.
 template <int D, int NW, bool F16 = false>
 static hipError_t launch_bf16(const AttnArgs& a0, hipStream_t s) {
   if constexpr (F16) {
-    if (!a0.pre || a0.table) return hipErrorInvalidValue;  // rejected on the host before
+    if (!a0.pre) return hipErrorInvalidValue;  // rejected on the host before
+    if (a0.table) return a0.page == 16 ? launch_stream<D, NW, 16, true>(a0, s) : launch_stream<D, NW, 32, true>(a0, s);
     return launch_stream<D, NW, 0, true>(a0, s);
   }
   if (a0.pre) {  // stream scheme
@@ -2094,7 +2095,6 @@ static spec_status_t verify_attention(const void* q, const void* k_new, const vo
   if (B < 1 || Hq < 1 || Hkv < 1 || n_q < 1 || D < 1 || max_T < 1 || max_len_hint < 0) return SPEC_ERR_ARG;
   if (Hq % Hkv != 0) return SPEC_ERR_ARG;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16 && dtype != SPEC_F16) return SPEC_ERR_ARG;
-  if (dtype == SPEC_F16 && table) return SPEC_ERR_UNSUPPORTED;  // paged: bf16 only
   if (!(scale > 0.f) || !isfinite(scale)) return SPEC_ERR_ARG;
   const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_new) |
                        reinterpret_cast<uintptr_t>(v_new) | reinterpret_cast<uintptr_t>(k_cache) |
@@ -2178,7 +2178,7 @@ extern "C" spec_status_t spec_verify_attention_paged(const void* q, const void* 
   if (!block_table) return SPEC_ERR_ARG;
   if (page_size != 16 && page_size != 32) return SPEC_ERR_UNSUPPORTED;
   if (num_pages < 1 || max_blocks < 1) return SPEC_ERR_ARG;
-  if (dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
+  if (dtype != SPEC_BF16 && dtype != SPEC_F16) return SPEC_ERR_UNSUPPORTED;
   // The logical capacity of a sequence is max_blocks pages.
   const long cap = (long)max_blocks * page_size;
   if (cap > 0x7fffffffL) return SPEC_ERR_ARG;

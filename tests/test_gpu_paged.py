@@ -153,15 +153,23 @@ def test_status_codes():
     assert e.value.status == 3
 
 
-def test_long_caches_merged_in_launch_equal_contiguous():
-    """Shares long enough that the stream launch merges each slab's pieces
-    itself: the paged kernel must give the contiguous kernel's bits (which
-    tests/test_gpu_attention.py checks against the oracle at the same shape),
-    with empty, ragged, full-hint and rejected lengths, pages at random slots."""
-    cfg = W.Config(95, "merge", B=20, gamma=8, V=1, dtype="bf16", Hq=64, Hkv=8, D=128, L=(8192, 32768),
-                   max_T=32800)
-    hint, page, n_q = 32768, 32, cfg.n_q
-    _case("paged merge-in-launch", B=cfg.B, page=page, hint=hint)
+@pytest.mark.parametrize("dtype,kind", [("bf16", "long"), ("f16", "long"), ("f16", "short")])
+def test_paged_equals_contiguous_device_built(dtype, kind):
+    """The paged kernel must give the contiguous kernel's bits (which
+    tests/test_gpu_attention.py checks against the oracle), with empty,
+    ragged, full-hint and rejected lengths and pages at random slots: long
+    shares (the launch merges each slab's pieces itself) and short ones (a
+    combine launch), bf16 and fp16 caches."""
+    if kind == "long":
+        cfg = W.Config(95, "merge", B=20, gamma=8, V=1, dtype=dtype, Hq=64, Hkv=8, D=128, L=(8192, 32768),
+                       max_T=32800)
+        hint = 32768
+    else:
+        cfg = W.Config(94, "short", B=6, gamma=4, V=1, dtype=dtype, Hq=32, Hkv=8, D=128, L=(100, 3000),
+                       max_T=3040)
+        hint = 3000
+    page, n_q = 32, cfg.n_q
+    _case("paged vs contiguous", dtype=dtype, kind=kind, B=cfg.B, page=page, hint=hint)
     d = W.attention_inputs_device(cfg, "cuda")
     for b, L in ((1, 0), (2, 31), (3, hint + 1), (4, hint)):
         d["lens"][b] = L
@@ -172,7 +180,7 @@ def test_long_caches_merged_in_launch_equal_contiguous():
     num_pages = sum(need) + 3
     perm = torch.from_numpy(rng.permutation(num_pages)).to("cuda")
     table = torch.full((cfg.B, max_blocks), -7, dtype=torch.int32, device="cuda")
-    pages = [torch.full((cfg.Hkv, num_pages, page, cfg.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pages = [torch.full((cfg.Hkv, num_pages, page, cfg.D), float("nan"), dtype=d["k_cache"].dtype, device="cuda")
              for _ in range(2)]
     k = 0
     for b in range(cfg.B):
@@ -191,7 +199,7 @@ def test_long_caches_merged_in_launch_equal_contiguous():
     torch.cuda.synchronize()
     assert torch.equal(out_p.view(torch.int16), out_c.view(torch.int16))
     assert torch.isnan(out_p[3].float()).all()
-    for b in (0, 4, 19):  # the appended rows landed in the tabled slots
+    for b in (0, 4, cfg.B - 1):  # the appended rows landed in the tabled slots
         L = int(lens[b])
         for t in range(n_q):
             slot = int(table[b, (L + t) // page])
