@@ -53,6 +53,9 @@ typedef enum {
   SPEC_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch          */
 } spec_status_t;
 
+/* Element type of the tensors a call reads and writes: fp32, bf16, or IEEE
+ * half (SPEC_F16: the verify attention entry points only; the sampler takes
+ * SPEC_F32 and SPEC_BF16 logits). */
 typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1, SPEC_F16 = 2 } spec_dtype_t;
 
 /* Library version, e.g. "specverify 0.1.0 gfx950". Static string. */
