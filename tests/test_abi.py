@@ -56,6 +56,11 @@ def test_workspace_sizes():
     assert sv.reject_sample_workspace_size(256, 8, 128256, 1) > 0
     assert sv.reject_sample_workspace_size(4, 0, 10, 0) == 0
     assert sv.reject_sample_workspace_size(4, 32, 10, 0) == 0
+    # fp16 (2): the attention's stream scheme sizes it as bf16; the sampler refuses it
+    assert sv.verify_attention_workspace_size(256, 64, 8, 9, 128, 32768, 2) == \
+        sv.verify_attention_workspace_size(256, 64, 8, 9, 128, 32768, 1)
+    assert sv.verify_attention_workspace_size(4, 4, 2, 5, 24, 100, 2) == 0  # fp16 D=24
+    assert sv.reject_sample_workspace_size(256, 8, 128256, 2) == 0
     # a workspace sized for a hint serves every smaller hint
     big = sv.verify_attention_workspace_size(32, 32, 8, 5, 128, 4096, 1)
     for h in range(0, 4097, 97):
