@@ -37,8 +37,12 @@ Modules:
 
 Parity status: every function here is pinned by ``-m "not gpu"`` tests against
 printed values of the pages, closed forms, library routines or brute force.
-Nothing is "parity unpinned" except the mapping of decisions that fall inside
-the 1e-6 threshold band (those draws are counted, not compared).
+That includes the margin helpers that decide which decisions fall inside the
+1e-6 threshold band (tests/test_oracle_band.py: a margin below eps is exactly
+a decision that a shift of eps would change) and the band probability that
+bounds how many sequences a comparison may leave out.  Nothing is "parity
+unpinned" except the mapping of the decisions inside that band: those draws
+are counted and bounded, not compared.
 """
 
 from . import attention, bf16, formulas, greedy, model, paged, quant, round, sampler, truncate  # noqa: F401

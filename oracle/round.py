@@ -35,12 +35,13 @@ from . import sampler as S
 
 
 def _draw(z, temperature, u):
-    """Token drawn from softmax(z / T) at u (argmax at T = 0), and its margin."""
+    """Token drawn from softmax(z / T) at u (argmax at T = 0), its margin and the
+    probability that a uniform lands inside the band around its boundaries."""
     if temperature == 0.0:
-        return G.argmax(z), float("inf")
+        return G.argmax(z), float("inf"), 0.0
     w = S.softmax_t(z, temperature)
     t = S.inverse_cdf(w, u)
-    return t, S.cdf_margin(w, t, float(u))
+    return t, S.cdf_margin(w, t, float(u)), S.band_probability(w, S.BAND)
 
 
 def propose(flat_d, cfg_d, seq, dkv, dlen, gamma, temperature, u_draft):
@@ -48,21 +49,22 @@ def propose(flat_d, cfg_d, seq, dkv, dlen, gamma, temperature, u_draft):
 
     dkv: the draft cache of this sequence [L, 2, 1, H, max_T, D] (fp64, updated
     in place).  Returns (proposals, draft logits [gamma, V], new dlen, the
-    smallest draw margin).
+    smallest draw margin, the summed band probability of the draws).
     """
     pending = list(seq[dlen:])
-    xs, zs, margin = [], [], float("inf")
+    xs, zs, margin, band = [], [], float("inf"), 0.0
     for j in range(gamma):
         lg, new = M.forward_cached(flat_d, cfg_d, np.array([pending]), dkv, [dlen])
         dkv[...] = new
         dlen += len(pending)
         z = lg[0, -1]
-        x, m = _draw(z, temperature, u_draft[j])
+        x, m, bp = _draw(z, temperature, u_draft[j])
         xs.append(x)
         zs.append(z)
         margin = min(margin, m)
+        band += bp
         pending = [x]
-    return xs, np.array(zs), dlen, margin
+    return xs, np.array(zs), dlen, margin, band
 
 
 def speculative_round(flat_t, cfg_t, flat_d, cfg_d, state, gamma, temperature, u_draft, u_verify):
@@ -73,17 +75,18 @@ def speculative_round(flat_t, cfg_t, flat_d, cfg_d, state, gamma, temperature, u
     u_draft [B, gamma], u_verify [B, gamma+1] fp64.
     Returns dict n_accepted [B], tokens (list of emitted lists), min_margin [B]
     (smallest decisive margin of the round: draft draws, accept tests and the
-    final draw).
+    final draw) and band_prob [B] (the summed chance of those decisions
+    landing inside the band).
     """
     B = len(state["seq"])
     n_acc = np.zeros(B, dtype=np.int64)
-    emitted, margins = [], np.full(B, np.inf)
+    emitted, margins, bands = [], np.full(B, np.inf), np.zeros(B)
     for b in range(B):
         seq = state["seq"][b]
         L = len(seq)
         assert state["tlen"][b] == L - 1 and L - 2 <= state["dlen"][b] <= L - 1
         dkv = state["dkv"][:, :, b : b + 1]
-        xs, zd, dlen, m_draft = propose(flat_d, cfg_d, seq, dkv, int(state["dlen"][b]), gamma, temperature,
+        xs, zd, dlen, m_draft, b_draft = propose(flat_d, cfg_d, seq, dkv, int(state["dlen"][b]), gamma, temperature,
                                         u_draft[b])
         state["dkv"][:, :, b : b + 1] = dkv
         tkv = state["tkv"][:, :, b : b + 1]
@@ -91,18 +94,24 @@ def speculative_round(flat_t, cfg_t, flat_d, cfg_d, state, gamma, temperature, u
         state["tkv"][:, :, b : b + 1] = tkv
         if temperature == 0.0:
             n, toks = G.verify_sequence(zt[0], xs)
-            m_ver = float("inf")
+            m_ver, b_ver = float("inf"), 0.0
         else:
             r = S.verify_sequence(zt[0], zd, xs, u_verify[b], temperature)
             n, toks = r["n_accepted"], r["tokens"]
             m_ver = min(r["accept_margins"] + [r["draw_margin"]])
+            b_ver = r["band_prob"]
         seq += toks
-        state["tlen"][b] = L - 1 + 1 + n  # tc.truncate(base + 1 + nacc)
-        state["dlen"][b] = min(dlen, len(seq) - 1)  # dc.truncate(min(dc.n, len(seq) - 1))
+        # The target cache keeps the rows of the committed tokens before the
+        # newest one: its old length, the verified last token and the n
+        # accepted proposals.  The draft cache keeps what it holds, at most
+        # up to that same point.
+        state["tlen"][b] = L - 1 + 1 + n
+        state["dlen"][b] = min(dlen, len(seq) - 1)
         n_acc[b] = n
         emitted.append(toks)
         margins[b] = min(m_draft, m_ver)
-    return {"n_accepted": n_acc, "tokens": emitted, "min_margin": margins}
+        bands[b] = b_draft + b_ver
+    return {"n_accepted": n_acc, "tokens": emitted, "min_margin": margins, "band_prob": bands}
 
 
 def start(flat_t, cfg_t, flat_d, cfg_d, prompts, max_T_t, max_T_d):

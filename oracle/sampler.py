@@ -40,6 +40,12 @@ import numpy as np
 
 from .bf16 import to_f64
 
+# Decisions whose uniform lies closer than this to its threshold are counted,
+# not compared, between the GPU and this oracle (fp32 versus fp64 rounding may
+# flip them; [P3] section 受理・棄却の規則と出力分布が変わらない理由 notes that
+# floating-point differences can change such outputs).
+BAND = 1e-6
+
 
 def softmax_t(z, temperature):
     """softmax(z / T) in fp64 with the maximum subtracted; T > 0."""
@@ -78,13 +84,52 @@ def cdf_margin(w, t, u):
     """Distance of ``u`` from the two CDF boundaries of token ``t``.
 
     Returns min(|u - C_{t-1}/C_last|, |u - C_t/C_last|) with C_{-1} = 0.  The
-    GPU parity rule exempts draws with a margin below 1e-6.
+    GPU parity rule exempts draws with a margin below 1e-6.  Since the draw
+    puts u in [C_{t-1}/C_last, C_t/C_last), this is the distance from u to the
+    nearest point of {0, C_0/C_last, ..., C_last/C_last}: the smallest shift of
+    u that changes the drawn token or leaves [0, 1).
     """
     c = np.cumsum(w)
     c = c / c[-1]
     lo = c[t - 1] if t > 0 else 0.0
     hi = c[t]
     return float(min(abs(u - lo), abs(u - hi)))
+
+
+def accept_margin(u, threshold):
+    """Distance of ``u`` from the accept threshold min(1, p/q): the smallest
+    shift of u that changes the strict test.  A NaN threshold rejects every u,
+    so no shift changes it: the margin is infinite."""
+    m = abs(np.float64(u) - np.float64(threshold))
+    return float("inf") if np.isnan(m) else float(m)
+
+
+def accept_band_probability(threshold, eps):
+    """Probability that a uniform u on [0, 1) lands within ``eps`` of the accept
+    threshold: the length of (thr - eps, thr + eps) inside [0, 1)."""
+    thr = np.float64(threshold)
+    if np.isnan(thr):
+        return 0.0
+    return float(max(0.0, min(1.0, thr + eps) - max(0.0, thr - eps)))
+
+
+def band_probability(w, eps):
+    """Probability that a uniform u on [0, 1) gives an inverse-CDF draw from the
+    weights ``w`` whose ``cdf_margin`` is below ``eps``.
+
+    That is the length of the set of u in [0, 1) within ``eps`` of a point of
+    {0, C_0/C_last, ..., C_last/C_last} (the union of the intervals of
+    half-width eps around the CDF boundaries, clipped to [0, 1)).  Used to
+    bound how many sequences the 1e-6 band may take out of a comparison.
+    """
+    c = np.cumsum(np.asarray(w, dtype=np.float64))
+    pts = np.concatenate(([0.0], c / c[-1]))
+    lo = np.maximum(pts - eps, 0.0)
+    hi = np.minimum(pts + eps, 1.0)
+    # The points are sorted, so both ends of the intervals are too: interval i
+    # adds what reaches past the end of interval i-1.
+    new = np.maximum(hi[1:] - np.maximum(lo[1:], hi[:-1]), 0.0)
+    return float(hi[0] - lo[0] + np.sum(new))
 
 
 def verify_sequence(z_target, z_draft, draft_tokens, uniforms, temperature):
@@ -98,6 +143,9 @@ def verify_sequence(z_target, z_draft, draft_tokens, uniforms, temperature):
     and draft probabilities of every draft token), and margins: the distance of
     every decisive uniform from its threshold (accept tests that were evaluated,
     then the final draw), plus whether the zero-residual fallback fired.
+    ``band_prob`` sums, over the same decisions, the probability that a uniform
+    lands within BAND of the threshold (an upper bound on the chance that this
+    sequence falls inside the band, given the decisions it took).
     """
     gamma = len(draft_tokens)
     z_target = to_f64(z_target)
@@ -110,12 +158,11 @@ def verify_sequence(z_target, z_draft, draft_tokens, uniforms, temperature):
     q_x = np.array([q[i][x[i]] for i in range(gamma)], dtype=np.float64)
 
     n = 0
-    accept_margins = []
+    accept_margins, band_prob = [], 0.0
     for i in range(gamma):
         thr = accept_threshold(p_x[i], q_x[i])
-        # A NaN threshold (p = q = 0) rejects for every u: no band around it.
-        m = abs(np.float64(uniforms[i]) - thr)
-        accept_margins.append(float("inf") if np.isnan(m) else float(m))
+        accept_margins.append(accept_margin(uniforms[i], thr))
+        band_prob += accept_band_probability(thr, BAND)
         if not accepts(uniforms[i], thr):
             break
         n += 1
@@ -136,6 +183,7 @@ def verify_sequence(z_target, z_draft, draft_tokens, uniforms, temperature):
         "q_x": q_x,
         "accept_margins": accept_margins,
         "draw_margin": cdf_margin(w, t, float(uniforms[gamma])),
+        "band_prob": band_prob + band_probability(w, BAND),
         "fallback": fallback,
     }
 
@@ -146,7 +194,8 @@ def verify_batch(z_target, z_draft, draft_tokens, uniforms, temperature, seqs=No
     Shapes: z_target [B, gamma+1, V], z_draft [B, gamma, V], draft_tokens
     [B, gamma], uniforms [B, gamma+1].  Returns arrays n_accepted [S],
     out_tokens [S, gamma+1] (n+1 valid tokens then -1), p_x/q_x [S, gamma],
-    min_margin [S] (smallest decisive margin of the sequence) and fallback [S].
+    min_margin [S] (smallest decisive margin of the sequence), band_prob [S]
+    and fallback [S].
     """
     B, gamma = np.asarray(draft_tokens).shape
     seqs = range(B) if seqs is None else list(seqs)
@@ -156,6 +205,7 @@ def verify_batch(z_target, z_draft, draft_tokens, uniforms, temperature, seqs=No
     p_x = np.zeros((S, gamma))
     q_x = np.zeros((S, gamma))
     margin = np.zeros(S)
+    band_prob = np.zeros(S)
     fallback = np.zeros(S, dtype=bool)
     for k, b in enumerate(seqs):
         r = verify_sequence(z_target[b], z_draft[b], draft_tokens[b], uniforms[b], temperature)
@@ -164,6 +214,7 @@ def verify_batch(z_target, z_draft, draft_tokens, uniforms, temperature, seqs=No
         p_x[k] = r["p_x"]
         q_x[k] = r["q_x"]
         margin[k] = min(r["accept_margins"] + [r["draw_margin"]])
+        band_prob[k] = r["band_prob"]
         fallback[k] = r["fallback"]
     return {
         "n_accepted": n_acc,
@@ -171,5 +222,6 @@ def verify_batch(z_target, z_draft, draft_tokens, uniforms, temperature, seqs=No
         "p_x": p_x,
         "q_x": q_x,
         "min_margin": margin,
+        "band_prob": band_prob,
         "fallback": fallback,
     }

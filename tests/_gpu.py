@@ -29,11 +29,24 @@ def as_f64(a):
     return obf16.to_f64(a)
 
 
+def band_bound(expected):
+    """Largest number of sequences the band may take out of one comparison.
+
+    Whether a sequence falls in the band is a Bernoulli draw of probability at
+    most its oracle ``band_prob`` (the length of the band around each decision
+    it took), so the count has mean at most ``expected``; the bound adds five
+    Poisson standard deviations and three.  A margin helper that returned 0
+    would exclude every sequence and fail this.
+    """
+    return int(np.floor(expected + 5.0 * np.sqrt(expected) + 3.0))
+
+
 def compare_sampler(orc, n_gpu, tok_gpu, p_gpu=None, q_gpu=None, seqs=None):
     """Compare GPU sampler outputs with the oracle's (``oracle.sampler.verify_batch``).
 
-    Returns a dict of counts; asserts that no sequence outside the band differs
-    and that p/q agree within P_RTOL.
+    Returns a dict of counts; asserts that the band holds no more sequences than
+    ``band_bound`` allows, that no sequence outside the band differs, and that
+    p/q agree within P_RTOL.
     """
     seqs = np.arange(len(n_gpu)) if seqs is None else np.asarray(seqs)
     n_g = np.asarray(n_gpu)[seqs]
@@ -41,13 +54,18 @@ def compare_sampler(orc, n_gpu, tok_gpu, p_gpu=None, q_gpu=None, seqs=None):
     band = orc["min_margin"] < BAND
     same = (n_g == orc["n_accepted"]) & np.all(t_g == orc["out_tokens"], axis=1)
     bad = ~same & ~band
+    expected = float(np.sum(orc["band_prob"]))
     stats = {
         "sequences": int(len(seqs)),
         "in_band": int(band.sum()),
+        "band_expected": expected,
+        "band_bound": band_bound(expected),
         "band_disagree": int((~same & band).sum()),
         "mismatch_outside_band": int(bad.sum()),
         "fallback": int(orc["fallback"].sum()),
     }
+    print(f"[compare_sampler] {stats}", flush=True)
+    assert stats["in_band"] <= stats["band_bound"], ("more sequences in the band than its bound", stats)
     assert not bad.any(), (stats, np.nonzero(bad)[0][:10], n_g[bad][:5], orc["n_accepted"][bad][:5])
     for got, want, name in ((p_gpu, orc["p_x"], "p"), (q_gpu, orc["q_x"], "q")):
         if got is None:

@@ -7,8 +7,9 @@ except for a sequence whose round had a decisive draw within 1e-6 of its
 threshold in the oracle (a draft draw, an accept test or the final draw);
 such a sequence is counted and left out from that round on (its state may
 then differ).  After the last round the committed tokens and the target
-cache's prefix rows must agree (rows within 1e-4).  Every case prints its
-name first.
+cache's prefix rows must agree (rows within 1e-4).  The number of sequences
+left out must stay within the band's bound (tests/_gpu.band_bound of the
+oracle's summed band probabilities).  Every case prints its name first.
 """
 
 import ctypes
@@ -20,6 +21,7 @@ import torch
 import speculative_decoding_verification_spec_amd as sv
 from oracle import model as M
 from oracle import round as R
+from tests import _gpu
 from workloads import gen
 
 pytestmark = pytest.mark.gpu
@@ -64,7 +66,7 @@ def test_rounds_match_oracle(T, gamma, rounds, models):
     }
     tp, dp = torch.from_numpy(pt).to(dev), torch.from_numpy(pd).to(dev)
     live = np.ones(B, bool)
-    band = 0
+    band, band_expected = 0, 0.0
     for r in range(rounds):
         ud = rng.random((B, gamma))
         uv = rng.random((B, gamma + 1))
@@ -77,6 +79,7 @@ def test_rounds_match_oracle(T, gamma, rounds, models):
         for b in range(B):
             if not live[b]:
                 continue
+            band_expected += res["band_prob"][b]
             if res["min_margin"][b] < BAND:
                 live[b] = False
                 band += 1
@@ -84,7 +87,9 @@ def test_rounds_match_oracle(T, gamma, rounds, models):
             want = res["tokens"][b]
             assert n_g[b] == res["n_accepted"][b], (r, b)
             assert list(tok_g[b, : len(want)]) == want and (tok_g[b, len(want):] == -1).all(), (r, b)
-    print(f"sequences left out by the 1e-6 band: {band} of {B}; n per round, last: {list(n_g)}", flush=True)
+    print(f"sequences left out by the 1e-6 band: {band} of {B} (expected {band_expected:.3g}); "
+          f"n per round, last: {list(n_g)}", flush=True)
+    assert band <= _gpu.band_bound(band_expected)
     assert live.sum() >= B // 2
     seq_g, len_g = g["seq"].cpu().numpy(), g["seq_len"].cpu().numpy()
     tl_g, dl_g = g["tlen"].cpu().numpy(), g["dlen"].cpu().numpy()

@@ -267,8 +267,8 @@ def test_draft_cache_kept_at_full_length_is_caught(monkeypatch):
     real = RO.propose
 
     def lying(*a, **k):
-        xs, zs, dlen, m = real(*a, **k)
-        return xs, zs, dlen + 1, m
+        xs, zs, dlen, m, band = real(*a, **k)
+        return xs, zs, dlen + 1, m, band
 
     monkeypatch.setattr(RO, "propose", lying)
     _assert_pin_fails(TR.test_draft_equal_to_target_accepts_everything)
