@@ -23,14 +23,22 @@ calls ``ln_fwd`` and ``gelu`` without defining them; the readings here are
 GPT-2's: LayerNorm over the last axis with the population variance and
 eps = 1e-5, and GELU in its tanh form.
 
-Parameters are one flat array in the order of ``param_shapes``:
-  wte [V, C], wpe [T, C],
-  per layer: ln1_g [C], ln1_b [C], wqkv [C, 3C], wo [C, C], ln2_g [C],
-             ln2_b [C], w1 [C, F], b1 [F], w2 [F, C], b2 [C],
-  lnf_g [C], lnf_b [C], wout [C, V].
-wqkv's columns are q, then k, then v, each head-major (head h owns columns
-[h D, (h+1) D) of its third).  Caches are [L][2][B][H][max_T][D] (layer,
-k/v, sequence, head, position, dimension).
+Parameters are one flat array in the order of ``param_shapes`` (the packing
+is this build's choice, defined again independently by the library):
+  token embedding [V, C], position embedding [T, C],
+  per block: norm1 gain [C], bias [C]; attention in [C, 3C]; attention
+             out [C, C]; norm2 gain [C], bias [C]; MLP up [C, F], up bias
+             [F]; MLP down [F, C], down bias [C],
+  final norm gain [C], bias [C], unembedding [C, V].
+The attention-in matrix's columns are q, then k, then v, each head-major
+(head h owns columns [h D, (h+1) D) of its third).  Caches are
+[L][2][B][H][max_T][D] (layer, k/v, sequence, head, position, dimension).
+
+Structure: the parameters are unpacked into a ``Model`` of ``Block``s; one
+function, ``_block``, is a whole residual block given how attention sees the
+keys, and the cached and uncached forwards differ only in that: the cached one
+writes the block's new key/value rows into the cache and attends over the
+cache's first p0 + n rows, the uncached one over the sequence's own rows.
 """
 
 from dataclasses import dataclass
@@ -46,7 +54,7 @@ class ModelConfig:
     C: int  # width
     L: int  # layers
     H: int  # heads
-    T: int  # positions (rows of wpe)
+    T: int  # positions (rows of the position embedding)
 
     @property
     def F(self):
@@ -65,16 +73,16 @@ DRAFT = ModelConfig(V=96, C=48, L=1, H=2, T=512)
 def param_shapes(cfg):
     """Ordered (name, shape) list of the flat parameter array."""
     C, F, V, T = cfg.C, cfg.F, cfg.V, cfg.T
-    out = [("wte", (V, C)), ("wpe", (T, C))]
+    out = [("token_embedding", (V, C)), ("position_embedding", (T, C))]
     for l in range(cfg.L):
         out += [
-            (f"{l}.ln1_g", (C,)), (f"{l}.ln1_b", (C,)),
-            (f"{l}.wqkv", (C, 3 * C)), (f"{l}.wo", (C, C)),
-            (f"{l}.ln2_g", (C,)), (f"{l}.ln2_b", (C,)),
-            (f"{l}.w1", (C, F)), (f"{l}.b1", (F,)),
-            (f"{l}.w2", (F, C)), (f"{l}.b2", (C,)),
+            (f"block{l}.norm1.gain", (C,)), (f"block{l}.norm1.bias", (C,)),
+            (f"block{l}.attn.in", (C, 3 * C)), (f"block{l}.attn.out", (C, C)),
+            (f"block{l}.norm2.gain", (C,)), (f"block{l}.norm2.bias", (C,)),
+            (f"block{l}.mlp.up", (C, F)), (f"block{l}.mlp.up_bias", (F,)),
+            (f"block{l}.mlp.down", (F, C)), (f"block{l}.mlp.down_bias", (C,)),
         ]
-    out += [("lnf_g", (C,)), ("lnf_b", (C,)), ("wout", (C, V))]
+    out += [("final_norm.gain", (C,)), ("final_norm.bias", (C,)), ("unembedding", (C, V))]
     return out
 
 
@@ -86,12 +94,64 @@ def unpack(flat, cfg):
     """Dict name -> fp64 array from the flat parameter array."""
     flat = np.asarray(flat, dtype=np.float64)
     assert flat.shape == (param_count(cfg),)
-    P, off = {}, 0
+    named, off = {}, 0
     for name, shape in param_shapes(cfg):
         n = int(np.prod(shape))
-        P[name] = flat[off : off + n].reshape(shape)
+        named[name] = flat[off : off + n].reshape(shape)
         off += n
-    return P
+    return named
+
+
+@dataclass
+class Norm:
+    gain: np.ndarray
+    bias: np.ndarray
+
+    def __call__(self, x):
+        return layer_norm(x, self.gain, self.bias)
+
+
+@dataclass
+class Block:
+    norm1: Norm
+    attn_in: np.ndarray    # [C, 3C]: q | k | v, each head-major
+    attn_out: np.ndarray   # [C, C]
+    norm2: Norm
+    up: np.ndarray         # [C, F]
+    up_bias: np.ndarray    # [F]
+    down: np.ndarray       # [F, C]
+    down_bias: np.ndarray  # [C]
+
+
+@dataclass
+class Model:
+    cfg: ModelConfig
+    token_embedding: np.ndarray     # [V, C]
+    position_embedding: np.ndarray  # [T, C]
+    blocks: list
+    final_norm: Norm
+    unembedding: np.ndarray         # [C, V]
+
+    def embed(self, tokens, first_position):
+        """Token plus position embedding of tokens at first_position, +1, ..."""
+        pos = np.arange(first_position, first_position + len(tokens))
+        return self.token_embedding[np.asarray(tokens)] + self.position_embedding[pos]
+
+    def logits(self, x):
+        return self.final_norm(x) @ self.unembedding
+
+
+def model_from_flat(flat, cfg):
+    """The flat parameter array as a ``Model``."""
+    named = unpack(flat, cfg)
+    blocks = []
+    for l in range(cfg.L):
+        g = lambda k: named[f"block{l}.{k}"]  # noqa: E731
+        blocks.append(Block(Norm(g("norm1.gain"), g("norm1.bias")), g("attn.in"), g("attn.out"),
+                            Norm(g("norm2.gain"), g("norm2.bias")), g("mlp.up"), g("mlp.up_bias"),
+                            g("mlp.down"), g("mlp.down_bias")))
+    return Model(cfg, named["token_embedding"], named["position_embedding"], blocks,
+                 Norm(named["final_norm.gain"], named["final_norm.bias"]), named["unembedding"])
 
 
 def layer_norm(x, g, b):
@@ -111,15 +171,43 @@ def softmax(s):
     return e / e.sum(axis=-1, keepdims=True)
 
 
-def _attend(q, K, V, p0):
-    """q [H, n, D] against K, V [H, p0+n, D]; new row i sees keys [0, p0+i]."""
+def _heads(m, H):
+    """[n, C] -> [H, n, D]: head h takes columns [h D, (h+1) D)."""
+    n, C = m.shape
+    return m.reshape(n, H, C // H).transpose(1, 0, 2)
+
+
+def _unheads(a):
+    """[H, n, D] -> [n, H D]."""
+    H, n, D = a.shape
+    return a.transpose(1, 0, 2).reshape(n, H * D)
+
+
+def _causal_attention(q, keys, values, first):
+    """q [H, n, D] against keys/values [H, first + n, D]: the query of new
+    position first + i sees keys [0, first + i], scores scaled by 1/sqrt(D)."""
     H, n, D = q.shape
-    out = np.zeros_like(q)
+    out = np.empty_like(q)
     for i in range(n):
-        m = p0 + i + 1
-        s = np.einsum("hd,hkd->hk", q[:, i], K[:, :m]) / np.sqrt(D)
-        out[:, i] = np.einsum("hk,hkd->hd", softmax(s), V[:, :m])
+        visible = first + i + 1
+        s = np.einsum("hd,hkd->hk", q[:, i], keys[:, :visible]) / np.sqrt(D)
+        out[:, i] = np.einsum("hk,hkd->hd", softmax(s), values[:, :visible])
     return out
+
+
+def _block(blk, x, H, keys_values):
+    """One pre-norm residual block on the rows x [n, C].
+
+    ``keys_values(k, v)`` receives the rows' own key and value heads [H, n, D]
+    and returns the keys, values and first position the rows attend over.
+    """
+    C = x.shape[1]
+    proj = blk.norm1(x) @ blk.attn_in
+    q, k, v = (_heads(proj[:, j * C : (j + 1) * C], H) for j in range(3))
+    keys, values, first = keys_values(k, v)
+    x = x + _unheads(_causal_attention(q, keys, values, first)) @ blk.attn_out
+    hidden = gelu(blk.norm2(x) @ blk.up + blk.up_bias)
+    return x + hidden @ blk.down + blk.down_bias
 
 
 def forward_cached(flat, cfg, tokens, kv, lens):
@@ -129,26 +217,23 @@ def forward_cached(flat, cfg, tokens, kv, lens):
     are never read), lens [B] the cache length p0 of each sequence.  Returns
     (logits fp64, kv fp64 copy with rows [p0, p0+n) of every layer written).
     """
-    P = unpack(flat, cfg)
-    C, H, D = cfg.C, cfg.H, cfg.D
+    model = model_from_flat(flat, cfg)
     tokens = np.asarray(tokens)
     B, n = tokens.shape
     kv = np.array(kv, dtype=np.float64, copy=True)
     logits = np.zeros((B, n, cfg.V))
     for b in range(B):
         p0 = int(lens[b])
-        x = P["wte"][tokens[b]] + P["wpe"][p0 : p0 + n]
-        for l in range(cfg.L):
-            h = layer_norm(x, P[f"{l}.ln1_g"], P[f"{l}.ln1_b"])
-            qkv = h @ P[f"{l}.wqkv"]
-            q, k, v = (qkv[:, j * C : (j + 1) * C].reshape(n, H, D).transpose(1, 0, 2) for j in range(3))
-            kv[l, 0, b, :, p0 : p0 + n] = k
-            kv[l, 1, b, :, p0 : p0 + n] = v
-            y = _attend(q, kv[l, 0, b, :, : p0 + n], kv[l, 1, b, :, : p0 + n], p0)
-            x = x + y.transpose(1, 0, 2).reshape(n, C) @ P[f"{l}.wo"]
-            h2 = layer_norm(x, P[f"{l}.ln2_g"], P[f"{l}.ln2_b"])
-            x = x + gelu(h2 @ P[f"{l}.w1"] + P[f"{l}.b1"]) @ P[f"{l}.w2"] + P[f"{l}.b2"]
-        logits[b] = layer_norm(x, P["lnf_g"], P["lnf_b"]) @ P["wout"]
+
+        def through_cache(k, v, layer):
+            kv[layer, 0, b, :, p0 : p0 + n] = k
+            kv[layer, 1, b, :, p0 : p0 + n] = v
+            return kv[layer, 0, b, :, : p0 + n], kv[layer, 1, b, :, : p0 + n], p0
+
+        x = model.embed(tokens[b], p0)
+        for layer, blk in enumerate(model.blocks):
+            x = _block(blk, x, cfg.H, lambda k, v: through_cache(k, v, layer))
+        logits[b] = model.logits(x)
     return logits, kv
 
 
@@ -159,20 +244,11 @@ def forward_uncached(flat, cfg, tokens):
     numpyで小さなTransformerを自作する, the uncached version it compares
     against): every position attends to itself and all earlier positions.
     """
-    P = unpack(flat, cfg)
-    C, H, D = cfg.C, cfg.H, cfg.D
-    tokens = np.asarray(tokens)
-    n = tokens.shape[0]
-    x = P["wte"][tokens] + P["wpe"][:n]
-    for l in range(cfg.L):
-        h = layer_norm(x, P[f"{l}.ln1_g"], P[f"{l}.ln1_b"])
-        qkv = h @ P[f"{l}.wqkv"]
-        q, k, v = (qkv[:, j * C : (j + 1) * C].reshape(n, H, D).transpose(1, 0, 2) for j in range(3))
-        y = _attend(q, k, v, 0)
-        x = x + y.transpose(1, 0, 2).reshape(n, C) @ P[f"{l}.wo"]
-        h2 = layer_norm(x, P[f"{l}.ln2_g"], P[f"{l}.ln2_b"])
-        x = x + gelu(h2 @ P[f"{l}.w1"] + P[f"{l}.b1"]) @ P[f"{l}.w2"] + P[f"{l}.b2"]
-    return layer_norm(x, P["lnf_g"], P["lnf_b"]) @ P["wout"]
+    model = model_from_flat(flat, cfg)
+    x = model.embed(np.asarray(tokens), 0)
+    for blk in model.blocks:
+        x = _block(blk, x, cfg.H, lambda k, v: (k, v, 0))
+    return model.logits(x)
 
 
 def empty_cache(cfg, B, max_T):

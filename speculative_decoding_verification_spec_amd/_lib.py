@@ -350,12 +350,13 @@ def model_param_layout(model):
     layout documented with spec_model_param_count)."""
     m = _model(model)
     C, F, V, T = m.C, 4 * m.C, m.V, m.T
-    out = [("wte", (V, C)), ("wpe", (T, C))]
+    out = [("token_embedding", (V, C)), ("position_embedding", (T, C))]
     for l in range(m.L):
-        out += [(f"{l}.ln1_g", (C,)), (f"{l}.ln1_b", (C,)), (f"{l}.wqkv", (C, 3 * C)), (f"{l}.wo", (C, C)),
-                (f"{l}.ln2_g", (C,)), (f"{l}.ln2_b", (C,)), (f"{l}.w1", (C, F)), (f"{l}.b1", (F,)),
-                (f"{l}.w2", (F, C)), (f"{l}.b2", (C,))]
-    out += [("lnf_g", (C,)), ("lnf_b", (C,)), ("wout", (C, V))]
+        out += [(f"block{l}.norm1.gain", (C,)), (f"block{l}.norm1.bias", (C,)), (f"block{l}.attn.in", (C, 3 * C)),
+                (f"block{l}.attn.out", (C, C)), (f"block{l}.norm2.gain", (C,)), (f"block{l}.norm2.bias", (C,)),
+                (f"block{l}.mlp.up", (C, F)), (f"block{l}.mlp.up_bias", (F,)), (f"block{l}.mlp.down", (F, C)),
+                (f"block{l}.mlp.down_bias", (C,))]
+    out += [("final_norm.gain", (C,)), ("final_norm.bias", (C,)), ("unembedding", (C, V))]
     return out
 
 

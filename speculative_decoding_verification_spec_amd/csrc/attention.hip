@@ -865,6 +865,7 @@ __device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, in
     const int row = e / D4, d = 4 * (e % D4);
     float mx = neg_inf_f(), den = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    bool flagged = false;  // a piece that met a bad page entry left m = NaN
     for (int j0 = 0; j0 < np; j0 += 4) {
       float2 ml[4];
       f32x4 po[4];
@@ -876,7 +877,9 @@ __device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, in
         const float2 lo = in ? co_load2(a.part_o + pj * D + d) : make_float2(0.f, 0.f);
         const float2 hi = in ? co_load2(a.part_o + pj * D + d + 2) : make_float2(0.f, 0.f);
         po[t] = f32x4{lo.x, lo.y, hi.x, hi.y};
+        flagged |= ml[t].x != ml[t].x;
       }
+      // fmaxf drops NaN: the flag above, not the maxima, carries it
       const float mc = fmaxf(fmaxf(ml[0].x, ml[1].x), fmaxf(ml[2].x, ml[3].x));
       const float mn = fmaxf(mx, mc);
       if (mn == neg_inf_f()) continue;  // no visible key in these pieces yet
@@ -891,7 +894,7 @@ __device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, in
       }
       mx = mn;
     }
-    acc *= 1.f / den;
+    acc *= flagged ? __builtin_nanf("") : 1.f / den;
     const int m = row0 + row;
     uint2 pk;
     pk.x = uint32_t(H::bits(acc[0])) | (uint32_t(H::bits(acc[1])) << 16);
@@ -1416,6 +1419,7 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
     // (the piece count is only known at run time).
     float mx = neg_inf_f(), den = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    bool flagged = false;  // a piece that met a bad page entry left m = NaN
     for (int j0 = 0; j0 < np; j0 += 4) {
       ML ml[4];
       f32x4 po[4];
@@ -1425,7 +1429,9 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
         const size_t pj = (base + j0 + t) * rows + row;
         ml[t] = in ? a.part_ml[pj] : ML{neg_inf_f(), 0.f};
         po[t] = in ? *reinterpret_cast<const f32x4*>(a.part_o + pj * D + d) : f32x4{0.f, 0.f, 0.f, 0.f};
+        flagged |= ml[t].m != ml[t].m;
       }
+      // fmaxf drops NaN: the flag above, not the maxima, carries it
       const float mc = fmaxf(fmaxf(ml[0].m, ml[1].m), fmaxf(ml[2].m, ml[3].m));
       const float mn = fmaxf(mx, mc);
       if (mn == neg_inf_f()) continue;  // no visible key in these pieces yet
@@ -1440,7 +1446,7 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
       }
       mx = mn;
     }
-    acc *= 1.f / den;
+    acc *= flagged ? __builtin_nanf("") : 1.f / den;
     uint2 pk;
     pk.x = uint32_t(H::bits(acc[0])) | (uint32_t(H::bits(acc[1])) << 16);
     pk.y = uint32_t(H::bits(acc[2])) | (uint32_t(H::bits(acc[3])) << 16);
@@ -1884,9 +1890,10 @@ static StreamPlan stream_plan(int B, int Hkv, int RG, int RT, int n_q, int D, in
 // workgroups per CU.  Residency is the occupancy query's answer, further
 // limited because the waves of a workgroup are spread round-robin over the 4
 // SIMDs of a CU: a workgroup of NW waves puts ceil(NW / 4) on one SIMD, which
-// holds 512 / VGPRs waves.  Cached per device.
-template <typename K>
-static int stream_workgroups(K kernel, int NW, int max_per_cu) {
+// holds 512 / VGPRs waves.  Cached per kernel (the template argument) and
+// device.
+template <auto kernel>
+static int stream_workgroups(int NW, int max_per_cu) {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -1924,7 +1931,7 @@ static hipError_t launch_stream_as(const AttnArgs& a0, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  a.P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG, kMerge, F16>, NW, SPECV_BF16_PER_CU);
+  a.P = stream_workgroups<attn_stream_bf16<D, NW, kStages, PG, kMerge, F16>>(NW, SPECV_BF16_PER_CU);
   hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG, kMerge, F16>), dim3((unsigned)a.P), dim3(64 * NW), 0, s,
                      a, a.table);
   hipError_t e = hipGetLastError();
@@ -1944,7 +1951,7 @@ static hipError_t launch_stream(const AttnArgs& a, hipStream_t s) {
   if constexpr (SPECV_STREAM_MERGE != 0) {
     const long nbmax = ((long)a.hint + a.n_q + KB - 1) / KB;
     const long wmax = (long)a.B * a.Hkv * a.RG * nbmax;
-    const int P = stream_workgroups(attn_stream_bf16<D, NW, kStages, PG, true, F16>, NW, SPECV_BF16_PER_CU);
+    const int P = stream_workgroups<attn_stream_bf16<D, NW, kStages, PG, true, F16>>(NW, SPECV_BF16_PER_CU);
     if (wmax >= (long)SPECV_MERGE_MIN_SHARE * P) return launch_stream_as<D, NW, PG, true, F16>(a, s);
   }
   return launch_stream_as<D, NW, PG, false, F16>(a, s);
@@ -1956,7 +1963,7 @@ static hipError_t launch_i8(const AttnArgs& a0, hipStream_t s) {
   hipLaunchKernelGGL((quant_new_rows<D>), dim3((unsigned)((size_t)a.B * a.Hkv)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.P = stream_workgroups(attn_stream_i8<D, NW, SPECV_I8_STAGES>, NW, 3);
+  a.P = stream_workgroups<attn_stream_i8<D, NW, SPECV_I8_STAGES>>(NW, 3);
   hipLaunchKernelGGL((attn_stream_i8<D, NW, SPECV_I8_STAGES>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

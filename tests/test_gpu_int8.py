@@ -42,8 +42,10 @@ def _check(inp, res, seqs=None, relative=False):
     # new row) are held to the tolerance relative to their magnitude.
     norm = np.maximum(1.0, np.abs(want)) if relative else 1.0
     err = np.max(np.abs(got - want) / norm)
-    print("max abs err" + (" (relative above 1)" if relative else ""), err, flush=True)
+    rel = _gpu.row_rel_err(got, want)
+    print("max abs err" + (" (relative above 1)" if relative else ""), err, "max row rel err", rel, flush=True)
     assert np.all(np.isfinite(got)) and err < _gpu.ATT_TOL["bf16"]
+    assert rel < _gpu.ROW_REL_TOL["bf16"], rel
     kq, ks, vq, vs = Q.kv_append_int8(inp["k_cache"], inp["k_scale"], inp["v_cache"], inp["v_scale"],
                                       inp["k_new"], inp["v_new"], inp["lens"])
     for name, want_a in (("k_cache", kq), ("k_scale", ks), ("v_cache", vq), ("v_scale", vs)):
@@ -78,6 +80,43 @@ def test_shapes(B, Hq, Hkv, n_q, D, lens):
                    max_T=max_T)
     inp = W.attention_inputs_int8(cfg, B=B, max_T=max_T, lens=lens)
     _check(inp, _run(inp))
+
+
+def test_config5_shape_sampled():
+    """The shape the benchmark times: 256 sequences of 8K-32K int8 keys per KV
+    head, long shares whose pieces are merged; 18 sequences compared (the
+    shortest, the longest, 16 at random), each copied to the host alone."""
+    cfg = W.get(5)
+    _case("int8 config5", B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, max_T=cfg.max_T)
+    d = W.attention_inputs_int8_device(cfg, "cuda")
+    lens = _gpu.to_host(d["lens"])
+    seqs = [int(np.argmin(lens)), int(np.argmax(lens))]
+    seqs += [int(b) for b in np.random.default_rng(6).permutation(cfg.B) if b not in seqs][:16]
+    n = cfg.n_q
+    before = {}
+    for b in seqs:
+        L = int(lens[b])
+        before[b] = {k: _gpu.to_host(d[k][b : b + 1, :, :L]) for k in ("k_cache", "k_scale", "v_cache", "v_scale")}
+    out = sv.spec_verify_attention_int8(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["k_scale"], d["v_cache"],
+                                        d["v_scale"], d["lens"], cfg.L[1])
+    torch.cuda.synchronize()
+    for b in seqs:
+        L = int(lens[b])
+        print(f"sequence {b} L={L}", end=": ", flush=True)
+        inp = {k: _gpu.to_host(d[k][b : b + 1]) for k in ("q", "k_new", "v_new")}
+        inp["lens"] = np.array([L], np.int32)
+        # the rows the call may write ([L, L + n)) start from the oracle's own
+        # copy of the input rows; everything else is the input as it was
+        for k in ("k_cache", "k_scale", "v_cache", "v_scale"):
+            after = _gpu.to_host(d[k][b : b + 1, :, : L + n])
+            pre = after.copy()
+            pre[:, :, :L] = before[b][k]
+            inp[k] = pre
+        res = {"out": _gpu.to_host(out[b : b + 1]),
+               **{k: _gpu.to_host(d[k][b : b + 1, :, : L + n]) for k in ("k_cache", "k_scale", "v_cache", "v_scale")}}
+        _check(inp, res)
+    del d
+    torch.cuda.empty_cache()
 
 
 def test_zero_and_loud_new_rows():

@@ -81,9 +81,7 @@ def _check(inp, page, res, skip=()):
     seqs = [b for b in range(len(lens)) if b not in skip]
     want = P.verify_attention_paged(inp["q"], inp["k_new"], inp["v_new"], kp, vp, table, lens, seqs=seqs)
     got = _gpu.as_f64(out[seqs])
-    err = np.max(np.abs(got - want))
-    print("max abs err", err, flush=True)
-    assert np.all(np.isfinite(got)) and err < _gpu.ATT_TOL["bf16"]
+    _gpu.check_attention(got, want, "bf16")
     assert np.array_equal(out[seqs], ref[seqs])  # same bits as the contiguous kernel
     # the new rows, and nothing else, were written
     kw, vw = P.kv_append_paged(kp, vp, inp["k_new"][seqs], inp["v_new"][seqs], table[seqs], lens[seqs])
@@ -153,13 +151,10 @@ def test_status_codes():
     assert e.value.status == 3
 
 
-@pytest.mark.parametrize("dtype,kind", [("bf16", "long"), ("f16", "long"), ("f16", "short")])
-def test_paged_equals_contiguous_device_built(dtype, kind):
-    """The paged kernel must give the contiguous kernel's bits (which
-    tests/test_gpu_attention.py checks against the oracle), with empty,
-    ragged, full-hint and rejected lengths and pages at random slots: long
-    shares (the launch merges each slab's pieces itself) and short ones (a
-    combine launch), bf16 and fp16 caches."""
+def _device_paged(dtype, kind):
+    """Device inputs of a long (merged in the launch) or short (combine launch)
+    batch with empty, ragged, full-hint and rejected lengths, and their pages
+    at random slots (32 positions a page; unused slots NaN)."""
     if kind == "long":
         cfg = W.Config(95, "merge", B=20, gamma=8, V=1, dtype=dtype, Hq=64, Hkv=8, D=128, L=(8192, 32768),
                        max_T=32800)
@@ -169,7 +164,6 @@ def test_paged_equals_contiguous_device_built(dtype, kind):
                        max_T=3040)
         hint = 3000
     page, n_q = 32, cfg.n_q
-    _case("paged vs contiguous", dtype=dtype, kind=kind, B=cfg.B, page=page, hint=hint)
     d = W.attention_inputs_device(cfg, "cuda")
     for b, L in ((1, 0), (2, 31), (3, hint + 1), (4, hint)):
         d["lens"][b] = L
@@ -194,6 +188,19 @@ def test_paged_equals_contiguous_device_built(dtype, kind):
                 dst[:, idx[:nf]] = src[b, :, : nf * page].reshape(cfg.Hkv, nf, page, cfg.D)
             if L % page:
                 dst[:, idx[nf], : L % page] = src[b, :, nf * page : L]
+    return cfg, hint, page, d, lens, need, table, pages
+
+
+@pytest.mark.parametrize("dtype,kind", [("bf16", "long"), ("f16", "long"), ("f16", "short")])
+def test_paged_equals_contiguous_device_built(dtype, kind):
+    """The paged kernel must give the contiguous kernel's bits (which
+    tests/test_gpu_attention.py checks against the oracle), with empty,
+    ragged, full-hint and rejected lengths and pages at random slots: long
+    shares (the launch merges each slab's pieces itself) and short ones (a
+    combine launch), bf16 and fp16 caches."""
+    _case("paged vs contiguous", dtype=dtype, kind=kind)
+    cfg, hint, page, d, lens, need, table, pages = _device_paged(dtype, kind)
+    n_q = cfg.n_q
     out_p = sv.spec_verify_attention_paged(d["q"], d["k_new"], d["v_new"], pages[0], pages[1], table, d["lens"], hint)
     out_c = sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], hint)
     torch.cuda.synchronize()
@@ -205,3 +212,22 @@ def test_paged_equals_contiguous_device_built(dtype, kind):
             slot = int(table[b, (L + t) // page])
             assert torch.equal(pages[0][:, slot, (L + t) % page], d["k_cache"][b, :, L + t])
             assert torch.equal(pages[1][:, slot, (L + t) % page], d["v_cache"][b, :, L + t])
+
+
+@pytest.mark.parametrize("kind", ["long", "short"])
+def test_bad_entries_over_the_first_pieces_flag_the_sequence(kind):
+    """Bad page entries over the first 60% of a long sequence's table: every
+    piece that meets one leaves NaN, and the merge of the slab's pieces (in
+    the launch or in the combine launch) must keep the NaN even when a whole
+    group of the first pieces it merges together is flagged.  The other
+    sequences keep the contiguous kernel's bits."""
+    _case("paged bad first pieces", kind=kind)
+    cfg, hint, page, d, lens, need, table, pages = _device_paged("bf16", kind)
+    bad = 4  # length = hint: the longest table
+    table[bad, : need[bad] * 6 // 10] = 10 ** 6
+    out_p = sv.spec_verify_attention_paged(d["q"], d["k_new"], d["v_new"], pages[0], pages[1], table, d["lens"], hint)
+    out_c = sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], hint)
+    torch.cuda.synchronize()
+    assert torch.isnan(out_p[bad].float()).all()
+    good = [b for b in range(cfg.B) if b not in (3, bad)]
+    assert torch.equal(out_p[good].view(torch.int16), out_c[good].view(torch.int16))

@@ -57,7 +57,7 @@ def test_model_attention_matches_attention_oracle():
     q = r.standard_normal((H, n, D))
     K = r.standard_normal((H, p0 + n, D))
     V = r.standard_normal((H, p0 + n, D))
-    got = M._attend(q, K, V, p0)
+    got = M._causal_attention(q, K, V, p0)
     kc = np.zeros((1, H, p0 + n, D))
     vc = np.zeros((1, H, p0 + n, D))
     kc[0, :, :p0] = K[:, :p0]
@@ -123,8 +123,8 @@ def _zeroed(cfg, flat):
     """Parameters with every block's matrices zero (the stream passes through)."""
     P = {k: v.copy() for k, v in M.unpack(flat, cfg).items()}
     for l in range(cfg.L):
-        for k in ("wqkv", "wo", "w1", "w2"):
-            P[f"{l}.{k}"][:] = 0.0
+        for k in ("attn.in", "attn.out", "mlp.up", "mlp.down"):
+            P[f"block{l}.{k}"][:] = 0.0
     return np.concatenate([P[name].ravel() for name, _ in M.param_shapes(cfg)]), P
 
 
@@ -133,34 +133,35 @@ def _ln(x, g, b, eps=1e-5):
 
 
 def test_residual_stream_closed_form():
-    """With zero block matrices each block adds only b2: the logits of token t
-    at position p are LNf(wte[t] + wpe[p] + sum_l b2_l) wout."""
+    """With zero block matrices each block adds only its MLP down bias: the
+    logits of token t at position p are LNf(E_tok[t] + E_pos[p] + sum_l
+    down_bias_l) W_unembed."""
     cfg = M.TARGET
     flat, P = _zeroed(cfg, _params(cfg, 11))
     tok, p = 17, 5
     kv = np.zeros((cfg.L, 2, 1, cfg.H, 8, cfg.D))
     got, _ = M.forward_cached(flat, cfg, np.array([[tok]]), kv, [p])
-    x = P["wte"][tok] + P["wpe"][p] + sum(P[f"{l}.b2"] for l in range(cfg.L))
-    want = _ln(x, P["lnf_g"], P["lnf_b"]) @ P["wout"]
+    x = P["token_embedding"][tok] + P["position_embedding"][p] + sum(P[f"block{l}.mlp.down_bias"] for l in range(cfg.L))
+    want = _ln(x, P["final_norm.gain"], P["final_norm.bias"]) @ P["unembedding"]
     np.testing.assert_allclose(got[0, 0], want, rtol=0, atol=1e-12)
 
 
 def test_value_path_and_head_layout_closed_form():
     """One layer, first token (p0 = 0, one key): attention returns v exactly,
-    so x = e + v wo with v = LN1(e) wqkv[:, 2C:3C] -- and the cache rows hold
-    k and v split by head as [h, d] = column h D + d of their thirds."""
+    so x = e + v W_out with v = LN1(e) W_in[:, 2C:3C] -- and the cache rows
+    hold k and v split by head as [h, d] = column h D + d of their thirds."""
     cfg = M.ModelConfig(V=11, C=8, L=1, H=2, T=4)
     flat = gen.model_params(M.param_shapes(cfg), 12).astype(np.float64)
     P = M.unpack(flat, cfg)
     kv = np.zeros((1, 2, 1, 2, 4, 4))
     got_logits, got_kv = M.forward_cached(flat, cfg, np.array([[3]]), kv, [0])
-    e = P["wte"][3] + P["wpe"][0]
-    h = _ln(e, P["0.ln1_g"], P["0.ln1_b"])
-    k, v = h @ P["0.wqkv"][:, 8:16], h @ P["0.wqkv"][:, 16:24]
+    e = P["token_embedding"][3] + P["position_embedding"][0]
+    h = _ln(e, P["block0.norm1.gain"], P["block0.norm1.bias"])
+    k, v = h @ P["block0.attn.in"][:, 8:16], h @ P["block0.attn.in"][:, 16:24]
     np.testing.assert_allclose(got_kv[0, 0, 0, :, 0], k.reshape(2, 4), rtol=0, atol=1e-12)
     np.testing.assert_allclose(got_kv[0, 1, 0, :, 0], v.reshape(2, 4), rtol=0, atol=1e-12)
-    x = e + v @ P["0.wo"]
-    u = M.gelu(_ln(x, P["0.ln2_g"], P["0.ln2_b"]) @ P["0.w1"] + P["0.b1"])
-    x = x + u @ P["0.w2"] + P["0.b2"]
-    want = _ln(x, P["lnf_g"], P["lnf_b"]) @ P["wout"]
+    x = e + v @ P["block0.attn.out"]
+    u = M.gelu(_ln(x, P["block0.norm2.gain"], P["block0.norm2.bias"]) @ P["block0.mlp.up"] + P["block0.mlp.up_bias"])
+    x = x + u @ P["block0.mlp.down"] + P["block0.mlp.down_bias"]
+    want = _ln(x, P["final_norm.gain"], P["final_norm.bias"]) @ P["unembedding"]
     np.testing.assert_allclose(got_logits[0, 0], want, rtol=0, atol=1e-12)

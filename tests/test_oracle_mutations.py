@@ -234,7 +234,7 @@ def test_unscaled_model_attention_is_caught(monkeypatch):
             out[:, i] = np.einsum("hk,hkd->hd", MO.softmax(s), V[:, :m])
         return out
 
-    monkeypatch.setattr(MO, "_attend", unscaled)
+    monkeypatch.setattr(MO, "_causal_attention", unscaled)
     _assert_pin_fails(TM.test_model_attention_matches_attention_oracle)
 
 
@@ -247,7 +247,7 @@ def test_model_attention_seeing_the_next_key_is_caught(monkeypatch):
             out[:, i] = np.einsum("hk,hkd->hd", MO.softmax(s), V[:, :m])
         return out
 
-    monkeypatch.setattr(MO, "_attend", peeks)
+    monkeypatch.setattr(MO, "_causal_attention", peeks)
     _assert_pin_fails(TM.test_model_attention_matches_attention_oracle)
 
 

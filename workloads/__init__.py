@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     attention_inputs,
     attention_inputs_device,
     attention_inputs_int8,
+    attention_inputs_int8_device,
     bf16_bits,
     sampler_inputs,
     sampler_inputs_device,

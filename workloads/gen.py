@@ -223,6 +223,38 @@ def attention_inputs_int8(cfg: Config, rep: int = 0, B=None, max_T=None, lens=No
     return out
 
 
+def attention_inputs_int8_device(cfg: Config, device, rep: int = 0, B=None):
+    """Device tensors for verify attention over an int8 cache, with the recipe
+    of ``attention_inputs_int8``: q, k_new, v_new N(0, 1) in the workload's
+    16-bit type, lens from the host stream 3, int8 codes of N(0, 1) rows with
+    one code of magnitude 127 per row, fp16 scales 2.7 / 127 times a
+    log-normal factor of spread 0.1.  Drawn sequence by sequence from a seeded
+    device stream (4) so no full-size 16-bit cache is ever formed."""
+    import torch
+
+    B = cfg.B if B is None else int(B)
+    dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(cfg.dtype, torch.float32)
+    g = _torch_gen(cfg, 4, rep, device)
+    n, D, T, Hkv = cfg.n_q, cfg.D, cfg.max_T, cfg.Hkv
+
+    def draw(*shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dt)
+
+    out = {"q": draw(B, cfg.Hq, n, D), "k_new": draw(B, Hkv, n, D), "v_new": draw(B, Hkv, n, D),
+           "lens": torch.from_numpy(lengths(cfg, rep, B)).to(device)}
+    for name in ("k", "v"):
+        codes = torch.empty((B, Hkv, T, D), dtype=torch.int8, device=device)
+        for b in range(B):
+            c = torch.clamp(torch.round(torch.randn((Hkv, T, D), generator=g, device=device) * (127 / 2.7)), -127, 127)
+            pos = torch.randint(0, D, (Hkv, T, 1), generator=g, device=device)
+            sign = torch.where(torch.rand((Hkv, T, 1), generator=g, device=device) < 0.5, -127.0, 127.0)
+            codes[b] = c.scatter(2, pos, sign).to(torch.int8)
+        out[f"{name}_cache"] = codes
+        out[f"{name}_scale"] = (torch.exp(0.1 * torch.randn((B, Hkv, T), generator=g, device=device))
+                                * (2.7 / 127)).to(torch.float16)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # the verify forward of a decoder model (random weights)
 # ---------------------------------------------------------------------------
@@ -232,7 +264,7 @@ def model_params(shapes, seed: int):
     """Random fp32 weights for a packed parameter layout.
 
     ``shapes`` is the ordered (name, shape) list of the layout.  Matrices are
-    N(0, 1/rows); LayerNorm gains (names ending in ``_g``) 1 + N(0, 0.1^2);
+    N(0, 1/rows); LayerNorm gains (names ending in ``gain``) 1 + N(0, 0.1^2);
     every other vector N(0, 0.1^2).  Stream 5 of ``default_rng([seed, 5])``.
     """
     r = np.random.default_rng([int(seed), 5])
@@ -240,7 +272,7 @@ def model_params(shapes, seed: int):
     for name, shape in shapes:
         if len(shape) == 2:
             a = r.standard_normal(shape) / np.sqrt(shape[0])
-        elif name.endswith("_g"):
+        elif name.endswith("gain"):
             a = 1.0 + 0.1 * r.standard_normal(shape)
         else:
             a = 0.1 * r.standard_normal(shape)
