@@ -207,9 +207,9 @@ size_t spec_reject_sample_workspace_size(int B, int gamma, int V, spec_dtype_t d
  *   the smallest j with C_j / C_{V-1} > u, C the prefix sum of the weights.
  *
  * T == 0 is greedy verification, [P2] section 投機的デコーディングとは (the
- * listing omits its temperature-0 branch; the results after it state that the
- * test becomes "the target's argmax equals the draft" and that the output
- * equals greedy decoding of the target alone):
+ * listing omits its temperature-0 branch; the results after it say that the
+ * test then checks whether the draft token is the target's most likely token,
+ * and that the output is then the target's own greedy decoding):
  *   position i is accepted iff argmax target_logits[b][i] == x_i; n as above;
  *   the final token is argmax target_logits[b][n].  argmax is the first index
  *   of the largest value (values compared exactly; -0 == +0; NaN is largest).
@@ -277,11 +277,13 @@ typedef struct {
 
 /* Floats in the packed fp32 parameter array of `model` (0 for an invalid
  * shape).  The array holds, in this order and each row-major:
- *   wte [V][C], wpe [T][C],
- *   per layer: ln1_g [C], ln1_b [C], wqkv [C][3C], wo [C][C], ln2_g [C],
- *              ln2_b [C], w1 [C][4C], b1 [4C], w2 [4C][C], b2 [C],
- *   lnf_g [C], lnf_b [C], wout [C][V].
- * wqkv's columns are q, then k, then v; within each third, head h owns the
+ *   token embedding E_tok [V][C], position embedding E_pos [T][C],
+ *   per block: norm1 gain [C], norm1 bias [C], attention-in W_in [C][3C],
+ *              attention-out W_out [C][C], norm2 gain [C], norm2 bias [C],
+ *              MLP up W_up [C][4C], up bias [4C], MLP down W_down [4C][C],
+ *              down bias [C],
+ *   final norm gain [C], final norm bias [C], unembedding W_vocab [C][V].
+ * W_in's columns are q, then k, then v; within each third, head h owns the
  * columns [h D, (h+1) D). */
 size_t spec_model_param_count(const spec_model_t* model);
 
@@ -292,12 +294,13 @@ size_t spec_verify_forward_workspace_size(const spec_model_t* model, int B, int 
  * numpyで小さなTransformerを自作する (for the verify call, the n = gamma+1
  * tokens [last committed token] + drafts, [P2] section 投機的デコーディングとは).
  * For sequence b with p0 = cache_len[b]:
- *   x_i = wte[tokens[b][i]] + wpe[p0 + i]
- *   per layer: h = LN1(x); q, k, v = h wqkv (split in thirds, then by head);
- *     the K/V rows go to positions [p0, p0+n) of the layer's cache; new row i
- *     attends to positions [0, p0+i] with scores scaled by 1/sqrt(D);
- *     x += (heads concatenated) wo; x += gelu(LN2(x) w1 + b1) w2 + b2
- *   logits = LNf(x) wout
+ *   x_i = E_tok[tokens[b][i]] + E_pos[p0 + i]
+ *   per block: h = norm1(x); q, k, v = h W_in (split in thirds, then by
+ *     head); the K/V rows go to positions [p0, p0+n) of the layer's cache;
+ *     new row i attends to positions [0, p0+i] with scores scaled by
+ *     1/sqrt(D); x += (heads concatenated) W_out;
+ *     x += gelu(norm2(x) W_up + up bias) W_down + down bias
+ *   logits = final_norm(x) W_vocab
  * LayerNorm: (x - mean) / sqrt(var + 1e-5) * g + b over C (population
  * variance); gelu(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  All
  * arithmetic is fp32 (the attention as spec_verify_attention with SPEC_F32).

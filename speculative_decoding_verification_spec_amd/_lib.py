@@ -14,8 +14,7 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# SPECV_LIB selects another build of the same library (e.g. a tuning variant).
-LIB_PATH = os.environ.get("SPECV_LIB") or os.path.join(_HERE, "libspecverify.so")
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SPEC_OK, SPEC_ERR_ARG, SPEC_ERR_OVERFLOW, SPEC_ERR_UNSUPPORTED, SPEC_ERR_LAUNCH = range(5)
 SPEC_F32, SPEC_BF16, SPEC_F16 = 0, 1, 2

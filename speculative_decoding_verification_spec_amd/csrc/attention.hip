@@ -279,23 +279,16 @@ __device__ __forceinline__ float group_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-#ifndef SPECV_ATTN_WPE
-#define SPECV_ATTN_WPE 4
-#endif
-#ifndef SPECV_I8_STAGES
-#define SPECV_I8_STAGES 2  // raw int8 stages: with two bf16 buffers, 2 keep the kernel in 128 VGPRs
-#endif
+// Waves per SIMD the compiler budgets registers for: 4 keeps a kernel within
+// 128 VGPRs, so two 5-wave workgroups share a CU.
+constexpr int kAttnWavesPerEU = 4;
+constexpr int kStreamWavesPerEU = 4;
+// Raw int8 stages: with two bf16 buffers, 2 keep the kernel in 128 VGPRs.
+constexpr int kI8Stages = 2;
 // Cache policy of the cache-block loads, which stream every key once per
 // call: non-temporal (nt = 2).
-#ifndef SPECV_KV_CPOL
-#define SPECV_KV_CPOL 2
-#endif
-#ifndef SPECV_I8_CPOL
-#define SPECV_I8_CPOL 2
-#endif
-#ifndef SPECV_STREAM_WPE
-#define SPECV_STREAM_WPE 4
-#endif
+constexpr int kKvCachePolicy = 2;
+constexpr int kI8CachePolicy = 2;
 
 // One LDS object per stage and tensor: reads of one stage then provably do
 // not alias the asynchronous copies into another, so the compiler does not
@@ -477,7 +470,7 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc((void*)cbase, (short)0, (PG == 16 ? 16 : KB) * D * 2, 0x00020000);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3)))*)dst, 16,
-                                                 (int)(loff * 2), 0, 0, SPECV_KV_CPOL);
+                                                 (int)(loff * 2), 0, 0, kKvCachePolicy);
       } else {  // new rows from k_new/v_new; keys past the end read a finite dummy row
         const int crow = (int)(coff[i] / D);
         const int key = kb + crow;
@@ -682,7 +675,7 @@ __device__ __forceinline__ void bf16_piece(const AttnArgs& a, KBuf kbuf, VBuf vb
 }
 
 template <int D, int NW, int NST>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_ATTN_WPE)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kAttnWavesPerEU)))
 void attn_split_bf16(AttnArgs a) {
   using LY = BfLayout<D>;
   SPECV_BF16_STAGE_LDS
@@ -906,7 +899,7 @@ __device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, in
 // MERGE: the pieces of a slab are merged by the last of its workgroups
 // (stream_merge) instead of by attn_combine_stream.
 template <int D, int NW, int NST, int PG, bool MERGE, bool F16 = false>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kStreamWavesPerEU)))
 void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
   using LY = BfLayout<D>;
   SPECV_BF16_STAGE_LDS
@@ -1076,7 +1069,7 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
         const __amdgpu_buffer_rsrc_t rsrc =
             __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (size_t)kb * D), (short)0, KB * D, 0x00020000);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3)))*)dst, 16, (int)boff,
-                                                 0, 0, SPECV_I8_CPOL);
+                                                 0, 0, kI8CachePolicy);
       } else {
         const int key = kb + (int)(boff / D);
         const int8_t* fresh = is_v ? vnb : knb;
@@ -1375,7 +1368,7 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
 }
 
 template <int D, int NW, int NST>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(SPECV_STREAM_WPE)))
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kStreamWavesPerEU)))
 void attn_stream_i8(AttnArgs a) {
   SPECV_I8_STAGE_LDS
   stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append, int) {
@@ -1465,11 +1458,9 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
 
 // Blocks of K/V held per wave (one computed, the rest in flight): three at
 // the small head dimensions, where a block takes 28 registers, else two.
-#ifndef SPECV_F32_RING
-#define SPECV_F32_RING 3
-#endif
+constexpr int kF32RingSmallD = 3;  // blocks per wave at D <= 32
 template <int D>
-constexpr int kF32Ring = D <= 32 ? SPECV_F32_RING : 2;
+constexpr int kF32Ring = D <= 32 ? kF32RingSmallD : 2;
 
 // LDS of the in-workgroup merge: every wave's O rows and (max, sum).
 template <int D, int RT, int NWK>
@@ -1761,24 +1752,16 @@ struct SplitPolicy {
   long target;     // aim for about this many work items
 };
 
-#ifndef SPECV_ATTN_ITEMS
-#define SPECV_ATTN_ITEMS 2048
-#endif
-#ifndef SPECV_ATTN_CMAX
-#define SPECV_ATTN_CMAX 8192
-#endif
-#ifndef SPECV_F32_ITEMS
-#define SPECV_F32_ITEMS 8192
-#endif
-#ifndef SPECV_F32_CMIN
-#define SPECV_F32_CMIN 128
-#endif
+constexpr int kSplitItems16 = 2048;   // bf16 fixed splits: aim for this many items
+constexpr int kSplitCmax16 = 8192;    // bf16: longest split
+constexpr int kSplitItemsF32 = 8192;  // fp32: aim for this many items
+constexpr int kSplitCminF32 = 128;    // fp32: shortest split
 
 static SplitPolicy policy(spec_dtype_t dt) {
   // bf16: workgroups of one wave per row tile, a few resident per CU; fp32:
   // single-wave items.
-  return dt != SPEC_F32 ? SplitPolicy{256, SPECV_ATTN_CMAX, SPECV_ATTN_ITEMS}
-                         : SplitPolicy{SPECV_F32_CMIN, 4096, SPECV_F32_ITEMS};
+  return dt != SPEC_F32 ? SplitPolicy{256, kSplitCmax16, kSplitItems16}
+                         : SplitPolicy{kSplitCminF32, 4096, kSplitItemsF32};
 }
 
 static int max_rt(spec_dtype_t dt, int D) {
@@ -1822,33 +1805,20 @@ static AttnPlan attn_plan(int B, int Hq, int Hkv, int n_q, int D, int hint, spec
 
 // Two stages measured faster than three with non-temporal loads (4.6%,
 // 32K-key caches), and halve the LDS.
-#ifndef SPECV_ATTN_STAGES
-#define SPECV_ATTN_STAGES 2
-#endif
-constexpr int kStages = SPECV_ATTN_STAGES;  // LDS stages; blocks in flight per workgroup: kStages - 1
+constexpr int kStages = 2;  // LDS stages; blocks in flight per workgroup: kStages - 1
 
 // ---- stream scheme ---------------------------------------------------------
 
 // Upper bound on the workgroups of a stream launch: 256 CUs, at most 3
 // resident workgroups each (LDS).  The partial slots per slab follow from it,
 // so the workspace size does not depend on the device.
-#ifndef SPECV_STREAM_MAX_WG
-#define SPECV_STREAM_MAX_WG 768
-#endif
 // Workgroups per CU of the bf16 stream kernel.  Its 2-wave build fits 3 per
 // CU but ran faster at 2 (fewer, longer shares: 78 -> 75 us at B = 32 with
 // 1-4K-key caches; 1 and 1.5 per CU were slower everywhere).  The int8
 // kernel keeps 3 (87 us against 109 us at 2).
-#ifndef SPECV_STREAM_MERGE
-#define SPECV_STREAM_MERGE 1  // allow merging a slab's pieces inside the bf16 stream launch
-#endif
-#ifndef SPECV_MERGE_MIN_SHARE
-#define SPECV_MERGE_MIN_SHARE 256  // blocks per workgroup from which the merge is used
-#endif
-#ifndef SPECV_BF16_PER_CU
-#define SPECV_BF16_PER_CU 2
-#endif
-constexpr int kStreamMaxWG = SPECV_STREAM_MAX_WG;
+constexpr int kStreamMaxWG = 768;
+constexpr int kMergeMinShare = 256;  // blocks per workgroup from which the launch merges pieces
+constexpr int kBf16PerCU = 2;        // resident 16-bit stream workgroups per CU
 
 // Sizes the stream scheme handles: every workgroup scans the B lengths, and
 // block counts stay in int.
@@ -1931,7 +1901,7 @@ static hipError_t launch_stream_as(const AttnArgs& a0, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  a.P = stream_workgroups<attn_stream_bf16<D, NW, kStages, PG, kMerge, F16>>(NW, SPECV_BF16_PER_CU);
+  a.P = stream_workgroups<attn_stream_bf16<D, NW, kStages, PG, kMerge, F16>>(NW, kBf16PerCU);
   hipLaunchKernelGGL((attn_stream_bf16<D, NW, kStages, PG, kMerge, F16>), dim3((unsigned)a.P), dim3(64 * NW), 0, s,
                      a, a.table);
   hipError_t e = hipGetLastError();
@@ -1944,16 +1914,14 @@ static hipError_t launch_stream_as(const AttnArgs& a0, hipStream_t s) {
 // (the write-through partials, the count, the last one's merge) and the
 // counters a launch of their own; the combine launch costs a fixed time that
 // grows with the slab count.  Merge when a workgroup's share can reach
-// SPECV_MERGE_MIN_SHARE blocks (measured: 32K-key caches, B = 256: 3.36 ->
+// kMergeMinShare blocks (measured: 32K-key caches, B = 256: 3.36 ->
 // 3.32 ms; 1-4K-key caches, B = 32: 74 -> 87 us, so those combine).
 template <int D, int NW, int PG, bool F16 = false>
 static hipError_t launch_stream(const AttnArgs& a, hipStream_t s) {
-  if constexpr (SPECV_STREAM_MERGE != 0) {
-    const long nbmax = ((long)a.hint + a.n_q + KB - 1) / KB;
-    const long wmax = (long)a.B * a.Hkv * a.RG * nbmax;
-    const int P = stream_workgroups<attn_stream_bf16<D, NW, kStages, PG, true, F16>>(NW, SPECV_BF16_PER_CU);
-    if (wmax >= (long)SPECV_MERGE_MIN_SHARE * P) return launch_stream_as<D, NW, PG, true, F16>(a, s);
-  }
+  const long nbmax = ((long)a.hint + a.n_q + KB - 1) / KB;
+  const long wmax = (long)a.B * a.Hkv * a.RG * nbmax;
+  const int P = stream_workgroups<attn_stream_bf16<D, NW, kStages, PG, true, F16>>(NW, kBf16PerCU);
+  if (wmax >= (long)kMergeMinShare * P) return launch_stream_as<D, NW, PG, true, F16>(a, s);
   return launch_stream_as<D, NW, PG, false, F16>(a, s);
 }
 
@@ -1963,8 +1931,8 @@ static hipError_t launch_i8(const AttnArgs& a0, hipStream_t s) {
   hipLaunchKernelGGL((quant_new_rows<D>), dim3((unsigned)((size_t)a.B * a.Hkv)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.P = stream_workgroups<attn_stream_i8<D, NW, SPECV_I8_STAGES>>(NW, 3);
-  hipLaunchKernelGGL((attn_stream_i8<D, NW, SPECV_I8_STAGES>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
+  a.P = stream_workgroups<attn_stream_i8<D, NW, kI8Stages>>(NW, 3);
+  hipLaunchKernelGGL((attn_stream_i8<D, NW, kI8Stages>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);

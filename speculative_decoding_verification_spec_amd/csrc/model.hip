@@ -14,16 +14,16 @@
 //
 // Launches, for the M = B*n new rows, 16 rows per workgroup with every
 // intermediate of a row block in LDS:
-//   embed_qkv              x = wte[token] + wpe[position]; then layer 0's
-//                          q | k_new | v_new = LN1(x) wqkv, written head-major
+//   embed_qkv              x = tok_emb[token] + pos_emb[position]; then layer 0's
+//                          q | k_new | v_new = LN1(x) w_in, written head-major
 //                          ([B][H][n][D]) for the attention
 // and per layer:
 //   spec_verify_attention  appends k_new, v_new at [p0, p0+n) of the layer's
 //                          cache and attends (the library's fp32 kernels)
-//   block_mlp              x += O wo (reading O [B][H][n][D] as [M][C]);
-//                          x += gelu(LN2(x) w1 + b1) w2 + b2; then the next
+//   block_mlp              x += O w_out (reading O [B][H][n][D] as [M][C]);
+//                          x += gelu(LN2(x) w_up + b_up) w_down + b_down; then the next
 //                          layer's q | k_new | v_new, or after the last layer
-//                          logits = LNf(x) wout (a launch of its own, gemm,
+//                          logits = LNf(x) w_vocab (a launch of its own, gemm,
 //                          above kFusedVocabMax tokens)
 // The products are fp32 matrix-core tiles (v_mfma_f32_16x16x4_f32: exact
 // fp32 products, fp32 sums); the LayerNorms, biases, GELU, residual adds and
@@ -42,14 +42,14 @@ namespace specv {
 constexpr float kLnEps = 1e-5f;
 
 // Offsets (in floats) of the parameters in the packed array, in the order
-// wte, wpe, per layer (ln1_g, ln1_b, wqkv, wo, ln2_g, ln2_b, w1, b1, w2, b2),
-// lnf_g, lnf_b, wout.
+// tok_emb, pos_emb, per layer (n1_gain, n1_bias, w_in, w_out, n2_gain, n2_bias, w_up, b_up, w_down, b_down),
+// nf_gain, nf_bias, w_vocab.
 struct ModelLayout {
   int V, C, L, H, T, F, D;
-  size_t wte, wpe, lnf_g, lnf_b, wout, total;
-  size_t layer0, layer_stride;  // first layer's ln1_g; floats per layer
+  size_t tok_emb, pos_emb, nf_gain, nf_bias, w_vocab, total;
+  size_t layer0, layer_stride;  // first layer's n1_gain; floats per layer
   // offsets inside a layer
-  size_t ln1_g, ln1_b, wqkv, wo, ln2_g, ln2_b, w1, b1, w2, b2;
+  size_t n1_gain, n1_bias, w_in, w_out, n2_gain, n2_bias, w_up, b_up, w_down, b_down;
 };
 
 static bool model_layout(const spec_model_t* m, ModelLayout* o) {
@@ -64,46 +64,46 @@ static bool model_layout(const spec_model_t* m, ModelLayout* o) {
   l.D = m->C / m->H;
   const size_t C = l.C, F = l.F, V = l.V, T = l.T;
   size_t off = 0;
-  l.wte = off;
+  l.tok_emb = off;
   off += V * C;
-  l.wpe = off;
+  l.pos_emb = off;
   off += T * C;
   l.layer0 = off;
   size_t in = 0;
-  l.ln1_g = in;
+  l.n1_gain = in;
   in += C;
-  l.ln1_b = in;
+  l.n1_bias = in;
   in += C;
-  l.wqkv = in;
+  l.w_in = in;
   in += 3 * C * C;
-  l.wo = in;
+  l.w_out = in;
   in += C * C;
-  l.ln2_g = in;
+  l.n2_gain = in;
   in += C;
-  l.ln2_b = in;
+  l.n2_bias = in;
   in += C;
-  l.w1 = in;
+  l.w_up = in;
   in += C * F;
-  l.b1 = in;
+  l.b_up = in;
   in += F;
-  l.w2 = in;
+  l.w_down = in;
   in += F * C;
-  l.b2 = in;
+  l.b_down = in;
   in += C;
   l.layer_stride = in;
   off += in * (size_t)l.L;
-  l.lnf_g = off;
+  l.nf_gain = off;
   off += C;
-  l.lnf_b = off;
+  l.nf_bias = off;
   off += C;
-  l.wout = off;
+  l.w_vocab = off;
   off += C * V;
   l.total = off;
   *o = l;
   return true;
 }
 
-// x[b n + i][:] = wte[tok[b][i]][:] + wpe[lens[b] + i][:]; an out-of-range
+// x[b n + i][:] = tok_emb[tok[b][i]][:] + pos_emb[lens[b] + i][:]; an out-of-range
 // token or position writes NaN rows (which then reach the logits).
 constexpr int kBM = 32, kBN = 32;    // output tile: 4 waves, 16 x 16 each
 constexpr int kFusedVocabMax = 1024;  // vocabularies projected inside the last layer's launch
@@ -113,8 +113,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 struct GemmArgs {
   const float* A;      // [M][K]
   const float* W;      // [K][N]
-  const float* ln_g;   // LN gain / bias over K
-  const float* ln_b;
+  const float* n_gain;   // LN gain / bias over K
+  const float* n_bias;
   float* out;          // [M][N]
   int M, N, K;
 };
@@ -134,9 +134,7 @@ __device__ __forceinline__ float gelu_tanh(float v) {
 // scalar base, issued without branches four steps ahead (a column past N or a
 // step past the last reads a valid element whose product is discarded), so
 // the compiler waits for the oldest only.
-#ifndef SPECV_W_RING
-#define SPECV_W_RING 4  // steps of W loads in flight per lane group
-#endif
+constexpr int kWRing = 4;  // steps of W loads in flight per lane group
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t w_rsrc(const float* W, int K, int N) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(W), 0, (int)((long)K * N * sizeof(float)), 0x00020000);
@@ -147,7 +145,7 @@ __device__ __forceinline__ f32x4 mfma_tile16(const float* A, int KP, int K, __am
   const int K4 = K / 4;
   const float* Ar = A + lr * KP + lgp * K4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int kRing = SPECV_W_RING;
+  constexpr int kRing = kWRing;
   const int NIT = K4 / 4;
   const uint32_t cbase = (uint32_t)(lgp * K4) * (uint32_t)N + (uint32_t)(col_ok ? col : 0);
   float w[kRing][4];
@@ -207,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       v += d * d;
     }
     const float rstd = 1.f / sqrtf(wave_sum(v) / (float)K + kLnEps);
-    for (int k = lane; k < K; k += kWave) As[r * KP + k] = (As[r * KP + k] - mu) * rstd * g.ln_g[k] + g.ln_b[k];
+    for (int k = lane; k < K; k += kWave) As[r * KP + k] = (As[r * KP + k] - mu) * rstd * g.n_gain[k] + g.n_bias[k];
   }
   __syncthreads();
 
@@ -294,22 +292,19 @@ __device__ __forceinline__ void draw_row(const DrawSpec& dr, const float* z, int
 // Waves of a 16-row block workgroup; each product's 16-column tiles are dealt
 // round-robin over them (16: 0.16 -> 0.14 ms per forward of the 4-layer
 // width-96 model against 8, and 4 were slower still).
-#ifndef SPECV_ROW_BLOCK_WAVES
-#define SPECV_ROW_BLOCK_WAVES 16
-#endif
-constexpr int kRowWaves = SPECV_ROW_BLOCK_WAVES;
+constexpr int kRowWaves = 16;
 static_assert(16 % kRowWaves == 0 || kRowWaves % 16 == 0, "rows per wave");
 
 // The product that follows a block of 16 rows held in LDS, by kRowWaves waves:
-// LayerNorm of the rows (ln_g, ln_b) into Hs, then
-//   NEXT_QKV:    q | k_new | v_new = Hs wqkv (the next layer's), written
+// LayerNorm of the rows (n_gain, n_bias) into Hs, then
+//   NEXT_QKV:    q | k_new | v_new = Hs w_in (the next layer's), written
 //                head-major ([B][H][n][D]) for its attention;
-//   NEXT_LOGITS: logits = Hs wout ([M][V]);
+//   NEXT_LOGITS: logits = Hs w_vocab ([M][V]);
 //   NEXT_NONE:   nothing (the vocabulary projection runs as its own launch).
 enum { NEXT_NONE = 0, NEXT_QKV = 1, NEXT_LOGITS = 2 };
 struct NextArgs {
   int mode;
-  const float *ln_g, *ln_b, *W;  // W: [C][N]
+  const float *n_gain, *n_bias, *W;  // W: [C][N]
   float *q, *kn, *vn;            // NEXT_QKV
   float* logits;                 // NEXT_LOGITS
   int N;                         // 3C or V
@@ -319,8 +314,8 @@ struct NextArgs {
 
 // LayerNorm of 16 rows (Rs -> Hs, row stride CP), a row per wave at a time:
 // the mean, then the variance about it.
-__device__ __forceinline__ void rows_ln16(const float* Rs, float* Hs, int CP, int C, const float* __restrict__ ln_g,
-                                          const float* __restrict__ ln_b, int wave, int lane) {
+__device__ __forceinline__ void rows_ln16(const float* Rs, float* Hs, int CP, int C, const float* __restrict__ n_gain,
+                                          const float* __restrict__ n_bias, int wave, int lane) {
   for (int r = wave; r < 16; r += kRowWaves) {
     float s = 0.f;
     for (int k = lane; k < C; k += kWave) s += Rs[r * CP + k];
@@ -331,7 +326,7 @@ __device__ __forceinline__ void rows_ln16(const float* Rs, float* Hs, int CP, in
       v += d * d;
     }
     const float rstd = 1.f / sqrtf(wave_sum(v) / (float)C + kLnEps);
-    for (int k = lane; k < C; k += kWave) Hs[r * CP + k] = (Rs[r * CP + k] - mu) * rstd * ln_g[k] + ln_b[k];
+    for (int k = lane; k < C; k += kWave) Hs[r * CP + k] = (Rs[r * CP + k] - mu) * rstd * n_gain[k] + n_bias[k];
   }
 }
 
@@ -341,7 +336,7 @@ __device__ __forceinline__ void next_product(const NextArgs& nx, const float* Rs
                                              int M, int n, int H, int D, int wave, int lane) {
   if (nx.mode == NEXT_NONE) return;  // uniform
   __syncthreads();
-  rows_ln16(Rs, Hs, CP, C, nx.ln_g, nx.ln_b, wave, lane);
+  rows_ln16(Rs, Hs, CP, C, nx.n_gain, nx.n_bias, wave, lane);
   __syncthreads();
   const int lr = lane & 15, lgp = lane >> 4;
   const __amdgpu_buffer_rsrc_t wr = w_rsrc(nx.W, C, nx.N);
@@ -385,7 +380,7 @@ __global__ __launch_bounds__(64) void draw_rows_kernel(DrawSpec dr, const float*
 // LayerNorm and q/k/v product (next_product).  The tokens and positions come
 // from src (TokenSource).
 struct EmbArgs {
-  const float *wte, *wpe;
+  const float *tok_emb, *pos_emb;
   TokenSource src;
   float* x;  // [M][C]
   NextArgs nx;
@@ -437,7 +432,7 @@ __global__ __launch_bounds__(64 * kRowWaves) void embed_qkv_kernel(EmbArgs g) {
       const int t = s_tok[r];
       const long pos = s_pos[r];
       const bool ok = t >= 0 && t < g.V && pos >= 0 && pos < g.T;
-      v = ok ? g.wte[(size_t)t * C + k] + g.wpe[(size_t)pos * C + k] : __builtin_nanf("");
+      v = ok ? g.tok_emb[(size_t)t * C + k] + g.pos_emb[(size_t)pos * C + k] : __builtin_nanf("");
       g.x[(size_t)m * C + k] = v;
     }
     Rs[r * CP + k] = v;
@@ -447,16 +442,16 @@ __global__ __launch_bounds__(64 * kRowWaves) void embed_qkv_kernel(EmbArgs g) {
 
 // The half of a layer after its attention, for 16 rows per workgroup of
 // kRowWaves waves, with every intermediate in LDS:
-//   y = O wo (O read head-major as [M][C]); X = x + y
-//   u = gelu(LN2(X) w1 + b1)
-//   x = X + u w2 + b2
+//   y = O w_out (O read head-major as [M][C]); X = x + y
+//   u = gelu(LN2(X) w_up + b_up)
+//   x = X + u w_down + b_down
 // then the next layer's LayerNorm and q/k/v product, or the final LayerNorm
 // and the vocabulary projection (next_product).  Waves take 16-column tiles
 // of each product in turn (mfma_tile16).
 struct MlpArgs {
   const float* O;  // [B][H][n][D]
   float* x;        // [M][C], updated in place
-  const float *wo, *ln_g, *ln_b, *w1, *b1, *w2, *b2;
+  const float *w_out, *n_gain, *n_bias, *w_up, *b_up, *w_down, *b_down;
   NextArgs nx;
   int M, n, H, D, C, F;
 };
@@ -482,8 +477,8 @@ __global__ __launch_bounds__(64 * kRowWaves) void block_mlp_kernel(MlpArgs g) {
     Os[r * CP + k] = a;
   }
   __syncthreads();
-  {  // X = x + O wo
-    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.wo, C, C);
+  {  // X = x + O w_out
+    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w_out, C, C);
     for (int ct = wave; ct < C / 16; ct += kRowWaves) {
       const int col = 16 * ct + lr;
       const f32x4 acc = mfma_tile16(Os, CP, C, wr, C, col, true, lr, lgp);
@@ -495,27 +490,27 @@ __global__ __launch_bounds__(64 * kRowWaves) void block_mlp_kernel(MlpArgs g) {
     }
   }
   __syncthreads();
-  rows_ln16(Xs, Hs, CP, C, g.ln_g, g.ln_b, wave, lane);  // LN2
+  rows_ln16(Xs, Hs, CP, C, g.n_gain, g.n_bias, wave, lane);  // LN2
   __syncthreads();
-  {  // u = gelu(H w1 + b1)
-    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w1, C, F);
+  {  // u = gelu(H w_up + b_up)
+    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w_up, C, F);
     for (int ct = wave; ct < F / 16; ct += kRowWaves) {
       const int col = 16 * ct + lr;
       const f32x4 acc = mfma_tile16(Hs, CP, C, wr, F, col, true, lr, lgp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Us[(4 * lgp + i) * FP + col] = gelu_tanh(acc[i] + g.b1[col]);
+      for (int i = 0; i < 4; ++i) Us[(4 * lgp + i) * FP + col] = gelu_tanh(acc[i] + g.b_up[col]);
     }
   }
   __syncthreads();
-  {  // x = X + u w2 + b2, also kept in Os (free since the first product)
-    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w2, F, C);
+  {  // x = X + u w_down + b_down, also kept in Os (free since the first product)
+    const __amdgpu_buffer_rsrc_t wr = w_rsrc(g.w_down, F, C);
     for (int ct = wave; ct < C / 16; ct += kRowWaves) {
       const int col = 16 * ct + lr;
       const f32x4 acc = mfma_tile16(Us, FP, F, wr, C, col, true, lr, lgp);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * lgp + i, m = m0 + r;
-        const float xv = Xs[r * CP + col] + acc[i] + g.b2[col];
+        const float xv = Xs[r * CP + col] + acc[i] + g.b_down[col];
         Os[r * CP + col] = xv;
         if (m < g.M) g.x[(size_t)m * C + col] = xv;
       }
@@ -616,9 +611,9 @@ spec_status_t verify_forward(const spec_model_t* model, const float* params, con
     const float* P = params + l.layer0 + (size_t)layer * l.layer_stride;
     NextArgs nx{};
     nx.mode = NEXT_QKV;
-    nx.ln_g = P + l.ln1_g;
-    nx.ln_b = P + l.ln1_b;
-    nx.W = P + l.wqkv;
+    nx.n_gain = P + l.n1_gain;
+    nx.n_bias = P + l.n1_bias;
+    nx.W = P + l.w_in;
     nx.q = q;
     nx.kn = kn;
     nx.vn = vn;
@@ -627,10 +622,10 @@ spec_status_t verify_forward(const spec_model_t* model, const float* params, con
   };
   const unsigned row_blocks = (unsigned)((M + 15) / 16);
 
-  // x = wte[token] + wpe[position]; q | k_new | v_new = LN1(x) wqkv (layer 0)
+  // x = tok_emb[token] + pos_emb[position]; q | k_new | v_new = LN1(x) w_in (layer 0)
   EmbArgs ea{};
-  ea.wte = params + l.wte;
-  ea.wpe = params + l.wpe;
+  ea.tok_emb = params + l.tok_emb;
+  ea.pos_emb = params + l.pos_emb;
   ea.src = src;
   ea.x = x;
   ea.nx = qkv_of(0);
@@ -655,25 +650,25 @@ spec_status_t verify_forward(const spec_model_t* model, const float* params, con
                                                    p.attn_bytes, stream);
     if (st != SPEC_OK) return st;
 
-    // x += O wo; x += gelu(LN2(x) w1 + b1) w2 + b2; then the next layer's
+    // x += O w_out; x += gelu(LN2(x) w_up + b_up) w_down + b_down; then the next layer's
     // q | k_new | v_new, or the logits, 16 rows per workgroup
     MlpArgs ma{};
     ma.O = o;
     ma.x = x;
-    ma.wo = P + l.wo;
-    ma.ln_g = P + l.ln2_g;
-    ma.ln_b = P + l.ln2_b;
-    ma.w1 = P + l.w1;
-    ma.b1 = P + l.b1;
-    ma.w2 = P + l.w2;
-    ma.b2 = P + l.b2;
+    ma.w_out = P + l.w_out;
+    ma.n_gain = P + l.n2_gain;
+    ma.n_bias = P + l.n2_bias;
+    ma.w_up = P + l.w_up;
+    ma.b_up = P + l.b_up;
+    ma.w_down = P + l.w_down;
+    ma.b_down = P + l.b_down;
     if (layer + 1 < l.L) {
       ma.nx = qkv_of(layer + 1);
     } else if (fuse_logits) {
       ma.nx.mode = NEXT_LOGITS;
-      ma.nx.ln_g = params + l.lnf_g;
-      ma.nx.ln_b = params + l.lnf_b;
-      ma.nx.W = params + l.wout;
+      ma.nx.n_gain = params + l.nf_gain;
+      ma.nx.n_bias = params + l.nf_bias;
+      ma.nx.W = params + l.w_vocab;
       ma.nx.logits = logits;
       ma.nx.N = l.V;
       if (draw) {
@@ -693,15 +688,15 @@ spec_status_t verify_forward(const spec_model_t* model, const float* params, con
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_LAUNCH;
   }
 
-  if (!fuse_logits) {  // logits = LNf(x) wout
+  if (!fuse_logits) {  // logits = LNf(x) w_vocab
     GemmArgs g{};
     g.M = M;
     g.A = x;
     g.K = l.C;
     g.N = l.V;
-    g.W = params + l.wout;
-    g.ln_g = params + l.lnf_g;
-    g.ln_b = params + l.lnf_b;
+    g.W = params + l.w_vocab;
+    g.n_gain = params + l.nf_gain;
+    g.n_bias = params + l.nf_bias;
     g.out = logits;
     if (gemm(g, stream) != hipSuccess) return SPEC_ERR_LAUNCH;
     if (draw) {

@@ -40,23 +40,16 @@
 #include <algorithm>
 #include <atomic>
 
-#ifndef SPECV_RS_LANE_BYTES
-#define SPECV_RS_LANE_BYTES 64
-#endif
-#ifndef SPECV_RS_SEGS_PER_WAVE
-#define SPECV_RS_SEGS_PER_WAVE 2
-#endif
-#ifndef SPECV_RS_WAVES_PER_BLOCK
-#define SPECV_RS_WAVES_PER_BLOCK 4
-#endif
-#ifndef SPECV_RS_RESID_PER_CU
-#define SPECV_RS_RESID_PER_CU 2  // residual workgroups per CU to aim for
-#endif
 
 #include "spec_common.h"
 #include "spec_verify.h"
 
 namespace specv {
+
+constexpr int kLaneBytes = 64;     // bytes of a row per lane per segment
+constexpr int kSegsPerWave = 2;    // segments a statistics wave loads at once
+constexpr int kWavesPerBlock = 4;  // waves of a statistics workgroup
+constexpr int kResidPerCU = 2;     // residual workgroups per CU to aim for
 
 struct RowPart {  // one wave's segment of one row
   float M;
@@ -169,30 +162,28 @@ struct RawVec<2> { using type = uint16_t; };
 // One raw vector through a buffer resource: a scalar base and a 32-bit byte
 // offset, so no 64-bit address is built in (and waits on) vector registers;
 // offsets past the resource's size read 0 and never fault.
-#ifndef SPECV_RESID_CPOL
-#define SPECV_RESID_CPOL 0  // cache policy bits of the buffer loads
-#endif
+constexpr int kResidCachePolicy = 0;  // cache policy bits of the residual pass's buffer loads
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 template <typename Raw>
 __device__ __forceinline__ Raw buf_raw(__amdgpu_buffer_rsrc_t r, uint32_t off);
 template <>
 __device__ __forceinline__ uint4 buf_raw<uint4>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SPECV_RESID_CPOL);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kResidCachePolicy);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 template <>
 __device__ __forceinline__ uint2 buf_raw<uint2>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, SPECV_RESID_CPOL);
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kResidCachePolicy);
   return make_uint2(v.x, v.y);
 }
 template <>
 __device__ __forceinline__ uint32_t buf_raw<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, SPECV_RESID_CPOL);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kResidCachePolicy);
 }
 template <>
 __device__ __forceinline__ uint16_t buf_raw<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, SPECV_RESID_CPOL);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kResidCachePolicy);
 }
 
 template <typename T, int VEC>
@@ -232,22 +223,15 @@ __device__ __forceinline__ void raw_to_f32(const typename RawVec<VEC * sizeof(T)
 // accepted): read last, its rows are the likeliest still to be in the
 // memory-side cache when rs_resid reads the decided row again.
 // The statistics pass reads every logit once: non-temporal loads.
-#ifndef SPECV_RS_NT
-#define SPECV_RS_NT 1
-#endif
 // A logit vector of the single streaming pass.
 template <typename R>
 __device__ __forceinline__ R stream_load(const R* p) {
-#if SPECV_RS_NT
   typedef unsigned int v4u __attribute__((ext_vector_type(4)));
   typedef unsigned int v2u __attribute__((ext_vector_type(2)));
   if constexpr (sizeof(R) == 16) return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p)));
   else if constexpr (sizeof(R) == 8) return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const v2u*>(p)));
   else if constexpr (sizeof(R) == 4) return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const unsigned int*>(p)));
   else return __builtin_bit_cast(R, __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p)));
-#else
-  return *p;
-#endif
 }
 
 template <typename T, int VEC, int NIT, int SPW>
@@ -666,9 +650,9 @@ __global__ __launch_bounds__(kResidWaves * kWave) void rs_resid(
 //
 // [P2] "LLM推論の高速化｜KVキャッシュと投機的デコーディングを自作で実測",
 // section 投機的デコーディングとは: the listing there leaves out its
-// temperature-0 branch; the results after it state that the accept test then
-// becomes "the target's argmax equals the draft", and that the output equals
-// greedy decoding with the target alone.  So: a_i = (argmax z_t[i] == x_i),
+// temperature-0 branch; the results after it say that the accept test then
+// asks whether the draft token is the target's most likely token, and that the
+// output is the target's own greedy decoding.  So: a_i = (argmax z_t[i] == x_i),
 // n = leading accepts, t = argmax z_t[n].  argmax is the first index of the
 // largest value, a NaN counting as largest.  Only the gamma+1 target rows are
 // read.
@@ -830,8 +814,8 @@ static int pick_vec(int V, int esize, uintptr_t a, uintptr_t b) {
 static RsPlan rs_plan(int B, int G, int V, int esize, int vec) {
   RsPlan p{};
   p.vec = vec;
-  // SPECV_RS_LANE_BYTES bytes of each row per lane per segment
-  p.nit = std::max(1, SPECV_RS_LANE_BYTES / (vec * esize));
+  // kLaneBytes bytes of each row per lane per segment
+  p.nit = std::max(1, kLaneBytes / (vec * esize));
   p.seg = kWave * vec * p.nit;
   p.nseg = (V + p.seg - 1) / p.seg;
   const int R = 2 * G + 1;
@@ -848,9 +832,9 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
                             float* p_out, float* q_out, hipStream_t stream) {
   const int R = 2 * G + 1;
   RowPart* part1 = reinterpret_cast<RowPart*>(ws + pl.off_part1);
-  constexpr int SPW = SPECV_RS_SEGS_PER_WAVE;
+  constexpr int SPW = kSegsPerWave;
   const int waves_row = (pl.nseg + SPW - 1) / SPW;
-  const int wpb = std::min(SPECV_RS_WAVES_PER_BLOCK, waves_row);  // waves per block
+  const int wpb = std::min(kWavesPerBlock, waves_row);  // waves per block
   const int cpr = (waves_row + wpb - 1) / wpb;  // workgroups per row
   uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
   hipLaunchKernelGGL((rs_stats<T, VEC, NIT, SPW>), dim3((unsigned)((long)B * R * cpr)), dim3(kWave * wpb), 0, stream,
@@ -859,7 +843,7 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
   if (e != hipSuccess) return e;
   double2* segsum = reinterpret_cast<double2*>(ws + pl.off_seg);
   // About two residual workgroups per CU, at least two segments per wave.
-  const int ngrp = std::max(1, std::min((SPECV_RS_RESID_PER_CU * device_cus() + B - 1) / B,
+  const int ngrp = std::max(1, std::min((kResidPerCU * device_cus() + B - 1) / B,
                                         (pl.nseg + 2 * kResidWaves - 1) / (2 * kResidWaves)));
   int spw = (pl.nseg + ngrp * kResidWaves - 1) / (ngrp * kResidWaves);
   spw += spw & 1;
@@ -877,7 +861,7 @@ static hipError_t rs_dispatch(const RsPlan& pl, const void* tgt, const void* drf
 #define RS_CASE(VEC_, NIT_)                                                                                     \
   if (pl.vec == VEC_ && pl.nit == NIT_)                                                                         \
     return rs_launch<T, VEC_, NIT_>(pl, tgt, drf, x, u, B, G, V, c32, c64, ws, n_out, tok_out, p_out, q_out, s);
-  constexpr int LB = SPECV_RS_LANE_BYTES;
+  constexpr int LB = kLaneBytes;
   if constexpr (sizeof(T) == 2) {
     RS_CASE(8, LB / 16)
     RS_CASE(4, LB / 8)
@@ -896,9 +880,9 @@ template <typename T, int VEC, int NIT>
 static hipError_t gs_launch(const RsPlan& pl, const void* tgt, const int32_t* x, int B, int G, int V, char* ws,
                             int32_t* n_out, int32_t* tok_out, float* p_out, float* q_out, hipStream_t stream) {
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + pl.off_part1);
-  constexpr int SPW = SPECV_RS_SEGS_PER_WAVE;
+  constexpr int SPW = kSegsPerWave;
   const int waves_row = (pl.nseg + SPW - 1) / SPW;
-  const int wpb = std::min(SPECV_RS_WAVES_PER_BLOCK, waves_row);
+  const int wpb = std::min(kWavesPerBlock, waves_row);
   hipLaunchKernelGGL((gs_stats<T, VEC, NIT, SPW>), dim3((unsigned)((long)B * (G + 1)), (unsigned)((waves_row + wpb - 1) / wpb)),
                      dim3(kWave * wpb), 0, stream, (const T*)tgt, V, pl.nseg, part);
   hipError_t e = hipGetLastError();
@@ -914,7 +898,7 @@ static hipError_t gs_dispatch(const RsPlan& pl, const void* tgt, const int32_t* 
                               int32_t* n_out, int32_t* tok_out, float* p_out, float* q_out, hipStream_t s) {
 #define GS_CASE(VEC_, NIT_) \
   if (pl.vec == VEC_ && pl.nit == NIT_) return gs_launch<T, VEC_, NIT_>(pl, tgt, x, B, G, V, ws, n_out, tok_out, p_out, q_out, s);
-  constexpr int LB = SPECV_RS_LANE_BYTES;
+  constexpr int LB = kLaneBytes;
   if constexpr (sizeof(T) == 2) {
     GS_CASE(8, LB / 16)
     GS_CASE(4, LB / 8)
@@ -957,7 +941,7 @@ extern "C" spec_status_t spec_reject_sample(const void* target_logits, const voi
     const int nseg1 = rs_plan(B, gamma, V, dtype == SPEC_BF16 ? 2 : 4, 1).nseg;
     if (nseg1 > kMaxSeg) return SPEC_ERR_UNSUPPORTED;
     // the statistics grid (one workgroup per chunk of every row) must fit in int
-    const long long chunk = (long long)SPECV_RS_WAVES_PER_BLOCK * SPECV_RS_SEGS_PER_WAVE;
+    const long long chunk = (long long)kWavesPerBlock * kSegsPerWave;
     if ((long long)B * (2 * gamma + 1) * ((nseg1 + chunk - 1) / chunk) > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
   }
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
