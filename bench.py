@@ -139,26 +139,12 @@ def paginate(att, cfg, hint, page, rep, order="random"):
 
 
 def quantized_cache(att, cfg, rep):
-    """int8 caches and fp16 scales drawn on the device with the host recipe of
-    ``workloads.gen.attention_inputs_int8`` (codes of N(0,1) rows, one code of
-    magnitude 127 per row, scales near 2.7 / 127); input generation only."""
-    import torch
+    """int8 caches and fp16 scales drawn on the device with the recipe of
+    ``workloads.attention_inputs_int8`` (input generation only)."""
+    import workloads as W
 
-    g = torch.Generator(device=att["q"].device).manual_seed(104729 * cfg.cid + rep)
-    B, Hkv, T, D = att["k_cache"].shape
-    out = {}
-    for name in ("k", "v"):
-        codes = torch.empty((B, Hkv, T, D), dtype=torch.int8, device=att["q"].device)
-        for b in range(B):
-            c = torch.clamp(torch.round(torch.randn((Hkv, T, D), generator=g, device=codes.device) * (127 / 2.7)),
-                            -127, 127)
-            pos = torch.randint(0, D, (Hkv, T, 1), generator=g, device=codes.device)
-            sign = torch.where(torch.rand((Hkv, T, 1), generator=g, device=codes.device) < 0.5, -127.0, 127.0)
-            codes[b] = c.scatter(2, pos, sign).to(torch.int8)
-        out[f"{name}_q"] = codes
-        out[f"{name}_scale"] = (torch.exp(0.1 * torch.randn((B, Hkv, T), generator=g, device=codes.device))
-                                * (2.7 / 127)).to(torch.float16)
-    return out
+    d = W.attention_inputs_int8_device(cfg, att["q"].device, rep=rep)
+    return {"k_q": d["k_cache"], "k_scale": d["k_scale"], "v_q": d["v_cache"], "v_scale": d["v_scale"]}
 
 
 def make_inputs(cfg, device, temperature, rep):
@@ -256,6 +242,77 @@ def cpu_baseline(cfg, att, smp, temperature, budget_s=12.0):
     }
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_worker(job):
+    """One worker of the all-core oracle leg: draws whole sequences of the
+    workload with the host generators (seeded by worker and count) and times
+    the oracle on each (attention over the full cache, then the sampler over
+    all vocabulary rows, or greedy verification at T = 0), one BLAS thread,
+    until ``budget_s`` of oracle time.  Returns (positions, oracle seconds)."""
+    cid, temperature, worker, budget_s = job
+    from threadpoolctl import threadpool_limits
+
+    import workloads as W
+    from oracle import attention as A
+    from oracle import greedy as Gr
+    from oracle import sampler as S
+
+    cfg = W.get(cid)
+    pos, spent, i = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        while spent < budget_s:
+            rep = 1000 + 100 * worker + i
+            i += 1
+            att = W.attention_inputs(cfg, rep=rep, B=1)
+            L = int(att["lens"][0])
+            smp = W.sampler_inputs(cfg, temperature=temperature if temperature > 0 else 1.0, rep=rep, B=1)
+            kc, vc = att["k_cache"][:, :, :L], att["v_cache"][:, :, :L]
+            t0 = time.perf_counter()
+            A.verify_attention(att["q"], att["k_new"], att["v_new"], kc, vc, att["lens"])
+            if temperature == 0:
+                Gr.verify_batch(smp["target_logits"], smp["draft_tokens"])
+            else:
+                S.verify_batch(smp["target_logits"], smp["draft_logits"], smp["draft_tokens"], smp["uniforms"],
+                               temperature)
+            spent += time.perf_counter() - t0
+            pos += cfg.gamma
+    return pos, spent
+
+
+def all_core_baseline(pool, workers, cid, temperature, budget_s=4.0):
+    """The oracle on every worker of ``pool`` at once (each on its own
+    sequences): the summed rate of the workers."""
+    t0 = time.perf_counter()
+    res = pool.map(_oracle_worker, [(cid, temperature, w, budget_s) for w in range(workers)])
+    wall = time.perf_counter() - t0
+    return {
+        "value": sum(p / t for p, t in res if t > 0),
+        "unit": "positions/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{workers} processes at once, each timing the oracle for about {budget_s:g} s on whole sequences "
+                  "of the workload drawn with the host generators (attention over the full cache + "
+                  + ("greedy verification" if temperature == 0 else "sampler over every vocabulary row")
+                  + "), numpy fp64, one BLAS thread each; the value sums the processes' rates; drawing the "
+                  "inputs is not timed",
+        "sequences": int(sum(p for p, _ in res) // W_GAMMA.get(cid, 1)),
+        "wall_s": wall,
+    }
+
+
+W_GAMMA = {3: 4, 4: 4, 5: 8}
+
+
 def copy_ceiling(torch, nbytes=2 << 30, reps=5):
     """Achieved HBM bytes/s of a plain 2 GiB device-to-device copy (read + write).
 
@@ -296,12 +353,23 @@ def main():
                     help="cache storage: the workload's bf16, the same values in fp16, or int8 codes with an fp16 scale per row")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 1 GiB device buffer 5 times (reference for HBM byte counters)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="at the default workload, skip the other measured points (config 5's sampler at T=0.7 "
+                         "and config 4's step)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the verification step has no multi-GPU "
               "path; sharded, each GPU would own B/N sequences and run the same calls with no exchange.",
               file=sys.stderr)
         sys.exit(2)
+    # The all-core oracle leg's worker processes are forked now, before this
+    # process touches the GPU, and never use it.
+    pool, workers = None, 0
+    if not args.no_cpu_baseline and args.workload != "model" and not args.copy_calibration:
+        import multiprocessing as mp
+
+        workers = max(1, min(16, os.cpu_count() or 1))
+        pool = mp.get_context("fork").Pool(workers)
 
     import torch
 
@@ -331,13 +399,10 @@ def main():
         return
     cfg = W.get(WORKLOADS[args.workload])
     T = cfg.temperatures[-1] if args.temperature is None else args.temperature
+    extras = (not args.no_extras and cfg.cid == 5 and T == 1.0 and args.kv == "bf16" and not args.paged)
     print(f"[bench] workload config{cfg.cid} ({cfg.name}) T={T}: generating inputs", file=sys.stderr, flush=True)
-
-    # Enough input sets that the step's bytes exceed the 256 MB last-level cache.
-    att_bytes_est = cfg.B * 2 * cfg.Hkv * cfg.D * cfg.elem_bytes * (sum(cfg.L) / 2 + cfg.n_q)
-    smp_bytes_est = cfg.B * (2 * cfg.gamma + 1) * cfg.V * cfg.elem_bytes
-    nsets = max(1, min(4, math.ceil(768e6 / (att_bytes_est + smp_bytes_est))))
-    sets = [make_inputs(cfg, dev, T, rep) for rep in range(nsets)]
+    sets = input_sets(cfg, dev, T)
+    nsets = len(sets)
     hint = cfg.L[1]
     if args.kv == "int8":
         if args.paged or cfg.dtype != "bf16":
@@ -361,54 +426,8 @@ def main():
             del att["k_cache"], att["v_cache"]  # the paged copies are the cache now
         torch.cuda.empty_cache()
     B = cfg.B
-
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-
-    def step(k, events=None):
-        att, smp = sets[k % nsets]
-        att["lens"].copy_(att["lens_base"])
-        if events:
-            events[0].record(stream)
-        if args.kv == "int8":
-            sv.spec_verify_attention_int8(att["q"], att["k_new"], att["v_new"], att["k_q"], att["k_scale"],
-                                          att["v_q"], att["v_scale"], att["lens"], hint, out=att["out"])
-        elif args.paged:
-            sv.spec_verify_attention_paged(att["q"], att["k_new"], att["v_new"], att["k_pages"], att["v_pages"],
-                                           att["table"], att["lens"], hint, out=att["out"])
-        else:
-            sv.spec_verify_attention(att["q"], att["k_new"], att["v_new"], att["k_cache"], att["v_cache"],
-                                     att["lens"], hint, out=att["out"])
-        if events:
-            events[1].record(stream)
-        greedy = T == 0
-        n, tok, _, _ = sv.spec_reject_sample(smp["target_logits"], None if greedy else smp["draft_logits"],
-                                             smp["draft_tokens"], None if greedy else smp["uniforms"], T,
-                                             n_accepted=smp["n"], out_tokens=smp["tok"])
-        if events:
-            events[2].record(stream)
-        sv.spec_kv_truncate(att["lens"], n, cfg.n_q)
-        if events:
-            events[3].record(stream)
-        return n
-
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
-    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        step(k, ev[k])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    att_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    smp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    trn_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    t = time_steps(torch, sv, cfg, T, sets, hint, args.steps, args.warmup, kv=args.kv, paged=args.paged)
+    ms_step, att_ms, smp_ms, trn_ms = t["ms_step"], t["att_ms"], t["smp_ms"], t["trn_ms"]
 
     # Algorithmic bytes per call, averaged over the rotated input sets (their
     # lengths differ); set k is used by steps k, k + nsets, ...
@@ -473,13 +492,151 @@ def main():
             "mean_accepted": float(n_last.mean()),
         },
     }
-    res["copy_ceiling"] = copy_ceiling(torch)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         att0, smp0 = sets[0]
-        res["cpu_baseline"] = cpu_baseline(cfg, att0, smp0, T)
+        cb = cpu_baseline(cfg, att0, smp0, T)
+        cb["cpu_model"] = cpu_model()
+        cb["os_cpu_count"] = os.cpu_count()
+        del att0, smp0
+    del sets
+    torch.cuda.empty_cache()
+    if extras:
+        # The other points the targets are set on, measured in the same run:
+        # config 5's sampler at its other temperature, and config 4's step.
+        res["sampler_c5_T0.7"] = sampler_only(torch, sv, cfg, 0.7, dev, args.steps, args.warmup)
+        res["parts_c4"] = step_parts(torch, sv, W.get(4), dev, max(args.steps, 50), max(args.warmup, 10))
+    res["copy_ceiling"] = copy_ceiling(torch)
+    if not args.no_cpu_baseline:
+        if pool is not None:
+            print(f"[bench] timing the CPU oracle on {workers} processes", file=sys.stderr, flush=True)
+            cb["all_cores"] = all_core_baseline(pool, workers, cfg.cid, T)
+        res["cpu_baseline"] = cb
+    if pool is not None:
+        pool.close()
+        pool.join()
     print(json.dumps(res), flush=True)
 
+
+def time_steps(torch, sv, cfg, T, sets, hint, steps, warmup, kv="bf16", paged=0):
+    """Warm up, then time ``steps`` verification steps between two events on
+    the launch stream, with per-call events around attention, the sampler and
+    the length reset.  Step k uses input set k mod len(sets); lengths are
+    restored before each step (a 1 KB device copy, outside the per-call events)."""
+    nsets = len(sets)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+
+    def step(k, events=None):
+        att, smp = sets[k % nsets]
+        att["lens"].copy_(att["lens_base"])
+        if events:
+            events[0].record(stream)
+        if kv == "int8":
+            sv.spec_verify_attention_int8(att["q"], att["k_new"], att["v_new"], att["k_q"], att["k_scale"],
+                                          att["v_q"], att["v_scale"], att["lens"], hint, out=att["out"])
+        elif paged:
+            sv.spec_verify_attention_paged(att["q"], att["k_new"], att["v_new"], att["k_pages"], att["v_pages"],
+                                           att["table"], att["lens"], hint, out=att["out"])
+        else:
+            sv.spec_verify_attention(att["q"], att["k_new"], att["v_new"], att["k_cache"], att["v_cache"],
+                                     att["lens"], hint, out=att["out"])
+        if events:
+            events[1].record(stream)
+        greedy = T == 0
+        n, tok, _, _ = sv.spec_reject_sample(smp["target_logits"], None if greedy else smp["draft_logits"],
+                                             smp["draft_tokens"], None if greedy else smp["uniforms"], T,
+                                             n_accepted=smp["n"], out_tokens=smp["tok"])
+        if events:
+            events[2].record(stream)
+        sv.spec_kv_truncate(att["lens"], n, cfg.n_q)
+        if events:
+            events[3].record(stream)
+        return n
+
+    for k in range(warmup):
+        step(k)
+    torch.cuda.synchronize()
+    print(f"[bench] config{cfg.cid}: warmup {warmup} done; timing {steps} steps", file=sys.stderr, flush=True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(steps):
+        step(k, ev[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    return {"ms_step": t_start.elapsed_time(t_end) / steps,
+            "att_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+            "smp_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+            "trn_ms": float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))}
+
+
+def input_sets(cfg, dev, T):
+    """Enough input sets that a step's bytes exceed the 256 MB last-level cache."""
+    att_bytes_est = cfg.B * 2 * cfg.Hkv * cfg.D * cfg.elem_bytes * (sum(cfg.L) / 2 + cfg.n_q)
+    smp_bytes_est = cfg.B * (2 * cfg.gamma + 1) * cfg.V * cfg.elem_bytes
+    nsets = max(1, min(4, math.ceil(768e6 / (att_bytes_est + smp_bytes_est))))
+    return [make_inputs(cfg, dev, T, rep) for rep in range(nsets)]
+
+
+def sampler_only(torch, sv, cfg, T, dev, steps, warmup):
+    """spec_reject_sample alone at temperature T over one batch of the
+    workload's logits (drafts drawn at T), timed with events per call."""
+    import workloads as W
+
+    print(f"[bench] config{cfg.cid} sampler at T={T}", file=sys.stderr, flush=True)
+    smp = W.sampler_inputs_device(cfg, dev, temperature=T)
+    n = torch.empty(cfg.B, dtype=torch.int32, device=dev)
+    tok = torch.empty((cfg.B, cfg.gamma + 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        sv.spec_reject_sample(smp["target_logits"], smp["draft_logits"], smp["draft_tokens"], smp["uniforms"], T,
+                              n_accepted=n, out_tokens=tok)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = algorithmic(cfg, np.zeros(cfg.B), cfg.B)[2]
+    del smp
+    torch.cuda.empty_cache()
+    return {"ms": ms, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "positions/s": cfg.B * cfg.gamma / (ms * 1e-3), "mean_accepted": float(n.float().mean().item())}
+
+
+def step_parts(torch, sv, cfg, dev, steps, warmup):
+    """The whole step at another configuration (its first temperature):
+    per-call event times and HBM fractions of attention and the sampler."""
+    T = cfg.temperatures[-1]
+    print(f"[bench] config{cfg.cid}: generating inputs", file=sys.stderr, flush=True)
+    sets = input_sets(cfg, dev, T)
+    t = time_steps(torch, sv, cfg, T, sets, cfg.L[1], steps, warmup)
+    per_set = [algorithmic(cfg, st[0]["lens_base"].cpu().numpy(), cfg.B) for st in sets]
+    counts = [len(range(k, steps, len(sets))) for k in range(len(sets))]
+    att_b = sum(c * a[0] for c, a in zip(counts, per_set)) / steps
+    smp_b = per_set[0][2]
+    pos = cfg.B * cfg.gamma
+    out = {"workload": f"config{cfg.cid} {cfg.name}: B={cfg.B} gamma={cfg.gamma} GQA {cfg.Hq}/{cfg.Hkv} "
+                       f"D={cfg.D} {cfg.dtype} KV, lengths U[{cfg.L[0]},{cfg.L[1]}], vocab {cfg.V}, T={T}",
+           "steps": steps, "input_sets": len(sets), "ms_per_step": t["ms_step"],
+           "positions/s": pos / (t["ms_step"] * 1e-3),
+           "attention": {"ms": t["att_ms"], "bytes": att_b, "hbm_frac": att_b / (t["att_ms"] * 1e-3) / 8e12,
+                         "positions/s": pos / (t["att_ms"] * 1e-3)},
+           "sampler": {"ms": t["smp_ms"], "bytes": smp_b, "hbm_frac": smp_b / (t["smp_ms"] * 1e-3) / 8e12,
+                       "positions/s": pos / (t["smp_ms"] * 1e-3)},
+           "truncate": {"ms": t["trn_ms"]}}
+    del sets
+    torch.cuda.empty_cache()
+    return out
 
 
 def model_bench(args, torch, sv, dev):
