@@ -50,7 +50,8 @@ typedef enum {
   SPEC_ERR_ARG = 1,         /* bad pointer, size, alignment or workspace size   */
   SPEC_ERR_OVERFLOW = 2,    /* cache too small: max_len_hint + n_q > max_T      */
   SPEC_ERR_UNSUPPORTED = 3, /* valid request outside what the library supports */
-  SPEC_ERR_LAUNCH = 4       /* the HIP runtime refused a kernel launch          */
+  SPEC_ERR_LAUNCH = 4,      /* the HIP runtime refused a kernel launch          */
+  SPEC_ERR_SCRATCH = 5      /* more than a no-allocation call's fixed scratch    */
 } spec_status_t;
 
 /* Element type of the tensors a call reads and writes: fp32, bf16, or IEEE
@@ -240,6 +241,25 @@ spec_status_t spec_reject_sample(const void* target_logits, const void* draft_lo
                                  const double* uniforms, int B, int gamma, int V, float temperature,
                                  spec_dtype_t dtype, int32_t* n_accepted, int32_t* out_tokens, float* p_draft,
                                  float* q_draft, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* spec_reject_sample without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and results, minus the
+ * workspace.  Its scratch is a fixed 16 MiB array in device memory that each
+ * GPU the library runs on holds from the first load of the library's code
+ * until the process ends; the call allocates nothing (no hipMalloc, no
+ * library routine that does).  Every call on a GPU uses that GPU's one
+ * array, so calls that overlap in time on one GPU (different streams, or
+ * other threads) race and must be ordered by the caller.  A request whose
+ * spec_reject_sample_workspace_size(B, gamma, V, dtype) exceeds 16 MiB
+ * returns SPEC_ERR_SCRATCH (about B * (2 gamma + 1) * ceil(V / 2048) * 16
+ * bytes for bf16: 256 sequences of gamma = 8 over 128,256 tokens need 4.6
+ * MiB); other errors as spec_reject_sample, SPEC_ERR_LAUNCH if the scratch's
+ * device address cannot be found. */
+spec_status_t spec_reject_sample_noalloc(const void* target_logits, const void* draft_logits,
+                                         const int32_t* draft_tokens, const double* uniforms, int B, int gamma, int V,
+                                         float temperature, spec_dtype_t dtype, int32_t* n_accepted,
+                                         int32_t* out_tokens, float* p_draft, float* q_draft, hipStream_t stream);
 
 /* ------------------------------------------------------------------------- */
 /* KV length reset                                                            */

@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
-SPEC_OK, SPEC_ERR_ARG, SPEC_ERR_OVERFLOW, SPEC_ERR_UNSUPPORTED, SPEC_ERR_LAUNCH = range(5)
+SPEC_OK, SPEC_ERR_ARG, SPEC_ERR_OVERFLOW, SPEC_ERR_UNSUPPORTED, SPEC_ERR_LAUNCH, SPEC_ERR_SCRATCH = range(6)
 SPEC_F32, SPEC_BF16, SPEC_F16 = 0, 1, 2
 
 EXPORTED = (
@@ -29,6 +29,7 @@ EXPORTED = (
     "spec_verify_attention_int8",
     "spec_reject_sample_workspace_size",
     "spec_reject_sample",
+    "spec_reject_sample_noalloc",
     "spec_kv_truncate",
     "spec_model_param_count",
     "spec_verify_forward_workspace_size",
@@ -84,6 +85,8 @@ def load(path=LIB_PATH):
     L.spec_reject_sample_workspace_size.argtypes = [c_int] * 4
     L.spec_reject_sample.restype = c_int
     L.spec_reject_sample.argtypes = [vp] * 4 + [c_int] * 3 + [c_float, c_int] + [vp] * 5 + [c_size, vp]
+    L.spec_reject_sample_noalloc.restype = c_int
+    L.spec_reject_sample_noalloc.argtypes = [vp] * 4 + [c_int] * 3 + [c_float, c_int] + [vp] * 5
     L.spec_kv_truncate.restype = c_int
     L.spec_kv_truncate.argtypes = [vp, vp, c_int, c_int, vp]
     pm = ctypes.POINTER(SpecModel)

@@ -10,6 +10,7 @@ extern "C" const char* spec_status_string(spec_status_t s) {
     case SPEC_ERR_OVERFLOW: return "SPEC_ERR_OVERFLOW";
     case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED";
     case SPEC_ERR_LAUNCH: return "SPEC_ERR_LAUNCH";
+    case SPEC_ERR_SCRATCH: return "SPEC_ERR_SCRATCH";
   }
   return "SPEC_ERR_UNKNOWN";
 }

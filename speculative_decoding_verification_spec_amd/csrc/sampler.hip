@@ -39,6 +39,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 
 #include "spec_common.h"
@@ -970,4 +971,49 @@ extern "C" spec_status_t spec_reject_sample(const void* target_logits, const voi
     e = rs_dispatch<float>(pl, target_logits, draft_logits, draft_tokens, uniforms, B, gamma, V, c32, c64, ws,
                            n_accepted, out_tokens, p_draft, q_draft, stream);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// the same call without a caller workspace
+// ---------------------------------------------------------------------------
+//
+// spec_reject_sample_noalloc uses this array as its workspace.  Every GPU the
+// library runs on holds its own copy (zero-initialised when the code object is
+// loaded) until the process ends.  Host code never passes the array's name to
+// a kernel: the name stands for a host-side shadow, so its device address is
+// looked up once per device with hipGetSymbolAddress and kept.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The device address of this device's `scratch`, looked up on the first call
+// made with the device current; nullptr if the lookup fails.
+static void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+extern "C" spec_status_t spec_reject_sample_noalloc(const void* target_logits, const void* draft_logits,
+                                                    const int32_t* draft_tokens, const double* uniforms, int B,
+                                                    int gamma, int V, float temperature, spec_dtype_t dtype,
+                                                    int32_t* n_accepted, int32_t* out_tokens, float* p_draft,
+                                                    float* q_draft, hipStream_t stream) {
+  const size_t need = spec_reject_sample_workspace_size(B, gamma, V, dtype);
+  if (need == 0) return SPEC_ERR_ARG;
+  if (need > kNoAllocScratchBytes) return SPEC_ERR_SCRATCH;
+  void* ws = scratch_address();
+  if (!ws) return SPEC_ERR_LAUNCH;
+  // Every scratch word the kernels read is written earlier in the same call
+  // (the arrival counters are zeroed by its first kernel), so nothing is
+  // cleared here and no memory is allocated.
+  return spec_reject_sample(target_logits, draft_logits, draft_tokens, uniforms, B, gamma, V, temperature, dtype,
+                            n_accepted, out_tokens, p_draft, q_draft, ws, kNoAllocScratchBytes, stream);
 }
