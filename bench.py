@@ -473,7 +473,7 @@ def main():
             "unit": "GB/s",
             "frac": att_gbs / HBM_PEAK_GBS,
             "traffic": None if traffic is None else traffic["bytes_per_call"],
-            "kernel": ("spec_verify_attention_int8: quant_new_rows + attn_stream_i8 + attn_combine_stream, one call"
+            "kernel": ("spec_verify_attention_int8: quant_new_rows + attn_stream_i8w + attn_combine_i8, one call"
                        if args.kv == "int8" else
                        "spec_verify_attention: attn_stream_bf16 with attn_combine_stream or, for long shares, "
                        "attn_stream_prep, one call"

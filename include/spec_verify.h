@@ -172,8 +172,11 @@ size_t spec_verify_attention_int8_workspace_size(int B, int Hq, int Hkv, int n_q
  *            cache_len[b] are never used.
  *   workspace device, >= spec_verify_attention_int8_workspace_size(...) bytes.
  * Arithmetic: scores from the bf16 MFMA on the exact int8 values, times the
- * key's scale in fp32; each probability is multiplied by its key's V scale
- * before the bf16 PV product; the row sum uses the unscaled probabilities.
+ * key's scale in fp32; V rows dequantised to bf16(q s) for the bf16 PV
+ * product.  Probabilities are taken against a fixed per-row reference (the
+ * row's largest score in its first key block); a row whose scores later
+ * exceed it by more than 2^64 in probability is computed again on an exact
+ * fp32 path with the usual running-maximum rescale.
  * Supported: D in {64, 128}, B <= 1024, and the limits of
  * spec_verify_attention.
  * Errors: as spec_verify_attention (dtype fixed to bf16 activations), and

@@ -110,6 +110,7 @@ struct AttnArgs {
   void* out;
   float* part_o;
   ML* part_ml;
+  uint32_t* ovf;  // int8 stream scheme: per slab, 1 if a piece left it to the exact path
   int* pre;  // stream scheme: [B + 1] blocks per slab before sequence b
   uint32_t* scnt;  // stream scheme merged in the kernel: pieces finished per slab
   int B, Hq, Hkv, n_q, G, M, RG, RT, NSP, C, max_T, hint;
@@ -283,12 +284,9 @@ __device__ __forceinline__ float group_sum(float v) {
 // 128 VGPRs, so two 5-wave workgroups share a CU.
 constexpr int kAttnWavesPerEU = 4;
 constexpr int kStreamWavesPerEU = 4;
-// Raw int8 stages: with two bf16 buffers, 2 keep the kernel in 128 VGPRs.
-constexpr int kI8Stages = 2;
 // Cache policy of the cache-block loads, which stream every key once per
 // call: non-temporal (nt = 2).
 constexpr int kKvCachePolicy = 2;
-constexpr int kI8CachePolicy = 2;
 
 // One LDS object per stage and tensor: reads of one stage then provably do
 // not alias the asynchronous copies into another, so the compiler does not
@@ -946,6 +944,7 @@ template <int D>
 __global__ __launch_bounds__(256) void quant_new_rows(AttnArgs a) {
   constexpr int EPL = D / 16;  // elements per lane
   const long bg = blockIdx.x;
+  if ((int)threadIdx.x < a.RG) a.ovf[bg * a.RG + threadIdx.x] = 0u;  // this call's slabs start unmarked
   const int grp = threadIdx.x >> 4, gl = threadIdx.x & 15;
   for (int r = grp; r < 2 * a.n_q; r += 16) {
     const bool is_v = r >= a.n_q;
@@ -974,66 +973,127 @@ __global__ __launch_bounds__(256) void quant_new_rows(AttnArgs a) {
   }
 }
 
-// Stages of the int8 kernel: raw int8 K and V tiles and the block's 32 K
-// then 32 V scales, one LDS object each (see the bf16 stages); the widened
-// bf16 tiles (swizzled like the bf16 kernel's stages) and the new rows'
-// scales.
-#define SPECV_I8_STAGE_LDS \
-  __shared__ __attribute__((aligned(1024))) int8_t qk0[KB * D], qv0[KB * D]; \
-  __shared__ __attribute__((aligned(1024))) int8_t qk1[KB * D], qv1[KB * D]; \
-  __shared__ __attribute__((aligned(1024))) int8_t qk2[NST > 2 ? KB * D : 16], qv2[NST > 2 ? KB * D : 16]; \
-  __shared__ __attribute__((aligned(16))) uint16_t sc0[64], sc1[64], sc2[64]; \
-  __shared__ __attribute__((aligned(1024))) uint16_t cvk[2 * KB * D], cvv[2 * KB * D]; \
-  __shared__ __attribute__((aligned(16))) uint16_t scv[128]; \
-  __shared__ float nsk[16], nsv[16]; \
-  auto qkbuf = [&](auto S) -> int8_t* { \
-    if constexpr (decltype(S)::value == 0) return qk0; \
-    else if constexpr (decltype(S)::value == 1) return qk1; \
-    else return qk2; \
-  }; \
-  auto qvbuf = [&](auto S) -> int8_t* { \
-    if constexpr (decltype(S)::value == 0) return qv0; \
-    else if constexpr (decltype(S)::value == 1) return qv1; \
-    else return qv2; \
-  }; \
-  auto scbuf = [&](auto S) -> uint16_t* { \
-    if constexpr (decltype(S)::value == 0) return sc0; \
-    else if constexpr (decltype(S)::value == 1) return sc1; \
-    else return sc2; \
-  };
-
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-// One piece of one (b, g, rg) over the int8 cache.  As bf16_piece, with:
-// copies move raw int8 rows (32 D bytes per tile) and the block's scales;
-// after the barrier every wave widens its share of the int8 tiles into the
-// bf16 tiles cvk / cvv (exactly: |q| <= 127), a second barrier, then the
-// bf16 MFMA path runs on them.  Scores are multiplied by their key's K scale
-// before the softmax, and each probability by its key's V scale before PV
-// (the row sum uses the unscaled probabilities).  Keys [L, L + n_q) are the
-// quantised new rows from the workspace.
-template <int D, int NW, int NST, typename QK, typename QV, typename SC>
-__device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, SC scbuf, uint16_t* cvk,
-                                         uint16_t* cvv, uint16_t* scv, float* nsk, float* nsv, int b, int g, int rg, int L, int k0,
-                                         int k1, bool whole, size_t slot, bool append) {
+// ---------------------------------------------------------------------------
+// int8 cache: one wave per workgroup
+// ---------------------------------------------------------------------------
+//
+// A wave holds all RT row tiles of its row group, so each key block is
+// widened once and used by every tile (a design that shared each widened
+// block between the waves of a workgroup moved it through LDS about 14 times
+// its HBM bytes, which bounded it; here a block costs LDS 4 times its
+// bytes).  Raw blocks are copied by the wave into I8W_STAGES private LDS
+// stages (global_load_lds: no registers held while in flight).  K goes from its stage
+// straight into the MFMA operand: the order of d inside the contraction is
+// permuted so that lane (lr, lg) takes bytes [lg D/4, (lg + 1) D/4) of key row
+// lr -- step s of the product its bytes [8 s, 8 s + 8) -- and the query
+// fragments follow the same permutation, which leaves every score unchanged.
+// K is widened exactly to f16 (two byte permutes and a packed subtract per
+// four values) and the products run in f16 against the query converted to
+// f16; the key's scale multiplies the score.  V is widened dequantised,
+// bf16(q s) (one rounding, as the probabilities get), into a wave-private
+// bf16 tile in the bf16 kernel's swizzled layout, then read transposed
+// (ds_read_b64_tr_b16) as there.
+//
+// The output accumulators (RT x D / 4 floats a lane) stay in the MFMA
+// accumulator registers: no vector instruction rewrites them (a rescale of
+// them would need all of them in vector registers, more than a wave has), so
+// the usual online-softmax rescale (O *= exp2(m_old - m_new) when a row's
+// maximum grows) is replaced by a fixed reference per row.  A row's reference
+// is the largest score of the first block in which it sees a key, and every
+// probability is exp2(score - reference) -- exact softmax terms up to a
+// common factor that the final division removes.  Later scores may exceed the
+// reference; while the row sum stays within 2^64 so does every (positive)
+// term, and then no sum can have overflowed (2^64 x 2^15 keys x |v| < 2^23
+// stays below 2^128).  A piece with a larger, infinite or NaN row sum (scores
+// growing by some 64 / (scale log2 e) along a row after its first block;
+// never for scores of ordinary size) marks its slab, and the combine launch
+// computes that slab again on an exact path with the usual rescaling
+// (attn_combine_i8).  The row sums themselves come from the MFMA.
+//
+// Each step overlaps the MFMA work of one block with the vector work of the
+// next: the previous block's PV runs while this block's V is dequantised and
+// its K widened, and the score products of tile r + 1 run under the
+// probabilities of tile r.
+
+// Raw int8 stages: 16-byte chunk c of row r sits at chunk c ^ swz(r) of its
+// row, so that the 16 rows an operand read touches (one chunk each) fall on
+// 16 different 16-byte bank groups of a 256-byte bank line.
+template <int D>
+struct I8Layout {
+  static constexpr int CH = D / 16;         // 16-byte chunks per row
+  static constexpr int RP = 256 / D;        // rows per 256-byte bank line
+  static constexpr int NI = KB * D / 1024;  // 1 KB copies per tile
+  static constexpr int CPB = 2 * NI + 1;    // copies per block: K, V, scales
+  __host__ __device__ static constexpr int swz(int r) { return (r / RP) % CH; }
+  // Byte offset of chunk c of row r.
+  __host__ __device__ static constexpr int at(int r, int c) { return r * D + 16 * (c ^ swz(r)); }
+};
+constexpr int I8W_STAGES = 3;
+
+// One copy of 16 bytes per lane from global memory into LDS: lane l's bytes
+// land at LDS byte lds + 16 l.  Written out (the instruction has no register
+// results) so that the compiler does not track it: it cannot tell the stages
+// apart and would make every LDS access wait for every copy in flight.  The
+// waits for the copies are explicit (wait_vmcnt), and the memory clobber keeps
+// LDS accesses on their side of each copy.  M0 takes the LDS address; one
+// wait state separates the write of M0 from the copy that reads it.
+__device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
+  __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds)
+                   : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ float ubyte_f32(uint32_t flipped, int i) {
+  return (float)((flipped >> (8 * i)) & 0xffu);
+}
+
+// Eight int8 values (two words, little-endian) as f16, exactly: with every
+// byte's top bit flipped, byte b = q + 128 becomes the low byte of the f16
+// 0x64bb = 1024 + b (high byte 0x64: exponent 10, so the low byte counts
+// units), and subtracting 1152 leaves q.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f16x8 widen8_f16(uint32_t w0, uint32_t w1) {
+  const f16x2 off = {(_Float16)1152.f, (_Float16)1152.f};
+  uint32_t o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t x = (k < 2 ? w0 : w1) ^ 0x80808080u;
+    const uint32_t h = __builtin_amdgcn_perm(0x64646464u, x, (k & 1) ? 0x04030402u : 0x04010400u);
+    o[k] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, h) - off);
+  }
+  return __builtin_bit_cast(f16x8, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// Eight int8 values as bf16(q s): (q + 128) s - 128 s in one fma, rounded.
+__device__ __forceinline__ bf16x8 widen8_scaled(uint32_t w0, uint32_t w1, float s, float m128s) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t word = (i < 4 ? w0 : w1) ^ 0x80808080u;
+    o[i] = (__bf16)fmaf(ubyte_f32(word, i & 3), s, m128s);
+  }
+  return o;
+}
+
+template <int D, int RT, typename KS, typename VS, typename SS>
+__device__ __forceinline__ void i8w_piece(const AttnArgs& a, KS kst, VS vst, SS sst, uint16_t* __restrict__ vt, int b,
+                                          int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append) {
   using LY = BfLayout<D>;
-  constexpr int DS = D / 32;
-  constexpr int DT = D / 16;
-  constexpr int NI8 = KB * D / 1024;                    // 1 KB copies per int8 tile
-  constexpr int WI = NW >= 4 ? 4 : (NW >= 2 ? 2 : 1);
-  constexpr int CPW8 = 2 * NI8 / WI;                    // data copies per issuing wave per block
-  constexpr int CPW = CPW8 + 1;                         // plus the scale copy
-  static_assert((2 * NI8) % WI == 0, "copies must split evenly over the issuing waves");
-  static_assert(NST >= 2 && NST <= 3 && (NST - 2) * CPW <= 63, "stages");
-  int tid = threadIdx.x;
-  __asm__ volatile("" : "+v"(tid));
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid & (kWave - 1);
-  const int lr = lane & 15;
-  const int lg = lane >> 4;
+  using IL = I8Layout<D>;
+  constexpr int NST = I8W_STAGES;
+  constexpr int DS = D / 32;  // product steps over D
+  constexpr int DT = D / 16;  // 16-wide output tiles over D
+  constexpr int ROWS = 16 * RT;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lr = lane & 15, lg = lane >> 4;
   const long bg = (long)b * a.Hkv + g;
   const int Ltot = L + a.n_q;
   const int nblk = (k1 - k0 + KB - 1) / KB;
+  const int kb_last = k0 + (nblk - 1) * KB;
 
   const int8_t* kc = static_cast<const int8_t*>(a.kc) + (size_t)bg * a.max_T * D;
   const int8_t* vc = static_cast<const int8_t*>(a.vc) + (size_t)bg * a.max_T * D;
@@ -1041,347 +1101,358 @@ __device__ __forceinline__ void i8_piece(const AttnArgs& a, QK qkbuf, QV qvbuf, 
   const int8_t* vnb = a.nvq + (size_t)bg * a.n_q * D;
   const uint16_t* ksr = a.ksc + (size_t)bg * a.max_T;
   const uint16_t* vsr = a.vsc + (size_t)bg * a.max_T;
+  const uint16_t* ksn = a.nks + (size_t)bg * a.n_q;
+  const uint16_t* vsn = a.nvs + (size_t)bg * a.n_q;
 
-  // The new rows' scales, for blocks reaching them (before any copy of this
-  // piece is in flight).
-  if (tid < a.n_q) {
-    nsk[tid] = f16_to_f32(a.nks[(size_t)bg * a.n_q + tid]);
-    nsv[tid] = f16_to_f32(a.nvs[(size_t)bg * a.n_q + tid]);
-  }
-
-  // Data copy i of an issuing wave: copy c = wave + i WI (K for c < NI8);
-  // lane l moves bytes [1024 c' + 16 l, +16) of the tile, row (1024 c' +
-  // 16 l) / D.  The scale copy: lanes 0..3 the K scales of keys 8 l .. 8 l +
-  // 7, lanes 4..7 the V scales; every issuing wave issues it (identical
-  // data), so each issues CPW copies per block.
-  auto issue_block = [&](int kb, auto S) {
-    if (wave >= WI) return;
-    const bool full = kb + KB <= L;
-#pragma unroll
-    for (int i = 0; i < CPW8; ++i) {
-      const int c = wave + i * WI;
-      const bool is_v = c >= NI8;
-      const int cc = is_v ? c - NI8 : c;
-      const uint32_t boff = (uint32_t)(cc * 1024 + 16 * lane);  // byte offset in the tile
-      int8_t* dst = (is_v ? qvbuf(S) : qkbuf(S)) + cc * 1024;
-      const int8_t* cache = is_v ? vc : kc;
-      if (full) {
-        const __amdgpu_buffer_rsrc_t rsrc =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(cache + (size_t)kb * D), (short)0, KB * D, 0x00020000);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (void __attribute__((address_space(3)))*)dst, 16, (int)boff,
-                                                 0, 0, kI8CachePolicy);
-      } else {
-        const int key = kb + (int)(boff / D);
-        const int8_t* fresh = is_v ? vnb : knb;
-        const int8_t* src = key < L ? cache + (size_t)kb * D + boff
-                                    : fresh + (size_t)(key < Ltot ? key - L : 0) * D + boff % D;
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                         (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
-      }
-    }
-    if (lane < 8) {
-      // Rows past the cache's end are never used: clamp the key into it.
-      const int key = min(kb + 8 * (lane & 3), a.max_T - 8);
-      const uint16_t* src = (lane < 4 ? ksr : vsr) + key;
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)scbuf(S), 16, 0, 0);
-    }
-  };
-
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const int m = rg * 16 * NW + 16 * wave + lr;
-  const bool valid = m < a.M;
-  const int h = g * a.G + (valid ? m / a.n_q : 0);
-  const int qi = valid ? m % a.n_q : a.n_q - 1;
-  const int lim = L + qi;
-  bf16x8 qf[DS];
-  {
-    const uint16_t* qrow = q + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
-#pragma unroll
-    for (int s = 0; s < DS; ++s)
-      qf[s] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg) : bf16x8{};
-  }
-  // The tiles are widened as k' = q + 128 (0..255, exact in bf16), so a score
-  // is s_k (k' . q_row - 128 sum_d q_row[d]): 128 times this row's sum of the
-  // same bf16 query values, subtracted after the product.
-  float qsum = 0.f;
-#pragma unroll
-  for (int s = 0; s < DS; ++s)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qsum += (float)qf[s][i];
-  const float q128 = 128.f * group_sum(qsum);
-
-  issue_block(k0, IC<0>{});
-  if (nblk > 1) issue_block(k0 + KB, IC<1>{});
-
-  int kofs[DS], vofs[DT];
-#pragma unroll
-  for (int s = 0; s < DS; ++s) kofs[s] = lr * D + 8 * LY::kslot(lr, 4 * s + lg);
-  {
-    const int vrow = 4 * lg + (lr >> 2), q4 = lr & 3;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vofs[dt] = vrow * D + 8 * LY::vslot(vrow, 2 * dt + (q4 >> 1)) + 4 * (q4 & 1);
-  }
-  static_assert(LY::same_swizzle_16_rows_apart(), "kt / hh offsets");
-
-  const float c = a.qk_scale;
-  float mrow = neg_inf_f(), lsum = 0.f;
-  float wsum = 0.f;  // this lane's share of sum_key P' (the bf16 values fed to PV), for the V offset
-  f32x4 oacc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Scales of this lane's 8 keys kb + 16 kt + 4 lg + jj (K then V).
-  auto key_scales = [&](const uint16_t* sc, int kb, float (&sk)[8], float (&sv)[8]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const uint2 wk = *reinterpret_cast<const uint2*>(sc + 16 * kt + 4 * lg);
-      const uint2 wv = *reinterpret_cast<const uint2*>(sc + 32 + 16 * kt + 4 * lg);
-      const uint32_t hk[4] = {wk.x & 0xffffu, wk.x >> 16, wk.y & 0xffffu, wk.y >> 16};
-      const uint32_t hv[4] = {wv.x & 0xffffu, wv.x >> 16, wv.y & 0xffffu, wv.y >> 16};
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        sk[4 * kt + jj] = f16_to_f32((uint16_t)hk[jj]);
-        sv[4 * kt + jj] = f16_to_f32((uint16_t)hv[jj]);
-      }
-    }
-    if (kb + KB > L) {  // keys at or past L: the new rows' scales, or 0 (masked)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int key = kb + 16 * kt + 4 * lg + jj;
-          if (key >= L) {
-            sk[4 * kt + jj] = key < Ltot ? nsk[key - L] : 0.f;
-            sv[4 * kt + jj] = key < Ltot ? nsv[key - L] : 0.f;
-          }
-        }
-    }
-  };
-
-  // Widen the int8 tiles of the block in raw stage S into bf16 buffer cb of
-  // cvk / cvv (8 values per item) as k' = q + 128: flipping each byte's top
-  // bit makes it the unsigned q + 128, which converts to fp32 in one
-  // instruction per byte, and an integer of 0..255 is exact in bf16 (the top
-  // half of its fp32 bits).  The offsets come back out per row: -128 sum_d q
-  // in the scores, -128 sum_key P' in the output.  Each thread issues the
-  // reads of all its items of both tiles before converting any (one LDS round
-  // trip, not one per item); each read names a single LDS object, so the
-  // compiler can tell the reads from the copies in flight into other stages
-  // and does not wait for them.
-  auto widen_block = [&](auto S, int cb) {
-    constexpr int PER = KB * D / 8;            // 8-value items per tile
-    constexpr int NT = 64 * NW;                // threads
-    constexpr int IPT = (PER + NT - 1) / NT;   // items per thread per tile
-    constexpr int SPR = D / 8;                 // items per row
-    static_assert((SPR & (SPR - 1)) == 0, "row of a power-of-two number of items");
-    auto widen8 = [&](uint2 w) {
-      uint32_t o[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t word = (k < 2 ? w.x : w.y) ^ 0x80808080u;
-        const int sh = 16 * (k & 1);
-        const float lo = (float)((word >> sh) & 0xffu);
-        const float hi = (float)((word >> (sh + 8)) & 0xffu);
-        o[k] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-      }
-      return make_uint4(o[0], o[1], o[2], o[3]);
-    };
-    if (tid < 64) scv[(cb ? 64 : 0) + tid] = scbuf(S)[tid];  // the block's K, V scales
-    const int8_t* tk = qkbuf(S);
-    const int8_t* tv = qvbuf(S);
-    uint2 wk[IPT], wv[IPT];
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      const unsigned it = (unsigned)tid + (unsigned)(k * NT);
-      if (it < (unsigned)PER) wk[k] = *reinterpret_cast<const uint2*>(tk + 8 * it);
-    }
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      const unsigned it = (unsigned)tid + (unsigned)(k * NT);
-      if (it < (unsigned)PER) wv[k] = *reinterpret_cast<const uint2*>(tv + 8 * it);
-    }
-#pragma unroll
-    for (int k = 0; k < IPT; ++k) {
-      const unsigned it = (unsigned)tid + (unsigned)(k * NT);
-      if (it < (unsigned)PER) {
-        const int row = (int)(it / SPR), sl = (int)(it % SPR);
-        *reinterpret_cast<uint4*>(cvk + cb + row * D + 8 * LY::kslot(row, sl)) = widen8(wk[k]);
-        *reinterpret_cast<uint4*>(cvv + cb + row * D + 8 * LY::vslot(row, sl)) = widen8(wv[k]);
-      }
-    }
-  };
-
-  // Software pipeline, one barrier per block.  Step j: wait for block j+1's
-  // copies; barrier (block j+1's raw tiles have landed, block j's widened
-  // tiles are complete, and every read of block j-1's widened buffer is
-  // done); copy block j+NST into raw stage j (free: block j was widened, and
-  // its scales copied, in step j-1); widen block j+1 into the other bf16
-  // buffer (and its scales into the other half of scv); then the product of
-  // block j.
-  auto step = [&](auto S, int j) {
-    const int kb = k0 + j * KB;
-    const bool next = j + 1 < nblk;
-    if (NST > 2 && next && j + 2 < nblk)
-      wait_vmcnt<(NST > 2 ? CPW : 0)>();  // block j+2's copies may stay in flight
-    else
-      wait_vmcnt<0>();
-    block_barrier();
-    if (j + NST < nblk) issue_block(kb + NST * KB, S);
-    const int cb = (j & 1) * KB * D;
-    if (next) widen_block(IC<(decltype(S)::value + 1) % NST>{}, KB * D - cb);
-    float skey[8], svkey[8];
-    key_scales(scv + (j & 1) * 64, kb, skey, svkey);
-
-    float sc[8];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < DS; ++s) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(cvk + cb + kofs[s] + 16 * kt * D);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) sc[4 * kt + jj] = (acc[jj] - q128) * skey[4 * kt + jj];
-    }
-    float alpha;
-    {
-      if (kb + KB > L) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int key = kb + 16 * kt + 4 * lg + jj;
-            if (key >= Ltot || key > lim) sc[4 * kt + jj] = neg_inf_f();
-          }
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int jj = 1; jj < 8; ++jj) mx = fmaxf(mx, sc[jj]);
-      const float mnew = fmaxf(mrow, group_max(mx) * c);
-      const bool none = (mnew == neg_inf_f());
-      alpha = none ? 1.f : exp2_fast(mrow - mnew);
-      float ps = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        sc[jj] = none ? 0.f : exp2_fast(fmaf(sc[jj], c, -mnew));
-        ps += sc[jj];
-      }
-      lsum = fmaf(lsum, alpha, ps);
-      mrow = mnew;
-    }
-    if (__ballot(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-    }
-    bf16x8 pf;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) pf[jj] = (__bf16)(sc[jj] * svkey[jj]);
-    {
-      float pw = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) pw += (float)pf[jj];
-      wsum = fmaf(wsum, alpha, pw);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      s16x4 v2[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        v2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(cvv + cb + vofs[dt] + 16 * hh * D));
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dt], 0, 0, 0);
-    }
-  };
-
-  // Prologue: blocks 0 .. NST-1 in flight (0 and 1 above), block 0 widened
-  // into buffer 0.
-  if constexpr (NST > 2) {
-    if (nblk > 2) issue_block(k0 + 2 * KB, IC<2>{});
-  }
-  if (NST > 2 && nblk > 2)
-    wait_vmcnt<(NST > 2 ? 2 * CPW : 0)>();  // blocks 1, 2 may stay in flight
-  else if (nblk > 1)
-    wait_vmcnt<CPW>();  // block 1 may stay in flight
-  else
-    wait_vmcnt<0>();
-  block_barrier();
-  widen_block(IC<0>{}, 0);
-
-  for (int j = 0; j < nblk; j += NST) {
-    step(IC<0>{}, j);
-    if (j + 1 < nblk) step(IC<1>{}, j + 1);
-    if constexpr (NST > 2) {
-      if (j + 2 < nblk) step(IC<2>{}, j + 2);
-    }
-  }
-
-  // A1: the quantised new rows and their scales into the cache.
+  // A1: the quantised new rows and their scales into the cache (only rows
+  // [L, L + n_q), which no piece reads from the cache).
   if (append) {
     constexpr int CPR = D / 16;  // 16-byte chunks per int8 row
-    for (int cidx = tid; cidx < 2 * a.n_q * CPR; cidx += 64 * NW) {
+    for (int cidx = lane; cidx < 2 * a.n_q * CPR; cidx += kWave) {
       const bool is_v = cidx >= a.n_q * CPR;
       const int cc = is_v ? cidx - a.n_q * CPR : cidx;
       const uint4* src = reinterpret_cast<const uint4*>(is_v ? vnb : knb) + cc;
       uint4* dst = reinterpret_cast<uint4*>(static_cast<int8_t*>(is_v ? a.vc : a.kc) + ((size_t)bg * a.max_T + L) * D) + cc;
       *dst = *src;
     }
-    if (tid < 2 * a.n_q) {
-      const bool is_v = tid >= a.n_q;
-      const int r = is_v ? tid - a.n_q : tid;
+    if (lane < 2 * a.n_q) {
+      const bool is_v = lane >= a.n_q;
+      const int r = is_v ? lane - a.n_q : lane;
       uint16_t* dst = const_cast<uint16_t*>(is_v ? a.vsc : a.ksc) + (size_t)bg * a.max_T + L + r;
-      *dst = (is_v ? a.nvs : a.nks)[(size_t)bg * a.n_q + r];
+      *dst = (is_v ? vsn : ksn)[r];
     }
   }
 
-  const float lt = group_sum(lsum);
-  {
-    // the V offset: O = sum P' v' - 128 sum P'
-    const float v128 = 128.f * group_sum(wsum);
+  // Copy i of a tile: lane l moves chunk (t % CH) ^ swz(r) of row r = t / CH,
+  // t = 64 i + l, to byte 16 t of the stage.  Rows past the new rows copy
+  // row 0 (masked).  Every block issues CPB copies, so waits stay static.
+  auto issue = [&](int kb, auto S) {
+    if (kb + KB <= L) {  // the whole block is in the cache
+      const int8_t* kbase = kc + (size_t)kb * D;
+      const int8_t* vbase = vc + (size_t)kb * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+      for (int i = 0; i < IL::NI; ++i) {
+        const int t = 64 * i + lane, r = t / IL::CH;
+        const int off = r * D + 16 * ((t % IL::CH) ^ IL::swz(r));
+        lds_copy16(kbase + off, lds_addr(kst(S) + 1024 * i));
+        lds_copy16(vbase + off, lds_addr(vst(S) + 1024 * i));
+      }
+    } else {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) oacc[dt][jj] -= v128;
-  }
-  const int row = 16 * wave + lr;
-  if (whole) {
-    if (valid) {
-      uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
-      const float inv = 1.f / lt;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = 16 * dt + 4 * lg;
-        uint2 pk;
-        pk.x = uint32_t(f32_to_bf16(oacc[dt][0] * inv)) | (uint32_t(f32_to_bf16(oacc[dt][1] * inv)) << 16);
-        pk.y = uint32_t(f32_to_bf16(oacc[dt][2] * inv)) | (uint32_t(f32_to_bf16(oacc[dt][3] * inv)) << 16);
-        *reinterpret_cast<uint2*>(o + d) = pk;
+      for (int i = 0; i < IL::NI; ++i) {
+        const int t = 64 * i + lane, r = t / IL::CH;
+        const int cb = 16 * ((t % IL::CH) ^ IL::swz(r));
+        const int key = kb + r;
+        const bool cached = key < L, fresh = !cached && key < Ltot;
+        const size_t ro = cached ? (size_t)key * D : (fresh ? (size_t)(key - L) * D : 0);
+        lds_copy16((fresh ? knb : kc) + ro + cb, lds_addr(kst(S) + 1024 * i));
+        lds_copy16((fresh ? vnb : vc) + ro + cb, lds_addr(vst(S) + 1024 * i));
       }
     }
+    if (lane < 8) {
+      // 8 K scales (lanes 0-3) or V scales (4-7) from a multiple of 8; a
+      // clamped copy only serves keys past the new rows.
+      const int key = min(kb + 8 * (lane & 3), a.max_T - 8);
+      lds_copy16((lane < 4 ? ksr : vsr) + key, lds_addr(sst(S)));
+    }
+  };
+  // Query fragments of the RT tiles, d permuted: step s, lane group lg hold
+  // d = lg D/4 + 8 s + (0..7).  The products run in f16, which holds every
+  // bf16 value of magnitude up to 65504 exactly (bf16's 8 significant bits
+  // fit f16's 11; below 2^-14 fewer bits remain, a change far below the
+  // scores' rounding); a larger or non-finite query leaves the slab to the
+  // exact path.
+  f16x8 qf[RT][DS];
+  bool qbad = false;
+  int lim[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const int m = rg * ROWS + 16 * r + lr;
+    const bool valid = m < a.M;
+    const int h = g * a.G + (valid ? m / a.n_q : 0);
+    const int qi = valid ? m % a.n_q : a.n_q - 1;
+    lim[r] = L + qi;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      const bf16x8 qv = valid ? *reinterpret_cast<const bf16x8*>(qrow + lg * (D / 4) + 8 * st) : bf16x8{};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = (float)qv[i];
+        qbad |= !(fabsf(x) <= 65504.f);
+        qf[r][st][i] = (_Float16)x;
+      }
+    }
+  }
+  // (taken as a wave-uniform flag here: left per lane until the end, the
+  // check kept more registers alive)
+  const bool qbad_any = __builtin_amdgcn_readfirstlane(__ballot(qbad) != 0);
+  // LDS element offsets of this lane's V^T reads (hh = 0; hh = 1 adds 16 rows)
+  int vofs[DT];
+  {
+    const int vrow = 4 * lg + (lr >> 2), q4 = lr & 3;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vofs[dt] = vrow * D + 8 * LY::vslot(vrow, 2 * dt + (q4 >> 1)) + 4 * (q4 & 1);
+  }
+  static_assert(LY::same_swizzle_16_rows_apart(), "hh offsets");
+
+  const float c = a.qk_scale;
+  // reference (scaled, log2 units; -inf until the row sees a key); the row
+  // sums come from the MFMA: an all-ones A fragment against the bf16
+  // probabilities adds each row's block sum to every element of lacc[r]
+  // (the sum of exactly the values the PV product uses).
+  float mref[RT];
+  f32x4 lacc[RT];
+  f32x4 oacc[RT][DT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    mref[r] = neg_inf_f();
+    lacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[r][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  issue(k0, IC<0>{});
+  issue(min(k0 + KB, kb_last), IC<1>{});
+  if constexpr (NST > 2) issue(min(k0 + 2 * KB, kb_last), IC<2>{});
+
+  // PV of the previous block (its probabilities pprev, its dequantised V in
+  // the tile) is issued while this block's V is dequantised into the same
+  // tile: for each 16-wide d tile dt, the tile's reads for dt precede, in
+  // program order, this block's writes of those d (a wave's LDS accesses
+  // take effect in order, and the compiler keeps possibly aliasing accesses
+  // in order).  The MFMA work of one block then overlaps the vector work of
+  // the next.  Lane l dequantises row l % 32, bf16 chunks 2 dt + l / 32.
+  const int vrow_w = lane & 31, vhalf = lane >> 5;
+  bf16x8 pprev[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) pprev[r] = bf16x8{};
+  // PV of the previous block: 5 MFMAs per 16-wide d tile dt (dt 0 also
+  // adds the row sums).
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  auto pv_tile = [&](int dt) {
+    s16x4 v2[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      v2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(vt + vofs[dt] + 16 * hh * D));
+    const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v2[0], v2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int r = 0; r < RT; ++r) oacc[r][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pprev[r], oacc[r][dt], 0, 0, 0);
+    if (dt == 0) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) lacc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pprev[r], lacc[r], 0, 0, 0);
+    }
+  };
+
+  // Everything a block needs from its stage, read into registers one step
+  // ahead (after the block's copies have landed).
+  struct Raw {
+    uint4 k[2][D / 64];
+    uint2 v[DT];
+    uint2 sk[2];
+    uint16_t sv;
+  };
+  auto read_stage = [&](Raw& R, auto S) {
+    wait_vmcnt<(NST - 1) * IL::CPB>();  // this block's copies have landed
+    const int8_t* ks = kst(S);
+    const int8_t* vs = vst(S);
+    const uint16_t* ss = sst(S);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int hh = 0; hh < D / 64; ++hh)
+        R.k[kt][hh] = *reinterpret_cast<const uint4*>(ks + IL::at(16 * kt + lr, lg * (D / 64) + hh));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) R.v[dt] = *reinterpret_cast<const uint2*>(vs + IL::at(vrow_w, dt) + 8 * vhalf);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) R.sk[kt] = *reinterpret_cast<const uint2*>(ss + 16 * kt + 4 * lg);
+    R.sv = ss[32 + vrow_w];
+  };
+  Raw R;
+
+  auto step = [&](int j, auto S) {
+    const int kb = k0 + j * KB;
+    // the block reaches the new rows (or past them): the only blocks with
+    // per-key cases, handled in branches of their own
+    const bool tail = __builtin_amdgcn_readfirstlane(kb + KB > L);
+    // The block's stage was read into R at the end of the previous step: once
+    // those reads are done, refill the stage with the block NST ahead (the
+    // last block again past the end).
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(min(kb + NST * KB, kb_last), S);
+    const auto& kr = R.k;
+    const auto& vr = R.v;
+    const auto& skr = R.sk;
+    float sv = f16_to_f32(R.sv);
+    if (tail) {
+      const int key = kb + vrow_w;
+      if (key >= L) sv = key < Ltot ? f16_to_f32(vsn[key - L]) : 0.f;
+    }
+    // The previous block's PV, with this block's V dequantised into the tile
+    // behind it and its K fragments widened (exact f16, each then used by
+    // every tile) alongside.
+    const float m128 = -128.f * sv;
+    f16x8 kf[2][DS];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      pv_tile(dt);
+      const int chunk = 2 * dt + vhalf;
+      *reinterpret_cast<bf16x8*>(vt + vrow_w * D + 8 * LY::vslot(vrow_w, chunk)) =
+          widen8_scaled(vr[dt].x, vr[dt].y, sv, m128);
+      if (dt < 2 * DS) {
+        const int kt = dt / DS, st = dt % DS;
+        const uint4 u = kr[kt][st / 2];
+        kf[kt][st] = (st & 1) ? widen8_f16(u.z, u.w) : widen8_f16(u.x, u.y);
+      }
+    }
+    // K scales of this lane's 8 keys kb + 16 kt + 4 lg + jj, times c.
+    float skc[8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      skc[4 * kt + 0] = f16_to_f32((uint16_t)(skr[kt].x & 0xffffu)) * c;
+      skc[4 * kt + 1] = f16_to_f32((uint16_t)(skr[kt].x >> 16)) * c;
+      skc[4 * kt + 2] = f16_to_f32((uint16_t)(skr[kt].y & 0xffffu)) * c;
+      skc[4 * kt + 3] = f16_to_f32((uint16_t)(skr[kt].y >> 16)) * c;
+    }
+    if (tail) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int key = kb + 16 * (jj >> 2) + 4 * lg + (jj & 3);
+        if (key >= L) skc[jj] = key < Ltot ? f16_to_f32(ksn[key - L]) * c : 0.f;
+      }
+    }
+    // The next block's stage into R, under this block's scores.
+    if (j + 1 < nblk) {
+      if constexpr (decltype(S)::value == NST - 1)
+        read_stage(R, IC<0>{});
+      else
+        read_stage(R, IC<decltype(S)::value + 1>{});
+    }
+
+    // Scores of tile r (the products of tile r + 1 can run under the vector
+    // work of tile r), then its probabilities.
+    auto qk = [&](int r, f32x4 (&acc)[2]) {
+      acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < DS; ++st)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[kt][st], qf[r][st], acc[kt], 0, 0, 0);
+    };
+    auto probs = [&](int r, const float (&e)[8]) {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) pprev[r][jj] = (__bf16)exp2_fast(e[jj]);
+    };
+    if (j == 0 || tail) {
+      // rows without a reference yet take this block's largest visible
+      // score; keys a row does not see get no weight
+      auto masked = [&](int r, int jj) {
+        const int key = kb + 16 * (jj >> 2) + 4 * lg + (jj & 3);
+        return key >= Ltot || key > lim[r];
+      };
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        f32x4 acc[2];
+        qk(r, acc);
+        float t[8], mx = neg_inf_f();
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          t[jj] = masked(r, jj) ? neg_inf_f() : acc[jj >> 2][jj & 3] * skc[jj];
+          mx = fmaxf(mx, t[jj]);
+        }
+        mx = group_max(mx);
+        if (mref[r] == neg_inf_f()) mref[r] = mx;
+        const float mr = mref[r] == neg_inf_f() ? 0.f : mref[r];  // such a row sees no key here
+        float e[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) e[jj] = t[jj] - mr;
+        probs(r, e);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        f32x4 acc[2];
+        qk(r, acc);
+        float e[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) e[jj] = fmaf(acc[jj >> 2][jj & 3], skc[jj], -mref[r]);
+        probs(r, e);
+      }
+    }
+  };
+
+  read_stage(R, IC<0>{});
+  for (int j = 0; j < nblk; j += NST) {
+    step(j, IC<0>{});
+    if (j + 1 < nblk) step(j + 1, IC<1>{});
+    if constexpr (NST > 2) {
+      if (j + 2 < nblk) step(j + 2, IC<2>{});
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) pv_tile(dt);  // the last block's PV
+  // The copies still in flight (the last block again) land before the stages
+  // serve another piece.
+  wait_vmcnt<0>();
+  float lt[RT];
+  bool over = qbad_any;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    lt[r] = lacc[r][0];
+    over |= !(lt[r] <= 18446744073709551616.f);  // 2^64
+  }
+  if (__ballot(over)) {
+    if (lane == 0) a.ovf[bg * a.RG + rg] = 1u;
     return;
   }
-  float* po = a.part_o + slot * (16 * NW) * D;
-  if (lg == 0) a.part_ml[slot * (16 * NW) + row] = ML{mrow, lt};
+
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[dt];
+  for (int r = 0; r < RT; ++r) {
+    const int m = rg * ROWS + 16 * r + lr;
+    if (whole) {
+      if (m < a.M) {
+        uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)b * a.Hq + g * a.G + m / a.n_q) * a.n_q + m % a.n_q) * D;
+        const float inv = 1.f / lt[r];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = 16 * dt + 4 * lg;
+          uint2 pk;
+          pk.x = uint32_t(f32_to_bf16(oacc[r][dt][0] * inv)) | (uint32_t(f32_to_bf16(oacc[r][dt][1] * inv)) << 16);
+          pk.y = uint32_t(f32_to_bf16(oacc[r][dt][2] * inv)) | (uint32_t(f32_to_bf16(oacc[r][dt][3] * inv)) << 16);
+          *reinterpret_cast<uint2*>(o + d) = pk;
+        }
+      }
+    } else {
+      const int row = 16 * r + lr;
+      float* po = a.part_o + slot * ROWS * D;
+      if (lg == 0) a.part_ml[slot * ROWS + row] = ML{mref[r], lt[r]};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[r][dt];
+    }
+  }
 }
 
-template <int D, int NW, int NST>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(kStreamWavesPerEU)))
-void attn_stream_i8(AttnArgs a) {
-  SPECV_I8_STAGE_LDS
+template <int D, int RT>
+__global__ __launch_bounds__(64) void attn_stream_i8w(AttnArgs a) {
+  constexpr int T = KB * D;
+  __shared__ __attribute__((aligned(1024))) int8_t stg[I8W_STAGES][2 * T];  // K tile, V tile
+  __shared__ __attribute__((aligned(16))) uint16_t ssc[I8W_STAGES][64];      // 32 K, 32 V scales
+  __shared__ __attribute__((aligned(1024))) uint16_t vt[KB * D];
+  // The bf16 tile starts as zeros: the first block of every piece issues a PV
+  // of zero probabilities against it.
+  for (int i = threadIdx.x; i < KB * D / 8; i += kWave) reinterpret_cast<uint4*>(vt)[i] = make_uint4(0, 0, 0, 0);
+  auto kst = [&](auto S) -> int8_t* { return stg[decltype(S)::value]; };
+  auto vst = [&](auto S) -> int8_t* { return stg[decltype(S)::value] + T; };
+  auto sst = [&](auto S) -> uint16_t* { return ssc[decltype(S)::value]; };
   stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append, int) {
-    i8_piece<D, NW, NST>(a, qkbuf, qvbuf, scbuf, cvk, cvv, scv, nsk, nsv, b, g, rg, L, k0, k1, whole, slot, append);
+    i8w_piece<D, RT>(a, kst, vst, sst, vt, b, g, rg, L, k0, k1, whole, slot, append);
   });
 }
 
 // Merge the pieces of each (b, g, rg) slab the stream kernel cut; one
 // workgroup per slab.  Slabs covered whole were written by the stream kernel.
 template <int D, bool F16 = false>
-__global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
+__device__ __forceinline__ void combine_stream_slab(const AttnArgs& a, long slab) {
   using H = Half16<F16>;
-  const long slab = blockIdx.x;
   const int rg = (int)(slab % a.RG);
   const int g = (int)((slab / a.RG) % a.Hkv);
   const int b = (int)(slab / ((long)a.RG * a.Hkv));
@@ -1445,6 +1516,73 @@ __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
     pk.y = uint32_t(H::bits(acc[2])) | (uint32_t(H::bits(acc[3])) << 16);
     *reinterpret_cast<uint2*>(out_ptr(row) + d) = pk;
   }
+}
+
+template <int D, bool F16 = false>
+__global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
+  combine_stream_slab<D, F16>(a, blockIdx.x);
+}
+
+// The exact path of the int8 call for a slab its stream pieces gave up on (a
+// probability term beyond the wave kernel's headroom): the plain online
+// softmax -- running maximum, sums rescaled whenever it grows -- over the
+// dequantised keys, fp32 throughout, two threads per row (each one half of
+// the output's D values; both compute every score).  Slow, and only run for
+// scores that grow by more than 64 / (scale log2 e) along a row.
+template <int D>
+__device__ void i8_slab_exact(const AttnArgs& a, long slab) {
+  const int rg = (int)(slab % a.RG);
+  const int g = (int)((slab / a.RG) % a.Hkv);
+  const int b = (int)(slab / ((long)a.RG * a.Hkv));
+  const int rows = 16 * a.RT, row0 = rg * rows, nrows = min(rows, a.M - row0);
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  if (row >= nrows) return;
+  constexpr int DH = D / 2;
+  const int m = row0 + row, h = g * a.G + m / a.n_q, qi = m % a.n_q;
+  const long bg = (long)b * a.Hkv + g;
+  const int L = a.len[b];
+  const uint16_t* q = static_cast<const uint16_t*>(a.q) + (((size_t)b * a.Hq + h) * a.n_q + qi) * D;
+  const int8_t* kc = static_cast<const int8_t*>(a.kc) + (size_t)bg * a.max_T * D;
+  const int8_t* vc = static_cast<const int8_t*>(a.vc) + (size_t)bg * a.max_T * D;
+  const int8_t* knb = a.nkq + (size_t)bg * a.n_q * D;
+  const int8_t* vnb = a.nvq + (size_t)bg * a.n_q * D;
+  float acc[DH];
+#pragma unroll
+  for (int d = 0; d < DH; ++d) acc[d] = 0.f;
+  float mx = neg_inf_f(), l = 0.f;
+  for (int j = 0; j <= L + qi; ++j) {  // the keys this row sees
+    const bool cached = j < L;
+    const int8_t* kr = cached ? kc + (size_t)j * D : knb + (size_t)(j - L) * D;
+    const int8_t* vr = (cached ? vc + (size_t)j * D : vnb + (size_t)(j - L) * D) + half * DH;
+    const float sk = f16_to_f32(cached ? a.ksc[bg * a.max_T + j] : a.nks[bg * a.n_q + (j - L)]);
+    const float sv = f16_to_f32(cached ? a.vsc[bg * a.max_T + j] : a.nvs[bg * a.n_q + (j - L)]);
+    float dot = 0.f;
+    for (int d = 0; d < D; ++d) dot = fmaf(bf16_to_f32(q[d]), (float)kr[d], dot);
+    const float sc = dot * sk * a.qk_scale;  // log2 units
+    const float mn = fmaxf(mx, sc);
+    const float r = exp2_fast(mx - mn);  // 0 for the first key
+    const float p = exp2_fast(sc - mn);
+    l = fmaf(l, r, p);
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc[d] = fmaf(acc[d], r, p * sv * (float)vr[d]);
+    mx = mn;
+  }
+  uint16_t* o = static_cast<uint16_t*>(a.out) + (((size_t)b * a.Hq + h) * a.n_q + qi) * D + half * DH;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int d = 0; d < DH; ++d) o[d] = f32_to_bf16(acc[d] * inv);
+}
+
+// Combine launch of the int8 call: slabs marked by the wave kernel take the
+// exact path, the others are merged as in the bf16 call.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_i8(AttnArgs a) {
+  const long slab = blockIdx.x;
+  if (a.ovf[slab] != 0u && slab_blocks(a, (int)(slab / ((long)a.RG * a.Hkv))) > 0) {
+    i8_slab_exact<D>(a, slab);
+    return;
+  }
+  combine_stream_slab<D, false>(a, slab);
 }
 
 // ---------------------------------------------------------------------------
@@ -1817,6 +1955,8 @@ constexpr int kStages = 2;  // LDS stages; blocks in flight per workgroup: kStag
 // 1-4K-key caches; 1 and 1.5 per CU were slower everywhere).  The int8
 // kernel keeps 3 (87 us against 109 us at 2).
 constexpr int kStreamMaxWG = 768;
+// The int8 kernel runs one-wave workgroups, one or two per SIMD.
+constexpr int kStreamMaxWG8 = 2048;
 constexpr int kMergeMinShare = 256;  // blocks per workgroup from which the launch merges pieces
 constexpr int kBf16PerCU = 2;        // resident 16-bit stream workgroups per CU
 
@@ -1832,13 +1972,13 @@ struct StreamPlan {
   size_t off_o, off_ml, off_pre, off_cnt, total;
 };
 
-static StreamPlan stream_plan(int B, int Hkv, int RG, int RT, int n_q, int D, int hint) {
+static StreamPlan stream_plan(int B, int Hkv, int RG, int RT, int n_q, int D, int hint, int maxwg = kStreamMaxWG) {
   StreamPlan p{};
   const long slabs = (long)B * Hkv * RG;
   // With shares of at least MINB = ceil(nbmax / jcap) blocks a slab is cut
   // into at most jcap + 1 pieces.  jcap is large enough that MINB stays below
-  // the even share W / P unless most lengths are far below the hint.
-  const long jcap = std::max(2L, 2 * ((kStreamMaxWG + slabs - 1) / slabs) + 2);
+  // the even share W / P (P <= maxwg) unless most lengths are far below the hint.
+  const long jcap = std::max(2L, 2 * ((maxwg + slabs - 1) / slabs) + 2);
   const long nbmax = ((long)hint + n_q + KB - 1) / KB;
   p.JP = (int)(jcap + 1);
   p.MINB = (int)std::max(1L, (nbmax + jcap - 1) / jcap);
@@ -1863,7 +2003,7 @@ static StreamPlan stream_plan(int B, int Hkv, int RG, int RT, int n_q, int D, in
 // holds 512 / VGPRs waves.  Cached per kernel (the template argument) and
 // device.
 template <auto kernel>
-static int stream_workgroups(int NW, int max_per_cu) {
+static int stream_workgroups(int NW, int max_per_cu, int maxwg = kStreamMaxWG) {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
@@ -1886,7 +2026,7 @@ static int stream_workgroups(int NW, int max_per_cu) {
   // CU left a third of them waiting for a slot).
   const int by_slots = NW <= 4 ? 4 * per_simd / NW : std::min(2, per_simd / ((NW + 3) / 4));
   int k = std::max(1, std::min(std::min(occ, by_slots), max_per_cu));
-  const int P = std::min(kStreamMaxWG, cus * k);
+  const int P = std::min(maxwg, cus * k);
   if (slot) slot->store(P, std::memory_order_relaxed);
   return P;
 }
@@ -1925,17 +2065,17 @@ static hipError_t launch_stream(const AttnArgs& a, hipStream_t s) {
   return launch_stream_as<D, NW, PG, false, F16>(a, s);
 }
 
-template <int D, int NW>
+template <int D, int RT>
 static hipError_t launch_i8(const AttnArgs& a0, hipStream_t s) {
   AttnArgs a = a0;
   hipLaunchKernelGGL((quant_new_rows<D>), dim3((unsigned)((size_t)a.B * a.Hkv)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.P = stream_workgroups<attn_stream_i8<D, NW, kI8Stages>>(NW, 3);
-  hipLaunchKernelGGL((attn_stream_i8<D, NW, kI8Stages>), dim3((unsigned)a.P), dim3(64 * NW), 0, s, a);
+  a.P = stream_workgroups<attn_stream_i8w<D, RT>>(1, 8, kStreamMaxWG8);
+  hipLaunchKernelGGL((attn_stream_i8w<D, RT>), dim3((unsigned)a.P), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine_stream<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_combine_i8<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -2165,16 +2305,16 @@ extern "C" spec_status_t spec_verify_attention_paged(const void* q, const void* 
 // ---- int8 cache entry points ------------------------------------------------
 
 // Stream-scheme workspace followed by the quantised new rows (int8 K, int8 V,
-// fp16 K scales, fp16 V scales).
+// fp16 K scales, fp16 V scales) and the per-slab exact-path marks.
 struct I8Plan {
   StreamPlan sp;
-  size_t off_nkq, off_nvq, off_nks, off_nvs, total;
+  size_t off_nkq, off_nvq, off_nks, off_nvs, off_ovf, total;
 };
 
 static I8Plan i8_plan(int B, int Hq, int Hkv, int n_q, int D, int hint) {
   I8Plan p{};
   const AttnPlan ap = attn_plan(B, Hq, Hkv, n_q, D, hint, SPEC_BF16);
-  p.sp = stream_plan(B, Hkv, ap.RG, ap.RT, n_q, D, hint);
+  p.sp = stream_plan(B, Hkv, ap.RG, ap.RT, n_q, D, hint, kStreamMaxWG8);
   const size_t rows = (size_t)B * Hkv * n_q;
   size_t off = p.sp.total;
   p.off_nkq = off;
@@ -2185,6 +2325,8 @@ static I8Plan i8_plan(int B, int Hq, int Hkv, int n_q, int D, int hint) {
   off = align256(off + rows * 2);
   p.off_nvs = off;
   off = align256(off + rows * 2);
+  p.off_ovf = off;
+  off = align256(off + sizeof(uint32_t) * (size_t)B * Hkv * ap.RG);
   p.total = off;
   return p;
 }
@@ -2240,6 +2382,7 @@ extern "C" spec_status_t spec_verify_attention_int8(const void* q, const void* k
   a.nvq = reinterpret_cast<int8_t*>(ws + ip.off_nvq);
   a.nks = reinterpret_cast<uint16_t*>(ws + ip.off_nks);
   a.nvs = reinterpret_cast<uint16_t*>(ws + ip.off_nvs);
+  a.ovf = reinterpret_cast<uint32_t*>(ws + ip.off_ovf);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

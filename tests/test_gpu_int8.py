@@ -69,6 +69,8 @@ def test_config4_int8():
         (2, 4, 4, 1, 64, [1, 1000]),          # n_q = 1, D = 64
         (1, 8, 1, 5, 128, [3000]),            # one sequence over many workgroups
         (300, 4, 4, 3, 128, None),            # many one- or two-block slabs
+        (2, 16, 2, 8, 64, [100, 700]),        # 64 rows per KV head (4 tiles), D = 64
+        (2, 8, 1, 16, 128, [40, 300]),        # 128 rows per KV head (8 tiles)
     ],
 )
 def test_shapes(B, Hq, Hkv, n_q, D, lens):
@@ -125,6 +127,36 @@ def test_zero_and_loud_new_rows():
     inp = W.attention_inputs_int8(cfg, B=2, lens=[100, 700])
     inp["k_new"][0, 1, 2] = 0       # a zero row: scale 0, codes 0
     inp["v_new"][1, 0, :] = W.bf16_bits(np.full(128, 1000.0, np.float32))  # one value per row
+    _check(inp, _run(inp, hint=cfg.L[1]), relative=True)
+
+
+def test_scores_beyond_the_headroom():
+    """Rows whose scores grow, past their first key block, by far more than
+    the wave kernel's headroom (64 in log2 units) take the exact path; the
+    other sequence of the call stays on the fast one.  Sequence 0: cached keys
+    from 64 on have 200 times larger K scales; sequence 1: loud new K rows
+    (quantised with a 200 times larger scale); sequence 2: untouched."""
+    cfg = W.get(4)
+    _case("int8 beyond the headroom")
+    inp = W.attention_inputs_int8(cfg, B=3, lens=[700, 300, 2000])
+    ks = inp["k_scale"].astype(np.float32)
+    ks[0, :, 64:] *= 200.0
+    inp["k_scale"] = ks.astype(np.float16)
+    kn = W.bf16_bits_to_f32(inp["k_new"]).copy()
+    kn[1] *= 200.0
+    inp["k_new"] = W.bf16_bits(kn)
+    _check(inp, _run(inp, hint=cfg.L[1]))
+
+
+def test_query_outside_f16():
+    """A query value beyond f16's range (the wave kernel's products run in
+    f16) sends its slab to the exact path; the rest of the call is unchanged."""
+    cfg = W.get(4)
+    _case("int8 query outside f16")
+    inp = W.attention_inputs_int8(cfg, B=2, lens=[500, 900])
+    q = W.bf16_bits_to_f32(inp["q"]).copy()
+    q[1, 3, 2, 17] = 70000.0
+    inp["q"] = W.bf16_bits(q)
     _check(inp, _run(inp, hint=cfg.L[1]), relative=True)
 
 

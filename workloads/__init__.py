@@ -18,6 +18,7 @@ from .gen import (  # noqa: F401
     attention_inputs_int8,
     attention_inputs_int8_device,
     bf16_bits,
+    bf16_bits_to_f32,
     sampler_inputs,
     sampler_inputs_device,
 )
