@@ -1451,7 +1451,7 @@ __global__ __launch_bounds__(64) void attn_stream_i8w(AttnArgs a) {
 // Merge the pieces of each (b, g, rg) slab the stream kernel cut; one
 // workgroup per slab.  Slabs covered whole were written by the stream kernel.
 template <int D, bool F16 = false>
-__device__ __forceinline__ void combine_stream_slab(const AttnArgs& a, long slab) {
+__device__ __forceinline__ void combine_stream_slab(const AttnArgs& a, long slab, int chunk, int nchunk) {
   using H = Half16<F16>;
   const int rg = (int)(slab % a.RG);
   const int g = (int)((slab / a.RG) % a.Hkv);
@@ -1466,7 +1466,7 @@ __device__ __forceinline__ void combine_stream_slab(const AttnArgs& a, long slab
   };
   const int nbb = slab_blocks(a, b);
   if (nbb == 0) {  // rejected length: NaN rows, nothing else touched
-    for (int e = threadIdx.x; e < nrows * D; e += blockDim.x) out_ptr(e / D)[e % D] = H::kNaN;
+    for (int e = chunk * blockDim.x + threadIdx.x; e < nrows * D; e += nchunk * blockDim.x) out_ptr(e / D)[e % D] = H::kNaN;
     return;
   }
   const int HR = a.Hkv * a.RG;
@@ -1477,7 +1477,7 @@ __device__ __forceinline__ void combine_stream_slab(const AttnArgs& a, long slab
   const int np = (int)min(w1 - w0 + 1, (long long)a.JP);
   const size_t base = (size_t)slab * a.JP;
   constexpr int D4 = D / 4;
-  for (int e = threadIdx.x; e < nrows * D4; e += blockDim.x) {
+  for (int e = chunk * blockDim.x + threadIdx.x; e < nrows * D4; e += nchunk * blockDim.x) {
     const int row = e / D4, d = 4 * (e % D4);
     // Online merge, four pieces at a time with all their loads in flight
     // (the piece count is only known at run time).
@@ -1518,9 +1518,17 @@ __device__ __forceinline__ void combine_stream_slab(const AttnArgs& a, long slab
   }
 }
 
+// Workgroups of the combine launches per slab: one output item (4 values of
+// a row) per thread, so each thread's loads are in flight at once.
+template <int D>
+__host__ __device__ constexpr int combine_chunks(int RT) {
+  return (16 * RT * (D / 4) + 255) / 256;
+}
+
 template <int D, bool F16 = false>
 __global__ __launch_bounds__(256) void attn_combine_stream(AttnArgs a) {
-  combine_stream_slab<D, F16>(a, blockIdx.x);
+  const int nchunk = combine_chunks<D>(a.RT);
+  combine_stream_slab<D, F16>(a, blockIdx.x / nchunk, (int)(blockIdx.x % nchunk), nchunk);
 }
 
 // The exact path of the int8 call for a slab its stream pieces gave up on (a
@@ -1577,12 +1585,14 @@ __device__ void i8_slab_exact(const AttnArgs& a, long slab) {
 // exact path, the others are merged as in the bf16 call.
 template <int D>
 __global__ __launch_bounds__(256) void attn_combine_i8(AttnArgs a) {
-  const long slab = blockIdx.x;
+  const int nchunk = combine_chunks<D>(a.RT);
+  const long slab = blockIdx.x / nchunk;
+  const int chunk = (int)(blockIdx.x % nchunk);
   if (a.ovf[slab] != 0u && slab_blocks(a, (int)(slab / ((long)a.RG * a.Hkv))) > 0) {
-    i8_slab_exact<D>(a, slab);
+    if (chunk == 0) i8_slab_exact<D>(a, slab);  // the whole slab, by one workgroup
     return;
   }
-  combine_stream_slab<D, false>(a, slab);
+  combine_stream_slab<D, false>(a, slab, chunk, nchunk);
 }
 
 // ---------------------------------------------------------------------------
@@ -2046,7 +2056,7 @@ static hipError_t launch_stream_as(const AttnArgs& a0, hipStream_t s) {
                      a, a.table);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || kMerge) return e;
-  hipLaunchKernelGGL((attn_combine_stream<D, F16>), dim3((unsigned)slabs), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_combine_stream<D, F16>), dim3((unsigned)(slabs * combine_chunks<D>(a.RT))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -2075,7 +2085,8 @@ static hipError_t launch_i8(const AttnArgs& a0, hipStream_t s) {
   hipLaunchKernelGGL((attn_stream_i8w<D, RT>), dim3((unsigned)a.P), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_combine_i8<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_combine_i8<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG * combine_chunks<D>(a.RT))),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
