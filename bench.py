@@ -428,6 +428,7 @@ def main():
     B = cfg.B
     t = time_steps(torch, sv, cfg, T, sets, hint, args.steps, args.warmup, kv=args.kv, paged=args.paged)
     ms_step, att_ms, smp_ms, trn_ms = t["ms_step"], t["att_ms"], t["smp_ms"], t["trn_ms"]
+    b2b_ms = attention_back_to_back(torch, sv, sets, hint, min(args.steps, 20), kv=args.kv, paged=args.paged)
 
     # Algorithmic bytes per call, averaged over the rotated input sets (their
     # lengths differ); set k is used by steps k, k + nsets, ...
@@ -485,7 +486,10 @@ def main():
         "parts": {
             "attention": {"ms": att_ms, "bytes": att_b, "GB/s": att_gbs, "hbm_frac": att_gbs / HBM_PEAK_GBS,
                           "positions/s": positions / (att_ms * 1e-3), "flops": att_f,
-                          "mfma_frac": att_f / (att_ms * 1e-3) / (mfma_peak * 1e12)},
+                          "mfma_frac": att_f / (att_ms * 1e-3) / (mfma_peak * 1e12),
+                          "back_to_back": {"ms": b2b_ms,
+                                           "hbm_frac": sum(a[0] for a in per_set) / len(per_set) / (b2b_ms * 1e-3) / 8e12,
+                                           "calls": min(args.steps, 20)}},
             "sampler": {"ms": smp_ms, "bytes": smp_b, "GB/s": smp_gbs, "hbm_frac": smp_gbs / HBM_PEAK_GBS,
                         "positions/s": positions / (smp_ms * 1e-3)},
             "truncate": {"ms": trn_ms},
@@ -613,6 +617,39 @@ def sampler_only(torch, sv, cfg, T, dev, steps, warmup):
             "positions/s": cfg.B * cfg.gamma / (ms * 1e-3), "mean_accepted": float(n.float().mean().item())}
 
 
+def attention_back_to_back(torch, sv, sets, hint, calls, kv="bf16", paged=0):
+    """Milliseconds per attention call when ``calls`` calls run back to back
+    (input sets alternating) between two events on the launch stream: the
+    call's own throughput, without the per-call events of the step loop
+    (each of which costs the stream a few microseconds).  Lengths are left as
+    they are, so every call appends the same rows again."""
+    stream = torch.cuda.current_stream()
+    for att, _ in sets:
+        att["lens"].copy_(att["lens_base"])
+
+    def call(att):
+        if kv == "int8":
+            sv.spec_verify_attention_int8(att["q"], att["k_new"], att["v_new"], att["k_q"], att["k_scale"],
+                                          att["v_q"], att["v_scale"], att["lens"], hint, out=att["out"])
+        elif paged:
+            sv.spec_verify_attention_paged(att["q"], att["k_new"], att["v_new"], att["k_pages"], att["v_pages"],
+                                           att["table"], att["lens"], hint, out=att["out"])
+        else:
+            sv.spec_verify_attention(att["q"], att["k_new"], att["v_new"], att["k_cache"], att["v_cache"],
+                                     att["lens"], hint, out=att["out"])
+
+    for k in range(len(sets)):
+        call(sets[k][0])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for k in range(calls):
+        call(sets[k % len(sets)][0])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / calls
+
+
 def step_parts(torch, sv, cfg, dev, steps, warmup):
     """The whole step at another configuration (its first temperature):
     per-call event times and HBM fractions of attention and the sampler."""
@@ -623,6 +660,8 @@ def step_parts(torch, sv, cfg, dev, steps, warmup):
     per_set = [algorithmic(cfg, st[0]["lens_base"].cpu().numpy(), cfg.B) for st in sets]
     counts = [len(range(k, steps, len(sets))) for k in range(len(sets))]
     att_b = sum(c * a[0] for c, a in zip(counts, per_set)) / steps
+    b2b = attention_back_to_back(torch, sv, sets, cfg.L[1], steps)
+    b2b_b = sum(a[0] for a in per_set) / len(per_set)
     smp_b = per_set[0][2]
     pos = cfg.B * cfg.gamma
     out = {"workload": f"config{cfg.cid} {cfg.name}: B={cfg.B} gamma={cfg.gamma} GQA {cfg.Hq}/{cfg.Hkv} "
@@ -630,7 +669,9 @@ def step_parts(torch, sv, cfg, dev, steps, warmup):
            "steps": steps, "input_sets": len(sets), "ms_per_step": t["ms_step"],
            "positions/s": pos / (t["ms_step"] * 1e-3),
            "attention": {"ms": t["att_ms"], "bytes": att_b, "hbm_frac": att_b / (t["att_ms"] * 1e-3) / 8e12,
-                         "positions/s": pos / (t["att_ms"] * 1e-3)},
+                         "positions/s": pos / (t["att_ms"] * 1e-3),
+                         "back_to_back": {"ms": b2b, "hbm_frac": b2b_b / (b2b * 1e-3) / 8e12,
+                                          "calls": steps}},
            "sampler": {"ms": t["smp_ms"], "bytes": smp_b, "hbm_frac": smp_b / (t["smp_ms"] * 1e-3) / 8e12,
                        "positions/s": pos / (t["smp_ms"] * 1e-3)},
            "truncate": {"ms": t["trn_ms"]}}
