@@ -474,7 +474,7 @@ def main():
             "unit": "GB/s",
             "frac": att_gbs / HBM_PEAK_GBS,
             "traffic": None if traffic is None else traffic["bytes_per_call"],
-            "kernel": ("spec_verify_attention_int8: quant_new_rows + attn_stream_i8w + attn_combine_i8, one call"
+            "kernel": ("spec_verify_attention_int8: quant_new_rows + attn_stream_i8w with attn_combine_i8 or, for long shares, attn_stream_prep and attn_exact_i8, one call"
                        if args.kv == "int8" else
                        "spec_verify_attention: attn_stream_bf16 with attn_combine_stream or, for long shares, "
                        "attn_stream_prep, one call"

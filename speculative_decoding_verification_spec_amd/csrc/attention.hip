@@ -836,7 +836,7 @@ __device__ __forceinline__ void stream_walk(const AttnArgs& a, Piece&& piece) {
 // whose add completes the count merges the slab's np partials (device-scope
 // loads) and writes the output, as attn_combine_stream would.  Every wave
 // calls it.
-template <int D, int NW, bool F16>
+template <int D, int ROWS, int NT, bool F16>
 __device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, int rg, size_t slot, int np) {
   using H = Half16<F16>;
   __shared__ int sh_last;
@@ -847,12 +847,12 @@ __device__ __forceinline__ void stream_merge(const AttnArgs& a, int b, int g, in
     sh_last = __hip_atomic_fetch_add(a.scnt + slab, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(np - 1);
   __syncthreads();
   if (!sh_last) return;  // uniform over the workgroup
-  constexpr int ROWS = 16 * NW, D4 = D / 4;
+  constexpr int D4 = D / 4;
   const int row0 = rg * ROWS;
   const int nrows = min(ROWS, a.M - row0);
   const size_t base = slab * (size_t)a.JP;
   uint16_t* out = static_cast<uint16_t*>(a.out);
-  for (int e = threadIdx.x; e < nrows * D4; e += 64 * NW) {
+  for (int e = threadIdx.x; e < nrows * D4; e += NT) {
     const int row = e / D4, d = 4 * (e % D4);
     float mx = neg_inf_f(), den = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -904,7 +904,7 @@ void attn_stream_bf16(AttnArgs a, const int32_t* __restrict__ table) {
   stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append, int np) {
     bf16_piece<D, NW, NST, PG, MERGE, F16>(a, kbuf, vbuf, b, g, rg, L, k0, k1, whole, slot, append, table);
     if constexpr (MERGE) {
-      if (!whole) stream_merge<D, NW, F16>(a, b, g, rg, slot, np);
+      if (!whole) stream_merge<D, 16 * NW, 64 * NW, F16>(a, b, g, rg, slot, np);
     }
   });
 }
@@ -1079,8 +1079,11 @@ __device__ __forceinline__ bf16x8 widen8_scaled(uint32_t w0, uint32_t w1, float 
   return o;
 }
 
-template <int D, int RT, typename KS, typename VS, typename SS>
-__device__ __forceinline__ void i8w_piece(const AttnArgs& a, KS kst, VS vst, SS sst, uint16_t* __restrict__ vt, int b,
+// Returns false when the piece left its slab to the exact path (its partial
+// is then not written).  MERGE: partials through device-scope stores, for the
+// in-launch merge.
+template <int D, int RT, bool MERGE, typename KS, typename VS, typename SS>
+__device__ __forceinline__ bool i8w_piece(const AttnArgs& a, KS kst, VS vst, SS sst, uint16_t* __restrict__ vt, int b,
                                           int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append) {
   using LY = BfLayout<D>;
   using IL = I8Layout<D>;
@@ -1402,7 +1405,7 @@ __device__ __forceinline__ void i8w_piece(const AttnArgs& a, KS kst, VS vst, SS 
   }
   if (__ballot(over)) {
     if (lane == 0) a.ovf[bg * a.RG + rg] = 1u;
-    return;
+    return false;
   }
 
 #pragma unroll
@@ -1424,14 +1427,28 @@ __device__ __forceinline__ void i8w_piece(const AttnArgs& a, KS kst, VS vst, SS 
     } else {
       const int row = 16 * r + lr;
       float* po = a.part_o + slot * ROWS * D;
-      if (lg == 0) a.part_ml[slot * ROWS + row] = ML{mref[r], lt[r]};
+      if constexpr (MERGE) {
+        if (lg == 0) co_store2(reinterpret_cast<float*>(a.part_ml + slot * ROWS + row), mref[r], lt[r]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[r][dt];
+        for (int dt = 0; dt < DT; ++dt) {
+          float* pd = po + (size_t)row * D + 16 * dt + 4 * lg;
+          co_store2(pd, oacc[r][dt][0], oacc[r][dt][1]);
+          co_store2(pd + 2, oacc[r][dt][2], oacc[r][dt][3]);
+        }
+      } else {
+        if (lg == 0) a.part_ml[slot * ROWS + row] = ML{mref[r], lt[r]};
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + (size_t)row * D + 16 * dt + 4 * lg) = oacc[r][dt];
+      }
     }
   }
+  return true;
 }
 
-template <int D, int RT>
+// MERGE: the pieces of a slab are merged by the last of its workgroups
+// (stream_merge, as in the bf16 kernel); a piece that leaves its slab to the
+// exact path does not count itself, so that slab is never merged here.
+template <int D, int RT, bool MERGE>
 __global__ __launch_bounds__(64) void attn_stream_i8w(AttnArgs a) {
   constexpr int T = KB * D;
   __shared__ __attribute__((aligned(1024))) int8_t stg[I8W_STAGES][2 * T];  // K tile, V tile
@@ -1443,8 +1460,11 @@ __global__ __launch_bounds__(64) void attn_stream_i8w(AttnArgs a) {
   auto kst = [&](auto S) -> int8_t* { return stg[decltype(S)::value]; };
   auto vst = [&](auto S) -> int8_t* { return stg[decltype(S)::value] + T; };
   auto sst = [&](auto S) -> uint16_t* { return ssc[decltype(S)::value]; };
-  stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append, int) {
-    i8w_piece<D, RT>(a, kst, vst, sst, vt, b, g, rg, L, k0, k1, whole, slot, append);
+  stream_walk(a, [&](int b, int g, int rg, int L, int k0, int k1, bool whole, size_t slot, bool append, int np) {
+    const bool counted = i8w_piece<D, RT, MERGE>(a, kst, vst, sst, vt, b, g, rg, L, k0, k1, whole, slot, append);
+    if constexpr (MERGE) {
+      if (!whole && counted) stream_merge<D, 16 * RT, kWave, false>(a, b, g, rg, slot, np);
+    }
   });
 }
 
@@ -1593,6 +1613,14 @@ __global__ __launch_bounds__(256) void attn_combine_i8(AttnArgs a) {
     return;
   }
   combine_stream_slab<D, false>(a, slab, chunk, nchunk);
+}
+
+// After a merging int8 stream launch: only the slabs marked for the exact
+// path have work.
+template <int D>
+__global__ __launch_bounds__(256) void attn_exact_i8(AttnArgs a) {
+  const long slab = blockIdx.x;
+  if (a.ovf[slab] != 0u && slab_blocks(a, (int)(slab / ((long)a.RG * a.Hkv))) > 0) i8_slab_exact<D>(a, slab);
 }
 
 // ---------------------------------------------------------------------------
@@ -2075,14 +2103,33 @@ static hipError_t launch_stream(const AttnArgs& a, hipStream_t s) {
   return launch_stream_as<D, NW, PG, false, F16>(a, s);
 }
 
+// As for bf16, shares of kMergeMinShare blocks or more merge their pieces in
+// the stream launch (a small prep launch zeroes the counters and writes the
+// NaN rows of rejected lengths; the exact-path launch after it has work only
+// for marked slabs); shorter ones keep the combine launch.
 template <int D, int RT>
 static hipError_t launch_i8(const AttnArgs& a0, hipStream_t s) {
   AttnArgs a = a0;
+  const size_t slabs = (size_t)a.B * a.Hkv * a.RG;
   hipLaunchKernelGGL((quant_new_rows<D>), dim3((unsigned)((size_t)a.B * a.Hkv)), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  a.P = stream_workgroups<attn_stream_i8w<D, RT>>(1, 8, kStreamMaxWG8);
-  hipLaunchKernelGGL((attn_stream_i8w<D, RT>), dim3((unsigned)a.P), dim3(64), 0, s, a);
+  const long nbmax = ((long)a.hint + a.n_q + KB - 1) / KB;
+  const int Pm = stream_workgroups<attn_stream_i8w<D, RT, true>>(1, 8, kStreamMaxWG8);
+  if ((long)slabs * nbmax >= (long)kMergeMinShare * Pm) {
+    a.P = Pm;
+    hipLaunchKernelGGL((attn_stream_prep<D, false>), dim3((unsigned)std::min<size_t>((slabs + 255) / 256, 1024)),
+                       dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_stream_i8w<D, RT, true>), dim3((unsigned)a.P), dim3(64), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_exact_i8<D>), dim3((unsigned)slabs), dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  a.P = stream_workgroups<attn_stream_i8w<D, RT, false>>(1, 8, kStreamMaxWG8);
+  hipLaunchKernelGGL((attn_stream_i8w<D, RT, false>), dim3((unsigned)a.P), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_combine_i8<D>), dim3((unsigned)((size_t)a.B * a.Hkv * a.RG * combine_chunks<D>(a.RT))),
@@ -2394,6 +2441,7 @@ extern "C" spec_status_t spec_verify_attention_int8(const void* q, const void* k
   a.nks = reinterpret_cast<uint16_t*>(ws + ip.off_nks);
   a.nvs = reinterpret_cast<uint16_t*>(ws + ip.off_nvs);
   a.ovf = reinterpret_cast<uint32_t*>(ws + ip.off_ovf);
+  a.scnt = reinterpret_cast<uint32_t*>(ws + ip.sp.off_cnt);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;

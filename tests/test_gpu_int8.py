@@ -121,6 +121,44 @@ def test_config5_shape_sampled():
     torch.cuda.empty_cache()
 
 
+def test_config5_shape_exact_path():
+    """At the benchmark's shape (pieces merged inside the stream launch), two
+    sequences are sent to the exact path -- one by K scales 200 times larger
+    after key 64, one by a query value beyond f16 -- while the others stay on
+    the fast path; four sequences are compared one by one."""
+    cfg = W.get(5)
+    _case("int8 config5 exact path", B=cfg.B, max_T=cfg.max_T)
+    d = W.attention_inputs_int8_device(cfg, "cuda")
+    lens = _gpu.to_host(d["lens"])
+    loud_k, loud_q = int(np.argmin(lens)), int(np.argmax(lens))
+    plain = [b for b in np.random.default_rng(7).permutation(cfg.B) if b not in (loud_k, loud_q)][:2]
+    d["k_scale"][loud_k, :, 64:] *= 200.0
+    d["q"][loud_q, 5, 3, 40] = 70000.0
+    seqs = [loud_k, loud_q] + [int(b) for b in plain]
+    n = cfg.n_q
+    before = {}
+    for b in seqs:
+        L = int(lens[b])
+        before[b] = {k: _gpu.to_host(d[k][b : b + 1, :, :L]) for k in ("k_cache", "k_scale", "v_cache", "v_scale")}
+    out = sv.spec_verify_attention_int8(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["k_scale"], d["v_cache"],
+                                        d["v_scale"], d["lens"], cfg.L[1])
+    torch.cuda.synchronize()
+    for b in seqs:
+        L = int(lens[b])
+        print(f"sequence {b} L={L}", end=": ", flush=True)
+        inp = {k: _gpu.to_host(d[k][b : b + 1]) for k in ("q", "k_new", "v_new")}
+        inp["lens"] = np.array([L], np.int32)
+        for k in ("k_cache", "k_scale", "v_cache", "v_scale"):
+            pre = _gpu.to_host(d[k][b : b + 1, :, : L + n]).copy()
+            pre[:, :, :L] = before[b][k]
+            inp[k] = pre
+        res = {"out": _gpu.to_host(out[b : b + 1]),
+               **{k: _gpu.to_host(d[k][b : b + 1, :, : L + n]) for k in ("k_cache", "k_scale", "v_cache", "v_scale")}}
+        _check(inp, res, relative=(b == loud_q))
+    del d
+    torch.cuda.empty_cache()
+
+
 def test_zero_and_loud_new_rows():
     cfg = W.get(4)
     _case("int8 zero / loud new rows")
