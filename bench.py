@@ -429,6 +429,7 @@ def main():
     t = time_steps(torch, sv, cfg, T, sets, hint, args.steps, args.warmup, kv=args.kv, paged=args.paged)
     ms_step, att_ms, smp_ms, trn_ms = t["ms_step"], t["att_ms"], t["smp_ms"], t["trn_ms"]
     b2b_ms = attention_back_to_back(torch, sv, sets, hint, min(args.steps, 20), kv=args.kv, paged=args.paged)
+    s2s_ms = sampler_back_to_back(torch, sv, sets[0][1], T, args.steps)
 
     # Algorithmic bytes per call, averaged over the rotated input sets (their
     # lengths differ); set k is used by steps k, k + nsets, ...
@@ -491,7 +492,9 @@ def main():
                                            "hbm_frac": sum(a[0] for a in per_set) / len(per_set) / (b2b_ms * 1e-3) / 8e12,
                                            "calls": min(args.steps, 20)}},
             "sampler": {"ms": smp_ms, "bytes": smp_b, "GB/s": smp_gbs, "hbm_frac": smp_gbs / HBM_PEAK_GBS,
-                        "positions/s": positions / (smp_ms * 1e-3)},
+                        "positions/s": positions / (smp_ms * 1e-3),
+                        "back_to_back": {"ms": s2s_ms, "hbm_frac": smp_b / (s2s_ms * 1e-3) / 8e12,
+                                         "calls": args.steps}},
             "truncate": {"ms": trn_ms},
             "mean_accepted": float(n_last.mean()),
         },
@@ -610,11 +613,14 @@ def sampler_only(torch, sv, cfg, T, dev, steps, warmup):
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     nbytes = algorithmic(cfg, np.zeros(cfg.B), cfg.B)[2]
+    smp["n"], smp["tok"] = n, tok
+    b2b = sampler_back_to_back(torch, sv, smp, T, steps)
     del smp
     torch.cuda.empty_cache()
     return {"ms": ms, "bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
             "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "positions/s": cfg.B * cfg.gamma / (ms * 1e-3), "mean_accepted": float(n.float().mean().item())}
+            "positions/s": cfg.B * cfg.gamma / (ms * 1e-3), "mean_accepted": float(n.float().mean().item()),
+            "back_to_back": {"ms": b2b, "hbm_frac": nbytes / (b2b * 1e-3) / 1e9 / HBM_PEAK_GBS, "calls": steps}}
 
 
 def attention_back_to_back(torch, sv, sets, hint, calls, kv="bf16", paged=0):
@@ -650,6 +656,27 @@ def attention_back_to_back(torch, sv, sets, hint, calls, kv="bf16", paged=0):
     return e0.elapsed_time(e1) / calls
 
 
+def sampler_back_to_back(torch, sv, smp, T, calls):
+    """Milliseconds per spec_reject_sample call, ``calls`` calls back to back
+    between two events on the launch stream (same inputs, outputs overwritten)."""
+    stream = torch.cuda.current_stream()
+    greedy = T == 0
+
+    def call():
+        sv.spec_reject_sample(smp["target_logits"], None if greedy else smp["draft_logits"], smp["draft_tokens"],
+                              None if greedy else smp["uniforms"], T, n_accepted=smp["n"], out_tokens=smp["tok"])
+
+    call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(calls):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / calls
+
+
 def step_parts(torch, sv, cfg, dev, steps, warmup):
     """The whole step at another configuration (its first temperature):
     per-call event times and HBM fractions of attention and the sampler."""
@@ -662,6 +689,7 @@ def step_parts(torch, sv, cfg, dev, steps, warmup):
     att_b = sum(c * a[0] for c, a in zip(counts, per_set)) / steps
     b2b = attention_back_to_back(torch, sv, sets, cfg.L[1], steps)
     b2b_b = sum(a[0] for a in per_set) / len(per_set)
+    s2s = sampler_back_to_back(torch, sv, sets[0][1], T, steps)
     smp_b = per_set[0][2]
     pos = cfg.B * cfg.gamma
     out = {"workload": f"config{cfg.cid} {cfg.name}: B={cfg.B} gamma={cfg.gamma} GQA {cfg.Hq}/{cfg.Hkv} "
@@ -673,7 +701,8 @@ def step_parts(torch, sv, cfg, dev, steps, warmup):
                          "back_to_back": {"ms": b2b, "hbm_frac": b2b_b / (b2b * 1e-3) / 8e12,
                                           "calls": steps}},
            "sampler": {"ms": t["smp_ms"], "bytes": smp_b, "hbm_frac": smp_b / (t["smp_ms"] * 1e-3) / 8e12,
-                       "positions/s": pos / (t["smp_ms"] * 1e-3)},
+                       "positions/s": pos / (t["smp_ms"] * 1e-3),
+                       "back_to_back": {"ms": s2s, "hbm_frac": smp_b / (s2s * 1e-3) / 8e12, "calls": steps}},
            "truncate": {"ms": t["trn_ms"]}}
     del sets
     torch.cuda.empty_cache()

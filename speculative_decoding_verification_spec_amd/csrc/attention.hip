@@ -51,6 +51,13 @@
 // fp32 kernel.  One wave per split holding every row tile; one key per lane
 // per MFMA, so V is read straight from memory.
 //
+// int8 kernel ([P2] section PagedAttentionとKVキャッシュの量子化).  The stream
+// scheme with one-wave workgroups holding every row tile of a slab: each raw
+// int8 block is widened once (K exactly to f16 for f16 products, V
+// dequantised to bf16 for the bf16 PV product) and used by every tile; the
+// probabilities are taken against a fixed per-row reference, with an exact
+// fp32 path for the rare slab whose scores outgrow it (see its section).
+//
 // Keys [0, L_b) come from the cache, keys [L_b, L_b + n_q) from k_new/v_new
 // directly (so the append in the same launch is never read back), and keys at
 // or past L_b + n_q are masked (they read a finite dummy row).  Cache rows at
