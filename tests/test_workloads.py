@@ -56,3 +56,14 @@ def test_gumbel_drafts_follow_softmax_of_draft_logits():
     cnt = np.bincount(x, minlength=V)
     chi2 = np.sum((cnt - N * p) ** 2 / (N * p))
     assert chi2 < V - 1 + 4 * np.sqrt(2 * (V - 1))
+
+
+def test_repeated_row_inputs_repeat_one_pair():
+    a = W.repeated_row_inputs(5, 65, 3, 1000, 0.7, chunk=300)
+    b = W.repeated_row_inputs(5, 65, 3, 1000, 0.7)
+    for k in ("target_logits", "draft_logits", "draft_tokens", "uniforms"):
+        assert np.array_equal(a[k], b[k])  # chunking does not change the draws
+    assert a["target_logits"].shape == (1000, 4, 65) and a["draft_logits"].shape == (1000, 3, 65)
+    assert np.all(a["target_logits"] == a["target_row"]) and np.all(a["draft_logits"] == a["draft_row"])
+    assert a["draft_tokens"].dtype == np.int32 and 0 <= a["draft_tokens"].min() and a["draft_tokens"].max() < 65
+    assert a["uniforms"].min() >= 0 and a["uniforms"].max() < 1

@@ -19,6 +19,7 @@ from .gen import (  # noqa: F401
     attention_inputs_int8_device,
     bf16_bits,
     bf16_bits_to_f32,
+    repeated_row_inputs,
     sampler_inputs,
     sampler_inputs_device,
 )

@@ -93,6 +93,44 @@ def sampler_inputs(cfg: Config, temperature=None, rep: int = 0, B=None):
     }
 
 
+def repeated_row_inputs(seed: int, V: int, gamma: int, N: int, temperature: float = 1.0, t_std: float = 2.5,
+                        noise_std: float = 0.45, chunk: int = 8192):
+    """N sequences that all verify one fixed (target row, draft row) pair.
+
+    Every target position holds the same fp32 logit row z_t ~ t_std * N(0, 1)
+    over V tokens, every draft position the row z_d = z_t + noise_std * N(0, 1)
+    (for V = 65 and the defaults the two distributions overlap by 0.78 to
+    0.97 depending on the seed, around the 0.86 to 0.90 acceptance of the
+    character models the pages measure).
+    Each sequence draws its own draft tokens from softmax(z_d / T) and its own
+    uniforms, so the N results are independent draws of one verification.
+    Streams: ``default_rng([seed, 0])`` the rows, ``[seed, 1]`` the
+    draft-sampling noise (drawn chunk by chunk), ``[seed, 2]`` the uniforms.
+    """
+    T = float(temperature)
+    r0 = np.random.default_rng([seed, 0])
+    zt_row = (t_std * r0.standard_normal(V)).astype(np.float32)
+    zd_row = (zt_row + noise_std * r0.standard_normal(V)).astype(np.float32)
+    zt = np.ascontiguousarray(np.broadcast_to(zt_row, (N, gamma + 1, V)))
+    zd = np.ascontiguousarray(np.broadcast_to(zd_row, (N, gamma, V)))
+    r1 = np.random.default_rng([seed, 1])
+    x = np.empty((N, gamma), np.int32)
+    zs = zd_row.astype(np.float64) / T
+    for s in range(0, N, chunk):
+        e = min(N, s + chunk)
+        x[s:e] = _gumbel_argmax(zs, r1.random((e - s, gamma, V)))
+    u = np.random.default_rng([seed, 2]).random((N, gamma + 1))
+    return {
+        "target_logits": zt,
+        "draft_logits": zd,
+        "draft_tokens": x,
+        "uniforms": np.ascontiguousarray(u, dtype=np.float64),
+        "temperature": T,
+        "target_row": zt_row,
+        "draft_row": zd_row,
+    }
+
+
 def lengths(cfg: Config, rep: int = 0, B=None):
     B = cfg.B if B is None else int(B)
     lo, hi = cfg.L
