@@ -658,22 +658,31 @@ def attention_back_to_back(torch, sv, sets, hint, calls, kv="bf16", paged=0):
 
 def sampler_back_to_back(torch, sv, smp, T, calls):
     """Milliseconds per spec_reject_sample call, ``calls`` calls back to back
-    between two events on the launch stream (same inputs, outputs overwritten)."""
+    between two events on the launch stream (outputs overwritten).  When one
+    call's logits are smaller than three times the 256 MB memory-side cache,
+    the calls cycle through copies of them in separate buffers (at most 8),
+    so that a call does not find the previous call's rows still cached."""
     stream = torch.cuda.current_stream()
     greedy = T == 0
+    keys = ("target_logits",) if greedy else ("target_logits", "draft_logits")
+    nbytes = sum(smp[k].numel() * smp[k].element_size() for k in keys)
+    copies = [smp] + [{**smp, **{k: smp[k].clone() for k in keys}}
+                      for _ in range(max(1, min(8, math.ceil(768e6 / nbytes))) - 1)]
 
-    def call():
-        sv.spec_reject_sample(smp["target_logits"], None if greedy else smp["draft_logits"], smp["draft_tokens"],
-                              None if greedy else smp["uniforms"], T, n_accepted=smp["n"], out_tokens=smp["tok"])
+    def call(c):
+        sv.spec_reject_sample(c["target_logits"], None if greedy else c["draft_logits"], c["draft_tokens"],
+                              None if greedy else c["uniforms"], T, n_accepted=c["n"], out_tokens=c["tok"])
 
-    call()
+    for c in copies:
+        call(c)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(calls):
-        call()
+    for k in range(calls):
+        call(copies[k % len(copies)])
     e1.record(stream)
     torch.cuda.synchronize()
+    del copies
     return e0.elapsed_time(e1) / calls
 
 

@@ -171,12 +171,16 @@ size_t spec_verify_attention_int8_workspace_size(int B, int Hq, int Hkv, int n_q
  *            with the quantised new rows; no other row is written; rows >=
  *            cache_len[b] are never used.
  *   workspace device, >= spec_verify_attention_int8_workspace_size(...) bytes.
- * Arithmetic: scores from the bf16 MFMA on the exact int8 values, times the
- * key's scale in fp32; V rows dequantised to bf16(q s) for the bf16 PV
- * product.  Probabilities are taken against a fixed per-row reference (the
- * row's largest score in its first key block); a row whose scores later
- * exceed it by more than 2^64 in probability is computed again on an exact
- * fp32 path with the usual running-maximum rescale.
+ * Arithmetic: scores from the f16 MFMA with fp32 accumulation, the int8
+ * values widened to f16 exactly and the bf16 query converted to f16 (exact
+ * down to 2^-14 in magnitude, a few low bits lost below), times the key's
+ * scale in fp32; V rows dequantised to bf16(q s) for the bf16 PV product.
+ * Probabilities are taken against a fixed per-row reference (the row's
+ * largest score in its first key block).  A group of rows sharing a KV head
+ * is computed again on an exact fp32 path with the usual running-maximum
+ * rescale when one of its rows sums to more than 2^64 against that reference
+ * or to a value that is not finite, or when one of its query elements is
+ * beyond f16's range (|x| > 65504, inf or NaN).
  * Supported: D in {64, 128}, B <= 1024, and the limits of
  * spec_verify_attention.
  * Errors: as spec_verify_attention (dtype fixed to bf16 activations), and

@@ -24,7 +24,7 @@ GPT-2's: LayerNorm over the last axis with the population variance and
 eps = 1e-5, and GELU in its tanh form.
 
 Parameters are one flat array in the order of ``param_shapes`` (the packing
-is this build's choice, defined again independently by the library):
+is a convention of this oracle, which the library defines again on its own):
   token embedding [V, C], position embedding [T, C],
   per block: norm1 gain [C], bias [C]; attention in [C, 3C]; attention
              out [C, C]; norm2 gain [C], bias [C]; MLP up [C, F], up bias

@@ -198,6 +198,28 @@ def test_query_outside_f16():
     _check(inp, _run(inp, hint=cfg.L[1]), relative=True)
 
 
+def test_cache_full_to_capacity():
+    cfg = W.get(4)
+    B, max_T = 2, 1024
+    _case("int8 capacity", B=B, max_T=max_T)
+    inp = W.attention_inputs_int8(cfg, B=B, max_T=max_T, lens=[max_T - cfg.n_q, 3])
+    _check(inp, _run(inp, hint=max_T - cfg.n_q))
+
+
+def test_length_beyond_hint_or_negative_is_flagged_not_written():
+    cfg = W.get(4)
+    B, max_T = 3, 512
+    _case("int8 bad lengths", B=B, max_T=max_T)
+    inp = W.attention_inputs_int8(cfg, B=B, max_T=max_T, lens=[100, 400, 50])
+    inp["lens"][2] = -1
+    res = _run(inp, hint=200)  # sequence 1 exceeds the hint, sequence 2 is negative
+    for b in (1, 2):
+        assert np.all(np.isnan(_gpu.as_f64(res["out"][b])))
+        for name in ("k_cache", "k_scale", "v_cache", "v_scale"):
+            assert np.array_equal(res[name][b].view(np.uint8), inp[name][b].view(np.uint8)), (b, name)
+    _check({k: v[:1] for k, v in inp.items()}, {k: v[:1] for k, v in res.items()})
+
+
 def test_status_codes():
     _case("int8 status")
     dev = "cuda"
