@@ -1,7 +1,9 @@
 """Benchmark of the verification step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c4|c3]
-                    [--temperature T] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5|c4|c3|model]
+                    [--temperature T] [--kv bf16|f16|int8] [--paged 16|32]
+                    [--page-order random|sequential] [--no-cpu-baseline] [--no-extras]
+                    [--copy-calibration]
 
 A step is one pass of the whole hot path on one batch: verify attention with
 KV append, rejection sampling, length reset (three C-ABI calls on one
@@ -11,10 +13,13 @@ gamma=8, GQA 64/8, head dim 128, bf16 cache with lengths uniform in
 [8192, 32768], vocabulary 128,256).  Lengths are restored before each step
 (a 1 KB device copy) so every step verifies the same batch.
 
-Prints one JSON line: verified draft positions per second for the whole step,
-per-call durations measured with HIP events on the launch stream, the
-achieved fraction of the HBM roofline for each part, and the CPU oracle timed
-on a bounded sample of the same workload.
+Prints one JSON line: verified draft positions per second for the whole step
+(K steps between two events), per-call durations measured with HIP events on
+the launch stream in a second loop and back to back, the achieved fraction of
+the HBM roofline for each part, and the CPU oracle timed on a bounded sample
+of the same workload (one thread, and on all host cores).  At the default
+workload the line also carries config 5's sampler at T = 0.7 and config 4's
+step (``--no-extras`` leaves them out).
 """
 
 import argparse
