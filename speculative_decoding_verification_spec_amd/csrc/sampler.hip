@@ -687,7 +687,38 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Word j (of 32 bits) of a raw vector.
+template <typename R>
+__device__ __forceinline__ uint32_t raw_word(const R& r, int j) {
+  if constexpr (sizeof(R) == 16) return j == 0 ? r.x : j == 1 ? r.y : j == 2 ? r.z : r.w;
+  else if constexpr (sizeof(R) == 8) return j == 0 ? r.x : r.y;
+  else return (uint32_t)r;
+}
+
+// The two bf16 values packed in w as two 16-bit keys (packed integer
+// arithmetic, both halves at once) whose unsigned order is the values' order
+// for every bit pattern but NaN, with -0 one below +0: a positive value's bits
+// with the sign bit set, a negative value's bits inverted.  +inf maps to
+// 0xff80 and -inf to 0x007f; a positive NaN lands above +inf (0xff81 and up),
+// a negative one below -inf (0x007e and down).
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 bf16_pair_keys(uint32_t w) {
+  const s16x2 x = __builtin_bit_cast(s16x2, w);
+  const uint32_t neg = __builtin_bit_cast(uint32_t, x >> (s16x2){15, 15});  // 0xffff for a negative half
+  return __builtin_bit_cast(u16x2, w ^ (neg | 0x80008000u));
+}
+constexpr int kKeyPosInf = 0xff80, kKeyNegInf = 0x007f, kKeyNegZero = 0x7fff, kKeyPosZero = 0x8000;
+
 // Grid: x = target row b * (gamma + 1) + r, y = group of waves along the row.
+//
+// bf16 rows take a packed pass: per pair of elements, three integer
+// operations make the two keys, and the lane keeps their largest and smallest
+// (per group of VEC elements for the largest).  The wave's largest key then
+// names the largest value, and only the lanes that hold it look for its first
+// index.  A segment with a NaN (a key above +inf's or below -inf's) or whose
+// largest value is a zero (where -0 and +0 must tie) takes the elementwise
+// pass instead, which implements the rule directly.  Both give the same word.
 template <typename T, int VEC, int NIT, int SPW>
 __global__ __launch_bounds__(1024) void gs_stats(const T* __restrict__ tgt, int V, int nseg, uint64_t* __restrict__ part) {
   constexpr int SEG = kWave * VEC * NIT;
@@ -712,6 +743,59 @@ __global__ __launch_bounds__(1024) void gs_stats(const T* __restrict__ tgt, int 
   for (int k = 0; k < SPW; ++k) {
     const int seg = seg0 + k;
     if (seg >= nseg) break;
+    if constexpr (sizeof(T) == 2 && VEC % 2 == 0) {
+      constexpr int WPG = VEC / 2;  // words per group
+      u16x2 gmax[NIT];
+      u16x2 kmax = {0, 0}, kmin = {0xffff, 0xffff};
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        gmax[it] = (u16x2){0, 0};
+        if (!ok[k][it]) continue;
+#pragma unroll
+        for (int j = 0; j < WPG; ++j) {
+          const u16x2 key = bf16_pair_keys(raw_word(raw[k][it], j));
+          gmax[it] = __builtin_elementwise_max(gmax[it], key);
+          kmin = __builtin_elementwise_min(kmin, key);
+        }
+        kmax = __builtin_elementwise_max(kmax, gmax[it]);
+      }
+      // A lane without elements keeps 0 as its largest key, below every
+      // element's (NaN aside, and a NaN sends the segment elementwise).
+      const int lmax = max((int)kmax.x, (int)kmax.y);
+      const int lmin = min((int)kmin.x, (int)kmin.y);
+      const int wmax = wave_max(lmax);
+      const bool elementwise = __ballot(lmax > kKeyPosInf || lmin < kKeyNegInf) != 0ull || wmax == kKeyNegZero ||
+                               wmax == kKeyPosZero;
+      if (!elementwise) {  // uniform over the wave
+        int first = 0x7fffffff;
+        if (lmax == wmax) {
+          bool found = false;
+#pragma unroll
+          for (int it = 0; it < NIT; ++it) {
+            if (found || !ok[k][it] || (gmax[it].x != wmax && gmax[it].y != wmax)) continue;
+            const int idx0 = seg * SEG + (it * kWave + lane) * VEC;
+#pragma unroll
+            for (int j = 0; j < WPG; ++j) {
+              const u16x2 key = bf16_pair_keys(raw_word(raw[k][it], j));
+              if (!found && key.x == wmax) {
+                first = idx0 + 2 * j;
+                found = true;
+              }
+              if (!found && key.y == wmax) {
+                first = idx0 + 2 * j + 1;
+                found = true;
+              }
+            }
+          }
+        }
+        first = wave_min(first);
+        // The value with key wmax: a positive one's bits are the key without
+        // its top bit, a negative one's the key inverted.
+        const uint32_t bits = wmax >= kKeyPosZero ? (uint32_t)(wmax ^ 0x8000) : (uint32_t)(~wmax & 0xffff);
+        if (lane == 0) out[seg] = arg_word(order_key(bf16_to_f32((uint16_t)bits)), first);
+        continue;
+      }
+    }
     // A lane sees its elements in increasing index order, so a strict '>'
     // keeps the first of equal keys.  Every value's key exceeds 0.
     uint32_t best = 0u;

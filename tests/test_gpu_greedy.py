@@ -94,11 +94,27 @@ def _row_cases(V, rng):
     r = np.full(V, -np.inf, np.float32); rows.append(r)                  # all -inf
     r = base.copy(); r[V // 2] = np.nan; r[V // 3] = 50.0; rows.append(r)  # a NaN wins
     r = base.copy(); r[1 % V] = np.inf; rows.append(r)
+    if V >= 16:
+        # bf16 rows are read as packed pairs of 16-bit keys: ties inside one
+        # pair, across two pairs and across lanes, a negative NaN, zeros of
+        # both signs as the largest value, the largest finite value, a
+        # subnormal maximum
+        r = base.copy(); r[[4, 5]] = 9.0; rows.append(r)                 # one pair, low half first
+        r = base.copy(); r[[5, 6]] = 9.0; rows.append(r)                 # two pairs
+        r = base.copy(); r[[3, 9]] = 9.0; rows.append(r)                 # two lanes, the earlier index wins
+        r = base.copy(); r[V // 2] = np.float32(np.frombuffer(np.uint32(0xFFC00000).tobytes(), np.float32)[0])
+        rows.append(r)                                                    # a negative NaN wins
+        r = -np.abs(base) - 1.0; r[5] = -0.0; r[9] = 0.0; rows.append(r)  # -0 before +0, zero largest
+        r = -np.abs(base) - 1.0; r[9] = -0.0; r[5] = 0.0; rows.append(r)  # +0 before -0
+        r = -np.abs(base) - 1.0; r[7] = -0.0; rows.append(r)             # -0 alone largest
+        r = base.copy(); r[[2, V - 3]] = np.inf; rows.append(r)          # two +inf
+        r = base.copy(); r[[6, V - 2]] = np.float32(3.3895314e38); rows.append(r)  # largest finite bf16
+        r = -np.abs(base) - 1.0; r[V // 3] = np.float32(1e-40); rows.append(r)    # subnormal maximum
     return rows
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V,gamma", [(1, 1), (7, 3), (1003, 4), (4099, 2), (40000, 31), (151936, 4)])
+@pytest.mark.parametrize("V,gamma", [(1, 1), (7, 3), (1003, 4), (4098, 3), (4099, 2), (4100, 2), (40000, 31), (151936, 4)])
 def test_edges(dtype, V, gamma):
     _case("greedy edges", dtype=dtype, V=V, gamma=gamma)
     rng = np.random.default_rng([V, gamma])
