@@ -231,3 +231,52 @@ def test_bad_entries_over_the_first_pieces_flag_the_sequence(kind):
     assert torch.isnan(out_p[bad].float()).all()
     good = [b for b in range(cfg.B) if b not in (3, bad)]
     assert torch.equal(out_p[good].view(torch.int16), out_c[good].view(torch.int16))
+
+
+def test_config5_shape_paged_equals_contiguous():
+    """The shape bench.py times with --paged: config 5 (256 sequences, GQA
+    64/8, 8K-32K keys per KV head), its cache copied into 32- and then
+    16-position pages at seeded random slots.  The paged call must give the
+    contiguous call's bits on every sequence (the contiguous kernel is checked
+    against the oracle at this shape in tests/test_gpu_attention.py), and the
+    appended rows must land in the tabled slots."""
+    cfg = W.get(5)
+    hint, n_q = cfg.L[1], cfg.n_q
+    d = W.attention_inputs_device(cfg, "cuda")
+    lens = _gpu.to_host(d["lens"]).astype(np.int64)
+    out_c = sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], hint)
+    torch.cuda.synchronize()
+    for page in (32, 16):
+        _case("paged vs contiguous, config 5", B=cfg.B, page=page)
+        need = [(int(L) + n_q + page - 1) // page for L in lens]
+        max_blocks = (hint + n_q + page - 1) // page
+        num_pages = sum(need) + 5
+        perm = torch.from_numpy(np.random.default_rng(page).permutation(num_pages)).to("cuda")
+        table = torch.full((cfg.B, max_blocks), -1, dtype=torch.int32, device="cuda")
+        pages = [torch.full((cfg.Hkv, num_pages, page, cfg.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+                 for _ in range(2)]
+        k = 0
+        for b in range(cfg.B):
+            idx = perm[k : k + need[b]]
+            k += need[b]
+            table[b, : need[b]] = idx.to(torch.int32)
+            L = int(lens[b])
+            nf = L // page
+            for src, dst in ((d["k_cache"], pages[0]), (d["v_cache"], pages[1])):  # rows < L: before any append
+                dst[:, idx[:nf]] = src[b, :, : nf * page].reshape(cfg.Hkv, nf, page, cfg.D)
+                if L % page:
+                    dst[:, idx[nf], : L % page] = src[b, :, nf * page : L]
+        out_p = sv.spec_verify_attention_paged(d["q"], d["k_new"], d["v_new"], pages[0], pages[1], table, d["lens"],
+                                               hint)
+        torch.cuda.synchronize()
+        same = (out_p.view(torch.int16) == out_c.view(torch.int16)).flatten(1).all(dim=1)
+        print("sequences identical", int(same.sum()), "of", cfg.B, flush=True)
+        assert bool(same.all()), torch.nonzero(~same).flatten()[:10].tolist()
+        for b in (0, 1, int(np.argmax(lens)), cfg.B - 1):
+            L = int(lens[b])
+            for t in range(n_q):
+                slot = int(table[b, (L + t) // page])
+                assert torch.equal(pages[0][:, slot, (L + t) % page], d["k_cache"][b, :, L + t])
+                assert torch.equal(pages[1][:, slot, (L + t) % page], d["v_cache"][b, :, L + t])
+        del pages, table, out_p
+        torch.cuda.empty_cache()
