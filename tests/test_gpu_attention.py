@@ -7,6 +7,8 @@ a 32K-key cache fails); the appended cache rows must equal k_new / v_new bit
 for bit and no other cache row may change.  Every case prints its name first.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -119,15 +121,19 @@ def _rows_before(d, seqs):
     return out
 
 
-def test_config5_full_size_sampled():
-    cfg = W.get(5)
-    _case("config5", B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, max_T=cfg.max_T)
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_config5_full_size_sampled(dtype):
+    """Config 5's shape as bench.py times it, with its bf16 cache and with an
+    fp16 cache (as with --kv f16): 18 (bf16) or 10 (fp16) sequences, the
+    shortest and the longest among them, compared one by one."""
+    cfg = dataclasses.replace(W.get(5), dtype=dtype)
+    _case("config5", dtype=dtype, B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, D=cfg.D, max_T=cfg.max_T)
     d = W.attention_inputs_device(cfg, "cuda")
-    seqs = _sample_long(_gpu.to_host(d["lens"]), 18, 5)
+    seqs = _sample_long(_gpu.to_host(d["lens"]), 18 if dtype == "bf16" else 10, 5)
     before = _rows_before(d, seqs)
     out = sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], cfg.L[1])
     torch.cuda.synchronize()
-    _check_one_by_one(d, out, seqs, "bf16", before)
+    _check_one_by_one(d, out, seqs, dtype, before)
     del d
     torch.cuda.empty_cache()
 
