@@ -48,15 +48,21 @@
 namespace specv {
 
 constexpr int kLaneBytes = 64;     // bytes of a row per lane per segment
-constexpr int kSegsPerWave = 2;    // segments a statistics wave loads at once
-constexpr int kWavesPerBlock = 4;  // waves of a statistics workgroup
 // The sampler's statistics pass over a small batch (at most kStatsSmallSegs
 // row segments in all) runs one segment per wave in 4-wave workgroups, so the
-// launch ends in finer pieces; a larger batch runs two segments per wave in
-// 8-wave workgroups (measured: about 3% off the call at B = 32 over 151,936
-// tokens, about 1% at B = 256 over 128,256).
+// launch ends in finer pieces; a larger batch runs two segments per wave (all
+// loads issued before the arithmetic) in 8-wave workgroups (measured against
+// two per wave in 4-wave workgroups for both: about 3% off the call at B = 32
+// over 151,936 tokens, about 1% at B = 256 over 128,256).
 constexpr long kStatsSmallSegs = 65536;
+constexpr int kStatsSmallWaves = 4;
 constexpr int kStatsLargeWaves = 8;
+constexpr int kStatsLargeSegsPerWave = 2;
+// The greedy pass: one segment per wave in 8-wave workgroups (measured: 91
+// against 94 us with two segments per wave in 4-wave workgroups at B = 256,
+// gamma = 8 over 128,256 tokens; no change at B = 32 over 151,936).
+constexpr int kGreedySegsPerWave = 1;
+constexpr int kGreedyWaves = 8;
 constexpr int kResidPerCU = 2;     // residual workgroups per CU to aim for
 
 struct RowPart {  // one wave's segment of one row
@@ -940,9 +946,9 @@ static hipError_t rs_launch(const RsPlan& pl, const void* tgt, const void* drf, 
   RowPart* part1 = reinterpret_cast<RowPart*>(ws + pl.off_part1);
   uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + pl.off_cnt);
   hipError_t e = (long)B * R * pl.nseg <= kStatsSmallSegs
-                     ? rs_stats_launch<T, VEC, NIT, 1>(pl, tgt, drf, B, G, V, c32, part1, cnt, kWavesPerBlock, stream)
-                     : rs_stats_launch<T, VEC, NIT, kSegsPerWave>(pl, tgt, drf, B, G, V, c32, part1, cnt,
-                                                                 kStatsLargeWaves, stream);
+                     ? rs_stats_launch<T, VEC, NIT, 1>(pl, tgt, drf, B, G, V, c32, part1, cnt, kStatsSmallWaves, stream)
+                     : rs_stats_launch<T, VEC, NIT, kStatsLargeSegsPerWave>(pl, tgt, drf, B, G, V, c32, part1, cnt,
+                                                                           kStatsLargeWaves, stream);
   if (e != hipSuccess) return e;
   double2* segsum = reinterpret_cast<double2*>(ws + pl.off_seg);
   // About two residual workgroups per CU, at least two segments per wave.
@@ -983,9 +989,9 @@ template <typename T, int VEC, int NIT>
 static hipError_t gs_launch(const RsPlan& pl, const void* tgt, const int32_t* x, int B, int G, int V, char* ws,
                             int32_t* n_out, int32_t* tok_out, float* p_out, float* q_out, hipStream_t stream) {
   uint64_t* part = reinterpret_cast<uint64_t*>(ws + pl.off_part1);
-  constexpr int SPW = kSegsPerWave;
+  constexpr int SPW = kGreedySegsPerWave;
   const int waves_row = (pl.nseg + SPW - 1) / SPW;
-  const int wpb = std::min(kWavesPerBlock, waves_row);
+  const int wpb = std::min(kGreedyWaves, waves_row);
   hipLaunchKernelGGL((gs_stats<T, VEC, NIT, SPW>), dim3((unsigned)((long)B * (G + 1)), (unsigned)((waves_row + wpb - 1) / wpb)),
                      dim3(kWave * wpb), 0, stream, (const T*)tgt, V, pl.nseg, part);
   hipError_t e = hipGetLastError();
@@ -1043,8 +1049,9 @@ extern "C" spec_status_t spec_reject_sample(const void* target_logits, const voi
   {
     const int nseg1 = rs_plan(B, gamma, V, dtype == SPEC_BF16 ? 2 : 4, 1).nseg;
     if (nseg1 > kMaxSeg) return SPEC_ERR_UNSUPPORTED;
-    // the statistics grid (one workgroup per chunk of every row) must fit in int
-    const long long chunk = (long long)kWavesPerBlock * kSegsPerWave;
+    // the statistics grid (one workgroup per chunk of every row) must fit in
+    // int: a grid of over kStatsSmallSegs segments has chunks of this size
+    const long long chunk = (long long)kStatsLargeWaves * kStatsLargeSegsPerWave;
     if ((long long)B * (2 * gamma + 1) * ((nseg1 + chunk - 1) / chunk) > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
   }
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return SPEC_ERR_ARG;
