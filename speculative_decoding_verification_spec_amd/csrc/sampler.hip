@@ -51,12 +51,12 @@ constexpr int kLaneBytes = 64;     // bytes of a row per lane per segment
 // The sampler's statistics pass over a small batch (at most kStatsSmallSegs
 // row segments in all) runs one segment per wave in 4-wave workgroups, so the
 // launch ends in finer pieces; a larger batch runs two segments per wave (all
-// loads issued before the arithmetic) in 8-wave workgroups (measured against
+// loads issued before the arithmetic) in 16-wave workgroups (measured against
 // two per wave in 4-wave workgroups for both: about 3% off the call at B = 32
-// over 151,936 tokens, about 1% at B = 256 over 128,256).
+// over 151,936 tokens, about 2% at B = 256 over 128,256).
 constexpr long kStatsSmallSegs = 65536;
 constexpr int kStatsSmallWaves = 4;
-constexpr int kStatsLargeWaves = 8;
+constexpr int kStatsLargeWaves = 16;
 constexpr int kStatsLargeSegsPerWave = 2;
 // The greedy pass: one segment per wave in 8-wave workgroups (measured: 91
 // against 94 us with two segments per wave in 4-wave workgroups at B = 256,
