@@ -671,8 +671,8 @@ __global__ __launch_bounds__(kResidWaves * kWave) void rs_resid(
 // largest value, a NaN counting as largest.  Only the gamma+1 target rows are
 // read.
 //
-//   gs_stats  wave per two segments of a target row: the segment's argmax as
-//             one 64-bit key (ordered value key, then inverted index).
+//   gs_stats  wave per segment of a target row: the segment's argmax as one
+//             64-bit key (ordered value key, then inverted index).
 //   gs_tail   workgroup per sequence: merges each row's keys, then one wave
 //             makes the decisions and writes the outputs.
 
