@@ -110,6 +110,7 @@ def _row_cases(V, rng):
         r = base.copy(); r[[2, V - 3]] = np.inf; rows.append(r)          # two +inf
         r = base.copy(); r[[6, V - 2]] = np.float32(3.3895314e38); rows.append(r)  # largest finite bf16
         r = -np.abs(base) - 1.0; r[V // 3] = np.float32(1e-40); rows.append(r)    # subnormal maximum
+        r = -np.abs(base) - 1.0; r[5] = 0.0; r[V - 3] = np.float32(1e-40); rows.append(r)  # above an earlier +0
     return rows
 
 
