@@ -1045,7 +1045,13 @@ constexpr int I8W_STAGES = 3;
 // apart and would make every LDS access wait for every copy in flight.  The
 // waits for the copies are explicit (wait_vmcnt), and the memory clobber keeps
 // LDS accesses on their side of each copy.  M0 takes the LDS address; one
-// wait state separates the write of M0 from the copy that reads it.
+// wait state separates the write of M0 from the copy that reads it.  M0 is a
+// reserved register, so the compiler ignores it in the clobber list (it warns)
+// and assumes M0 unchanged across the statement: nothing here may rely on a
+// value it keeps in M0.  The int8 kernels that use this copy have no other M0
+// user (their generated code writes M0 only right before these copies); a
+// kernel that added one (an LDS-direct builtin, indexed register access) would
+// have to keep it away from these statements.
 __device__ __forceinline__ void lds_copy16(const void* src, uint32_t lds) {
   __asm__ volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds)
                    : "memory", "m0");
