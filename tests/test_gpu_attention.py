@@ -191,6 +191,8 @@ def test_f16_outside_its_support_is_refused():
         ("f16", 3, 8, 2, 5, 128, [0, 31, 33]),   # the fp16 cache: empty, block edges
         ("f16", 2, 4, 4, 1, 64, [1, 1000]),      # fp16, n_q = 1, MHA, D = 64
         ("f16", 4, 32, 8, 5, 128, [1024, 4096, 2000, 3001]),  # fp16 at config 4's head layout and lengths
+        ("bf16", 2, 16, 1, 16, 128, [100, 300]),  # n_q = 16, 256 rows per KV head: the largest group
+        ("f32", 1, 16, 1, 16, 64, [50]),          # the same for fp32
     ],
 )
 def test_shapes_and_edges(dtype, B, Hq, Hkv, n_q, D, lens):
@@ -208,6 +210,7 @@ def test_shapes_and_edges(dtype, B, Hq, Hkv, n_q, D, lens):
     [
         (1, 8, 1, 5, 128, 5000, 5000),    # one slab cut into hundreds of pieces
         (300, 4, 4, 3, 128, 0, 3),        # many slabs of one or two blocks
+        (1024, 2, 1, 2, 64, 0, 40),       # B = 1024: the largest batch of the stream scheme
         (1100, 2, 1, 2, 64, 0, 70),       # B > 1024: the fixed-split scheme
     ],
 )
