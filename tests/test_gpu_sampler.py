@@ -145,7 +145,9 @@ def test_config5_full_size_sampled(T):
 @pytest.mark.parametrize(
     "V,gamma,dtype,B",
     [(1, 1, "f32", 5), (7, 3, "f32", 33), (1003, 5, "bf16", 17), (4099, 2, "f32", 9),
-     (40000, 31, "bf16", 3), (96, 4, "bf16", 70)],
+     (40000, 31, "bf16", 3), (96, 4, "bf16", 70),
+     (1048576, 3, "bf16", 4),   # 512 segments a row
+     (4099, 8, "f32", 2000)],   # one element per load, over 65,536 row segments: the large-batch launch shape
 )
 def test_ragged_shapes(V, gamma, dtype, B):
     _case("ragged", V=V, gamma=gamma, dtype=dtype, B=B)
