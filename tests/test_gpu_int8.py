@@ -71,6 +71,8 @@ def test_config4_int8():
         (300, 4, 4, 3, 128, None),            # many one- or two-block slabs
         (2, 16, 2, 8, 64, [100, 700]),        # 64 rows per KV head (4 tiles), D = 64
         (2, 8, 1, 16, 128, [40, 300]),        # 128 rows per KV head (8 tiles)
+        (1, 16, 1, 16, 128, [300]),           # 256 rows per KV head: two row groups of 8 tiles
+        (2, 16, 1, 16, 64, [9, 200]),         # the same at D = 64
     ],
 )
 def test_shapes(B, Hq, Hkv, n_q, D, lens):
