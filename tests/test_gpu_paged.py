@@ -103,10 +103,15 @@ def test_config4_paged(page):
         (2, 16, 2, 9, 128, [257, 2000], 32),      # 72 rows per KV head (5 tiles)
         (2, 4, 4, 1, 64, [1, 1000], 16),          # n_q = 1, D = 64
         (1, 8, 1, 5, 128, [3000], 32),            # one sequence over many workgroups
+        (2, 16, 1, 16, 128, [100, 300], 16),      # 256 rows per KV head: row groups
+        (2, 32, 1, 7, 64, [70, 5], 32),           # MQA at D = 64, 224 rows
+        (300, 4, 4, 3, 128, None, 16),            # many one- or two-block slabs
     ],
 )
 def test_shapes(B, Hq, Hkv, n_q, D, lens, page):
     _case("paged shape", B=B, Hq=Hq, Hkv=Hkv, n_q=n_q, D=D, lens=lens, page=page)
+    if lens is None:
+        lens = np.random.default_rng(B).integers(0, 40, B).astype(np.int32)
     max_T = max(lens) + n_q + 7
     cfg = W.Config(96, "paged", B=B, gamma=n_q - 1, V=1, dtype="bf16", Hq=Hq, Hkv=Hkv, D=D, L=(0, max(lens)),
                    max_T=max_T)
