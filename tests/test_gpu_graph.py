@@ -73,6 +73,49 @@ def test_verify_step_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_sampler_large_batch_graph_replays_match_eager(T):
+    """The sampler at a batch above 65,536 row segments (its large-batch launch
+    shape) and greedy verification, captured and replayed."""
+    B = 100
+    _case("sampler-graph", config=4, B=B, T=T)
+    dev = torch.device("cuda:0")
+    cfg = W.get(4)
+    s = W.sampler_inputs(cfg, B=B, temperature=1.0)
+    u = {k: to_dev(v, dev) for k, v in s.items() if k != "temperature"}
+    if T == 0.0:
+        u["draft_tokens"] = torch.argmax(u["draft_logits"].float(), dim=-1).to(torch.int32)
+    n = torch.empty(B, dtype=torch.int32, device=dev)
+    tok = torch.empty((B, cfg.gamma + 1), dtype=torch.int32, device=dev)
+    p = torch.empty((B, cfg.gamma), dtype=torch.float32, device=dev)
+    q = torch.empty((B, cfg.gamma), dtype=torch.float32, device=dev)
+    ws = sv.Workspace()
+
+    def call():
+        sv.spec_reject_sample(u["target_logits"], None if T == 0.0 else u["draft_logits"], u["draft_tokens"],
+                              None if T == 0.0 else u["uniforms"], T, n_accepted=n, out_tokens=tok, p_draft=p,
+                              q_draft=q, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    want = (n.clone(), tok.clone(), p.clone(), q.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(3):
+        n.fill_(-9)
+        tok.fill_(-7)
+        p.zero_()
+        q.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for w_, g_ in zip(want, (n, tok, p, q)):
+            assert torch.equal(w_.view(torch.int32), g_.view(torch.int32)), f"replay {rep} differs from the eager call"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+
+
 def test_speculative_round_graph_replays_match_eager():
     _case("round-graph", B=4, gamma=4)
     dev = torch.device("cuda:0")
