@@ -88,6 +88,26 @@ def test_noalloc_equals_the_workspace_call_twice_in_a_row(T):
             print("stats", _gpu.compare_sampler(orc, got[0], got[1], got[2], got[3]), flush=True)
 
 
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_noalloc_at_config5_then_config4(T):
+    """Config 5 (256 sequences over 128,256 tokens: the statistics pass's
+    large-batch launch shape, 4.6 MiB of scratch), then config 4 over the
+    scratch it left: bit for bit the workspace call's outputs (which the
+    sampler tests check against the oracle at both shapes)."""
+    for cid in (5, 4):
+        cfg = W.get(cid)
+        print(f"\n[case] noalloc T={T} config{cid} B={cfg.B} gamma={cfg.gamma} V={cfg.V}", flush=True)
+        d = W.sampler_inputs_device(cfg, "cuda", temperature=1.0 if T == 0 else T)
+        d = {k: d[k] for k in ("target_logits", "draft_logits", "draft_tokens", "uniforms")}
+        if T == 0:
+            d["draft_tokens"] = torch.argmax(d["draft_logits"].float(), dim=-1).to(torch.int32)
+        want = _run(d, T, noalloc=False)
+        got = _run(d, T, noalloc=True)
+        _same_bits(got, want)
+        del d
+        torch.cuda.empty_cache()
+
+
 def test_noalloc_refuses_more_than_its_scratch():
     print("\n[case] noalloc size limit", flush=True)
     L = sv.load()
