@@ -238,3 +238,12 @@ def test_status_codes():
     with pytest.raises(sv.SpecError) as e:
         sv.spec_verify_attention_int8(q, kn, kn, kc, ks, kc.clone(), ks.clone(), lens, 60)  # 60 + 5 > 64
     assert e.value.status == 2
+    B = 1025  # above the stream scheme's 1024 sequences
+    qb = torch.zeros((B, 4, 5, 128), dtype=torch.bfloat16, device=dev)
+    knb = torch.zeros((B, 2, 5, 128), dtype=torch.bfloat16, device=dev)
+    kcb = torch.zeros((B, 2, 64, 128), dtype=torch.int8, device=dev)
+    ksb = torch.zeros((B, 2, 64), dtype=torch.float16, device=dev)
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_verify_attention_int8(qb, knb, knb, kcb, ksb, kcb.clone(), ksb.clone(),
+                                      torch.zeros(B, dtype=torch.int32, device=dev), 10)
+    assert e.value.status == 3

@@ -154,6 +154,14 @@ def test_status_codes():
     with pytest.raises(sv.SpecError) as e:
         sv.spec_verify_attention_paged(q, kn, kn, p8, p8.clone(), table, lens, 10)  # page size 8
     assert e.value.status == 3
+    B = 1025  # above the stream scheme's 1024 sequences
+    with pytest.raises(sv.SpecError) as e:
+        sv.spec_verify_attention_paged(torch.zeros((B, 4, 5, 128), dtype=torch.bfloat16, device=dev),
+                                       torch.zeros((B, 2, 5, 128), dtype=torch.bfloat16, device=dev),
+                                       torch.zeros((B, 2, 5, 128), dtype=torch.bfloat16, device=dev), pages,
+                                       pages.clone(), torch.zeros((B, 4), dtype=torch.int32, device=dev),
+                                       torch.zeros(B, dtype=torch.int32, device=dev), 10)
+    assert e.value.status == 3
 
 
 def _device_paged(dtype, kind):
