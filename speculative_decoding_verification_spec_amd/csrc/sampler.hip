@@ -40,6 +40,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 
 #include "spec_common.h"
@@ -275,34 +276,44 @@ __global__ __launch_bounds__(1024) void rs_stats(const T* __restrict__ tgt, cons
   const T* row = (r <= G) ? tgt + ((size_t)b * (G + 1) + r) * V : drf + ((size_t)b * G + (r - G - 1)) * V;
   RowPart* out = part + (size_t)rowid * nseg;
   // Strided, fully coalesced loads: iteration it of a segment covers 64*VEC
-  // consecutive elements.  Order does not matter for a max and a sum.
-  Raw raw[SPW][NIT];
-  bool ok[SPW][NIT];
+  // consecutive elements.  Order does not matter for a max and a sum.  FULL:
+  // every element of the wave's segments lies in the row (all but a row's
+  // last segment), so no element needs a bounds test or -inf padding; the
+  // arithmetic is the same either way.
+  auto body = [&](auto FULL) {
+    constexpr bool kFull = decltype(FULL)::value;
+    Raw raw[SPW][NIT];
+    bool ok[SPW][NIT];
 #pragma unroll
-  for (int k = 0; k < SPW; ++k)
+    for (int k = 0; k < SPW; ++k)
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int idx = (seg0 + k) * SEG + (it * kWave + lane) * VEC;
-      ok[k][it] = idx < V;
-      if (ok[k][it]) raw[k][it] = stream_load(reinterpret_cast<const Raw*>(row + idx));
-    }
-#pragma unroll
-  for (int k = 0; k < SPW; ++k) {
-    const int seg = seg0 + k;
-    if (seg >= nseg) break;
-    float v[NIT][VEC];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      if (ok[k][it]) {
-        raw_to_f32<T, VEC>(raw[k][it], v[it]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) v[it][e] = neg_inf_f();
+      for (int it = 0; it < NIT; ++it) {
+        const int idx = (seg0 + k) * SEG + (it * kWave + lane) * VEC;
+        ok[k][it] = kFull || idx < V;
+        if (ok[k][it]) raw[k][it] = stream_load(reinterpret_cast<const Raw*>(row + idx));
       }
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) {
+      const int seg = seg0 + k;
+      if (!kFull && seg >= nseg) break;
+      float v[NIT][VEC];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        if (ok[k][it]) {
+          raw_to_f32<T, VEC>(raw[k][it], v[it]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) v[it][e] = neg_inf_f();
+        }
+      }
+      const RowPart rp = segment_stats<NIT, VEC>(v, c32);
+      if (lane == 0) out[seg] = rp;
     }
-    const RowPart rp = segment_stats<NIT, VEC>(v, c32);
-    if (lane == 0) out[seg] = rp;
-  }
+  };
+  if ((long)(seg0 + SPW) * SEG <= V)  // uniform per wave
+    body(std::true_type{});
+  else
+    body(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
