@@ -753,95 +753,104 @@ __global__ __launch_bounds__(1024) void gs_stats(const T* __restrict__ tgt, int 
   if (seg0 >= nseg) return;  // uniform per wave
   const T* row = tgt + (size_t)blockIdx.x * V;
   uint64_t* out = part + (size_t)blockIdx.x * nseg;
-  Raw raw[SPW][NIT];
-  bool ok[SPW][NIT];
+  // FULL: every element of the wave's segments lies in the row (all but a
+  // row's last segment), so no element needs a bounds test.
+  auto body = [&](auto FULL) {
+    constexpr bool kFull = decltype(FULL)::value;
+    Raw raw[SPW][NIT];
+    bool ok[SPW][NIT];
 #pragma unroll
-  for (int k = 0; k < SPW; ++k)
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int idx = (seg0 + k) * SEG + (it * kWave + lane) * VEC;
-      ok[k][it] = idx < V;
-      if (ok[k][it]) raw[k][it] = stream_load(reinterpret_cast<const Raw*>(row + idx));
-    }
-#pragma unroll
-  for (int k = 0; k < SPW; ++k) {
-    const int seg = seg0 + k;
-    if (seg >= nseg) break;
-    if constexpr (sizeof(T) == 2 && VEC % 2 == 0) {
-      constexpr int WPG = VEC / 2;  // words per group
-      u16x2 gmax[NIT];
-      u16x2 kmax = {0, 0}, kmin = {0xffff, 0xffff};
+    for (int k = 0; k < SPW; ++k)
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        gmax[it] = (u16x2){0, 0};
-        if (!ok[k][it]) continue;
-#pragma unroll
-        for (int j = 0; j < WPG; ++j) {
-          const u16x2 key = bf16_pair_keys(raw_word(raw[k][it], j));
-          gmax[it] = __builtin_elementwise_max(gmax[it], key);
-          kmin = __builtin_elementwise_min(kmin, key);
-        }
-        kmax = __builtin_elementwise_max(kmax, gmax[it]);
+        const int idx = (seg0 + k) * SEG + (it * kWave + lane) * VEC;
+        ok[k][it] = kFull || idx < V;
+        if (ok[k][it]) raw[k][it] = stream_load(reinterpret_cast<const Raw*>(row + idx));
       }
-      // A lane without elements keeps 0 as its largest key, below every
-      // element's (NaN aside, and a NaN sends the segment elementwise).
-      const int lmax = max((int)kmax.x, (int)kmax.y);
-      const int lmin = min((int)kmin.x, (int)kmin.y);
-      const int wmax = wave_max(lmax);
-      const bool elementwise = __ballot(lmax > kKeyPosInf || lmin < kKeyNegInf) != 0ull || wmax == kKeyNegZero ||
-                               wmax == kKeyPosZero;
-      if (!elementwise) {  // uniform over the wave
-        int first = 0x7fffffff;
-        if (lmax == wmax) {
-          bool found = false;
 #pragma unroll
-          for (int it = 0; it < NIT; ++it) {
-            if (found || !ok[k][it] || (gmax[it].x != wmax && gmax[it].y != wmax)) continue;
-            const int idx0 = seg * SEG + (it * kWave + lane) * VEC;
+    for (int k = 0; k < SPW; ++k) {
+      const int seg = seg0 + k;
+      if (!kFull && seg >= nseg) break;
+      if constexpr (sizeof(T) == 2 && VEC % 2 == 0) {
+        constexpr int WPG = VEC / 2;  // words per group
+        u16x2 gmax[NIT];
+        u16x2 kmax = {0, 0}, kmin = {0xffff, 0xffff};
 #pragma unroll
-            for (int j = 0; j < WPG; ++j) {
-              const u16x2 key = bf16_pair_keys(raw_word(raw[k][it], j));
-              if (!found && key.x == wmax) {
-                first = idx0 + 2 * j;
-                found = true;
-              }
-              if (!found && key.y == wmax) {
-                first = idx0 + 2 * j + 1;
-                found = true;
+        for (int it = 0; it < NIT; ++it) {
+          gmax[it] = (u16x2){0, 0};
+          if (!ok[k][it]) continue;
+#pragma unroll
+          for (int j = 0; j < WPG; ++j) {
+            const u16x2 key = bf16_pair_keys(raw_word(raw[k][it], j));
+            gmax[it] = __builtin_elementwise_max(gmax[it], key);
+            kmin = __builtin_elementwise_min(kmin, key);
+          }
+          kmax = __builtin_elementwise_max(kmax, gmax[it]);
+        }
+        // A lane without elements keeps 0 as its largest key, below every
+        // element's (NaN aside, and a NaN sends the segment elementwise).
+        const int lmax = max((int)kmax.x, (int)kmax.y);
+        const int lmin = min((int)kmin.x, (int)kmin.y);
+        const int wmax = wave_max(lmax);
+        const bool elementwise = __ballot(lmax > kKeyPosInf || lmin < kKeyNegInf) != 0ull || wmax == kKeyNegZero ||
+                                 wmax == kKeyPosZero;
+        if (!elementwise) {  // uniform over the wave
+          int first = 0x7fffffff;
+          if (lmax == wmax) {
+            bool found = false;
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+              if (found || !ok[k][it] || (gmax[it].x != wmax && gmax[it].y != wmax)) continue;
+              const int idx0 = seg * SEG + (it * kWave + lane) * VEC;
+#pragma unroll
+              for (int j = 0; j < WPG; ++j) {
+                const u16x2 key = bf16_pair_keys(raw_word(raw[k][it], j));
+                if (!found && key.x == wmax) {
+                  first = idx0 + 2 * j;
+                  found = true;
+                }
+                if (!found && key.y == wmax) {
+                  first = idx0 + 2 * j + 1;
+                  found = true;
+                }
               }
             }
           }
-        }
-        first = wave_min(first);
-        // The value with key wmax: a positive one's bits are the key without
-        // its top bit, a negative one's the key inverted.
-        const uint32_t bits = wmax >= kKeyPosZero ? (uint32_t)(wmax ^ 0x8000) : (uint32_t)(~wmax & 0xffff);
-        if (lane == 0) out[seg] = arg_word(order_key(bf16_to_f32((uint16_t)bits)), first);
-        continue;
-      }
-    }
-    // A lane sees its elements in increasing index order, so a strict '>'
-    // keeps the first of equal keys.  Every value's key exceeds 0.
-    uint32_t best = 0u;
-    int bidx = 0;
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      if (!ok[k][it]) continue;
-      float v[VEC];
-      raw_to_f32<T, VEC>(raw[k][it], v);
-      const int idx0 = seg * SEG + (it * kWave + lane) * VEC;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const uint32_t key = order_key(v[e]);
-        if (key > best) {
-          best = key;
-          bidx = idx0 + e;
+          first = wave_min(first);
+          // The value with key wmax: a positive one's bits are the key without
+          // its top bit, a negative one's the key inverted.
+          const uint32_t bits = wmax >= kKeyPosZero ? (uint32_t)(wmax ^ 0x8000) : (uint32_t)(~wmax & 0xffff);
+          if (lane == 0) out[seg] = arg_word(order_key(bf16_to_f32((uint16_t)bits)), first);
+          continue;
         }
       }
+      // A lane sees its elements in increasing index order, so a strict '>'
+      // keeps the first of equal keys.  Every value's key exceeds 0.
+      uint32_t best = 0u;
+      int bidx = 0;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        if (!ok[k][it]) continue;
+        float v[VEC];
+        raw_to_f32<T, VEC>(raw[k][it], v);
+        const int idx0 = seg * SEG + (it * kWave + lane) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const uint32_t key = order_key(v[e]);
+          if (key > best) {
+            best = key;
+            bidx = idx0 + e;
+          }
+        }
+      }
+      const uint64_t w = wave_max_u64(best == 0u ? 0ull : arg_word(best, bidx));
+      if (lane == 0) out[seg] = w;
     }
-    const uint64_t w = wave_max_u64(best == 0u ? 0ull : arg_word(best, bidx));
-    if (lane == 0) out[seg] = w;
-  }
+  };
+  if ((long)(seg0 + SPW) * SEG <= V)  // uniform per wave
+    body(std::true_type{});
+  else
+    body(std::false_type{});
 }
 
 __global__ __launch_bounds__(1024) void gs_tail(const int32_t* __restrict__ xtok, int G, int V, int nseg,
