@@ -323,6 +323,18 @@ __global__ __launch_bounds__(1024) void rs_stats(const T* __restrict__ tgt, cons
 
 constexpr int kMaxSeg = 1024;  // segments of one row held in LDS
 
+// p_n of one element, and its residual weight max(0, p - q), each with the
+// roundings written out (one product for p, one fma for p - q) so that the
+// residual pass's segment sums and the draw's re-scan round alike whatever
+// the compiler would contract.
+__device__ __forceinline__ float residual_p(float zt, float Mt, float c32, float inv_st) {
+#pragma clang fp contract(off)
+  return exp2_fast((zt - Mt) * c32) * inv_st;
+}
+__device__ __forceinline__ float residual_w(float p, float zd, float Md, float c32, float inv_sd) {
+  return fmaxf(fmaf(-exp2_fast((zd - Md) * c32), inv_sd, p), 0.f);
+}
+
 // Weights of the E = VEC*NIT contiguous elements starting at idx0 (used by
 // the final re-scan, in index order).  resid: max(0, p - q); else p.
 template <typename T, int VEC, int NIT>
@@ -338,8 +350,8 @@ __device__ __forceinline__ void lane_weights(const T* __restrict__ rt, const T* 
       if (resid) load_vec<T, VEC>(rd + idx, zd);
 #pragma unroll
       for (int k = 0; k < VEC; ++k) {
-        const float p = exp2_fast((zt[k] - Mt) * c32) * inv_st;
-        w[it * VEC + k] = resid ? fmaxf(p - exp2_fast((zd[k] - Md) * c32) * inv_sd, 0.f) : p;
+        const float p = residual_p(zt[k], Mt, c32, inv_st);
+        w[it * VEC + k] = resid ? residual_w(p, zd[k], Md, c32, inv_sd) : p;
       }
     } else {
 #pragma unroll
@@ -615,48 +627,59 @@ __global__ __launch_bounds__(kResidWaves * kWave) void rs_resid(
       __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(rd), 0, (int)((long)V * sizeof(T)), 0x00020000);
 
   // wave w takes segments [s0, s1) of this workgroup's spw * kResidWaves,
-  // two at a time
+  // two at a time; the decided row's case (a residual, or the bonus row
+  // alone) is fixed outside the element loops
   const int s0 = (blockIdx.y * kResidWaves + wave) * spw;
   const int s1 = min(s0 + spw, nseg);
-  for (int seg0 = s0; seg0 < s1; seg0 += 2) {  // uniform per wave
-    Raw at[2][NIT], ad[2][NIT];
+  auto sums = [&](auto RESID) {
+    constexpr bool kResid = decltype(RESID)::value;
+    for (int seg0 = s0; seg0 < s1; seg0 += 2) {  // uniform per wave
+      Raw at[2][NIT], ad[2][NIT];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+      for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        // elements past V read 0 from the buffer and are masked out below
-        const uint32_t off = (uint32_t)((seg0 + k) * SEG + (it * kWave + lane) * VEC) * (uint32_t)sizeof(T);
-        at[k][it] = buf_raw<Raw>(rsrc_t, off);
-        if (resid) ad[k][it] = buf_raw<Raw>(rsrc_d, off);
-      }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int seg = seg0 + k;
-      if (seg >= s1) break;
-      double lw = 0.0, lp = 0.0;
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int idx = seg * SEG + (it * kWave + lane) * VEC;
-        if (idx < V) {
-          float zt[VEC], zd[VEC];
-          raw_to_f32<T, VEC>(at[k][it], zt);
-          if (resid) raw_to_f32<T, VEC>(ad[k][it], zd);
-          float sw = 0.f, sp = 0.f;
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) {
-            const float p = exp2_fast((zt[e] - Mt) * c32) * inv_st;
-            sw += resid ? fmaxf(p - exp2_fast((zd[e] - Md) * c32) * inv_sd, 0.f) : p;
-            sp += p;
-          }
-          lw += (double)sw;
-          lp += (double)sp;
+        for (int it = 0; it < NIT; ++it) {
+          // elements past V read 0 from the buffer and are masked out below
+          const uint32_t off = (uint32_t)((seg0 + k) * SEG + (it * kWave + lane) * VEC) * (uint32_t)sizeof(T);
+          at[k][it] = buf_raw<Raw>(rsrc_t, off);
+          if constexpr (kResid) ad[k][it] = buf_raw<Raw>(rsrc_d, off);
         }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int seg = seg0 + k;
+        if (seg >= s1) break;
+        double lw = 0.0, lp = 0.0;
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+          const int idx = seg * SEG + (it * kWave + lane) * VEC;
+          if (idx < V) {
+            float zt[VEC], zd[VEC];
+            raw_to_f32<T, VEC>(at[k][it], zt);
+            if constexpr (kResid) raw_to_f32<T, VEC>(ad[k][it], zd);
+            float sw = 0.f, sp = 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+              const float p = residual_p(zt[e], Mt, c32, inv_st);
+              if constexpr (kResid)
+                sw += residual_w(p, zd[e], Md, c32, inv_sd);
+              else
+                sw += p;
+              sp += p;
+            }
+            lw += (double)sw;
+            lp += (double)sp;
+          }
+        }
+        lw = wave_sum(lw);
+        lp = wave_sum(lp);
+        if (lane == 0) store_segsum(segsum + (size_t)b * nseg + seg, lw, lp);
       }
-      lw = wave_sum(lw);
-      lp = wave_sum(lp);
-      if (lane == 0) store_segsum(segsum + (size_t)b * nseg + seg, lw, lp);
     }
-  }
+  };
+  if (resid)
+    sums(std::true_type{});
+  else
+    sums(std::false_type{});
   // The last of b's workgroups to finish draws: its count follows every
   // other workgroup's completed segment stores (device-scope, write-through).
   wait_vm_all();
