@@ -115,7 +115,8 @@ def _row_cases(V, rng):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("V,gamma", [(1, 1), (7, 3), (1003, 4), (4098, 3), (4099, 2), (4100, 2), (40000, 31), (151936, 4)])
+@pytest.mark.parametrize("V,gamma", [(1, 1), (7, 3), (1003, 4), (2048, 2), (4096, 3), (4098, 3), (4099, 2), (4100, 2),
+                                     (40000, 31), (151936, 4)])
 def test_edges(dtype, V, gamma):
     _case("greedy edges", dtype=dtype, V=V, gamma=gamma)
     rng = np.random.default_rng([V, gamma])

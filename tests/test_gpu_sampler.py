@@ -158,6 +158,24 @@ def test_ragged_shapes(V, gamma, dtype, B):
     print("stats", st)
 
 
+@pytest.mark.parametrize(
+    "V,B,gamma",
+    [(65536, 130, 8),   # 32 whole segments of 2,048 bf16 logits, large-batch shape: every wave's segments are whole
+     (67584, 120, 8),   # 33 whole segments: the last wave has one whole segment and none after it
+     (67585, 120, 8),   # one element into a 34th segment
+     (65536, 8, 4)],    # whole segments in the small-batch shape (one segment per wave)
+)
+def test_segment_boundaries(V, B, gamma):
+    _case("segment boundaries", V=V, B=B, gamma=gamma)
+    cfg = W.Config(98, "segments", B=B, gamma=gamma, V=V, dtype="bf16", t_std=2.5, mix=0.9, noise_std=1.0)
+    inp = W.sampler_inputs(cfg, temperature=1.0)
+    n, tok, p, q = _run(inp)
+    seqs = np.sort(np.random.default_rng(V + B).choice(B, size=min(B, 16), replace=False))
+    sub = {k: (v[seqs] if isinstance(v, np.ndarray) else v) for k, v in inp.items()}
+    st = _gpu.compare_sampler(_oracle(sub), n[seqs], tok[seqs], p[seqs], q[seqs])
+    print("stats", st)
+
+
 def test_edge_conventions():
     _case("edges")
     V = 4
