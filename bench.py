@@ -83,6 +83,63 @@ def measured_traffic(cid):
     return None
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence.
+
+    Recording a default event (torch.cuda.Event) also performs a system-scope
+    release: a cache write-back and invalidate that costs the stream a few
+    microseconds per record and is charged to the calls between events.  This
+    event only writes its timestamp once the work before it on the stream is
+    done.  The HIP runtime is the one torch has loaded (found by its path in
+    the process's mappings), so torch's streams are valid handles.  Read it
+    only after torch.cuda.synchronize().
+    """
+
+    _hip = None
+    _DISABLE_SYSTEM_FENCE = 0x20000000
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+
+            with open("/proc/self/maps") as f:
+                paths = sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln and ln.split()[-1].startswith("/")})
+            if len(paths) != 1:
+                raise RuntimeError(f"expected one HIP runtime mapped in this process, found {paths}")
+            hip = ctypes.CDLL(paths[0])
+            vp = ctypes.c_void_p
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [vp, vp]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            hip.hipEventDestroy.argtypes = [vp]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+
+        self._ev = ctypes.c_void_p()
+        if self._lib().hipEventCreateWithFlags(ctypes.byref(self._ev), self._DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self._lib().hipEventRecord(self._ev, stream.cuda_stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        import ctypes
+
+        ms = ctypes.c_float()
+        if self._lib().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self._ev:
+            self._hip.hipEventDestroy(self._ev)
+
+
 def algorithmic(cfg, lens, B, greedy=False, kv="bf16"):
     """Bytes and flops the step must move / compute (every input read once).
 
@@ -534,14 +591,14 @@ def main():
 def time_steps(torch, sv, cfg, T, sets, hint, steps, warmup, kv="bf16", paged=0):
     """Warm up, then time ``steps`` verification steps between two events on
     the launch stream (the step time), then ``steps`` more with per-call
-    events around attention, the sampler and the length reset (the parts; the
-    events themselves cost the stream a few microseconds each, so they stay
-    out of the step time).  Step k uses input set k mod len(sets); lengths are
-    restored before each step (a 1 KB device copy, inside the step time and
-    outside the per-call events)."""
+    timing events (TimingEvent: no system-scope fence) around attention, the
+    sampler and the length reset (the parts; even so each event costs the
+    stream a little, so they stay out of the step time).  Step k uses input
+    set k mod len(sets); lengths are restored before each step (a 1 KB device
+    copy, inside the step time and outside the per-call events)."""
     nsets = len(sets)
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
 
     def step(k, events=None):
         att, smp = sets[k % nsets]
@@ -620,7 +677,7 @@ def sampler_only(torch, sv, cfg, T, dev, steps, warmup):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
     for a, b in ev:
         a.record(stream)
         call()
@@ -642,8 +699,8 @@ def attention_back_to_back(torch, sv, sets, hint, calls, kv="bf16", paged=0):
     """Milliseconds per attention call when ``calls`` calls run back to back
     (input sets alternating) between two events on the launch stream: the
     call's own throughput, without the per-call events of the step loop
-    (each of which costs the stream a few microseconds).  Lengths are left as
-    they are, so every call appends the same rows again."""
+    (each of which costs the stream a little).  Lengths are left as they
+    are, so every call appends the same rows again."""
     stream = torch.cuda.current_stream()
     for att, _ in sets:
         att["lens"].copy_(att["lens_base"])
