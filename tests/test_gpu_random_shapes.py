@@ -1,0 +1,113 @@
+"""GPU parity at seeded random shapes, beside the hand-picked ones.
+
+Valid shapes drawn once from a fixed seed: verify attention (bf16, fp16 and
+fp32 caches; GQA/MQA/MHA groupings; 1-16 verify rows; caches from empty to
+6,000 keys; hints at and above the longest length; rows past each length
+poisoned with NaN), the rejection sampler (fp32 and bf16 logits, V from 1 to
+200,003, gamma 1-31, temperatures 0.3-1.6, sharp to flat distributions) and
+greedy verification.  Each case is checked against the oracle exactly as the
+fixed-shape tests check theirs.  Every case prints its shape first.
+"""
+
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import _gpu
+from tests import test_gpu_attention as TA
+from tests import test_gpu_greedy as TG
+from tests import test_gpu_sampler as TS
+
+pytestmark = pytest.mark.gpu
+
+
+def _attention_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = ["bf16", "f16", "f32"][rng.integers(3)]
+        D = int(rng.choice([64, 128])) if dtype != "f32" else int(rng.choice([24, 32, 64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        n_q = int(rng.integers(1, 17))
+        while G * n_q > 256:
+            n_q //= 2
+        Lmax = int(rng.choice([5, 40, 300, 2000, 6000]))
+        B = int(rng.integers(1, 25))
+        while B * G * Hkv * n_q * max(Lmax, 1) > 3e7 and B > 1:
+            B //= 2
+        lens = rng.integers(0, Lmax + 1, size=B).astype(np.int32)
+        hint = int(lens.max()) + int(rng.choice([0, 0, 7, 100]))
+        max_T = hint + n_q + int(rng.integers(0, 9))
+        out.append(dict(dtype=dtype, B=B, Hq=G * Hkv, Hkv=Hkv, n_q=n_q, D=D, lens=lens, hint=hint, max_T=max_T))
+    return out
+
+
+def _sampler_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = ["f32", "bf16"][rng.integers(2)]
+        V = int(rng.choice([1, 2, 17, 96, 1000, 4097, 32000, 65536, 128256, 151936, 200003]))
+        gamma = int(rng.integers(1, 32))
+        B = int(rng.integers(1, 200))
+        while B * (2 * gamma + 1) * V > 6e7 and B > 1:
+            B //= 2
+        out.append(dict(dtype=dtype, V=V, gamma=gamma, B=B, T=float(rng.choice([0.3, 0.7, 1.0, 1.6])),
+                        t_std=float(rng.choice([1.0, 2.5, 4.0])), mix=float(rng.choice([0.5, 0.9, 1.0])),
+                        noise_std=float(rng.choice([0.3, 1.0]))))
+    return out
+
+
+def _greedy_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        dtype = ["f32", "bf16"][rng.integers(2)]
+        V = int(rng.choice([1, 3, 96, 2048, 4096, 4097, 50000, 131072, 151936]))
+        gamma = int(rng.integers(1, 32))
+        B = int(rng.integers(1, 200))
+        while B * (gamma + 1) * V > 6e7 and B > 1:
+            B //= 2
+        out.append(dict(dtype=dtype, V=V, gamma=gamma, B=B))
+    return out
+
+
+ATT = _attention_cases(40, 2026)
+SMP = _sampler_cases(30, 2027)
+GR = _greedy_cases(20, 2028)
+
+
+@pytest.mark.parametrize("i", range(len(ATT)))
+def test_attention_random_shape(i):
+    c = ATT[i]
+    print(f"\n[case] attention {i} " + " ".join(f"{k}={v}" for k, v in c.items() if k != "lens")
+          + f" lens[:8]={c['lens'][:8].tolist()}", flush=True)
+    cfg = W.Config(90, "random", B=c["B"], gamma=c["n_q"] - 1, V=1, dtype=c["dtype"], Hq=c["Hq"], Hkv=c["Hkv"],
+                   D=c["D"], L=(0, max(int(c["lens"].max()), 1)), max_T=c["max_T"])
+    inp = W.attention_inputs(cfg, B=c["B"], max_T=c["max_T"], lens=c["lens"])
+    out, kc, vc = TA._run_host(inp, hint=c["hint"], poison_tail=True)
+    TA._check(inp, out, kc, vc, c["dtype"])
+
+
+@pytest.mark.parametrize("i", range(len(SMP)))
+def test_sampler_random_shape(i):
+    c = SMP[i]
+    print(f"\n[case] sampler {i} {c}", flush=True)
+    cfg = W.Config(91, "random", B=c["B"], gamma=c["gamma"], V=c["V"], dtype=c["dtype"], t_std=c["t_std"],
+                   mix=c["mix"], noise_std=c["noise_std"])
+    inp = W.sampler_inputs(cfg, temperature=c["T"])
+    n, tok, p, q = TS._run(inp)
+    print("stats", _gpu.compare_sampler(TS._oracle(inp), n, tok, p, q), flush=True)
+
+
+@pytest.mark.parametrize("i", range(len(GR)))
+def test_greedy_random_shape(i):
+    c = GR[i]
+    print(f"\n[case] greedy {i} {c}", flush=True)
+    cfg = W.Config(92, "random", B=c["B"], gamma=c["gamma"], V=c["V"], dtype=c["dtype"], t_std=2.0, mix=0.9,
+                   noise_std=0.5)
+    inp = W.sampler_inputs(cfg)
+    zt = inp["target_logits"]
+    x = TG._greedy_drafts(inp["draft_logits"])
+    TG._check(zt, x, TG._run(zt, x))
