@@ -3,7 +3,8 @@
 Valid shapes drawn once from a fixed seed: verify attention (bf16, fp16 and
 fp32 caches; GQA/MQA/MHA groupings; 1-16 verify rows; caches from empty to
 6,000 keys; hints at and above the longest length; rows past each length
-poisoned with NaN), the rejection sampler (fp32 and bf16 logits, V from 1 to
+poisoned with NaN), the same over 16- and 32-position pages at random slots
+and over the int8 cache, the rejection sampler (fp32 and bf16 logits, V from 1 to
 200,003, gamma 1-31, temperatures 0.3-1.6, sharp to flat distributions) and
 greedy verification.  Each case is checked against the oracle exactly as the
 fixed-shape tests check theirs.  Every case prints its shape first.
@@ -16,6 +17,8 @@ import workloads as W
 from tests import _gpu
 from tests import test_gpu_attention as TA
 from tests import test_gpu_greedy as TG
+from tests import test_gpu_int8 as TI
+from tests import test_gpu_paged as TP
 from tests import test_gpu_sampler as TS
 
 pytestmark = pytest.mark.gpu
@@ -73,7 +76,36 @@ def _greedy_cases(n, seed):
     return out
 
 
+def _cache_cases(n, seed, int8):
+    """bf16 attention shapes for the paged and int8 caches (D 64 or 128)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        n_q = int(rng.integers(1, 17))
+        while G * n_q > 256:
+            n_q //= 2
+        Lmax = int(rng.choice([5, 40, 300, 3000]))
+        B = int(rng.integers(1, 21))
+        while B * G * Hkv * n_q * max(Lmax, 1) > 2e7 and B > 1:
+            B //= 2
+        lens = rng.integers(0, Lmax + 1, size=B).astype(np.int32)
+        hint = int(lens.max()) + int(rng.choice([0, 0, 7, 100]))
+        c = dict(B=B, Hq=G * Hkv, Hkv=Hkv, n_q=n_q, D=D, lens=lens, hint=hint)
+        if int8:
+            c["max_T"] = (hint + n_q + int(rng.integers(0, 9)) + 7) // 8 * 8
+        else:
+            c["page"] = int(rng.choice([16, 32]))
+            c["max_T"] = hint + n_q + int(rng.integers(0, 9))
+        out.append(c)
+    return out
+
+
 ATT = _attention_cases(40, 2026)
+PAGED = _cache_cases(15, 2029, int8=False)
+INT8 = _cache_cases(15, 2030, int8=True)
 SMP = _sampler_cases(30, 2027)
 GR = _greedy_cases(20, 2028)
 
@@ -88,6 +120,30 @@ def test_attention_random_shape(i):
     inp = W.attention_inputs(cfg, B=c["B"], max_T=c["max_T"], lens=c["lens"])
     out, kc, vc = TA._run_host(inp, hint=c["hint"], poison_tail=True)
     TA._check(inp, out, kc, vc, c["dtype"])
+
+
+def _describe(c):
+    return " ".join(f"{k}={v}" for k, v in c.items() if k != "lens") + f" lens[:8]={c['lens'][:8].tolist()}"
+
+
+@pytest.mark.parametrize("i", range(len(PAGED)))
+def test_paged_random_shape(i):
+    c = PAGED[i]
+    print(f"\n[case] paged {i} " + _describe(c), flush=True)
+    cfg = W.Config(93, "random", B=c["B"], gamma=c["n_q"] - 1, V=1, dtype="bf16", Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"],
+                   L=(0, max(int(c["lens"].max()), 1)), max_T=c["max_T"])
+    inp = W.attention_inputs(cfg, B=c["B"], max_T=c["max_T"], lens=c["lens"])
+    TP._check(inp, c["page"], TP._run(inp, c["page"], rng=1000 + i, hint=c["hint"]))
+
+
+@pytest.mark.parametrize("i", range(len(INT8)))
+def test_int8_random_shape(i):
+    c = INT8[i]
+    print(f"\n[case] int8 {i} " + _describe(c), flush=True)
+    cfg = W.Config(94, "random", B=c["B"], gamma=c["n_q"] - 1, V=1, dtype="bf16", Hq=c["Hq"], Hkv=c["Hkv"], D=c["D"],
+                   L=(0, max(int(c["lens"].max()), 1)), max_T=c["max_T"])
+    inp = W.attention_inputs_int8(cfg, B=c["B"], max_T=c["max_T"], lens=c["lens"])
+    TI._check(inp, TI._run(inp, hint=c["hint"]))
 
 
 @pytest.mark.parametrize("i", range(len(SMP)))
