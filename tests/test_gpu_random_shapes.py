@@ -4,7 +4,8 @@ Valid shapes drawn once from a fixed seed: verify attention (bf16, fp16 and
 fp32 caches; GQA/MQA/MHA groupings; 1-16 verify rows; caches from empty to
 6,000 keys; hints at and above the longest length; rows past each length
 poisoned with NaN), the same over 16- and 32-position pages at random slots
-and over the int8 cache, the rejection sampler (fp32 and bf16 logits, V from 1 to
+and over the int8 cache, the verify forward of random decoders (widths 32-144,
+head dimensions 24-128, 1-4 layers, vocabularies 5-5,000), the rejection sampler (fp32 and bf16 logits, V from 1 to
 200,003, gamma 1-31, temperatures 0.3-1.6, sharp to flat distributions) and
 greedy verification.  Each case is checked against the oracle exactly as the
 fixed-shape tests check theirs.  Every case prints its shape first.
@@ -14,12 +15,15 @@ import numpy as np
 import pytest
 
 import workloads as W
+from oracle import model as M
 from tests import _gpu
 from tests import test_gpu_attention as TA
+from tests import test_gpu_forward as TF
 from tests import test_gpu_greedy as TG
 from tests import test_gpu_int8 as TI
 from tests import test_gpu_paged as TP
 from tests import test_gpu_sampler as TS
+from workloads import gen
 
 pytestmark = pytest.mark.gpu
 
@@ -103,7 +107,28 @@ def _cache_cases(n, seed, int8):
     return out
 
 
+def _forward_cases(n, seed):
+    """Decoder shapes the forward supports: C a multiple of 16 up to 144, C/H
+    a head dimension of the fp32 attention."""
+    rng = np.random.default_rng(seed)
+    shapes = [(48, 2), (96, 4), (144, 6), (32, 1), (64, 2), (96, 3), (128, 4), (64, 1), (128, 2), (128, 1)]
+    out = []
+    for _ in range(n):
+        C, H = shapes[rng.integers(len(shapes))]
+        V = int(rng.choice([5, 96, 1000, 1500, 5000]))
+        L = int(rng.integers(1, 5))
+        nq = int(rng.integers(1, 17))
+        B = int(rng.integers(1, 21))
+        hi = int(rng.choice([0, 30, 200, 480]))
+        lo = int(rng.integers(0, hi + 1))
+        max_T = hi + nq + int(rng.integers(0, 9))
+        T = max(max_T, int(rng.choice([64, 512])))
+        out.append(dict(V=V, C=C, L=L, H=H, T=T, B=B, n=nq, lo=lo, hi=hi, max_T=max_T))
+    return out
+
+
 ATT = _attention_cases(40, 2026)
+FWD = _forward_cases(12, 2031)
 PAGED = _cache_cases(15, 2029, int8=False)
 INT8 = _cache_cases(15, 2030, int8=True)
 SMP = _sampler_cases(30, 2027)
@@ -144,6 +169,26 @@ def test_int8_random_shape(i):
                    L=(0, max(int(c["lens"].max()), 1)), max_T=c["max_T"])
     inp = W.attention_inputs_int8(cfg, B=c["B"], max_T=c["max_T"], lens=c["lens"])
     TI._check(inp, TI._run(inp, hint=c["hint"]))
+
+
+@pytest.mark.parametrize("i", range(len(FWD)))
+def test_forward_random_shape(i):
+    c = FWD[i]
+    print(f"\n[case] forward {i} {c}", flush=True)
+    cfg = M.ModelConfig(c["V"], c["C"], c["L"], c["H"], c["T"])
+    params = gen.model_params(M.param_shapes(cfg), 300 + i)
+    inp = gen.forward_inputs(cfg.V, cfg.L, cfg.H, cfg.D, c["B"], c["n"], (c["lo"], c["hi"]), c["max_T"], 400 + i)
+    lg_g, kv_g = TF._run(cfg, params, inp["tokens"], inp["lens"], inp["kv"], c["hi"])
+    lg_o, kv_o = M.forward_cached(params, cfg, inp["tokens"], inp["kv"], inp["lens"])
+    err = np.abs(lg_g - lg_o).max()
+    print(f"max |logit error| {err:.3g}", flush=True)
+    assert err < TF.TOL
+    for b in range(c["B"]):
+        p0 = int(inp["lens"][b])
+        np.testing.assert_allclose(kv_g[:, :, b, :, p0 : p0 + c["n"]], kv_o[:, :, b, :, p0 : p0 + c["n"]], rtol=0,
+                                   atol=TF.TOL)
+        np.testing.assert_array_equal(kv_g[:, :, b, :, :p0], inp["kv"][:, :, b, :, :p0])
+        np.testing.assert_array_equal(kv_g[:, :, b, :, p0 + c["n"] :], inp["kv"][:, :, b, :, p0 + c["n"] :])
 
 
 @pytest.mark.parametrize("i", range(len(SMP)))
