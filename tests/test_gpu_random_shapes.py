@@ -5,7 +5,8 @@ fp32 caches; GQA/MQA/MHA groupings; 1-16 verify rows; caches from empty to
 6,000 keys; hints at and above the longest length; rows past each length
 poisoned with NaN), the same over 16- and 32-position pages at random slots
 and over the int8 cache, the verify forward of random decoders (widths 32-144,
-head dimensions 24-128, 1-4 layers, vocabularies 5-5,000), the rejection sampler (fp32 and bf16 logits, V from 1 to
+head dimensions 24-128, 1-4 layers, vocabularies 5-5,000), whole speculative
+rounds of random target and draft decoders (gamma 1-15, T 0-1.5), the rejection sampler (fp32 and bf16 logits, V from 1 to
 200,003, gamma 1-31, temperatures 0.3-1.6, sharp to flat distributions) and
 greedy verification.  Each case is checked against the oracle exactly as the
 fixed-shape tests check theirs.  Every case prints its shape first.
@@ -22,6 +23,7 @@ from tests import test_gpu_forward as TF
 from tests import test_gpu_greedy as TG
 from tests import test_gpu_int8 as TI
 from tests import test_gpu_paged as TP
+from tests import test_gpu_round as TR
 from tests import test_gpu_sampler as TS
 from workloads import gen
 
@@ -127,7 +129,26 @@ def _forward_cases(n, seed):
     return out
 
 
+def _round_cases(n, seed):
+    """Target and draft decoders of one vocabulary, round counts and lengths
+    that fit the caches (prompts of 4-12 tokens)."""
+    rng = np.random.default_rng(seed)
+    shapes = [(48, 2), (96, 4), (144, 6), (32, 1), (64, 2), (96, 3), (128, 4), (64, 1), (128, 2)]
+    out = []
+    for _ in range(n):
+        V = int(rng.choice([96, 500, 1500]))
+        (tc, th), (dc, dh) = shapes[rng.integers(len(shapes))], shapes[rng.integers(len(shapes))]
+        gamma = int(rng.integers(1, 16))
+        rounds = int(rng.integers(2, 5))
+        max_len = 12 + rounds * (gamma + 1) + 2
+        out.append(dict(V=V, target=(tc, int(rng.integers(1, 4)), th), draft=(dc, int(rng.integers(1, 3)), dh),
+                        gamma=gamma, T=float(rng.choice([0.0, 0.5, 1.0, 1.5])), rounds=rounds,
+                        B=int(rng.integers(2, 13)), max_len=max_len))
+    return out
+
+
 ATT = _attention_cases(40, 2026)
+RND = _round_cases(8, 2032)
 FWD = _forward_cases(12, 2031)
 PAGED = _cache_cases(15, 2029, int8=False)
 INT8 = _cache_cases(15, 2030, int8=True)
@@ -189,6 +210,16 @@ def test_forward_random_shape(i):
                                    atol=TF.TOL)
         np.testing.assert_array_equal(kv_g[:, :, b, :, :p0], inp["kv"][:, :, b, :, :p0])
         np.testing.assert_array_equal(kv_g[:, :, b, :, p0 + c["n"] :], inp["kv"][:, :, b, :, p0 + c["n"] :])
+
+
+@pytest.mark.parametrize("i", range(len(RND)))
+def test_round_random_shape(i):
+    c = RND[i]
+    print(f"\n[case] round {i} {c}", flush=True)
+    ct = M.ModelConfig(c["V"], c["target"][0], c["target"][1], c["target"][2], 128)
+    cd = M.ModelConfig(c["V"], c["draft"][0], c["draft"][1], c["draft"][2], 128)
+    TR.run_rounds(ct, cd, c["T"], c["gamma"], c["rounds"], B=c["B"], max_len=c["max_len"], max_T=c["max_len"],
+                  seed=500 + i)
 
 
 @pytest.mark.parametrize("i", range(len(SMP)))

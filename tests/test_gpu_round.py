@@ -43,13 +43,18 @@ BIGV_MODELS = (M.ModelConfig(1500, 48, 2, 2, 64), M.ModelConfig(1500, 48, 1, 2, 
                                                     (1.0, 4, 2, "bigvocab"), (0.0, 3, 2, "bigvocab")])
 def test_rounds_match_oracle(T, gamma, rounds, models):
     _case("rounds", T=T, gamma=gamma, rounds=rounds, models=models)
-    dev = torch.device("cuda:0")
     ct, cd = (M.TARGET, M.DRAFT) if models == "char" else BIGV_MODELS
-    pt = gen.model_params(M.param_shapes(ct), 30)
-    pd = gen.model_params(M.param_shapes(cd), 31)
-    B, max_len, max_T = 8, 64, 64
-    rng = np.random.default_rng(32)
-    prompts = [list(rng.integers(0, ct.V, size=int(rng.integers(4, 13)))) for _ in range(B)]
+    run_rounds(ct, cd, T, gamma, rounds, B=8, max_len=64, max_T=64, seed=32)
+
+
+def run_rounds(ct, cd, T, gamma, rounds, B, max_len, max_T, seed, prompt_len=(4, 13)):
+    """``rounds`` rounds of B sequences on the GPU and in the oracle, compared
+    round by round (see the module docstring); prompts of prompt_len tokens."""
+    dev = torch.device("cuda:0")
+    pt = gen.model_params(M.param_shapes(ct), seed - 2)
+    pd = gen.model_params(M.param_shapes(cd), seed - 1)
+    rng = np.random.default_rng(seed)
+    prompts = [list(rng.integers(0, ct.V, size=int(rng.integers(*prompt_len)))) for _ in range(B)]
     st = R.start(pt, ct, pd, cd, prompts, max_T, max_T)
 
     seq = np.zeros((B, max_len), np.int32)
