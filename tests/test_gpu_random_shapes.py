@@ -3,7 +3,9 @@
 Valid shapes drawn once from a fixed seed: verify attention (bf16, fp16 and
 fp32 caches; GQA/MQA/MHA groupings; 1-16 verify rows; caches from empty to
 6,000 keys; hints at and above the longest length; rows past each length
-poisoned with NaN), the same over 16- and 32-position pages at random slots
+poisoned with NaN; and long caches of up to 32K keys, drawn on the device,
+whose shares are long enough that the launch merges each slab's pieces
+itself, checked on sampled sequences), the same over 16- and 32-position pages at random slots
 and over the int8 cache, the verify forward of random decoders (widths 32-144,
 head dimensions 24-128, 1-4 layers, vocabularies 5-5,000), whole speculative
 rounds of random target and draft decoders (gamma 1-15, T 0-1.5), the rejection sampler (fp32 and bf16 logits, V from 1 to
@@ -14,7 +16,9 @@ fixed-shape tests check theirs.  Every case prints its shape first.
 
 import numpy as np
 import pytest
+import torch
 
+import speculative_decoding_verification_spec_amd as sv
 import workloads as W
 from oracle import model as M
 from tests import _gpu
@@ -147,7 +151,27 @@ def _round_cases(n, seed):
     return out
 
 
+def _long_cases(n, seed):
+    """Batches of long caches (device-drawn), sequences sampled for the check.
+    65-80 rows per KV head run the five-wave kernel on 512 workgroups, and the
+    batch is large enough that an equal share of the key blocks exceeds 300
+    blocks, so the launch merges the pieces itself."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        # 65-80 rows per KV head: the five-wave kernel (512 workgroups)
+        Hq, Hkv, n_q = [(64, 8, 9), (32, 4, 9), (64, 4, 5), (128, 8, 5)][rng.integers(4)]
+        hi = int(rng.integers(24576, 32769))
+        lo = int(rng.integers(8192, hi + 1))
+        need = -(-300 * 512 * 32 * 2 // (Hkv * (lo + hi)))  # sequences for a 300-block share
+        B = max(need, int(rng.integers(8, 65)))
+        out.append(dict(dtype=["bf16", "f16"][rng.integers(2)], D=int(rng.choice([64, 128])), Hq=Hq, Hkv=Hkv,
+                        n_q=n_q, B=B, L=(lo, hi)))
+    return out
+
+
 ATT = _attention_cases(40, 2026)
+LONG = _long_cases(4, 2033)
 RND = _round_cases(8, 2032)
 FWD = _forward_cases(12, 2031)
 PAGED = _cache_cases(15, 2029, int8=False)
@@ -166,6 +190,22 @@ def test_attention_random_shape(i):
     inp = W.attention_inputs(cfg, B=c["B"], max_T=c["max_T"], lens=c["lens"])
     out, kc, vc = TA._run_host(inp, hint=c["hint"], poison_tail=True)
     TA._check(inp, out, kc, vc, c["dtype"])
+
+
+@pytest.mark.parametrize("i", range(len(LONG)))
+def test_attention_random_long(i):
+    c = LONG[i]
+    print(f"\n[case] long attention {i} {c}", flush=True)
+    cfg = W.Config(89, "random-long", B=c["B"], gamma=c["n_q"] - 1, V=1, dtype=c["dtype"], Hq=c["Hq"], Hkv=c["Hkv"],
+                   D=c["D"], L=c["L"], max_T=c["L"][1] + c["n_q"] + 8)
+    d = W.attention_inputs_device(cfg, "cuda")
+    seqs = TA._sample_long(_gpu.to_host(d["lens"]), 4, 89 + i)
+    before = TA._rows_before(d, seqs)
+    out = sv.spec_verify_attention(d["q"], d["k_new"], d["v_new"], d["k_cache"], d["v_cache"], d["lens"], c["L"][1])
+    torch.cuda.synchronize()
+    TA._check_one_by_one(d, out, seqs, c["dtype"], before)
+    del d
+    torch.cuda.empty_cache()
 
 
 def _describe(c):
