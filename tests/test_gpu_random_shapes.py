@@ -1,17 +1,24 @@
 """GPU parity at seeded random shapes, beside the hand-picked ones.
 
-Valid shapes drawn once from a fixed seed: verify attention (bf16, fp16 and
-fp32 caches; GQA/MQA/MHA groupings; 1-16 verify rows; caches from empty to
-6,000 keys; hints at and above the longest length; rows past each length
-poisoned with NaN; and long caches of up to 32K keys, drawn on the device,
-whose shares are long enough that the launch merges each slab's pieces
-itself, checked on sampled sequences), the same over 16- and 32-position pages at random slots
-and over the int8 cache, the verify forward of random decoders (widths 32-144,
-head dimensions 24-128, 1-4 layers, vocabularies 5-5,000), whole speculative
-rounds of random target and draft decoders (gamma 1-15, T 0-1.5), the rejection sampler (fp32 and bf16 logits, V from 1 to
-200,003, gamma 1-31, temperatures 0.3-1.6, sharp to flat distributions) and
-greedy verification.  Each case is checked against the oracle exactly as the
-fixed-shape tests check theirs.  Every case prints its shape first.
+Valid shapes drawn once from fixed seeds, each case checked against the
+oracle exactly as the fixed-shape tests check theirs:
+  * verify attention over bf16, fp16 and fp32 caches: GQA/MQA/MHA groupings,
+    1-16 verify rows, caches from empty to 6,000 keys, hints at and above
+    the longest length, rows past each length poisoned with NaN;
+  * long caches of up to 32K keys drawn on the device, whose shares are long
+    enough that the launch merges each slab's pieces itself (sampled
+    sequences checked);
+  * the same attention over 16- and 32-position pages at random slots, and
+    over the int8 cache;
+  * the verify forward of random decoders (widths 32-144, head dimensions
+    24-128, 1-4 layers, vocabularies 5-5,000);
+  * whole speculative rounds of random target and draft decoders (gamma
+    1-15, T 0-1.5);
+  * the rejection sampler over fp32 and bf16 logits (V from 1 to 200,003,
+    gamma 1-31, T 0.3-1.6, sharp to flat distributions), and large batches
+    drawn on the device (sampled sequences checked);
+  * greedy verification.
+Every case prints its shape first.
 """
 
 import numpy as np
@@ -170,7 +177,24 @@ def _long_cases(n, seed):
     return out
 
 
+def _large_sampler_cases(n, seed):
+    """bf16 logits drawn on the device, batches of over 65,536 row segments of
+    2,048 logits (the statistics pass's large-batch launch shape)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        V = int(rng.choice([65536, 100003, 128256, 151936]))
+        gamma = int(rng.integers(2, 16))
+        nseg = -(-V // 2048)
+        need = -(-65537 // ((2 * gamma + 1) * nseg))
+        out.append(dict(V=V, gamma=gamma, B=max(need, int(rng.integers(16, 129))), T=float(rng.choice([0.7, 1.0, 1.3])),
+                        t_std=float(rng.choice([2.5, 4.0])), mix=float(rng.choice([0.8, 0.95])),
+                        noise_std=float(rng.choice([0.5, 1.0]))))
+    return out
+
+
 ATT = _attention_cases(40, 2026)
+SMP_LARGE = _large_sampler_cases(4, 2034)
 LONG = _long_cases(4, 2033)
 RND = _round_cases(8, 2032)
 FWD = _forward_cases(12, 2031)
@@ -271,6 +295,24 @@ def test_sampler_random_shape(i):
     inp = W.sampler_inputs(cfg, temperature=c["T"])
     n, tok, p, q = TS._run(inp)
     print("stats", _gpu.compare_sampler(TS._oracle(inp), n, tok, p, q), flush=True)
+
+
+@pytest.mark.parametrize("i", range(len(SMP_LARGE)))
+def test_sampler_random_large_batch(i):
+    c = SMP_LARGE[i]
+    print(f"\n[case] large-batch sampler {i} {c}", flush=True)
+    cfg = W.Config(88, "random-large", B=c["B"], gamma=c["gamma"], V=c["V"], dtype="bf16", t_std=c["t_std"],
+                   mix=c["mix"], noise_std=c["noise_std"])
+    d = W.sampler_inputs_device(cfg, "cuda", temperature=c["T"])
+    n, tok, p, q = sv.spec_reject_sample(d["target_logits"], d["draft_logits"], d["draft_tokens"], d["uniforms"],
+                                         c["T"], want_probs=True)
+    torch.cuda.synchronize()
+    seqs = np.sort(np.random.default_rng(88 + i).choice(c["B"], size=16, replace=False))
+    host = {k: _gpu.to_host(d[k][seqs]) for k in ("target_logits", "draft_logits", "draft_tokens", "uniforms")}
+    host["temperature"] = c["T"]
+    st = _gpu.compare_sampler(TS._oracle(host), _gpu.to_host(n)[seqs], _gpu.to_host(tok)[seqs],
+                              _gpu.to_host(p)[seqs], _gpu.to_host(q)[seqs])
+    print("stats", st, flush=True)
 
 
 @pytest.mark.parametrize("i", range(len(GR)))
